@@ -1,0 +1,116 @@
+"""fp64 CPU oracle of the delta-rule forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The library path never does, and this package imports nothing
+from the library: the two share no code.  The arithmetic lives in
+``dr_oracle.c`` (plain C, fp64, one token at a time); this file builds it with
+gcc and calls it through ctypes.
+
+Recurrence (FG2-GDN page, section 2, the scaled key/value and state-update
+equations; DeltaNet page, step list, step 6 for the output):
+    kt = sqrt(beta) * k,  vt = sqrt(beta) * v
+    S_t = (I - kt kt^T) Diag(alpha_t) S_{t-1} + kt vt^T,   o_t = S_t^T q_t
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dr_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libdr_oracle.so")
+
+GATE_CODES = {"none": 0, "scalar": 1, "channel": 2}
+BETA_CODES = {"scalar": 0, "channel": 1}
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = LIB_PATH) -> str:
+    """Compile the oracle with gcc (fp64, OpenMP over sequences)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+           "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str = LIB_PATH):
+    """Load (building if absent) an oracle library and declare its entry points."""
+    if not os.path.exists(path):
+        build(out=path)
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.dro_forward.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp,
+                                                      ctypes.c_int, dp, dp, dp, ctypes.c_int]
+    lib.dro_forward.restype = ctypes.c_int
+    lib.dro_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def _get():
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+def _f64(a: Optional[np.ndarray]):
+    if a is None:
+        return None, None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
+            nthreads: int = 0, lib=None):
+    """Run the recurrence over [B, H, L, D] inputs; returns (o, S_final) in fp64.
+
+    log_alpha is [B,H,L] (scalar gate), [B,H,L,Dk] (channel gate) or None
+    (gate "none"); beta is [B,H,L] or [B,H,L,Dk]; S0 is [B,H,Dk,Dv] or None.
+    """
+    lib = lib or _get()
+    q = np.asarray(q)
+    B, H, L, Dk = q.shape
+    Dv = np.asarray(v).shape[-1]
+    qa, qp = _f64(q)
+    ka, kp = _f64(k)
+    va, vp = _f64(v)
+    la, lp = _f64(log_alpha)
+    ba, bp = _f64(beta)
+    sa, sp = _f64(S0)
+    o = np.empty((B, H, L, Dv), np.float64)
+    Sf = np.empty((B, H, Dk, Dv), np.float64)
+    rc = lib.dro_forward(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp,
+                         BETA_CODES[beta_mode], sp,
+                         o.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                         Sf.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"dro_forward rejected its arguments (code {rc})")
+    return o, Sf
+
+
+def forward_problem(p, nthreads: int = 0, lib=None):
+    """Oracle over a ChunkProblem-like object (fields as the input generator's)."""
+    return forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, gate=p.gate,
+                   beta_mode=p.beta_mode, nthreads=nthreads, lib=lib)
+
+
+def decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str,
+                nthreads: int = 0, lib=None):
+    """One recurrent step for a batch of states: S [N,H,Dk,Dv], q/k/v [N,H,D].
+
+    The decode step is the forward with a single token, started from S.
+    Returns (o [N,H,Dv], S_new [N,H,Dk,Dv]) in fp64.
+    """
+    ex = lambda a: None if a is None else np.asarray(a)[:, :, None]
+    o, Sn = forward(ex(q), ex(k), ex(v), ex(log_alpha), ex(beta), S, gate=gate,
+                    beta_mode=beta_mode, nthreads=nthreads, lib=lib)
+    return o[:, :, 0], Sn
+
+
+def max_threads(lib=None) -> int:
+    return int((lib or _get()).dro_max_threads())

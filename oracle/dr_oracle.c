@@ -1,0 +1,170 @@
+/*
+ * dr_oracle.c -- plain fp64 CPU oracle of the delta-rule forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library path may include, link or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no code with the HIP kernels.
+ *
+ * What it computes, token by token, for every (batch b, head h) independently:
+ *
+ *   FG2-GDN page, section 2 ("Kerninnovation"), the scaled key/value equation:
+ *       kt = sqrt(beta_t) (.) k_t        vt = sqrt(beta_t) (.) v_t
+ *     beta_t is a scalar (DeltaNet / GDN / KDA) or a d_k-vector (FG2-GDN);
+ *     a scalar beta scales every channel alike.
+ *   FG2-GDN page, section 2, the state-update equation:
+ *       S_t = (I - kt kt^T) Diag(alpha_t) S_{t-1} + kt vt^T
+ *     S is d_k x d_v.  alpha_t is 1 (plain DeltaNet), a scalar (Gated
+ *     DeltaNet, section 1 of the same page) or a d_k-vector (KDA, idem);
+ *     it is passed as log alpha.
+ *   DeltaNet page, the seven-step list, step 6: the output reads the updated
+ *   state, o_t = S_t^T q_t (the page writes S q with S stored d_v x d_k).
+ *
+ * The update is evaluated in the rank-one form that the DeltaNet page's steps
+ * 3-5 describe (read the current map, form the error, add the outer product):
+ *       S'  = Diag(alpha_t) S_{t-1}
+ *       p   = S'^T kt                     (what the memory returns for kt)
+ *       S_t = S' + kt (vt - p)^T
+ * which is the printed product expanded: (I - kt kt^T) S' + kt vt^T.  A test
+ * checks it against the literal dense product.
+ *
+ * No query scaling is applied.  All arithmetic is IEEE fp64.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { DRO_GATE_NONE = 0, DRO_GATE_SCALAR = 1, DRO_GATE_CHANNEL = 2 };
+enum { DRO_BETA_SCALAR = 0, DRO_BETA_CHANNEL = 1 };
+
+/* Return codes. */
+enum { DRO_OK = 0, DRO_EINVAL = 1, DRO_ENOMEM = 2 };
+
+/* One (b, h) sequence.  Pointers are already offset to that sequence:
+ *   q, k   [L][Dk]      v, o [L][Dv]
+ *   la     [L] or [L][Dk] (NULL when gate == NONE)
+ *   beta   [L] or [L][Dk]
+ *   S      [Dk][Dv]  in: initial state, out: final state
+ *   kt, vt scratch of Dk and Dv doubles, p scratch of Dv doubles. */
+static void run_sequence(int L, int Dk, int Dv,
+                         const double* q, const double* k, const double* v,
+                         const double* la, int gate, const double* beta, int beta_mode,
+                         double* S, double* o, double* kt, double* vt, double* p)
+{
+    for (int t = 0; t < L; ++t) {
+        const double* qt = q + (size_t)t * Dk;
+        const double* k_t = k + (size_t)t * Dk;
+        const double* v_t = v + (size_t)t * Dv;
+
+        /* scaled key and value */
+        for (int c = 0; c < Dk; ++c) {
+            double b = beta_mode == DRO_BETA_SCALAR ? beta[t] : beta[(size_t)t * Dk + c];
+            kt[c] = sqrt(b) * k_t[c];
+        }
+        for (int j = 0; j < Dv; ++j) {
+            /* channel beta scales v's channel j by beta's channel j (d_v == d_k) */
+            double b = beta_mode == DRO_BETA_SCALAR ? beta[t] : beta[(size_t)t * Dk + j];
+            vt[j] = sqrt(b) * v_t[j];
+        }
+
+        /* S' = Diag(alpha_t) S : row c of S is scaled by alpha_t[c] */
+        if (gate != DRO_GATE_NONE) {
+            for (int c = 0; c < Dk; ++c) {
+                double a = gate == DRO_GATE_SCALAR ? exp(la[t]) : exp(la[(size_t)t * Dk + c]);
+                double* row = S + (size_t)c * Dv;
+                for (int j = 0; j < Dv; ++j) row[j] *= a;
+            }
+        }
+
+        /* p = S'^T kt */
+        for (int j = 0; j < Dv; ++j) p[j] = 0.0;
+        for (int c = 0; c < Dk; ++c) {
+            const double* row = S + (size_t)c * Dv;
+            for (int j = 0; j < Dv; ++j) p[j] += row[j] * kt[c];
+        }
+
+        /* S_t = S' + kt (vt - p)^T */
+        for (int c = 0; c < Dk; ++c) {
+            double* row = S + (size_t)c * Dv;
+            for (int j = 0; j < Dv; ++j) row[j] += kt[c] * (vt[j] - p[j]);
+        }
+
+        /* o_t = S_t^T q_t */
+        double* ot = o + (size_t)t * Dv;
+        for (int j = 0; j < Dv; ++j) ot[j] = 0.0;
+        for (int c = 0; c < Dk; ++c) {
+            const double* row = S + (size_t)c * Dv;
+            for (int j = 0; j < Dv; ++j) ot[j] += row[j] * qt[c];
+        }
+    }
+}
+
+/*
+ * dro_forward -- the whole batch.
+ *   q, k      [B][H][L][Dk] fp64
+ *   v         [B][H][L][Dv] fp64
+ *   log_alpha [B][H][L] (gate SCALAR) or [B][H][L][Dk] (gate CHANNEL); NULL for NONE
+ *   beta      [B][H][L] (SCALAR) or [B][H][L][Dk] (CHANNEL; needs Dv == Dk)
+ *   S0        [B][H][Dk][Dv] or NULL (zeros)
+ *   o         [B][H][L][Dv]     out
+ *   S_final   [B][H][Dk][Dv]    out, may be NULL
+ *   nthreads  worker threads over (b, h); <= 0 means the OpenMP default
+ * Decode is the same call with L == 1 and S0 the current states.
+ */
+int dro_forward(int B, int H, int L, int Dk, int Dv,
+                const double* q, const double* k, const double* v,
+                const double* log_alpha, int gate, const double* beta, int beta_mode,
+                const double* S0, double* o, double* S_final, int nthreads)
+{
+    if (B <= 0 || H <= 0 || L < 0 || Dk <= 0 || Dv <= 0) return DRO_EINVAL;
+    if (!q || !k || !v || !beta || !o) return DRO_EINVAL;
+    if (gate < DRO_GATE_NONE || gate > DRO_GATE_CHANNEL) return DRO_EINVAL;
+    if (beta_mode != DRO_BETA_SCALAR && beta_mode != DRO_BETA_CHANNEL) return DRO_EINVAL;
+    if ((gate == DRO_GATE_NONE) != (log_alpha == NULL)) return DRO_EINVAL;
+    if (beta_mode == DRO_BETA_CHANNEL && Dv != Dk) return DRO_EINVAL;
+
+    const long nseq = (long)B * H;
+    const size_t sz = (size_t)Dk * Dv;
+    int err = DRO_OK;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (long s = 0; s < nseq; ++s) {
+        double* S = (double*)malloc(sizeof(double) * (sz + 2 * (size_t)Dk + 2 * (size_t)Dv));
+        if (!S) {
+            err = DRO_ENOMEM;
+            continue;
+        }
+        double* kt = S + sz;
+        double* vt = kt + Dk;
+        double* p = vt + Dv;
+        if (S0) memcpy(S, S0 + (size_t)s * sz, sizeof(double) * sz);
+        else memset(S, 0, sizeof(double) * sz);
+        const size_t lw = (gate == DRO_GATE_CHANNEL) ? (size_t)L * Dk : (size_t)L;
+        const size_t bw = (beta_mode == DRO_BETA_CHANNEL) ? (size_t)L * Dk : (size_t)L;
+        run_sequence(L, Dk, Dv,
+                     q + (size_t)s * L * Dk, k + (size_t)s * L * Dk, v + (size_t)s * L * Dv,
+                     log_alpha ? log_alpha + (size_t)s * lw : NULL, gate,
+                     beta + (size_t)s * bw, beta_mode,
+                     S, o + (size_t)s * L * Dv, kt, vt, p);
+        if (S_final) memcpy(S_final + (size_t)s * sz, S, sizeof(double) * sz);
+        free(S);
+    }
+    (void)nthreads;
+    return err;
+}
+
+/* Threads the OpenMP runtime would use by default (1 without OpenMP). */
+int dro_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,48 @@
+"""Plant plausible mistakes in copies of the oracle's C source and check that
+the pin suite catches every one of them (CPU only).  The mistakes are planted
+in temporary copies; the committed oracle is never modified."""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "dr_oracle.c")
+
+# (name, original text, planted text): each original must occur exactly once.
+MUTANTS = [
+    ("drop_decay", "row[j] *= a;", "row[j] *= 1.0;"),
+    ("sign_of_error", "row[j] += kt[c] * (vt[j] - p[j]);", "row[j] += kt[c] * (vt[j] + p[j]);"),
+    ("beta_not_sqrt", "kt[c] = sqrt(b) * k_t[c];", "kt[c] = b * k_t[c];"),
+    ("value_unscaled", "vt[j] = sqrt(b) * v_t[j];", "vt[j] = v_t[j];"),
+    ("read_unscaled_key", "p[j] += row[j] * kt[c];", "p[j] += row[j] * k_t[c];"),
+    ("output_from_query_free_state", "ot[j] += row[j] * qt[c];", "ot[j] += row[j] * k_t[c];"),
+    ("gate_index_shift", "exp(la[(size_t)t * Dk + c])", "exp(la[(size_t)t * Dk + (c + 1) % Dk])"),
+    ("channel_beta_wrong_channel", "beta[(size_t)t * Dk + j]", "beta[(size_t)t * Dk + (Dk - 1 - j)]"),
+    ("error_drops_read", "(vt[j] - p[j])", "(vt[j] - 0.0 * p[j])"),
+    ("state_not_carried", "if (S0) memcpy(S, S0", "if (0) memcpy(S, S0"),
+    ("output_before_update",
+     "/* S_t = S' + kt (vt - p)^T */",
+     "for (int j = 0; j < Dv; ++j) { double a_ = 0; for (int c = 0; c < Dk; ++c) a_ += S[(size_t)c * Dv + j] * qt[c]; o[(size_t)t * Dv + j] = a_; }\n        if (0)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+
+    def fwd(q, k, v, la, beta, S0, *, gate, beta_mode):
+        return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, lib=lib)
+
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(fwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"

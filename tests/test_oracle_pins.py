@@ -1,0 +1,41 @@
+"""The fp64 oracle against its pins (CPU only).  See oracle_pins.py for the
+passage each pin follows."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+
+
+def fwd(q, k, v, la, beta, S0, *, gate, beta_mode):
+    return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(fwd)
+
+
+def test_thread_count_does_not_change_bits():
+    q, k, v, la, beta, S0 = oracle_pins.random_case(7, B=3, H=5, L=20, Dk=8, Dv=8, gate="channel",
+                                                    beta_mode="channel")
+    a = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode="channel", nthreads=1)
+    b = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode="channel", nthreads=8)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_rejects_bad_arguments():
+    q, k, v, la, beta, S0 = oracle_pins.random_case(8, gate="scalar", Dk=4, Dv=3)
+    with pytest.raises(ValueError):       # channel beta needs d_v == d_k
+        oracle.forward(q, k, v, la, np.repeat(beta[..., None], 4, -1), S0, gate="scalar",
+                       beta_mode="channel")
+    with pytest.raises(ValueError):       # gate none with a log alpha given
+        oracle.forward(q, k, v, la, beta, S0, gate="none", beta_mode="scalar")
+
+
+def test_decode_step_is_one_token_forward():
+    q, k, v, la, beta, S0 = oracle_pins.random_case(9, B=3, H=2, L=1, Dk=6, Dv=5, gate="scalar")
+    o1, S1 = oracle.decode_step(S0, q[:, :, 0], k[:, :, 0], v[:, :, 0], la[:, :, 0], beta[:, :, 0],
+                                gate="scalar", beta_mode="scalar")
+    o2, S2 = oracle.forward(q, k, v, la, beta, S0, gate="scalar", beta_mode="scalar")
+    assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
