@@ -1,0 +1,224 @@
+"""delta_rule_linear_amd -- MI355X (gfx950) delta-rule linear-attention forward.
+
+Thin Python binding over the C ABI in include/deltarule.h, with the same names.
+It only marshals arguments (shape checks, output and workspace allocation with
+PyTorch, the current HIP stream); every step of the computation runs in the
+HIP kernels of libdeltarule.so.  If the library is missing the binding raises:
+there is no fallback path.
+
+    o, S = dr_chunk_fwd(q, k, v, log_alpha, beta, S0, gate="scalar", beta_mode="scalar")
+    o = dr_decode_step(S, q, k, v, log_alpha, beta, gate="scalar", beta_mode="scalar")
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
+
+DR_ABI_VERSION = 1
+DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
+DR_F32, DR_BF16 = 0, 1
+GATES = {"none": 0, "scalar": 1, "channel": 2}
+BETAS = {"scalar": 0, "channel": 1}
+EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_decode_step", "dr_status_str",
+           "dr_last_error", "dr_abi_version")
+
+
+class DeltaRuleError(RuntimeError):
+    """A dr_* call returned an error status."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{dr_status_str(status)} ({detail})")
+
+
+class ChunkDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("L", ctypes.c_int), ("Dk", ctypes.c_int),
+                ("Dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("gate", ctypes.c_int), ("beta", ctypes.c_int)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("Dk", ctypes.c_int), ("Dv", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("gate", ctypes.c_int),
+                ("beta", ctypes.c_int)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m delta_rule_linear_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.dr_chunk_fwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.dr_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.dr_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
+        L.dr_chunk_fwd.restype = ctypes.c_int
+        L.dr_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp]
+        L.dr_decode_step.restype = ctypes.c_int
+        L.dr_status_str.argtypes = [ctypes.c_int]
+        L.dr_status_str.restype = ctypes.c_char_p
+        L.dr_last_error.argtypes = []
+        L.dr_last_error.restype = ctypes.c_char_p
+        L.dr_abi_version.argtypes = []
+        L.dr_abi_version.restype = ctypes.c_int
+        if L.dr_abi_version() != DR_ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {L.dr_abi_version()}, binding expects {DR_ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def dr_abi_version() -> int:
+    return int(lib().dr_abi_version())
+
+
+def dr_status_str(status: int) -> str:
+    return lib().dr_status_str(int(status)).decode()
+
+
+def dr_last_error() -> str:
+    return lib().dr_last_error().decode()
+
+
+def _check(status: int):
+    if status != DR_OK:
+        raise DeltaRuleError(status, dr_last_error())
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (argument marshalling only)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return DR_BF16
+    if dt == torch.float32:
+        return DR_F32
+    raise TypeError(f"unsupported dtype {dt}: use torch.bfloat16 or torch.float32")
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _need(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def chunk_desc(B, H, L, Dk, Dv, in_dtype, out_dtype, gate: str, beta_mode: str) -> ChunkDesc:
+    return ChunkDesc(B, H, L, Dk, Dv, in_dtype, out_dtype, GATES[gate], BETAS[beta_mode])
+
+
+def dr_chunk_fwd_workspace_bytes(desc: ChunkDesc) -> int:
+    return int(lib().dr_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def dr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
+                 out_dtype=None, o=None, S_final=None, want_state: bool = True,
+                 workspace=None, stream=None):
+    """Chunked forward over [B, H, L, D] device tensors; returns (o, S_final).
+
+    q, k: [B,H,L,Dk]; v: [B,H,L,Dv] (bf16 or fp32, same dtype); log_alpha:
+    [B,H,L] / [B,H,L,Dk] fp32 or None for gate "none"; beta: [B,H,L] /
+    [B,H,L,Dk] fp32; S0: [B,H,Dk,Dv] fp32 or None.  S_final may be passed in
+    (it may be S0 itself for an in-place carry); with want_state=False no
+    final state is written and None is returned for it.
+    """
+    torch = _torch()
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, H, L, Dk))
+    _need(v, "v", q.dtype, (B, H, L, Dv))
+    gshape = {"none": None, "scalar": (B, H, L), "channel": (B, H, L, Dk)}[gate]
+    if gshape is None:
+        if log_alpha is not None:
+            raise ValueError("gate 'none' takes no log_alpha")
+    else:
+        _need(log_alpha, "log_alpha", torch.float32, gshape)
+    _need(beta, "beta", torch.float32, (B, H, L) if beta_mode == "scalar" else (B, H, L, Dk))
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, H, L, Dv), dtype=out_dtype, device=q.device)
+    else:
+        _need(o, "o", out_dtype, (B, H, L, Dv))
+    if want_state and S_final is None:
+        S_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    elif S_final is not None:
+        _need(S_final, "S_final", torch.float32, (B, H, Dk, Dv))
+    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), gate, beta_mode)
+    nbytes = dr_chunk_fwd_workspace_bytes(desc)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                              _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace),
+                              wbytes, _stream(stream)))
+    return o, S_final
+
+
+def dr_decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str, out_dtype=None,
+                   o=None, stream=None):
+    """One decode step for N x H states (updated in place); returns o [N,H,Dv].
+
+    S: [N,H,Dk,Dv] fp32; q, k: [N,H,Dk]; v: [N,H,Dv]; log_alpha: [N,H] /
+    [N,H,Dk] or None; beta: [N,H] / [N,H,Dk].
+    """
+    torch = _torch()
+    N, H, Dk, Dv = S.shape
+    _need(S, "S", torch.float32)
+    _need(q, "q", None, (N, H, Dk))
+    _need(k, "k", q.dtype, (N, H, Dk))
+    _need(v, "v", q.dtype, (N, H, Dv))
+    gshape = {"none": None, "scalar": (N, H), "channel": (N, H, Dk)}[gate]
+    if gshape is None:
+        if log_alpha is not None:
+            raise ValueError("gate 'none' takes no log_alpha")
+    else:
+        _need(log_alpha, "log_alpha", torch.float32, gshape)
+    _need(beta, "beta", torch.float32, (N, H) if beta_mode == "scalar" else (N, H, Dk))
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=out_dtype, device=S.device)
+    else:
+        _need(o, "o", out_dtype, (N, H, Dv))
+    desc = DecodeDesc(N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), GATES[gate],
+                      BETAS[beta_mode])
+    _check(lib().dr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                _ptr(beta), _ptr(S), _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,223 @@
+// dr_abi.hip -- host side of the C ABI declared in include/deltarule.h:
+// argument validation, workspace layout, dispatch to the kernel launchers and
+// the per-thread error text.  Nothing here allocates device memory.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <limits>
+
+#include "../../include/deltarule.h"
+#include "dr_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dr_status fail(dr_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dr_status fail(dr_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool valid_dtype(int x) { return x == DR_F32 || x == DR_BF16; }
+bool valid_gate(int x) { return x == DR_GATE_NONE || x == DR_GATE_SCALAR || x == DR_GATE_CHANNEL; }
+bool valid_beta(int x) { return x == DR_BETA_SCALAR || x == DR_BETA_CHANNEL; }
+
+// Shared shape/mode checks.  `nseq` sequences (or states) of Dk x Dv.
+dr_status check_modes(int Dk, int Dv, int in_dtype, int out_dtype, int gate, int beta) {
+    if (Dk != 64 && Dk != 128) return fail(DR_ERR_UNSUPPORTED, "Dk=%d: supported Dk are 64 and 128", Dk);
+    if (Dv < 16 || Dv > 256 || Dv % 16 != 0)
+        return fail(DR_ERR_UNSUPPORTED, "Dv=%d: Dv must be a multiple of 16 in [16, 256]", Dv);
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+        return fail(DR_ERR_UNSUPPORTED, "unknown dtype (in %d, out %d)", in_dtype, out_dtype);
+    if (!valid_gate(gate)) return fail(DR_ERR_UNSUPPORTED, "unknown gate mode %d", gate);
+    if (!valid_beta(beta)) return fail(DR_ERR_UNSUPPORTED, "unknown beta mode %d", beta);
+    if (beta == DR_BETA_CHANNEL && Dv != Dk)
+        return fail(DR_ERR_UNSUPPORTED, "channel-wise beta scales v by beta's channels: needs Dv == Dk (%d != %d)", Dv, Dk);
+    return DR_OK;
+}
+
+// Workspace regions, each 256-byte aligned, for a validated descriptor.
+struct WsLayout {
+    size_t T, Pm, G, Q, Ks, Kl, V, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const dr_chunk_desc& d) {
+    WsLayout w{};
+    const size_t P = d.in_dtype == DR_F32 ? 2 : 1;
+    const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
+    const size_t NCH = (size_t)d.B * d.H * NC;
+    const bool cg = d.gate == DR_GATE_CHANNEL, cb = d.beta == DR_BETA_CHANNEL;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    const size_t opnd = NCH * P * dr::CH * d.Dk * sizeof(dr::half_t);
+    w.T = take(NCH * P * dr::CH * dr::CH * sizeof(dr::half_t));
+    w.Pm = take(NCH * P * dr::CH * dr::CH * sizeof(dr::half_t));
+    w.G = take(NCH * dr::kGW * sizeof(float));
+    w.Q = cg ? take(opnd) : 0;
+    w.Ks = (cg || cb) ? take(opnd) : 0;
+    w.Kl = cg ? take(opnd) : 0;
+    w.V = cb ? take(opnd) : 0;
+    w.total = NCH ? off : 0;
+    return w;
+}
+
+dr_status check_chunk_desc(const dr_chunk_desc* d) {
+    if (!d) return fail(DR_ERR_NULL, "descriptor is NULL");
+    if (d->B < 0 || d->H < 0 || d->L < 0)
+        return fail(DR_ERR_SHAPE, "negative dimension (B=%d H=%d L=%d)", d->B, d->H, d->L);
+    dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta);
+    if (s != DR_OK) return s;
+    if (d->B > 65535 || d->H > 65535)
+        return fail(DR_ERR_UNSUPPORTED, "B and H are limited to 65535 (grid dimensions)");
+    const size_t nseq = (size_t)d->B * d->H;
+    if (nseq > (size_t)std::numeric_limits<int>::max() / 256)
+        return fail(DR_ERR_UNSUPPORTED, "B*H=%zu too large", nseq);
+    return DR_OK;
+}
+
+__global__ void copy_state_kernel(float* dst, const float* src, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dr_abi_version(void) { return DR_ABI_VERSION; }
+
+const char* dr_last_error(void) { return g_err; }
+
+const char* dr_status_str(dr_status s) {
+    switch (s) {
+        case DR_OK: return "DR_OK";
+        case DR_ERR_NULL: return "DR_ERR_NULL: required pointer missing";
+        case DR_ERR_SHAPE: return "DR_ERR_SHAPE: invalid dimension";
+        case DR_ERR_UNSUPPORTED: return "DR_ERR_UNSUPPORTED: unsupported size, mode or dtype";
+        case DR_ERR_ALIGN: return "DR_ERR_ALIGN: pointer not 16-byte aligned";
+        case DR_ERR_WORKSPACE: return "DR_ERR_WORKSPACE: workspace missing or too small";
+        case DR_ERR_HIP: return "DR_ERR_HIP: HIP runtime or launch failure";
+    }
+    return "unknown dr_status";
+}
+
+size_t dr_chunk_fwd_workspace_bytes(const dr_chunk_desc* d) {
+    if (check_chunk_desc(d) != DR_OK) return 0;
+    return ws_layout(*d).total;
+}
+
+dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* S0, void* o,
+                       float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    dr_status s = check_chunk_desc(d);
+    if (s != DR_OK) return s;
+    const size_t nseq = (size_t)d->B * d->H;
+    const bool tokens = nseq > 0 && d->L > 0;
+    if (tokens) {
+        if (!q || !k || !v || !beta || !o) return fail(DR_ERR_NULL, "q, k, v, beta and o are required");
+        if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
+            return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
+    }
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_final, workspace};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "S0", "o", "S_final", "workspace"};
+    for (int i = 0; i < 9; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    if (S_final && S0 && S_final != S0) {
+        const size_t bytes = nseq * d->Dk * d->Dv * sizeof(float);
+        const char* a0 = (const char*)S0;
+        const char* a1 = (const char*)S_final;
+        if (a0 < a1 + bytes && a1 < a0 + bytes)
+            return fail(DR_ERR_UNSUPPORTED, "S_final overlaps S0 without being the same array");
+    }
+    const WsLayout w = ws_layout(*d);
+    if (w.total) {
+        if (!workspace) return fail(DR_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
+        if (workspace_bytes < w.total)
+            return fail(DR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    if (nseq == 0) return DR_OK;
+    if (d->L == 0) {
+        // no tokens: the final state is the initial state
+        if (S_final && S_final != S0) {
+            const size_t n = nseq * d->Dk * d->Dv;
+            hipLaunchKernelGGL(copy_state_kernel, dim3(256), dim3(256), 0, st, S_final, S0, n);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(DR_ERR_HIP, "state copy launch: %s", hipGetErrorString(e));
+        }
+        return DR_OK;
+    }
+    dr::ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.log_alpha = log_alpha; a.beta = beta; a.S0 = S0;
+    a.o = o; a.S_final = S_final;
+    a.B = d->B; a.H = d->H; a.L = d->L; a.Dv = d->Dv;
+    a.NC = (d->L + dr::CH - 1) / dr::CH;
+    a.nseq = (int)nseq;
+    a.has_gate = d->gate != DR_GATE_NONE;
+    a.out_bf16 = d->out_dtype == DR_BF16;
+    char* ws = (char*)workspace;
+    a.wsT = (dr::half_t*)(ws + w.T);
+    a.wsP = (dr::half_t*)(ws + w.Pm);
+    a.wsG = (float*)(ws + w.G);
+    a.wsQ = w.Q ? (dr::half_t*)(ws + w.Q) : nullptr;
+    a.wsKs = w.Ks ? (dr::half_t*)(ws + w.Ks) : nullptr;
+    a.wsKl = w.Kl ? (dr::half_t*)(ws + w.Kl) : nullptr;
+    a.wsV = w.V ? (dr::half_t*)(ws + w.V) : nullptr;
+    hipError_t e = dr::launch_chunk(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL,
+                                    d->beta == DR_BETA_CHANNEL, st);
+    if (e != hipSuccess) return fail(DR_ERR_HIP, "chunk kernels launch: %s", hipGetErrorString(e));
+    return DR_OK;
+}
+
+dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta, float* S, void* o,
+                         void* stream) {
+    g_err[0] = '\0';
+    if (!d) return fail(DR_ERR_NULL, "descriptor is NULL");
+    if (d->N < 0 || d->H < 0) return fail(DR_ERR_SHAPE, "negative dimension (N=%d H=%d)", d->N, d->H);
+    dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta);
+    if (s != DR_OK) return s;
+    const size_t nst = (size_t)d->N * d->H;
+    const size_t blocks = nst * ((d->Dv + 63) / 64);
+    if (blocks > (size_t)std::numeric_limits<int>::max())
+        return fail(DR_ERR_UNSUPPORTED, "N*H=%zu too large", nst);
+    if (nst == 0) return DR_OK;
+    if (!q || !k || !v || !beta || !S || !o) return fail(DR_ERR_NULL, "q, k, v, beta, S and o are required");
+    if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
+        return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S, o};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "S", "o"};
+    for (int i = 0; i < 7; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    dr::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.log_alpha = log_alpha; a.beta = beta;
+    a.S = S; a.o = o;
+    a.N = d->N; a.H = d->H; a.Dv = d->Dv;
+    a.has_gate = d->gate != DR_GATE_NONE;
+    a.out_bf16 = d->out_dtype == DR_BF16;
+    hipError_t e = dr::launch_decode(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL,
+                                     d->beta == DR_BETA_CHANNEL, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(DR_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+    return DR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,672 @@
+// dr_chunk.hip -- chunked forward of the delta-rule recurrence on gfx950.
+//
+// Recurrence (FG2-GDN page, section 2, scaled key/value and state-update
+// equations; DeltaNet page, step list, steps 3-6):
+//   S_t = (I - kt kt^T) Diag(alpha_t) S_{t-1} + kt vt^T,  o_t = S_t^T q_t,
+//   kt = sqrt(beta) (.) k, vt = sqrt(beta) (.) v.
+//
+// Chunk algebra (the chunkwise / WY form the DeltaNet page's step 7 and the
+// FG2-GDN page's section 2 refer to, written out here for 64-token chunks).
+// Inside a chunk with start state S, rows r = 0..63, cumulative log gate
+// G_r = sum_{j<=r} log alpha_j (scalar or per key channel):
+//   A_ri = sum_c kt_rc kt_ic e^{G_rc - G_ic}   (i < r),   T = (I + A)^-1
+//   P_ri = sum_c q_rc  kt_ic e^{G_rc - G_ic}   (i <= r)
+//   U    = T (Vt - (Kt (.) e^G) S)                      (the per-chunk "new values")
+//   O    = (Q (.) e^G) S + P U
+//   S'   = Diag(e^{G_63}) S + (Kt (.) e^{G_63 - G})^T U
+// For a scalar beta the kernels use the equivalent "beta form": A carries beta
+// on its rows, T^ = T Diag(beta), Kt -> k and Vt -> v (a diagonal similarity
+// transform of the above, exact in exact arithmetic), so the raw bf16 inputs
+// are matrix-core operands without any rounding.
+//
+// Two kernels:
+//   prep  one workgroup per (chunk, head, batch): G, A and P on the matrix
+//         cores, T = (I + A)^-1 by blocked forward substitution in fp32,
+//         writes T^ and P (fp16), the gate factors, and for channel-wise
+//         gates / betas the gated fp16 operands the scan needs.
+//   scan  one workgroup per (sequence, 16-column tile of S): walks the chunks
+//         in order holding its fp32 S tile in registers; per chunk
+//         X = Ks S, R = V - g X, U = T^ R, O = g Q S + P U, S = g63 S + Kl^T U.
+//         Columns of S evolve independently (the transition acts on the key
+//         side only), so tiles of one head never exchange data.
+//
+// All matrix-core operands are fp16 (bf16 inputs convert exactly); fp32
+// inputs use two fp16 terms.  Accumulation and the state are fp32.
+
+#include <hip/hip_runtime.h>
+
+#include "dr_device.h"
+#include "dr_internal.h"
+
+namespace dr {
+
+// ===========================================================================
+// prep kernel
+// ===========================================================================
+
+// Lower-triangular 16x16 block pairs (R, I), R >= I, of a 64-token chunk.
+__constant__ int kPairR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ int kPairI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+
+// Largest |G_r - G_m| (m = block middle) for which a diagonal block's factors
+// e^{G_r - G_m}, e^{G_m - G_i} stay in fp16's normal range.
+constexpr float kDiagRange = 9.0f;
+
+// Shared-memory plan of the prep kernel (in floats).
+//   channel gate: [Kg | Ki | Qg | constants | A | P | g | beta | flags], with T
+//                 and the blocked-solve scratch X reusing Kg/Ki/Qg once A and P exist;
+//   scalar gate:  [A | P | T | X | g | beta | flags].
+template <int DK, bool CGATE>
+struct PrepSmem {
+    static constexpr int KP = DK + 4;    // fp32 row pitch of the factor arrays
+    static constexpr int NCST = 14;      // per-channel constants (channel gate)
+    static constexpr int kKg = 0;
+    static constexpr int kKi = kKg + (CGATE ? 64 * KP : 0);
+    static constexpr int kQg = kKi + (CGATE ? 64 * KP : 0);
+    static constexpr int kCst = kQg + (CGATE ? 64 * KP : 0);
+    static constexpr int kA = kCst + (CGATE ? NCST * DK : 0);
+    static constexpr int kP = kA + 64 * 65;
+    static constexpr int kT = CGATE ? kKg : kP + 64 * 65;
+    static constexpr int kX = kT + 64 * 65;
+    static constexpr int kG = CGATE ? kP + 64 * 65 : kX + 3 * 16 * 17;
+    static constexpr int kB = kG + 64;
+    static constexpr int kFlag = kB + 64;
+    static constexpr int FLOATS = kFlag + 4;
+    static_assert(!CGATE || kX + 3 * 16 * 17 <= kCst, "T and X must fit inside Kg, Ki, Qg");
+};
+
+// Per-channel constants of the channel-gate prep (G is the cumulative log
+// gate inside the chunk, blocks are 16 tokens, m = 16R + 8 a block middle):
+//   CST_C + p   e^{G_{16R} - G_{16I+15}} for off-diagonal pair p = (R, I)
+//   CST_IGM + R e^{G_{16R} - G_m}        diagonal row-factor rescale
+//   CST_IIM + R e^{G_m - G_{16R+15}}     diagonal column-factor rescale
+// Row factors are stored relative to the block start, column factors relative
+// to the block end, so every factor of an off-diagonal pair is <= 1.
+enum { CST_C = 0, CST_IGM = 6, CST_IIM = 10 };
+
+// Off-diagonal pair index of (R, I), R > I: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+__device__ __forceinline__ int offdiag_index(int R, int I) { return R * (R - 1) / 2 + I; }
+
+template <int DK, bool F32IN, bool CGATE, bool CBETA>
+__global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
+    constexpr int P = F32IN ? 2 : 1;
+    using SM = PrepSmem<DK, CGATE>;
+    __shared__ float smem[SM::FLOATS];
+    float(*sA)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kA);
+    float(*sP)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kP);
+    float(*sT)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kT);
+    float(*sX)[16][17] = reinterpret_cast<float(*)[16][17]>(smem + SM::kX);
+    float* sg = smem + SM::kG;
+    float* sb = smem + SM::kB;
+    int* sflag = reinterpret_cast<int*>(smem + SM::kFlag);
+
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int seq = b * a.H + h;
+    const size_t cs = (size_t)seq * a.NC + c;
+    const int t0 = c * CH;
+    const int Lc = min(CH, a.L - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int Dv = a.Dv;
+
+    if (tid < 4) sflag[tid] = 0;
+    __syncthreads();   // flags are set with atomicOr by other waves below
+
+    // ---------------------------------------------------------------- gates
+    if constexpr (!CGATE) {
+        if (w == 0) {
+            float g = (a.has_gate && l < Lc) ? a.log_alpha[tok0 + l] : 0.f;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                float y = __shfl_up(g, off);
+                if (l >= off) g += y;
+            }
+            sg[l] = g;
+            sb[l] = (!CBETA && l < Lc) ? a.beta[tok0 + l] : 0.f;
+            const float g63 = __shfl(g, 63);
+            a.wsG[cs * kGW + l] = expf(g);             // gamma_r = e^{G_r}
+            a.wsG[cs * kGW + 64 + l] = expf(g63 - g);  // lambda_r = e^{G_63 - G_r}
+        }
+        // channel beta with a scalar gate: the scan needs kt and vt in fp16
+        if constexpr (CBETA) {
+            for (int e = tid; e < CH * DK; e += 256) {
+                const int r = e / DK, col = e % DK;
+                float kv = 0.f, vv = 0.f;
+                if (r < Lc) {
+                    const float sbv = sqrtf(a.beta[(tok0 + r) * DK + col]);
+                    kv = sbv * load1<F32IN>(a.k, (tok0 + r) * DK + col);
+                    vv = sbv * load1<F32IN>(a.v, (tok0 + r) * Dv + col);
+                }
+                store_split<P>(a.wsKs, cs * (size_t)(P * CH * DK), (size_t)CH * DK, r * DK + col, kv);
+                store_split<P>(a.wsV, cs * (size_t)(P * CH * DK), (size_t)CH * DK, r * DK + col, vv);
+            }
+        }
+    } else {
+        float* sKg = smem + SM::kKg;
+        float* sKi = smem + SM::kKi;
+        float* sQg = smem + SM::kQg;
+        float* cst = smem + SM::kCst;
+        constexpr int KP = SM::KP;
+        // one thread per key channel walks the chunk's 64 tokens
+        if (tid < DK) {
+            const int col = tid;
+            float G[CH];
+            float run = 0.f;
+#pragma unroll
+            for (int r = 0; r < CH; ++r) {
+                run += (r < Lc) ? a.log_alpha[(tok0 + r) * DK + col] : 0.f;
+                G[r] = run;
+            }
+            // per-block factors, <= 1 for non-positive log gates:
+            //   rowf_r = e^{G_r - G_{16R}},  colf_r = e^{G_{16R+15} - G_r}
+            int badbits = 0;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                const float gs = G[16 * R];
+                const float gm = G[16 * R + 8];
+                const float ge = G[16 * R + 15];
+                const float Egs = expf(gs);          // e^{G_{16R}}, chunk-start relative
+                const float Fr = expf(G[63] - ge);   // e^{G_63 - G_{16R+15}}
+                // the diagonal block's rescaled factors reach e^{|G_r - G_m|}
+                if (!(gs - gm <= kDiagRange && gm - ge <= kDiagRange &&
+                      gs - gm >= -kDiagRange && gm - ge >= -kDiagRange))
+                    badbits |= 1 << R;
+                cst[(CST_IGM + R) * DK + col] = expf(gs - gm);
+                cst[(CST_IIM + R) * DK + col] = expf(gm - ge);
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int r = 16 * R + rr;
+                    float kv = 0.f, qv = 0.f, vv = 0.f, sbv = 1.f;
+                    if (r < Lc) {
+                        kv = load1<F32IN>(a.k, (tok0 + r) * DK + col);
+                        qv = load1<F32IN>(a.q, (tok0 + r) * DK + col);
+                        if constexpr (CBETA) {
+                            sbv = sqrtf(a.beta[(tok0 + r) * DK + col]);
+                            vv = sbv * load1<F32IN>(a.v, (tok0 + r) * Dv + col);
+                        }
+                    }
+                    const float kt = sbv * kv;
+                    const float rowf = expf(G[r] - gs);
+                    const float colf = expf(ge - G[r]);
+                    sKg[r * KP + col] = kt * rowf;
+                    sKi[r * KP + col] = kt * colf;
+                    sQg[r * KP + col] = qv * rowf;
+                    // operands for the scan: Q e^{G}, Kt e^{G}, Kt e^{G_63 - G} (and vt)
+                    const size_t pl = (size_t)CH * DK, base = cs * (size_t)(P * CH * DK);
+                    store_split<P>(a.wsQ, base, pl, r * DK + col, qv * rowf * Egs);
+                    store_split<P>(a.wsKs, base, pl, r * DK + col, kt * rowf * Egs);
+                    store_split<P>(a.wsKl, base, pl, r * DK + col, kt * colf * Fr);
+                    if constexpr (CBETA) store_split<P>(a.wsV, base, pl, r * DK + col, vv);
+                }
+            }
+#pragma unroll
+            for (int R = 1; R < 4; ++R)
+#pragma unroll
+                for (int I = 0; I < R; ++I)
+                    cst[(CST_C + offdiag_index(R, I)) * DK + col] = expf(G[16 * R] - G[16 * I + 15]);
+            a.wsG[cs * kGW + col] = expf(G[63]);   // state decay over the chunk
+            if (badbits) atomicOr(&sflag[0], badbits);
+        }
+        if constexpr (!CBETA) {
+            if (w == 3) sb[l] = (l < Lc) ? a.beta[tok0 + l] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------- A and P on the matrix cores
+    // 20 jobs: 10 lower block pairs for A, the same 10 for P; 5 per wave.
+    const int badmask = CGATE ? sflag[0] : 0;
+    for (int job = w; job < 20; job += 4) {
+        const bool isP = job >= 10;
+        const int pr = isP ? job - 10 : job;
+        const int R = kPairR[pr], I = kPairI[pr];
+        if (CGATE && R == I && (badmask >> R) & 1) continue;   // handled by the exact path below
+        const int ra = 16 * R + (l & 15);   // operand row (A side)
+        const int ca = 16 * I + (l & 15);   // operand row (B side)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const int k0 = 32 * s + 8 * (l >> 4);
+            Frag<P> fa, fb;
+            if constexpr (!CGATE) {
+                if constexpr (!CBETA) {
+                    fa = load_frag_in<F32IN, P>(isP ? a.q : a.k, (tok0 + ra) * DK + k0, ra < Lc);
+                    fb = load_frag_in<F32IN, P>(a.k, (tok0 + ca) * DK + k0, ca < Lc);
+                } else {
+                    float xa[8], xb[8];
+                    load8<F32IN>(isP ? a.q : a.k, (tok0 + ra) * DK + k0, ra < Lc, xa);
+                    load8<F32IN>(a.k, (tok0 + ca) * DK + k0, ca < Lc, xb);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        if (!isP && ra < Lc) xa[j] *= sqrtf(a.beta[(tok0 + ra) * DK + k0 + j]);
+                        if (ca < Lc) xb[j] *= sqrtf(a.beta[(tok0 + ca) * DK + k0 + j]);
+                    }
+                    fa = split8<P>(xa);
+                    fb = split8<P>(xb);
+                }
+            } else {
+                constexpr int KP = SM::KP;
+                const float* sKg = smem + SM::kKg;
+                const float* sKi = smem + SM::kKi;
+                const float* sQg = smem + SM::kQg;
+                const float* cst = smem + SM::kCst;
+                float xa[8], xb[8];
+                const float* rowsrc = isP ? sQg : sKg;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int col = k0 + j;
+                    // rescale both factors to a reference point between the
+                    // two blocks (off-diagonal: end of block I; diagonal: middle)
+                    const float fr = (R == I) ? cst[(CST_IGM + R) * DK + col]
+                                              : cst[(CST_C + offdiag_index(R, I)) * DK + col];
+                    const float fc = (R == I) ? cst[(CST_IIM + R) * DK + col] : 1.f;
+                    xa[j] = rowsrc[ra * KP + col] * fr;
+                    xb[j] = sKi[ca * KP + col] * fc;
+                }
+                fa = split8<P>(xa);
+                fb = split8<P>(xb);
+            }
+            acc = mma<P, P>(fa, fb, acc);
+        }
+        // gate factors and masks; write the block to LDS
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * R + 4 * (l >> 4) + j;
+            const int i = 16 * I + (l & 15);
+            float val = acc[j];
+            if constexpr (!CGATE) val *= (i <= r) ? expf(sg[r] - sg[i]) : 0.f;
+            if (isP) {
+                sP[r][i] = (i <= r) ? val : 0.f;
+            } else {
+                if constexpr (!CBETA) val *= sb[r];
+                sA[r][i] = (i < r) ? val : 0.f;
+            }
+        }
+    }
+    if constexpr (CGATE) {
+        if (badmask) {
+            __syncthreads();
+            // exact path for diagonal blocks whose in-block decay exceeds the
+            // fp16 factor range: sum_c kt_rc kt_ic e^{G_rc - G_ic}, the exponent
+            // taken as the sum of log alpha over tokens i+1..r
+            for (int R = 0; R < 4; ++R) {
+                if (!((badmask >> R) & 1)) continue;
+                const int r = 16 * R + (tid >> 4), i = 16 * R + (tid & 15);
+                float accA = 0.f, accP = 0.f;
+                if (i <= r && r < Lc) {
+                    for (int col = 0; col < DK; ++col) {
+                        float e = 0.f;
+                        for (int t = i + 1; t <= r; ++t) e += a.log_alpha[(tok0 + t) * DK + col];
+                        const float dec = expf(e);
+                        float kr = load1<F32IN>(a.k, (tok0 + r) * DK + col);
+                        float ki = load1<F32IN>(a.k, (tok0 + i) * DK + col);
+                        if constexpr (CBETA) {
+                            kr *= sqrtf(a.beta[(tok0 + r) * DK + col]);
+                            ki *= sqrtf(a.beta[(tok0 + i) * DK + col]);
+                        }
+                        const float qr = load1<F32IN>(a.q, (tok0 + r) * DK + col);
+                        accA += kr * ki * dec;
+                        accP += qr * ki * dec;
+                    }
+                }
+                if constexpr (!CBETA) accA *= sb[r];
+                sA[r][i] = (i < r) ? accA : 0.f;
+                sP[r][i] = (i <= r) ? accP : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------- T = (I + A)^-1, blocked, fp32
+    // diagonal 16x16 blocks: wave w inverts block w, lane j < 16 owns column j
+    if (l < 16) {
+        const int base = 16 * w, j = l;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) s += sA[base + r][base + i] * t[i];
+            t[r] = (r == j) ? 1.f : (r < j ? 0.f : -s);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[base + r][base + j] = t[r];
+    }
+    __syncthreads();
+    // off-diagonal blocks, one block row at a time:
+    //   X_RI = sum_{J=I}^{R-1} A_RJ T_JI,   T_RI = -T_RR X_RI
+    for (int R = 1; R < 4; ++R) {
+        for (int e = tid; e < R * 256; e += 256) {
+            const int I = e >> 8, r = (e >> 4) & 15, i = e & 15;
+            float s = 0.f;
+            for (int m = 16 * I; m < 16 * R; ++m) s += sA[16 * R + r][m] * sT[m][16 * I + i];
+            sX[I][r][i] = s;
+        }
+        __syncthreads();
+        for (int e = tid; e < R * 256; e += 256) {
+            const int I = e >> 8, r = (e >> 4) & 15, i = e & 15;
+            float s = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) s += sT[16 * R + r][16 * R + m] * sX[I][m][i];
+            sT[16 * R + r][16 * I + i] = -s;
+        }
+        __syncthreads();
+    }
+
+    // --------------------------------------------------- outputs T^ and P
+    {
+        const int r = tid >> 2, i0 = 16 * (tid & 3);
+        float tv[16], pv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = i0 + j;
+            float tt = (i <= r) ? sT[r][i] : 0.f;
+            if constexpr (!CBETA) tt *= sb[i];
+            tv[j] = tt;
+            pv[j] = (i <= r) ? sP[r][i] : 0.f;
+        }
+        const size_t base = cs * (size_t)(P * CH * CH);
+        store_row16<P>(a.wsT + base, (size_t)CH * CH, r * CH + i0, tv);
+        store_row16<P>(a.wsP + base, (size_t)CH * CH, r * CH + i0, pv);
+    }
+}
+
+// ===========================================================================
+// scan kernel
+// ===========================================================================
+
+template <int DK, int P>
+struct ScanSmem {
+    static constexpr int SP = DK + 8;   // half pitch of S^T rows
+    static constexpr int RP = CH + 8;   // half pitch of token-major rows
+    static constexpr int kS = 0;                       // [P][16][SP]  S^T (B operand of K S)
+    static constexpr int kR = kS + P * 16 * SP;        // [P][16][RP]  R^T
+    static constexpr int kV = kR + P * 16 * RP;        // [P][16][RP]  U^T
+    static constexpr int kVl = kV + P * 16 * RP;       // [P][16][RP]  (lambda U)^T
+    static constexpr int kKT = kVl + P * 16 * RP;      // [P][DK][RP]  Kl^T
+    static constexpr int HALFS = kKT + P * DK * RP;
+};
+
+// Per-chunk operands a wave prefetches into registers.
+template <int DK, int P>
+struct ScanRegs {
+    Frag<P> ks[DK / 32];     // rows 16w.. of Ks, A operand of K S
+    Frag<P> qs[DK / 32];     // rows 16w.. of Qs
+    Frag<P> th[2];           // rows 16w.. of T^
+    Frag<P> pm[2];           // rows 16w.. of P
+    float v[4];              // V tile in accumulator layout
+    float gam[4], lam[4];    // scalar-gate row factors (rows of this lane)
+    float g63[DK / 64 * 4];  // state decay for this lane's S rows
+    float kt[DK / 4];        // this thread's slice of Kl (token tid & 63, 32 or 16 channels)
+};
+
+template <int DK, bool F32IN, bool CGATE, bool CBETA>
+__device__ __forceinline__ void scan_load(const ChunkArgs& a, ScanRegs<DK, F32IN ? 2 : 1>& g,
+                                          int seq, int c, int n0, int w, int l, int tid) {
+    constexpr int P = F32IN ? 2 : 1;
+    const int t0 = c * CH;
+    const int Lc = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const size_t cs = (size_t)seq * a.NC + c;
+    const int ra = 16 * w + (l & 15);
+    const size_t opl = (size_t)CH * DK;              // plane stride of [64][DK] operands
+    const size_t obase = cs * (size_t)(P * CH * DK);
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+        const int k0 = 32 * s + 8 * (l >> 4);
+        if constexpr (CGATE) {
+            g.ks[s] = load_frag_h<P>(a.wsKs, obase + ra * DK + k0, opl);
+            g.qs[s] = load_frag_h<P>(a.wsQ, obase + ra * DK + k0, opl);
+        } else {
+            if constexpr (CBETA) g.ks[s] = load_frag_h<P>(a.wsKs, obase + ra * DK + k0, opl);
+            else g.ks[s] = load_frag_in<F32IN, P>(a.k, (tok0 + ra) * DK + k0, ra < Lc);
+            g.qs[s] = load_frag_in<F32IN, P>(a.q, (tok0 + ra) * DK + k0, ra < Lc);
+        }
+    }
+    const size_t tbase = cs * (size_t)(P * CH * CH);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int k0 = 32 * s + 8 * (l >> 4);
+        g.th[s] = load_frag_h<P>(a.wsT, tbase + ra * CH + k0, (size_t)CH * CH);
+        g.pm[s] = load_frag_h<P>(a.wsP, tbase + ra * CH + k0, (size_t)CH * CH);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * w + 4 * (l >> 4) + j;
+        const int col = n0 + (l & 15);
+        if constexpr (CBETA) {
+            float vv = 0.f;
+            const half_t* vb = a.wsV + obase + r * DK + col;
+            vv = (float)vb[0];
+            if constexpr (P == 2) vv += (float)vb[opl];
+            g.v[j] = vv;
+        } else {
+            g.v[j] = (r < Lc) ? load1<F32IN>(a.v, (tok0 + r) * a.Dv + col) : 0.f;
+        }
+        if constexpr (!CGATE) {
+            g.gam[j] = a.wsG[cs * kGW + r];
+            g.lam[j] = a.wsG[cs * kGW + 64 + r];
+        }
+    }
+    if constexpr (!CGATE) {
+        const float d = a.wsG[cs * kGW + 63];
+#pragma unroll
+        for (int j = 0; j < DK / 64 * 4; ++j) g.g63[j] = d;
+    } else {
+#pragma unroll
+        for (int t = 0; t < DK / 64; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                g.g63[t * 4 + j] = a.wsG[cs * kGW + 16 * (w * (DK / 64) + t) + 4 * (l >> 4) + j];
+    }
+    // Kl slice for the transposed LDS copy: token tid & 63, channels
+    // [(tid >> 6) * DK/4, +DK/4)
+    {
+        const int r = tid & 63, c0 = (tid >> 6) * (DK / 4);
+#pragma unroll
+        for (int j0 = 0; j0 < DK / 4; j0 += 8) {
+            float x[8];
+            if constexpr (CGATE || CBETA) {
+                const half_t* src = (CGATE ? a.wsKl : a.wsKs) + obase + r * DK + c0 + j0;
+                half8 hi = *reinterpret_cast<const half8*>(src);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = (float)hi[j];
+                if constexpr (P == 2) {
+                    half8 lo = *reinterpret_cast<const half8*>(src + opl);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) x[j] += (float)lo[j];
+                }
+            } else {
+                load8<F32IN>(a.k, (tok0 + r) * DK + c0 + j0, r < Lc, x);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) g.kt[j0 + j] = x[j];
+        }
+    }
+}
+
+template <int DK, bool F32IN, bool CGATE, bool CBETA>
+__global__ __launch_bounds__(256) void scan_kernel(ChunkArgs a) {
+    constexpr int P = F32IN ? 2 : 1;
+    constexpr int NTS = DK / 64;    // S row tiles (16 rows) per wave
+    using SM = ScanSmem<DK, P>;
+    __shared__ half_t smem[SM::HALFS];
+    half_t* sS = smem + SM::kS;
+    half_t* sR = smem + SM::kR;
+    half_t* sV = smem + SM::kV;
+    half_t* sVl = smem + SM::kVl;
+    half_t* sKT = smem + SM::kKT;
+    constexpr int SPL = 16 * SM::SP;   // plane strides
+    constexpr int RPL = 16 * SM::RP;
+    constexpr int KPL = DK * SM::RP;
+
+    // XCD-aware mapping: consecutive workgroup ids go round-robin over the 8
+    // XCDs, so put all column tiles of one sequence on the same XCD (they read
+    // the same chunk operands) by striding sequences with the XCD index.
+    const int NT = a.Dv / 16;
+    const int bid = blockIdx.x;
+    const int grp = bid / (8 * NT);
+    const int seq = grp * 8 + (bid & 7);
+    const int tile = (bid >> 3) % NT;
+    if (seq >= a.nseq) return;
+    const int n0 = tile * 16;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int col = n0 + (l & 15);
+
+    // fp32 state tile in registers: rows 16*(w*NTS + t) + 4*(l>>4) + j, column col
+    f32x4 S[NTS];
+#pragma unroll
+    for (int t = 0; t < NTS; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * (w * NTS + t) + 4 * (l >> 4) + j;
+            S[t][j] = a.S0 ? a.S0[((size_t)seq * DK + row) * a.Dv + col] : 0.f;
+        }
+        st4_lds<P>(sS + (l & 15) * SM::SP + 16 * (w * NTS + t) + 4 * (l >> 4), SPL, S[t]);
+    }
+
+    ScanRegs<DK, P> cur;
+    if (a.NC > 0) scan_load<DK, F32IN, CGATE, CBETA>(a, cur, seq, 0, n0, w, l, tid);
+    __syncthreads();
+
+    for (int c = 0; c < a.NC; ++c) {
+        ScanRegs<DK, P> nxt;
+        if (c + 1 < a.NC) scan_load<DK, F32IN, CGATE, CBETA>(a, nxt, seq, c + 1, n0, w, l, tid);
+        const int t0 = c * CH;
+        const int Lc = min(CH, a.L - t0);
+
+        // Kl^T into LDS (read by the state update after the next barriers)
+        {
+            const int r = tid & 63, c0 = (tid >> 6) * (DK / 4);
+#pragma unroll
+            for (int j = 0; j < DK / 4; ++j) {
+                const float x = cur.kt[j];
+                const half_t hi = (half_t)x;
+                sKT[(c0 + j) * SM::RP + r] = hi;
+                if constexpr (P == 2) sKT[KPL + (c0 + j) * SM::RP + r] = (half_t)(x - (float)hi);
+            }
+        }
+
+        // step 1: X = Ks S, Y = Qs S for rows 16w..16w+15
+        f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const int k0 = 32 * s + 8 * (l >> 4);
+            Frag<P> sf = load_frag_h<P>(sS, (l & 15) * SM::SP + k0, SPL);
+            X = mma<P, P>(cur.ks[s], sf, X);
+            Y = mma<P, P>(cur.qs[s], sf, Y);
+        }
+        // step 2: R = V - gamma X
+        f32x4 Rv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Rv[j] = cur.v[j] - (CGATE ? 1.f : cur.gam[j]) * X[j];
+        st4_lds<P>(sR + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, Rv);
+        __syncthreads();
+
+        // step 3: U = T^ R
+        f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int k0 = 32 * s + 8 * (l >> 4);
+            U = mma<P, P>(cur.th[s], load_frag_h<P>(sR, (l & 15) * SM::RP + k0, RPL), U);
+        }
+        st4_lds<P>(sV + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, U);
+        if constexpr (!CGATE) {
+            f32x4 Ul;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Ul[j] = cur.lam[j] * U[j];
+            st4_lds<P>(sVl + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, Ul);
+        }
+        __syncthreads();
+
+        // step 4: O = gamma Y + P U
+        f32x4 O;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) O[j] = (CGATE ? 1.f : cur.gam[j]) * Y[j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int k0 = 32 * s + 8 * (l >> 4);
+            O = mma<P, P>(cur.pm[s], load_frag_h<P>(sV, (l & 15) * SM::RP + k0, RPL), O);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * w + 4 * (l >> 4) + j;
+            if (r < Lc) {
+                const size_t oi = ((size_t)seq * a.L + t0 + r) * a.Dv + col;
+                if (a.out_bf16) static_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(O[j]);
+                else static_cast<float*>(a.o)[oi] = O[j];
+            }
+        }
+
+        // step 5: S = g63 S + Kl^T (lambda U)
+        const half_t* sU = CGATE ? sV : sVl;
+#pragma unroll
+        for (int t = 0; t < NTS; ++t) {
+            const int rt = 16 * (w * NTS + t);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int k0 = 32 * s + 8 * (l >> 4);
+                Frag<P> ka = load_frag_h<P>(sKT, (rt + (l & 15)) * SM::RP + k0, KPL);
+                acc = mma<P, P>(ka, load_frag_h<P>(sU, (l & 15) * SM::RP + k0, RPL), acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S[t][j] = cur.g63[t * 4 + j] * S[t][j] + acc[j];
+            st4_lds<P>(sS + (l & 15) * SM::SP + rt + 4 * (l >> 4), SPL, S[t]);
+        }
+        __syncthreads();
+        if (c + 1 < a.NC) cur = nxt;
+    }
+
+    if (a.S_final) {
+#pragma unroll
+        for (int t = 0; t < NTS; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * (w * NTS + t) + 4 * (l >> 4) + j;
+                a.S_final[((size_t)seq * DK + row) * a.Dv + col] = S[t][j];
+            }
+    }
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+
+template <int DK, bool F32IN, bool CGATE, bool CBETA>
+static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
+    const int nseq = a.nseq;
+    if (a.NC > 0 && nseq > 0) {
+        dim3 g1(a.NC, a.H, a.B);
+        hipLaunchKernelGGL((prep_kernel<DK, F32IN, CGATE, CBETA>), g1, dim3(256), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (nseq > 0) {
+        const int NT = a.Dv / 16;
+        const int groups = (nseq + 7) / 8;
+        hipLaunchKernelGGL((scan_kernel<DK, F32IN, CGATE, CBETA>), dim3(groups * 8 * NT), dim3(256),
+                           0, st, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <int DK, bool F32IN>
+static hipError_t launch_chunk_d(const ChunkArgs& a, bool cgate, bool cbeta, hipStream_t st) {
+    if (cgate) return cbeta ? launch_chunk_t<DK, F32IN, true, true>(a, st)
+                            : launch_chunk_t<DK, F32IN, true, false>(a, st);
+    return cbeta ? launch_chunk_t<DK, F32IN, false, true>(a, st)
+                 : launch_chunk_t<DK, F32IN, false, false>(a, st);
+}
+
+hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
+                        hipStream_t st) {
+    if (Dk == 64) return f32in ? launch_chunk_d<64, true>(a, cgate, cbeta, st)
+                               : launch_chunk_d<64, false>(a, cgate, cbeta, st);
+    return f32in ? launch_chunk_d<128, true>(a, cgate, cbeta, st)
+                 : launch_chunk_d<128, false>(a, cgate, cbeta, st);
+}
+
+}  // namespace dr

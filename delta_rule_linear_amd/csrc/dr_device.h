@@ -1,0 +1,166 @@
+// dr_device.h -- gfx950 device helpers shared by the delta-rule kernels:
+// vector types, the 16x16x32 fp16 matrix-core op, operand fragments in one or
+// two fp16 terms, and bf16/fp32 conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dr {
+
+typedef _Float16 half_t;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int CH = 64;     // tokens per chunk
+constexpr int WAVE = 64;   // wavefront width
+
+// ---------------------------------------------------------------------------
+// Matrix core: D(16x16, fp32) += A(16x32, fp16) * B(32x16, fp16).
+// Lane l holds A row (l & 15) and B column (l & 15), eight k-values each at
+// k = 8 * (l >> 4) + [0, 8); it holds D rows 4 * (l >> 4) + [0, 4) of column
+// (l & 15).  (A and B use the same lane-to-k map, so the k order inside the
+// instruction never matters.)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16(const half8& a, const half8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// An operand fragment carried as P fp16 terms: P == 1 is a plain fp16 value,
+// P == 2 is hi + lo with hi = fp16(x), lo = fp16(x - hi) (about 22 significant
+// bits).  Products drop lo * lo.
+template <int P>
+struct Frag {
+    half8 t[P];
+};
+
+template <int PA, int PB>
+__device__ __forceinline__ f32x4 mma(const Frag<PA>& a, const Frag<PB>& b, f32x4 c) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i)
+#pragma unroll
+        for (int j = 0; j < PB; ++j)
+            if (i + j < 2) c = mfma16(a.t[i], b.t[j], c);
+    return c;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Split eight fp32 values into P fp16 terms.
+template <int P>
+__device__ __forceinline__ Frag<P> split8(const float* x) {
+    Frag<P> f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        half_t hi = (half_t)x[j];
+        f.t[0][j] = hi;
+        if constexpr (P == 2) f.t[1][j] = (half_t)(x[j] - (float)hi);
+    }
+    return f;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& r, float* x) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[2 * j] = __uint_as_float(w[j] << 16);
+        x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+}
+
+// Eight consecutive input values (bf16 or fp32) at element offset `off`,
+// converted to fp32; `ok == false` gives zeros without touching memory.
+template <bool F32IN>
+__device__ __forceinline__ void load8(const void* base, size_t off, bool ok, float* x) {
+    if (!ok) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = 0.f;
+        return;
+    }
+    if constexpr (F32IN) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+        float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+        unpack_bf16x8(r, x);
+    }
+}
+
+// Load an fp16 operand fragment stored as P planes (plane stride in halfs).
+template <int P>
+__device__ __forceinline__ Frag<P> load_frag_h(const half_t* base, size_t off, size_t plane) {
+    Frag<P> f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) f.t[p] = *reinterpret_cast<const half8*>(base + off + p * plane);
+    return f;
+}
+
+// Raw-input fragment: eight values of an input row, in P fp16 terms.
+template <bool F32IN, int P>
+__device__ __forceinline__ Frag<P> load_frag_in(const void* base, size_t off, bool ok) {
+    float x[8];
+    load8<F32IN>(base, off, ok, x);
+    return split8<P>(x);
+}
+
+// Write four fp32 values as P fp16 terms at consecutive LDS halfs.
+template <int P>
+__device__ __forceinline__ void st4_lds(half_t* dst, size_t plane, const f32x4& v) {
+    half4 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        hi[j] = (half_t)v[j];
+        if constexpr (P == 2) lo[j] = (half_t)(v[j] - (float)hi[j]);
+    }
+    *reinterpret_cast<half4*>(dst) = hi;
+    if constexpr (P == 2) *reinterpret_cast<half4*>(dst + plane) = lo;
+}
+
+// One input value (bf16 or fp32) as fp32.
+template <bool F32IN>
+__device__ __forceinline__ float load1(const void* base, size_t off) {
+    if constexpr (F32IN) return static_cast<const float*>(base)[off];
+    else return bf16_to_f32(static_cast<const uint16_t*>(base)[off]);
+}
+
+// Store one fp32 value as P fp16 terms: base[off + idx] (hi) and
+// base[off + plane + idx] (lo).
+template <int P>
+__device__ __forceinline__ void store_split(half_t* base, size_t off, size_t plane, size_t idx,
+                                            float x) {
+    const half_t hi = (half_t)x;
+    base[off + idx] = hi;
+    if constexpr (P == 2) base[off + plane + idx] = (half_t)(x - (float)hi);
+}
+
+// Store sixteen fp32 values as P fp16 terms at base[idx .. idx + 16) of each
+// plane (16-byte aligned).
+template <int P>
+__device__ __forceinline__ void store_row16(half_t* base, size_t plane, size_t idx, const float* x) {
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8) {
+        half8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            hi[j] = (half_t)x[8 * h8 + j];
+            if constexpr (P == 2) lo[j] = (half_t)(x[8 * h8 + j] - (float)hi[j]);
+        }
+        *reinterpret_cast<half8*>(base + idx + 8 * h8) = hi;
+        if constexpr (P == 2) *reinterpret_cast<half8*>(base + plane + idx + 8 * h8) = lo;
+    }
+}
+
+}  // namespace dr

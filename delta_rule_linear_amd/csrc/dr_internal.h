@@ -1,0 +1,63 @@
+// dr_internal.h -- argument blocks and launchers shared by the host ABI and
+// the kernel translation units (not part of the public interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "dr_device.h"
+
+namespace dr {
+
+// floats of per-chunk gate data in the workspace (scalar gate: gamma[64] and
+// lambda[64]; channel gate: the chunk's state decay e^{G_63}[Dk])
+constexpr int kGW = 128;
+
+// Everything the chunked-forward kernels read.  Workspace planes, per chunk
+// slot cs = (b * H + h) * NC + c, with P = 1 (bf16 inputs) or 2 (fp32 inputs)
+// fp16 terms per value:
+//   wsT, wsP  [NCH][P][64][64]   T^ = (I + A)^-1 (beta-scaled columns) and P
+//   wsG       [NCH][kGW]         gate factors
+//   wsQ/Ks/Kl [NCH][P][64][Dk]   gated operands (channel gate; Ks also holds
+//                                sqrt(beta) k for a channel beta)
+//   wsV       [NCH][P][64][Dk]   sqrt(beta) v (channel beta)
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const float* S0;
+    void* o;
+    float* S_final;
+    int B, H, L, Dv, NC, nseq;
+    int has_gate;
+    int out_bf16;
+    half_t* wsT;
+    half_t* wsP;
+    float* wsG;
+    half_t* wsQ;
+    half_t* wsKs;
+    half_t* wsKl;
+    half_t* wsV;
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    float* S;
+    void* o;
+    int N, H, Dv;
+    int has_gate;
+    int out_bf16;
+};
+
+hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
+                        hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
+                         hipStream_t st);
+
+}  // namespace dr

@@ -1,0 +1,157 @@
+/*
+ * deltarule.h -- C ABI of the MI355X (gfx950) delta-rule linear-attention forward.
+ *
+ * The operation (FG2-GDN page, section 2 "Kerninnovation", the scaled
+ * key/value equation and the state-update equation; DeltaNet page, the
+ * seven-step list, steps 3-6):
+ *
+ *     kt_t = sqrt(beta_t) (.) k_t,      vt_t = sqrt(beta_t) (.) v_t
+ *     S_t  = (I - kt_t kt_t^T) Diag(alpha_t) S_{t-1} + kt_t vt_t^T
+ *     o_t  = S_t^T q_t                   (the output reads the updated state)
+ *
+ * per (batch b, head h), S a d_k x d_v matrix.  Variants, chosen by mode enums:
+ *   plain DeltaNet  alpha == 1, scalar beta          (DeltaNet page, step list)
+ *   Gated DeltaNet  scalar alpha_t                   (FG2-GDN page, section 1)
+ *   KDA             alpha_t a d_k-vector             (FG2-GDN page, section 1)
+ *   FG2-GDN         beta_t a d_k-vector, as sqrt on both k and v (section 2)
+ * No query scaling is applied; callers pre-scale q if they want one.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *   library never allocates, frees or retains memory, and keeps no state
+ *   between calls apart from the per-thread error text.  Every tensor pointer
+ *   must be 16-byte aligned.  Tensors are dense, row-major (C order).
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Work is enqueued asynchronously; inputs, outputs and workspace
+ *   must stay untouched until the stream reaches the enqueued work's end.
+ * Errors.  Arguments are validated on the host before any device work, so on
+ *   any error status nothing has been enqueued and nothing written.  A HIP
+ *   launch failure returns DR_ERR_HIP; faults inside kernels surface at the
+ *   caller's next synchronisation.  dr_last_error() returns the detail text of
+ *   the calling thread's most recent failure.
+ * Numerics.  The state and every accumulation are fp32.  Matrix-core operands
+ *   are fp16 (bf16 inputs convert to fp16 exactly for |x| in [2^-14, 65504];
+ *   below 2^-14 the absolute error is under 2^-25), and fp32 inputs use a
+ *   two-term fp16 split (about 22 significant bits).  NaN/Inf inputs propagate
+ *   and are not checked.  For a channel-wise gate, each chunk's cumulative
+ *   log-gate must stay above -80 per channel (i.e. alpha products over 64
+ *   tokens above e^-80); stronger decay underflows fp32 in the chunk algebra.
+ */
+#ifndef DELTARULE_H
+#define DELTARULE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DR_ABI_VERSION 1
+
+typedef enum {
+    DR_OK = 0,
+    DR_ERR_NULL = 1,        /* a required pointer is NULL (or a forbidden one is not) */
+    DR_ERR_SHAPE = 2,       /* a dimension is negative */
+    DR_ERR_UNSUPPORTED = 3, /* d_k / d_v / mode / dtype combination not provided */
+    DR_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+    DR_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+    DR_ERR_HIP = 6          /* a HIP runtime call or kernel launch failed */
+} dr_status;
+
+typedef enum { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+
+/* alpha_t: none (alpha == 1), one scalar per token, or one per key channel. */
+typedef enum { DR_GATE_NONE = 0, DR_GATE_SCALAR = 1, DR_GATE_CHANNEL = 2 } dr_gate_mode;
+
+/* beta_t: one scalar per token, or one per key channel (needs d_v == d_k). */
+typedef enum { DR_BETA_SCALAR = 0, DR_BETA_CHANNEL = 1 } dr_beta_mode;
+
+/* Shapes and modes of a chunked forward.
+ *   B, H >= 0 sequences x heads; L >= 0 tokens; Dk in {64, 128};
+ *   Dv a multiple of 16 in [16, 256] (Dv == Dk when beta == DR_BETA_CHANNEL).
+ *   in_dtype types q, k, v; out_dtype types o. */
+typedef struct {
+    int B, H, L, Dk, Dv;
+    dr_dtype in_dtype;
+    dr_dtype out_dtype;
+    dr_gate_mode gate;
+    dr_beta_mode beta;
+} dr_chunk_desc;
+
+/* Shapes and modes of one recurrent decode step on N x H independent states
+ * (same limits as dr_chunk_desc for Dk, Dv and the modes). */
+typedef struct {
+    int N, H, Dk, Dv;
+    dr_dtype in_dtype;
+    dr_dtype out_dtype;
+    dr_gate_mode gate;
+    dr_beta_mode beta;
+} dr_decode_desc;
+
+/* Bytes of device workspace dr_chunk_fwd needs for `d` (0 if d is invalid or
+ * there is no work).  Depends only on the shape and the modes. */
+size_t dr_chunk_fwd_workspace_bytes(const dr_chunk_desc* d);
+
+/*
+ * dr_chunk_fwd -- chunked prefill over whole sequences.
+ *
+ * Computes, for every (b, h), o_t for t = 0..L-1 and the final state S_L of
+ * the recurrence above, started from S0.  The method (DeltaNet page, step 7,
+ * and the FG2-GDN page, section 2, on the WY form) is chunkwise: 64-token
+ * chunks, a per-chunk triangular solve, and a sequential pass that carries
+ * the fp32 state between chunks.  Any L >= 0 is accepted; a partial last chunk
+ * is masked.
+ *
+ *   q          [B][H][L][Dk]  in_dtype
+ *   k          [B][H][L][Dk]  in_dtype
+ *   v          [B][H][L][Dv]  in_dtype
+ *   log_alpha  [B][H][L] (GATE_SCALAR) or [B][H][L][Dk] (GATE_CHANNEL) fp32,
+ *              natural log of alpha_t; must be NULL iff gate == DR_GATE_NONE
+ *   beta       [B][H][L] (BETA_SCALAR) or [B][H][L][Dk] (BETA_CHANNEL) fp32,
+ *              expected in [0, 1] (not checked)
+ *   S0         [B][H][Dk][Dv] fp32 initial states, or NULL for zeros
+ *   o          [B][H][L][Dv]  out_dtype, written
+ *   S_final    [B][H][Dk][Dv] fp32, written, or NULL to skip; may alias S0
+ *              exactly (in-place state carry) but no other argument
+ *   workspace  device scratch of at least dr_chunk_fwd_workspace_bytes(d)
+ *              bytes (may be NULL when that is 0); its contents on entry are
+ *              ignored and on exit are unspecified
+ * o must not overlap any input.  Returns DR_OK or an error status (see above).
+ */
+dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* S0, void* o,
+                       float* S_final, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dr_decode_step -- one recurrent step (DeltaNet page, property list: inference
+ * uses the recurrent form with a constant-size state) for N x H independent
+ * states, one new token each, updating the states in place:
+ *
+ *   S[n][h] <- (I - kt kt^T) Diag(alpha) S[n][h] + kt vt^T,  o[n][h] = S[n][h]^T q
+ *
+ *   q, k       [N][H][Dk] in_dtype;  v [N][H][Dv] in_dtype
+ *   log_alpha  [N][H] or [N][H][Dk] fp32, NULL iff gate == DR_GATE_NONE
+ *   beta       [N][H] or [N][H][Dk] fp32
+ *   S          [N][H][Dk][Dv] fp32, read and overwritten
+ *   o          [N][H][Dv] out_dtype, written; must not overlap S or the inputs
+ * Equivalent to dr_chunk_fwd with L == 1, S0 == S_final == S.
+ */
+dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta, float* S, void* o,
+                         void* stream);
+
+/* Static text for a status code. */
+const char* dr_status_str(dr_status s);
+
+/* Detail text of the calling thread's last failing call ("" if none). */
+const char* dr_last_error(void);
+
+/* DR_ABI_VERSION of the built library. */
+int dr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTARULE_H */

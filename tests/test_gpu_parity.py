@@ -1,0 +1,271 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+
+Every call goes through the C ABI (ctypes binding) into libdeltarule.so.
+Bounds (max|x - y| / max|y|, per output tensor): 1e-4 for fp32 inputs,
+3e-3 for bf16 inputs with an fp32 state.
+"""
+import numpy as np
+import pytest
+
+from delta_rule_linear_amd import inputs
+from gpu_common import TOL, announce, rel_err, run_hip, run_oracle, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import delta_rule_linear_amd as drl
+    drl.lib()
+
+
+def _check(p, out_dtype=None, tol=None):
+    announce(p.name, p.B, p.H, p.L, p.Dk, p.Dv, p.in_dtype, p.gate, p.beta_mode)
+    o, S = run_hip(p, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    oy, Sy = run_oracle(p)
+    tol = TOL[p.in_dtype] if tol is None else tol
+    eo, es = rel_err(to_np(o), oy), rel_err(to_np(S), Sy)
+    assert eo <= tol and es <= tol, f"{p.name}: o err {eo:.2e}, S err {es:.2e} (tol {tol:.0e})"
+    return eo, es
+
+
+MODES = [("none", "scalar"), ("scalar", "scalar"), ("scalar", "channel"), ("channel", "scalar"),
+         ("channel", "channel")]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,beta_mode", MODES)
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_small_sweep(dtype, gate, beta_mode, L, D):
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    p = inputs.make_chunk_problem(1, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
+                                  log_alpha_range=rng, s0_var=0.01, seed=L + D,
+                                  name=f"sweep-{dtype}-{gate}-{beta_mode}-L{L}-D{D}")
+    _check(p)
+
+
+@pytest.mark.parametrize("Dv", [16, 48, 256])
+def test_value_width(Dv):
+    p = inputs.make_chunk_problem(2, 3, 130, 128, Dv, gate="scalar", s0_var=0.01, seed=3,
+                                  name=f"dv{Dv}")
+    _check(p)
+
+
+def test_bf16_output():
+    p = inputs.make_chunk_problem(1, 4, 300, 128, 128, gate="scalar", s0_var=0.01, seed=4,
+                                  name="bf16-out")
+    # rounding o to bf16 adds up to 2^-9 relative to each element
+    _check(p, out_dtype=torch.bfloat16, tol=TOL["bf16"] + 2 ** -9)
+
+
+def test_many_heads_grid_mapping():
+    # nseq not a multiple of 8 exercises the sequence-to-XCD remapping tail
+    p = inputs.make_chunk_problem(3, 5, 100, 64, 64, gate="scalar", s0_var=0.01, seed=5,
+                                  name="b3h5")
+    _check(p)
+
+
+def test_strong_channel_gate_exact_path():
+    # per-token log alpha down to -3: in-block decay exceeds the fp16 factor
+    # range, so diagonal blocks take the exact path
+    p = inputs.make_chunk_problem(1, 2, 128, 128, 128, gate="channel", beta_mode="scalar",
+                                  log_alpha_range=(-3.0, -0.5), seed=6, name="strong-gate")
+    _check(p)
+
+
+def test_very_strong_scalar_gate():
+    p = inputs.make_chunk_problem(1, 2, 128, 64, 64, gate="scalar", log_alpha_range=(-20.0, -5.0),
+                                  s0_var=0.01, seed=7, name="very-strong-scalar")
+    _check(p)
+
+
+# ---------------------------------------------------------------- full sizes
+
+FULL = {
+    # name: heads the oracle recomputes (b, h)
+    "deltanet_f32": None,                       # small enough for every head
+    "gdn_b4h16_4k": [(0, 0), (3, 15), (1, 7)],
+    "kda_b2h32_16k": [(0, 0), (1, 31)],
+    "fg2_b2h16_16k": [(0, 0), (1, 15)],
+    "gdn_b2h16_16k": [(0, 0), (1, 15)],
+    "gdn_b1h16_64k": [(0, 0), (0, 15)],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_workload_sampled_heads(name):
+    p = inputs.workload(name)
+    announce("full", name, p.B, p.H, p.L, p.Dk, p.gate, p.beta_mode)
+    o, S = run_hip(p)
+    torch.cuda.synchronize()
+    heads = FULL[name] or [(b, h) for b in range(p.B) for h in range(p.H)]
+    tol = TOL[p.in_dtype]
+    # every output finite
+    assert torch.isfinite(o).all().item() and torch.isfinite(S).all().item()
+    for b, h in heads:
+        oy, Sy = run_oracle(p.head(b, h))
+        eo = rel_err(to_np(o[b, h]), oy[0, 0])
+        es = rel_err(to_np(S[b, h]), Sy[0, 0])
+        print(f"{name} head ({b},{h}): o {eo:.2e}  S {es:.2e}")
+        assert eo <= tol and es <= tol, f"{name} ({b},{h}): o {eo:.2e} S {es:.2e}"
+
+
+# ---------------------------------------------------------------- decode
+
+def _decode_case(N, H, D, gate, beta_mode, steps, dtype="bf16", seed=0):
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    return inputs.make_decode_problem(N, H, D, D, steps, in_dtype=dtype, gate=gate,
+                                      beta_mode=beta_mode, log_alpha_range=rng, seed=seed)
+
+
+@pytest.mark.parametrize("gate,beta_mode", MODES)
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_steps(gate, beta_mode, D, dtype):
+    import delta_rule_linear_amd as drl
+    import oracle
+    from gpu_common import to_dev
+    dp = _decode_case(5, 3, D, gate, beta_mode, 4, dtype)
+    announce("decode", gate, beta_mode, D, dtype)
+    S = to_dev(dp.S, "f32")
+    Sy = dp.S.astype(np.float64)
+    for t in range(dp.steps):
+        la = None if dp.log_alpha is None else dp.log_alpha[t]
+        o = drl.dr_decode_step(S, to_dev(dp.q[t], dtype), to_dev(dp.k[t], dtype), to_dev(dp.v[t], dtype),
+                               to_dev(la, "f32"), to_dev(dp.beta[t], "f32"), gate=gate,
+                               beta_mode=beta_mode)
+        oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], la, dp.beta[t], gate=gate,
+                                    beta_mode=beta_mode)
+        assert rel_err(to_np(o), oy) <= 1e-5, f"step {t} o"
+    assert rel_err(to_np(S), Sy) <= 1e-5
+
+
+def test_decode_full_batch_sampled():
+    """256 sequences x 16 heads, 128x128 fp32 states, bf16 tokens, GDN gating:
+    8 consecutive steps, every output and state checked."""
+    import delta_rule_linear_amd as drl
+    import oracle
+    from gpu_common import to_dev
+    dp = inputs.make_decode_problem(256, 16, 128, 128, 8)
+    announce("decode full batch", dp.N, dp.H)
+    S = to_dev(dp.S, "f32")
+    Sy = dp.S.astype(np.float64)
+    for t in range(dp.steps):
+        o = drl.dr_decode_step(S, to_dev(dp.q[t], "bf16"), to_dev(dp.k[t], "bf16"),
+                               to_dev(dp.v[t], "bf16"), to_dev(dp.log_alpha[t], "f32"),
+                               to_dev(dp.beta[t], "f32"), gate="scalar", beta_mode="scalar")
+        oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], dp.log_alpha[t], dp.beta[t],
+                                    gate="scalar", beta_mode="scalar")
+        assert rel_err(to_np(o), oy) <= 1e-5
+    assert rel_err(to_np(S), Sy) <= 1e-5
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_split_invariance_and_inplace_state():
+    import delta_rule_linear_amd as drl
+    from gpu_common import problem_to_dev
+    p = inputs.make_chunk_problem(2, 3, 320, 128, 128, gate="channel", beta_mode="channel",
+                                  log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=11, name="split")
+    t = problem_to_dev(p)
+    announce("split invariance")
+    o_full, S_full = drl.dr_chunk_fwd(**t, gate=p.gate, beta_mode=p.beta_mode)
+    # split at a non-multiple of 64, carrying the state in place (S_final == S0)
+    cut = 150
+    sl = lambda x, s: None if x is None else x[:, :, s].contiguous()
+    S = t["S0"].clone()
+    o1, _ = drl.dr_chunk_fwd(sl(t["q"], slice(0, cut)), sl(t["k"], slice(0, cut)), sl(t["v"], slice(0, cut)),
+                             sl(t["log_alpha"], slice(0, cut)), sl(t["beta"], slice(0, cut)), S,
+                             S_final=S, gate=p.gate, beta_mode=p.beta_mode)
+    o2, _ = drl.dr_chunk_fwd(sl(t["q"], slice(cut, None)), sl(t["k"], slice(cut, None)),
+                             sl(t["v"], slice(cut, None)), sl(t["log_alpha"], slice(cut, None)),
+                             sl(t["beta"], slice(cut, None)), S, S_final=S, gate=p.gate,
+                             beta_mode=p.beta_mode)
+    o_split = torch.cat([o1, o2], dim=2)
+    assert rel_err(to_np(o_split), to_np(o_full)) <= 2e-3
+    assert rel_err(to_np(S), to_np(S_full)) <= 2e-3
+
+
+def test_prefill_then_decode_matches_longer_prefill():
+    import delta_rule_linear_amd as drl
+    from gpu_common import problem_to_dev
+    p = inputs.make_chunk_problem(2, 4, 200, 128, 128, gate="scalar", s0_var=0.01, seed=12,
+                                  name="prefill+decode")
+    t = problem_to_dev(p)
+    announce("prefill then decode")
+    o_full, S_full = drl.dr_chunk_fwd(**t, gate="scalar", beta_mode="scalar")
+    n = 5
+    sl = lambda x, s: x[:, :, s].contiguous()
+    _, S = drl.dr_chunk_fwd(sl(t["q"], slice(0, 200 - n)), sl(t["k"], slice(0, 200 - n)),
+                            sl(t["v"], slice(0, 200 - n)), sl(t["log_alpha"], slice(0, 200 - n)),
+                            sl(t["beta"], slice(0, 200 - n)), t["S0"], gate="scalar", beta_mode="scalar")
+    for j in range(200 - n, 200):
+        o = drl.dr_decode_step(S, t["q"][:, :, j].contiguous(), t["k"][:, :, j].contiguous(),
+                               t["v"][:, :, j].contiguous(), t["log_alpha"][:, :, j].contiguous(),
+                               t["beta"][:, :, j].contiguous(), gate="scalar", beta_mode="scalar")
+        assert rel_err(to_np(o), to_np(o_full[:, :, j])) <= 3e-3
+    assert rel_err(to_np(S), to_np(S_full)) <= 3e-3
+
+
+def test_cross_mode_equivalence_on_gpu():
+    import delta_rule_linear_amd as drl
+    from gpu_common import problem_to_dev
+    p = inputs.make_chunk_problem(1, 3, 130, 128, 128, gate="scalar", s0_var=0.01, seed=13, name="xmode")
+    t = problem_to_dev(p)
+    announce("cross-mode equivalence")
+    o_s, S_s = drl.dr_chunk_fwd(**t, gate="scalar", beta_mode="scalar")
+    lac = t["log_alpha"][..., None].expand(-1, -1, -1, 128).contiguous()
+    bc = t["beta"][..., None].expand(-1, -1, -1, 128).contiguous()
+    o_c, S_c = drl.dr_chunk_fwd(t["q"], t["k"], t["v"], lac, bc, t["S0"], gate="channel",
+                                beta_mode="channel")
+    assert rel_err(to_np(o_c), to_np(o_s)) <= 2e-3 and rel_err(to_np(S_c), to_np(S_s)) <= 2e-3
+    o_n, S_n = drl.dr_chunk_fwd(t["q"], t["k"], t["v"], None, t["beta"], t["S0"], gate="none",
+                                beta_mode="scalar")
+    o_z, S_z = drl.dr_chunk_fwd(t["q"], t["k"], t["v"], torch.zeros_like(t["log_alpha"]), t["beta"],
+                                t["S0"], gate="scalar", beta_mode="scalar")
+    assert torch.equal(o_n, o_z) and torch.equal(S_n, S_z)
+
+
+def test_beta_zero_is_pure_decay():
+    import delta_rule_linear_amd as drl
+    from gpu_common import problem_to_dev
+    p = inputs.make_chunk_problem(1, 2, 100, 128, 128, gate="channel", log_alpha_range=(-0.2, -0.0005),
+                                  s0_var=0.01, seed=14, name="beta0")
+    t = problem_to_dev(p)
+    t["beta"] = torch.zeros_like(t["beta"])
+    announce("beta zero")
+    o, S = drl.dr_chunk_fwd(**t, gate="channel", beta_mode="scalar")
+    g = torch.cumsum(t["log_alpha"].double(), dim=2)               # [B,H,L,Dk]
+    St = torch.exp(g)[..., None] * t["S0"].double()[:, :, None]    # [B,H,L,Dk,Dv]
+    o_want = torch.einsum("bhlk,bhlkv->bhlv", t["q"].double(), St)
+    assert rel_err(to_np(o), o_want.cpu().numpy()) <= 3e-3
+    assert rel_err(to_np(S), St[:, :, -1].cpu().numpy()) <= 1e-5
+
+
+def test_empty_sequence_returns_initial_state():
+    import delta_rule_linear_amd as drl
+    S0 = torch.randn(2, 3, 128, 64, device="cuda")
+    z = lambda *s: torch.empty(*s, device="cuda", dtype=torch.bfloat16)
+    o, S = drl.dr_chunk_fwd(z(2, 3, 0, 128), z(2, 3, 0, 128), z(2, 3, 0, 64),
+                            torch.empty(2, 3, 0, device="cuda"), torch.empty(2, 3, 0, device="cuda"),
+                            S0, gate="scalar", beta_mode="scalar")
+    assert o.shape == (2, 3, 0, 64) and torch.equal(S, S0)
+    o, S = drl.dr_chunk_fwd(z(2, 3, 0, 128), z(2, 3, 0, 128), z(2, 3, 0, 64),
+                            torch.empty(2, 3, 0, device="cuda"), torch.empty(2, 3, 0, device="cuda"),
+                            None, gate="scalar", beta_mode="scalar")
+    assert torch.equal(S, torch.zeros_like(S0))
+
+
+def test_deterministic_bits():
+    p = inputs.make_chunk_problem(2, 4, 257, 128, 128, gate="channel", beta_mode="channel",
+                                  log_alpha_range=(-0.2, -0.0005), seed=15, name="determinism")
+    announce("determinism")
+    o1, S1 = run_hip(p)
+    o2, S2 = run_hip(p)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
