@@ -35,6 +35,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "dr_device.h"
 #include "dr_internal.h"
 
@@ -115,14 +117,21 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     // ---------------------------------------------------------------- gates
     if constexpr (!CGATE) {
         if (w == 0) {
-            float g = (a.has_gate && l < Lc) ? a.log_alpha[tok0 + l] : 0.f;
+            const int lc = l < Lc ? l : 0;   // masked rows load a valid row, then drop it
+            float g = a.has_gate ? a.log_alpha[tok0 + lc] : 0.f;
+            g = l < Lc ? g : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 float y = __shfl_up(g, off);
                 if (l >= off) g += y;
             }
             sg[l] = g;
-            sb[l] = (!CBETA && l < Lc) ? a.beta[tok0 + l] : 0.f;
+            if constexpr (!CBETA) {
+                const float bl = a.beta[tok0 + lc];
+                sb[l] = l < Lc ? bl : 0.f;
+            } else {
+                sb[l] = 0.f;
+            }
             const float g63 = __shfl(g, 63);
             a.wsG[cs * kGW + l] = expf(g);             // gamma_r = e^{G_r}
             a.wsG[cs * kGW + 64 + l] = expf(g63 - g);  // lambda_r = e^{G_63 - G_r}
@@ -131,12 +140,12 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
         if constexpr (CBETA) {
             for (int e = tid; e < CH * DK; e += 256) {
                 const int r = e / DK, col = e % DK;
-                float kv = 0.f, vv = 0.f;
-                if (r < Lc) {
-                    const float sbv = sqrtf(a.beta[(tok0 + r) * DK + col]);
-                    kv = sbv * load1<F32IN>(a.k, (tok0 + r) * DK + col);
-                    vv = sbv * load1<F32IN>(a.v, (tok0 + r) * Dv + col);
-                }
+                const int rc = r < Lc ? r : 0;
+                const float sbv = sqrtf(a.beta[(tok0 + rc) * DK + col]);
+                float kv = sbv * load1<F32IN>(a.k, (tok0 + rc) * DK + col);
+                float vv = sbv * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
+                kv = r < Lc ? kv : 0.f;
+                vv = r < Lc ? vv : 0.f;
                 store_split<P>(a.wsKs, cs * (size_t)(P * CH * DK), (size_t)CH * DK, r * DK + col, kv);
                 store_split<P>(a.wsV, cs * (size_t)(P * CH * DK), (size_t)CH * DK, r * DK + col, vv);
             }
@@ -154,7 +163,8 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
             float run = 0.f;
 #pragma unroll
             for (int r = 0; r < CH; ++r) {
-                run += (r < Lc) ? a.log_alpha[(tok0 + r) * DK + col] : 0.f;
+                const float x = a.log_alpha[(tok0 + (r < Lc ? r : 0)) * DK + col];
+                run += (r < Lc) ? x : 0.f;
                 G[r] = run;
             }
             // per-block factors, <= 1 for non-positive log gates:
@@ -176,15 +186,17 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) {
                     const int r = 16 * R + rr;
-                    float kv = 0.f, qv = 0.f, vv = 0.f, sbv = 1.f;
-                    if (r < Lc) {
-                        kv = load1<F32IN>(a.k, (tok0 + r) * DK + col);
-                        qv = load1<F32IN>(a.q, (tok0 + r) * DK + col);
-                        if constexpr (CBETA) {
-                            sbv = sqrtf(a.beta[(tok0 + r) * DK + col]);
-                            vv = sbv * load1<F32IN>(a.v, (tok0 + r) * Dv + col);
-                        }
+                    const int rc = r < Lc ? r : 0;
+                    float kv = load1<F32IN>(a.k, (tok0 + rc) * DK + col);
+                    float qv = load1<F32IN>(a.q, (tok0 + rc) * DK + col);
+                    float vv = 0.f, sbv = 1.f;
+                    if constexpr (CBETA) {
+                        sbv = sqrtf(a.beta[(tok0 + rc) * DK + col]);
+                        vv = sbv * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
                     }
+                    kv = r < Lc ? kv : 0.f;
+                    qv = r < Lc ? qv : 0.f;
+                    vv = r < Lc ? vv : 0.f;
                     const float kt = sbv * kv;
                     const float rowf = expf(G[r] - gs);
                     const float colf = expf(ge - G[r]);
@@ -208,7 +220,10 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
             if (badbits) atomicOr(&sflag[0], badbits);
         }
         if constexpr (!CBETA) {
-            if (w == 3) sb[l] = (l < Lc) ? a.beta[tok0 + l] : 0.f;
+            if (w == 3) {
+                const float bl = a.beta[tok0 + (l < Lc ? l : 0)];
+                sb[l] = l < Lc ? bl : 0.f;
+            }
         }
     }
     __syncthreads();
@@ -229,17 +244,26 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
             const int k0 = 32 * s + 8 * (l >> 4);
             Frag<P> fa, fb;
             if constexpr (!CGATE) {
+                const int rac = ra < Lc ? ra : 0, cac = ca < Lc ? ca : 0;
+                const Raw8<F32IN> rwa = ld_raw8<F32IN>(isP ? a.q : a.k, (tok0 + rac) * DK + k0);
+                const Raw8<F32IN> rwb = ld_raw8<F32IN>(a.k, (tok0 + cac) * DK + k0);
                 if constexpr (!CBETA) {
-                    fa = load_frag_in<F32IN, P>(isP ? a.q : a.k, (tok0 + ra) * DK + k0, ra < Lc);
-                    fb = load_frag_in<F32IN, P>(a.k, (tok0 + ca) * DK + k0, ca < Lc);
+                    fa = raw_to_frag<F32IN, P>(rwa, ra < Lc);
+                    fb = raw_to_frag<F32IN, P>(rwb, ca < Lc);
                 } else {
-                    float xa[8], xb[8];
-                    load8<F32IN>(isP ? a.q : a.k, (tok0 + ra) * DK + k0, ra < Lc, xa);
-                    load8<F32IN>(a.k, (tok0 + ca) * DK + k0, ca < Lc, xb);
+                    float xa[8], xb[8], ba[8], bb[8];
+                    const float4* pa = reinterpret_cast<const float4*>(a.beta + (tok0 + rac) * DK + k0);
+                    const float4* pb = reinterpret_cast<const float4*>(a.beta + (tok0 + cac) * DK + k0);
+                    *reinterpret_cast<float4*>(ba) = pa[0];
+                    *reinterpret_cast<float4*>(ba + 4) = pa[1];
+                    *reinterpret_cast<float4*>(bb) = pb[0];
+                    *reinterpret_cast<float4*>(bb + 4) = pb[1];
+                    cvt_raw8<F32IN>(rwa, ra < Lc, xa);
+                    cvt_raw8<F32IN>(rwb, ca < Lc, xb);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        if (!isP && ra < Lc) xa[j] *= sqrtf(a.beta[(tok0 + ra) * DK + k0 + j]);
-                        if (ca < Lc) xb[j] *= sqrtf(a.beta[(tok0 + ca) * DK + k0 + j]);
+                        if (!isP) xa[j] *= sqrtf(ba[j]);
+                        xb[j] *= sqrtf(bb[j]);
                     }
                     fa = split8<P>(xa);
                     fb = split8<P>(xb);
@@ -387,41 +411,45 @@ struct ScanSmem {
     static constexpr int HALFS = kKT + P * DK * RP;
 };
 
-// Per-chunk operands a wave prefetches into registers.
-template <int DK, int P>
+// Per-chunk operands a thread prefetches one chunk ahead.  Loads are issued
+// unconditionally (masked rows are clamped to row 0 of the chunk) and kept as
+// raw bits, so nothing waits on them until the chunk is consumed.
+template <int DK, bool F32IN>
 struct ScanRegs {
-    Frag<P> ks[DK / 32];     // rows 16w.. of Ks, A operand of K S
-    Frag<P> qs[DK / 32];     // rows 16w.. of Qs
-    Frag<P> th[2];           // rows 16w.. of T^
-    Frag<P> pm[2];           // rows 16w.. of P
-    float v[4];              // V tile in accumulator layout
-    float gam[4], lam[4];    // scalar-gate row factors (rows of this lane)
-    float g63[DK / 64 * 4];  // state decay for this lane's S rows
-    float kt[DK / 4];        // this thread's slice of Kl (token tid & 63, 32 or 16 channels)
+    static constexpr int P = F32IN ? 2 : 1;
+    using VT = typename std::conditional<F32IN, float, uint16_t>::type;
+    int Lc;
+    Raw8<F32IN> ksr[DK / 32], qsr[DK / 32];   // rows 16w.. of K, Q (raw inputs)
+    Frag<P> ksh[DK / 32], qsh[DK / 32];       // the same from the workspace (gated forms)
+    Frag<P> th[2], pm[2];                     // rows 16w.. of T^ and P
+    VT vr[4];                                 // V tile (raw input), accumulator layout
+    half_t vh[4][P];                          // V tile from the workspace (channel beta)
+    float gam[4], lam[4];                     // scalar-gate row factors
+    float g63[DK / 64 * 4];                   // state decay of this lane's S rows
+    Raw8<F32IN> ktr[DK / 32];                 // Kl slice: token tid & 63, DK/4 channels (raw)
+    half8 kth[DK / 32][P];                    // the same from the workspace
 };
 
 template <int DK, bool F32IN, bool CGATE, bool CBETA>
-__device__ __forceinline__ void scan_load(const ChunkArgs& a, ScanRegs<DK, F32IN ? 2 : 1>& g,
-                                          int seq, int c, int n0, int w, int l, int tid) {
+__device__ __forceinline__ void scan_fetch(const ChunkArgs& a, ScanRegs<DK, F32IN>& g, int seq,
+                                           int c, int n0, int w, int l, int tid) {
     constexpr int P = F32IN ? 2 : 1;
     const int t0 = c * CH;
     const int Lc = min(CH, a.L - t0);
+    g.Lc = Lc;
     const size_t tok0 = (size_t)seq * a.L + t0;
     const size_t cs = (size_t)seq * a.NC + c;
     const int ra = 16 * w + (l & 15);
+    const int rac = ra < Lc ? ra : 0;                // clamped row for raw loads
     const size_t opl = (size_t)CH * DK;              // plane stride of [64][DK] operands
     const size_t obase = cs * (size_t)(P * CH * DK);
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
         const int k0 = 32 * s + 8 * (l >> 4);
-        if constexpr (CGATE) {
-            g.ks[s] = load_frag_h<P>(a.wsKs, obase + ra * DK + k0, opl);
-            g.qs[s] = load_frag_h<P>(a.wsQ, obase + ra * DK + k0, opl);
-        } else {
-            if constexpr (CBETA) g.ks[s] = load_frag_h<P>(a.wsKs, obase + ra * DK + k0, opl);
-            else g.ks[s] = load_frag_in<F32IN, P>(a.k, (tok0 + ra) * DK + k0, ra < Lc);
-            g.qs[s] = load_frag_in<F32IN, P>(a.q, (tok0 + ra) * DK + k0, ra < Lc);
-        }
+        if constexpr (CGATE || CBETA) g.ksh[s] = load_frag_h<P>(a.wsKs, obase + ra * DK + k0, opl);
+        else g.ksr[s] = ld_raw8<F32IN>(a.k, (tok0 + rac) * DK + k0);
+        if constexpr (CGATE) g.qsh[s] = load_frag_h<P>(a.wsQ, obase + ra * DK + k0, opl);
+        else g.qsr[s] = ld_raw8<F32IN>(a.q, (tok0 + rac) * DK + k0);
     }
     const size_t tbase = cs * (size_t)(P * CH * CH);
 #pragma unroll
@@ -430,18 +458,16 @@ __device__ __forceinline__ void scan_load(const ChunkArgs& a, ScanRegs<DK, F32IN
         g.th[s] = load_frag_h<P>(a.wsT, tbase + ra * CH + k0, (size_t)CH * CH);
         g.pm[s] = load_frag_h<P>(a.wsP, tbase + ra * CH + k0, (size_t)CH * CH);
     }
+    const int col = n0 + (l & 15);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = 16 * w + 4 * (l >> 4) + j;
-        const int col = n0 + (l & 15);
         if constexpr (CBETA) {
-            float vv = 0.f;
-            const half_t* vb = a.wsV + obase + r * DK + col;
-            vv = (float)vb[0];
-            if constexpr (P == 2) vv += (float)vb[opl];
-            g.v[j] = vv;
+#pragma unroll
+            for (int p = 0; p < P; ++p) g.vh[j][p] = a.wsV[obase + p * opl + r * DK + col];
         } else {
-            g.v[j] = (r < Lc) ? load1<F32IN>(a.v, (tok0 + r) * a.Dv + col) : 0.f;
+            const int rc = r < Lc ? r : 0;
+            g.vr[j] = static_cast<const typename ScanRegs<DK, F32IN>::VT*>(a.v)[(tok0 + rc) * a.Dv + col];
         }
         if constexpr (!CGATE) {
             g.gam[j] = a.wsG[cs * kGW + r];
@@ -459,30 +485,157 @@ __device__ __forceinline__ void scan_load(const ChunkArgs& a, ScanRegs<DK, F32IN
             for (int j = 0; j < 4; ++j)
                 g.g63[t * 4 + j] = a.wsG[cs * kGW + 16 * (w * (DK / 64) + t) + 4 * (l >> 4) + j];
     }
-    // Kl slice for the transposed LDS copy: token tid & 63, channels
-    // [(tid >> 6) * DK/4, +DK/4)
+    {
+        const int r = tid & 63, c0 = (tid >> 6) * (DK / 4);
+        const int rc = r < Lc ? r : 0;
+#pragma unroll
+        for (int i = 0; i < DK / 32; ++i) {
+            if constexpr (CGATE || CBETA) {
+                const half_t* src = (CGATE ? a.wsKl : a.wsKs) + obase + r * DK + c0 + 8 * i;
+#pragma unroll
+                for (int p = 0; p < P; ++p) g.kth[i][p] = *reinterpret_cast<const half8*>(src + p * opl);
+            } else {
+                g.ktr[i] = ld_raw8<F32IN>(a.k, (tok0 + rc) * DK + c0 + 8 * i);
+            }
+        }
+    }
+}
+
+// One chunk of the scan for one workgroup: consumes the prefetched operands
+// in `cur`, updates the fp32 state tile S (registers) and its fp16 copy in LDS.
+template <int DK, bool F32IN, bool CGATE, bool CBETA>
+__device__ __forceinline__ void scan_chunk(const ChunkArgs& a, const ScanRegs<DK, F32IN>& cur,
+                                           f32x4 (&S)[DK / 64], half_t* smem, int seq, int c,
+                                           int col, int w, int l, int tid) {
+    constexpr int P = F32IN ? 2 : 1;
+    constexpr int NTS = DK / 64;
+    using SM = ScanSmem<DK, P>;
+    half_t* sS = smem + SM::kS;
+    half_t* sR = smem + SM::kR;
+    half_t* sV = smem + SM::kV;
+    half_t* sVl = smem + SM::kVl;
+    half_t* sKT = smem + SM::kKT;
+    constexpr int SPL = 16 * SM::SP;
+    constexpr int RPL = 16 * SM::RP;
+    constexpr int KPL = DK * SM::RP;
+    const int t0 = c * CH;
+    const int Lc = cur.Lc;
+    const int ra = 16 * w + (l & 15);
+
+    // Kl^T into LDS (read by the state update after the next barriers)
     {
         const int r = tid & 63, c0 = (tid >> 6) * (DK / 4);
 #pragma unroll
-        for (int j0 = 0; j0 < DK / 4; j0 += 8) {
-            float x[8];
+        for (int i = 0; i < DK / 32; ++i) {
             if constexpr (CGATE || CBETA) {
-                const half_t* src = (CGATE ? a.wsKl : a.wsKs) + obase + r * DK + c0 + j0;
-                half8 hi = *reinterpret_cast<const half8*>(src);
+                // already fp16 terms: copy each plane
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = (float)hi[j];
-                if constexpr (P == 2) {
-                    half8 lo = *reinterpret_cast<const half8*>(src + opl);
+                for (int j = 0; j < 8; ++j)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) x[j] += (float)lo[j];
-                }
+                    for (int p = 0; p < P; ++p) sKT[p * KPL + (c0 + 8 * i + j) * SM::RP + r] = cur.kth[i][p][j];
             } else {
-                load8<F32IN>(a.k, (tok0 + r) * DK + c0 + j0, r < Lc, x);
-            }
+                float x[8];
+                cvt_raw8<F32IN>(cur.ktr[i], r < Lc, x);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) g.kt[j0 + j] = x[j];
+                for (int j = 0; j < 8; ++j) {
+                    if constexpr (P == 2) {
+                        half_t hi, lo;
+                        split2(x[j], hi, lo);
+                        sKT[(c0 + 8 * i + j) * SM::RP + r] = hi;
+                        sKT[KPL + (c0 + 8 * i + j) * SM::RP + r] = lo;
+                    } else {
+                        sKT[(c0 + 8 * i + j) * SM::RP + r] = (half_t)x[j];
+                    }
+                }
+            }
         }
     }
+
+    // step 1: X = Ks S, Y = Qs S for rows 16w..16w+15
+    f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+        const int k0 = 32 * s + 8 * (l >> 4);
+        Frag<P> sf = load_frag_h<P>(sS, (l & 15) * SM::SP + k0, SPL);
+        Frag<P> kf, qf;
+        if constexpr (CGATE || CBETA) kf = cur.ksh[s];
+        else kf = raw_to_frag<F32IN, P>(cur.ksr[s], ra < Lc);
+        if constexpr (CGATE) qf = cur.qsh[s];
+        else qf = raw_to_frag<F32IN, P>(cur.qsr[s], ra < Lc);
+        X = mma<P, P>(kf, sf, X);
+        Y = mma<P, P>(qf, sf, Y);
+    }
+    // step 2: R = V - gamma X
+    f32x4 Rv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * w + 4 * (l >> 4) + j;
+        float vv;
+        if constexpr (CBETA) {
+            vv = (float)cur.vh[j][0];
+            if constexpr (P == 2) vv += (float)cur.vh[j][P - 1];
+        } else if constexpr (F32IN) {
+            vv = r < Lc ? cur.vr[j] : 0.f;
+        } else {
+            vv = r < Lc ? bf16_to_f32(cur.vr[j]) : 0.f;
+        }
+        Rv[j] = vv - (CGATE ? 1.f : cur.gam[j]) * X[j];
+    }
+    st4_lds<P>(sR + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, Rv);
+    __syncthreads();
+
+    // step 3: U = T^ R
+    f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int k0 = 32 * s + 8 * (l >> 4);
+        U = mma<P, P>(cur.th[s], load_frag_h<P>(sR, (l & 15) * SM::RP + k0, RPL), U);
+    }
+    st4_lds<P>(sV + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, U);
+    if constexpr (!CGATE) {
+        f32x4 Ul;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Ul[j] = cur.lam[j] * U[j];
+        st4_lds<P>(sVl + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, Ul);
+    }
+    __syncthreads();
+
+    // step 4: O = gamma Y + P U
+    f32x4 O;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) O[j] = (CGATE ? 1.f : cur.gam[j]) * Y[j];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int k0 = 32 * s + 8 * (l >> 4);
+        O = mma<P, P>(cur.pm[s], load_frag_h<P>(sV, (l & 15) * SM::RP + k0, RPL), O);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * w + 4 * (l >> 4) + j;
+        if (r < Lc) {
+            const size_t oi = ((size_t)seq * a.L + t0 + r) * a.Dv + col;
+            if (a.out_bf16) static_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(O[j]);
+            else static_cast<float*>(a.o)[oi] = O[j];
+        }
+    }
+
+    // step 5: S = g63 S + Kl^T (lambda U)
+    const half_t* sU = CGATE ? sV : sVl;
+#pragma unroll
+    for (int t = 0; t < NTS; ++t) {
+        const int rt = 16 * (w * NTS + t);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int k0 = 32 * s + 8 * (l >> 4);
+            Frag<P> ka = load_frag_h<P>(sKT, (rt + (l & 15)) * SM::RP + k0, KPL);
+            acc = mma<P, P>(ka, load_frag_h<P>(sU, (l & 15) * SM::RP + k0, RPL), acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[t][j] = cur.g63[t * 4 + j] * S[t][j] + acc[j];
+        st4_lds<P>(sS + (l & 15) * SM::SP + rt + 4 * (l >> 4), SPL, S[t]);
+    }
+    __syncthreads();
 }
 
 template <int DK, bool F32IN, bool CGATE, bool CBETA>
@@ -526,97 +679,22 @@ __global__ __launch_bounds__(256) void scan_kernel(ChunkArgs a) {
         st4_lds<P>(sS + (l & 15) * SM::SP + 16 * (w * NTS + t) + 4 * (l >> 4), SPL, S[t]);
     }
 
-    ScanRegs<DK, P> cur;
-    if (a.NC > 0) scan_load<DK, F32IN, CGATE, CBETA>(a, cur, seq, 0, n0, w, l, tid);
+    // Two register sets, alternating: while one chunk is consumed the next
+    // one's loads are in flight, with no loop-carried copies.
+    ScanRegs<DK, F32IN> ra_, rb_;
+    if (a.NC > 0) scan_fetch<DK, F32IN, CGATE, CBETA>(a, ra_, seq, 0, n0, w, l, tid);
     __syncthreads();
-
-    for (int c = 0; c < a.NC; ++c) {
-        ScanRegs<DK, P> nxt;
-        if (c + 1 < a.NC) scan_load<DK, F32IN, CGATE, CBETA>(a, nxt, seq, c + 1, n0, w, l, tid);
-        const int t0 = c * CH;
-        const int Lc = min(CH, a.L - t0);
-
-        // Kl^T into LDS (read by the state update after the next barriers)
-        {
-            const int r = tid & 63, c0 = (tid >> 6) * (DK / 4);
-#pragma unroll
-            for (int j = 0; j < DK / 4; ++j) {
-                const float x = cur.kt[j];
-                const half_t hi = (half_t)x;
-                sKT[(c0 + j) * SM::RP + r] = hi;
-                if constexpr (P == 2) sKT[KPL + (c0 + j) * SM::RP + r] = (half_t)(x - (float)hi);
-            }
-        }
-
-        // step 1: X = Ks S, Y = Qs S for rows 16w..16w+15
-        f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            const int k0 = 32 * s + 8 * (l >> 4);
-            Frag<P> sf = load_frag_h<P>(sS, (l & 15) * SM::SP + k0, SPL);
-            X = mma<P, P>(cur.ks[s], sf, X);
-            Y = mma<P, P>(cur.qs[s], sf, Y);
-        }
-        // step 2: R = V - gamma X
-        f32x4 Rv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Rv[j] = cur.v[j] - (CGATE ? 1.f : cur.gam[j]) * X[j];
-        st4_lds<P>(sR + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, Rv);
-        __syncthreads();
-
-        // step 3: U = T^ R
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int k0 = 32 * s + 8 * (l >> 4);
-            U = mma<P, P>(cur.th[s], load_frag_h<P>(sR, (l & 15) * SM::RP + k0, RPL), U);
-        }
-        st4_lds<P>(sV + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, U);
-        if constexpr (!CGATE) {
-            f32x4 Ul;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Ul[j] = cur.lam[j] * U[j];
-            st4_lds<P>(sVl + (l & 15) * SM::RP + 16 * w + 4 * (l >> 4), RPL, Ul);
-        }
-        __syncthreads();
-
-        // step 4: O = gamma Y + P U
-        f32x4 O;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) O[j] = (CGATE ? 1.f : cur.gam[j]) * Y[j];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int k0 = 32 * s + 8 * (l >> 4);
-            O = mma<P, P>(cur.pm[s], load_frag_h<P>(sV, (l & 15) * SM::RP + k0, RPL), O);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * w + 4 * (l >> 4) + j;
-            if (r < Lc) {
-                const size_t oi = ((size_t)seq * a.L + t0 + r) * a.Dv + col;
-                if (a.out_bf16) static_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(O[j]);
-                else static_cast<float*>(a.o)[oi] = O[j];
-            }
-        }
-
-        // step 5: S = g63 S + Kl^T (lambda U)
-        const half_t* sU = CGATE ? sV : sVl;
-#pragma unroll
-        for (int t = 0; t < NTS; ++t) {
-            const int rt = 16 * (w * NTS + t);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int k0 = 32 * s + 8 * (l >> 4);
-                Frag<P> ka = load_frag_h<P>(sKT, (rt + (l & 15)) * SM::RP + k0, KPL);
-                acc = mma<P, P>(ka, load_frag_h<P>(sU, (l & 15) * SM::RP + k0, RPL), acc);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) S[t][j] = cur.g63[t * 4 + j] * S[t][j] + acc[j];
-            st4_lds<P>(sS + (l & 15) * SM::SP + rt + 4 * (l >> 4), SPL, S[t]);
-        }
-        __syncthreads();
-        if (c + 1 < a.NC) cur = nxt;
+    // The fetches are unconditional (past the end they re-read the last chunk)
+    // so that no control-flow join makes the compiler wait on the newer set.
+    const int last = a.NC - 1;
+    for (int c = 0; c < a.NC; c += 2) {
+        scan_fetch<DK, F32IN, CGATE, CBETA>(a, rb_, seq, min(c + 1, last), n0, w, l, tid);
+        __builtin_amdgcn_sched_barrier(0);   // keep every prefetch load at the top
+        scan_chunk<DK, F32IN, CGATE, CBETA>(a, ra_, S, smem, seq, c, col, w, l, tid);
+        if (c + 1 > last) break;
+        scan_fetch<DK, F32IN, CGATE, CBETA>(a, ra_, seq, min(c + 2, last), n0, w, l, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        scan_chunk<DK, F32IN, CGATE, CBETA>(a, rb_, S, smem, seq, c + 1, col, w, l, tid);
     }
 
     if (a.S_final) {

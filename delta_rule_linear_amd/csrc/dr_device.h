@@ -57,15 +57,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return (uint16_t)(u >> 16);
 }
 
+// Two-term fp16 split x ~ hi + lo.  x is pinned in a register first: otherwise
+// the compiler may fold x's producing multiply into one of the two conversions
+// (a fused multiply-convert rounds the exact product, a plain convert the fp32
+// product; the two differ by one fp16 ulp on near-ties) and then hi + lo is
+// off by that ulp.
+__device__ __forceinline__ void split2(float x, half_t& hi, half_t& lo) {
+    asm volatile("" : "+v"(x));
+    hi = (half_t)x;
+    lo = (half_t)(x - (float)hi);
+}
+
 // Split eight fp32 values into P fp16 terms.
 template <int P>
 __device__ __forceinline__ Frag<P> split8(const float* x) {
     Frag<P> f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        half_t hi = (half_t)x[j];
-        f.t[0][j] = hi;
-        if constexpr (P == 2) f.t[1][j] = (half_t)(x[j] - (float)hi);
+        if constexpr (P == 2) {
+            half_t hi, lo;
+            split2(x[j], hi, lo);
+            f.t[0][j] = hi;
+            f.t[1][j] = lo;
+        } else {
+            f.t[0][j] = (half_t)x[j];
+        }
     }
     return f;
 }
@@ -122,11 +138,63 @@ __device__ __forceinline__ void st4_lds(half_t* dst, size_t plane, const f32x4& 
     half4 hi, lo;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        hi[j] = (half_t)v[j];
-        if constexpr (P == 2) lo[j] = (half_t)(v[j] - (float)hi[j]);
+        if constexpr (P == 2) {
+            half_t h, o;
+            split2(v[j], h, o);
+            hi[j] = h;
+            lo[j] = o;
+        } else {
+            hi[j] = (half_t)v[j];
+        }
     }
     *reinterpret_cast<half4*>(dst) = hi;
     if constexpr (P == 2) *reinterpret_cast<half4*>(dst + plane) = lo;
+}
+
+// Eight consecutive raw input values as loaded (bf16 bits or fp32), so a load
+// can be issued early and converted later without a dependent wait.
+template <bool F32IN>
+struct Raw8 {
+    uint4 x;
+};
+template <>
+struct Raw8<true> {
+    float4 a, b;
+};
+
+// Unconditional load of eight input values at element offset `off` (the caller
+// keeps `off` in bounds, e.g. by clamping a masked row to a valid one).
+template <bool F32IN>
+__device__ __forceinline__ Raw8<F32IN> ld_raw8(const void* base, size_t off) {
+    Raw8<F32IN> r;
+    if constexpr (F32IN) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+        r.a = p[0];
+        r.b = p[1];
+    } else {
+        r.x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    }
+    return r;
+}
+
+// Raw values to fp32, zeroed when !ok.
+template <bool F32IN>
+__device__ __forceinline__ void cvt_raw8(const Raw8<F32IN>& r, bool ok, float* x) {
+    if constexpr (F32IN) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+    } else {
+        unpack_bf16x8(r.x, x);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = ok ? x[j] : 0.f;
+}
+
+template <bool F32IN, int P>
+__device__ __forceinline__ Frag<P> raw_to_frag(const Raw8<F32IN>& r, bool ok) {
+    float x[8];
+    cvt_raw8<F32IN>(r, ok, x);
+    return split8<P>(x);
 }
 
 // One input value (bf16 or fp32) as fp32.
@@ -141,9 +209,14 @@ __device__ __forceinline__ float load1(const void* base, size_t off) {
 template <int P>
 __device__ __forceinline__ void store_split(half_t* base, size_t off, size_t plane, size_t idx,
                                             float x) {
-    const half_t hi = (half_t)x;
-    base[off + idx] = hi;
-    if constexpr (P == 2) base[off + plane + idx] = (half_t)(x - (float)hi);
+    if constexpr (P == 2) {
+        half_t hi, lo;
+        split2(x, hi, lo);
+        base[off + idx] = hi;
+        base[off + plane + idx] = lo;
+    } else {
+        base[off + idx] = (half_t)x;
+    }
 }
 
 // Store sixteen fp32 values as P fp16 terms at base[idx .. idx + 16) of each
@@ -155,8 +228,14 @@ __device__ __forceinline__ void store_row16(half_t* base, size_t plane, size_t i
         half8 hi, lo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            hi[j] = (half_t)x[8 * h8 + j];
-            if constexpr (P == 2) lo[j] = (half_t)(x[8 * h8 + j] - (float)hi[j]);
+            if constexpr (P == 2) {
+                half_t h, o;
+                split2(x[8 * h8 + j], h, o);
+                hi[j] = h;
+                lo[j] = o;
+            } else {
+                hi[j] = (half_t)x[8 * h8 + j];
+            }
         }
         *reinterpret_cast<half8*>(base + idx + 8 * h8) = hi;
         if constexpr (P == 2) *reinterpret_cast<half8*>(base + plane + idx + 8 * h8) = lo;

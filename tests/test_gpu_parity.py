@@ -47,7 +47,10 @@ def test_small_sweep(dtype, gate, beta_mode, L, D):
     p = inputs.make_chunk_problem(1, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
                                   log_alpha_range=rng, s0_var=0.01, seed=L + D,
                                   name=f"sweep-{dtype}-{gate}-{beta_mode}-L{L}-D{D}")
-    _check(p)
+    # fp32 inputs run on two-term fp16 splits, whose arithmetic reaches ~1e-6:
+    # hold them to 1e-5 (ten times inside the 1e-4 contract) so that a lost
+    # low term anywhere shows up
+    _check(p, tol=1e-5 if dtype == "f32" else None)
 
 
 @pytest.mark.parametrize("Dv", [16, 48, 256])
