@@ -69,7 +69,7 @@ WsLayout ws_layout(const dr_chunk_desc& d) {
     w.T = take(NCH * P * dr::CH * dr::CH * sizeof(dr::half_t));
     w.Pm = take(NCH * P * dr::CH * dr::CH * sizeof(dr::half_t));
     w.G = take(NCH * dr::kGW * sizeof(float));
-    w.Q = cg ? take(opnd) : 0;
+    w.Q = (cg || cb) ? take(opnd) : 0;
     w.Ks = (cg || cb) ? take(opnd) : 0;
     w.Kl = cg ? take(opnd) : 0;
     w.V = cb ? take(opnd) : 0;

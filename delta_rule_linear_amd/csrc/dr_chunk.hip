@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
             a.wsG[cs * kGW + l] = expf(g);             // gamma_r = e^{G_r}
             a.wsG[cs * kGW + 64 + l] = expf(g63 - g);  // lambda_r = e^{G_63 - G_r}
         }
-        // channel beta with a scalar gate: the scan needs kt and vt in fp16
+        // channel beta with a scalar gate: the scan needs kt, vt (and q) in fp16
         if constexpr (CBETA) {
             for (int e = tid; e < CH * DK; e += 256) {
                 const int r = e / DK, col = e % DK;
@@ -144,8 +144,11 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
                 const float sbv = sqrtf(a.beta[(tok0 + rc) * DK + col]);
                 float kv = sbv * load1<F32IN>(a.k, (tok0 + rc) * DK + col);
                 float vv = sbv * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
+                float qv = load1<F32IN>(a.q, (tok0 + rc) * DK + col);
                 kv = r < Lc ? kv : 0.f;
                 vv = r < Lc ? vv : 0.f;
+                qv = r < Lc ? qv : 0.f;
+                store_split<P>(a.wsQ, cs * (size_t)(P * CH * DK), (size_t)CH * DK, r * DK + col, qv);
                 store_split<P>(a.wsKs, cs * (size_t)(P * CH * DK), (size_t)CH * DK, r * DK + col, kv);
                 store_split<P>(a.wsV, cs * (size_t)(P * CH * DK), (size_t)CH * DK, r * DK + col, vv);
             }
@@ -722,6 +725,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (nseq > 0) {
+        if constexpr (!F32IN) return launch_scan16(a, DK, CGATE, CBETA, st);
         const int NT = a.Dv / 16;
         const int groups = (nseq + 7) / 8;
         hipLaunchKernelGGL((scan_kernel<DK, F32IN, CGATE, CBETA>), dim3(groups * 8 * NT), dim3(256),

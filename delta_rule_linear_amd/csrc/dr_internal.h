@@ -18,8 +18,9 @@ constexpr int kGW = 128;
 // fp16 terms per value:
 //   wsT, wsP  [NCH][P][64][64]   T^ = (I + A)^-1 (beta-scaled columns) and P
 //   wsG       [NCH][kGW]         gate factors
-//   wsQ/Ks/Kl [NCH][P][64][Dk]   gated operands (channel gate; Ks also holds
-//                                sqrt(beta) k for a channel beta)
+//   wsQ/Ks/Kl [NCH][P][64][Dk]   gated operands (channel gate; with a channel
+//                                beta and scalar gate Ks holds sqrt(beta) k and
+//                                Q a copy of q)
 //   wsV       [NCH][P][64][Dk]   sqrt(beta) v (channel beta)
 struct ChunkArgs {
     const void* q;
@@ -57,6 +58,8 @@ struct DecodeArgs {
 
 hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                         hipStream_t st);
+// the state scan for bf16 inputs (dr_scan16.hip)
+hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st);
 
