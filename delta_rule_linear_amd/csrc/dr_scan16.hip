@@ -2,28 +2,33 @@
 //
 // Same algebra as the scan in dr_chunk.hip (per chunk, with T^ and P from the
 // prep kernel):  X = Ks S,  R = V - g X,  U = T^ R,  O = g Q S + P U,
-// S <- g63 S + Kl^T (l U);  written for low instruction count:
+// S <- g63 S + Kl^T (l U).  Built around the data movement:
 //
+//  * Each chunk's operand tiles (Kl, Ks, Q, T^, P, the V tile, gate factors)
+//    are copied once per workgroup straight into LDS with 16-byte global->LDS
+//    loads, fully coalesced, one chunk ahead into a double buffer.  Rows of a
+//    tile are stored with their 16-byte pieces XOR-swizzled by row, so the
+//    fragment reads below are free of bank conflicts.
 //  * Operand types.  With a scalar beta and no channel gate, Ks = Kl = k and
-//    Qs = q are the raw bf16 inputs: they feed bf16 matrix-core ops directly,
+//    Q = q are the raw bf16 inputs: they feed bf16 matrix-core ops directly,
 //    with the fp32 state S and l U carried as bf16 hi + lo pairs (16
 //    significant bits).  With a channel-wise gate or beta the gated operands
 //    come from the workspace in fp16 and S, U are single fp16 terms.  T^ R and
 //    P U are fp16 ops in both cases.
-//  * Kl^T fragments are read from a row-major LDS copy of the chunk's Kl with
-//    the transposing LDS read (ds_read_b64_tr_b16), so no element-wise
-//    transposition or conversion happens in registers.
+//  * Kl^T fragments come from the row-major Kl tile through the transposing
+//    LDS read (ds_read_b64_tr_b16): no transposition in registers.
 //  * No masking: rows past a sequence's end load a valid clamped row; their
 //    U is exactly zero (beta or the prep kernel's zero rows make it so), so
 //    they contribute nothing to S, and their O is never stored.
+//  * Barriers are raw s_barrier with an explicit LDS-only wait, so the
+//    copies for the next chunk stay in flight across them; the copies are
+//    waited for once, before the chunk's last barrier.
 //
 // One workgroup of four waves per (sequence, 16-column tile of S).  Wave w owns
 // chunk rows 16w..16w+15 for X, Y, R, U, O and state rows [DK/4 w, DK/4 (w+1))
-// for the state update.  Three barriers per chunk.
+// for the state update.
 
 #include <hip/hip_runtime.h>
-
-#include <type_traits>
 
 #include "dr_device.h"
 #include "dr_internal.h"
@@ -34,6 +39,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // 16x16x32 matrix-core op on raw 16-byte fragments, bf16 or fp16 elements.
 template <bool BF>
@@ -46,10 +52,12 @@ __device__ __forceinline__ f32x4 mfma_raw(const uint4& a, const uint4& b, const 
                                                       __builtin_bit_cast(half8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint4 lds16(const half_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Transposed 4 x 16-bit LDS read (see the lane map in the kernel comment).
-__device__ __forceinline__ uint2 lds_tr4(const half_t* p) {
+// Transposed LDS read of four 16-bit values.  Within each group of 16 lanes,
+// lane i receives element (i mod 4) of the 8-byte rows addressed by lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4, in that order.
+__device__ __forceinline__ uint2 lds_tr4(const char* p) {
     s16x4 v = {0, 0, 0, 0};
 #if defined(__HIP_DEVICE_COMPILE__)
     v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
@@ -57,10 +65,67 @@ __device__ __forceinline__ uint2 lds_tr4(const half_t* p) {
     return __builtin_bit_cast(uint2, v);
 }
 
-// Four fp32 values as NPL 16-bit terms (bf16 hi/lo pair, or one fp16) written
-// to consecutive LDS halfs of each plane.
+// 16 bytes from global memory into LDS at lds_base + 16 * lane (lds_base
+// must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* g, char* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+#endif
+}
+
+// Workgroup barrier over LDS only: wait for this wave's own LDS accesses,
+// then s_barrier.  Global->LDS copies in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Wait for every vector-memory operation of this wave, including the
+// global->LDS copies.
+__device__ __forceinline__ void vmem_wait_all() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    asm volatile("" ::: "memory");
+}
+
+// Swizzle of 16-byte pieces in a 64-row tile with RB bytes per row: piece p
+// of row r is stored at piece p ^ swz(r).  256-byte rows: 16 consecutive rows
+// land on 16 distinct bank groups; 128-byte rows: two rows share the 64
+// banks, so pairs of rows get distinct swizzles.
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+    return RB == 256 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int RB>
+__device__ __forceinline__ const char* tile_at(const char* tile, int r, int piece) {
+    return tile + r * RB + 16 * (piece ^ swz<RB>(r));
+}
+
+// Copy a [64][RB]-byte tile of 16-bit values (row r at src + r * pitch
+// elements; rows >= valid read row 0) into swizzled LDS; the four waves
+// share it, 1 KiB per instruction.
+template <int RB>
+__device__ __forceinline__ void dma_tile(const uint16_t* src, size_t pitch, int valid, char* tile, int w, int l) {
+    constexpr int PPR = RB / 16;      // pieces per row
+    constexpr int RPI = 64 / PPR;     // rows per 1 KiB instruction
+    constexpr int NI = 64 / RPI / 4;  // instructions per wave
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int blk = w * NI + j;
+        const int r = blk * RPI + l / PPR;
+        const int rc = r < valid ? r : 0;
+        const int lp = (l % PPR) ^ swz<RB>(r);
+        dma16(src + (size_t)rc * pitch + 8 * lp, tile + blk * 1024);
+    }
+}
+
+// Four fp32 values as NPL 16-bit terms (bf16 hi/lo pair, or one fp16) at
+// consecutive LDS halfs of each plane (plane stride in bytes).
 template <bool BF, int NPL>
-__device__ __forceinline__ void st4_terms(half_t* dst, int plane, const f32x4& v) {
+__device__ __forceinline__ void st4_terms(char* dst, int plane, const f32x4& v) {
     if constexpr (BF) {
         bf16x4 hi, lo;
 #pragma unroll
@@ -81,211 +146,74 @@ __device__ __forceinline__ void st4_terms(half_t* dst, int plane, const f32x4& v
     }
 }
 
-template <int DK, bool RAW>
-struct S16Smem {
-    static constexpr int NPL = RAW ? 2 : 1;   // terms of S and of l U
-    static constexpr int SP = DK + 8;         // pitch of S^T rows (halfs)
-    static constexpr int RP = CH + 8;         // pitch of token-major rows
-    static constexpr int KP = DK + 16;        // pitch of the Kl tile rows
-    static constexpr int kS = 0;                       // [NPL][16][SP]   S^T
-    static constexpr int kR = kS + NPL * 16 * SP;      // [16][RP]        R^T (fp16)
-    static constexpr int kU = kR + 16 * RP;            // [16][RP]        U^T (fp16)
-    static constexpr int kUl = kU + 16 * RP;           // [NPL][16][RP]   (l U)^T
-    static constexpr int kK = kUl + NPL * 16 * RP;     // [64][KP]        Kl, row-major
-    static constexpr int HALFS = kK + CH * KP;
+// LDS plan (bytes).  Two operand buffers, each
+//   [Kl 64 x RB][Ks 64 x RB, channel gate only][Q 64 x RB][T^ 64 x 128][P 64 x 128]
+//   [V 64 x 32][gate factors 512]
+// then the working area [S^T NPL x 16 x SP][R^T 16 x RP][U^T 16 x RP][(lU)^T NPL x 16 x RP].
+template <int DK, bool RAW, bool CGATE>
+struct SD {
+    static constexpr int NPL = RAW ? 2 : 1;
+    static constexpr int RB = DK * 2;               // bytes per K / Q row
+    static constexpr int KL = 0;
+    static constexpr int KS = CGATE ? KL + 64 * RB : KL;   // Ks == Kl unless the gate is per channel
+    static constexpr int QT = KS + 64 * RB;
+    static constexpr int TT = QT + 64 * RB;
+    static constexpr int PT = TT + 64 * 128;
+    static constexpr int VT = PT + 64 * 128;
+    static constexpr int GT = VT + 64 * 32;
+    static constexpr int BUF = GT + 512;
+    static constexpr int SP = (DK + 8) * 2;          // bytes per S^T row
+    static constexpr int RP = (CH + 8) * 2;          // bytes per token-major row
+    static constexpr int WS = 2 * BUF;
+    static constexpr int WR = WS + NPL * 16 * SP;
+    static constexpr int WU = WR + 16 * RP;
+    static constexpr int WUL = WU + 16 * RP;
+    static constexpr int TOTAL = WUL + NPL * 16 * RP;
 };
 
-// Operands of one chunk, prefetched a chunk ahead as raw 16-byte pieces.
-template <int DK>
-struct S16Regs {
-    uint4 ks[DK / 32];        // A fragments of Ks, rows 16w + (l & 15)
-    uint4 qs[DK / 32];        // A fragments of Qs
-    uint4 th[2], pm[2];       // A fragments of T^ and P
-    uint4 kt[DK / 32];        // this thread's piece of the Kl tile
-    uint16_t v[4];            // V tile (bf16 bits, or fp16 bits of vt), accumulator layout
-    float gam[4], lam[4];     // scalar-gate row factors
-    float g63[DK / 64 * 4];   // state decay of this lane's state rows
-};
-
+// Issue the copies of chunk c's operands into buffer `buf`.
 template <int DK, bool RAW, bool CGATE, bool CBETA>
-__device__ __forceinline__ void s16_fetch(const ChunkArgs& a, S16Regs<DK>& g, int seq, int c, int n0,
-                                          int w, int l, int tid) {
+__device__ __forceinline__ void s16_dma(const ChunkArgs& a, char* buf, int seq, int c, int n0, int w, int l) {
+    using L = SD<DK, RAW, CGATE>;
     const int t0 = c * CH;
     const int Lc = min(CH, a.L - t0);
     const size_t tok0 = (size_t)seq * a.L + t0;
     const size_t cs = (size_t)seq * a.NC + c;
-    const size_t obase = cs * (size_t)(CH * DK);     // [64][DK] workspace operand of this chunk
-    const int ra = 16 * w + (l & 15);
-    const int rac = ra < Lc ? ra : 0;                // clamped row for raw inputs
-    const uint16_t* k16 = static_cast<const uint16_t*>(a.k);
-    const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
-#pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-        const int k0 = 32 * s + 8 * (l >> 4);
-        if constexpr (RAW) {
-            g.ks[s] = *reinterpret_cast<const uint4*>(k16 + (tok0 + rac) * DK + k0);
-            g.qs[s] = *reinterpret_cast<const uint4*>(q16 + (tok0 + rac) * DK + k0);
-        } else {
-            g.ks[s] = *reinterpret_cast<const uint4*>(a.wsKs + obase + ra * DK + k0);
-            g.qs[s] = *reinterpret_cast<const uint4*>(a.wsQ + obase + ra * DK + k0);
-        }
+    const size_t obase = cs * (size_t)(CH * DK);
+    if constexpr (RAW) {
+        dma_tile<L::RB>(static_cast<const uint16_t*>(a.k) + tok0 * DK, DK, Lc, buf + L::KL, w, l);
+        dma_tile<L::RB>(static_cast<const uint16_t*>(a.q) + tok0 * DK, DK, Lc, buf + L::QT, w, l);
+    } else {
+        const half_t* kl = CGATE ? a.wsKl : a.wsKs;
+        dma_tile<L::RB>(reinterpret_cast<const uint16_t*>(kl) + obase, DK, CH, buf + L::KL, w, l);
+        if constexpr (CGATE)
+            dma_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsKs) + obase, DK, CH, buf + L::KS, w, l);
+        dma_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsQ) + obase, DK, CH, buf + L::QT, w, l);
     }
     const size_t tbase = cs * (size_t)(CH * CH);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int k0 = 32 * s + 8 * (l >> 4);
-        g.th[s] = *reinterpret_cast<const uint4*>(a.wsT + tbase + ra * CH + k0);
-        g.pm[s] = *reinterpret_cast<const uint4*>(a.wsP + tbase + ra * CH + k0);
-    }
-    {
-        const int r = tid >> 2, c0 = (tid & 3) * (DK / 4);
-        const int rc = r < Lc ? r : 0;
-#pragma unroll
-        for (int i = 0; i < DK / 32; ++i) {
-            if constexpr (RAW) {
-                g.kt[i] = *reinterpret_cast<const uint4*>(k16 + (tok0 + rc) * DK + c0 + 8 * i);
-            } else {
-                const half_t* src = (CGATE ? a.wsKl : a.wsKs) + obase + r * DK + c0 + 8 * i;
-                g.kt[i] = *reinterpret_cast<const uint4*>(src);
-            }
-        }
-    }
-    const int col = n0 + (l & 15);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 16 * w + 4 * (l >> 4) + j;
+    dma_tile<128>(reinterpret_cast<const uint16_t*>(a.wsT) + tbase, CH, CH, buf + L::TT, w, l);
+    dma_tile<128>(reinterpret_cast<const uint16_t*>(a.wsP) + tbase, CH, CH, buf + L::PT, w, l);
+    if (w < 2) {   // V tile: 64 rows x 16 columns, two 16-byte pieces per row
+        const int r = 32 * w + (l >> 1), piece = l & 1;
         if constexpr (CBETA) {
-            g.v[j] = reinterpret_cast<const uint16_t*>(a.wsV)[obase + r * DK + col];
+            dma16(reinterpret_cast<const uint16_t*>(a.wsV) + obase + r * DK + n0 + 8 * piece, buf + L::VT + w * 1024);
         } else {
             const int rc = r < Lc ? r : 0;
-            g.v[j] = static_cast<const uint16_t*>(a.v)[(tok0 + rc) * a.Dv + col];
+            dma16(static_cast<const uint16_t*>(a.v) + (tok0 + rc) * a.Dv + n0 + 8 * piece, buf + L::VT + w * 1024);
         }
-        if constexpr (!CGATE) {
-            g.gam[j] = a.wsG[cs * kGW + r];
-            g.lam[j] = a.wsG[cs * kGW + 64 + r];
-        }
+    } else if (w == 2) {   // gate factors: gamma[64] and lambda[64], or the state decay [DK]
+        constexpr int NG = CGATE ? DK / 4 : 32;
+        if (l < NG) dma16(a.wsG + cs * kGW + 4 * l, buf + L::GT);
     }
-    if constexpr (!CGATE) {
-        const float d = a.wsG[cs * kGW + 63];
-#pragma unroll
-        for (int j = 0; j < DK / 64 * 4; ++j) g.g63[j] = d;
-    } else {
-#pragma unroll
-        for (int t = 0; t < DK / 64; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                g.g63[t * 4 + j] = a.wsG[cs * kGW + 16 * (w * (DK / 64) + t) + 4 * (l >> 4) + j];
-    }
-}
-
-template <int DK, bool RAW, bool CGATE, bool CBETA>
-__device__ __forceinline__ void s16_chunk(const ChunkArgs& a, const S16Regs<DK>& cur, f32x4 (&S)[DK / 64],
-                                          half_t* smem, int seq, int c, int col, int w, int l, int tid) {
-    using SM = S16Smem<DK, RAW>;
-    constexpr int NPL = SM::NPL;
-    constexpr int NTS = DK / 64;
-    // raw bf16 operands use bf16 ops; workspace operands are fp16
-    constexpr bool BF = RAW;
-    half_t* sS = smem + SM::kS;
-    half_t* sR = smem + SM::kR;
-    half_t* sU = smem + SM::kU;
-    half_t* sUl = smem + SM::kUl;
-    half_t* sK = smem + SM::kK;
-    const int i16 = l & 15, g = l >> 4;
-    const int t0 = c * CH;
-    const int Lc = min(CH, a.L - t0);
-
-    // Kl tile for this chunk's state update (read after the next two barriers)
-    {
-        const int r = tid >> 2, c0 = (tid & 3) * (DK / 4);
-#pragma unroll
-        for (int i = 0; i < DK / 32; ++i) *reinterpret_cast<uint4*>(sK + r * SM::KP + c0 + 8 * i) = cur.kt[i];
-    }
-
-    // X = Ks S and Y = Qs S (rows 16w..16w+15)
-    f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-#pragma unroll
-        for (int p = 0; p < NPL; ++p) {
-            const uint4 sf = lds16(sS + p * 16 * SM::SP + i16 * SM::SP + 32 * s + 8 * g);
-            X = mfma_raw<BF>(cur.ks[s], sf, X);
-            Y = mfma_raw<BF>(cur.qs[s], sf, Y);
-        }
-    }
-    // R = V - g X
-    f32x4 Rv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        float vv;
-        if constexpr (CBETA) vv = (float)__builtin_bit_cast(half_t, cur.v[j]);
-        else vv = bf16_to_f32(cur.v[j]);
-        Rv[j] = vv - (CGATE ? 1.f : cur.gam[j]) * X[j];
-    }
-    st4_terms<false, 1>(sR + i16 * SM::RP + 16 * w + 4 * g, 0, Rv);
-    __syncthreads();
-
-    // U = T^ R
-    f32x4 U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-        U = mfma_raw<false>(cur.th[s], lds16(sR + i16 * SM::RP + 32 * s + 8 * g), U);
-    st4_terms<false, 1>(sU + i16 * SM::RP + 16 * w + 4 * g, 0, U);
-    {
-        f32x4 Ul;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Ul[j] = CGATE ? U[j] : cur.lam[j] * U[j];
-        st4_terms<BF, NPL>(sUl + i16 * SM::RP + 16 * w + 4 * g, 16 * SM::RP, Ul);
-    }
-    __syncthreads();
-
-    // O = g Y + P U
-    f32x4 O;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) O[j] = (CGATE ? 1.f : cur.gam[j]) * Y[j];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-        O = mfma_raw<false>(cur.pm[s], lds16(sU + i16 * SM::RP + 32 * s + 8 * g), O);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 16 * w + 4 * g + j;
-        if (r < Lc) {
-            const size_t oi = ((size_t)seq * a.L + t0 + r) * a.Dv + col;
-            if (a.out_bf16) static_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(O[j]);
-            else static_cast<float*>(a.o)[oi] = O[j];
-        }
-    }
-
-    // S = g63 S + Kl^T (l U).  The A fragment (state row rt + (l & 15), tokens
-    // 32 s + 8 g + 0..7) comes from two transposed reads: within each group
-    // of 16 lanes, lane q points at token 32 s + 8 g + (q >> 2) (+4) and key
-    // column rt + 4 (q & 3); lane i then holds column rt + i of four tokens.
-#pragma unroll
-    for (int t = 0; t < NTS; ++t) {
-        const int rt = 16 * (w * NTS + t);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const half_t* kp = sK + (32 * s + 8 * g + (i16 >> 2)) * SM::KP + rt + 4 * (i16 & 3);
-            const uint2 lo4 = lds_tr4(kp);
-            const uint2 hi4 = lds_tr4(kp + 4 * SM::KP);
-            const uint4 ka = {lo4.x, lo4.y, hi4.x, hi4.y};
-#pragma unroll
-            for (int p = 0; p < NPL; ++p)
-                acc = mfma_raw<BF>(ka, lds16(sUl + p * 16 * SM::RP + i16 * SM::RP + 32 * s + 8 * g), acc);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[t][j] = cur.g63[t * 4 + j] * S[t][j] + acc[j];
-        st4_terms<BF, NPL>(sS + i16 * SM::SP + rt + 4 * g, 16 * SM::SP, S[t]);
-    }
-    __syncthreads();
 }
 
 template <int DK, bool RAW, bool CGATE, bool CBETA>
 __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
-    using SM = S16Smem<DK, RAW>;
-    constexpr int NTS = DK / 64;
-    __shared__ __attribute__((aligned(16))) half_t smem[SM::HALFS];
+    using L = SD<DK, RAW, CGATE>;
+    constexpr int NPL = L::NPL;
+    constexpr int NTS = DK / 64;   // 16-row state tiles per wave
+    constexpr bool BF = RAW;       // raw bf16 operands use bf16 ops, workspace ones fp16
+    extern __shared__ __attribute__((aligned(16))) char smem[];
 
     // all column tiles of one sequence on one XCD (workgroups are dealt
     // round-robin to the 8 XCDs), so they share the chunk operands in L2
@@ -296,49 +224,145 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
     if (seq >= a.nseq) return;
     const int n0 = tile * 16;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int col = n0 + (l & 15);
+    const int i16 = l & 15, g = l >> 4;
+    const int col = n0 + i16;
+    const int ra = 16 * w + i16;
+    char* sS = smem + L::WS;
+    char* sR = smem + L::WR;
+    char* sU = smem + L::WU;
+    char* sUl = smem + L::WUL;
 
     f32x4 S[NTS];
 #pragma unroll
     for (int t = 0; t < NTS; ++t) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int row = 16 * (w * NTS + t) + 4 * (l >> 4) + j;
+            const int row = 16 * (w * NTS + t) + 4 * g + j;
             S[t][j] = a.S0 ? a.S0[((size_t)seq * DK + row) * a.Dv + col] : 0.f;
         }
-        st4_terms<RAW, SM::NPL>(smem + SM::kS + (l & 15) * SM::SP + 16 * (w * NTS + t) + 4 * (l >> 4),
-                                16 * SM::SP, S[t]);
+        st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (16 * (w * NTS + t) + 4 * g), 16 * L::SP, S[t]);
     }
+    s16_dma<DK, RAW, CGATE, CBETA>(a, smem, seq, 0, n0, w, l);
+    vmem_wait_all();
+    lds_barrier();
 
-    // Three register sets in rotation: chunk c is consumed while the loads of
-    // chunks c + 1 and c + 2 are in flight.  Fetches past the end re-read the
-    // last chunk, so every fetch is unconditional (no control-flow join makes
-    // the compiler wait on a newer set).
-    S16Regs<DK> r0, r1, r2;
-    const int last = a.NC - 1;
-    s16_fetch<DK, RAW, CGATE, CBETA>(a, r0, seq, 0, n0, w, l, tid);
-    s16_fetch<DK, RAW, CGATE, CBETA>(a, r1, seq, min(1, last), n0, w, l, tid);
-    __syncthreads();
-    for (int c = 0; c < a.NC; c += 3) {
-        s16_fetch<DK, RAW, CGATE, CBETA>(a, r2, seq, min(c + 2, last), n0, w, l, tid);
-        __builtin_amdgcn_sched_barrier(0);   // keep every prefetch load at the top
-        s16_chunk<DK, RAW, CGATE, CBETA>(a, r0, S, smem, seq, c, col, w, l, tid);
-        if (c + 1 > last) break;
-        s16_fetch<DK, RAW, CGATE, CBETA>(a, r0, seq, min(c + 3, last), n0, w, l, tid);
-        __builtin_amdgcn_sched_barrier(0);
-        s16_chunk<DK, RAW, CGATE, CBETA>(a, r1, S, smem, seq, c + 1, col, w, l, tid);
-        if (c + 2 > last) break;
-        s16_fetch<DK, RAW, CGATE, CBETA>(a, r1, seq, min(c + 4, last), n0, w, l, tid);
-        __builtin_amdgcn_sched_barrier(0);
-        s16_chunk<DK, RAW, CGATE, CBETA>(a, r2, S, smem, seq, c + 2, col, w, l, tid);
+    f32x4 Oprev = {0.f, 0.f, 0.f, 0.f};
+    int oprev_t0 = -1, oprev_Lc = 0;
+    auto store_o = [&]() {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * w + 4 * g + j;
+            if (r < oprev_Lc) {
+                const size_t oi = ((size_t)seq * a.L + oprev_t0 + r) * a.Dv + col;
+                if (a.out_bf16) static_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(Oprev[j]);
+                else static_cast<float*>(a.o)[oi] = Oprev[j];
+            }
+        }
+    };
+
+    for (int c = 0; c < a.NC; ++c) {
+        const char* buf = smem + (c & 1) * L::BUF;
+        const int t0 = c * CH;
+        const int Lc = min(CH, a.L - t0);
+        // copies for the next chunk into the other buffer (last read in the
+        // previous chunk, before its final barrier)
+        if (c + 1 < a.NC) s16_dma<DK, RAW, CGATE, CBETA>(a, smem + ((c + 1) & 1) * L::BUF, seq, c + 1, n0, w, l);
+
+        // X = Ks S and Y = Q S (rows 16w..16w+15)
+        f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const uint4 kf = lds16(tile_at<L::RB>(buf + L::KS, ra, 4 * s + g));
+            const uint4 qf = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
+#pragma unroll
+            for (int p = 0; p < NPL; ++p) {
+                const uint4 sf = lds16(sS + p * 16 * L::SP + i16 * L::SP + 2 * (32 * s + 8 * g));
+                X = mfma_raw<BF>(kf, sf, X);
+                Y = mfma_raw<BF>(qf, sf, Y);
+            }
+        }
+        // the previous chunk's output, deferred so that its store is not
+        // waited for at the end of the chunk it was computed in
+        if (oprev_t0 >= 0) store_o();
+        // R = V - g X
+        const float* gt = reinterpret_cast<const float*>(buf + L::GT);
+        f32x4 Rv, gam, lam;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * w + 4 * g + j;
+            const uint16_t vb = *reinterpret_cast<const uint16_t*>(buf + L::VT + r * 32 + 2 * i16);
+            const float vv = CBETA ? (float)__builtin_bit_cast(half_t, vb) : bf16_to_f32(vb);
+            gam[j] = CGATE ? 1.f : gt[r];
+            lam[j] = CGATE ? 1.f : gt[64 + r];
+            Rv[j] = vv - gam[j] * X[j];
+        }
+        st4_terms<false, 1>(sR + i16 * L::RP + 2 * (16 * w + 4 * g), 0, Rv);
+        lds_barrier();
+
+        // U = T^ R
+        f32x4 U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            U = mfma_raw<false>(lds16(tile_at<128>(buf + L::TT, ra, 4 * s + g)),
+                                lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
+        st4_terms<false, 1>(sU + i16 * L::RP + 2 * (16 * w + 4 * g), 0, U);
+        {
+            f32x4 Ul;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Ul[j] = lam[j] * U[j];
+            st4_terms<BF, NPL>(sUl + i16 * L::RP + 2 * (16 * w + 4 * g), 16 * L::RP, Ul);
+        }
+        lds_barrier();
+
+        // O = g Y + P U (stored during the next chunk)
+        f32x4 O;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) O[j] = gam[j] * Y[j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            O = mfma_raw<false>(lds16(tile_at<128>(buf + L::PT, ra, 4 * s + g)),
+                                lds16(sU + i16 * L::RP + 2 * (32 * s + 8 * g)), O);
+        Oprev = O;
+        oprev_t0 = t0;
+        oprev_Lc = Lc;
+
+        // S = g63 S + Kl^T (l U).  A fragment (state row rt + i16, tokens
+        // 32 s + 8 g + 0..7) from two transposed reads: lane q of each
+        // 16-lane group points at token 32 s + 8 g + (q >> 2) (+4) and key
+        // column rt + 4 (q & 3); lane i then holds column rt + i.
+#pragma unroll
+        for (int t = 0; t < NTS; ++t) {
+            const int rt = 16 * (w * NTS + t);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int tok = 32 * s + 8 * g + (i16 >> 2);
+                const int d = rt + 4 * (i16 & 3);
+                const uint2 lo4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok, d >> 3) + 2 * (d & 7));
+                const uint2 hi4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok + 4, d >> 3) + 2 * (d & 7));
+                const uint4 ka = {lo4.x, lo4.y, hi4.x, hi4.y};
+#pragma unroll
+                for (int p = 0; p < NPL; ++p)
+                    acc = mfma_raw<BF>(ka, lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g)), acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float d63 = CGATE ? gt[rt + 4 * g + j] : gt[63];
+                S[t][j] = d63 * S[t][j] + acc[j];
+            }
+            st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, S[t]);
+        }
+        vmem_wait_all();   // the next chunk's copies have landed
+        lds_barrier();
     }
+    if (oprev_t0 >= 0) store_o();
 
     if (a.S_final) {
 #pragma unroll
         for (int t = 0; t < NTS; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int row = 16 * (w * NTS + t) + 4 * (l >> 4) + j;
+                const int row = 16 * (w * NTS + t) + 4 * g + j;
                 a.S_final[((size_t)seq * DK + row) * a.Dv + col] = S[t][j];
             }
     }
@@ -347,9 +371,14 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
 template <int DK, bool CGATE, bool CBETA>
 static hipError_t launch_s16(const ChunkArgs& a, hipStream_t st) {
     constexpr bool RAW = !CGATE && !CBETA;
+    using L = SD<DK, RAW, CGATE>;
+    static_assert(L::TOTAL <= 160 * 1024, "LDS plan exceeds 160 KiB");
+    auto kern = scan16_kernel<DK, RAW, CGATE, CBETA>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+    if (e != hipSuccess) return e;
     const int NT = a.Dv / 16;
     const int groups = (a.nseq + 7) / 8;
-    hipLaunchKernelGGL((scan16_kernel<DK, RAW, CGATE, CBETA>), dim3(groups * 8 * NT), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kern, dim3(groups * 8 * NT), dim3(256), L::TOTAL, st, a);
     return hipGetLastError();
 }
 
