@@ -719,9 +719,14 @@ template <int DK, bool F32IN, bool CGATE, bool CBETA>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     const int nseq = a.nseq;
     if (a.NC > 0 && nseq > 0) {
-        dim3 g1(a.NC, a.H, a.B);
-        hipLaunchKernelGGL((prep_kernel<DK, F32IN, CGATE, CBETA>), g1, dim3(256), 0, st, a);
-        hipError_t e = hipGetLastError();
+        hipError_t e;
+        if constexpr (!F32IN && !CGATE && !CBETA) {
+            e = launch_prep16(a, DK, st);
+        } else {
+            dim3 g1(a.NC, a.H, a.B);
+            hipLaunchKernelGGL((prep_kernel<DK, F32IN, CGATE, CBETA>), g1, dim3(256), 0, st, a);
+            e = hipGetLastError();
+        }
         if (e != hipSuccess) return e;
     }
     if (nseq > 0) {

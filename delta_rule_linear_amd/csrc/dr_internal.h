@@ -58,6 +58,8 @@ struct DecodeArgs {
 
 hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                         hipStream_t st);
+// chunk preparation for bf16 inputs, scalar gate and scalar beta (dr_prep16.hip)
+hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);
 // the state scan for bf16 inputs (dr_scan16.hip)
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,

@@ -1,0 +1,242 @@
+// dr_prep16.hip -- per-chunk preparation for bf16 inputs with a scalar (or no)
+// gate and a scalar beta, on gfx950.
+//
+// For one 64-token chunk of one (batch, head) it produces what the state scan
+// needs (the chunk algebra is written out at the top of dr_chunk.hip):
+//   G_r     cumulative log gate inside the chunk; gamma_r = e^{G_r},
+//           lambda_r = e^{G_63 - G_r}                         -> workspace G
+//   A_ri  = beta_r (k_r . k_i) e^{G_r - G_i}   (i < r),   T = (I + A)^-1
+//   T^    = T Diag(beta)                                    -> workspace T (fp16)
+//   P_ri  = (q_r . k_i) e^{G_r - G_i}          (i <= r)    -> workspace P (fp16)
+// Rows past the sequence end are masked out of A and P, so their T^ rows are
+// zero and the scan's U vanishes there.
+//
+// Data path: the chunk's k and q tiles are copied once into LDS (coalesced
+// 16-byte global->LDS loads, XOR-swizzled rows).  k.k and q.k products are
+// exact on bf16 matrix cores (bf16 x bf16 products are exact in fp32).  The
+// triangular inverse is blocked in 16 x 16 tiles: diagonal tiles by a
+// 16-step column sweep in fp32, off-diagonal tiles on fp32 matrix cores,
+//   T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI,
+// one block row R at a time.
+
+#include <hip/hip_runtime.h>
+
+#include "dr_device.h"
+#include "dr_internal.h"
+
+namespace dr {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+
+// fp32 matrix core, 16 x 16 x 4: lane l holds A[l % 16][l / 16] and
+// B[l / 16][l % 16]; the accumulator layout is that of the 16x16x32 ops.
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void dma16(const void* g, char* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
+#endif
+}
+
+template <int RB>
+__device__ __forceinline__ int swz(int r) {
+    return RB == 256 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int RB>
+__device__ __forceinline__ const char* tile_at(const char* tile, int r, int piece) {
+    return tile + r * RB + 16 * (piece ^ swz<RB>(r));
+}
+
+// [64][RB]-byte tile of 16-bit values into swizzled LDS (rows >= valid read
+// row 0; those rows are masked out of every product that uses them).
+template <int RB>
+__device__ __forceinline__ void dma_tile(const uint16_t* src, size_t pitch, int valid, char* tile, int w, int l) {
+    constexpr int PPR = RB / 16;
+    constexpr int RPI = 64 / PPR;
+    constexpr int NI = 64 / RPI / 4;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int blk = w * NI + j;
+        const int r = blk * RPI + l / PPR;
+        const int rc = r < valid ? r : 0;
+        const int lp = (l % PPR) ^ swz<RB>(r);
+        dma16(src + (size_t)rc * pitch + 8 * lp, tile + blk * 1024);
+    }
+}
+
+}  // namespace
+
+// LDS plan (bytes): k tile, q tile, A (fp32), T (fp32), P (fp16), gates,
+// per-wave 16 x 16 fp32 scratch.
+template <int DK>
+struct P16 {
+    static constexpr int RB = DK * 2;
+    static constexpr int KT = 0;
+    static constexpr int QT = KT + 64 * RB;
+    static constexpr int AP = 65;                 // fp32 pitch of A and T
+    static constexpr int SA = QT + 64 * RB;
+    static constexpr int ST = SA + 64 * AP * 4;
+    static constexpr int PP = 72;                 // fp16 pitch of P
+    static constexpr int SPm = ST + 64 * AP * 4;
+    static constexpr int SG = SPm + 64 * PP * 2;  // G[64], beta[64]
+    static constexpr int SX = SG + 128 * 4;       // [4][16][17] fp32
+    static constexpr int TOTAL = SX + 4 * 16 * 17 * 4;
+};
+
+template <int DK>
+__global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
+    using L = P16<DK>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float(*sA)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::SA);
+    float(*sT)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::ST);
+    half_t(*sP)[L::PP] = reinterpret_cast<half_t(*)[L::PP]>(smem + L::SPm);
+    float* sg = reinterpret_cast<float*>(smem + L::SG);
+    float* sb = sg + 64;
+    float(*sX)[16][17] = reinterpret_cast<float(*)[16][17]>(smem + L::SX);
+
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int seq = b * a.H + h;
+    const size_t cs = (size_t)seq * a.NC + c;
+    const int t0 = c * CH;
+    const int Lc = min(CH, a.L - t0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int i16 = l & 15, g = l >> 4;
+    const size_t tok0 = (size_t)seq * a.L + t0;
+
+    dma_tile<L::RB>(static_cast<const uint16_t*>(a.k) + tok0 * DK, DK, Lc, smem + L::KT, w, l);
+    dma_tile<L::RB>(static_cast<const uint16_t*>(a.q) + tok0 * DK, DK, Lc, smem + L::QT, w, l);
+    if (w == 0) {
+        const int lc = l < Lc ? l : 0;
+        float gl = a.has_gate ? a.log_alpha[tok0 + lc] : 0.f;
+        gl = l < Lc ? gl : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gl, off);
+            if (l >= off) gl += y;
+        }
+        const float bl = a.beta[tok0 + lc];
+        sg[l] = gl;
+        sb[l] = l < Lc ? bl : 0.f;
+        const float g63 = __shfl(gl, 63);
+        a.wsG[cs * kGW + l] = expf(gl);             // gamma_r
+        a.wsG[cs * kGW + 64 + l] = expf(g63 - gl);  // lambda_r
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies landed
+    __syncthreads();
+
+    // A and P, 16 x 16 blocks on the bf16 matrix cores: 10 lower blocks each,
+    // 20 jobs, 5 per wave
+    for (int job = w; job < 20; job += 4) {
+        const bool isP = job >= 10;
+        const int pr = isP ? job - 10 : job;
+        // lower block pairs (R, I), R >= I: 0,0 1,0 1,1 2,0 2,1 2,2 3,0 3,1 3,2 3,3
+        const int R = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
+        const int I = pr - R * (R + 1) / 2;
+        const char* rows = smem + (isP ? L::QT : L::KT);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) {
+            const uint4 fa = *reinterpret_cast<const uint4*>(tile_at<L::RB>(rows, 16 * R + i16, 4 * s + g));
+            const uint4 fb = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::KT, 16 * I + i16, 4 * s + g));
+            acc = mfma_bf16(fa, fb, acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
+            const bool in = r < Lc && i <= r;
+            const float v = in ? acc[j] * expf(sg[r] - sg[i]) : 0.f;
+            if (isP) sP[r][i] = (half_t)v;
+            else sA[r][i] = (i < r) ? v * sb[r] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // diagonal 16 x 16 blocks of T: wave w inverts block w by a column sweep,
+    // lane j < 16 owns column j (16 dependent steps, the updates within a
+    // step are independent)
+    if (l < 16) {
+        const int base = 16 * w, j = l;
+        float acc[16], t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            t[i] = (i == j ? 1.f : 0.f) - acc[i];
+            if (i < j) t[i] = 0.f;
+#pragma unroll
+            for (int r = i + 1; r < 16; ++r) acc[r] += sA[base + r][base + i] * t[i];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[base + r][base + j] = t[r];
+    }
+    __syncthreads();
+
+    // off-diagonal blocks, block row R = 1..3; wave I < R computes T_RI:
+    //   X = sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .],  T_RI = -T_RR X
+    for (int R = 1; R < 4; ++R) {
+        if (w < R) {
+            const int I = w;
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4 * (R - I); ++s) {
+                const int m = 16 * I + 4 * s + g;
+                X = mfma_f32(sA[16 * R + i16][m], sT[m][16 * I + i16], X);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sX[w][4 * g + j][i16] = X[j];
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's scratch is written
+            __builtin_amdgcn_wave_barrier();
+            asm volatile("" ::: "memory");
+            f32x4 Tn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                Tn = mfma_f32(sT[16 * R + i16][16 * R + 4 * s + g], sX[w][4 * s + g][i16], Tn);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sT[16 * R + 4 * g + j][16 * I + i16] = -Tn[j];
+        }
+        __syncthreads();
+    }
+
+    // outputs: T^ = T Diag(beta) and P, lower triangles, fp16
+    {
+        const int r = tid >> 2, i0 = 16 * (tid & 3);
+        half8 tv[2], pv[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int i = i0 + j;
+            tv[j >> 3][j & 7] = (half_t)((i <= r) ? sT[r][i] * sb[i] : 0.f);
+            pv[j >> 3][j & 7] = (i <= r) ? sP[r][i] : (half_t)0.f;
+        }
+        const size_t base = cs * (size_t)(CH * CH) + (size_t)r * CH + i0;
+        *reinterpret_cast<half8*>(a.wsT + base) = tv[0];
+        *reinterpret_cast<half8*>(a.wsT + base + 8) = tv[1];
+        *reinterpret_cast<half8*>(a.wsP + base) = pv[0];
+        *reinterpret_cast<half8*>(a.wsP + base + 8) = pv[1];
+    }
+}
+
+template <int DK>
+static hipError_t launch_p16(const ChunkArgs& a, hipStream_t st) {
+    using L = P16<DK>;
+    auto kern = prep16_kernel<DK>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(a.NC, a.H, a.B), dim3(256), L::TOTAL, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st) {
+    return Dk == 64 ? launch_p16<64>(a, st) : launch_p16<128>(a, st);
+}
+
+}  // namespace dr
