@@ -207,6 +207,50 @@ __device__ __forceinline__ void s16_dma(const ChunkArgs& a, char* buf, int seq, 
     }
 }
 
+// How many chunks ahead the L2 is warmed (see s16_warm).
+#ifndef DR_SCAN_PFD
+#define DR_SCAN_PFD 3
+#endif
+
+// Warm L2 with chunk cc's operands: each workgroup of a sequence touches one
+// dword in a 1/NT share of the chunk's 128-byte operand lines (two per
+// thread), so the lines are already on their way from HBM when the copies
+// into LDS ask for them.  The caller keeps the loaded values until its
+// end-of-chunk wait for all vector memory, so no extra wait is ever taken.
+template <int DK, bool RAW, bool CGATE, bool CBETA>
+__device__ __forceinline__ void s16_warm(const ChunkArgs& a, int seq, int cc, int li, float& w0, float& w1) {
+    const int t0 = cc * CH;
+    const int Lc = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const size_t cs = (size_t)seq * a.NC + cc;
+    const size_t ob = cs * (size_t)(CH * DK) * 2;   // byte offset of a workspace operand tile
+    const int nraw = (Lc * DK * 2 + 127) >> 7;
+    const char* p0 = nullptr;
+    const char* p1 = nullptr;
+    int x0 = li, x1 = li + 256 * (a.Dv / 16);
+    auto region = [&](const void* base, int n) {
+        if (!p0 && x0 >= 0 && x0 < n) p0 = static_cast<const char*>(base) + 128 * x0;
+        if (!p1 && x1 >= 0 && x1 < n) p1 = static_cast<const char*>(base) + 128 * x1;
+        x0 -= n;
+        x1 -= n;
+    };
+    if constexpr (RAW) {
+        region(static_cast<const char*>(a.k) + tok0 * DK * 2, nraw);
+        region(static_cast<const char*>(a.q) + tok0 * DK * 2, nraw);
+    } else {
+        region(reinterpret_cast<const char*>(CGATE ? a.wsKl : a.wsKs) + ob, DK);
+        if constexpr (CGATE) region(reinterpret_cast<const char*>(a.wsKs) + ob, DK);
+        region(reinterpret_cast<const char*>(a.wsQ) + ob, DK);
+    }
+    region(a.wsT + cs * (CH * CH), CH * CH * 2 / 128);
+    region(a.wsP + cs * (CH * CH), CH * CH * 2 / 128);
+    if constexpr (CBETA) region(reinterpret_cast<const char*>(a.wsV) + ob, DK);
+    else region(static_cast<const char*>(a.v) + tok0 * a.Dv * 2, (Lc * a.Dv * 2 + 127) >> 7);
+    region(a.wsG + cs * kGW, kGW * 4 / 128);
+    w0 = p0 ? *reinterpret_cast<const float*>(p0) : 0.f;
+    w1 = p1 ? *reinterpret_cast<const float*>(p1) : 0.f;
+}
+
 template <int DK, bool RAW, bool CGATE, bool CBETA>
 __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
     using L = SD<DK, RAW, CGATE>;
@@ -267,6 +311,9 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
         // copies for the next chunk into the other buffer (last read in the
         // previous chunk, before its final barrier)
         if (c + 1 < a.NC) s16_dma<DK, RAW, CGATE, CBETA>(a, smem + ((c + 1) & 1) * L::BUF, seq, c + 1, n0, w, l);
+        float warm0 = 0.f, warm1 = 0.f;
+        if (DR_SCAN_PFD > 1 && c + DR_SCAN_PFD < a.NC)
+            s16_warm<DK, RAW, CGATE, CBETA>(a, seq, c + DR_SCAN_PFD, tile + NT * tid, warm0, warm1);
 
         // X = Ks S and Y = Q S (rows 16w..16w+15)
         f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
@@ -353,6 +400,7 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
             st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, S[t]);
         }
         vmem_wait_all();   // the next chunk's copies have landed
+        asm volatile("" ::"v"(warm0), "v"(warm1));
         lds_barrier();
     }
     if (oprev_t0 >= 0) store_o();
