@@ -6,17 +6,34 @@
 A step is one dr_chunk_fwd over the headline batch: Gated DeltaNet gating
 (scalar log alpha ~ U(-0.1, -0.001), scalar beta = sigmoid(N(0,1)), q and k
 L2-normalised, bf16 q/k/v, fp32 S0 ~ N(0, 0.01), fp32 output), B=2, H=16,
-L=16384, d_k=d_v=128.  `value` is tokens/s of that step (B*L per step).
-The same run also times the recurrent decode: 512 consecutive dr_decode_step
-calls on 256 sequences x 16 heads of 128x128 fp32 states with bf16 tokens,
-reported as HBM GB/s under "decode".  Inputs are synthetic, seeded, and
-resident in device memory before any timed region.  One JSON line is printed.
+L=16384, d_k=d_v=128.  `value` is tokens/s of that step (B*L per step), from
+HIP events around each step on the launch stream; between steps (outside the
+timed events) a 512 MiB buffer is rewritten so that no input is served from
+the 256 MB last-level cache.
+
+Also reported in the same line:
+  roofline      the dominant kernel (the state scan) against HBM bandwidth,
+                with its duration from per-kernel events recorded by the
+                library during the timed steps;
+  mfma          the whole forward's algorithmic flops against bf16 MFMA peak;
+  decode        512 consecutive dr_decode_step calls on 256 sequences x 16
+                heads of 128x128 fp32 states (bf16 tokens, GDN gating);
+  configs       the other forward workloads (FG2-GDN at the headline shape,
+                KDA, GDN at L=4K and 64K), a few steps each;
+  cpu_baseline  the fp64 CPU oracle on the whole headline batch, on the
+                host's cores, with the GPU result checked against it.
+The headline inputs follow the seeded NumPy recipe of
+delta_rule_linear_amd.inputs; decode and the extra workloads draw the same
+distributions with a seeded on-device generator (their values only matter
+for timing there).  One JSON line is printed.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,15 +44,31 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix peak, TFLOP/s
-# algorithmic work per token-head of the chunked forward at d = 128, chunk 64:
-# 2 * (5 C d + 3 d^2) flops; bytes = q, k, v bf16 (768) + o fp32 (512) + log alpha
-# and beta fp32 (8) + S0 and S_final amortised over L (2 * 64 KiB / L)
-FLOPS_PER_TOKEN_HEAD = 2 * (5 * 64 * 128 + 3 * 128 * 128)
-DECODE_BYTES_PER_STATE = 2 * 128 * 128 * 4 + 3 * 128 * 2 + 4 + 4 + 128 * 4
+CH = 64                        # chunk length
+# algorithmic work of the chunked forward per token-head at d_k = d_v = d:
+# 2 (5 C d + 3 d^2) flops (K K^T, Q K^T, W, U, P V' as full C x C tiles; W S,
+# Q S, K^T V'); bytes: q, k, v once, o once, the gate and beta, S0 and
+# S_final amortised over L.
+def flops_per_token_head(d: int) -> int:
+    return 2 * (5 * CH * d + 3 * d * d)
 
 
-def chunk_bytes_per_token_head(L: int) -> float:
-    return 3 * 128 * 2 + 128 * 4 + 4 + 4 + 2 * 128 * 128 * 4 / L
+def fwd_bytes_per_token_head(d: int, L: int, in_bytes: int = 2, gate_floats: int = 1,
+                             beta_floats: int = 1) -> float:
+    return 3 * d * in_bytes + d * 4 + 4 * gate_floats + 4 * beta_floats + 2 * d * d * 4 / L
+
+
+# the state scan alone (bf16 inputs, scalar gate and beta): q, k, v read once,
+# T^ and P (64 x 64 fp16 per chunk, so 2 * 64 * 2 bytes per token), the gate
+# factors (2 fp32 per token), o written once, S0 and S_final amortised
+def scan_bytes_per_token_head(d: int, L: int) -> float:
+    return 3 * d * 2 + 2 * CH * 2 + 2 * 4 + d * 4 + 2 * d * d * 4 / L
+
+
+# decode, per state: S read and written once (fp32), q, k, v (bf16), the gate
+# and beta (fp32), o (fp32)
+def decode_bytes_per_state(d: int) -> int:
+    return 2 * d * d * 4 + 3 * d * 2 + 4 + 4 + d * 4
 
 
 def parse():
@@ -44,15 +77,47 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--config-steps", type=int, default=5,
+                    help="timed steps per extra workload (0 skips them)")
+    ap.add_argument("--no-flush", action="store_true", help="do not rewrite the 512 MiB buffer between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+SCAN_SOURCES = ["delta_rule_linear_amd/csrc/dr_scan16.hip", "delta_rule_linear_amd/csrc/dr_device.h",
+                "delta_rule_linear_amd/csrc/dr_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan16_gdn_b2h16_16k_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per scan launch from the committed counter summary, or None
+    when the scan's sources changed since the counters were taken."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_hash") != source_hash(SCAN_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -63,6 +128,26 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     drl.lib()
+    stream = torch.cuda.current_stream()
+    flush_buf = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+
+    def time_steps(fn, steps, warmup):
+        """Per-step event times (ms), the cache rewritten between steps."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            flush()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
 
     def to_dev(a, bf16=False):
         if a is None:
@@ -71,9 +156,8 @@ def main():
             return torch.from_numpy(inputs.bf16_bits(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
 
-    # ------------------------------------------------------------ chunked forward
-    name = "gdn_b2h16_16k"
-    p = inputs.workload(name)
+    # ------------------------------------------------------------ headline forward
+    p = inputs.workload("gdn_b2h16_16k")
     B, H, L, D = p.B, p.H, p.L, p.Dk
     q, k, v = to_dev(p.q, True), to_dev(p.k, True), to_dev(p.v, True)
     la, be, S0 = to_dev(p.log_alpha), to_dev(p.beta), to_dev(p.S0)
@@ -89,89 +173,145 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]   # ms per call
-    ms = float(np.mean(per))
+    t_wall = time.perf_counter()
+    drl.dr_profile_begin()
+    per = time_steps(step, args.steps, 0)
+    prof = drl.dr_profile_end()
+    wall = time.perf_counter() - t_wall
+    ms = float(np.median(per))
     tok_s = B * L / (ms * 1e-3)
     token_heads = B * H * L
-    alg_bytes = chunk_bytes_per_token_head(L) * token_heads
-    alg_flops = FLOPS_PER_TOKEN_HEAD * token_heads
-    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    alg_flops = flops_per_token_head(D) * token_heads
     tflops = alg_flops / (ms * 1e-3) / 1e12
+    fwd_bytes = fwd_bytes_per_token_head(D, L) * token_heads
+    scan_ms = prof["scan_ms"] / max(1, prof["chunk_calls"])
+    prep_ms = prof["prep_ms"] / max(1, prof["chunk_calls"])
+    scan_bytes = scan_bytes_per_token_head(D, L) * token_heads
+    scan_gbs = scan_bytes / (scan_ms * 1e-3) / 1e9
 
     # ------------------------------------------------------------ decode
+    gen = torch.Generator(device=dev)
+
+    def l2n(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
     dec = None
     if args.decode_steps > 0:
-        dp = inputs.make_decode_problem(256, 16, 128, 128, args.decode_steps)
-        S = to_dev(dp.S)
-        dq, dk, dv_ = to_dev(dp.q, True), to_dev(dp.k, True), to_dev(dp.v, True)
-        dla, dbe = to_dev(dp.log_alpha), to_dev(dp.beta)
-        do = torch.empty((dp.steps, 256, 16, 128), dtype=torch.float32, device=dev)
-        ddesc = drl.DecodeDesc(256, 16, 128, 128, drl.DR_BF16, drl.DR_F32, drl.GATES["scalar"],
-                               drl.BETAS["scalar"])
-        lib = drl.lib()
+        gen.manual_seed(0)
+        N, Hd, T = 256, 16, args.decode_steps
+        S = torch.randn((N, Hd, D, D), generator=gen, device=dev) * 0.1
+        dq = l2n(torch.randn((T, N, Hd, D), generator=gen, device=dev)).bfloat16()
+        dk = l2n(torch.randn((T, N, Hd, D), generator=gen, device=dev)).bfloat16()
+        dv_ = torch.randn((T, N, Hd, D), generator=gen, device=dev).bfloat16()
+        dla = torch.rand((T, N, Hd), generator=gen, device=dev) * (-0.001 + 0.1) - 0.1
+        dbe = torch.sigmoid(torch.randn((T, N, Hd), generator=gen, device=dev))
+        do = torch.empty((T, N, Hd, D), dtype=torch.float32, device=dev)
+        # direct C-ABI calls with the pointers marshalled once, so that the
+        # host keeps ahead of the ~80 us kernels
         import ctypes
+        lib = drl.lib()
+        ddesc = drl.DecodeDesc(N, Hd, D, D, drl.DR_BF16, drl.DR_F32, drl.GATES["scalar"], drl.BETAS["scalar"])
+        dref = ctypes.byref(ddesc)
+        sptr = stream.cuda_stream
+        args_t = [(dq[t].data_ptr(), dk[t].data_ptr(), dv_[t].data_ptr(), dla[t].data_ptr(),
+                   dbe[t].data_ptr(), do[t].data_ptr()) for t in range(T)]
 
-        def dstep(t):
-            rc = lib.dr_decode_step(ctypes.byref(ddesc), dq[t].data_ptr(), dk[t].data_ptr(),
-                                    dv_[t].data_ptr(), dla[t].data_ptr(), dbe[t].data_ptr(),
-                                    S.data_ptr(), do[t].data_ptr(), stream.cuda_stream)
+        def dstep(t, Sp):
+            a_ = args_t[t]
+            rc = lib.dr_decode_step(dref, a_[0], a_[1], a_[2], a_[3], a_[4], Sp, a_[5], sptr)
             if rc:
                 raise drl.DeltaRuleError(rc, drl.dr_last_error())
 
         Swarm = S.clone()
-        for t in range(min(3, dp.steps)):     # warm-up on a scratch copy of the states
-            rc = lib.dr_decode_step(ctypes.byref(ddesc), dq[t].data_ptr(), dk[t].data_ptr(),
-                                    dv_[t].data_ptr(), dla[t].data_ptr(), dbe[t].data_ptr(),
-                                    Swarm.data_ptr(), do[t].data_ptr(), stream.cuda_stream)
-        del Swarm
+        for t in range(min(3, T)):
+            dstep(t, Swarm.data_ptr())
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        Sp = S.data_ptr()
         e0.record(stream)
-        for t in range(dp.steps):
-            dstep(t)
+        for t in range(T):
+            dstep(t, Sp)
         e1.record(stream)
         torch.cuda.synchronize()
-        dms = e0.elapsed_time(e1) / dp.steps
-        dbytes = DECODE_BYTES_PER_STATE * 256 * 16
-        dgbs = dbytes / (dms * 1e-3) / 1e9
-        dec = {"workload": "256 sequences x 16 heads, 128x128 fp32 states, bf16 tokens, GDN gating",
-               "steps": dp.steps, "us_per_step": round(dms * 1e3, 2),
-               "tokens_per_s": round(256 / (dms * 1e-3), 1),
-               "GB_per_s": round(dgbs, 1), "hbm_frac": round(dgbs / HBM_PEAK_GBS, 4),
+        dtotal = e0.elapsed_time(e1)
+        dms = dtotal / T
+        # kernel durations from per-kernel events, on a scratch copy of the states
+        drl.dr_profile_begin()
+        for t in range(min(64, T)):
+            dstep(t, Swarm.data_ptr())
+        dprof = drl.dr_profile_end()
+        del Swarm
+        dkern = dprof["decode_ms"] / max(1, dprof["decode_calls"])
+        dbytes = decode_bytes_per_state(D) * N * Hd
+        dec = {"workload": f"{N} sequences x {Hd} heads, {D}x{D} fp32 states, bf16 tokens, GDN gating",
+               "steps": T, "us_per_step": round(dms * 1e3, 2), "total_ms": round(dtotal, 3),
+               "kernel_us_mean": round(dkern * 1e3, 2),
+               "tokens_per_s": round(N / (dms * 1e-3), 1),
+               "GB_per_s": round(dbytes / (dms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "alg_bytes_per_step": dbytes}
+        del S, dq, dk, dv_, dla, dbe, do
+
+    # ------------------------------------------------------------ other forward workloads
+    configs = {}
+    extra = [
+        ("fg2_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False),
+        ("kda_b2h32_16k", 2, 32, 16384, "channel", "scalar", (-0.2, -0.0005), False),
+        ("gdn_b4h16_4k", 4, 16, 4096, "scalar", "scalar", (-0.1, -0.001), True),
+        ("gdn_b1h16_64k", 1, 16, 65536, "scalar", "scalar", (-0.1, -0.001), True),
+    ]
+    for name, b_, h_, l_, gate, bmode, rng, s0 in (extra if args.config_steps > 0 else []):
+        gen.manual_seed(0)
+        xq = l2n(torch.randn((b_, h_, l_, D), generator=gen, device=dev)).bfloat16()
+        xk = l2n(torch.randn((b_, h_, l_, D), generator=gen, device=dev)).bfloat16()
+        xv = torch.randn((b_, h_, l_, D), generator=gen, device=dev).bfloat16()
+        gshape = (b_, h_, l_) if gate == "scalar" else (b_, h_, l_, D)
+        xla = torch.rand(gshape, generator=gen, device=dev) * (rng[1] - rng[0]) + rng[0]
+        bshape = (b_, h_, l_) if bmode == "scalar" else (b_, h_, l_, D)
+        xbe = torch.sigmoid(torch.randn(bshape, generator=gen, device=dev))
+        xS0 = torch.randn((b_, h_, D, D), generator=gen, device=dev) * 0.1 if s0 else None
+        xo = torch.empty((b_, h_, l_, D), dtype=torch.float32, device=dev)
+        xSf = torch.empty((b_, h_, D, D), dtype=torch.float32, device=dev)
+        xdesc = drl.chunk_desc(b_, h_, l_, D, D, drl.DR_BF16, drl.DR_F32, gate, bmode)
+        xws = torch.empty(drl.dr_chunk_fwd_workspace_bytes(xdesc), dtype=torch.uint8, device=dev)
+
+        def xstep():
+            drl.dr_chunk_fwd(xq, xk, xv, xla, xbe, xS0, gate=gate, beta_mode=bmode, o=xo, S_final=xSf,
+                             workspace=xws)
+
+        drl.dr_profile_begin()
+        xper = time_steps(xstep, args.config_steps, 2)
+        xprof = drl.dr_profile_end()
+        xms = float(np.median(xper))
+        th = b_ * h_ * l_
+        calls = max(1, xprof["chunk_calls"])
+        configs[name] = {
+            "shape": f"B={b_} H={h_} L={l_} d={D}, gate {gate}, beta {bmode}",
+            "ms_per_step": round(xms, 4), "tokens_per_s": round(b_ * l_ / (xms * 1e-3), 1),
+            "prep_ms": round(xprof["prep_ms"] / calls, 4), "scan_ms": round(xprof["scan_ms"] / calls, 4),
+            "mfma_frac": round(flops_per_token_head(D) * th / (xms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "hbm_frac": round(fwd_bytes_per_token_head(D, l_, 2, 1 if gate == "scalar" else D,
+                                                       1 if bmode == "scalar" else D) * th
+                              / (xms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del xq, xk, xv, xla, xbe, xS0, xo, xSf, xws
+    torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline (oracle)
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
         import oracle
-        nthr = len(os.sched_getaffinity(0))
-        heads = [(0, h) for h in range(min(H, max(1, nthr)))]
-        sub = p.head(0, 0)
-        sl = slice(heads[0][1], heads[-1][1] + 1)
-        sub.H = len(heads)
-        for fld in ("q", "k", "v", "log_alpha", "beta", "S0"):
-            setattr(sub, fld, getattr(p, fld)[0:1, sl])
+        nthr = min(oracle.max_threads(), len(os.sched_getaffinity(0)))
         tc = time.perf_counter()
-        oy, Sy = oracle.forward_problem(sub, nthreads=nthr)
+        oy, Sy = oracle.forward_problem(p, nthreads=nthr)
         tcpu = time.perf_counter() - tc
-        th = len(heads) * L
-        cpu = {"value": round(th / tcpu / H, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
-               "sample": f"heads (b=0, h={heads[0][1]}..{heads[-1][1]}) of the B=2 H=16 L=16384 "
-                         f"workload at full length, fp64, {tcpu:.1f} s; tokens/s = token-heads/s / H"}
-        og = o[0, sl].double().cpu().numpy()
-        Sg = Sf[0, sl].double().cpu().numpy()
-        parity = {"heads": len(heads), "o_max_rel_err": float(np.abs(og - oy[0]).max() / np.abs(oy[0]).max()),
-                  "S_max_rel_err": float(np.abs(Sg - Sy[0]).max() / np.abs(Sy[0]).max()), "tol": 3e-3}
+        cpu = {"value": round(B * L / tcpu, 1), "unit": "tokens/s", "cores": min(nthr, B * H), "kind": "oracle",
+               "sample": f"the whole headline batch (B={B} H={H} L={L} d={D}), fp64 token-by-token "
+                         f"recurrence, one thread per (b, h), {tcpu:.1f} s wall"}
+        og = o.double().cpu().numpy()
+        Sg = Sf.double().cpu().numpy()
+        parity = {"heads": B * H, "o_max_rel_err": float(np.abs(og - oy).max() / np.abs(oy).max()),
+                  "S_max_rel_err": float(np.abs(Sg - Sy).max() / np.abs(Sy).max()), "tol": 3e-3}
 
     out = {
         "metric": "tokens/s + % bf16 MFMA peak, chunked GDN fwd H=16 d=128 L=16K; decode GB/s",
@@ -184,19 +324,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp16 MFMA operands, fp32 accumulate/state",
+        "dtype": "bf16",
+        "precision": "bf16 inputs; bf16/fp16 matrix-core operands (state as bf16 hi+lo), fp32 accumulation, "
+                     "fp32 state and output",
         "data": "synthetic (seeded)",
         "config": {"workload": "chunked GDN forward, B=2 H=16 L=16384 d_k=d_v=128, scalar gate, "
                                "scalar beta, bf16 q/k/v, fp32 S0 and o",
-                   "global_batch": B, "seq_len": L, "heads": H, "d": D, "chunk": 64,
+                   "global_batch": B, "seq_len": L, "heads": H, "d": D, "chunk": CH,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "dr_chunk_fwd (prep_kernel + scan_kernel)",
-                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": int(alg_bytes)},
+        "roofline": {"bound": "hbm", "kernel": "scan16_kernel (inter-chunk state scan)",
+                     "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "alg_bytes_per_launch": int(scan_bytes), "kernel_ms": round(scan_ms, 4),
+                     "prep_kernel_ms": round(prep_ms, 4)},
         "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": MFMA_PEAK_TFLOPS,
-                 "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "alg_flops_per_launch": int(alg_flops)},
+                 "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "alg_flops_per_step": int(alg_flops),
+                 "hbm_frac_whole_forward": round(fwd_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "decode": dec,
+        "configs": configs,
         "cpu_baseline": cpu,
         "parity": parity,
         "wall_s_timed": round(wall, 3),

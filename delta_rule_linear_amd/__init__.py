@@ -18,13 +18,13 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 1
+DR_ABI_VERSION = 2
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
 BETAS = {"scalar": 0, "channel": 1}
 EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_decode_step", "dr_status_str",
-           "dr_last_error", "dr_abi_version")
+           "dr_last_error", "dr_abi_version", "dr_profile_begin", "dr_profile_end")
 
 
 class DeltaRuleError(RuntimeError):
@@ -39,6 +39,11 @@ class ChunkDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("L", ctypes.c_int), ("Dk", ctypes.c_int),
                 ("Dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
                 ("gate", ctypes.c_int), ("beta", ctypes.c_int)]
+
+
+class ProfileReport(ctypes.Structure):
+    _fields_ = [("chunk_calls", ctypes.c_int), ("decode_calls", ctypes.c_int), ("prep_ms", ctypes.c_double),
+                ("scan_ms", ctypes.c_double), ("decode_ms", ctypes.c_double)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -72,6 +77,10 @@ def lib() -> ctypes.CDLL:
         L.dr_last_error.restype = ctypes.c_char_p
         L.dr_abi_version.argtypes = []
         L.dr_abi_version.restype = ctypes.c_int
+        L.dr_profile_begin.argtypes = []
+        L.dr_profile_begin.restype = ctypes.c_int
+        L.dr_profile_end.argtypes = [ctypes.POINTER(ProfileReport)]
+        L.dr_profile_end.restype = ctypes.c_int
         if L.dr_abi_version() != DR_ABI_VERSION:
             raise ImportError(f"{LIB_PATH} has ABI {L.dr_abi_version()}, binding expects {DR_ABI_VERSION}")
         _lib = L
@@ -93,6 +102,18 @@ def dr_last_error() -> str:
 def _check(status: int):
     if status != DR_OK:
         raise DeltaRuleError(status, dr_last_error())
+
+
+def dr_profile_begin() -> None:
+    """Start recording per-kernel HIP events in later calls."""
+    _check(lib().dr_profile_begin())
+
+
+def dr_profile_end() -> dict:
+    """Stop recording; wait for the events and return the summed kernel times (ms)."""
+    rep = ProfileReport()
+    _check(lib().dr_profile_end(ctypes.byref(rep)))
+    return {f: getattr(rep, f) for f, _ in ProfileReport._fields_}
 
 
 # ---------------------------------------------------------------------------

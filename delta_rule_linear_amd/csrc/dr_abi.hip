@@ -8,7 +8,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <limits>
+#include <mutex>
+#include <vector>
 
 #include "../../include/deltarule.h"
 #include "dr_internal.h"
@@ -96,9 +99,78 @@ __global__ void copy_state_kernel(float* dst, const float* src, size_t n) {
         dst[i] = src ? src[i] : 0.f;
 }
 
+
+// ---------------------------------------------------------------- profiling
+struct ProfRec {
+    hipEvent_t ev;
+    int slot;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfRec> g_prof;
+hipError_t g_prof_err = hipSuccess;
+
+void prof_clear() {
+    for (auto& r : g_prof) hipEventDestroy(r.ev);
+    g_prof.clear();
+}
+
 }  // namespace
 
+namespace dr {
+void prof_mark(hipStream_t st, int slot) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e == hipSuccess) e = hipEventRecord(ev, st);
+    if (e != hipSuccess) {
+        if (g_prof_err == hipSuccess) g_prof_err = e;
+        return;
+    }
+    g_prof.push_back({ev, slot});
+}
+}  // namespace dr
+
 extern "C" {
+
+dr_status dr_profile_begin(void) {
+    g_err[0] = '\0';
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    prof_clear();
+    g_prof_err = hipSuccess;
+    g_prof_on.store(true);
+    return DR_OK;
+}
+
+dr_status dr_profile_end(dr_profile_report* report) {
+    g_err[0] = '\0';
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on.store(false);
+    if (!report) {
+        prof_clear();
+        return fail(DR_ERR_NULL, "report is NULL");
+    }
+    *report = dr_profile_report{};
+    hipError_t e = g_prof_err;
+    double ms[3] = {0, 0, 0};
+    for (size_t i = 0; e == hipSuccess && i < g_prof.size(); ++i) {
+        const int slot = g_prof[i].slot;
+        if (slot == dr::kProfPrep) ++report->chunk_calls;
+        if (slot == dr::kProfDecode) ++report->decode_calls;
+        if (slot == dr::kProfEnd || i + 1 == g_prof.size()) continue;
+        e = hipEventSynchronize(g_prof[i + 1].ev);
+        float t = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof[i].ev, g_prof[i + 1].ev);
+        if (e == hipSuccess) ms[slot] += t;
+    }
+    prof_clear();
+    if (e != hipSuccess) return fail(DR_ERR_HIP, "profiling events: %s", hipGetErrorString(e));
+    report->prep_ms = ms[dr::kProfPrep];
+    report->scan_ms = ms[dr::kProfScan];
+    report->decode_ms = ms[dr::kProfDecode];
+    return DR_OK;
+}
 
 int dr_abi_version(void) { return DR_ABI_VERSION; }
 

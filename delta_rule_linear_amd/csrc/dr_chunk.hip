@@ -720,6 +720,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     const int nseq = a.nseq;
     if (a.NC > 0 && nseq > 0) {
         hipError_t e;
+        prof_mark(st, kProfPrep);
         if constexpr (!F32IN && !CGATE && !CBETA) {
             e = launch_prep16(a, DK, st);
         } else {
@@ -730,12 +731,19 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (nseq > 0) {
-        if constexpr (!F32IN) return launch_scan16(a, DK, CGATE, CBETA, st);
-        const int NT = a.Dv / 16;
-        const int groups = (nseq + 7) / 8;
-        hipLaunchKernelGGL((scan_kernel<DK, F32IN, CGATE, CBETA>), dim3(groups * 8 * NT), dim3(256),
-                           0, st, a);
-        return hipGetLastError();
+        prof_mark(st, kProfScan);
+        hipError_t e;
+        if constexpr (!F32IN) {
+            e = launch_scan16(a, DK, CGATE, CBETA, st);
+        } else {
+            const int NT = a.Dv / 16;
+            const int groups = (nseq + 7) / 8;
+            hipLaunchKernelGGL((scan_kernel<DK, F32IN, CGATE, CBETA>), dim3(groups * 8 * NT), dim3(256),
+                               0, st, a);
+            e = hipGetLastError();
+        }
+        prof_mark(st, kProfEnd);
+        return e;
     }
     return hipSuccess;
 }

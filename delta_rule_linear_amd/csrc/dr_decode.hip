@@ -139,10 +139,14 @@ static hipError_t launch_decode_d(const DecodeArgs& a, bool cgate, bool cbeta, h
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st) {
     if ((size_t)a.N * a.H == 0) return hipSuccess;
-    if (Dk == 64) return f32in ? launch_decode_d<64, true>(a, cgate, cbeta, st)
-                               : launch_decode_d<64, false>(a, cgate, cbeta, st);
-    return f32in ? launch_decode_d<128, true>(a, cgate, cbeta, st)
-                 : launch_decode_d<128, false>(a, cgate, cbeta, st);
+    prof_mark(st, kProfDecode);
+    hipError_t e;
+    if (Dk == 64) e = f32in ? launch_decode_d<64, true>(a, cgate, cbeta, st)
+                            : launch_decode_d<64, false>(a, cgate, cbeta, st);
+    else e = f32in ? launch_decode_d<128, true>(a, cgate, cbeta, st)
+                   : launch_decode_d<128, false>(a, cgate, cbeta, st);
+    prof_mark(st, kProfEnd);
+    return e;
 }
 
 }  // namespace dr

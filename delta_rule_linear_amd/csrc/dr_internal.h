@@ -56,6 +56,11 @@ struct DecodeArgs {
     int out_bf16;
 };
 
+// Optional per-kernel timing: launchers mark the start of each kernel and the
+// end of their last one (dr_profile_begin / dr_profile_end).
+enum ProfSlot { kProfPrep = 0, kProfScan = 1, kProfDecode = 2, kProfEnd = 3 };
+void prof_mark(hipStream_t st, int slot);
+
 hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                         hipStream_t st);
 // chunk preparation for bf16 inputs, scalar gate and scalar beta (dr_prep16.hip)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 1
+#define DR_ABI_VERSION 2
 
 typedef enum {
     DR_OK = 0,
@@ -140,6 +140,28 @@ dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, con
 dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, const void* v,
                          const float* log_alpha, const float* beta, float* S, void* o,
                          void* stream);
+
+/*
+ * Per-kernel timing, for benchmarks and profiling (not part of the method).
+ * Between dr_profile_begin and dr_profile_end every dr_chunk_fwd and
+ * dr_decode_step also records HIP events on its stream around each kernel it
+ * launches; dr_profile_end waits for those events and reports the summed
+ * kernel durations (event to event, so a launch gap between two kernels of
+ * one call is counted with the earlier kernel).  Calls made while profiling
+ * must come from one host thread.  dr_profile_begin discards any earlier
+ * unreported records.  The events are created and destroyed by the library.
+ * Returns DR_ERR_NULL for a NULL report, DR_ERR_HIP if an event fails.
+ */
+typedef struct dr_profile_report {
+    int chunk_calls;    /* dr_chunk_fwd calls that launched kernels */
+    int decode_calls;   /* dr_decode_step calls that launched kernels */
+    double prep_ms;     /* chunk preparation kernel (gates, A, T, P) */
+    double scan_ms;     /* inter-chunk state scan kernel (o and S_final) */
+    double decode_ms;   /* recurrent decode kernel */
+} dr_profile_report;
+
+dr_status dr_profile_begin(void);
+dr_status dr_profile_end(dr_profile_report* report);
 
 /* Static text for a status code. */
 const char* dr_status_str(dr_status s);
