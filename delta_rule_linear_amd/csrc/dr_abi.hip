@@ -13,7 +13,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/deltarule.h"
+#include "deltarule.h"
 #include "dr_internal.h"
 
 namespace {

@@ -257,7 +257,13 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
     constexpr int NPL = L::NPL;
     constexpr int NTS = DK / 64;   // 16-row state tiles per wave
     constexpr bool BF = RAW;       // raw bf16 operands use bf16 ops, workspace ones fp16
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    // Separate LDS objects for the two operand buffers and the working area:
+    // the compiler then sees that the copies into one buffer cannot alias the
+    // reads of the other, and does not wait for the copies before every LDS
+    // access.
+    __shared__ __attribute__((aligned(16))) char lds_buf0[L::BUF];
+    __shared__ __attribute__((aligned(16))) char lds_buf1[L::BUF];
+    __shared__ __attribute__((aligned(16))) char lds_work[L::TOTAL - L::WS];
 
     // all column tiles of one sequence on one XCD (workgroups are dealt
     // round-robin to the 8 XCDs), so they share the chunk operands in L2
@@ -271,10 +277,10 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
     const int i16 = l & 15, g = l >> 4;
     const int col = n0 + i16;
     const int ra = 16 * w + i16;
-    char* sS = smem + L::WS;
-    char* sR = smem + L::WR;
-    char* sU = smem + L::WU;
-    char* sUl = smem + L::WUL;
+    char* sS = lds_work;
+    char* sR = lds_work + (L::WR - L::WS);
+    char* sU = lds_work + (L::WU - L::WS);
+    char* sUl = lds_work + (L::WUL - L::WS);
 
     f32x4 S[NTS];
 #pragma unroll
@@ -286,7 +292,7 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
         }
         st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (16 * (w * NTS + t) + 4 * g), 16 * L::SP, S[t]);
     }
-    s16_dma<DK, RAW, CGATE, CBETA>(a, smem, seq, 0, n0, w, l);
+    s16_dma<DK, RAW, CGATE, CBETA>(a, lds_buf0, seq, 0, n0, w, l);
     vmem_wait_all();
     lds_barrier();
 
@@ -304,13 +310,13 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
         }
     };
 
-    for (int c = 0; c < a.NC; ++c) {
-        const char* buf = smem + (c & 1) * L::BUF;
+    // one chunk: operands in `buf`, copies of the next chunk into `nbuf`
+    auto chunk = [&](const int c, const char* buf, char* nbuf) {
         const int t0 = c * CH;
         const int Lc = min(CH, a.L - t0);
         // copies for the next chunk into the other buffer (last read in the
         // previous chunk, before its final barrier)
-        if (c + 1 < a.NC) s16_dma<DK, RAW, CGATE, CBETA>(a, smem + ((c + 1) & 1) * L::BUF, seq, c + 1, n0, w, l);
+        if (c + 1 < a.NC) s16_dma<DK, RAW, CGATE, CBETA>(a, nbuf, seq, c + 1, n0, w, l);
         float warm0 = 0.f, warm1 = 0.f;
         if (DR_SCAN_PFD > 1 && c + DR_SCAN_PFD < a.NC)
             s16_warm<DK, RAW, CGATE, CBETA>(a, seq, c + DR_SCAN_PFD, tile + NT * tid, warm0, warm1);
@@ -402,6 +408,10 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
         vmem_wait_all();   // the next chunk's copies have landed
         asm volatile("" ::"v"(warm0), "v"(warm1));
         lds_barrier();
+    };
+    for (int c = 0; c < a.NC; c += 2) {
+        chunk(c, lds_buf0, lds_buf1);
+        if (c + 1 < a.NC) chunk(c + 1, lds_buf1, lds_buf0);
     }
     if (oprev_t0 >= 0) store_o();
 
@@ -422,11 +432,9 @@ static hipError_t launch_s16(const ChunkArgs& a, hipStream_t st) {
     using L = SD<DK, RAW, CGATE>;
     static_assert(L::TOTAL <= 160 * 1024, "LDS plan exceeds 160 KiB");
     auto kern = scan16_kernel<DK, RAW, CGATE, CBETA>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
-    if (e != hipSuccess) return e;
     const int NT = a.Dv / 16;
     const int groups = (a.nseq + 7) / 8;
-    hipLaunchKernelGGL(kern, dim3(groups * 8 * NT), dim3(256), L::TOTAL, st, a);
+    hipLaunchKernelGGL(kern, dim3(groups * 8 * NT), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
