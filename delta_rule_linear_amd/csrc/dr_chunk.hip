@@ -381,7 +381,30 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     }
 
     // --------------------------------------------------- outputs T^ and P
-    {
+    if constexpr (P == 1) {
+        // packed lower-block form (tri_off), one 8-column piece per thread and step
+        for (int e = tid; e < 2 * 320; e += 256) {
+            const bool isP = e >= 320;
+            const int x = isP ? e - 320 : e;
+            const int blk = x >> 5, r = (x >> 1) & 15, hh = x & 1;
+            const int R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+            const int I = blk - R * (R + 1) / 2;
+            const int row = 16 * R + r, c0 = 16 * I + 8 * hh;
+            half8 hv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = c0 + j;
+                float tt = 0.f;
+                if (col <= row) {
+                    tt = isP ? sP[row][col] : sT[row][col];
+                    if (!isP && !CBETA) tt *= sb[col];
+                }
+                hv[j] = (half_t)tt;
+            }
+            half_t* dst = (isP ? a.wsP : a.wsT) + cs * (size_t)(CH * CH) + tri_off(row, c0);
+            *reinterpret_cast<half8*>(dst) = hv;
+        }
+    } else {
         const int r = tid >> 2, i0 = 16 * (tid & 3);
         float tv[16], pv[16];
 #pragma unroll

@@ -13,10 +13,24 @@ namespace dr {
 // lambda[64]; channel gate: the chunk's state decay e^{G_63}[Dk])
 constexpr int kGW = 128;
 
+// Packed lower-triangular form of the 64 x 64 per-chunk matrices T^ and P for
+// bf16 inputs: the ten 16 x 16 blocks (R, I), R >= I, in the order
+// (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ..., 512 bytes each; row r of a
+// block is 32 bytes whose two 8-column halves are swapped when (r & 8), so
+// that 16 lanes reading one half of 16 consecutive rows hit distinct banks.
+// 5120 bytes per matrix, at the start of its 64 x 64 workspace slot.
+constexpr int kTriBytes = 10 * 512;
+__host__ __device__ constexpr int tri_block(int R, int I) { return R * (R + 1) / 2 + I; }
+// offset (in 16-bit elements) of element (r, c), c <= r rounded to blocks
+__host__ __device__ constexpr int tri_off(int r, int c) {
+    return tri_block(r >> 4, c >> 4) * 256 + (r & 15) * 16 + 8 * (((c >> 3) & 1) ^ ((r >> 3) & 1)) + (c & 7);
+}
+
 // Everything the chunked-forward kernels read.  Workspace planes, per chunk
 // slot cs = (b * H + h) * NC + c, with P = 1 (bf16 inputs) or 2 (fp32 inputs)
 // fp16 terms per value:
 //   wsT, wsP  [NCH][P][64][64]   T^ = (I + A)^-1 (beta-scaled columns) and P
+//                                (bf16 inputs: packed lower blocks, see tri_off)
 //   wsG       [NCH][kGW]         gate factors
 //   wsQ/Ks/Kl [NCH][P][64][Dk]   gated operands (channel gate; with a channel
 //                                beta and scalar gate Ks holds sqrt(beta) k and

@@ -207,21 +207,23 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
         __syncthreads();
     }
 
-    // outputs: T^ = T Diag(beta) and P, lower triangles, fp16
-    {
-        const int r = tid >> 2, i0 = 16 * (tid & 3);
-        half8 tv[2], pv[2];
+    // outputs: T^ = T Diag(beta) and P in the packed lower-block form, fp16;
+    // one 16-byte piece (8 columns of one block row) per thread and step
+    for (int e = tid; e < 2 * 320; e += 256) {
+        const bool isP = e >= 320;
+        const int x = isP ? e - 320 : e;
+        const int blk = x >> 5, r = (x >> 1) & 15, h = x & 1;
+        const int R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+        const int I = blk - R * (R + 1) / 2;
+        const int row = 16 * R + r, c0 = 16 * I + 8 * h;
+        half8 hv;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int i = i0 + j;
-            tv[j >> 3][j & 7] = (half_t)((i <= r) ? sT[r][i] * sb[i] : 0.f);
-            pv[j >> 3][j & 7] = (i <= r) ? sP[r][i] : (half_t)0.f;
+        for (int j = 0; j < 8; ++j) {
+            const int col = c0 + j;
+            hv[j] = col <= row ? (isP ? sP[row][col] : (half_t)(sT[row][col] * sb[col])) : (half_t)0.f;
         }
-        const size_t base = cs * (size_t)(CH * CH) + (size_t)r * CH + i0;
-        *reinterpret_cast<half8*>(a.wsT + base) = tv[0];
-        *reinterpret_cast<half8*>(a.wsT + base + 8) = tv[1];
-        *reinterpret_cast<half8*>(a.wsP + base) = pv[0];
-        *reinterpret_cast<half8*>(a.wsP + base + 8) = pv[1];
+        half_t* dst = (isP ? a.wsP : a.wsT) + cs * (size_t)(CH * CH) + tri_off(row, c0);
+        *reinterpret_cast<half8*>(dst) = hv;
     }
 }
 

@@ -4,11 +4,18 @@
 // prep kernel):  X = Ks S,  R = V - g X,  U = T^ R,  O = g Q S + P U,
 // S <- g63 S + Kl^T (l U).  Built around the data movement:
 //
-//  * Each chunk's operand tiles (Kl, Ks, Q, T^, P, the V tile, gate factors)
-//    are copied once per workgroup straight into LDS with 16-byte global->LDS
-//    loads, fully coalesced, one chunk ahead into a double buffer.  Rows of a
-//    tile are stored with their 16-byte pieces XOR-swizzled by row, so the
-//    fragment reads below are free of bank conflicts.
+//  * One workgroup per (sequence, 16-column tile of S): four compute waves
+//    and one copy wave.  The copy wave issues every global memory operation
+//    of the chunk loop: the chunk operand tiles (Kl, Ks, Q, T^, P, the V
+//    tile, gate factors) straight into LDS with 16-byte global->LDS loads,
+//    two chunks ahead into a triple buffer (double with a channel gate, whose
+//    tiles are larger), a one-dword touch of the chunk four ahead to start
+//    its HBM reads early, and the coalesced store of the previous chunk's
+//    output from LDS.  Vector-memory issue stalls (the copies are 45-61
+//    1 KiB instructions per chunk) thus never hold up the compute waves.
+//  * Rows of a K / Q tile are stored with their 16-byte pieces XOR-swizzled
+//    by row, so fragment reads are free of bank conflicts; T^ and P arrive in
+//    the packed lower-block form written by the prep kernels.
 //  * Operand types.  With a scalar beta and no channel gate, Ks = Kl = k and
 //    Q = q are the raw bf16 inputs: they feed bf16 matrix-core ops directly,
 //    with the fp32 state S and l U carried as bf16 hi + lo pairs (16
@@ -20,13 +27,15 @@
 //  * No masking: rows past a sequence's end load a valid clamped row; their
 //    U is exactly zero (beta or the prep kernel's zero rows make it so), so
 //    they contribute nothing to S, and their O is never stored.
-//  * Barriers are raw s_barrier with an explicit LDS-only wait, so the
-//    copies for the next chunk stay in flight across them; the copies are
-//    waited for once, before the chunk's last barrier.
+//  * Three barriers per chunk, all raw s_barrier with an LDS-only wait.  The
+//    copy wave waits for the copies of the next chunk just before the last
+//    one, by count, leaving the newest chunk's copies in flight.
+//  * The operand buffers and the working area are separate LDS objects, so
+//    the compiler can see that copies into one buffer never alias reads of
+//    another and inserts no waits of its own.
 //
-// One workgroup of four waves per (sequence, 16-column tile of S).  Wave w owns
-// chunk rows 16w..16w+15 for X, Y, R, U, O and state rows [DK/4 w, DK/4 (w+1))
-// for the state update.
+// Compute wave w owns chunk rows 16w..16w+15 for X, Y, R, U, O and state rows
+// [DK/4 w, DK/4 (w+1)) for the state update.
 
 #include <hip/hip_runtime.h>
 
@@ -40,6 +49,35 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+// LDS addresses are kept in the LDS address space end to end: no generic
+// pointers, so no null checks on conversion, and the compiler keeps exact
+// knowledge of which LDS object every access touches.
+typedef __attribute__((address_space(3))) char lchar;
+
+// LDS load / store of a 2-, 4-, 8- or 16-byte value through plain integer
+// (vector) types, reinterpreted to T.
+template <int N>
+struct LdsWord;
+template <>
+struct LdsWord<2> { typedef unsigned short type; };
+template <>
+struct LdsWord<4> { typedef unsigned type; };
+template <>
+struct LdsWord<8> { typedef unsigned type __attribute__((ext_vector_type(2))); };
+template <>
+struct LdsWord<16> { typedef unsigned type __attribute__((ext_vector_type(4))); };
+
+template <class T>
+__device__ __forceinline__ T lds_ld(const lchar* p) {
+    typedef typename LdsWord<sizeof(T)>::type W;
+    const W x = *reinterpret_cast<const __attribute__((address_space(3))) W*>(p);
+    return __builtin_bit_cast(T, x);
+}
+template <class T>
+__device__ __forceinline__ void lds_st(lchar* p, const T& v) {
+    typedef typename LdsWord<sizeof(T)>::type W;
+    *reinterpret_cast<__attribute__((address_space(3))) W*>(p) = __builtin_bit_cast(W, v);
+}
 
 // 16x16x32 matrix-core op on raw 16-byte fragments, bf16 or fp16 elements.
 template <bool BF>
@@ -52,12 +90,12 @@ __device__ __forceinline__ f32x4 mfma_raw(const uint4& a, const uint4& b, const 
                                                       __builtin_bit_cast(half8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint4 lds16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 lds16(const lchar* p) { return lds_ld<uint4>(p); }
 
 // Transposed LDS read of four 16-bit values.  Within each group of 16 lanes,
 // lane i receives element (i mod 4) of the 8-byte rows addressed by lanes
 // i/4, 4 + i/4, 8 + i/4 and 12 + i/4, in that order.
-__device__ __forceinline__ uint2 lds_tr4(const char* p) {
+__device__ __forceinline__ uint2 lds_tr4(const lchar* p) {
     s16x4 v = {0, 0, 0, 0};
 #if defined(__HIP_DEVICE_COMPILE__)
     v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
@@ -66,11 +104,33 @@ __device__ __forceinline__ uint2 lds_tr4(const char* p) {
 }
 
 // 16 bytes from global memory into LDS at lds_base + 16 * lane (lds_base
-// must be the same for the whole wave).
-__device__ __forceinline__ void dma16(const void* g, char* lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
-#endif
+// must be the same for the whole wave; it goes to M0).  Written as inline
+// assembly so that the compiler does not track these copies: it would
+// otherwise assume any LDS access may alias a copy in flight and wait for
+// all of them before every LDS read.  The copies have no register results;
+// their completion is waited for explicitly, by count (vmcnt_imm).  M0 is
+// saved and restored around the copy.
+__device__ __forceinline__ void dma16(const void* g, lchar* lds_base) {
+    const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(size_t)lds_base);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(m)
+        : "memory");
+}
+
+// One dword from global memory into LDS at lds_base + 4 * lane (as dma16).
+__device__ __forceinline__ void dma4(const void* g, lchar* lds_base) {
+    const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(size_t)lds_base);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(g), "s"(m)
+        : "memory");
 }
 
 // Workgroup barrier over LDS only: wait for this wave's own LDS accesses,
@@ -79,14 +139,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Wait for every vector-memory operation of this wave, including the
-// global->LDS copies.
-__device__ __forceinline__ void vmem_wait_all() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
     asm volatile("" ::: "memory");
 }
 
@@ -100,32 +152,14 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 template <int RB>
-__device__ __forceinline__ const char* tile_at(const char* tile, int r, int piece) {
+__device__ __forceinline__ const lchar* tile_at(const lchar* tile, int r, int piece) {
     return tile + r * RB + 16 * (piece ^ swz<RB>(r));
-}
-
-// Copy a [64][RB]-byte tile of 16-bit values (row r at src + r * pitch
-// elements; rows >= valid read row 0) into swizzled LDS; the four waves
-// share it, 1 KiB per instruction.
-template <int RB>
-__device__ __forceinline__ void dma_tile(const uint16_t* src, size_t pitch, int valid, char* tile, int w, int l) {
-    constexpr int PPR = RB / 16;      // pieces per row
-    constexpr int RPI = 64 / PPR;     // rows per 1 KiB instruction
-    constexpr int NI = 64 / RPI / 4;  // instructions per wave
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int blk = w * NI + j;
-        const int r = blk * RPI + l / PPR;
-        const int rc = r < valid ? r : 0;
-        const int lp = (l % PPR) ^ swz<RB>(r);
-        dma16(src + (size_t)rc * pitch + 8 * lp, tile + blk * 1024);
-    }
 }
 
 // Four fp32 values as NPL 16-bit terms (bf16 hi/lo pair, or one fp16) at
 // consecutive LDS halfs of each plane (plane stride in bytes).
 template <bool BF, int NPL>
-__device__ __forceinline__ void st4_terms(char* dst, int plane, const f32x4& v) {
+__device__ __forceinline__ void st4_terms(lchar* dst, int plane, const f32x4& v) {
     if constexpr (BF) {
         bf16x4 hi, lo;
 #pragma unroll
@@ -136,103 +170,161 @@ __device__ __forceinline__ void st4_terms(char* dst, int plane, const f32x4& v) 
             hi[j] = h;
             lo[j] = (__bf16)(x - (float)h);
         }
-        *reinterpret_cast<bf16x4*>(dst) = hi;
-        if constexpr (NPL == 2) *reinterpret_cast<bf16x4*>(dst + plane) = lo;
+        lds_st(dst, hi);
+        if constexpr (NPL == 2) lds_st(dst + plane, lo);
     } else {
         half4 hi;
 #pragma unroll
         for (int j = 0; j < 4; ++j) hi[j] = (half_t)v[j];
-        *reinterpret_cast<half4*>(dst) = hi;
+        lds_st(dst, hi);
     }
 }
 
-// LDS plan (bytes).  Two operand buffers, each
-//   [Kl 64 x RB][Ks 64 x RB, channel gate only][Q 64 x RB][T^ 64 x 128][P 64 x 128]
-//   [V 64 x 32][gate factors 512]
-// then the working area [S^T NPL x 16 x SP][R^T 16 x RP][U^T 16 x RP][(lU)^T NPL x 16 x RP].
+// s_waitcnt immediate: wait until at most n vector-memory operations of this
+// wave are outstanding (export and LDS counters not waited for).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// LDS plan (bytes).  NB operand buffers, each
+//   [Kl 64 x RB][Ks 64 x RB, channel gate only][Q 64 x RB][T^ packed][P packed]
+//   [V 64 x 32][gate factors 1024]
+// and the working area [S^T NPL x 16 x SP][R^T 16 x RP][U^T 16 x RP]
+// [(lU)^T NPL x 16 x RP][O 64 x OP].
 template <int DK, bool RAW, bool CGATE>
 struct SD {
     static constexpr int NPL = RAW ? 2 : 1;
+    static constexpr int NB = CGATE ? 2 : 3;
     static constexpr int RB = DK * 2;               // bytes per K / Q row
     static constexpr int KL = 0;
     static constexpr int KS = CGATE ? KL + 64 * RB : KL;   // Ks == Kl unless the gate is per channel
     static constexpr int QT = KS + 64 * RB;
     static constexpr int TT = QT + 64 * RB;
-    static constexpr int PT = TT + 64 * 128;
-    static constexpr int VT = PT + 64 * 128;
+    static constexpr int PT = TT + kTriBytes;
+    static constexpr int VT = PT + kTriBytes;
     static constexpr int GT = VT + 64 * 32;
-    static constexpr int BUF = GT + 512;
+    static constexpr int BUF = GT + 1024;
     static constexpr int SP = (DK + 8) * 2;          // bytes per S^T row
     static constexpr int RP = (CH + 8) * 2;          // bytes per token-major row
-    static constexpr int WS = 2 * BUF;
+    static constexpr int OP = 16 * 4 + 16;           // bytes per O row (fp32)
+    static constexpr int WS = 0;
     static constexpr int WR = WS + NPL * 16 * SP;
     static constexpr int WU = WR + 16 * RP;
     static constexpr int WUL = WU + 16 * RP;
-    static constexpr int TOTAL = WUL + NPL * 16 * RP;
+    static constexpr int WO = WUL + NPL * 16 * RP;
+    static constexpr int WORK = WO + 64 * OP;
+    static constexpr int TOTAL = NB * BUF + WORK + 1024;
+    // copy waves, and the copy instructions each issues per chunk: a quarter
+    // of every K / Q tile (RB / 16 instructions each) and four of the 16
+    // slots holding T^ (5), P (5), the V tile (2), the gate factors (1) and
+    // three repeats of the gate copy, so that every copy wave issues the same
+    // count
+    static constexpr int NCW = 4;
+    static constexpr int NCOPY = (CGATE ? 3 : 2) * (RB / 16) / NCW + 4;
 };
 
-// Issue the copies of chunk c's operands into buffer `buf`.
-template <int DK, bool RAW, bool CGATE, bool CBETA>
-__device__ __forceinline__ void s16_dma(const ChunkArgs& a, char* buf, int seq, int c, int n0, int w, int l) {
+// Copy wave cw's quarter of a [64][RB]-byte tile of 16-bit values (row r at
+// src + r * pitch elements; rows >= valid read row 0) into swizzled LDS.
+template <int RB>
+__device__ __forceinline__ void copy_tile(const uint16_t* src, size_t pitch, int valid, lchar* tile, int l, int cw) {
+    constexpr int PPR = RB / 16;      // pieces per row
+    constexpr int RPI = 64 / PPR;     // rows per 1 KiB instruction
+    constexpr int NI = 64 / RPI;      // instructions per tile
+#pragma unroll
+    for (int jj = 0; jj < NI / 4; ++jj) {
+        const int j = cw + 4 * jj;
+        const int r = j * RPI + l / PPR;
+        const int rc = r < valid ? r : 0;
+        const int lp = (l % PPR) ^ swz<RB>(r);
+        dma16(src + (size_t)rc * pitch + 8 * lp, tile + j * 1024);
+    }
+}
+
+// Part `PART` of the copies of chunk c into buffer `buf`, copy wave cw's share:
+//   0: Kl;  1: Ks (channel gate), T^, P, the V tile, the gate factors;  2: Q.
+template <int DK, bool RAW, bool CGATE, bool CBETA, int PART>
+__device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq, int c, int n0, int l, int cw) {
     using L = SD<DK, RAW, CGATE>;
     const int t0 = c * CH;
     const int Lc = min(CH, a.L - t0);
     const size_t tok0 = (size_t)seq * a.L + t0;
     const size_t cs = (size_t)seq * a.NC + c;
     const size_t obase = cs * (size_t)(CH * DK);
-    if constexpr (RAW) {
-        dma_tile<L::RB>(static_cast<const uint16_t*>(a.k) + tok0 * DK, DK, Lc, buf + L::KL, w, l);
-        dma_tile<L::RB>(static_cast<const uint16_t*>(a.q) + tok0 * DK, DK, Lc, buf + L::QT, w, l);
-    } else {
-        const half_t* kl = CGATE ? a.wsKl : a.wsKs;
-        dma_tile<L::RB>(reinterpret_cast<const uint16_t*>(kl) + obase, DK, CH, buf + L::KL, w, l);
+    if constexpr (PART == 0) {
+        if constexpr (RAW)
+            copy_tile<L::RB>(static_cast<const uint16_t*>(a.k) + tok0 * DK, DK, Lc, buf + L::KL, l, cw);
+        else
+            copy_tile<L::RB>(reinterpret_cast<const uint16_t*>(CGATE ? a.wsKl : a.wsKs) + obase, DK, CH,
+                             buf + L::KL, l, cw);
+    } else if constexpr (PART == 1) {
         if constexpr (CGATE)
-            dma_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsKs) + obase, DK, CH, buf + L::KS, w, l);
-        dma_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsQ) + obase, DK, CH, buf + L::QT, w, l);
-    }
-    const size_t tbase = cs * (size_t)(CH * CH);
-    dma_tile<128>(reinterpret_cast<const uint16_t*>(a.wsT) + tbase, CH, CH, buf + L::TT, w, l);
-    dma_tile<128>(reinterpret_cast<const uint16_t*>(a.wsP) + tbase, CH, CH, buf + L::PT, w, l);
-    if (w < 2) {   // V tile: 64 rows x 16 columns, two 16-byte pieces per row
-        const int r = 32 * w + (l >> 1), piece = l & 1;
-        if constexpr (CBETA) {
-            dma16(reinterpret_cast<const uint16_t*>(a.wsV) + obase + r * DK + n0 + 8 * piece, buf + L::VT + w * 1024);
-        } else {
-            const int rc = r < Lc ? r : 0;
-            dma16(static_cast<const uint16_t*>(a.v) + (tok0 + rc) * a.Dv + n0 + 8 * piece, buf + L::VT + w * 1024);
+            copy_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsKs) + obase, DK, CH, buf + L::KS, l, cw);
+        // slots k = cw, cw + 4, cw + 8, cw + 12 of: T^ (0-4), P (5-9), the V
+        // tile (10-11: 64 rows x 16 columns, two 16-byte pieces per row), the
+        // gate factors (12-15; lanes past the data repeat it into the unused
+        // upper part of the 1 KiB area)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int k = cw + 4 * jj;
+            if (k < 5) {
+                dma16(a.wsT + cs * (size_t)(CH * CH) + 512 * k + 8 * l, buf + L::TT + 1024 * k);
+            } else if (k < 10) {
+                dma16(a.wsP + cs * (size_t)(CH * CH) + 512 * (k - 5) + 8 * l, buf + L::PT + 1024 * (k - 5));
+            } else if (k < 12) {
+                const int hh = k - 10;
+                const int r = 32 * hh + (l >> 1), piece = l & 1;
+                if constexpr (CBETA) {
+                    dma16(reinterpret_cast<const uint16_t*>(a.wsV) + obase + r * DK + n0 + 8 * piece,
+                          buf + L::VT + hh * 1024);
+                } else {
+                    const int rc = r < Lc ? r : 0;
+                    dma16(static_cast<const uint16_t*>(a.v) + (tok0 + rc) * a.Dv + n0 + 8 * piece,
+                          buf + L::VT + hh * 1024);
+                }
+            } else {
+                constexpr int NG = CGATE ? DK / 4 : 32;
+                dma16(a.wsG + cs * kGW + 4 * (l % NG), buf + L::GT);
+            }
         }
-    } else if (w == 2) {   // gate factors: gamma[64] and lambda[64], or the state decay [DK]
-        constexpr int NG = CGATE ? DK / 4 : 32;
-        if (l < NG) dma16(a.wsG + cs * kGW + 4 * l, buf + L::GT);
+    } else {
+        if constexpr (RAW)
+            copy_tile<L::RB>(static_cast<const uint16_t*>(a.q) + tok0 * DK, DK, Lc, buf + L::QT, l, cw);
+        else
+            copy_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsQ) + obase, DK, CH, buf + L::QT, l, cw);
     }
 }
 
-// How many chunks ahead the L2 is warmed (see s16_warm).
+template <int DK, bool RAW, bool CGATE, bool CBETA>
+__device__ __forceinline__ void s16_copy_all(const ChunkArgs& a, lchar* buf, int seq, int c, int n0, int l, int cw) {
+    s16_copy<DK, RAW, CGATE, CBETA, 0>(a, buf, seq, c, n0, l, cw);
+    s16_copy<DK, RAW, CGATE, CBETA, 1>(a, buf, seq, c, n0, l, cw);
+    s16_copy<DK, RAW, CGATE, CBETA, 2>(a, buf, seq, c, n0, l, cw);
+}
+
+// How many chunks ahead of the one being computed the copy wave touches the
+// operands (see s16_warm).
 #ifndef DR_SCAN_PFD
-#define DR_SCAN_PFD 3
+#define DR_SCAN_PFD 4
 #endif
 
-// Warm L2 with chunk cc's operands: each workgroup of a sequence touches one
-// dword in a 1/NT share of the chunk's 128-byte operand lines (two per
-// thread), so the lines are already on their way from HBM when the copies
-// into LDS ask for them.  The caller keeps the loaded values until its
-// end-of-chunk wait for all vector memory, so no extra wait is ever taken.
+// Start the HBM reads of chunk cc early: each workgroup of a sequence touches
+// one dword in each of a 1/NT share of the chunk's 128-byte operand lines
+// (line li, clamped to the last line), as one global->LDS load into a
+// scratch row that is never read.  Always exactly one instruction.
 template <int DK, bool RAW, bool CGATE, bool CBETA>
-__device__ __forceinline__ void s16_warm(const ChunkArgs& a, int seq, int cc, int li, float& w0, float& w1) {
+__device__ __forceinline__ void s16_warm(const ChunkArgs& a, int seq, int cc, int li, lchar* sink) {
     const int t0 = cc * CH;
     const int Lc = min(CH, a.L - t0);
     const size_t tok0 = (size_t)seq * a.L + t0;
     const size_t cs = (size_t)seq * a.NC + cc;
     const size_t ob = cs * (size_t)(CH * DK) * 2;   // byte offset of a workspace operand tile
     const int nraw = (Lc * DK * 2 + 127) >> 7;
-    const char* p0 = nullptr;
-    const char* p1 = nullptr;
-    int x0 = li, x1 = li + 256 * (a.Dv / 16);
+    const char* p = nullptr;
+    const char* last = nullptr;
+    int x = li;
     auto region = [&](const void* base, int n) {
-        if (!p0 && x0 >= 0 && x0 < n) p0 = static_cast<const char*>(base) + 128 * x0;
-        if (!p1 && x1 >= 0 && x1 < n) p1 = static_cast<const char*>(base) + 128 * x1;
-        x0 -= n;
-        x1 -= n;
+        const char* b = static_cast<const char*>(base);
+        if (!p && x >= 0 && x < n) p = b + 128 * x;
+        last = b + 128 * (n - 1);
+        x -= n;
     };
     if constexpr (RAW) {
         region(static_cast<const char*>(a.k) + tok0 * DK * 2, nraw);
@@ -242,28 +334,29 @@ __device__ __forceinline__ void s16_warm(const ChunkArgs& a, int seq, int cc, in
         if constexpr (CGATE) region(reinterpret_cast<const char*>(a.wsKs) + ob, DK);
         region(reinterpret_cast<const char*>(a.wsQ) + ob, DK);
     }
-    region(a.wsT + cs * (CH * CH), CH * CH * 2 / 128);
-    region(a.wsP + cs * (CH * CH), CH * CH * 2 / 128);
+    region(a.wsT + cs * (CH * CH), kTriBytes / 128);
+    region(a.wsP + cs * (CH * CH), kTriBytes / 128);
     if constexpr (CBETA) region(reinterpret_cast<const char*>(a.wsV) + ob, DK);
     else region(static_cast<const char*>(a.v) + tok0 * a.Dv * 2, (Lc * a.Dv * 2 + 127) >> 7);
     region(a.wsG + cs * kGW, kGW * 4 / 128);
-    w0 = p0 ? *reinterpret_cast<const float*>(p0) : 0.f;
-    w1 = p1 ? *reinterpret_cast<const float*>(p1) : 0.f;
+    dma4(p ? p : last, sink);
 }
 
 template <int DK, bool RAW, bool CGATE, bool CBETA>
-__global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
     using L = SD<DK, RAW, CGATE>;
+    constexpr int NB = L::NB;
     constexpr int NPL = L::NPL;
-    constexpr int NTS = DK / 64;   // 16-row state tiles per wave
+    constexpr int NTS = DK / 64;   // 16-row state tiles per compute wave
     constexpr bool BF = RAW;       // raw bf16 operands use bf16 ops, workspace ones fp16
-    // Separate LDS objects for the two operand buffers and the working area:
-    // the compiler then sees that the copies into one buffer cannot alias the
-    // reads of the other, and does not wait for the copies before every LDS
-    // access.
-    __shared__ __attribute__((aligned(16))) char lds_buf0[L::BUF];
-    __shared__ __attribute__((aligned(16))) char lds_buf1[L::BUF];
-    __shared__ __attribute__((aligned(16))) char lds_work[L::TOTAL - L::WS];
+    // Separate LDS objects for the operand buffers and the working area: the
+    // compiler then sees that copies into one buffer cannot alias the reads
+    // of another, and does not wait for copies before every LDS access.
+    __shared__ __attribute__((aligned(16))) char lds_b0[L::BUF];
+    __shared__ __attribute__((aligned(16))) char lds_b1[L::BUF];
+    __shared__ __attribute__((aligned(16))) char lds_b2[NB == 3 ? L::BUF : 16];
+    __shared__ __attribute__((aligned(16))) char lds_work[L::WORK];
+    __shared__ __attribute__((aligned(16))) char lds_sink[1024];
 
     // all column tiles of one sequence on one XCD (workgroups are dealt
     // round-robin to the 8 XCDs), so they share the chunk operands in L2
@@ -274,92 +367,127 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
     if (seq >= a.nseq) return;
     const int n0 = tile * 16;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const bool copier = w >= 4;   // waves 4-7 copy, 0-3 compute (wave-uniform)
+    const int cw = __builtin_amdgcn_readfirstlane(w - 4);
     const int i16 = l & 15, g = l >> 4;
     const int col = n0 + i16;
     const int ra = 16 * w + i16;
-    char* sS = lds_work;
-    char* sR = lds_work + (L::WR - L::WS);
-    char* sU = lds_work + (L::WU - L::WS);
-    char* sUl = lds_work + (L::WUL - L::WS);
+    lchar* b0 = (lchar*)lds_b0;
+    lchar* b1 = (lchar*)lds_b1;
+    lchar* b2 = (lchar*)lds_b2;
+    lchar* work = (lchar*)lds_work;
+    lchar* sink = (lchar*)lds_sink;
+    lchar* sS = work + L::WS;
+    lchar* sR = work + L::WR;
+    lchar* sU = work + L::WU;
+    lchar* sUl = work + L::WUL;
+    lchar* sO = work + L::WO;
 
-    f32x4 S[NTS];
-#pragma unroll
-    for (int t = 0; t < NTS; ++t) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * (w * NTS + t) + 4 * g + j;
-            S[t][j] = a.S0 ? a.S0[((size_t)seq * DK + row) * a.Dv + col] : 0.f;
-        }
-        st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (16 * (w * NTS + t) + 4 * g), 16 * L::SP, S[t]);
-    }
-    s16_dma<DK, RAW, CGATE, CBETA>(a, lds_buf0, seq, 0, n0, w, l);
-    vmem_wait_all();
-    lds_barrier();
-
-    f32x4 Oprev = {0.f, 0.f, 0.f, 0.f};
-    int oprev_t0 = -1, oprev_Lc = 0;
-    auto store_o = [&]() {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * w + 4 * g + j;
-            if (r < oprev_Lc) {
-                const size_t oi = ((size_t)seq * a.L + oprev_t0 + r) * a.Dv + col;
-                if (a.out_bf16) static_cast<uint16_t*>(a.o)[oi] = f32_to_bf16(Oprev[j]);
-                else static_cast<float*>(a.o)[oi] = Oprev[j];
-            }
-        }
+    // coalesced store of chunk cc's output tile from sO: copy wave cw stores
+    // rows 16 cw .. 16 cw + 15.  Both output types are formed and the store
+    // is chosen by predicate (a branch on the type here trips the gfx950
+    // backend).
+    auto store_o = [&](int cc) {
+        const int t0 = cc * CH;
+        const int Lc = min(CH, a.L - t0);
+        const int q4 = l & 3;
+        const int row = 16 * cw + (l >> 2);
+        float* of = static_cast<float*>(a.o);
+        uint16_t* ob = static_cast<uint16_t*>(a.o);
+        const bool bf = a.out_bf16;
+        const float4 v = lds_ld<float4>(sO + row * L::OP + 16 * q4);
+        const size_t oi = ((size_t)seq * a.L + t0 + row) * a.Dv + n0 + 4 * q4;
+        const uint2 pk = {(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                          (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+        if (row < Lc && bf) *reinterpret_cast<uint2*>(ob + oi) = pk;
+        if (row < Lc && !bf) *reinterpret_cast<float4*>(of + oi) = v;
     };
 
-    // one chunk: operands in `buf`, copies of the next chunk into `nbuf`
-    auto chunk = [&](const int c, const char* buf, char* nbuf) {
-        const int t0 = c * CH;
-        const int Lc = min(CH, a.L - t0);
-        // copies for the next chunk into the other buffer (last read in the
-        // previous chunk, before its final barrier)
-        if (c + 1 < a.NC) s16_dma<DK, RAW, CGATE, CBETA>(a, nbuf, seq, c + 1, n0, w, l);
-        float warm0 = 0.f, warm1 = 0.f;
-        if (DR_SCAN_PFD > 1 && c + DR_SCAN_PFD < a.NC)
-            s16_warm<DK, RAW, CGATE, CBETA>(a, seq, c + DR_SCAN_PFD, tile + NT * tid, warm0, warm1);
-
-        // X = Ks S and Y = Q S (rows 16w..16w+15)
-        f32x4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+    f32x4 S[NTS];
+    if (!copier) {
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            const uint4 kf = lds16(tile_at<L::RB>(buf + L::KS, ra, 4 * s + g));
-            const uint4 qf = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
+        for (int t = 0; t < NTS; ++t) {
 #pragma unroll
-            for (int p = 0; p < NPL; ++p) {
-                const uint4 sf = lds16(sS + p * 16 * L::SP + i16 * L::SP + 2 * (32 * s + 8 * g));
-                X = mfma_raw<BF>(kf, sf, X);
-                Y = mfma_raw<BF>(qf, sf, Y);
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * (w * NTS + t) + 4 * g + j;
+                S[t][j] = a.S0 ? a.S0[((size_t)seq * DK + row) * a.Dv + col] : 0.f;
             }
+            st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (16 * (w * NTS + t) + 4 * g), 16 * L::SP, S[t]);
         }
-        // the previous chunk's output, deferred so that its store is not
-        // waited for at the end of the chunk it was computed in
-        if (oprev_t0 >= 0) store_o();
-        // R = V - g X
-        const float* gt = reinterpret_cast<const float*>(buf + L::GT);
-        f32x4 Rv, gam, lam;
+    } else {
+        s16_copy_all<DK, RAW, CGATE, CBETA>(a, b0, seq, 0, n0, l, cw);
+        if constexpr (NB == 3) {
+            s16_copy_all<DK, RAW, CGATE, CBETA>(a, b1, seq, min(1, a.NC - 1), n0, l, cw);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(L::NCOPY));   // this wave's copies of chunk 0 have landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+    }
+    lds_barrier();
+
+    // one chunk: operands in `buf`; the copy wave fills `cbuf` with chunk
+    // c + NB - 1 (clamped to the last chunk: a buffer nobody reads again)
+    auto chunk = [&](const int c, const lchar* buf, lchar* cbuf) {
+        const int cn = min(c + NB - 1, a.NC - 1);
+        auto gt = [&](int i) { return lds_ld<float>(buf + L::GT + 4 * i); };
+        f32x4 Y, gam, lam;
+
+        // ---------------- phase 1: X = Ks S, Y = Q S, R = V - g X
+        if (copier) {
+            if (c > 0) store_o(c - 1);
+            s16_copy<DK, RAW, CGATE, CBETA, 0>(a, cbuf, seq, cn, n0, l, cw);
+        } else {
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            Y = X;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * w + 4 * g + j;
-            const uint16_t vb = *reinterpret_cast<const uint16_t*>(buf + L::VT + r * 32 + 2 * i16);
-            const float vv = CBETA ? (float)__builtin_bit_cast(half_t, vb) : bf16_to_f32(vb);
-            gam[j] = CGATE ? 1.f : gt[r];
-            lam[j] = CGATE ? 1.f : gt[64 + r];
-            Rv[j] = vv - gam[j] * X[j];
+            for (int s = 0; s < DK / 32; ++s) {
+                const uint4 kf = lds16(tile_at<L::RB>(buf + L::KS, ra, 4 * s + g));
+                const uint4 qf = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
+#pragma unroll
+                for (int p = 0; p < NPL; ++p) {
+                    const uint4 sf = lds16(sS + p * 16 * L::SP + i16 * L::SP + 2 * (32 * s + 8 * g));
+                    X = mfma_raw<BF>(kf, sf, X);
+                    Y = mfma_raw<BF>(qf, sf, Y);
+                }
+            }
+            f32x4 Rv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * w + 4 * g + j;
+                const uint16_t vb = lds_ld<uint16_t>(buf + L::VT + r * 32 + 2 * i16);
+                const float vv = CBETA ? (float)__builtin_bit_cast(half_t, vb) : bf16_to_f32(vb);
+                gam[j] = CGATE ? 1.f : gt(r);
+                lam[j] = CGATE ? 1.f : gt(64 + r);
+                Rv[j] = vv - gam[j] * X[j];
+            }
+            st4_terms<false, 1>(sR + i16 * L::RP + 2 * (16 * w + 4 * g), 0, Rv);
         }
-        st4_terms<false, 1>(sR + i16 * L::RP + 2 * (16 * w + 4 * g), 0, Rv);
         lds_barrier();
 
-        // U = T^ R
-        f32x4 U = {0.f, 0.f, 0.f, 0.f};
+        // ---------------- phase 2: U = T^ R (and l U for the state update)
+        // A fragment of a packed triangle: row 16 w + i16, columns 32 s + 8 g
+        // .. +7, i.e. block (w, 2 s + g / 2), half g & 1; zero above the
+        // diagonal blocks.
+        auto tri_frag = [&](const lchar* tri, int s) {
+            const int I = 2 * s + (g >> 1);
+            const int Ic = I <= w ? I : w;
+            uint4 f = lds16(tri + tri_block(w, Ic) * 512 + i16 * 32 + 16 * ((g & 1) ^ ((i16 >> 3) & 1)));
+            const uint32_t m = I <= w ? ~0u : 0u;
+            f.x &= m;
+            f.y &= m;
+            f.z &= m;
+            f.w &= m;
+            return f;
+        };
+        f32x4 U;
+        if (copier) {
+            s16_copy<DK, RAW, CGATE, CBETA, 1>(a, cbuf, seq, cn, n0, l, cw);
+        } else {
+            U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            U = mfma_raw<false>(lds16(tile_at<128>(buf + L::TT, ra, 4 * s + g)),
-                                lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
-        st4_terms<false, 1>(sU + i16 * L::RP + 2 * (16 * w + 4 * g), 0, U);
-        {
+            for (int s = 0; s < 2; ++s)
+                U = mfma_raw<false>(tri_frag(buf + L::TT, s), lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
+            st4_terms<false, 1>(sU + i16 * L::RP + 2 * (16 * w + 4 * g), 0, U);
             f32x4 Ul;
 #pragma unroll
             for (int j = 0; j < 4; ++j) Ul[j] = lam[j] * U[j];
@@ -367,55 +495,71 @@ __global__ __launch_bounds__(256) void scan16_kernel(ChunkArgs a) {
         }
         lds_barrier();
 
-        // O = g Y + P U (stored during the next chunk)
-        f32x4 O;
+        // ---------------- phase 3: O = g Y + P U; S = g63 S + Kl^T (l U)
+        if (copier) {
+            s16_copy<DK, RAW, CGATE, CBETA, 2>(a, cbuf, seq, cn, n0, l, cw);
+            s16_warm<DK, RAW, CGATE, CBETA>(a, seq, min(c + DR_SCAN_PFD, a.NC - 1), tile + NT * (64 * cw + l),
+                                            sink + 256 * cw);
+            // the copies of chunk c + 1 have landed: with three buffers every
+            // operation but the NCOPY + 1 just issued for later chunks is
+            // complete; with two, every one but the touch
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(NB == 3 ? L::NCOPY + 1 : 1));
+        } else {
+            f32x4 O;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) O[j] = gam[j] * Y[j];
+            for (int j = 0; j < 4; ++j) O[j] = gam[j] * Y[j];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            O = mfma_raw<false>(lds16(tile_at<128>(buf + L::PT, ra, 4 * s + g)),
-                                lds16(sU + i16 * L::RP + 2 * (32 * s + 8 * g)), O);
-        Oprev = O;
-        oprev_t0 = t0;
-        oprev_Lc = Lc;
+            for (int s = 0; s < 2; ++s)
+                O = mfma_raw<false>(tri_frag(buf + L::PT, s), lds16(sU + i16 * L::RP + 2 * (32 * s + 8 * g)), O);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                lds_st(sO + (16 * w + 4 * g + j) * L::OP + 4 * i16, O[j]);
 
-        // S = g63 S + Kl^T (l U).  A fragment (state row rt + i16, tokens
-        // 32 s + 8 g + 0..7) from two transposed reads: lane q of each
-        // 16-lane group points at token 32 s + 8 g + (q >> 2) (+4) and key
-        // column rt + 4 (q & 3); lane i then holds column rt + i.
+            // A fragment (state row rt + i16, tokens 32 s + 8 g + 0..7) from two
+            // transposed reads: lane q of each 16-lane group points at token
+            // 32 s + 8 g + (q >> 2) (+4) and key column rt + 4 (q & 3); lane i
+            // then holds column rt + i.
 #pragma unroll
-        for (int t = 0; t < NTS; ++t) {
-            const int rt = 16 * (w * NTS + t);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NTS; ++t) {
+                const int rt = 16 * (w * NTS + t);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int tok = 32 * s + 8 * g + (i16 >> 2);
-                const int d = rt + 4 * (i16 & 3);
-                const uint2 lo4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok, d >> 3) + 2 * (d & 7));
-                const uint2 hi4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok + 4, d >> 3) + 2 * (d & 7));
-                const uint4 ka = {lo4.x, lo4.y, hi4.x, hi4.y};
+                for (int s = 0; s < 2; ++s) {
+                    const int tok = 32 * s + 8 * g + (i16 >> 2);
+                    const int d = rt + 4 * (i16 & 3);
+                    const uint2 lo4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok, d >> 3) + 2 * (d & 7));
+                    const uint2 hi4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok + 4, d >> 3) + 2 * (d & 7));
+                    const uint4 ka = {lo4.x, lo4.y, hi4.x, hi4.y};
 #pragma unroll
-                for (int p = 0; p < NPL; ++p)
-                    acc = mfma_raw<BF>(ka, lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g)), acc);
+                    for (int p = 0; p < NPL; ++p)
+                        acc = mfma_raw<BF>(ka, lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g)), acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float d63 = CGATE ? gt(rt + 4 * g + j) : gt(63);
+                    S[t][j] = d63 * S[t][j] + acc[j];
+                }
+                st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, S[t]);
             }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float d63 = CGATE ? gt[rt + 4 * g + j] : gt[63];
-                S[t][j] = d63 * S[t][j] + acc[j];
-            }
-            st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, S[t]);
         }
-        vmem_wait_all();   // the next chunk's copies have landed
-        asm volatile("" ::"v"(warm0), "v"(warm1));
         lds_barrier();
     };
-    for (int c = 0; c < a.NC; c += 2) {
-        chunk(c, lds_buf0, lds_buf1);
-        if (c + 1 < a.NC) chunk(c + 1, lds_buf1, lds_buf0);
-    }
-    if (oprev_t0 >= 0) store_o();
 
-    if (a.S_final) {
+    for (int c = 0; c < a.NC; c += NB) {
+        if constexpr (NB == 3) {
+            chunk(c, b0, b2);
+            if (c + 1 < a.NC) chunk(c + 1, b1, b0);
+            if (c + 2 < a.NC) chunk(c + 2, b2, b1);
+        } else {
+            chunk(c, b0, b1);
+            if (c + 1 < a.NC) chunk(c + 1, b1, b0);
+        }
+    }
+
+    if (copier) {
+        store_o(a.NC - 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no copy may land after the workgroup ends
+    } else if (a.S_final) {
 #pragma unroll
         for (int t = 0; t < NTS; ++t)
 #pragma unroll
@@ -431,10 +575,11 @@ static hipError_t launch_s16(const ChunkArgs& a, hipStream_t st) {
     constexpr bool RAW = !CGATE && !CBETA;
     using L = SD<DK, RAW, CGATE>;
     static_assert(L::TOTAL <= 160 * 1024, "LDS plan exceeds 160 KiB");
+    static_assert(L::NCOPY + 1 <= 63, "copies per chunk exceed the vector-memory counter");
     auto kern = scan16_kernel<DK, RAW, CGATE, CBETA>;
     const int NT = a.Dv / 16;
     const int groups = (a.nseq + 7) / 8;
-    hipLaunchKernelGGL(kern, dim3(groups * 8 * NT), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(kern, dim3(groups * 8 * NT), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
