@@ -133,6 +133,28 @@ __device__ __forceinline__ void dma4(const void* g, lchar* lds_base) {
         : "memory");
 }
 
+// 16 bytes from base + voff (base the same for the whole wave, voff per
+// lane) into LDS at lds_base + 16 * lane: the scalar-base addressing form,
+// with no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16s(const char* base, unsigned voff, lchar* lds_base) {
+    const unsigned m = __builtin_amdgcn_readfirstlane((unsigned)(size_t)lds_base);
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(base), "s"(m)
+        : "memory");
+}
+
+// A pointer known to be the same in every lane, kept in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+    const unsigned long long u = (unsigned long long)p;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
+}
+
 // Workgroup barrier over LDS only: wait for this wave's own LDS accesses,
 // then s_barrier.  Global->LDS copies in flight are not waited for.
 __device__ __forceinline__ void lds_barrier() {
@@ -239,7 +261,7 @@ __device__ __forceinline__ void copy_tile(const uint16_t* src, size_t pitch, int
 }
 
 // Part `PART` of the copies of chunk c into buffer `buf`, copy wave cw's share:
-//   0: Kl;  1: Ks (channel gate), T^, P, the V tile, the gate factors;  2: Q.
+//   0: Kl;  1: Q;  2: Ks (channel gate), T^, P, the V tile, the gate factors.
 template <int DK, bool RAW, bool CGATE, bool CBETA, int PART>
 __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq, int c, int n0, int l, int cw) {
     using L = SD<DK, RAW, CGATE>;
@@ -254,7 +276,7 @@ __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq
         else
             copy_tile<L::RB>(reinterpret_cast<const uint16_t*>(CGATE ? a.wsKl : a.wsKs) + obase, DK, CH,
                              buf + L::KL, l, cw);
-    } else if constexpr (PART == 1) {
+    } else if constexpr (PART == 2) {
         if constexpr (CGATE)
             copy_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsKs) + obase, DK, CH, buf + L::KS, l, cw);
         // slots k = cw, cw + 4, cw + 8, cw + 12 of: T^ (0-4), P (5-9), the V
@@ -292,55 +314,158 @@ __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq
     }
 }
 
-template <int DK, bool RAW, bool CGATE, bool CBETA>
-__device__ __forceinline__ void s16_copy_all(const ChunkArgs& a, lchar* buf, int seq, int c, int n0, int l, int cw) {
-    s16_copy<DK, RAW, CGATE, CBETA, 0>(a, buf, seq, c, n0, l, cw);
-    s16_copy<DK, RAW, CGATE, CBETA, 1>(a, buf, seq, c, n0, l, cw);
-    s16_copy<DK, RAW, CGATE, CBETA, 2>(a, buf, seq, c, n0, l, cw);
-}
-
-// How many chunks ahead of the one being computed the copy wave touches the
-// operands (see s16_warm).
+// How many chunks ahead of the one being computed the copy waves touch the
+// operands to start their HBM reads early: each workgroup of a sequence
+// touches one dword in each of a 1/NT share of the chunk's 128-byte operand
+// lines, as one global->LDS load per copy wave into a scratch row that is
+// never read (Copier::warm).
 #ifndef DR_SCAN_PFD
 #define DR_SCAN_PFD 4
 #endif
 
-// Start the HBM reads of chunk cc early: each workgroup of a sequence touches
-// one dword in each of a 1/NT share of the chunk's 128-byte operand lines
-// (line li, clamped to the last line), as one global->LDS load into a
-// scratch row that is never read.  Always exactly one instruction.
+// A copy wave's per-lane address plan: byte offsets inside each operand tile
+// it copies, computed once, so that every copy in the chunk loop is a scalar
+// base (per chunk) plus a fixed lane offset.  A partial last chunk, whose raw
+// rows must be clamped, goes through s16_copy instead.
 template <int DK, bool RAW, bool CGATE, bool CBETA>
-__device__ __forceinline__ void s16_warm(const ChunkArgs& a, int seq, int cc, int li, lchar* sink) {
-    const int t0 = cc * CH;
-    const int Lc = min(CH, a.L - t0);
-    const size_t tok0 = (size_t)seq * a.L + t0;
-    const size_t cs = (size_t)seq * a.NC + cc;
-    const size_t ob = cs * (size_t)(CH * DK) * 2;   // byte offset of a workspace operand tile
-    const int nraw = (Lc * DK * 2 + 127) >> 7;
-    const char* p = nullptr;
-    const char* last = nullptr;
-    int x = li;
-    auto region = [&](const void* base, int n) {
-        const char* b = static_cast<const char*>(base);
-        if (!p && x >= 0 && x < n) p = b + 128 * x;
-        last = b + 128 * (n - 1);
-        x -= n;
-    };
-    if constexpr (RAW) {
-        region(static_cast<const char*>(a.k) + tok0 * DK * 2, nraw);
-        region(static_cast<const char*>(a.q) + tok0 * DK * 2, nraw);
-    } else {
-        region(reinterpret_cast<const char*>(CGATE ? a.wsKl : a.wsKs) + ob, DK);
-        if constexpr (CGATE) region(reinterpret_cast<const char*>(a.wsKs) + ob, DK);
-        region(reinterpret_cast<const char*>(a.wsQ) + ob, DK);
+struct Copier {
+    using L = SD<DK, RAW, CGATE>;
+    static constexpr int PPR = L::RB / 16;   // 16-byte pieces per tile row
+    static constexpr int RPI = 64 / PPR;     // tile rows per 1 KiB instruction
+    static constexpr int NTI = PPR / 4;      // tile instructions per copy wave
+    unsigned toff[NTI];   // lane offsets in a K / Q tile (row pitch DK)
+    unsigned soff[4];     // lane offsets of the part-1 slots
+    const char* wbase;    // this lane's warm-up line in chunk 0
+    unsigned wstride;     // and its per-chunk stride
+    unsigned ooff;        // output lane offset (elements)
+    int cw;
+
+    __device__ __forceinline__ void init(const ChunkArgs& a, int seq, int n0, int l, int cw_, int tile, int NT) {
+        cw = cw_;
+#pragma unroll
+        for (int jj = 0; jj < NTI; ++jj) {
+            const int j = cw + 4 * jj;
+            const int r = j * RPI + l / PPR;
+            const int lp = (l % PPR) ^ swz<L::RB>(r);
+            toff[jj] = (unsigned)(r * DK + 8 * lp) * 2u;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int k = cw + 4 * jj;
+            unsigned o;
+            if (k < 5) o = 1024u * k + 16u * l;
+            else if (k < 10) o = 1024u * (k - 5) + 16u * l;
+            else if (k < 12) {
+                const int r = 32 * (k - 10) + (l >> 1), piece = l & 1;
+                o = (unsigned)(r * (CBETA ? DK : a.Dv) + n0 + 8 * piece) * 2u;
+            } else {
+                constexpr int NG = CGATE ? DK / 4 : 32;
+                o = 16u * (l % NG);
+            }
+            soff[jj] = o;
+        }
+        ooff = (unsigned)((16 * cw + (l >> 2)) * a.Dv + n0 + 4 * (l & 3));
+        // warm-up line: regions of one full chunk, in order
+        const size_t seq0 = (size_t)seq * a.L;           // first token of the sequence
+        const size_t cs0 = (size_t)seq * a.NC;           // its first chunk slot
+        int x = tile + NT * (64 * cw + l);
+        const char* b = nullptr;
+        unsigned st = 0;
+        const char* lastb = nullptr;
+        unsigned lastst = 0;
+        auto region = [&](const void* base0, unsigned stride, int n) {
+            const char* bb = static_cast<const char*>(base0);
+            if (!b && x >= 0 && x < n) { b = bb + 128 * x; st = stride; }
+            lastb = bb + 128 * (n - 1);
+            lastst = stride;
+            x -= n;
+        };
+        if constexpr (RAW) {
+            region(static_cast<const char*>(a.k) + seq0 * DK * 2, CH * DK * 2, DK);
+            region(static_cast<const char*>(a.q) + seq0 * DK * 2, CH * DK * 2, DK);
+        } else {
+            region(reinterpret_cast<const char*>(CGATE ? a.wsKl : a.wsKs) + cs0 * CH * DK * 2, CH * DK * 2, DK);
+            if constexpr (CGATE) region(reinterpret_cast<const char*>(a.wsKs) + cs0 * CH * DK * 2, CH * DK * 2, DK);
+            region(reinterpret_cast<const char*>(a.wsQ) + cs0 * CH * DK * 2, CH * DK * 2, DK);
+        }
+        region(a.wsT + cs0 * CH * CH, CH * CH * 2, kTriBytes / 128);
+        region(a.wsP + cs0 * CH * CH, CH * CH * 2, kTriBytes / 128);
+        if constexpr (CBETA) region(reinterpret_cast<const char*>(a.wsV) + cs0 * CH * DK * 2, CH * DK * 2, DK);
+        else region(static_cast<const char*>(a.v) + seq0 * a.Dv * 2, CH * a.Dv * 2, a.Dv);
+        region(a.wsG + cs0 * kGW, kGW * 4, kGW * 4 / 128);
+        wbase = b ? b : lastb;
+        wstride = b ? st : lastst;
     }
-    region(a.wsT + cs * (CH * CH), kTriBytes / 128);
-    region(a.wsP + cs * (CH * CH), kTriBytes / 128);
-    if constexpr (CBETA) region(reinterpret_cast<const char*>(a.wsV) + ob, DK);
-    else region(static_cast<const char*>(a.v) + tok0 * a.Dv * 2, (Lc * a.Dv * 2 + 127) >> 7);
-    region(a.wsG + cs * kGW, kGW * 4 / 128);
-    dma4(p ? p : last, sink);
-}
+
+    // chunk cn's raw rows need clamping (partial last chunk)?
+    __device__ __forceinline__ static bool tail(const ChunkArgs& a, int cn) { return (cn + 1) * CH > a.L; }
+
+    // part PART of chunk cn's copies (numbered as in s16_copy)
+    template <int PART>
+    __device__ __forceinline__ void copy(const ChunkArgs& a, lchar* buf, int seq, int cn, int n0, int l) const {
+        constexpr bool RAWROWS = PART == 2 ? !CBETA : RAW;
+        if (RAWROWS && tail(a, cn)) {
+            s16_copy<DK, RAW, CGATE, CBETA, PART>(a, buf, seq, cn, n0, l, cw);
+            return;
+        }
+        const size_t tok0 = (size_t)seq * a.L + (size_t)cn * CH;
+        const size_t cs = (size_t)seq * a.NC + cn;
+        const size_t obase = cs * (size_t)(CH * DK) * 2;   // bytes
+        if constexpr (PART == 0 || PART == 1) {
+            const char* src;
+            if constexpr (PART == 0)
+                src = RAW ? static_cast<const char*>(a.k) + tok0 * DK * 2
+                          : reinterpret_cast<const char*>(CGATE ? a.wsKl : a.wsKs) + obase;
+            else
+                src = RAW ? static_cast<const char*>(a.q) + tok0 * DK * 2
+                          : reinterpret_cast<const char*>(a.wsQ) + obase;
+            src = uniform_ptr(src);
+            lchar* dst = buf + (PART == 0 ? L::KL : L::QT);
+#pragma unroll
+            for (int jj = 0; jj < NTI; ++jj) dma16s(src, toff[jj], dst + (cw + 4 * jj) * 1024);
+        } else {
+            if constexpr (CGATE) {
+                const char* src = uniform_ptr(reinterpret_cast<const char*>(a.wsKs) + obase);
+#pragma unroll
+                for (int jj = 0; jj < NTI; ++jj) dma16s(src, toff[jj], buf + L::KS + (cw + 4 * jj) * 1024);
+            }
+            const char* tb = uniform_ptr(a.wsT + cs * (size_t)(CH * CH));
+            const char* pb = uniform_ptr(a.wsP + cs * (size_t)(CH * CH));
+            const char* vb = uniform_ptr(CBETA ? reinterpret_cast<const char*>(a.wsV) + obase
+                                               : static_cast<const char*>(a.v) + tok0 * a.Dv * 2);
+            const char* gb = uniform_ptr(a.wsG + cs * kGW);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int k = cw + 4 * jj;   // wave-uniform: selects, no branches
+                const char* src = k < 5 ? tb : k < 10 ? pb : k < 12 ? vb : gb;
+                const int dst = k < 5 ? L::TT + 1024 * k
+                              : k < 10 ? L::PT + 1024 * (k - 5)
+                              : k < 12 ? L::VT + 1024 * (k - 10) : L::GT;
+                dma16s(src, soff[jj], buf + dst);
+            }
+        }
+    }
+
+    // one dword of chunk cc's lines (cc < 0: the first workspace line)
+    __device__ __forceinline__ void warm(const ChunkArgs& a, int seq, int cc, lchar* sink) const {
+        const char* p = cc >= 0 ? wbase + (size_t)cc * wstride
+                                : reinterpret_cast<const char*>(a.wsT + (size_t)seq * a.NC * (CH * CH));
+        dma4(p, sink);
+    }
+
+    // chunk cc's output rows 16 cw .. 16 cw + 15 from sO
+    __device__ __forceinline__ void store_o(const ChunkArgs& a, const lchar* sO, int seq, int cc, int l) const {
+        const int t0 = cc * CH;
+        const int Lc = min(CH, a.L - t0);
+        const int row = 16 * cw + (l >> 2);
+        const float4 v = lds_ld<float4>(sO + row * L::OP + 16 * (l & 3));
+        const size_t e0 = ((size_t)seq * a.L + t0) * a.Dv;   // first element of the chunk's rows
+        const bf16x4 h = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+        const bool bf = a.out_bf16;
+        if (row < Lc && bf) *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(a.o) + e0 + ooff) = h;
+        if (row < Lc && !bf) *reinterpret_cast<float4*>(static_cast<float*>(a.o) + e0 + ooff) = v;
+    }
+};
 
 template <int DK, bool RAW, bool CGATE, bool CBETA>
 __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
@@ -383,25 +508,10 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
     lchar* sUl = work + L::WUL;
     lchar* sO = work + L::WO;
 
-    // coalesced store of chunk cc's output tile from sO: copy wave cw stores
-    // rows 16 cw .. 16 cw + 15.  Both output types are formed and the store
-    // is chosen by predicate (a branch on the type here trips the gfx950
-    // backend).
-    auto store_o = [&](int cc) {
-        const int t0 = cc * CH;
-        const int Lc = min(CH, a.L - t0);
-        const int q4 = l & 3;
-        const int row = 16 * cw + (l >> 2);
-        float* of = static_cast<float*>(a.o);
-        uint16_t* ob = static_cast<uint16_t*>(a.o);
-        const bool bf = a.out_bf16;
-        const float4 v = lds_ld<float4>(sO + row * L::OP + 16 * q4);
-        const size_t oi = ((size_t)seq * a.L + t0 + row) * a.Dv + n0 + 4 * q4;
-        const uint2 pk = {(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
-                          (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
-        if (row < Lc && bf) *reinterpret_cast<uint2*>(ob + oi) = pk;
-        if (row < Lc && !bf) *reinterpret_cast<float4*>(of + oi) = v;
-    };
+    Copier<DK, RAW, CGATE, CBETA> cp;
+    if (copier) cp.init(a, seq, n0, l, cw, tile, NT);
+    // chunks that are whole (only those are touched ahead)
+    const int NCF = a.L / CH;
 
     f32x4 S[NTS];
     if (!copier) {
@@ -415,9 +525,14 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (16 * (w * NTS + t) + 4 * g), 16 * L::SP, S[t]);
         }
     } else {
-        s16_copy_all<DK, RAW, CGATE, CBETA>(a, b0, seq, 0, n0, l, cw);
+        cp.template copy<0>(a, b0, seq, 0, n0, l);
+        cp.template copy<1>(a, b0, seq, 0, n0, l);
+        cp.template copy<2>(a, b0, seq, 0, n0, l);
         if constexpr (NB == 3) {
-            s16_copy_all<DK, RAW, CGATE, CBETA>(a, b1, seq, min(1, a.NC - 1), n0, l, cw);
+            const int c1 = min(1, a.NC - 1);
+            cp.template copy<0>(a, b1, seq, c1, n0, l);
+            cp.template copy<1>(a, b1, seq, c1, n0, l);
+            cp.template copy<2>(a, b1, seq, c1, n0, l);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(L::NCOPY));   // this wave's copies of chunk 0 have landed
         } else {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -431,11 +546,28 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
         const int cn = min(c + NB - 1, a.NC - 1);
         auto gt = [&](int i) { return lds_ld<float>(buf + L::GT + 4 * i); };
         f32x4 Y, gam, lam;
+        // A fragment of a packed triangle: row 16 w + i16, columns 32 s + 8 g
+        // .. +7, i.e. block (w, 2 s + g / 2), half g & 1; zero above the
+        // diagonal blocks.
+        auto tri_frag = [&](const lchar* tri, int s) {
+            const int I = 2 * s + (g >> 1);
+            const int Ic = I <= w ? I : w;
+            uint4 f = lds16(tri + tri_block(w, Ic) * 512 + i16 * 32 + 16 * ((g & 1) ^ ((i16 >> 3) & 1)));
+            const uint32_t m = I <= w ? ~0u : 0u;
+            f.x &= m;
+            f.y &= m;
+            f.z &= m;
+            f.w &= m;
+            return f;
+        };
+        // operands of phases 2 and 3 that depend only on the chunk's tiles,
+        // read during phase 1 so that their LDS latency is off the chain
+        uint4 tfr[2], pfr[2], kfr[NTS][2];
 
         // ---------------- phase 1: X = Ks S, Y = Q S, R = V - g X
         if (copier) {
-            if (c > 0) store_o(c - 1);
-            s16_copy<DK, RAW, CGATE, CBETA, 0>(a, cbuf, seq, cn, n0, l, cw);
+            if (c > 0) cp.store_o(a, sO, seq, c - 1, l);
+            cp.template copy<0>(a, cbuf, seq, cn, n0, l);
         } else {
             f32x4 X = {0.f, 0.f, 0.f, 0.f};
             Y = X;
@@ -448,6 +580,27 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
                     const uint4 sf = lds16(sS + p * 16 * L::SP + i16 * L::SP + 2 * (32 * s + 8 * g));
                     X = mfma_raw<BF>(kf, sf, X);
                     Y = mfma_raw<BF>(qf, sf, Y);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                tfr[s] = tri_frag(buf + L::TT, s);
+                pfr[s] = tri_frag(buf + L::PT, s);
+            }
+            // Kl^T fragments (state row rt + i16, tokens 32 s + 8 g + 0..7) from
+            // two transposed reads: lane q of each 16-lane group points at
+            // token 32 s + 8 g + (q >> 2) (+4) and key column rt + 4 (q & 3);
+            // lane i then holds column rt + i.
+#pragma unroll
+            for (int t = 0; t < NTS; ++t) {
+                const int rt = 16 * (w * NTS + t);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int tok = 32 * s + 8 * g + (i16 >> 2);
+                    const int d = rt + 4 * (i16 & 3);
+                    const uint2 lo4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok, d >> 3) + 2 * (d & 7));
+                    const uint2 hi4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok + 4, d >> 3) + 2 * (d & 7));
+                    kfr[t][s] = {lo4.x, lo4.y, hi4.x, hi4.y};
                 }
             }
             f32x4 Rv;
@@ -465,28 +618,14 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
         lds_barrier();
 
         // ---------------- phase 2: U = T^ R (and l U for the state update)
-        // A fragment of a packed triangle: row 16 w + i16, columns 32 s + 8 g
-        // .. +7, i.e. block (w, 2 s + g / 2), half g & 1; zero above the
-        // diagonal blocks.
-        auto tri_frag = [&](const lchar* tri, int s) {
-            const int I = 2 * s + (g >> 1);
-            const int Ic = I <= w ? I : w;
-            uint4 f = lds16(tri + tri_block(w, Ic) * 512 + i16 * 32 + 16 * ((g & 1) ^ ((i16 >> 3) & 1)));
-            const uint32_t m = I <= w ? ~0u : 0u;
-            f.x &= m;
-            f.y &= m;
-            f.z &= m;
-            f.w &= m;
-            return f;
-        };
         f32x4 U;
         if (copier) {
-            s16_copy<DK, RAW, CGATE, CBETA, 1>(a, cbuf, seq, cn, n0, l, cw);
+            cp.template copy<1>(a, cbuf, seq, cn, n0, l);
         } else {
             U = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                U = mfma_raw<false>(tri_frag(buf + L::TT, s), lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
+                U = mfma_raw<false>(tfr[s], lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
             st4_terms<false, 1>(sU + i16 * L::RP + 2 * (16 * w + 4 * g), 0, U);
             f32x4 Ul;
 #pragma unroll
@@ -497,9 +636,8 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
 
         // ---------------- phase 3: O = g Y + P U; S = g63 S + Kl^T (l U)
         if (copier) {
-            s16_copy<DK, RAW, CGATE, CBETA, 2>(a, cbuf, seq, cn, n0, l, cw);
-            s16_warm<DK, RAW, CGATE, CBETA>(a, seq, min(c + DR_SCAN_PFD, a.NC - 1), tile + NT * (64 * cw + l),
-                                            sink + 256 * cw);
+            cp.template copy<2>(a, cbuf, seq, cn, n0, l);
+            cp.warm(a, seq, NCF > 0 ? min(c + DR_SCAN_PFD, NCF - 1) : -1, sink + 256 * cw);
             // the copies of chunk c + 1 have landed: with three buffers every
             // operation but the NCOPY + 1 just issued for later chunks is
             // complete; with two, every one but the touch
@@ -510,26 +648,18 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             for (int j = 0; j < 4; ++j) O[j] = gam[j] * Y[j];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                O = mfma_raw<false>(tri_frag(buf + L::PT, s), lds16(sU + i16 * L::RP + 2 * (32 * s + 8 * g)), O);
+                O = mfma_raw<false>(pfr[s], lds16(sU + i16 * L::RP + 2 * (32 * s + 8 * g)), O);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 lds_st(sO + (16 * w + 4 * g + j) * L::OP + 4 * i16, O[j]);
 
-            // A fragment (state row rt + i16, tokens 32 s + 8 g + 0..7) from two
-            // transposed reads: lane q of each 16-lane group points at token
-            // 32 s + 8 g + (q >> 2) (+4) and key column rt + 4 (q & 3); lane i
-            // then holds column rt + i.
 #pragma unroll
             for (int t = 0; t < NTS; ++t) {
                 const int rt = 16 * (w * NTS + t);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const int tok = 32 * s + 8 * g + (i16 >> 2);
-                    const int d = rt + 4 * (i16 & 3);
-                    const uint2 lo4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok, d >> 3) + 2 * (d & 7));
-                    const uint2 hi4 = lds_tr4(tile_at<L::RB>(buf + L::KL, tok + 4, d >> 3) + 2 * (d & 7));
-                    const uint4 ka = {lo4.x, lo4.y, hi4.x, hi4.y};
+                    const uint4 ka = kfr[t][s];
 #pragma unroll
                     for (int p = 0; p < NPL; ++p)
                         acc = mfma_raw<BF>(ka, lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g)), acc);
@@ -557,7 +687,7 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
     }
 
     if (copier) {
-        store_o(a.NC - 1);
+        cp.store_o(a, sO, seq, a.NC - 1, l);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no copy may land after the workgroup ends
     } else if (a.S_final) {
 #pragma unroll
