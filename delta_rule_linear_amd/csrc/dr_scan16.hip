@@ -656,18 +656,18 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
 #pragma unroll
             for (int t = 0; t < NTS; ++t) {
                 const int rt = 16 * (w * NTS + t);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const uint4 ka = kfr[t][s];
 #pragma unroll
                     for (int p = 0; p < NPL; ++p)
-                        acc = mfma_raw<BF>(ka, lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g)), acc);
+                        acc[s] = mfma_raw<BF>(ka, lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g)), acc[s]);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const float d63 = CGATE ? gt(rt + 4 * g + j) : gt(63);
-                    S[t][j] = d63 * S[t][j] + acc[j];
+                    S[t][j] = d63 * S[t][j] + (acc[0][j] + acc[1][j]);
                 }
                 st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, S[t]);
             }
