@@ -77,7 +77,7 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, size_t pitch, int 
 
 }  // namespace
 
-// LDS plan (bytes): k tile, q tile, A (fp32), T (fp32), P (fp16), gates,
+// LDS plan (bytes): k tile, q tile, A (fp32), T (fp32), P (fp16, packed), gates,
 // per-wave 16 x 16 fp32 scratch.
 template <int DK>
 struct P16 {
@@ -87,9 +87,8 @@ struct P16 {
     static constexpr int AP = 65;                 // fp32 pitch of A and T
     static constexpr int SA = QT + 64 * RB;
     static constexpr int ST = SA + 64 * AP * 4;
-    static constexpr int PP = 72;                 // fp16 pitch of P
-    static constexpr int SPm = ST + 64 * AP * 4;
-    static constexpr int SG = SPm + 64 * PP * 2;  // G[64], beta[64]
+    static constexpr int SPm = ST + 64 * AP * 4;  // P, packed lower blocks (fp16)
+    static constexpr int SG = SPm + kTriBytes;    // G[64], beta[64]
     static constexpr int SX = SG + 128 * 4;       // [4][16][17] fp32
     static constexpr int TOTAL = SX + 4 * 16 * 17 * 4;
 };
@@ -100,7 +99,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float(*sA)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::SA);
     float(*sT)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::ST);
-    half_t(*sP)[L::PP] = reinterpret_cast<half_t(*)[L::PP]>(smem + L::SPm);
+    half_t* sPp = reinterpret_cast<half_t*>(smem + L::SPm);
     float* sg = reinterpret_cast<float*>(smem + L::SG);
     float* sb = sg + 64;
     float(*sX)[16][17] = reinterpret_cast<float(*)[16][17]>(smem + L::SX);
@@ -135,29 +134,46 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies landed
     __syncthreads();
 
-    // A and P, 16 x 16 blocks on the bf16 matrix cores: 10 lower blocks each,
-    // 20 jobs, 5 per wave
-    for (int job = w; job < 20; job += 4) {
-        const bool isP = job >= 10;
-        const int pr = isP ? job - 10 : job;
-        // lower block pairs (R, I), R >= I: 0,0 1,0 1,1 2,0 2,1 2,2 3,0 3,1 3,2 3,3
+    // gate values this lane needs, in registers (log2 units): rows
+    // 16 R + 4 g + j of every block row R, column 16 I + i16 of every block
+    // column I; beta of the rows
+    constexpr float kLog2e = 1.4426950408889634f;
+    float grow[4][4], brow[4][4], gcol[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            grow[R][j] = sg[16 * R + 4 * g + j] * kLog2e;
+            brow[R][j] = sb[16 * R + 4 * g + j];
+        }
+        gcol[R] = sg[16 * R + i16] * kLog2e;
+    }
+
+    // A and P, 16 x 16 block pairs (R, I), R >= I, on the bf16 matrix cores:
+    // both share the k_I fragments and the decay factors e^{G_r - G_i}
+    for (int pr = w; pr < 10; pr += 4) {
+        // lower block pairs in order: 0,0 1,0 1,1 2,0 2,1 2,2 3,0 3,1 3,2 3,3
         const int R = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
         const int I = pr - R * (R + 1) / 2;
-        const char* rows = smem + (isP ? L::QT : L::KT);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
-            const uint4 fa = *reinterpret_cast<const uint4*>(tile_at<L::RB>(rows, 16 * R + i16, 4 * s + g));
-            const uint4 fb = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::KT, 16 * I + i16, 4 * s + g));
-            acc = mfma_bf16(fa, fb, acc);
+            const uint4 kb = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::KT, 16 * I + i16, 4 * s + g));
+            const uint4 ka = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::KT, 16 * R + i16, 4 * s + g));
+            const uint4 qa = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::QT, 16 * R + i16, 4 * s + g));
+            accA = mfma_bf16(ka, kb, accA);
+            accP = mfma_bf16(qa, kb, accP);
         }
+        const float gi = I == 0 ? gcol[0] : I == 1 ? gcol[1] : I == 2 ? gcol[2] : gcol[3];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
-            const bool in = r < Lc && i <= r;
-            const float v = in ? acc[j] * expf(sg[r] - sg[i]) : 0.f;
-            if (isP) sP[r][i] = (half_t)v;
-            else sA[r][i] = (i < r) ? v * sb[r] : 0.f;
+            const float gr = R == 0 ? grow[0][j] : R == 1 ? grow[1][j] : R == 2 ? grow[2][j] : grow[3][j];
+            const float br = R == 0 ? brow[0][j] : R == 1 ? brow[1][j] : R == 2 ? brow[2][j] : brow[3][j];
+            const float f = __builtin_amdgcn_exp2f(gr - gi);   // e^{G_r - G_i} <= 1
+            const bool live = r < Lc;
+            sA[r][i] = (live && i < r) ? accA[j] * f * br : 0.f;
+            sPp[tri_off(r, i)] = (half_t)((live && i <= r) ? accP[j] * f : 0.f);
         }
     }
     __syncthreads();
@@ -207,23 +223,26 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
         __syncthreads();
     }
 
-    // outputs: T^ = T Diag(beta) and P in the packed lower-block form, fp16;
-    // one 16-byte piece (8 columns of one block row) per thread and step
+    // outputs in the packed lower-block form, fp16: T^ = T Diag(beta) from
+    // its fp32 blocks (one 8-column piece per thread and step), P copied
     for (int e = tid; e < 2 * 320; e += 256) {
-        const bool isP = e >= 320;
-        const int x = isP ? e - 320 : e;
-        const int blk = x >> 5, r = (x >> 1) & 15, h = x & 1;
-        const int R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-        const int I = blk - R * (R + 1) / 2;
-        const int row = 16 * R + r, c0 = 16 * I + 8 * h;
-        half8 hv;
+        if (e < 320) {
+            const int blk = e >> 5, r = (e >> 1) & 15, h = e & 1;
+            const int R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+            const int I = blk - R * (R + 1) / 2;
+            const int row = 16 * R + r, c0 = 16 * I + 8 * h;
+            half8 hv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = c0 + j;
-            hv[j] = col <= row ? (isP ? sP[row][col] : (half_t)(sT[row][col] * sb[col])) : (half_t)0.f;
+            for (int j = 0; j < 8; ++j) {
+                const int col = c0 + j;
+                hv[j] = (half_t)(col <= row ? sT[row][col] * sb[col] : 0.f);
+            }
+            *reinterpret_cast<half8*>(a.wsT + cs * (size_t)(CH * CH) + tri_off(row, c0)) = hv;
+        } else {
+            const int x = e - 320;
+            *reinterpret_cast<uint4*>(a.wsP + cs * (size_t)(CH * CH) + 8 * x) =
+                *reinterpret_cast<const uint4*>(sPp + 8 * x);
         }
-        half_t* dst = (isP ? a.wsP : a.wsT) + cs * (size_t)(CH * CH) + tri_off(row, c0);
-        *reinterpret_cast<half8*>(dst) = hv;
     }
 }
 
