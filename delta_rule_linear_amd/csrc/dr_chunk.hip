@@ -159,67 +159,128 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
         float* sQg = smem + SM::kQg;
         float* cst = smem + SM::kCst;
         constexpr int KP = SM::KP;
-        // one thread per key channel walks the chunk's 64 tokens
+        // scratch, free until A and P are formed: per token-group totals of
+        // log alpha, and G at each block's start, middle, end and at token 63
+        float* stot = smem + SM::kA;   // [16][DK]
+        float* sbnd = smem + SM::kP;   // [13][DK]: 3 R + {0, 1, 2}, then 12: G_63
+        constexpr float kL2E = 1.4426950408889634f;
+        // thread = (channel group cg: CPT channels, token group tg: 4 tokens)
+        constexpr int CPT = DK / 16;
+        const int cg = tid & 15, tg = tid >> 4;
+        const int ch0 = cg * CPT;
+        const size_t pl = (size_t)CH * DK, base = cs * (size_t)(P * CH * DK);
+        float G[4][CPT];
+        {
+            float run[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) run[c] = 0.f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * tg + u;
+                float x[CPT];
+                load_f32_n<CPT>(a.log_alpha + (tok0 + (r < Lc ? r : 0)) * DK + ch0, x);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    run[c] += (r < Lc) ? x[c] : 0.f;
+                    G[u][c] = run[c];
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) stot[tg * DK + ch0 + c] = run[c];
+        }
+        __syncthreads();
+        {
+            float off[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) off[c] = 0.f;
+            for (int t = 0; t < tg; ++t)
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) off[c] += stot[t * DK + ch0 + c];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * tg + u;
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    G[u][c] += off[c];
+                    const int slot = (r & 15) == 0 ? 0 : (r & 15) == 8 ? 1 : (r & 15) == 15 ? 2 : -1;
+                    if (slot >= 0) sbnd[(3 * (r >> 4) + slot) * DK + ch0 + c] = G[u][c];
+                    if (r == 63) sbnd[12 * DK + ch0 + c] = G[u][c];
+                }
+            }
+        }
+        __syncthreads();
+        // gated operands of this thread's 4 tokens x CPT channels:
+        //   rowf_r = e^{G_r - G_{16R}},  colf_r = e^{G_{16R+15} - G_r}  (<= 1)
+        // for the A / P products here, and Q e^{G}, Kt e^{G}, Kt e^{G_63 - G}
+        // (and vt) for the scan
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * tg + u, R = r >> 4;
+            const int rc = r < Lc ? r : 0;
+            const bool live = r < Lc;
+            float kx[CPT], qx[CPT], bx[CPT], vx[CPT];
+            load_n<F32IN, CPT>(a.k, (tok0 + rc) * DK + ch0, kx);
+            load_n<F32IN, CPT>(a.q, (tok0 + rc) * DK + ch0, qx);
+            if constexpr (CBETA) {
+                load_f32_n<CPT>(a.beta + (tok0 + rc) * DK + ch0, bx);
+                load_n<F32IN, CPT>(a.v, (tok0 + rc) * Dv + ch0, vx);
+            }
+            float okg[CPT], oki[CPT], oqg[CPT], wq[CPT], wks[CPT], wkl[CPT], wv[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const float sbv = CBETA ? sqrtf(bx[c]) : 1.f;
+                const float kt = live ? sbv * kx[c] : 0.f;
+                const float qv = live ? qx[c] : 0.f;
+                const float g2 = G[u][c] * kL2E;
+                const float gs2 = sbnd[(3 * R) * DK + ch0 + c] * kL2E;
+                const float ge2 = sbnd[(3 * R + 2) * DK + ch0 + c] * kL2E;
+                const float g632 = sbnd[12 * DK + ch0 + c] * kL2E;
+                const float rowf = __builtin_amdgcn_exp2f(g2 - gs2);
+                const float colf = __builtin_amdgcn_exp2f(ge2 - g2);
+                okg[c] = kt * rowf;
+                oki[c] = kt * colf;
+                oqg[c] = qv * rowf;
+                const float eg = __builtin_amdgcn_exp2f(g2);
+                wq[c] = qv * eg;
+                wks[c] = kt * eg;
+                wkl[c] = kt * __builtin_amdgcn_exp2f(g632 - g2);
+                wv[c] = CBETA ? (live ? sbv * vx[c] : 0.f) : 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; c += 4) {
+                *reinterpret_cast<float4*>(sKg + r * KP + ch0 + c) = make_float4(okg[c], okg[c + 1], okg[c + 2], okg[c + 3]);
+                *reinterpret_cast<float4*>(sKi + r * KP + ch0 + c) = make_float4(oki[c], oki[c + 1], oki[c + 2], oki[c + 3]);
+                *reinterpret_cast<float4*>(sQg + r * KP + ch0 + c) = make_float4(oqg[c], oqg[c + 1], oqg[c + 2], oqg[c + 3]);
+            }
+            store_split_n<P, CPT>(a.wsQ, base, pl, r * DK + ch0, wq);
+            store_split_n<P, CPT>(a.wsKs, base, pl, r * DK + ch0, wks);
+            store_split_n<P, CPT>(a.wsKl, base, pl, r * DK + ch0, wkl);
+            if constexpr (CBETA) store_split_n<P, CPT>(a.wsV, base, pl, r * DK + ch0, wv);
+        }
+        // per-channel constants, the range check of the diagonal blocks and
+        // the state decay over the chunk (one thread per channel)
         if (tid < DK) {
             const int col = tid;
-            float G[CH];
-            float run = 0.f;
-#pragma unroll
-            for (int r = 0; r < CH; ++r) {
-                const float x = a.log_alpha[(tok0 + (r < Lc ? r : 0)) * DK + col];
-                run += (r < Lc) ? x : 0.f;
-                G[r] = run;
-            }
-            // per-block factors, <= 1 for non-positive log gates:
-            //   rowf_r = e^{G_r - G_{16R}},  colf_r = e^{G_{16R+15} - G_r}
             int badbits = 0;
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                const float gs = G[16 * R];
-                const float gm = G[16 * R + 8];
-                const float ge = G[16 * R + 15];
-                const float Egs = expf(gs);          // e^{G_{16R}}, chunk-start relative
-                const float Fr = expf(G[63] - ge);   // e^{G_63 - G_{16R+15}}
+                const float gs = sbnd[(3 * R) * DK + col];
+                const float gm = sbnd[(3 * R + 1) * DK + col];
+                const float ge = sbnd[(3 * R + 2) * DK + col];
                 // the diagonal block's rescaled factors reach e^{|G_r - G_m|}
                 if (!(gs - gm <= kDiagRange && gm - ge <= kDiagRange &&
                       gs - gm >= -kDiagRange && gm - ge >= -kDiagRange))
                     badbits |= 1 << R;
                 cst[(CST_IGM + R) * DK + col] = expf(gs - gm);
                 cst[(CST_IIM + R) * DK + col] = expf(gm - ge);
-#pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int r = 16 * R + rr;
-                    const int rc = r < Lc ? r : 0;
-                    float kv = load1<F32IN>(a.k, (tok0 + rc) * DK + col);
-                    float qv = load1<F32IN>(a.q, (tok0 + rc) * DK + col);
-                    float vv = 0.f, sbv = 1.f;
-                    if constexpr (CBETA) {
-                        sbv = sqrtf(a.beta[(tok0 + rc) * DK + col]);
-                        vv = sbv * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
-                    }
-                    kv = r < Lc ? kv : 0.f;
-                    qv = r < Lc ? qv : 0.f;
-                    vv = r < Lc ? vv : 0.f;
-                    const float kt = sbv * kv;
-                    const float rowf = expf(G[r] - gs);
-                    const float colf = expf(ge - G[r]);
-                    sKg[r * KP + col] = kt * rowf;
-                    sKi[r * KP + col] = kt * colf;
-                    sQg[r * KP + col] = qv * rowf;
-                    // operands for the scan: Q e^{G}, Kt e^{G}, Kt e^{G_63 - G} (and vt)
-                    const size_t pl = (size_t)CH * DK, base = cs * (size_t)(P * CH * DK);
-                    store_split<P>(a.wsQ, base, pl, r * DK + col, qv * rowf * Egs);
-                    store_split<P>(a.wsKs, base, pl, r * DK + col, kt * rowf * Egs);
-                    store_split<P>(a.wsKl, base, pl, r * DK + col, kt * colf * Fr);
-                    if constexpr (CBETA) store_split<P>(a.wsV, base, pl, r * DK + col, vv);
-                }
             }
 #pragma unroll
             for (int R = 1; R < 4; ++R)
 #pragma unroll
                 for (int I = 0; I < R; ++I)
-                    cst[(CST_C + offdiag_index(R, I)) * DK + col] = expf(G[16 * R] - G[16 * I + 15]);
-            a.wsG[cs * kGW + col] = expf(G[63]);   // state decay over the chunk
+                    cst[(CST_C + offdiag_index(R, I)) * DK + col] =
+                        expf(sbnd[(3 * R) * DK + col] - sbnd[(3 * I + 2) * DK + col]);
+            a.wsG[cs * kGW + col] = expf(sbnd[12 * DK + col]);   // state decay over the chunk
             if (badbits) atomicOr(&sflag[0], badbits);
         }
         if constexpr (!CBETA) {

@@ -219,6 +219,60 @@ __device__ __forceinline__ void store_split(half_t* base, size_t off, size_t pla
     }
 }
 
+// Store N (4 or 8) consecutive fp32 values as P fp16 terms at base[off + idx ..]
+// (hi) and base[off + plane + idx ..] (lo), as one vector store per plane.
+template <int P, int N>
+__device__ __forceinline__ void store_split_n(half_t* base, size_t off, size_t plane, size_t idx, const float* x) {
+    typedef half_t hvec __attribute__((ext_vector_type(N)));
+    hvec hi, lo;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        if constexpr (P == 2) {
+            half_t h, o;
+            split2(x[j], h, o);
+            hi[j] = h;
+            lo[j] = o;
+        } else {
+            hi[j] = (half_t)x[j];
+        }
+    }
+    *reinterpret_cast<hvec*>(base + off + idx) = hi;
+    if constexpr (P == 2) *reinterpret_cast<hvec*>(base + off + plane + idx) = lo;
+}
+
+// N (4 or 8) consecutive input values (bf16 or fp32) as fp32.
+template <bool F32IN, int N>
+__device__ __forceinline__ void load_n(const void* base, size_t off, float* x) {
+    if constexpr (F32IN) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+        for (int v = 0; v < N / 4; ++v) {
+            const float4 f = p[v];
+            x[4 * v] = f.x; x[4 * v + 1] = f.y; x[4 * v + 2] = f.z; x[4 * v + 3] = f.w;
+        }
+    } else {
+        const uint16_t* h = static_cast<const uint16_t*>(base) + off;
+        if constexpr (N == 8) {
+            unpack_bf16x8(*reinterpret_cast<const uint4*>(h), x);
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2*>(h);
+            x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+            x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+        }
+    }
+}
+
+// N (4 or 8) consecutive fp32 values.
+template <int N>
+__device__ __forceinline__ void load_f32_n(const float* p, float* x) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int v = 0; v < N / 4; ++v) {
+        const float4 f = q[v];
+        x[4 * v] = f.x; x[4 * v + 1] = f.y; x[4 * v + 2] = f.z; x[4 * v + 3] = f.w;
+    }
+}
+
 // Store sixteen fp32 values as P fp16 terms at base[idx .. idx + 16) of each
 // plane (16-byte aligned).
 template <int P>
