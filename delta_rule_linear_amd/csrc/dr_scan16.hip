@@ -562,31 +562,61 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
         };
         // operands of phases 2 and 3 that depend only on the chunk's tiles,
         // read during phase 1 so that their LDS latency is off the chain
-        uint4 tfr[2], pfr[2], kfr[NTS][2];
+        uint4 tfr[2], pfr[2], kfr[NTS][2], sfr[DK / 32][NPL];
 
-        // ---------------- phase 1: X = Ks S, Y = Q S, R = V - g X
+        // ---------------- phase 1: X = Ks S, R = V - g X
         if (copier) {
             if (c > 0) cp.store_o(a, sO, seq, c - 1, l);
             cp.template copy<0>(a, cbuf, seq, cn, n0, l);
         } else {
+            // X only: the state fragments are kept for Y = Q S, which is off
+            // the chain and done in phase 2
             f32x4 X = {0.f, 0.f, 0.f, 0.f};
-            Y = X;
 #pragma unroll
             for (int s = 0; s < DK / 32; ++s) {
                 const uint4 kf = lds16(tile_at<L::RB>(buf + L::KS, ra, 4 * s + g));
-                const uint4 qf = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
 #pragma unroll
                 for (int p = 0; p < NPL; ++p) {
-                    const uint4 sf = lds16(sS + p * 16 * L::SP + i16 * L::SP + 2 * (32 * s + 8 * g));
-                    X = mfma_raw<BF>(kf, sf, X);
-                    Y = mfma_raw<BF>(qf, sf, Y);
+                    sfr[s][p] = lds16(sS + p * 16 * L::SP + i16 * L::SP + 2 * (32 * s + 8 * g));
+                    X = mfma_raw<BF>(kf, sfr[s][p], X);
                 }
             }
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                tfr[s] = tri_frag(buf + L::TT, s);
-                pfr[s] = tri_frag(buf + L::PT, s);
+            for (int s = 0; s < 2; ++s) tfr[s] = tri_frag(buf + L::TT, s);
+            f32x4 Rv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * w + 4 * g + j;
+                const uint16_t vb = lds_ld<uint16_t>(buf + L::VT + r * 32 + 2 * i16);
+                const float vv = CBETA ? (float)__builtin_bit_cast(half_t, vb) : bf16_to_f32(vb);
+                gam[j] = CGATE ? 1.f : gt(r);
+                lam[j] = CGATE ? 1.f : gt(64 + r);
+                Rv[j] = vv - gam[j] * X[j];
             }
+            st4_terms<false, 1>(sR + i16 * L::RP + 2 * (16 * w + 4 * g), 0, Rv);
+        }
+        lds_barrier();
+
+        // ---------------- phase 2: U = T^ R (and l U for the state update), Y = Q S
+        f32x4 U;
+        if (copier) {
+            cp.template copy<1>(a, cbuf, seq, cn, n0, l);
+        } else {
+            U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                U = mfma_raw<false>(tfr[s], lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
+            // off the chain: Y = Q S, and the phase-3 operands that depend only
+            // on the chunk's tiles
+            Y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < DK / 32; ++s) {
+                const uint4 qf = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
+#pragma unroll
+                for (int p = 0; p < NPL; ++p) Y = mfma_raw<BF>(qf, sfr[s][p], Y);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) pfr[s] = tri_frag(buf + L::PT, s);
             // Kl^T fragments (state row rt + i16, tokens 32 s + 8 g + 0..7) from
             // two transposed reads: lane q of each 16-lane group points at
             // token 32 s + 8 g + (q >> 2) (+4) and key column rt + 4 (q & 3);
@@ -603,29 +633,6 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
                     kfr[t][s] = {lo4.x, lo4.y, hi4.x, hi4.y};
                 }
             }
-            f32x4 Rv;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * w + 4 * g + j;
-                const uint16_t vb = lds_ld<uint16_t>(buf + L::VT + r * 32 + 2 * i16);
-                const float vv = CBETA ? (float)__builtin_bit_cast(half_t, vb) : bf16_to_f32(vb);
-                gam[j] = CGATE ? 1.f : gt(r);
-                lam[j] = CGATE ? 1.f : gt(64 + r);
-                Rv[j] = vv - gam[j] * X[j];
-            }
-            st4_terms<false, 1>(sR + i16 * L::RP + 2 * (16 * w + 4 * g), 0, Rv);
-        }
-        lds_barrier();
-
-        // ---------------- phase 2: U = T^ R (and l U for the state update)
-        f32x4 U;
-        if (copier) {
-            cp.template copy<1>(a, cbuf, seq, cn, n0, l);
-        } else {
-            U = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                U = mfma_raw<false>(tfr[s], lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
             st4_terms<false, 1>(sU + i16 * L::RP + 2 * (16 * w + 4 * g), 0, U);
             f32x4 Ul;
 #pragma unroll
