@@ -59,10 +59,13 @@ def fwd_bytes_per_token_head(d: int, L: int, in_bytes: int = 2, gate_floats: int
 
 
 # the state scan alone (bf16 inputs, scalar gate and beta): q, k, v read once,
-# T^ and P (64 x 64 fp16 per chunk, so 2 * 64 * 2 bytes per token), the gate
-# factors (2 fp32 per token), o written once, S0 and S_final amortised
+# T^ and P (the ten lower 16 x 16 fp16 blocks of each, 5120 bytes per chunk),
+# the gate factors (2 fp32 per token), o written once, S0 and S_final amortised
+TRI_BYTES = 10 * 16 * 16 * 2
+
+
 def scan_bytes_per_token_head(d: int, L: int) -> float:
-    return 3 * d * 2 + 2 * CH * 2 + 2 * 4 + d * 4 + 2 * d * d * 4 / L
+    return 3 * d * 2 + 2 * TRI_BYTES / CH + 2 * 4 + d * 4 + 2 * d * d * 4 / L
 
 
 # decode, per state: S read and written once (fp32), q, k, v (bf16), the gate
