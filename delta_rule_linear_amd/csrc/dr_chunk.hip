@@ -19,19 +19,22 @@
 // transform of the above, exact in exact arithmetic), so the raw bf16 inputs
 // are matrix-core operands without any rounding.
 //
-// Two kernels:
+// Kernels in this file:
 //   prep  one workgroup per (chunk, head, batch): G, A and P on the matrix
 //         cores, T = (I + A)^-1 by blocked forward substitution in fp32,
-//         writes T^ and P (fp16), the gate factors, and for channel-wise
-//         gates / betas the gated fp16 operands the scan needs.
-//   scan  one workgroup per (sequence, 16-column tile of S): walks the chunks
-//         in order holding its fp32 S tile in registers; per chunk
-//         X = Ks S, R = V - g X, U = T^ R, O = g Q S + P U, S = g63 S + Kl^T U.
-//         Columns of S evolve independently (the transition acts on the key
-//         side only), so tiles of one head never exchange data.
+//         writes T^ and P, the gate factors, and for channel-wise gates /
+//         betas the gated fp16 operands the scan needs.  Used for fp32 inputs
+//         and for channel-wise gates or betas; bf16 inputs with a scalar gate
+//         and beta use prep16_kernel (dr_prep16.hip).
+//   scan  (fp32 inputs) one workgroup per (sequence, 16-column tile of S):
+//         walks the chunks in order holding its fp32 S tile in registers; per
+//         chunk X = Ks S, R = V - g X, U = T^ R, O = g Q S + P U,
+//         S = g63 S + Kl^T U.  Columns of S evolve independently (the
+//         transition acts on the key side only), so tiles of one head never
+//         exchange data.  bf16 inputs use scan16_kernel (dr_scan16.hip).
 //
-// All matrix-core operands are fp16 (bf16 inputs convert exactly); fp32
-// inputs use two fp16 terms.  Accumulation and the state are fp32.
+// Matrix-core operands here are fp16; fp32 inputs use two fp16 terms (hi +
+// lo).  Accumulation and the state are fp32.
 
 #include <hip/hip_runtime.h>
 
