@@ -77,8 +77,11 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, size_t pitch, int 
 
 }  // namespace
 
-// LDS plan (bytes): k tile, q tile, A (fp32), T (fp32), P (fp16, packed), gates,
-// per-wave 16 x 16 fp32 scratch.
+// LDS plan (bytes): k tile, q tile, A (fp32), gates.  T (fp32) and the
+// per-wave 16 x 16 scratch of the triangular solve reuse the k / q tiles,
+// which are dead once A and P are formed (d = 128; at d = 64 the tiles are
+// too small and T follows the gates); P goes straight to the workspace.
+// 49.9 KB at d = 128: three workgroups per CU.
 template <int DK>
 struct P16 {
     static constexpr int RB = DK * 2;
@@ -86,11 +89,12 @@ struct P16 {
     static constexpr int QT = KT + 64 * RB;
     static constexpr int AP = 65;                 // fp32 pitch of A and T
     static constexpr int SA = QT + 64 * RB;
-    static constexpr int ST = SA + 64 * AP * 4;
-    static constexpr int SPm = ST + 64 * AP * 4;  // P, packed lower blocks (fp16)
-    static constexpr int SG = SPm + kTriBytes;    // G[64], beta[64]
-    static constexpr int SX = SG + 128 * 4;       // [4][16][17] fp32
-    static constexpr int TOTAL = SX + 4 * 16 * 17 * 4;
+    static constexpr int SG = SA + 64 * AP * 4;   // G[64], beta[64]
+    static constexpr int TX = 64 * AP * 4 + 4 * 16 * 17 * 4;   // T and the scratch
+    static constexpr bool ALIAS = TX <= 2 * 64 * RB;            // they fit in the tiles
+    static constexpr int ST = ALIAS ? KT : SG + 128 * 4;
+    static constexpr int SX = ST + 64 * AP * 4;   // [4][16][17] fp32
+    static constexpr int TOTAL = ALIAS ? SG + 128 * 4 : SX + 4 * 16 * 17 * 4;
 };
 
 template <int DK>
@@ -99,7 +103,6 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     float(*sA)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::SA);
     float(*sT)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::ST);
-    half_t* sPp = reinterpret_cast<half_t*>(smem + L::SPm);
     float* sg = reinterpret_cast<float*>(smem + L::SG);
     float* sb = sg + 64;
     float(*sX)[16][17] = reinterpret_cast<float(*)[16][17]>(smem + L::SX);
@@ -173,7 +176,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             const float f = __builtin_amdgcn_exp2f(gr - gi);   // e^{G_r - G_i} <= 1
             const bool live = r < Lc;
             sA[r][i] = (live && i < r) ? accA[j] * f * br : 0.f;
-            sPp[tri_off(r, i)] = (half_t)((live && i <= r) ? accP[j] * f : 0.f);
+            // P to the workspace, packed: 16 lanes write one 32-byte block row
+            a.wsP[cs * (size_t)(CH * CH) + tri_off(r, i)] = (half_t)((live && i <= r) ? accP[j] * f : 0.f);
         }
     }
     __syncthreads();
@@ -223,26 +227,20 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
         __syncthreads();
     }
 
-    // outputs in the packed lower-block form, fp16: T^ = T Diag(beta) from
-    // its fp32 blocks (one 8-column piece per thread and step), P copied
-    for (int e = tid; e < 2 * 320; e += 256) {
-        if (e < 320) {
-            const int blk = e >> 5, r = (e >> 1) & 15, h = e & 1;
-            const int R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-            const int I = blk - R * (R + 1) / 2;
-            const int row = 16 * R + r, c0 = 16 * I + 8 * h;
-            half8 hv;
+    // T^ = T Diag(beta) in the packed lower-block form, fp16, from its fp32
+    // blocks: one 8-column piece per thread and step
+    for (int e = tid; e < 320; e += 256) {
+        const int blk = e >> 5, r = (e >> 1) & 15, h = e & 1;
+        const int R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
+        const int I = blk - R * (R + 1) / 2;
+        const int row = 16 * R + r, c0 = 16 * I + 8 * h;
+        half8 hv;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int col = c0 + j;
-                hv[j] = (half_t)(col <= row ? sT[row][col] * sb[col] : 0.f);
-            }
-            *reinterpret_cast<half8*>(a.wsT + cs * (size_t)(CH * CH) + tri_off(row, c0)) = hv;
-        } else {
-            const int x = e - 320;
-            *reinterpret_cast<uint4*>(a.wsP + cs * (size_t)(CH * CH) + 8 * x) =
-                *reinterpret_cast<const uint4*>(sPp + 8 * x);
+        for (int j = 0; j < 8; ++j) {
+            const int col = c0 + j;
+            hv[j] = (half_t)(col <= row ? sT[row][col] * sb[col] : 0.f);
         }
+        *reinterpret_cast<half8*>(a.wsT + cs * (size_t)(CH * CH) + tri_off(row, c0)) = hv;
     }
 }
 
