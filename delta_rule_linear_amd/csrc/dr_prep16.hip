@@ -207,22 +207,26 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
     for (int R = 1; R < 4; ++R) {
         if (w < R) {
             const int I = w;
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < 4 * (R - I); ++s) {
+            // two accumulators (even / odd k-steps) halve the dependent chain
+            f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0;
+            for (int s = 0; s < 4 * (R - I); s += 2) {
                 const int m = 16 * I + 4 * s + g;
-                X = mfma_f32(sA[16 * R + i16][m], sT[m][16 * I + i16], X);
+                X0 = mfma_f32(sA[16 * R + i16][m], sT[m][16 * I + i16], X0);
+                X1 = mfma_f32(sA[16 * R + i16][m + 4], sT[m + 4][16 * I + i16], X1);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sX[w][4 * g + j][i16] = X[j];
+            for (int j = 0; j < 4; ++j) sX[w][4 * g + j][i16] = X0[j] + X1[j];
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's scratch is written
             __builtin_amdgcn_wave_barrier();
             asm volatile("" ::: "memory");
-            f32x4 Tn = {0.f, 0.f, 0.f, 0.f};
+            f32x4 Tn0 = {0.f, 0.f, 0.f, 0.f}, Tn1 = Tn0;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                Tn = mfma_f32(sT[16 * R + i16][16 * R + 4 * s + g], sX[w][4 * s + g][i16], Tn);
+            for (int s = 0; s < 4; s += 2) {
+                Tn0 = mfma_f32(sT[16 * R + i16][16 * R + 4 * s + g], sX[w][4 * s + g][i16], Tn0);
+                Tn1 = mfma_f32(sT[16 * R + i16][16 * R + 4 * s + 4 + g], sX[w][4 * s + 4 + g][i16], Tn1);
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sT[16 * R + 4 * g + j][16 * I + i16] = -Tn[j];
+            for (int j = 0; j < 4; ++j) sT[16 * R + 4 * g + j][16 * I + i16] = -(Tn0[j] + Tn1[j]);
         }
         __syncthreads();
     }
