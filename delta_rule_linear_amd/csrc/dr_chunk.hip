@@ -296,43 +296,46 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     __syncthreads();
 
     // ------------------------------------------------- A and P on the matrix cores
-    // 20 jobs: 10 lower block pairs for A, the same 10 for P; 5 per wave.
+    // 10 lower block pairs (R, I); A and P of a pair share the k_I fragments
+    // and the decay factors.
     const int badmask = CGATE ? sflag[0] : 0;
-    for (int job = w; job < 20; job += 4) {
-        const bool isP = job >= 10;
-        const int pr = isP ? job - 10 : job;
+    for (int pr = w; pr < 10; pr += 4) {
         const int R = kPairR[pr], I = kPairI[pr];
         if (CGATE && R == I && (badmask >> R) & 1) continue;   // handled by the exact path below
         const int ra = 16 * R + (l & 15);   // operand row (A side)
         const int ca = 16 * I + (l & 15);   // operand row (B side)
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
             const int k0 = 32 * s + 8 * (l >> 4);
-            Frag<P> fa, fb;
+            Frag<P> fk, fq, fb;
             if constexpr (!CGATE) {
                 const int rac = ra < Lc ? ra : 0, cac = ca < Lc ? ca : 0;
-                const Raw8<F32IN> rwa = ld_raw8<F32IN>(isP ? a.q : a.k, (tok0 + rac) * DK + k0);
+                const Raw8<F32IN> rwk = ld_raw8<F32IN>(a.k, (tok0 + rac) * DK + k0);
+                const Raw8<F32IN> rwq = ld_raw8<F32IN>(a.q, (tok0 + rac) * DK + k0);
                 const Raw8<F32IN> rwb = ld_raw8<F32IN>(a.k, (tok0 + cac) * DK + k0);
                 if constexpr (!CBETA) {
-                    fa = raw_to_frag<F32IN, P>(rwa, ra < Lc);
+                    fk = raw_to_frag<F32IN, P>(rwk, ra < Lc);
+                    fq = raw_to_frag<F32IN, P>(rwq, ra < Lc);
                     fb = raw_to_frag<F32IN, P>(rwb, ca < Lc);
                 } else {
-                    float xa[8], xb[8], ba[8], bb[8];
+                    float xk[8], xq[8], xb[8], ba[8], bb[8];
                     const float4* pa = reinterpret_cast<const float4*>(a.beta + (tok0 + rac) * DK + k0);
                     const float4* pb = reinterpret_cast<const float4*>(a.beta + (tok0 + cac) * DK + k0);
                     *reinterpret_cast<float4*>(ba) = pa[0];
                     *reinterpret_cast<float4*>(ba + 4) = pa[1];
                     *reinterpret_cast<float4*>(bb) = pb[0];
                     *reinterpret_cast<float4*>(bb + 4) = pb[1];
-                    cvt_raw8<F32IN>(rwa, ra < Lc, xa);
+                    cvt_raw8<F32IN>(rwk, ra < Lc, xk);
+                    cvt_raw8<F32IN>(rwq, ra < Lc, xq);
                     cvt_raw8<F32IN>(rwb, ca < Lc, xb);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
-                        if (!isP) xa[j] *= sqrtf(ba[j]);
+                        xk[j] *= sqrtf(ba[j]);
                         xb[j] *= sqrtf(bb[j]);
                     }
-                    fa = split8<P>(xa);
+                    fk = split8<P>(xk);
+                    fq = split8<P>(xq);
                     fb = split8<P>(xb);
                 }
             } else {
@@ -341,8 +344,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
                 const float* sKi = smem + SM::kKi;
                 const float* sQg = smem + SM::kQg;
                 const float* cst = smem + SM::kCst;
-                float xa[8], xb[8];
-                const float* rowsrc = isP ? sQg : sKg;
+                float xk[8], xq[8], xb[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int col = k0 + j;
@@ -351,27 +353,28 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
                     const float fr = (R == I) ? cst[(CST_IGM + R) * DK + col]
                                               : cst[(CST_C + offdiag_index(R, I)) * DK + col];
                     const float fc = (R == I) ? cst[(CST_IIM + R) * DK + col] : 1.f;
-                    xa[j] = rowsrc[ra * KP + col] * fr;
+                    xk[j] = sKg[ra * KP + col] * fr;
+                    xq[j] = sQg[ra * KP + col] * fr;
                     xb[j] = sKi[ca * KP + col] * fc;
                 }
-                fa = split8<P>(xa);
+                fk = split8<P>(xk);
+                fq = split8<P>(xq);
                 fb = split8<P>(xb);
             }
-            acc = mma<P, P>(fa, fb, acc);
+            accA = mma<P, P>(fk, fb, accA);
+            accP = mma<P, P>(fq, fb, accP);
         }
-        // gate factors and masks; write the block to LDS
+        // gate factors and masks; write the blocks to LDS
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * R + 4 * (l >> 4) + j;
             const int i = 16 * I + (l & 15);
-            float val = acc[j];
-            if constexpr (!CGATE) val *= (i <= r) ? expf(sg[r] - sg[i]) : 0.f;
-            if (isP) {
-                sP[r][i] = (i <= r) ? val : 0.f;
-            } else {
-                if constexpr (!CBETA) val *= sb[r];
-                sA[r][i] = (i < r) ? val : 0.f;
-            }
+            float dec = 1.f;
+            if constexpr (!CGATE) dec = (i <= r) ? expf(sg[r] - sg[i]) : 0.f;
+            sP[r][i] = (i <= r) ? accP[j] * dec : 0.f;
+            float va = accA[j] * dec;
+            if constexpr (!CBETA) va *= sb[r];
+            sA[r][i] = (i < r) ? va : 0.f;
         }
     }
     if constexpr (CGATE) {
@@ -424,24 +427,37 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
         for (int r = 0; r < 16; ++r) sT[base + r][base + j] = t[r];
     }
     __syncthreads();
-    // off-diagonal blocks, one block row at a time:
-    //   X_RI = sum_{J=I}^{R-1} A_RJ T_JI,   T_RI = -T_RR X_RI
-    for (int R = 1; R < 4; ++R) {
-        for (int e = tid; e < R * 256; e += 256) {
-            const int I = e >> 8, r = (e >> 4) & 15, i = e & 15;
-            float s = 0.f;
-            for (int m = 16 * I; m < 16 * R; ++m) s += sA[16 * R + r][m] * sT[m][16 * I + i];
-            sX[I][r][i] = s;
-        }
-        __syncthreads();
-        for (int e = tid; e < R * 256; e += 256) {
-            const int I = e >> 8, r = (e >> 4) & 15, i = e & 15;
-            float s = 0.f;
+    // off-diagonal blocks, one block row R at a time on the fp32 matrix cores;
+    // wave I < R computes
+    //   X_RI = sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .],  T_RI = -T_RR X_RI
+    {
+        const int i16 = l & 15, g = l >> 4;
+        for (int R = 1; R < 4; ++R) {
+            if (w < R) {
+                const int I = w;
+                // two accumulators (even / odd k-steps) halve the dependent chain
+                f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0;
+                for (int s = 0; s < 4 * (R - I); s += 2) {
+                    const int m = 16 * I + 4 * s + g;
+                    X0 = mfma_f32x4(sA[16 * R + i16][m], sT[m][16 * I + i16], X0);
+                    X1 = mfma_f32x4(sA[16 * R + i16][m + 4], sT[m + 4][16 * I + i16], X1);
+                }
 #pragma unroll
-            for (int m = 0; m < 16; ++m) s += sT[16 * R + r][16 * R + m] * sX[I][m][i];
-            sT[16 * R + r][16 * I + i] = -s;
+                for (int j = 0; j < 4; ++j) sX[w][4 * g + j][i16] = X0[j] + X1[j];
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's scratch is written
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+                f32x4 T0 = {0.f, 0.f, 0.f, 0.f}, T1 = T0;
+#pragma unroll
+                for (int s = 0; s < 4; s += 2) {
+                    T0 = mfma_f32x4(sT[16 * R + i16][16 * R + 4 * s + g], sX[w][4 * s + g][i16], T0);
+                    T1 = mfma_f32x4(sT[16 * R + i16][16 * R + 4 * s + 4 + g], sX[w][4 * s + 4 + g][i16], T1);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sT[16 * R + 4 * g + j][16 * I + i16] = -(T0[j] + T1[j]);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     // --------------------------------------------------- outputs T^ and P

@@ -57,6 +57,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     return (uint16_t)(u >> 16);
 }
 
+// fp32 matrix core, 16 x 16 x 4: lane l holds A[l % 16][l / 16] and
+// B[l / 16][l % 16]; the accumulator layout is that of the 16x16x32 ops
+// (lane l holds C[4 (l / 16) + j][l % 16]).
+__device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Two-term fp16 split x ~ hi + lo.  x is pinned in a register first: otherwise
 // the compiler may fold x's producing multiply into one of the two conversions
 // (a fused multiply-convert rounds the exact product, a plain convert the fp32

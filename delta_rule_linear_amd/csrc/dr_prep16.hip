@@ -36,12 +36,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(const uint4& a, const uint4& b, const
                                                    c, 0, 0, 0);
 }
 
-// fp32 matrix core, 16 x 16 x 4: lane l holds A[l % 16][l / 16] and
-// B[l / 16][l % 16]; the accumulator layout is that of the 16x16x32 ops.
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ void dma16(const void* g, char* lds_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
@@ -211,8 +205,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0;
             for (int s = 0; s < 4 * (R - I); s += 2) {
                 const int m = 16 * I + 4 * s + g;
-                X0 = mfma_f32(sA[16 * R + i16][m], sT[m][16 * I + i16], X0);
-                X1 = mfma_f32(sA[16 * R + i16][m + 4], sT[m + 4][16 * I + i16], X1);
+                X0 = mfma_f32x4(sA[16 * R + i16][m], sT[m][16 * I + i16], X0);
+                X1 = mfma_f32x4(sA[16 * R + i16][m + 4], sT[m + 4][16 * I + i16], X1);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) sX[w][4 * g + j][i16] = X0[j] + X1[j];
@@ -222,8 +216,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             f32x4 Tn0 = {0.f, 0.f, 0.f, 0.f}, Tn1 = Tn0;
 #pragma unroll
             for (int s = 0; s < 4; s += 2) {
-                Tn0 = mfma_f32(sT[16 * R + i16][16 * R + 4 * s + g], sX[w][4 * s + g][i16], Tn0);
-                Tn1 = mfma_f32(sT[16 * R + i16][16 * R + 4 * s + 4 + g], sX[w][4 * s + 4 + g][i16], Tn1);
+                Tn0 = mfma_f32x4(sT[16 * R + i16][16 * R + 4 * s + g], sX[w][4 * s + g][i16], Tn0);
+                Tn1 = mfma_f32x4(sT[16 * R + i16][16 * R + 4 * s + 4 + g], sX[w][4 * s + 4 + g][i16], Tn1);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) sT[16 * R + 4 * g + j][16 * I + i16] = -(Tn0[j] + Tn1[j]);
