@@ -216,38 +216,50 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
         //   rowf_r = e^{G_r - G_{16R}},  colf_r = e^{G_{16R+15} - G_r}  (<= 1)
         // for the A / P products here, and Q e^{G}, Kt e^{G}, Kt e^{G_63 - G}
         // (and vt) for the scan
+        // all four tokens of this thread lie in block R = tg / 4; inputs are
+        // loaded for all four first (the workspace stores below could alias
+        // them as far as the compiler knows, which would serialise the loads)
+        const int R = tg >> 2;
+        float gs2[CPT], ge2[CPT], g632[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            gs2[c] = sbnd[(3 * R) * DK + ch0 + c] * kL2E;
+            ge2[c] = sbnd[(3 * R + 2) * DK + ch0 + c] * kL2E;
+            g632[c] = sbnd[12 * DK + ch0 + c] * kL2E;
+        }
+        float kx[4][CPT], qx[4][CPT], bx[4][CPT], vx[4][CPT];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int r = 4 * tg + u, R = r >> 4;
+            const int r = 4 * tg + u;
             const int rc = r < Lc ? r : 0;
-            const bool live = r < Lc;
-            float kx[CPT], qx[CPT], bx[CPT], vx[CPT];
-            load_n<F32IN, CPT>(a.k, (tok0 + rc) * DK + ch0, kx);
-            load_n<F32IN, CPT>(a.q, (tok0 + rc) * DK + ch0, qx);
+            load_n<F32IN, CPT>(a.k, (tok0 + rc) * DK + ch0, kx[u]);
+            load_n<F32IN, CPT>(a.q, (tok0 + rc) * DK + ch0, qx[u]);
             if constexpr (CBETA) {
-                load_f32_n<CPT>(a.beta + (tok0 + rc) * DK + ch0, bx);
-                load_n<F32IN, CPT>(a.v, (tok0 + rc) * Dv + ch0, vx);
+                load_f32_n<CPT>(a.beta + (tok0 + rc) * DK + ch0, bx[u]);
+                load_n<F32IN, CPT>(a.v, (tok0 + rc) * Dv + ch0, vx[u]);
             }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * tg + u;
+            const bool live = r < Lc;
             float okg[CPT], oki[CPT], oqg[CPT], wq[CPT], wks[CPT], wkl[CPT], wv[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float sbv = CBETA ? sqrtf(bx[c]) : 1.f;
-                const float kt = live ? sbv * kx[c] : 0.f;
-                const float qv = live ? qx[c] : 0.f;
+                const float sbv = CBETA ? sqrtf(bx[u][c]) : 1.f;
+                const float kt = live ? sbv * kx[u][c] : 0.f;
+                const float qv = live ? qx[u][c] : 0.f;
                 const float g2 = G[u][c] * kL2E;
-                const float gs2 = sbnd[(3 * R) * DK + ch0 + c] * kL2E;
-                const float ge2 = sbnd[(3 * R + 2) * DK + ch0 + c] * kL2E;
-                const float g632 = sbnd[12 * DK + ch0 + c] * kL2E;
-                const float rowf = __builtin_amdgcn_exp2f(g2 - gs2);
-                const float colf = __builtin_amdgcn_exp2f(ge2 - g2);
+                const float rowf = __builtin_amdgcn_exp2f(g2 - gs2[c]);
+                const float colf = __builtin_amdgcn_exp2f(ge2[c] - g2);
                 okg[c] = kt * rowf;
                 oki[c] = kt * colf;
                 oqg[c] = qv * rowf;
                 const float eg = __builtin_amdgcn_exp2f(g2);
                 wq[c] = qv * eg;
                 wks[c] = kt * eg;
-                wkl[c] = kt * __builtin_amdgcn_exp2f(g632 - g2);
-                wv[c] = CBETA ? (live ? sbv * vx[c] : 0.f) : 0.f;
+                wkl[c] = kt * __builtin_amdgcn_exp2f(g632[c] - g2);
+                wv[c] = CBETA ? (live ? sbv * vx[u][c] : 0.f) : 0.f;
             }
 #pragma unroll
             for (int c = 0; c < CPT; c += 4) {
