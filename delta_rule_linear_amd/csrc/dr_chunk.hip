@@ -38,7 +38,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "dr_device.h"
 #include "dr_internal.h"
@@ -49,9 +51,11 @@ namespace dr {
 // prep kernel
 // ===========================================================================
 
-// Lower-triangular 16x16 block pairs (R, I), R >= I, of a 64-token chunk.
-__constant__ int kPairR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int kPairI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// Lower-triangular 16x16 block pair number pr = R (R + 1) / 2 + I, R >= I,
+// of a 64-token chunk: (0,0) (1,0) (1,1) (2,0) ... (3,3).  Arithmetic, not a
+// table: a table load would be a vector-memory load, and waiting for it would
+// also wait for every global load issued before it.
+__device__ __forceinline__ int pair_row(int pr) { return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3; }
 
 // Largest |G_r - G_m| (m = block middle) for which a diagonal block's factors
 // e^{G_r - G_m}, e^{G_m - G_i} stay in fp16's normal range.
@@ -78,6 +82,8 @@ struct PrepSmem {
     static constexpr int kFlag = kB + 64;
     static constexpr int FLOATS = kFlag + 4;
     static_assert(!CGATE || kX + 3 * 16 * 17 <= kCst, "T and X must fit inside Kg, Ki, Qg");
+    static_assert(KP % 4 == 0 && kKi % 4 == 0 && kQg % 4 == 0 && kCst % 4 == 0 && DK % 4 == 0,
+                  "factor rows are read as 16-byte vectors");
 };
 
 // Per-channel constants of the channel-gate prep (G is the cumulative log
@@ -89,14 +95,65 @@ struct PrepSmem {
 // to the block end, so every factor of an off-diagonal pair is <= 1.
 enum { CST_C = 0, CST_IGM = 6, CST_IIM = 10 };
 
+// Eight floats from 16-byte aligned shared memory.
+__device__ __forceinline__ void ld8_lds(const float* p, float* x) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 // Off-diagonal pair index of (R, I), R > I: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
 __device__ __forceinline__ int offdiag_index(int R, int I) { return R * (R - 1) / 2 + I; }
 
+// One thread's raw inputs of a chunk for the channel-gate prep: tokens
+// 4 tg .. 4 tg + 3, channels CPT cg .. (tg = tid / 16, cg = tid % 16).  Rows
+// past the sequence's end load row 0 of the chunk and are masked at use.
+template <int DK, bool F32IN, bool CBETA>
+struct CgIn {
+    static constexpr int CPT = DK / 16;
+    float la[4][CPT];               // log alpha
+    RawN<F32IN, CPT> k[4], q[4];
+    RawN<F32IN, CPT> v[CBETA ? 4 : 1];
+    float be[CBETA ? 4 : 1][CPT];   // channel beta
+    float bs;                       // scalar beta of token tid % 64
+};
+
+template <int DK, bool F32IN, bool CBETA>
+__device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBETA>& in, int job, int tid) {
+    constexpr int CPT = DK / 16;
+    const int seq = job / a.NC, c = job % a.NC;
+    const int t0 = c * CH;
+    const int Lc = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int ch0 = (tid & 15) * CPT, tg = tid >> 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = 4 * tg + u;
+        const size_t row = tok0 + (r < Lc ? r : 0);
+        load_f32_n<CPT>(a.log_alpha + row * DK + ch0, in.la[u]);
+        in.k[u] = ld_rawn<F32IN, CPT>(a.k, row * DK + ch0);
+        in.q[u] = ld_rawn<F32IN, CPT>(a.q, row * DK + ch0);
+        if constexpr (CBETA) {
+            load_f32_n<CPT>(a.beta + row * DK + ch0, in.be[u]);
+            in.v[u] = ld_rawn<F32IN, CPT>(a.v, row * a.Dv + ch0);
+        }
+    }
+    if constexpr (!CBETA) {
+        const int r = tid & 63;
+        in.bs = a.beta[tok0 + (r < Lc ? r : 0)];
+    }
+}
+
+// The preparation of chunk c of sequence seq.  With a channel gate the
+// chunk's raw inputs arrive in `in`; once they are consumed, the inputs of
+// chunk `next_job` (>= 0) are loaded into it, so that those loads are in
+// flight during this chunk's matrix work.
 template <int DK, bool F32IN, bool CGATE, bool CBETA>
-__global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
+__device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, const int seq, const int c,
+                                           CgIn<DK, F32IN, CBETA>& in, const int next_job) {
     constexpr int P = F32IN ? 2 : 1;
     using SM = PrepSmem<DK, CGATE>;
-    __shared__ float smem[SM::FLOATS];
     float(*sA)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kA);
     float(*sP)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kP);
     float(*sT)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kT);
@@ -105,8 +162,6 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     float* sb = smem + SM::kB;
     int* sflag = reinterpret_cast<int*>(smem + SM::kFlag);
 
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int seq = b * a.H + h;
     const size_t cs = (size_t)seq * a.NC + c;
     const int t0 = c * CH;
     const int Lc = min(CH, a.L - t0);
@@ -115,7 +170,10 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     const int Dv = a.Dv;
 
     if (tid < 4) sflag[tid] = 0;
-    __syncthreads();   // flags are set with atomicOr by other waves below
+    // flags are set with atomicOr by other waves below; in a loop over chunks
+    // this barrier also orders the previous chunk's last reads before this
+    // chunk's first writes
+    lds_barrier();
 
     // ---------------------------------------------------------------- gates
     if constexpr (!CGATE) {
@@ -180,8 +238,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int r = 4 * tg + u;
-                float x[CPT];
-                load_f32_n<CPT>(a.log_alpha + (tok0 + (r < Lc ? r : 0)) * DK + ch0, x);
+                const float* x = in.la[u];
 #pragma unroll
                 for (int c = 0; c < CPT; ++c) {
                     run[c] += (r < Lc) ? x[c] : 0.f;
@@ -191,7 +248,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
 #pragma unroll
             for (int c = 0; c < CPT; ++c) stot[tg * DK + ch0 + c] = run[c];
         }
-        __syncthreads();
+        lds_barrier();
         {
             float off[CPT];
 #pragma unroll
@@ -211,14 +268,12 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
         // gated operands of this thread's 4 tokens x CPT channels:
         //   rowf_r = e^{G_r - G_{16R}},  colf_r = e^{G_{16R+15} - G_r}  (<= 1)
         // for the A / P products here, and Q e^{G}, Kt e^{G}, Kt e^{G_63 - G}
         // (and vt) for the scan
-        // all four tokens of this thread lie in block R = tg / 4; inputs are
-        // loaded for all four first (the workspace stores below could alias
-        // them as far as the compiler knows, which would serialise the loads)
+        // all four tokens of this thread lie in block R = tg / 4
         const int R = tg >> 2;
         float gs2[CPT], ge2[CPT], g632[CPT];
 #pragma unroll
@@ -227,28 +282,20 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
             ge2[c] = sbnd[(3 * R + 2) * DK + ch0 + c] * kL2E;
             g632[c] = sbnd[12 * DK + ch0 + c] * kL2E;
         }
-        float kx[4][CPT], qx[4][CPT], bx[4][CPT], vx[4][CPT];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = 4 * tg + u;
-            const int rc = r < Lc ? r : 0;
-            load_n<F32IN, CPT>(a.k, (tok0 + rc) * DK + ch0, kx[u]);
-            load_n<F32IN, CPT>(a.q, (tok0 + rc) * DK + ch0, qx[u]);
-            if constexpr (CBETA) {
-                load_f32_n<CPT>(a.beta + (tok0 + rc) * DK + ch0, bx[u]);
-                load_n<F32IN, CPT>(a.v, (tok0 + rc) * Dv + ch0, vx[u]);
-            }
-        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = 4 * tg + u;
             const bool live = r < Lc;
+            float kx[CPT], qx[CPT], vx[CPT];
+            cvt_rawn<F32IN, CPT>(in.k[u], kx);
+            cvt_rawn<F32IN, CPT>(in.q[u], qx);
+            if constexpr (CBETA) cvt_rawn<F32IN, CPT>(in.v[u], vx);
             float okg[CPT], oki[CPT], oqg[CPT], wq[CPT], wks[CPT], wkl[CPT], wv[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float sbv = CBETA ? sqrtf(bx[u][c]) : 1.f;
-                const float kt = live ? sbv * kx[u][c] : 0.f;
-                const float qv = live ? qx[u][c] : 0.f;
+                const float sbv = CBETA ? sqrtf(in.be[u][c]) : 1.f;
+                const float kt = live ? sbv * kx[c] : 0.f;
+                const float qv = live ? qx[c] : 0.f;
                 const float g2 = G[u][c] * kL2E;
                 const float rowf = __builtin_amdgcn_exp2f(g2 - gs2[c]);
                 const float colf = __builtin_amdgcn_exp2f(ge2[c] - g2);
@@ -259,7 +306,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
                 wq[c] = qv * eg;
                 wks[c] = kt * eg;
                 wkl[c] = kt * __builtin_amdgcn_exp2f(g632[c] - g2);
-                wv[c] = CBETA ? (live ? sbv * vx[u][c] : 0.f) : 0.f;
+                wv[c] = CBETA ? (live ? sbv * vx[c] : 0.f) : 0.f;
             }
 #pragma unroll
             for (int c = 0; c < CPT; c += 4) {
@@ -299,20 +346,18 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
             if (badbits) atomicOr(&sflag[0], badbits);
         }
         if constexpr (!CBETA) {
-            if (w == 3) {
-                const float bl = a.beta[tok0 + (l < Lc ? l : 0)];
-                sb[l] = l < Lc ? bl : 0.f;
-            }
+            if (w == 3) sb[l] = l < Lc ? in.bs : 0.f;
         }
+        if (next_job >= 0) cg_fetch(a, in, next_job, tid);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------------- A and P on the matrix cores
     // 10 lower block pairs (R, I); A and P of a pair share the k_I fragments
     // and the decay factors.
     const int badmask = CGATE ? sflag[0] : 0;
     for (int pr = w; pr < 10; pr += 4) {
-        const int R = kPairR[pr], I = kPairI[pr];
+        const int R = pair_row(pr), I = pr - R * (R + 1) / 2;
         if (CGATE && R == I && (badmask >> R) & 1) continue;   // handled by the exact path below
         const int ra = 16 * R + (l & 15);   // operand row (A side)
         const int ca = 16 * I + (l & 15);   // operand row (B side)
@@ -356,18 +401,21 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
                 const float* sKi = smem + SM::kKi;
                 const float* sQg = smem + SM::kQg;
                 const float* cst = smem + SM::kCst;
-                float xk[8], xq[8], xb[8];
+                // rescale both factors to a reference point between the two
+                // blocks (off-diagonal: end of block I; diagonal: middle);
+                // eight consecutive channels per lane, as two 16-byte reads
+                const int frow = (R == I) ? CST_IGM + R : CST_C + offdiag_index(R, I);
+                float xk[8], xq[8], xb[8], fr[8], fc[8];
+                ld8_lds(sKg + ra * KP + k0, xk);
+                ld8_lds(sQg + ra * KP + k0, xq);
+                ld8_lds(sKi + ca * KP + k0, xb);
+                ld8_lds(cst + frow * DK + k0, fr);
+                ld8_lds(cst + (CST_IIM + R) * DK + k0, fc);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int col = k0 + j;
-                    // rescale both factors to a reference point between the
-                    // two blocks (off-diagonal: end of block I; diagonal: middle)
-                    const float fr = (R == I) ? cst[(CST_IGM + R) * DK + col]
-                                              : cst[(CST_C + offdiag_index(R, I)) * DK + col];
-                    const float fc = (R == I) ? cst[(CST_IIM + R) * DK + col] : 1.f;
-                    xk[j] = sKg[ra * KP + col] * fr;
-                    xq[j] = sQg[ra * KP + col] * fr;
-                    xb[j] = sKi[ca * KP + col] * fc;
+                    xk[j] *= fr[j];
+                    xq[j] *= fr[j];
+                    xb[j] *= (R == I) ? fc[j] : 1.f;
                 }
                 fk = split8<P>(xk);
                 fq = split8<P>(xq);
@@ -391,7 +439,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
     }
     if constexpr (CGATE) {
         if (badmask) {
-            __syncthreads();
+            lds_barrier();
             // exact path for diagonal blocks whose in-block decay exceeds the
             // fp16 factor range: sum_c kt_rc kt_ic e^{G_rc - G_ic}, the exponent
             // taken as the sum of log alpha over tokens i+1..r
@@ -421,7 +469,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ------------------------------------------- T = (I + A)^-1, blocked, fp32
     // diagonal 16x16 blocks: wave w inverts block w, lane j < 16 owns column j
@@ -438,7 +486,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[base + r][base + j] = t[r];
     }
-    __syncthreads();
+    lds_barrier();
     // off-diagonal blocks, one block row R at a time on the fp32 matrix cores;
     // wave I < R computes
     //   X_RI = sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .],  T_RI = -T_RR X_RI
@@ -468,7 +516,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sT[16 * R + 4 * g + j][16 * I + i16] = -(T0[j] + T1[j]);
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -510,6 +558,31 @@ __global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
         const size_t base = cs * (size_t)(P * CH * CH);
         store_row16<P>(a.wsT + base, (size_t)CH * CH, r * CH + i0, tv);
         store_row16<P>(a.wsP + base, (size_t)CH * CH, r * CH + i0, pv);
+    }
+}
+
+// One workgroup per chunk, or, with a channel gate, a persistent loop over
+// chunks (job = chunk + NC * sequence) that loads the next chunk's inputs
+// while it works on the current one.
+template <int DK, bool F32IN, bool CGATE, bool CBETA>
+__global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
+    using SM = PrepSmem<DK, CGATE>;
+    __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
+    CgIn<DK, F32IN, CBETA> in;
+    if constexpr (CGATE) {
+        // fp32 inputs would need twice the registers: they are loaded per chunk
+        constexpr bool PREF = !F32IN;
+        const int njobs = a.nseq * a.NC;
+        int job = blockIdx.x;
+        if (PREF && job < njobs) cg_fetch(a, in, job, threadIdx.x);
+        for (; job < njobs; job += gridDim.x) {
+            if (!PREF) cg_fetch(a, in, job, threadIdx.x);
+            const int nj = job + gridDim.x;
+            prep_chunk<DK, F32IN, CGATE, CBETA>(a, smem, job / a.NC, job % a.NC, in,
+                                                PREF && nj < njobs ? nj : -1);
+        }
+    } else {
+        prep_chunk<DK, F32IN, CGATE, CBETA>(a, smem, blockIdx.z * a.H + blockIdx.y, blockIdx.x, in, -1);
     }
 }
 
@@ -830,6 +903,26 @@ __global__ __launch_bounds__(256) void scan_kernel(ChunkArgs a) {
 // launchers
 // ===========================================================================
 
+// Workgroups of `kern` (with `threads` threads, static LDS only) resident on
+// the current device at once: compute units times workgroups per unit.
+// Cached per device and kernel (a device attribute and an occupancy query).
+static long resident_groups(const void* kern, int threads) {
+    struct Entry { const void* k; int dev; long n; };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry& e : cache)
+        if (e.k == kern && e.dev == dev) return e.n;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || per <= 0) per = 1;
+    const long n = (long)cus * per;
+    cache.push_back({kern, dev, n});
+    return n;
+}
+
 template <int DK, bool F32IN, bool CGATE, bool CBETA>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     const int nseq = a.nseq;
@@ -838,6 +931,13 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
         prof_mark(st, kProfPrep);
         if constexpr (!F32IN && !CGATE && !CBETA) {
             e = launch_prep16(a, DK, st);
+        } else if constexpr (CGATE) {
+            auto kern = prep_kernel<DK, F32IN, CGATE, CBETA>;
+            const long njobs = (long)nseq * a.NC;
+            const long slots = resident_groups((const void*)kern, 256);
+            const int grid = (int)(njobs < slots ? njobs : slots);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a);
+            e = hipGetLastError();
         } else {
             dim3 g1(a.NC, a.H, a.B);
             hipLaunchKernelGGL((prep_kernel<DK, F32IN, CGATE, CBETA>), g1, dim3(256), 0, st, a);

@@ -184,6 +184,53 @@ __device__ __forceinline__ Raw8<F32IN> ld_raw8(const void* base, size_t off) {
     return r;
 }
 
+// N (4 or 8) consecutive raw input values as loaded (bf16 bits or fp32 bits).
+template <bool F32IN, int N>
+struct RawN {
+    uint32_t w[F32IN ? N : N / 2];
+};
+
+template <bool F32IN, int N>
+__device__ __forceinline__ RawN<F32IN, N> ld_rawn(const void* base, size_t off) {
+    RawN<F32IN, N> r;
+    constexpr int W = F32IN ? N : N / 2;   // dwords
+    const char* p = static_cast<const char*>(base) + off * (F32IN ? 4 : 2);
+    if constexpr (W % 4 == 0) {
+#pragma unroll
+        for (int v = 0; v < W / 4; ++v) {
+            const uint4 u = reinterpret_cast<const uint4*>(p)[v];
+            r.w[4 * v] = u.x; r.w[4 * v + 1] = u.y; r.w[4 * v + 2] = u.z; r.w[4 * v + 3] = u.w;
+        }
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        r.w[0] = u.x; r.w[1] = u.y;
+    }
+    return r;
+}
+
+template <bool F32IN, int N>
+__device__ __forceinline__ void cvt_rawn(const RawN<F32IN, N>& r, float* x) {
+#pragma unroll
+    for (int j = 0; j < (F32IN ? N : N / 2); ++j) {
+        if constexpr (F32IN) {
+            x[j] = __uint_as_float(r.w[j]);
+        } else {
+            x[2 * j] = __uint_as_float(r.w[j] << 16);
+            x[2 * j + 1] = __uint_as_float(r.w[j] & 0xffff0000u);
+        }
+    }
+}
+
+// Workgroup barrier over LDS only: wait for this wave's own LDS accesses,
+// then s_barrier.  Global memory operations in flight (loads issued ahead,
+// global->LDS copies) are not waited for, unlike __syncthreads.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Raw values to fp32, zeroed when !ok.
 template <bool F32IN>
 __device__ __forceinline__ void cvt_raw8(const Raw8<F32IN>& r, bool ok, float* x) {

@@ -155,15 +155,6 @@ __device__ __forceinline__ const char* uniform_ptr(const void* p) {
     return reinterpret_cast<const char*>(((unsigned long long)hi << 32) | lo);
 }
 
-// Workgroup barrier over LDS only: wait for this wave's own LDS accesses,
-// then s_barrier.  Global->LDS copies in flight are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // Swizzle of 16-byte pieces in a 64-row tile with RB bytes per row: piece p
 // of row r is stored at piece p ^ swz(r).  256-byte rows: 16 consecutive rows
 // land on 16 distinct bank groups; 128-byte rows: two rows share the 64
