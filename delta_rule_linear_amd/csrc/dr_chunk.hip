@@ -106,12 +106,19 @@ __device__ __forceinline__ void ld8_lds(const float* p, float* x) {
 // Off-diagonal pair index of (R, I), R > I: (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
 __device__ __forceinline__ int offdiag_index(int R, int I) { return R * (R - 1) / 2 + I; }
 
+// Threads of the prep workgroup: with a channel gate one per 4 tokens x 4
+// channels (512 at d_k = 128: two waves per SIMD hide each other's
+// latencies), otherwise 256.
+template <int DK, bool CGATE>
+constexpr int prep_threads() { return CGATE ? 4 * DK : 256; }
+
 // One thread's raw inputs of a chunk for the channel-gate prep: tokens
-// 4 tg .. 4 tg + 3, channels CPT cg .. (tg = tid / 16, cg = tid % 16).  Rows
-// past the sequence's end load row 0 of the chunk and are masked at use.
+// 4 tg .. 4 tg + 3, channels 4 cg .. 4 cg + 3 (cg = tid % (DK / 4),
+// tg = tid / (DK / 4)).  Rows past the sequence's end load row 0 of the chunk
+// and are masked at use.
 template <int DK, bool F32IN, bool CBETA>
 struct CgIn {
-    static constexpr int CPT = DK / 16;
+    static constexpr int CPT = 4;
     float la[4][CPT];               // log alpha
     RawN<F32IN, CPT> k[4], q[4];
     RawN<F32IN, CPT> v[CBETA ? 4 : 1];
@@ -121,12 +128,12 @@ struct CgIn {
 
 template <int DK, bool F32IN, bool CBETA>
 __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBETA>& in, int job, int tid) {
-    constexpr int CPT = DK / 16;
+    constexpr int CPT = 4;
     const int seq = job / a.NC, c = job % a.NC;
     const int t0 = c * CH;
     const int Lc = min(CH, a.L - t0);
     const size_t tok0 = (size_t)seq * a.L + t0;
-    const int ch0 = (tid & 15) * CPT, tg = tid >> 4;
+    const int ch0 = (tid % (DK / 4)) * CPT, tg = tid / (DK / 4);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int r = 4 * tg + u;
@@ -153,6 +160,7 @@ template <int DK, bool F32IN, bool CGATE, bool CBETA>
 __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, const int seq, const int c,
                                            CgIn<DK, F32IN, CBETA>& in, const int next_job) {
     constexpr int P = F32IN ? 2 : 1;
+    constexpr int NTH = prep_threads<DK, CGATE>();
     using SM = PrepSmem<DK, CGATE>;
     float(*sA)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kA);
     float(*sP)[65] = reinterpret_cast<float(*)[65]>(smem + SM::kP);
@@ -226,8 +234,8 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
         float* sbnd = smem + SM::kP;   // [13][DK]: 3 R + {0, 1, 2}, then 12: G_63
         constexpr float kL2E = 1.4426950408889634f;
         // thread = (channel group cg: CPT channels, token group tg: 4 tokens)
-        constexpr int CPT = DK / 16;
-        const int cg = tid & 15, tg = tid >> 4;
+        constexpr int CPT = 4;
+        const int cg = tid % (DK / 4), tg = tid / (DK / 4);
         const int ch0 = cg * CPT;
         const size_t pl = (size_t)CH * DK, base = cs * (size_t)(P * CH * DK);
         float G[4][CPT];
@@ -253,9 +261,16 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             float off[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) off[c] = 0.f;
-            for (int t = 0; t < tg; ++t)
+            // the earlier token groups' totals: independent reads, all issued at once
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) off[c] += stot[t * DK + ch0 + c];
+            for (int t = 0; t < 15; ++t) {
+                const float4 x = *reinterpret_cast<const float4*>(stot + t * DK + ch0);
+                const bool e = t < tg;
+                off[0] += e ? x.x : 0.f;
+                off[1] += e ? x.y : 0.f;
+                off[2] += e ? x.z : 0.f;
+                off[3] += e ? x.w : 0.f;
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int r = 4 * tg + u;
@@ -356,7 +371,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     // 10 lower block pairs (R, I); A and P of a pair share the k_I fragments
     // and the decay factors.
     const int badmask = CGATE ? sflag[0] : 0;
-    for (int pr = w; pr < 10; pr += 4) {
+    for (int pr = w; pr < 10; pr += NTH / 64) {
         const int R = pair_row(pr), I = pr - R * (R + 1) / 2;
         if (CGATE && R == I && (badmask >> R) & 1) continue;   // handled by the exact path below
         const int ra = 16 * R + (l & 15);   // operand row (A side)
@@ -405,17 +420,21 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 // blocks (off-diagonal: end of block I; diagonal: middle);
                 // eight consecutive channels per lane, as two 16-byte reads
                 const int frow = (R == I) ? CST_IGM + R : CST_C + offdiag_index(R, I);
-                float xk[8], xq[8], xb[8], fr[8], fc[8];
+                float xk[8], xq[8], xb[8], fr[8];
                 ld8_lds(sKg + ra * KP + k0, xk);
                 ld8_lds(sQg + ra * KP + k0, xq);
                 ld8_lds(sKi + ca * KP + k0, xb);
                 ld8_lds(cst + frow * DK + k0, fr);
-                ld8_lds(cst + (CST_IIM + R) * DK + k0, fc);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     xk[j] *= fr[j];
                     xq[j] *= fr[j];
-                    xb[j] *= (R == I) ? fc[j] : 1.f;
+                }
+                if (R == I) {   // wave-uniform
+                    float fc[8];
+                    ld8_lds(cst + (CST_IIM + R) * DK + k0, fc);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) xb[j] *= fc[j];
                 }
                 fk = split8<P>(xk);
                 fq = split8<P>(xq);
@@ -445,6 +464,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             // taken as the sum of log alpha over tokens i+1..r
             for (int R = 0; R < 4; ++R) {
                 if (!((badmask >> R) & 1)) continue;
+                if (tid >= 256) continue;
                 const int r = 16 * R + (tid >> 4), i = 16 * R + (tid & 15);
                 float accA = 0.f, accP = 0.f;
                 if (i <= r && r < Lc) {
@@ -473,7 +493,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 
     // ------------------------------------------- T = (I + A)^-1, blocked, fp32
     // diagonal 16x16 blocks: wave w inverts block w, lane j < 16 owns column j
-    if (l < 16) {
+    if (w < 4 && l < 16) {
         const int base = 16 * w, j = l;
         float t[16];
 #pragma unroll
@@ -523,7 +543,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     // --------------------------------------------------- outputs T^ and P
     if constexpr (P == 1) {
         // packed lower-block form (tri_off), one 8-column piece per thread and step
-        for (int e = tid; e < 2 * 320; e += 256) {
+        for (int e = tid; e < 2 * 320; e += NTH) {
             const bool isP = e >= 320;
             const int x = isP ? e - 320 : e;
             const int blk = x >> 5, r = (x >> 1) & 15, hh = x & 1;
@@ -544,7 +564,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             half_t* dst = (isP ? a.wsP : a.wsT) + cs * (size_t)(CH * CH) + tri_off(row, c0);
             *reinterpret_cast<half8*>(dst) = hv;
         }
-    } else {
+    } else if (tid < 256) {
         const int r = tid >> 2, i0 = 16 * (tid & 3);
         float tv[16], pv[16];
 #pragma unroll
@@ -565,7 +585,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 // chunks (job = chunk + NC * sequence) that loads the next chunk's inputs
 // while it works on the current one.
 template <int DK, bool F32IN, bool CGATE, bool CBETA>
-__global__ __launch_bounds__(256) void prep_kernel(ChunkArgs a) {
+__global__ __launch_bounds__((prep_threads<DK, CGATE>())) void prep_kernel(ChunkArgs a) {
     using SM = PrepSmem<DK, CGATE>;
     __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
     CgIn<DK, F32IN, CBETA> in;
@@ -934,9 +954,10 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
         } else if constexpr (CGATE) {
             auto kern = prep_kernel<DK, F32IN, CGATE, CBETA>;
             const long njobs = (long)nseq * a.NC;
-            const long slots = resident_groups((const void*)kern, 256);
+            constexpr int NTH = prep_threads<DK, CGATE>();
+            const long slots = resident_groups((const void*)kern, NTH);
             const int grid = (int)(njobs < slots ? njobs : slots);
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, a);
+            hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), 0, st, a);
             e = hipGetLastError();
         } else {
             dim3 g1(a.NC, a.H, a.B);
