@@ -257,20 +257,22 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             for (int c = 0; c < CPT; ++c) stot[tg * DK + ch0 + c] = run[c];
         }
         lds_barrier();
-        {
-            float off[CPT];
+        if (tid < DK) {
+            // one thread per channel: exclusive prefix of the 16 group totals, in place
+            float x[16];
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) off[c] = 0.f;
-            // the earlier token groups' totals: independent reads, all issued at once
+            for (int t = 0; t < 16; ++t) x[t] = stot[t * DK + tid];
+            float run = 0.f;
 #pragma unroll
-            for (int t = 0; t < 15; ++t) {
-                const float4 x = *reinterpret_cast<const float4*>(stot + t * DK + ch0);
-                const bool e = t < tg;
-                off[0] += e ? x.x : 0.f;
-                off[1] += e ? x.y : 0.f;
-                off[2] += e ? x.z : 0.f;
-                off[3] += e ? x.w : 0.f;
+            for (int t = 0; t < 16; ++t) {
+                stot[t * DK + tid] = run;
+                run += x[t];
             }
+        }
+        lds_barrier();
+        {
+            const float4 o4 = *reinterpret_cast<const float4*>(stot + tg * DK + ch0);
+            const float off[CPT] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int r = 4 * tg + u;
@@ -289,13 +291,19 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
         // for the A / P products here, and Q e^{G}, Kt e^{G}, Kt e^{G_63 - G}
         // (and vt) for the scan
         // all four tokens of this thread lie in block R = tg / 4
+        // e^{G_r} = e^{G_{16R}} rowf_r and e^{G_63 - G_r} = e^{G_63 - G_{16R+15}} colf_r:
+        // two exponentials per element (G does not increase, so every factor is <= 1)
         const int R = tg >> 2;
-        float gs2[CPT], ge2[CPT], g632[CPT];
+        float gs2[CPT], ge2[CPT], egs[CPT], e63[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            gs2[c] = sbnd[(3 * R) * DK + ch0 + c] * kL2E;
-            ge2[c] = sbnd[(3 * R + 2) * DK + ch0 + c] * kL2E;
-            g632[c] = sbnd[12 * DK + ch0 + c] * kL2E;
+            const float gs = sbnd[(3 * R) * DK + ch0 + c];
+            const float ge = sbnd[(3 * R + 2) * DK + ch0 + c];
+            const float g63 = sbnd[12 * DK + ch0 + c];
+            gs2[c] = gs * kL2E;
+            ge2[c] = ge * kL2E;
+            egs[c] = __builtin_amdgcn_exp2f(gs2[c]);
+            e63[c] = __builtin_amdgcn_exp2f((g63 - ge) * kL2E);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -317,10 +325,10 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 okg[c] = kt * rowf;
                 oki[c] = kt * colf;
                 oqg[c] = qv * rowf;
-                const float eg = __builtin_amdgcn_exp2f(g2);
+                const float eg = egs[c] * rowf;
                 wq[c] = qv * eg;
                 wks[c] = kt * eg;
-                wkl[c] = kt * __builtin_amdgcn_exp2f(g632[c] - g2);
+                wkl[c] = kt * (e63[c] * colf);
                 wv[c] = CBETA ? (live ? sbv * vx[c] : 0.f) : 0.f;
             }
 #pragma unroll
