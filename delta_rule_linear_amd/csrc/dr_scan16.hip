@@ -540,16 +540,19 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
         // A fragment of a packed triangle: row 16 w + i16, columns 32 s + 8 g
         // .. +7, i.e. block (w, 2 s + g / 2), half g & 1; zero above the
         // diagonal blocks.
+        // (read with tri_frag, zeroed above the diagonal blocks with
+        // tri_mask once the read has landed)
         auto tri_frag = [&](const lchar* tri, int s) {
             const int I = 2 * s + (g >> 1);
             const int Ic = I <= w ? I : w;
-            uint4 f = lds16(tri + tri_block(w, Ic) * 512 + i16 * 32 + 16 * ((g & 1) ^ ((i16 >> 3) & 1)));
-            const uint32_t m = I <= w ? ~0u : 0u;
+            return lds16(tri + tri_block(w, Ic) * 512 + i16 * 32 + 16 * ((g & 1) ^ ((i16 >> 3) & 1)));
+        };
+        auto tri_mask = [&](uint4& f, int s) {
+            const uint32_t m = 2 * s + (g >> 1) <= w ? ~0u : 0u;
             f.x &= m;
             f.y &= m;
             f.z &= m;
             f.w &= m;
-            return f;
         };
         // operands of phases 2 and 3 that depend only on the chunk's tiles,
         // read during phase 1 so that their LDS latency is off the chain
@@ -561,27 +564,39 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             cp.template copy<0>(a, cbuf, seq, cn, n0, l);
         } else {
             // X only: the state fragments are kept for Y = Q S, which is off
-            // the chain and done in phase 2
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+            // the chain and done in phase 2.  Every LDS read of the phase is
+            // issued first, so that one read latency is exposed, not one per
+            // k-step.
+            uint4 kf[DK / 32];
 #pragma unroll
             for (int s = 0; s < DK / 32; ++s) {
-                const uint4 kf = lds16(tile_at<L::RB>(buf + L::KS, ra, 4 * s + g));
+                kf[s] = lds16(tile_at<L::RB>(buf + L::KS, ra, 4 * s + g));
 #pragma unroll
-                for (int p = 0; p < NPL; ++p) {
+                for (int p = 0; p < NPL; ++p)
                     sfr[s][p] = lds16(sS + p * 16 * L::SP + i16 * L::SP + 2 * (32 * s + 8 * g));
-                    X = mfma_raw<BF>(kf, sfr[s][p], X);
-                }
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s) tfr[s] = tri_frag(buf + L::TT, s);
-            f32x4 Rv;
+            uint16_t vb[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * w + 4 * g + j;
-                const uint16_t vb = lds_ld<uint16_t>(buf + L::VT + r * 32 + 2 * i16);
-                const float vv = CBETA ? (float)__builtin_bit_cast(half_t, vb) : bf16_to_f32(vb);
+                vb[j] = lds_ld<uint16_t>(buf + L::VT + r * 32 + 2 * i16);
                 gam[j] = CGATE ? 1.f : gt(r);
                 lam[j] = CGATE ? 1.f : gt(64 + r);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) tri_mask(tfr[s], s);
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < DK / 32; ++s)
+#pragma unroll
+                for (int p = 0; p < NPL; ++p) X = mfma_raw<BF>(kf[s], sfr[s][p], X);
+            f32x4 Rv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float vv = CBETA ? (float)__builtin_bit_cast(half_t, vb[j]) : bf16_to_f32(vb[j]);
                 Rv[j] = vv - gam[j] * X[j];
             }
             st4_terms<false, 1>(sR + i16 * L::RP + 2 * (16 * w + 4 * g), 0, Rv);
@@ -593,19 +608,13 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
         if (copier) {
             cp.template copy<1>(a, cbuf, seq, cn, n0, l);
         } else {
-            U = {0.f, 0.f, 0.f, 0.f};
+            // all LDS reads first: R, then Q and the phase-3 operands that
+            // depend only on the chunk's tiles
+            uint4 rf[2], qf[DK / 32];
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                U = mfma_raw<false>(tfr[s], lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g)), U);
-            // off the chain: Y = Q S, and the phase-3 operands that depend only
-            // on the chunk's tiles
-            Y = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 2; ++s) rf[s] = lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g));
 #pragma unroll
-            for (int s = 0; s < DK / 32; ++s) {
-                const uint4 qf = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
-#pragma unroll
-                for (int p = 0; p < NPL; ++p) Y = mfma_raw<BF>(qf, sfr[s][p], Y);
-            }
+            for (int s = 0; s < DK / 32; ++s) qf[s] = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
 #pragma unroll
             for (int s = 0; s < 2; ++s) pfr[s] = tri_frag(buf + L::PT, s);
             // Kl^T fragments (state row rt + i16, tokens 32 s + 8 g + 0..7) from
@@ -624,11 +633,23 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
                     kfr[t][s] = {lo4.x, lo4.y, hi4.x, hi4.y};
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) tri_mask(pfr[s], s);
+            U = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) U = mfma_raw<false>(tfr[s], rf[s], U);
             st4_terms<false, 1>(sU + i16 * L::RP + 2 * (16 * w + 4 * g), 0, U);
             f32x4 Ul;
 #pragma unroll
             for (int j = 0; j < 4; ++j) Ul[j] = lam[j] * U[j];
             st4_terms<BF, NPL>(sUl + i16 * L::RP + 2 * (16 * w + 4 * g), 16 * L::RP, Ul);
+            // off the chain: Y = Q S
+            Y = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < DK / 32; ++s)
+#pragma unroll
+                for (int p = 0; p < NPL; ++p) Y = mfma_raw<BF>(qf[s], sfr[s][p], Y);
         }
         lds_barrier();
 
@@ -641,12 +662,26 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             // complete; with two, every one but the touch
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(NB == 3 ? L::NCOPY + 1 : 1));
         } else {
+            // all LDS reads first: U, l U and the state decay
+            uint4 uf[2], ulf[2][NPL];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                uf[s] = lds16(sU + i16 * L::RP + 2 * (32 * s + 8 * g));
+#pragma unroll
+                for (int p = 0; p < NPL; ++p)
+                    ulf[s][p] = lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g));
+            }
+            float d63[NTS][4];
+#pragma unroll
+            for (int t = 0; t < NTS; ++t)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) d63[t][j] = CGATE ? gt(16 * (w * NTS + t) + 4 * g + j) : gt(63);
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 O;
 #pragma unroll
             for (int j = 0; j < 4; ++j) O[j] = gam[j] * Y[j];
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                O = mfma_raw<false>(pfr[s], lds16(sU + i16 * L::RP + 2 * (32 * s + 8 * g)), O);
+            for (int s = 0; s < 2; ++s) O = mfma_raw<false>(pfr[s], uf[s], O);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 lds_st(sO + (16 * w + 4 * g + j) * L::OP + 4 * i16, O[j]);
@@ -656,17 +691,11 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
                 const int rt = 16 * (w * NTS + t);
                 f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const uint4 ka = kfr[t][s];
+                for (int s = 0; s < 2; ++s)
 #pragma unroll
-                    for (int p = 0; p < NPL; ++p)
-                        acc[s] = mfma_raw<BF>(ka, lds16(sUl + p * 16 * L::RP + i16 * L::RP + 2 * (32 * s + 8 * g)), acc[s]);
-                }
+                    for (int p = 0; p < NPL; ++p) acc[s] = mfma_raw<BF>(kfr[t][s], ulf[s][p], acc[s]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float d63 = CGATE ? gt(rt + 4 * g + j) : gt(63);
-                    S[t][j] = d63 * S[t][j] + (acc[0][j] + acc[1][j]);
-                }
+                for (int j = 0; j < 4; ++j) S[t][j] = d63[t][j] * S[t][j] + (acc[0][j] + acc[1][j]);
                 st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, S[t]);
             }
         }
