@@ -198,40 +198,45 @@ __device__ __forceinline__ void st4_terms(lchar* dst, int plane, const f32x4& v)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // LDS plan (bytes).  NB operand buffers, each
-//   [Kl 64 x RB][Ks 64 x RB, channel gate only][Q 64 x RB][T^ packed][P packed]
-//   [V 64 x 32][gate factors 1024]
+//   [Kl 64 x RB][Ks 64 x RB, channel gate only][Q 64 x RB, channel gate only]
+//   [T^ packed][P packed][V 64 x 32][gate factors 1024]
+// Without a channel gate (QREG) Q is not staged: the compute waves load their
+// Q fragments into registers one chunk ahead, which leaves the copy waves
+// less to issue.  With a channel gate the copy waves carry Q as well (the
+// compute waves' own loads would queue behind the larger copies).
 // and the working area [S^T NPL x 16 x SP][R^T 16 x RP][U^T 16 x RP]
 // [(lU)^T NPL x 16 x RP][O 64 x OP].
 template <int DK, bool RAW, bool CGATE>
 struct SD {
     static constexpr int NPL = RAW ? 2 : 1;
-    static constexpr int NB = CGATE ? 2 : 3;
+    static constexpr bool QREG = !CGATE;
+    static constexpr int NB = QREG ? 3 : 2;
     static constexpr int RB = DK * 2;               // bytes per K / Q row
     static constexpr int KL = 0;
     static constexpr int KS = CGATE ? KL + 64 * RB : KL;   // Ks == Kl unless the gate is per channel
     static constexpr int QT = KS + 64 * RB;
-    static constexpr int TT = QT + 64 * RB;
+    static constexpr int TT = QT + (QREG ? 0 : 64 * RB);
     static constexpr int PT = TT + kTriBytes;
     static constexpr int VT = PT + kTriBytes;
     static constexpr int GT = VT + 64 * 32;
     static constexpr int BUF = GT + 1024;
     static constexpr int SP = (DK + 8) * 2;          // bytes per S^T row
     static constexpr int RP = (CH + 8) * 2;          // bytes per token-major row
-    static constexpr int OP = 16 * 4 + 16;           // bytes per O row (fp32)
     static constexpr int WS = 0;
     static constexpr int WR = WS + NPL * 16 * SP;
     static constexpr int WU = WR + 16 * RP;
     static constexpr int WUL = WU + 16 * RP;
+    static constexpr int OP = 16 * 4 + 16;           // bytes per O row (fp32)
     static constexpr int WO = WUL + NPL * 16 * RP;
     static constexpr int WORK = WO + 64 * OP;
     static constexpr int TOTAL = NB * BUF + WORK + 1024;
     // copy waves, and the copy instructions each issues per chunk: a quarter
-    // of every K / Q tile (RB / 16 instructions each) and four of the 16
+    // of every K (and Q) tile (RB / 16 instructions each) and four of the 16
     // slots holding T^ (5), P (5), the V tile (2), the gate factors (1) and
     // three repeats of the gate copy, so that every copy wave issues the same
     // count
     static constexpr int NCW = 4;
-    static constexpr int NCOPY = (CGATE ? 3 : 2) * (RB / 16) / NCW + 4;
+    static constexpr int NCOPY = ((CGATE ? 2 : 1) + (QREG ? 0 : 1)) * (RB / 16) / NCW + 4;
 };
 
 // Copy wave cw's quarter of a [64][RB]-byte tile of 16-bit values (row r at
@@ -252,7 +257,7 @@ __device__ __forceinline__ void copy_tile(const uint16_t* src, size_t pitch, int
 }
 
 // Part `PART` of the copies of chunk c into buffer `buf`, copy wave cw's share:
-//   0: Kl;  1: Q;  2: Ks (channel gate), T^, P, the V tile, the gate factors.
+//   0: Kl;  1: Q (channel gate);  2: Ks (channel gate), T^, P, the V tile, the gate factors.
 template <int DK, bool RAW, bool CGATE, bool CBETA, int PART>
 __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq, int c, int n0, int l, int cw) {
     using L = SD<DK, RAW, CGATE>;
@@ -298,10 +303,7 @@ __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq
             }
         }
     } else {
-        if constexpr (RAW)
-            copy_tile<L::RB>(static_cast<const uint16_t*>(a.q) + tok0 * DK, DK, Lc, buf + L::QT, l, cw);
-        else
-            copy_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsQ) + obase, DK, CH, buf + L::QT, l, cw);
+        copy_tile<L::RB>(reinterpret_cast<const uint16_t*>(a.wsQ) + obase, DK, CH, buf + L::QT, l, cw);
     }
 }
 
@@ -326,9 +328,9 @@ struct Copier {
     static constexpr int NTI = PPR / 4;      // tile instructions per copy wave
     unsigned toff[NTI];   // lane offsets in a K / Q tile (row pitch DK)
     unsigned soff[4];     // lane offsets of the part-1 slots
+    unsigned ooff;        // output lane offset (elements)
     const char* wbase;    // this lane's warm-up line in chunk 0
     unsigned wstride;     // and its per-chunk stride
-    unsigned ooff;        // output lane offset (elements)
     int cw;
 
     __device__ __forceinline__ void init(const ChunkArgs& a, int seq, int n0, int l, int cw_, int tile, int NT) {
@@ -402,18 +404,15 @@ struct Copier {
         const size_t tok0 = (size_t)seq * a.L + (size_t)cn * CH;
         const size_t cs = (size_t)seq * a.NC + cn;
         const size_t obase = cs * (size_t)(CH * DK) * 2;   // bytes
-        if constexpr (PART == 0 || PART == 1) {
-            const char* src;
-            if constexpr (PART == 0)
-                src = RAW ? static_cast<const char*>(a.k) + tok0 * DK * 2
-                          : reinterpret_cast<const char*>(CGATE ? a.wsKl : a.wsKs) + obase;
-            else
-                src = RAW ? static_cast<const char*>(a.q) + tok0 * DK * 2
-                          : reinterpret_cast<const char*>(a.wsQ) + obase;
-            src = uniform_ptr(src);
-            lchar* dst = buf + (PART == 0 ? L::KL : L::QT);
+        if constexpr (PART == 0) {
+            const char* src = uniform_ptr(RAW ? static_cast<const char*>(a.k) + tok0 * DK * 2
+                                              : reinterpret_cast<const char*>(CGATE ? a.wsKl : a.wsKs) + obase);
 #pragma unroll
-            for (int jj = 0; jj < NTI; ++jj) dma16s(src, toff[jj], dst + (cw + 4 * jj) * 1024);
+            for (int jj = 0; jj < NTI; ++jj) dma16s(src, toff[jj], buf + L::KL + (cw + 4 * jj) * 1024);
+        } else if constexpr (PART == 1) {
+            const char* src = uniform_ptr(reinterpret_cast<const char*>(a.wsQ) + obase);
+#pragma unroll
+            for (int jj = 0; jj < NTI; ++jj) dma16s(src, toff[jj], buf + L::QT + (cw + 4 * jj) * 1024);
         } else {
             if constexpr (CGATE) {
                 const char* src = uniform_ptr(reinterpret_cast<const char*>(a.wsKs) + obase);
@@ -444,7 +443,9 @@ struct Copier {
         dma4(p, sink);
     }
 
-    // chunk cc's output rows 16 cw .. 16 cw + 15 from sO
+    // chunk cc's output rows 16 cw .. 16 cw + 15 from sO.  The LDS read waits
+    // (lgkmcnt) for this wave's global->LDS copies issued before it as well,
+    // so it is placed where those have long landed.
     __device__ __forceinline__ void store_o(const ChunkArgs& a, const lchar* sO, int seq, int cc, int l) const {
         const int t0 = cc * CH;
         const int Lc = min(CH, a.L - t0);
@@ -499,6 +500,13 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
     lchar* sUl = work + L::WUL;
     lchar* sO = work + L::WO;
 
+    // Barrier.  On gfx950 a wave's LDS counter also covers its global->LDS
+    // copies in flight, so at each barrier the copy waves wait for the copies
+    // they issued in that phase.  Measured, that is faster than letting the
+    // copies run on: unthrottled copies fill the memory pipeline, and the
+    // compute waves' own loads and stores then wait at issue.
+    auto sync = [&]() { lds_barrier(); };
+
     Copier<DK, RAW, CGATE, CBETA> cp;
     if (copier) cp.init(a, seq, n0, l, cw, tile, NT);
     // chunks that are whole (only those are touched ahead)
@@ -517,19 +525,35 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
         }
     } else {
         cp.template copy<0>(a, b0, seq, 0, n0, l);
-        cp.template copy<1>(a, b0, seq, 0, n0, l);
+        if constexpr (!L::QREG) cp.template copy<1>(a, b0, seq, 0, n0, l);
         cp.template copy<2>(a, b0, seq, 0, n0, l);
         if constexpr (NB == 3) {
             const int c1 = min(1, a.NC - 1);
             cp.template copy<0>(a, b1, seq, c1, n0, l);
-            cp.template copy<1>(a, b1, seq, c1, n0, l);
             cp.template copy<2>(a, b1, seq, c1, n0, l);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(L::NCOPY));   // this wave's copies of chunk 0 have landed
         } else {
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
     }
-    lds_barrier();
+    // Q fragments of row 16 w + i16 (columns 32 s + 8 g .. +7), loaded into
+    // registers by the compute waves one chunk ahead; rows past a sequence's
+    // end load row 0 of the chunk (their output is never stored)
+    uint4 qn[DK / 32];
+    auto fetch_q = [&](int cq) {
+        const int t0 = cq * CH;
+        const int Lc = min(CH, a.L - t0);
+        const int r = ra < Lc ? ra : 0;
+        const uint16_t* src = RAW ? static_cast<const uint16_t*>(a.q) + ((size_t)seq * a.L + t0 + r) * DK
+                                  : reinterpret_cast<const uint16_t*>(a.wsQ) +
+                                        ((size_t)seq * a.NC + cq) * (size_t)(CH * DK) + (size_t)ra * DK;
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) qn[s] = *reinterpret_cast<const uint4*>(src + 32 * s + 8 * g);
+    };
+    if constexpr (L::QREG) {
+        if (!copier) fetch_q(0);
+    }
+    sync();
 
     // one chunk: operands in `buf`; the copy wave fills `cbuf` with chunk
     // c + NB - 1 (clamped to the last chunk: a buffer nobody reads again)
@@ -601,12 +625,12 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             }
             st4_terms<false, 1>(sR + i16 * L::RP + 2 * (16 * w + 4 * g), 0, Rv);
         }
-        lds_barrier();
+        sync();
 
         // ---------------- phase 2: U = T^ R (and l U for the state update), Y = Q S
         f32x4 U;
         if (copier) {
-            cp.template copy<1>(a, cbuf, seq, cn, n0, l);
+            if constexpr (!L::QREG) cp.template copy<1>(a, cbuf, seq, cn, n0, l);
         } else {
             // all LDS reads first: R, then Q and the phase-3 operands that
             // depend only on the chunk's tiles
@@ -614,7 +638,8 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) rf[s] = lds16(sR + i16 * L::RP + 2 * (32 * s + 8 * g));
 #pragma unroll
-            for (int s = 0; s < DK / 32; ++s) qf[s] = lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
+            for (int s = 0; s < DK / 32; ++s)
+                qf[s] = L::QREG ? qn[s] : lds16(tile_at<L::RB>(buf + L::QT, ra, 4 * s + g));
 #pragma unroll
             for (int s = 0; s < 2; ++s) pfr[s] = tri_frag(buf + L::PT, s);
             // Kl^T fragments (state row rt + i16, tokens 32 s + 8 g + 0..7) from
@@ -650,8 +675,9 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             for (int s = 0; s < DK / 32; ++s)
 #pragma unroll
                 for (int p = 0; p < NPL; ++p) Y = mfma_raw<BF>(qf[s], sfr[s][p], Y);
+            if constexpr (L::QREG) fetch_q(min(c + 1, a.NC - 1));
         }
-        lds_barrier();
+        sync();
 
         // ---------------- phase 3: O = g Y + P U; S = g63 S + Kl^T (l U)
         if (copier) {
@@ -682,6 +708,9 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             for (int j = 0; j < 4; ++j) O[j] = gam[j] * Y[j];
 #pragma unroll
             for (int s = 0; s < 2; ++s) O = mfma_raw<false>(pfr[s], uf[s], O);
+            // to LDS; the copy waves store it to global memory during the
+            // next chunk (global stores would block these waves at issue
+            // behind the copies)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 lds_st(sO + (16 * w + 4 * g + j) * L::OP + 4 * i16, O[j]);
@@ -699,7 +728,7 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
                 st4_terms<BF, NPL>(sS + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, S[t]);
             }
         }
-        lds_barrier();
+        sync();
     };
 
     for (int c = 0; c < a.NC; c += NB) {
