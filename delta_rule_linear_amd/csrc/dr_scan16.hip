@@ -584,7 +584,9 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
 
         // ---------------- phase 1: X = Ks S, R = V - g X
         if (copier) {
-            if (c > 0) cp.store_o(a, sO, seq, c - 1, l);
+            if constexpr (!L::QREG) {
+                if (c > 0) cp.store_o(a, sO, seq, c - 1, l);
+            }
             cp.template copy<0>(a, cbuf, seq, cn, n0, l);
         } else {
             // X only: the state fragments are kept for Y = Q S, which is off
@@ -630,7 +632,12 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
         // ---------------- phase 2: U = T^ R (and l U for the state update), Y = Q S
         f32x4 U;
         if (copier) {
-            if constexpr (!L::QREG) cp.template copy<1>(a, cbuf, seq, cn, n0, l);
+            if constexpr (!L::QREG) {
+                cp.template copy<1>(a, cbuf, seq, cn, n0, l);
+            } else {
+                // the previous chunk's output (sO is rewritten in phase 3)
+                if (c > 0) cp.store_o(a, sO, seq, c - 1, l);
+            }
         } else {
             // all LDS reads first: R, then Q and the phase-3 operands that
             // depend only on the chunk's tiles
