@@ -146,33 +146,56 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
         gcol[R] = sg[16 * R + i16] * kLog2e;
     }
 
-    // A and P, 16 x 16 block pairs (R, I), R >= I, on the bf16 matrix cores:
-    // both share the k_I fragments and the decay factors e^{G_r - G_i}
-    for (int pr = w; pr < 10; pr += 4) {
-        // lower block pairs in order: 0,0 1,0 1,1 2,0 2,1 2,2 3,0 3,1 3,2 3,3
-        const int R = pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3;
-        const int I = pr - R * (R + 1) / 2;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+    // A and P, 16 x 16 block pairs (R, I), R >= I, on the bf16 matrix cores.
+    // A and P of a pair share the k_I fragments and the decay factors
+    // e^{G_r - G_i}; the pairs of a wave share the block row R, so its k_R and
+    // q_R fragments are read once: wave 0 takes (3, 0..2), wave 1 (2, 0..2),
+    // wave 2 (1, 0..1), wave 3 (0, 0) and (3, 3).
+    auto pair_group = [&](const int R, const int I0, const int NI) {
+        f32x4 accA[3], accP[3];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) accA[t] = accP[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
-            const uint4 kb = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::KT, 16 * I + i16, 4 * s + g));
             const uint4 ka = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::KT, 16 * R + i16, 4 * s + g));
             const uint4 qa = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::QT, 16 * R + i16, 4 * s + g));
-            accA = mfma_bf16(ka, kb, accA);
-            accP = mfma_bf16(qa, kb, accP);
-        }
-        const float gi = I == 0 ? gcol[0] : I == 1 ? gcol[1] : I == 2 ? gcol[2] : gcol[3];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
-            const float gr = R == 0 ? grow[0][j] : R == 1 ? grow[1][j] : R == 2 ? grow[2][j] : grow[3][j];
-            const float br = R == 0 ? brow[0][j] : R == 1 ? brow[1][j] : R == 2 ? brow[2][j] : brow[3][j];
-            const float f = __builtin_amdgcn_exp2f(gr - gi);   // e^{G_r - G_i} <= 1
-            const bool live = r < Lc;
-            sA[r][i] = (live && i < r) ? accA[j] * f * br : 0.f;
-            // P to the workspace, packed: 16 lanes write one 32-byte block row
-            a.wsP[cs * (size_t)(CH * CH) + tri_off(r, i)] = (half_t)((live && i <= r) ? accP[j] * f : 0.f);
+            for (int t = 0; t < 3; ++t) {
+                if (t < NI) {   // wave-uniform
+                    const int I = I0 + t;
+                    const uint4 kb = I == R ? ka
+                                            : *reinterpret_cast<const uint4*>(
+                                                  tile_at<L::RB>(smem + L::KT, 16 * I + i16, 4 * s + g));
+                    accA[t] = mfma_bf16(ka, kb, accA[t]);
+                    accP[t] = mfma_bf16(qa, kb, accP[t]);
+                }
+            }
         }
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            if (t < NI) {
+                const int I = I0 + t;
+                const float gi = I == 0 ? gcol[0] : I == 1 ? gcol[1] : I == 2 ? gcol[2] : gcol[3];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
+                    const float gr = R == 0 ? grow[0][j] : R == 1 ? grow[1][j] : R == 2 ? grow[2][j] : grow[3][j];
+                    const float br = R == 0 ? brow[0][j] : R == 1 ? brow[1][j] : R == 2 ? brow[2][j] : brow[3][j];
+                    const float f = __builtin_amdgcn_exp2f(gr - gi);   // e^{G_r - G_i} <= 1
+                    const bool live = r < Lc;
+                    sA[r][i] = (live && i < r) ? accA[t][j] * f * br : 0.f;
+                    // P to the workspace, packed: 16 lanes write one 32-byte block row
+                    a.wsP[cs * (size_t)(CH * CH) + tri_off(r, i)] = (half_t)((live && i <= r) ? accP[t][j] * f : 0.f);
+                }
+            }
+        }
+    };
+    if (w == 0) pair_group(3, 0, 3);
+    else if (w == 1) pair_group(2, 0, 3);
+    else if (w == 2) pair_group(1, 0, 2);
+    else {
+        pair_group(0, 0, 1);
+        pair_group(3, 3, 1);
     }
     __syncthreads();
 
