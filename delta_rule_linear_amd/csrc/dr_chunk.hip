@@ -51,11 +51,6 @@ namespace dr {
 // prep kernel
 // ===========================================================================
 
-// Lower-triangular 16x16 block pair number pr = R (R + 1) / 2 + I, R >= I,
-// of a 64-token chunk: (0,0) (1,0) (1,1) (2,0) ... (3,3).  Arithmetic, not a
-// table: a table load would be a vector-memory load, and waiting for it would
-// also wait for every global load issued before it.
-__device__ __forceinline__ int pair_row(int pr) { return pr < 1 ? 0 : pr < 3 ? 1 : pr < 6 ? 2 : 3; }
 
 // Largest |G_r - G_m| (m = block middle) for which a diagonal block's factors
 // e^{G_r - G_m}, e^{G_m - G_i} stay in fp16's normal range.
@@ -376,92 +371,131 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     lds_barrier();
 
     // ------------------------------------------------- A and P on the matrix cores
-    // 10 lower block pairs (R, I); A and P of a pair share the k_I fragments
-    // and the decay factors.
+    // 10 lower block pairs (R, I).  A and P of a pair share the k_I fragments
+    // and the decay factors; the pairs of a wave share the block row R, so its
+    // k_R and q_R rows are read once per k-step.  Pairs per wave: with 8 waves
+    // (3,0-1) (3,2-3) (2,0-1) (2,2) (1,0-1) (0,0); with 4 waves (3,0-2)
+    // (2,0-2) (1,0-1) and (0,0) + (3,3).
     const int badmask = CGATE ? sflag[0] : 0;
-    for (int pr = w; pr < 10; pr += NTH / 64) {
-        const int R = pair_row(pr), I = pr - R * (R + 1) / 2;
-        if (CGATE && R == I && (badmask >> R) & 1) continue;   // handled by the exact path below
+    auto pair_group = [&](const int R, const int I0, const int NI) {
         const int ra = 16 * R + (l & 15);   // operand row (A side)
-        const int ca = 16 * I + (l & 15);   // operand row (B side)
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+        const int rac = ra < Lc ? ra : 0;
+        f32x4 accA[2], accP[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) accA[t] = accP[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 accA2 = {0.f, 0.f, 0.f, 0.f}, accP2 = accA2;   // third pair (4 waves only)
 #pragma unroll
         for (int s = 0; s < DK / 32; ++s) {
             const int k0 = 32 * s + 8 * (l >> 4);
-            Frag<P> fk, fq, fb;
+            // A side: the raw rows of block R
+            float xk[8], xq[8];
             if constexpr (!CGATE) {
-                const int rac = ra < Lc ? ra : 0, cac = ca < Lc ? ca : 0;
-                const Raw8<F32IN> rwk = ld_raw8<F32IN>(a.k, (tok0 + rac) * DK + k0);
-                const Raw8<F32IN> rwq = ld_raw8<F32IN>(a.q, (tok0 + rac) * DK + k0);
-                const Raw8<F32IN> rwb = ld_raw8<F32IN>(a.k, (tok0 + cac) * DK + k0);
-                if constexpr (!CBETA) {
-                    fk = raw_to_frag<F32IN, P>(rwk, ra < Lc);
-                    fq = raw_to_frag<F32IN, P>(rwq, ra < Lc);
-                    fb = raw_to_frag<F32IN, P>(rwb, ca < Lc);
-                } else {
-                    float xk[8], xq[8], xb[8], ba[8], bb[8];
-                    const float4* pa = reinterpret_cast<const float4*>(a.beta + (tok0 + rac) * DK + k0);
-                    const float4* pb = reinterpret_cast<const float4*>(a.beta + (tok0 + cac) * DK + k0);
-                    *reinterpret_cast<float4*>(ba) = pa[0];
-                    *reinterpret_cast<float4*>(ba + 4) = pa[1];
-                    *reinterpret_cast<float4*>(bb) = pb[0];
-                    *reinterpret_cast<float4*>(bb + 4) = pb[1];
-                    cvt_raw8<F32IN>(rwk, ra < Lc, xk);
-                    cvt_raw8<F32IN>(rwq, ra < Lc, xq);
-                    cvt_raw8<F32IN>(rwb, ca < Lc, xb);
+                cvt_raw8<F32IN>(ld_raw8<F32IN>(a.k, (tok0 + rac) * DK + k0), ra < Lc, xk);
+                cvt_raw8<F32IN>(ld_raw8<F32IN>(a.q, (tok0 + rac) * DK + k0), ra < Lc, xq);
+                if constexpr (CBETA) {
+                    float ba[8];
+                    load_f32_n<8>(a.beta + (tok0 + rac) * DK + k0, ba);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        xk[j] *= sqrtf(ba[j]);
-                        xb[j] *= sqrtf(bb[j]);
-                    }
-                    fk = split8<P>(xk);
-                    fq = split8<P>(xq);
-                    fb = split8<P>(xb);
+                    for (int j = 0; j < 8; ++j) xk[j] *= sqrtf(ba[j]);
                 }
             } else {
-                constexpr int KP = SM::KP;
-                const float* sKg = smem + SM::kKg;
-                const float* sKi = smem + SM::kKi;
-                const float* sQg = smem + SM::kQg;
-                const float* cst = smem + SM::kCst;
-                // rescale both factors to a reference point between the two
-                // blocks (off-diagonal: end of block I; diagonal: middle);
-                // eight consecutive channels per lane, as two 16-byte reads
-                const int frow = (R == I) ? CST_IGM + R : CST_C + offdiag_index(R, I);
-                float xk[8], xq[8], xb[8], fr[8];
-                ld8_lds(sKg + ra * KP + k0, xk);
-                ld8_lds(sQg + ra * KP + k0, xq);
-                ld8_lds(sKi + ca * KP + k0, xb);
-                ld8_lds(cst + frow * DK + k0, fr);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    xk[j] *= fr[j];
-                    xq[j] *= fr[j];
-                }
-                if (R == I) {   // wave-uniform
-                    float fc[8];
-                    ld8_lds(cst + (CST_IIM + R) * DK + k0, fc);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) xb[j] *= fc[j];
-                }
+                ld8_lds(smem + SM::kKg + ra * SM::KP + k0, xk);
+                ld8_lds(smem + SM::kQg + ra * SM::KP + k0, xq);
+            }
+            Frag<P> fk, fq;
+            if constexpr (!CGATE) {
                 fk = split8<P>(xk);
                 fq = split8<P>(xq);
-                fb = split8<P>(xb);
             }
-            accA = mma<P, P>(fk, fb, accA);
-            accP = mma<P, P>(fq, fb, accP);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                if (t < NI) {   // wave-uniform
+                    const int I = I0 + t;
+                    if (CGATE && R == I && (badmask >> R) & 1) continue;   // exact path below
+                    const int ca = 16 * I + (l & 15);   // operand row (B side)
+                    float xb[8];
+                    if constexpr (!CGATE) {
+                        const int cac = ca < Lc ? ca : 0;
+                        cvt_raw8<F32IN>(ld_raw8<F32IN>(a.k, (tok0 + cac) * DK + k0), ca < Lc, xb);
+                        if constexpr (CBETA) {
+                            float bb[8];
+                            load_f32_n<8>(a.beta + (tok0 + cac) * DK + k0, bb);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) xb[j] *= sqrtf(bb[j]);
+                        }
+                    } else {
+                        const float* cst = smem + SM::kCst;
+                        // rescale both factors to a reference point between
+                        // the two blocks (off-diagonal: end of block I;
+                        // diagonal: middle)
+                        const int frow = (R == I) ? CST_IGM + R : CST_C + offdiag_index(R, I);
+                        float fr[8], yk[8], yq[8];
+                        ld8_lds(smem + SM::kKi + ca * SM::KP + k0, xb);
+                        ld8_lds(cst + frow * DK + k0, fr);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            yk[j] = xk[j] * fr[j];
+                            yq[j] = xq[j] * fr[j];
+                        }
+                        if (R == I) {   // wave-uniform
+                            float fc[8];
+                            ld8_lds(cst + (CST_IIM + R) * DK + k0, fc);
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) xb[j] *= fc[j];
+                        }
+                        fk = split8<P>(yk);
+                        fq = split8<P>(yq);
+                    }
+                    const Frag<P> fb = split8<P>(xb);
+                    if (t == 0) {
+                        accA[0] = mma<P, P>(fk, fb, accA[0]);
+                        accP[0] = mma<P, P>(fq, fb, accP[0]);
+                    } else if (t == 1) {
+                        accA[1] = mma<P, P>(fk, fb, accA[1]);
+                        accP[1] = mma<P, P>(fq, fb, accP[1]);
+                    } else {
+                        accA2 = mma<P, P>(fk, fb, accA2);
+                        accP2 = mma<P, P>(fq, fb, accP2);
+                    }
+                }
+            }
         }
         // gate factors and masks; write the blocks to LDS
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * R + 4 * (l >> 4) + j;
-            const int i = 16 * I + (l & 15);
-            float dec = 1.f;
-            if constexpr (!CGATE) dec = (i <= r) ? expf(sg[r] - sg[i]) : 0.f;
-            sP[r][i] = (i <= r) ? accP[j] * dec : 0.f;
-            float va = accA[j] * dec;
-            if constexpr (!CBETA) va *= sb[r];
-            sA[r][i] = (i < r) ? va : 0.f;
+        for (int t = 0; t < 3; ++t) {
+            if (t < NI) {
+                const int I = I0 + t;
+                if (CGATE && R == I && (badmask >> R) & 1) continue;
+                const f32x4 cA = t == 0 ? accA[0] : t == 1 ? accA[1] : accA2;
+                const f32x4 cP = t == 0 ? accP[0] : t == 1 ? accP[1] : accP2;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * R + 4 * (l >> 4) + j;
+                    const int i = 16 * I + (l & 15);
+                    float dec = 1.f;
+                    if constexpr (!CGATE) dec = (i <= r) ? expf(sg[r] - sg[i]) : 0.f;
+                    sP[r][i] = (i <= r) ? cP[j] * dec : 0.f;
+                    float va = cA[j] * dec;
+                    if constexpr (!CBETA) va *= sb[r];
+                    sA[r][i] = (i < r) ? va : 0.f;
+                }
+            }
+        }
+    };
+    if constexpr (NTH / 64 == 8) {
+        if (w == 0) pair_group(3, 0, 2);
+        else if (w == 1) pair_group(3, 2, 2);
+        else if (w == 2) pair_group(2, 0, 2);
+        else if (w == 3) pair_group(2, 2, 1);
+        else if (w == 4) pair_group(1, 0, 2);
+        else if (w == 5) pair_group(0, 0, 1);
+    } else {
+        if (w == 0) pair_group(3, 0, 3);
+        else if (w == 1) pair_group(2, 0, 3);
+        else if (w == 2) pair_group(1, 0, 2);
+        else {
+            pair_group(0, 0, 1);
+            pair_group(3, 3, 1);
         }
     }
     if constexpr (CGATE) {
