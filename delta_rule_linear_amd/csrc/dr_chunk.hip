@@ -121,9 +121,13 @@ struct CgIn {
     float bs;                       // scalar beta of token tid % 64
 };
 
-template <int DK, bool F32IN, bool CBETA>
+// Part PART of the loads (0: log alpha and k, 1: q and scalar beta, 2: channel
+// beta and v, -1: all), so that a chunk's loads can be spread over the next
+// chunk's phases instead of queueing behind one another.
+template <int DK, bool F32IN, bool CBETA, int PART = -1>
 __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBETA>& in, int job, int tid) {
     constexpr int CPT = 4;
+    constexpr bool P0 = PART < 0 || PART == 0, P1 = PART < 0 || PART == 1, P2 = PART < 0 || PART == 2;
     const int seq = job / a.NC, c = job % a.NC;
     const int t0 = c * CH;
     const int Lc = min(CH, a.L - t0);
@@ -133,15 +137,17 @@ __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBE
     for (int u = 0; u < 4; ++u) {
         const int r = 4 * tg + u;
         const size_t row = tok0 + (r < Lc ? r : 0);
-        load_f32_n<CPT>(a.log_alpha + row * DK + ch0, in.la[u]);
-        in.k[u] = ld_rawn<F32IN, CPT>(a.k, row * DK + ch0);
-        in.q[u] = ld_rawn<F32IN, CPT>(a.q, row * DK + ch0);
-        if constexpr (CBETA) {
+        if constexpr (P0) {
+            load_f32_n<CPT>(a.log_alpha + row * DK + ch0, in.la[u]);
+            in.k[u] = ld_rawn<F32IN, CPT>(a.k, row * DK + ch0);
+        }
+        if constexpr (P1) in.q[u] = ld_rawn<F32IN, CPT>(a.q, row * DK + ch0);
+        if constexpr (CBETA && P2) {
             load_f32_n<CPT>(a.beta + row * DK + ch0, in.be[u]);
             in.v[u] = ld_rawn<F32IN, CPT>(a.v, row * a.Dv + ch0);
         }
     }
-    if constexpr (!CBETA) {
+    if constexpr (!CBETA && P1) {
         const int r = tid & 63;
         in.bs = a.beta[tok0 + (r < Lc ? r : 0)];
     }
@@ -366,7 +372,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
         if constexpr (!CBETA) {
             if (w == 3) sb[l] = l < Lc ? in.bs : 0.f;
         }
-        if (next_job >= 0) cg_fetch(a, in, next_job, tid);
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, 0>(a, in, next_job, tid);
     }
     lds_barrier();
 
@@ -534,6 +540,9 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     lds_barrier();
 
     // ------------------------------------------- T = (I + A)^-1, blocked, fp32
+    if constexpr (CGATE) {
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, 1>(a, in, next_job, tid);
+    }
     // diagonal 16x16 blocks: wave w inverts block w, lane j < 16 owns column j
     if (w < 4 && l < 16) {
         const int base = 16 * w, j = l;
@@ -549,6 +558,9 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
         for (int r = 0; r < 16; ++r) sT[base + r][base + j] = t[r];
     }
     lds_barrier();
+    if constexpr (CGATE) {
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, 2>(a, in, next_job, tid);
+    }
     // off-diagonal blocks, one block row R at a time on the fp32 matrix cores;
     // wave I < R computes
     //   X_RI = sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .],  T_RI = -T_RR X_RI
