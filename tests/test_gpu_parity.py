@@ -82,6 +82,19 @@ def test_strong_channel_gate_exact_path():
     _check(p)
 
 
+@pytest.mark.parametrize("beta_mode", ["scalar", "channel"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_channel_prep_loop_uneven_jobs(beta_mode, D):
+    # channel-gate preparation runs a persistent loop over chunks with the next
+    # chunk's inputs loaded ahead: 5 x 61 = 305 chunks on a grid of one
+    # workgroup per compute unit, so some workgroups take two chunks and others
+    # one, and the last chunk of each sequence is ragged
+    p = inputs.make_chunk_problem(1, 5, 64 * 60 + 17, D, D, gate="channel", beta_mode=beta_mode,
+                                  log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=9,
+                                  name=f"cg-loop-{beta_mode}-D{D}")
+    _check(p)
+
+
 def test_very_strong_scalar_gate():
     p = inputs.make_chunk_problem(1, 2, 128, 64, 64, gate="scalar", log_alpha_range=(-20.0, -5.0),
                                   s0_var=0.01, seed=7, name="very-strong-scalar")
