@@ -5,14 +5,19 @@
 // S <- g63 S + Kl^T (l U).  Built around the data movement:
 //
 //  * One workgroup per (sequence, 16-column tile of S): four compute waves
-//    and one copy wave.  The copy wave issues every global memory operation
-//    of the chunk loop: the chunk operand tiles (Kl, Ks, Q, T^, P, the V
-//    tile, gate factors) straight into LDS with 16-byte global->LDS loads,
-//    two chunks ahead into a triple buffer (double with a channel gate, whose
-//    tiles are larger), a one-dword touch of the chunk four ahead to start
-//    its HBM reads early, and the coalesced store of the previous chunk's
-//    output from LDS.  Vector-memory issue stalls (the copies are 45-61
-//    1 KiB instructions per chunk) thus never hold up the compute waves.
+//    and four copy waves.  The copy waves issue the chunk loop's global
+//    memory operations: the chunk operand tiles (Kl, Ks and Q with a channel
+//    gate, T^, P, the V tile, gate factors) straight into LDS with 16-byte
+//    global->LDS loads, two chunks ahead into a triple buffer (double with a
+//    channel gate, whose tiles are larger), a one-dword touch of the chunk
+//    four ahead to start its HBM reads early, and the coalesced store of the
+//    previous chunk's output from LDS.  Vector-memory issue stalls thus fall
+//    on the copy waves.  Without a channel gate the compute waves load their
+//    own Q rows into registers one chunk ahead (four 16-byte loads per lane
+//    and chunk), which leaves the copy waves less to issue.
+//  * On gfx950 a wave's LDS counter also covers its global->LDS copies in
+//    flight: each barrier's LDS wait makes the copy waves' copies of that
+//    phase complete, and so does the LDS read of the output tile.
 //  * Rows of a K / Q tile are stored with their 16-byte pieces XOR-swizzled
 //    by row, so fragment reads are free of bank conflicts; T^ and P arrive in
 //    the packed lower-block form written by the prep kernels.
@@ -28,11 +33,11 @@
 //    U is exactly zero (beta or the prep kernel's zero rows make it so), so
 //    they contribute nothing to S, and their O is never stored.
 //  * Three barriers per chunk, all raw s_barrier with an LDS-only wait.  The
-//    copy wave waits for the copies of the next chunk just before the last
-//    one, by count, leaving the newest chunk's copies in flight.
-//  * The operand buffers and the working area are separate LDS objects, so
-//    the compiler can see that copies into one buffer never alias reads of
-//    another and inserts no waits of its own.
+//    copy waves also wait for the copies of the next chunk before the last
+//    one, by count.
+//  * The copies are inline assembly, invisible to the compiler, which would
+//    otherwise wait for every copy in flight before each LDS read; the
+//    operand buffers and the working area are separate LDS objects as well.
 //
 // Compute wave w owns chunk rows 16w..16w+15 for X, Y, R, U, O and state rows
 // [DK/4 w, DK/4 (w+1)) for the state update.
