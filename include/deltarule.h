@@ -30,11 +30,14 @@
  *   launch failure returns DR_ERR_HIP; faults inside kernels surface at the
  *   caller's next synchronisation.  dr_last_error() returns the detail text of
  *   the calling thread's most recent failure.
- * Numerics.  The state and every accumulation are fp32.  Matrix-core operands
- *   are fp16 (bf16 inputs convert to fp16 exactly for |x| in [2^-14, 65504];
- *   below 2^-14 the absolute error is under 2^-25), and fp32 inputs use a
- *   two-term fp16 split (about 22 significant bits).  NaN/Inf inputs propagate
- *   and are not checked.  For a channel-wise gate, each chunk's cumulative
+ * Numerics.  The state and every accumulation are fp32.  Matrix-core
+ *   operands: with bf16 inputs, a scalar gate and a scalar beta, the raw bf16
+ *   q and k feed bf16 ops as they are, and the fp32 quantities they meet (the
+ *   state, lambda U) are carried as bf16 hi + lo pairs (16 significant bits);
+ *   with a channel-wise gate or beta, the gated operands and the state are
+ *   single fp16 terms; fp32 inputs use a two-term fp16 split (about 22
+ *   significant bits).  The chunk matrices T^ and P are stored in fp16 (two
+ *   terms for fp32 inputs).  NaN/Inf inputs propagate and are not checked.  For a channel-wise gate, each chunk's cumulative
  *   log-gate must stay above -80 per channel (i.e. alpha products over 64
  *   tokens above e^-80); stronger decay underflows fp32 in the chunk algebra.
  */
