@@ -219,8 +219,26 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
     }
     __syncthreads();
 
+    // T^ = T Diag(beta) in the packed lower-block form, fp16, from the fp32
+    // blocks of block row R, one 8-column piece (of 32 R + 32) per thread
+    // index e = 0, nthr, 2 nthr, ... starting at e0
+    auto out_row = [&](const int R, int e0, const int nthr) {
+        for (int e = e0; e < 32 * (R + 1); e += nthr) {
+            const int I = e >> 5, r = (e >> 1) & 15, h = e & 1;
+            const int row = 16 * R + r, c0 = 16 * I + 8 * h;
+            half8 hv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int col = c0 + j;
+                hv[j] = (half_t)(col <= row ? sT[row][col] * sb[col] : 0.f);
+            }
+            *reinterpret_cast<half8*>(a.wsT + cs * (size_t)(CH * CH) + tri_off(row, c0)) = hv;
+        }
+    };
+
     // off-diagonal blocks, block row R = 1..3; wave I < R computes T_RI:
     //   X = sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .],  T_RI = -T_RR X
+    // while the idle waves (w >= R) write block row R - 1 of T^, final by now
     for (int R = 1; R < 4; ++R) {
         if (w < R) {
             const int I = w;
@@ -244,25 +262,12 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) sT[16 * R + 4 * g + j][16 * I + i16] = -(Tn0[j] + Tn1[j]);
+        } else {
+            out_row(R - 1, tid - 64 * R, 64 * (4 - R));
         }
         __syncthreads();
     }
-
-    // T^ = T Diag(beta) in the packed lower-block form, fp16, from its fp32
-    // blocks: one 8-column piece per thread and step
-    for (int e = tid; e < 320; e += 256) {
-        const int blk = e >> 5, r = (e >> 1) & 15, h = e & 1;
-        const int R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-        const int I = blk - R * (R + 1) / 2;
-        const int row = 16 * R + r, c0 = 16 * I + 8 * h;
-        half8 hv;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = c0 + j;
-            hv[j] = (half_t)(col <= row ? sT[row][col] * sb[col] : 0.f);
-        }
-        *reinterpret_cast<half8*>(a.wsT + cs * (size_t)(CH * CH) + tri_off(row, c0)) = hv;
-    }
+    out_row(3, tid, 256);
 }
 
 template <int DK>
