@@ -84,6 +84,7 @@ class ChunkProblem:
     beta: np.ndarray
     S0: Optional[np.ndarray]
     meta: dict = field(default_factory=dict)
+    beta_v: Optional[np.ndarray] = None   # separate write strength (FG2-GDN+), beta's shape
 
     @property
     def token_heads(self) -> int:
@@ -95,13 +96,17 @@ class ChunkProblem:
         return ChunkProblem(
             f"{self.name}[b={b},h={h}]", 1, 1, self.L, self.Dk, self.Dv, self.in_dtype,
             self.gate, self.beta_mode, sl(self.q), sl(self.k), sl(self.v),
-            sl(self.log_alpha), sl(self.beta), sl(self.S0), dict(self.meta))
+            sl(self.log_alpha), sl(self.beta), sl(self.S0), dict(self.meta), sl(self.beta_v))
 
 
 def make_chunk_problem(B, H, L, Dk, Dv, *, in_dtype="bf16", gate="scalar", beta_mode="scalar",
                        log_alpha_range=(-0.1, -0.001), s0_var: Optional[float] = None,
-                       seed: int = 0, name: str = "custom") -> ChunkProblem:
-    """Draw one chunked-forward batch following the module recipe."""
+                       seed: int = 0, name: str = "custom", beta_v: bool = False) -> ChunkProblem:
+    """Draw one chunked-forward batch following the module recipe.
+
+    beta_v=True adds a separate write strength beta^v (FG2-GDN+), drawn like
+    beta and after every other tensor, so the rest of the batch is unchanged.
+    """
     if gate not in GATES or beta_mode not in BETAS or in_dtype not in DTYPES:
         raise ValueError("unknown mode")
     rng = np.random.default_rng(seed)
@@ -118,13 +123,14 @@ def make_chunk_problem(B, H, L, Dk, Dv, *, in_dtype="bf16", gate="scalar", beta_
     S0 = None
     if s0_var is not None:
         S0 = (rng.standard_normal((B, H, Dk, Dv)) * np.sqrt(s0_var)).astype(np.float32)
+    bv = _sigmoid(rng.standard_normal(bshape)).astype(np.float32) if beta_v else None
     q = _to_dtype(_l2norm(q), in_dtype)
     k = _to_dtype(_l2norm(k), in_dtype)
     v = _to_dtype(v, in_dtype)
     return ChunkProblem(name, B, H, L, Dk, Dv, in_dtype, gate, beta_mode, q, k, v,
                         None if la is None else la.astype(np.float32),
                         beta.astype(np.float32), S0,
-                        {"seed": seed, "log_alpha_range": log_alpha_range, "s0_var": s0_var})
+                        {"seed": seed, "log_alpha_range": log_alpha_range, "s0_var": s0_var}, bv)
 
 
 # The named workloads.  Gate ranges are U(lo, hi) on log alpha.
@@ -144,6 +150,9 @@ WORKLOADS = {
     # FG2-GDN: channel-wise gate and channel-wise beta, S0 = 0
     "fg2_b2h16_16k": dict(B=2, H=16, L=16384, Dk=128, Dv=128, in_dtype="bf16", gate="channel",
                           beta_mode="channel", log_alpha_range=KDA_GATE, s0_var=None),
+    # FG2-GDN+: as FG2-GDN with a separate channel-wise write strength beta^v
+    "fg2plus_b2h16_16k": dict(B=2, H=16, L=16384, Dk=128, Dv=128, in_dtype="bf16", gate="channel",
+                              beta_mode="channel", log_alpha_range=KDA_GATE, s0_var=None, beta_v=True),
     # long-context GDN prefill, gating as the B=4 GDN workload
     "gdn_b1h16_64k": dict(B=1, H=16, L=65536, Dk=128, Dv=128, in_dtype="bf16", gate="scalar",
                           beta_mode="scalar", log_alpha_range=GDN_GATE, s0_var=0.01),

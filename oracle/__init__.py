@@ -10,6 +10,9 @@ Recurrence (FG2-GDN page, section 2, the scaled key/value and state-update
 equations; DeltaNet page, step list, step 6 for the output):
     kt = sqrt(beta) * k,  vt = sqrt(beta) * v
     S_t = (I - kt kt^T) Diag(alpha_t) S_{t-1} + kt vt^T,   o_t = S_t^T q_t
+With separate erase and write strengths (FG2-GDN page, section "Erweiterung:
+FG2-GDN+"; the page prints no equation, the reading taken is) kt = sqrt(beta^k)
+* k in both terms and vt = sqrt(beta^v) * v.
 """
 from __future__ import annotations
 
@@ -47,6 +50,9 @@ def load(path: str = LIB_PATH):
     lib.dro_forward.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp,
                                                       ctypes.c_int, dp, dp, dp, ctypes.c_int]
     lib.dro_forward.restype = ctypes.c_int
+    lib.dro_forward_kv.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp, dp,
+                                                         ctypes.c_int, dp, dp, dp, ctypes.c_int]
+    lib.dro_forward_kv.restype = ctypes.c_int
     lib.dro_max_threads.restype = ctypes.c_int
     return lib
 
@@ -66,11 +72,12 @@ def _f64(a: Optional[np.ndarray]):
 
 
 def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
-            nthreads: int = 0, lib=None):
+            nthreads: int = 0, lib=None, beta_v=None):
     """Run the recurrence over [B, H, L, D] inputs; returns (o, S_final) in fp64.
 
     log_alpha is [B,H,L] (scalar gate), [B,H,L,Dk] (channel gate) or None
     (gate "none"); beta is [B,H,L] or [B,H,L,Dk]; S0 is [B,H,Dk,Dv] or None.
+    beta_v (beta's shape) is a separate write strength; None means beta.
     """
     lib = lib or _get()
     q = np.asarray(q)
@@ -84,10 +91,17 @@ def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
     sa, sp = _f64(S0)
     o = np.empty((B, H, L, Dv), np.float64)
     Sf = np.empty((B, H, Dk, Dv), np.float64)
-    rc = lib.dro_forward(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp,
-                         BETA_CODES[beta_mode], sp,
-                         o.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                         Sf.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), int(nthreads))
+    op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    fp = Sf.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    if beta_v is None:
+        rc = lib.dro_forward(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp,
+                             BETA_CODES[beta_mode], sp, op, fp, int(nthreads))
+    else:
+        if np.shape(beta_v) != np.shape(beta):
+            raise ValueError("beta_v must have beta's shape")
+        bva, bvp = _f64(beta_v)
+        rc = lib.dro_forward_kv(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp, bvp,
+                                BETA_CODES[beta_mode], sp, op, fp, int(nthreads))
     if rc != 0:
         raise ValueError(f"dro_forward rejected its arguments (code {rc})")
     return o, Sf
@@ -96,11 +110,12 @@ def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
 def forward_problem(p, nthreads: int = 0, lib=None):
     """Oracle over a ChunkProblem-like object (fields as the input generator's)."""
     return forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, gate=p.gate,
-                   beta_mode=p.beta_mode, nthreads=nthreads, lib=lib)
+                   beta_mode=p.beta_mode, nthreads=nthreads, lib=lib,
+                   beta_v=getattr(p, "beta_v", None))
 
 
 def decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str,
-                nthreads: int = 0, lib=None):
+                nthreads: int = 0, lib=None, beta_v=None):
     """One recurrent step for a batch of states: S [N,H,Dk,Dv], q/k/v [N,H,D].
 
     The decode step is the forward with a single token, started from S.
@@ -108,7 +123,7 @@ def decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str,
     """
     ex = lambda a: None if a is None else np.asarray(a)[:, :, None]
     o, Sn = forward(ex(q), ex(k), ex(v), ex(log_alpha), ex(beta), S, gate=gate,
-                    beta_mode=beta_mode, nthreads=nthreads, lib=lib)
+                    beta_mode=beta_mode, nthreads=nthreads, lib=lib, beta_v=ex(beta_v))
     return o[:, :, 0], Sn
 
 

@@ -18,6 +18,11 @@
  *     it is passed as log alpha.
  *   DeltaNet page, the seven-step list, step 6: the output reads the updated
  *   state, o_t = S_t^T q_t (the page writes S q with S stored d_v x d_k).
+ *   FG2-GDN page, section "Erweiterung: FG2-GDN+": separate erase and write
+ *   strengths beta^k_t and beta^v_t.  The page prints no equation; the reading
+ *   taken here is kt = sqrt(beta^k_t) (.) k_t (in both the erase and the
+ *   write term) and vt = sqrt(beta^v_t) (.) v_t (dro_forward_kv); with
+ *   beta^v = beta^k it is the equation above.
  *
  * The update is evaluated in the rank-one form that the DeltaNet page's steps
  * 3-5 describe (read the current map, form the error, add the outer product):
@@ -47,13 +52,15 @@ enum { DRO_OK = 0, DRO_EINVAL = 1, DRO_ENOMEM = 2 };
 /* One (b, h) sequence.  Pointers are already offset to that sequence:
  *   q, k   [L][Dk]      v, o [L][Dv]
  *   la     [L] or [L][Dk] (NULL when gate == NONE)
- *   beta   [L] or [L][Dk]
+ *   beta   [L] or [L][Dk]      scales kt
+ *   betav  [L] or [L][Dk]      scales vt (the same array as beta unless the
+ *                              write strength is separate)
  *   S      [Dk][Dv]  in: initial state, out: final state
  *   kt, vt scratch of Dk and Dv doubles, p scratch of Dv doubles. */
 static void run_sequence(int L, int Dk, int Dv,
                          const double* q, const double* k, const double* v,
-                         const double* la, int gate, const double* beta, int beta_mode,
-                         double* S, double* o, double* kt, double* vt, double* p)
+                         const double* la, int gate, const double* beta, const double* betav,
+                         int beta_mode, double* S, double* o, double* kt, double* vt, double* p)
 {
     for (int t = 0; t < L; ++t) {
         const double* qt = q + (size_t)t * Dk;
@@ -67,7 +74,7 @@ static void run_sequence(int L, int Dk, int Dv,
         }
         for (int j = 0; j < Dv; ++j) {
             /* channel beta scales v's channel j by beta's channel j (d_v == d_k) */
-            double b = beta_mode == DRO_BETA_SCALAR ? beta[t] : beta[(size_t)t * Dk + j];
+            double b = beta_mode == DRO_BETA_SCALAR ? betav[t] : betav[(size_t)t * Dk + j];
             vt[j] = sqrt(b) * v_t[j];
         }
 
@@ -104,24 +111,25 @@ static void run_sequence(int L, int Dk, int Dv,
 }
 
 /*
- * dro_forward -- the whole batch.
+ * dro_forward_kv -- the whole batch, with separate key and value strengths.
  *   q, k      [B][H][L][Dk] fp64
  *   v         [B][H][L][Dv] fp64
  *   log_alpha [B][H][L] (gate SCALAR) or [B][H][L][Dk] (gate CHANNEL); NULL for NONE
- *   beta      [B][H][L] (SCALAR) or [B][H][L][Dk] (CHANNEL; needs Dv == Dk)
+ *   beta      [B][H][L] (SCALAR) or [B][H][L][Dk] (CHANNEL; needs Dv == Dk): beta^k
+ *   beta_v    beta^v, the same shape as beta
  *   S0        [B][H][Dk][Dv] or NULL (zeros)
  *   o         [B][H][L][Dv]     out
  *   S_final   [B][H][Dk][Dv]    out, may be NULL
  *   nthreads  worker threads over (b, h); <= 0 means the OpenMP default
  * Decode is the same call with L == 1 and S0 the current states.
  */
-int dro_forward(int B, int H, int L, int Dk, int Dv,
-                const double* q, const double* k, const double* v,
-                const double* log_alpha, int gate, const double* beta, int beta_mode,
-                const double* S0, double* o, double* S_final, int nthreads)
+int dro_forward_kv(int B, int H, int L, int Dk, int Dv,
+                   const double* q, const double* k, const double* v,
+                   const double* log_alpha, int gate, const double* beta, const double* beta_v,
+                   int beta_mode, const double* S0, double* o, double* S_final, int nthreads)
 {
     if (B <= 0 || H <= 0 || L < 0 || Dk <= 0 || Dv <= 0) return DRO_EINVAL;
-    if (!q || !k || !v || !beta || !o) return DRO_EINVAL;
+    if (!q || !k || !v || !beta || !beta_v || !o) return DRO_EINVAL;
     if (gate < DRO_GATE_NONE || gate > DRO_GATE_CHANNEL) return DRO_EINVAL;
     if (beta_mode != DRO_BETA_SCALAR && beta_mode != DRO_BETA_CHANNEL) return DRO_EINVAL;
     if ((gate == DRO_GATE_NONE) != (log_alpha == NULL)) return DRO_EINVAL;
@@ -150,13 +158,23 @@ int dro_forward(int B, int H, int L, int Dk, int Dv,
         run_sequence(L, Dk, Dv,
                      q + (size_t)s * L * Dk, k + (size_t)s * L * Dk, v + (size_t)s * L * Dv,
                      log_alpha ? log_alpha + (size_t)s * lw : NULL, gate,
-                     beta + (size_t)s * bw, beta_mode,
+                     beta + (size_t)s * bw, beta_v + (size_t)s * bw, beta_mode,
                      S, o + (size_t)s * L * Dv, kt, vt, p);
         if (S_final) memcpy(S_final + (size_t)s * sz, S, sizeof(double) * sz);
         free(S);
     }
     (void)nthreads;
     return err;
+}
+
+/* The same with one strength for both the key and the value (beta^v = beta). */
+int dro_forward(int B, int H, int L, int Dk, int Dv,
+                const double* q, const double* k, const double* v,
+                const double* log_alpha, int gate, const double* beta, int beta_mode,
+                const double* S0, double* o, double* S_final, int nthreads)
+{
+    return dro_forward_kv(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta, beta_mode, S0, o,
+                          S_final, nthreads);
 }
 
 /* Threads the OpenMP runtime would use by default (1 without OpenMP). */

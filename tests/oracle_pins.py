@@ -382,3 +382,78 @@ ALL_PINS = [
     pin_split_and_resume,
     pin_zero_state_defaults,
 ]
+
+
+# ---------------------------------------------------------------------------
+# Separate erase and write strengths (FG2-GDN page, section "Erweiterung:
+# FG2-GDN+").  The page prints no equation; the reading pinned here is
+# kt = sqrt(beta^k) k in both the erase and the write term and
+# vt = sqrt(beta^v) v.  Each pin takes fwd_kv(q, k, v, la, beta, beta_v, S0,
+# *, gate, beta_mode).
+# ---------------------------------------------------------------------------
+
+def _dense_kv(q, k, v, la, beta, beta_v, S0, gate, beta_mode):
+    L, Dk = q.shape
+    Dv = v.shape[1]
+    S = np.zeros((Dk, Dv)) if S0 is None else S0.copy()
+    o = np.zeros((L, Dv))
+    for t in range(L):
+        sk = np.sqrt(_beta_vec(beta, t, beta_mode, Dk))
+        sv = np.sqrt(_beta_vec(beta_v, t, beta_mode, Dk))
+        kt = sk * k[t]
+        vt = (sv[:Dv] if beta_mode == "channel" else sv[0]) * v[t]
+        M = (np.eye(Dk) - np.outer(kt, kt)) @ np.diag(_alpha_vec(la, t, gate, Dk))
+        S = M @ S + np.outer(kt, vt)
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def pin_kv_dense_product(fwd_kv):
+    """Oracle == literal dense product with vt scaled by sqrt(beta^v) and kt by
+    sqrt(beta^k) in both terms, every gate and beta mode."""
+    salt = 40
+    for gate in ("none", "scalar", "channel"):
+        for beta_mode in ("scalar", "channel"):
+            Dk, Dv = (6, 6) if beta_mode == "channel" else (6, 4)
+            salt += 1
+            q, k, v, la, beta, S0 = random_case(salt, B=2, H=2, L=9, Dk=Dk, Dv=Dv, gate=gate,
+                                                beta_mode=beta_mode)
+            bv = _rng(salt + 100).uniform(0.05, 1.0, beta.shape)
+            o, S = fwd_kv(q, k, v, la, beta, bv, S0, gate=gate, beta_mode=beta_mode)
+            for b in range(2):
+                for h in range(2):
+                    oy, Sy = _dense_kv(q[b, h], k[b, h], v[b, h], None if la is None else la[b, h],
+                                       beta[b, h], bv[b, h], S0[b, h], gate, beta_mode)
+                    _close(o[b, h], oy, 1e-12, f"o ({gate},{beta_mode})")
+                    _close(S[b, h], Sy, 1e-12, f"S ({gate},{beta_mode})")
+
+
+def pin_kv_write_scaling(fwd_kv):
+    """From S0 = 0 the recurrence is linear in vt for fixed kt and alpha:
+    beta^v = c^2 beta^k scales every output and the final state by c."""
+    for beta_mode in ("scalar", "channel"):
+        q, k, v, la, beta, _ = random_case(60, L=14, Dk=6, Dv=6, gate="scalar",
+                                           beta_mode=beta_mode, s0=False)
+        c = 0.37
+        o1, S1 = fwd_kv(q, k, v, la, beta, beta, None, gate="scalar", beta_mode=beta_mode)
+        o2, S2 = fwd_kv(q, k, v, la, beta, c * c * beta, None, gate="scalar", beta_mode=beta_mode)
+        _close(o2, c * o1, 1e-13, f"o ({beta_mode})")
+        _close(S2, c * S1, 1e-13, f"S ({beta_mode})")
+
+
+def pin_kv_superposition(fwd_kv):
+    """The response to (S0, writes) is the response to (S0, no writes) plus the
+    response to (0, writes): beta^v enters only the write term."""
+    for beta_mode in ("scalar", "channel"):
+        q, k, v, la, beta, S0 = random_case(61, L=13, Dk=5, Dv=5, gate="channel",
+                                            beta_mode=beta_mode)
+        bv = _rng(62).uniform(0.05, 1.0, beta.shape)
+        o, S = fwd_kv(q, k, v, la, beta, bv, S0, gate="channel", beta_mode=beta_mode)
+        oa, Sa = fwd_kv(q, k, v, la, beta, np.zeros_like(bv), S0, gate="channel",
+                        beta_mode=beta_mode)
+        ob, Sb = fwd_kv(q, k, v, la, beta, bv, None, gate="channel", beta_mode=beta_mode)
+        _close(o, oa + ob, 1e-12, f"o ({beta_mode})")
+        _close(S, Sa + Sb, 1e-12, f"S ({beta_mode})")
+
+
+KV_PINS = [pin_kv_dense_product, pin_kv_write_scaling, pin_kv_superposition]

@@ -19,7 +19,7 @@ MUTANTS = [
     ("read_unscaled_key", "p[j] += row[j] * kt[c];", "p[j] += row[j] * k_t[c];"),
     ("output_from_query_free_state", "ot[j] += row[j] * qt[c];", "ot[j] += row[j] * k_t[c];"),
     ("gate_index_shift", "exp(la[(size_t)t * Dk + c])", "exp(la[(size_t)t * Dk + (c + 1) % Dk])"),
-    ("channel_beta_wrong_channel", "beta[(size_t)t * Dk + j]", "beta[(size_t)t * Dk + (Dk - 1 - j)]"),
+    ("channel_beta_wrong_channel", "betav[(size_t)t * Dk + j]", "betav[(size_t)t * Dk + (Dk - 1 - j)]"),
     ("error_drops_read", "(vt[j] - p[j])", "(vt[j] - 0.0 * p[j])"),
     ("state_not_carried", "if (S0) memcpy(S, S0", "if (0) memcpy(S, S0"),
     ("output_before_update",
@@ -43,6 +43,35 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(fwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
+
+
+# Mistakes in the separate write strength, caught by the pins of that reading.
+KV_MUTANTS = [
+    ("value_uses_key_strength", "? betav[t] : betav[(size_t)t * Dk + j]", "? beta[t] : beta[(size_t)t * Dk + j]"),
+    ("key_uses_value_strength", "? beta[t] : beta[(size_t)t * Dk + c]", "? betav[t] : betav[(size_t)t * Dk + c]"),
+    ("value_strength_not_sqrt", "vt[j] = sqrt(b) * v_t[j];", "vt[j] = b * v_t[j];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", KV_MUTANTS, ids=[m[0] for m in KV_MUTANTS])
+def test_kv_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+
+    def fwd_kv(q, k, v, la, beta, beta_v, S0, *, gate, beta_mode):
+        return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, lib=lib,
+                              beta_v=beta_v)
+
+    caught = []
+    for pin in oracle_pins.KV_PINS:
+        try:
+            pin(fwd_kv)
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"

@@ -39,3 +39,32 @@ def test_decode_step_is_one_token_forward():
                                 gate="scalar", beta_mode="scalar")
     o2, S2 = oracle.forward(q, k, v, la, beta, S0, gate="scalar", beta_mode="scalar")
     assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
+
+
+
+def fwd_kv(q, k, v, la, beta, beta_v, S0, *, gate, beta_mode):
+    return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, beta_v=beta_v)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.KV_PINS, ids=lambda f: f.__name__)
+def test_kv_pin(pin):
+    pin(fwd_kv)
+
+
+def test_kv_equal_strengths_is_the_single_strength_forward():
+    for beta_mode in ("scalar", "channel"):
+        q, k, v, la, beta, S0 = oracle_pins.random_case(33, L=10, Dk=5, Dv=5, gate="channel",
+                                                        beta_mode=beta_mode)
+        a = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode=beta_mode)
+        b = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode=beta_mode, beta_v=beta)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_kv_decode_step_is_one_token_forward():
+    q, k, v, la, beta, S0 = oracle_pins.random_case(37, B=3, H=2, L=1, Dk=6, Dv=6, gate="channel",
+                                                    beta_mode="channel")
+    bv = np.random.default_rng(38).uniform(0.05, 1.0, beta.shape)
+    o1, S1 = oracle.decode_step(S0, q[:, :, 0], k[:, :, 0], v[:, :, 0], la[:, :, 0], beta[:, :, 0],
+                                gate="channel", beta_mode="channel", beta_v=bv[:, :, 0])
+    o2, S2 = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode="channel", beta_v=bv)
+    assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
