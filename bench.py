@@ -18,8 +18,8 @@ Also reported in the same line:
   mfma          the whole forward's algorithmic flops against bf16 MFMA peak;
   decode        512 consecutive dr_decode_step calls on 256 sequences x 16
                 heads of 128x128 fp32 states (bf16 tokens, GDN gating);
-  configs       the other forward workloads (FG2-GDN at the headline shape,
-                KDA, GDN at L=4K and 64K), a few steps each;
+  configs       the other forward workloads (FG2-GDN and FG2-GDN+ at the
+                headline shape, KDA, GDN at L=4K and 64K), a few steps each;
   cpu_baseline  the fp64 CPU oracle on the whole headline batch, on the
                 host's cores, with the GPU result checked against it.
 The headline inputs follow the seeded NumPy recipe of
@@ -258,12 +258,13 @@ def main():
     # ------------------------------------------------------------ other forward workloads
     configs = {}
     extra = [
-        ("fg2_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False),
-        ("kda_b2h32_16k", 2, 32, 16384, "channel", "scalar", (-0.2, -0.0005), False),
-        ("gdn_b4h16_4k", 4, 16, 4096, "scalar", "scalar", (-0.1, -0.001), True),
-        ("gdn_b1h16_64k", 1, 16, 65536, "scalar", "scalar", (-0.1, -0.001), True),
+        ("fg2_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, False),
+        ("fg2plus_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, True),
+        ("kda_b2h32_16k", 2, 32, 16384, "channel", "scalar", (-0.2, -0.0005), False, False),
+        ("gdn_b4h16_4k", 4, 16, 4096, "scalar", "scalar", (-0.1, -0.001), True, False),
+        ("gdn_b1h16_64k", 1, 16, 65536, "scalar", "scalar", (-0.1, -0.001), True, False),
     ]
-    for name, b_, h_, l_, gate, bmode, rng, s0 in (extra if args.config_steps > 0 else []):
+    for name, b_, h_, l_, gate, bmode, rng, s0, sepv in (extra if args.config_steps > 0 else []):
         gen.manual_seed(0)
         xq = l2n(torch.randn((b_, h_, l_, D), generator=gen, device=dev)).bfloat16()
         xk = l2n(torch.randn((b_, h_, l_, D), generator=gen, device=dev)).bfloat16()
@@ -273,14 +274,20 @@ def main():
         bshape = (b_, h_, l_) if bmode == "scalar" else (b_, h_, l_, D)
         xbe = torch.sigmoid(torch.randn(bshape, generator=gen, device=dev))
         xS0 = torch.randn((b_, h_, D, D), generator=gen, device=dev) * 0.1 if s0 else None
+        # separate write strength (FG2-GDN+), drawn like beta
+        xbv = torch.sigmoid(torch.randn(bshape, generator=gen, device=dev)) if sepv else None
         xo = torch.empty((b_, h_, l_, D), dtype=torch.float32, device=dev)
         xSf = torch.empty((b_, h_, D, D), dtype=torch.float32, device=dev)
         xdesc = drl.chunk_desc(b_, h_, l_, D, D, drl.DR_BF16, drl.DR_F32, gate, bmode)
         xws = torch.empty(drl.dr_chunk_fwd_workspace_bytes(xdesc), dtype=torch.uint8, device=dev)
 
         def xstep():
-            drl.dr_chunk_fwd(xq, xk, xv, xla, xbe, xS0, gate=gate, beta_mode=bmode, o=xo, S_final=xSf,
-                             workspace=xws)
+            if xbv is not None:
+                drl.dr_chunk_fwd_kv(xq, xk, xv, xla, xbe, xbv, xS0, gate=gate, o=xo, S_final=xSf,
+                                    workspace=xws)
+            else:
+                drl.dr_chunk_fwd(xq, xk, xv, xla, xbe, xS0, gate=gate, beta_mode=bmode, o=xo,
+                                 S_final=xSf, workspace=xws)
 
         drl.dr_profile_begin()
         xper = time_steps(xstep, args.config_steps, 2)
@@ -289,14 +296,16 @@ def main():
         th = b_ * h_ * l_
         calls = max(1, xprof["chunk_calls"])
         configs[name] = {
-            "shape": f"B={b_} H={h_} L={l_} d={D}, gate {gate}, beta {bmode}",
+            "shape": f"B={b_} H={h_} L={l_} d={D}, gate {gate}, beta {bmode}"
+                     + (", separate write strength" if sepv else ""),
             "ms_per_step": round(xms, 4), "tokens_per_s": round(b_ * l_ / (xms * 1e-3), 1),
             "prep_ms": round(xprof["prep_ms"] / calls, 4), "scan_ms": round(xprof["scan_ms"] / calls, 4),
             "mfma_frac": round(flops_per_token_head(D) * th / (xms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
             "hbm_frac": round(fwd_bytes_per_token_head(D, l_, 2, 1 if gate == "scalar" else D,
-                                                       1 if bmode == "scalar" else D) * th
+                                                       (1 if bmode == "scalar" else D) * (2 if sepv else 1))
+                              * th
                               / (xms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        del xq, xk, xv, xla, xbe, xS0, xo, xSf, xws
+        del xq, xk, xv, xla, xbe, xbv, xS0, xo, xSf, xws
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline (oracle)

@@ -8,6 +8,11 @@ there is no fallback path.
 
     o, S = dr_chunk_fwd(q, k, v, log_alpha, beta, S0, gate="scalar", beta_mode="scalar")
     o = dr_decode_step(S, q, k, v, log_alpha, beta, gate="scalar", beta_mode="scalar")
+
+With separate channel-wise erase and write strengths (FG2-GDN+):
+
+    o, S = dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0, gate="channel")
+    o = dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, gate="channel")
 """
 from __future__ import annotations
 
@@ -18,13 +23,14 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 2
+DR_ABI_VERSION = 3
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
 BETAS = {"scalar": 0, "channel": 1}
-EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_decode_step", "dr_status_str",
-           "dr_last_error", "dr_abi_version", "dr_profile_begin", "dr_profile_end")
+EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "dr_decode_step",
+           "dr_decode_step_kv", "dr_status_str", "dr_last_error", "dr_abi_version",
+           "dr_profile_begin", "dr_profile_end")
 
 
 class DeltaRuleError(RuntimeError):
@@ -69,8 +75,13 @@ def lib() -> ctypes.CDLL:
         L.dr_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
         L.dr_chunk_fwd.restype = ctypes.c_int
+        L.dr_chunk_fwd_kv.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, ctypes.c_size_t, vp]
+        L.dr_chunk_fwd_kv.restype = ctypes.c_int
         L.dr_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp]
         L.dr_decode_step.restype = ctypes.c_int
+        L.dr_decode_step_kv.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.dr_decode_step_kv.restype = ctypes.c_int
         L.dr_status_str.argtypes = [ctypes.c_int]
         L.dr_status_str.restype = ctypes.c_char_p
         L.dr_last_error.argtypes = []
@@ -178,6 +189,22 @@ def dr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str
     (it may be S0 itself for an in-place carry); with want_state=False no
     final state is written and None is returned for it.
     """
+    return _chunk(q, k, v, log_alpha, beta, None, S0, gate, beta_mode, out_dtype, o, S_final,
+                  want_state, workspace, stream)
+
+
+def dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0=None, *, gate: str, out_dtype=None,
+                    o=None, S_final=None, want_state: bool = True, workspace=None, stream=None):
+    """dr_chunk_fwd with separate channel-wise erase (beta_k) and write
+    (beta_v) strengths, both [B,H,L,Dk] fp32; Dv == Dk."""
+    if beta_v is None:
+        raise ValueError("beta_v is required")
+    return _chunk(q, k, v, log_alpha, beta_k, beta_v, S0, gate, "channel", out_dtype, o, S_final,
+                  want_state, workspace, stream)
+
+
+def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, S_final, want_state,
+           workspace, stream):
     torch = _torch()
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
@@ -190,7 +217,10 @@ def dr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str
             raise ValueError("gate 'none' takes no log_alpha")
     else:
         _need(log_alpha, "log_alpha", torch.float32, gshape)
-    _need(beta, "beta", torch.float32, (B, H, L) if beta_mode == "scalar" else (B, H, L, Dk))
+    bshape = (B, H, L) if beta_mode == "scalar" else (B, H, L, Dk)
+    _need(beta, "beta", torch.float32, bshape)
+    if beta_v is not None:
+        _need(beta_v, "beta_v", torch.float32, bshape)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
     out_dtype = torch.float32 if out_dtype is None else out_dtype
@@ -207,9 +237,14 @@ def dr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().dr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                              _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace),
-                              wbytes, _stream(stream)))
+    if beta_v is None:
+        _check(lib().dr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                  _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace),
+                                  wbytes, _stream(stream)))
+    else:
+        _check(lib().dr_chunk_fwd_kv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                     _ptr(beta), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(S_final),
+                                     _ptr(workspace), wbytes, _stream(stream)))
     return o, S_final
 
 
@@ -220,6 +255,19 @@ def dr_decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str, ou
     S: [N,H,Dk,Dv] fp32; q, k: [N,H,Dk]; v: [N,H,Dv]; log_alpha: [N,H] /
     [N,H,Dk] or None; beta: [N,H] / [N,H,Dk].
     """
+    return _decode(S, q, k, v, log_alpha, beta, None, gate, beta_mode, out_dtype, o, stream)
+
+
+def dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, *, gate: str, out_dtype=None, o=None,
+                      stream=None):
+    """dr_decode_step with separate channel-wise erase (beta_k) and write
+    (beta_v) strengths, both [N,H,Dk] fp32; Dv == Dk."""
+    if beta_v is None:
+        raise ValueError("beta_v is required")
+    return _decode(S, q, k, v, log_alpha, beta_k, beta_v, gate, "channel", out_dtype, o, stream)
+
+
+def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, stream):
     torch = _torch()
     N, H, Dk, Dv = S.shape
     _need(S, "S", torch.float32)
@@ -232,7 +280,10 @@ def dr_decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str, ou
             raise ValueError("gate 'none' takes no log_alpha")
     else:
         _need(log_alpha, "log_alpha", torch.float32, gshape)
-    _need(beta, "beta", torch.float32, (N, H) if beta_mode == "scalar" else (N, H, Dk))
+    bshape = (N, H) if beta_mode == "scalar" else (N, H, Dk)
+    _need(beta, "beta", torch.float32, bshape)
+    if beta_v is not None:
+        _need(beta_v, "beta_v", torch.float32, bshape)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if o is None:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=S.device)
@@ -240,6 +291,10 @@ def dr_decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str, ou
         _need(o, "o", out_dtype, (N, H, Dv))
     desc = DecodeDesc(N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), GATES[gate],
                       BETAS[beta_mode])
-    _check(lib().dr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                                _ptr(beta), _ptr(S), _ptr(o), _stream(stream)))
+    if beta_v is None:
+        _check(lib().dr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                    _ptr(beta), _ptr(S), _ptr(o), _stream(stream)))
+    else:
+        _check(lib().dr_decode_step_kv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                       _ptr(beta), _ptr(beta_v), _ptr(S), _ptr(o), _stream(stream)))
     return o

@@ -194,22 +194,28 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_chunk_desc* d) {
     return ws_layout(*d).total;
 }
 
-dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
-                       const float* log_alpha, const float* beta, const float* S0, void* o,
-                       float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
-    g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+// The chunked forward; beta_v is the write strength on v (beta itself for
+// dr_chunk_fwd, a separate channel-wise array for dr_chunk_fwd_kv).
+dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                    const float* log_alpha, const float* beta, const float* beta_v, const float* S0,
+                    void* o, float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
     dr_status s = check_chunk_desc(d);
     if (s != DR_OK) return s;
     const size_t nseq = (size_t)d->B * d->H;
     const bool tokens = nseq > 0 && d->L > 0;
     if (tokens) {
-        if (!q || !k || !v || !beta || !o) return fail(DR_ERR_NULL, "q, k, v, beta and o are required");
+        if (!q || !k || !v || !beta || !beta_v || !o)
+            return fail(DR_ERR_NULL, "q, k, v, beta (beta_k and beta_v) and o are required");
         if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
             return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
     }
-    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, o, S_final, workspace};
-    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "S0", "o", "S_final", "workspace"};
-    for (int i = 0; i < 9; ++i)
+    const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, S0, o, S_final, workspace};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "S0", "o", "S_final", "workspace"};
+    for (int i = 0; i < 10; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     if (S_final && S0 && S_final != S0) {
         const size_t bytes = nseq * d->Dk * d->Dv * sizeof(float);
@@ -238,7 +244,7 @@ dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, con
     }
     dr::ChunkArgs a{};
     a.q = q; a.k = k; a.v = v;
-    a.log_alpha = log_alpha; a.beta = beta; a.S0 = S0;
+    a.log_alpha = log_alpha; a.beta = beta; a.beta_v = beta_v; a.S0 = S0;
     a.o = o; a.S_final = S_final;
     a.B = d->B; a.H = d->H; a.L = d->L; a.Dv = d->Dv;
     a.NC = (d->L + dr::CH - 1) / dr::CH;
@@ -254,15 +260,14 @@ dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, con
     a.wsKl = w.Kl ? (dr::half_t*)(ws + w.Kl) : nullptr;
     a.wsV = w.V ? (dr::half_t*)(ws + w.V) : nullptr;
     hipError_t e = dr::launch_chunk(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL,
-                                    d->beta == DR_BETA_CHANNEL, st);
+                                    d->beta == DR_BETA_CHANNEL, beta_v != beta, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "chunk kernels launch: %s", hipGetErrorString(e));
     return DR_OK;
 }
 
-dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, const void* v,
-                         const float* log_alpha, const float* beta, float* S, void* o,
-                         void* stream) {
-    g_err[0] = '\0';
+dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                      const float* log_alpha, const float* beta, const float* beta_v, float* S,
+                      void* o, void* stream) {
     if (!d) return fail(DR_ERR_NULL, "descriptor is NULL");
     if (d->N < 0 || d->H < 0) return fail(DR_ERR_SHAPE, "negative dimension (N=%d H=%d)", d->N, d->H);
     dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta);
@@ -272,16 +277,17 @@ dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, 
     if (blocks > (size_t)std::numeric_limits<int>::max())
         return fail(DR_ERR_UNSUPPORTED, "N*H=%zu too large", nst);
     if (nst == 0) return DR_OK;
-    if (!q || !k || !v || !beta || !S || !o) return fail(DR_ERR_NULL, "q, k, v, beta, S and o are required");
+    if (!q || !k || !v || !beta || !beta_v || !S || !o)
+        return fail(DR_ERR_NULL, "q, k, v, beta (beta_k and beta_v), S and o are required");
     if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
         return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
-    const void* ptrs[] = {q, k, v, log_alpha, beta, S, o};
-    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "S", "o"};
-    for (int i = 0; i < 7; ++i)
+    const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, S, o};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "S", "o"};
+    for (int i = 0; i < 8; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     dr::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v;
-    a.log_alpha = log_alpha; a.beta = beta;
+    a.log_alpha = log_alpha; a.beta = beta; a.beta_v = beta_v;
     a.S = S; a.o = o;
     a.N = d->N; a.H = d->H; a.Dv = d->Dv;
     a.has_gate = d->gate != DR_GATE_NONE;
@@ -290,6 +296,51 @@ dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, 
                                      d->beta == DR_BETA_CHANNEL, (hipStream_t)stream);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
     return DR_OK;
+}
+
+// The separate-strength entry points take channel-wise strengths only.
+dr_status check_kv_mode(int beta_mode) {
+    if (beta_mode != DR_BETA_CHANNEL)
+        return fail(DR_ERR_UNSUPPORTED, "separate erase and write strengths are channel-wise: "
+                                        "beta mode must be DR_BETA_CHANNEL");
+    return DR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* S0, void* o,
+                       float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    return chunk_fwd(d, q, k, v, log_alpha, beta, beta, S0, o, S_final, workspace, workspace_bytes,
+                     stream);
+}
+
+dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta_k, const float* beta_v,
+                          const float* S0, void* o, float* S_final, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
+    return chunk_fwd(d, q, k, v, log_alpha, beta_k, beta_v, S0, o, S_final, workspace,
+                     workspace_bytes, stream);
+}
+
+dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_alpha, const float* beta, float* S, void* o,
+                         void* stream) {
+    g_err[0] = '\0';
+    return decode_step(d, q, k, v, log_alpha, beta, beta, S, o, stream);
+}
+
+dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* beta_k, const float* beta_v,
+                            float* S, void* o, void* stream) {
+    g_err[0] = '\0';
+    if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
+    return decode_step(d, q, k, v, log_alpha, beta_k, beta_v, S, o, stream);
 }
 
 }  // extern "C"

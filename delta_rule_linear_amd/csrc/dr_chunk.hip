@@ -3,7 +3,9 @@
 // Recurrence (FG2-GDN page, section 2, scaled key/value and state-update
 // equations; DeltaNet page, step list, steps 3-6):
 //   S_t = (I - kt kt^T) Diag(alpha_t) S_{t-1} + kt vt^T,  o_t = S_t^T q_t,
-//   kt = sqrt(beta) (.) k, vt = sqrt(beta) (.) v.
+//   kt = sqrt(beta) (.) k, vt = sqrt(beta) (.) v,
+// or vt = sqrt(beta_v) (.) v with a separate channel-wise write strength
+// (FG2-GDN page, section "Erweiterung: FG2-GDN+"; beta stays on both kt).
 //
 // Chunk algebra (the chunkwise / WY form the DeltaNet page's step 7 and the
 // FG2-GDN page's section 2 refer to, written out here for 64-token chunks).
@@ -111,12 +113,14 @@ constexpr int prep_threads() { return CGATE ? 4 * DK : 256; }
 // 4 tg .. 4 tg + 3, channels 4 cg .. 4 cg + 3 (cg = tid % (DK / 4),
 // tg = tid / (DK / 4)).  Rows past the sequence's end load row 0 of the chunk
 // and are masked at use.
-template <int DK, bool F32IN, bool CBETA>
+// With a separate write strength (SEPV) v is not held here: v and beta_v are
+// loaded at the start of the chunk's preparation instead.
+template <int DK, bool F32IN, bool CBETA, bool SEPV = false>
 struct CgIn {
     static constexpr int CPT = 4;
     float la[4][CPT];               // log alpha
     RawN<F32IN, CPT> k[4], q[4];
-    RawN<F32IN, CPT> v[CBETA ? 4 : 1];
+    RawN<F32IN, CPT> v[CBETA && !SEPV ? 4 : 1];
     float be[CBETA ? 4 : 1][CPT];   // channel beta
     float bs;                       // scalar beta of token tid % 64
 };
@@ -124,8 +128,9 @@ struct CgIn {
 // Part PART of the loads (0: log alpha and k, 1: q and scalar beta, 2: channel
 // beta and v, -1: all), so that a chunk's loads can be spread over the next
 // chunk's phases instead of queueing behind one another.
-template <int DK, bool F32IN, bool CBETA, int PART = -1>
-__device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBETA>& in, int job, int tid) {
+template <int DK, bool F32IN, bool CBETA, bool SEPV, int PART = -1>
+__device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBETA, SEPV>& in, int job,
+                                         int tid) {
     constexpr int CPT = 4;
     constexpr bool P0 = PART < 0 || PART == 0, P1 = PART < 0 || PART == 1, P2 = PART < 0 || PART == 2;
     const int seq = job / a.NC, c = job % a.NC;
@@ -144,7 +149,7 @@ __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBE
         if constexpr (P1) in.q[u] = ld_rawn<F32IN, CPT>(a.q, row * DK + ch0);
         if constexpr (CBETA && P2) {
             load_f32_n<CPT>(a.beta + row * DK + ch0, in.be[u]);
-            in.v[u] = ld_rawn<F32IN, CPT>(a.v, row * a.Dv + ch0);
+            if constexpr (!SEPV) in.v[u] = ld_rawn<F32IN, CPT>(a.v, row * a.Dv + ch0);
         }
     }
     if constexpr (!CBETA && P1) {
@@ -157,9 +162,9 @@ __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBE
 // chunk's raw inputs arrive in `in`; once they are consumed, the inputs of
 // chunk `next_job` (>= 0) are loaded into it, so that those loads are in
 // flight during this chunk's matrix work.
-template <int DK, bool F32IN, bool CGATE, bool CBETA>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV>
 __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, const int seq, const int c,
-                                           CgIn<DK, F32IN, CBETA>& in, const int next_job) {
+                                           CgIn<DK, F32IN, CBETA, SEPV>& in, const int next_job) {
     constexpr int P = F32IN ? 2 : 1;
     constexpr int NTH = prep_threads<DK, CGATE>();
     using SM = PrepSmem<DK, CGATE>;
@@ -212,8 +217,9 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 const int r = e / DK, col = e % DK;
                 const int rc = r < Lc ? r : 0;
                 const float sbv = sqrtf(a.beta[(tok0 + rc) * DK + col]);
+                const float sbw = sqrtf(a.beta_v[(tok0 + rc) * DK + col]);
                 float kv = sbv * load1<F32IN>(a.k, (tok0 + rc) * DK + col);
-                float vv = sbv * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
+                float vv = sbw * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
                 float qv = load1<F32IN>(a.q, (tok0 + rc) * DK + col);
                 kv = r < Lc ? kv : 0.f;
                 vv = r < Lc ? vv : 0.f;
@@ -239,6 +245,19 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
         const int cg = tid % (DK / 4), tg = tid / (DK / 4);
         const int ch0 = cg * CPT;
         const size_t pl = (size_t)CH * DK, base = cs * (size_t)(P * CH * DK);
+        // with a separate write strength, v and beta_v are not among the
+        // inputs held across chunks (no registers to spare there): they are
+        // loaded here, and land during the gate prefix
+        float bwv[SEPV ? 4 : 1][CPT];
+        RawN<F32IN, CPT> vin[SEPV ? 4 : 1];
+        if constexpr (SEPV) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const size_t row = tok0 + (4 * tg + u < Lc ? 4 * tg + u : 0);
+                load_f32_n<CPT>(a.beta_v + row * DK + ch0, bwv[u]);
+                vin[u] = ld_rawn<F32IN, CPT>(a.v, row * Dv + ch0);
+            }
+        }
         float G[4][CPT];
         {
             float run[CPT];
@@ -313,11 +332,13 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             float kx[CPT], qx[CPT], vx[CPT];
             cvt_rawn<F32IN, CPT>(in.k[u], kx);
             cvt_rawn<F32IN, CPT>(in.q[u], qx);
-            if constexpr (CBETA) cvt_rawn<F32IN, CPT>(in.v[u], vx);
+            if constexpr (SEPV) cvt_rawn<F32IN, CPT>(vin[u], vx);
+            else if constexpr (CBETA) cvt_rawn<F32IN, CPT>(in.v[u], vx);
             float okg[CPT], oki[CPT], oqg[CPT], wq[CPT], wks[CPT], wkl[CPT], wv[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
                 const float sbv = CBETA ? sqrtf(in.be[u][c]) : 1.f;
+                const float sbw = SEPV ? sqrtf(bwv[u][c]) : sbv;
                 const float kt = live ? sbv * kx[c] : 0.f;
                 const float qv = live ? qx[c] : 0.f;
                 const float g2 = G[u][c] * kL2E;
@@ -330,7 +351,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 wq[c] = qv * eg;
                 wks[c] = kt * eg;
                 wkl[c] = kt * (e63[c] * colf);
-                wv[c] = CBETA ? (live ? sbv * vx[c] : 0.f) : 0.f;
+                wv[c] = CBETA ? (live ? sbw * vx[c] : 0.f) : 0.f;
             }
 #pragma unroll
             for (int c = 0; c < CPT; c += 4) {
@@ -372,7 +393,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
         if constexpr (!CBETA) {
             if (w == 3) sb[l] = l < Lc ? in.bs : 0.f;
         }
-        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, 0>(a, in, next_job, tid);
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, 0>(a, in, next_job, tid);
     }
     lds_barrier();
 
@@ -541,7 +562,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 
     // ------------------------------------------- T = (I + A)^-1, blocked, fp32
     if constexpr (CGATE) {
-        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, 1>(a, in, next_job, tid);
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, 1>(a, in, next_job, tid);
     }
     // diagonal 16x16 blocks: wave w inverts block w, lane j < 16 owns column j
     if (w < 4 && l < 16) {
@@ -559,7 +580,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     }
     lds_barrier();
     if constexpr (CGATE) {
-        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, 2>(a, in, next_job, tid);
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, 2>(a, in, next_job, tid);
     }
     // off-diagonal blocks, one block row R at a time on the fp32 matrix cores;
     // wave I < R computes
@@ -638,11 +659,11 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 // One workgroup per chunk, or, with a channel gate, a persistent loop over
 // chunks (job = chunk + NC * sequence) that loads the next chunk's inputs
 // while it works on the current one.
-template <int DK, bool F32IN, bool CGATE, bool CBETA>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false>
 __global__ __launch_bounds__((prep_threads<DK, CGATE>())) void prep_kernel(ChunkArgs a) {
     using SM = PrepSmem<DK, CGATE>;
     __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
-    CgIn<DK, F32IN, CBETA> in;
+    CgIn<DK, F32IN, CBETA, SEPV> in;
     if constexpr (CGATE) {
         // fp32 inputs would need twice the registers: they are loaded per chunk
         constexpr bool PREF = !F32IN;
@@ -652,11 +673,11 @@ __global__ __launch_bounds__((prep_threads<DK, CGATE>())) void prep_kernel(Chunk
         for (; job < njobs; job += gridDim.x) {
             if (!PREF) cg_fetch(a, in, job, threadIdx.x);
             const int nj = job + gridDim.x;
-            prep_chunk<DK, F32IN, CGATE, CBETA>(a, smem, job / a.NC, job % a.NC, in,
-                                                PREF && nj < njobs ? nj : -1);
+            prep_chunk<DK, F32IN, CGATE, CBETA, SEPV>(a, smem, job / a.NC, job % a.NC, in,
+                                                      PREF && nj < njobs ? nj : -1);
         }
     } else {
-        prep_chunk<DK, F32IN, CGATE, CBETA>(a, smem, blockIdx.z * a.H + blockIdx.y, blockIdx.x, in, -1);
+        prep_chunk<DK, F32IN, CGATE, CBETA, SEPV>(a, smem, blockIdx.z * a.H + blockIdx.y, blockIdx.x, in, -1);
     }
 }
 
@@ -997,7 +1018,7 @@ static long resident_groups(const void* kern, int threads) {
     return n;
 }
 
-template <int DK, bool F32IN, bool CGATE, bool CBETA>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     const int nseq = a.nseq;
     if (a.NC > 0 && nseq > 0) {
@@ -1006,7 +1027,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
         if constexpr (!F32IN && !CGATE && !CBETA) {
             e = launch_prep16(a, DK, st);
         } else if constexpr (CGATE) {
-            auto kern = prep_kernel<DK, F32IN, CGATE, CBETA>;
+            auto kern = prep_kernel<DK, F32IN, CGATE, CBETA, SEPV>;
             const long njobs = (long)nseq * a.NC;
             constexpr int NTH = prep_threads<DK, CGATE>();
             const long slots = resident_groups((const void*)kern, NTH);
@@ -1038,20 +1059,27 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     return hipSuccess;
 }
 
+// A separate write strength changes only what the preparation writes for vt:
+// the scalar-gate preparation reads a.beta_v as it is; the channel-gate one
+// holds the next chunk's inputs in registers, so only the variant that needs
+// beta_v carries room for it.
 template <int DK, bool F32IN>
-static hipError_t launch_chunk_d(const ChunkArgs& a, bool cgate, bool cbeta, hipStream_t st) {
-    if (cgate) return cbeta ? launch_chunk_t<DK, F32IN, true, true>(a, st)
-                            : launch_chunk_t<DK, F32IN, true, false>(a, st);
+static hipError_t launch_chunk_d(const ChunkArgs& a, bool cgate, bool cbeta, bool sepv, hipStream_t st) {
+    if (cgate) {
+        if (!cbeta) return launch_chunk_t<DK, F32IN, true, false>(a, st);
+        return sepv ? launch_chunk_t<DK, F32IN, true, true, true>(a, st)
+                    : launch_chunk_t<DK, F32IN, true, true>(a, st);
+    }
     return cbeta ? launch_chunk_t<DK, F32IN, false, true>(a, st)
                  : launch_chunk_t<DK, F32IN, false, false>(a, st);
 }
 
-hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
+hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta, bool sepv,
                         hipStream_t st) {
-    if (Dk == 64) return f32in ? launch_chunk_d<64, true>(a, cgate, cbeta, st)
-                               : launch_chunk_d<64, false>(a, cgate, cbeta, st);
-    return f32in ? launch_chunk_d<128, true>(a, cgate, cbeta, st)
-                 : launch_chunk_d<128, false>(a, cgate, cbeta, st);
+    if (Dk == 64) return f32in ? launch_chunk_d<64, true>(a, cgate, cbeta, sepv, st)
+                               : launch_chunk_d<64, false>(a, cgate, cbeta, sepv, st);
+    return f32in ? launch_chunk_d<128, true>(a, cgate, cbeta, sepv, st)
+                 : launch_chunk_d<128, false>(a, cgate, cbeta, sepv, st);
 }
 
 }  // namespace dr

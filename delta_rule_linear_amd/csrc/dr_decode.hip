@@ -1,7 +1,9 @@
 // dr_decode.hip -- one recurrent decode step for a batch of independent states.
 //
 // Per state S (d_k x d_v, fp32) and one new token (FG2-GDN page, section 2,
-// the state-update equation; DeltaNet page, step list, steps 3-6):
+// the state-update equation; DeltaNet page, step list, steps 3-6; with a
+// separate write strength, vt = sqrt(beta_v) v, section "Erweiterung:
+// FG2-GDN+"):
 //   S' = Diag(alpha) S;  p = S'^T kt;  r = S'^T q;  u = vt - p;
 //   S  = S' + kt u^T;    o = S^T q = r + (q . kt) u.
 // Each state is read once and written once, so the step is bound by HBM
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float u = 0.f;
         if (col < a.Dv) {
             const size_t vi = (size_t)sidx * a.Dv + col;
-            const float bv = CBETA ? a.beta[(size_t)sidx * DK + col] : a.beta[sidx];
+            const float bv = CBETA ? a.beta_v[(size_t)sidx * DK + col] : a.beta_v[sidx];
             const float vt = sqrtf(bv) * load1<F32IN>(a.v, vi);
             u = vt - p;
             const float o = r + qk * u;

@@ -35,13 +35,16 @@ __host__ __device__ constexpr int tri_off(int r, int c) {
 //   wsQ/Ks/Kl [NCH][P][64][Dk]   gated operands (channel gate; with a channel
 //                                beta and scalar gate Ks holds sqrt(beta) k and
 //                                Q a copy of q)
-//   wsV       [NCH][P][64][Dk]   sqrt(beta) v (channel beta)
+//   wsV       [NCH][P][64][Dk]   sqrt(beta_v) v (channel beta)
+// beta_v is the write strength that scales v; it is beta itself unless the
+// caller gives a separate one (channel beta only).
 struct ChunkArgs {
     const void* q;
     const void* k;
     const void* v;
     const float* log_alpha;
     const float* beta;
+    const float* beta_v;
     const float* S0;
     void* o;
     float* S_final;
@@ -63,6 +66,7 @@ struct DecodeArgs {
     const void* v;
     const float* log_alpha;
     const float* beta;
+    const float* beta_v;   // write strength on v (== beta unless separate)
     float* S;
     void* o;
     int N, H, Dv;
@@ -75,7 +79,8 @@ struct DecodeArgs {
 enum ProfSlot { kProfPrep = 0, kProfScan = 1, kProfDecode = 2, kProfEnd = 3 };
 void prof_mark(hipStream_t st, int slot);
 
-hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
+// sepv: a.beta_v differs from a.beta (channel beta only)
+hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta, bool sepv,
                         hipStream_t st);
 // chunk preparation for bf16 inputs, scalar gate and scalar beta (dr_prep16.hip)
 hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);

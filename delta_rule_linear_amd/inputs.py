@@ -186,12 +186,15 @@ class DecodeProblem:
     v: np.ndarray                 # [steps, N, H, Dv]
     log_alpha: Optional[np.ndarray]   # [steps, N, H] or [steps, N, H, Dk]
     beta: np.ndarray              # [steps, N, H] or [steps, N, H, Dk]
+    beta_v: Optional[np.ndarray] = None   # separate write strength (FG2-GDN+), beta's shape
 
 
 def make_decode_problem(N=256, H=16, Dk=128, Dv=128, steps=512, *, in_dtype="bf16",
                         gate="scalar", beta_mode="scalar", log_alpha_range=GDN_GATE,
-                        s0_var=0.01, seed=0) -> DecodeProblem:
-    """Decode batch: states first, then each step's tokens, in step order."""
+                        s0_var=0.01, seed=0, beta_v: bool = False) -> DecodeProblem:
+    """Decode batch: states first, then each step's tokens, in step order;
+    with beta_v=True a separate write strength per step is drawn last, like
+    beta, so the other arrays are those of beta_v=False."""
     rng = np.random.default_rng(seed)
     S = (rng.standard_normal((N, H, Dk, Dv)) * np.sqrt(s0_var)).astype(np.float32)
     qs, ks, vs, las, bs = [], [], [], [], []
@@ -210,6 +213,9 @@ def make_decode_problem(N=256, H=16, Dk=128, Dv=128, steps=512, *, in_dtype="bf1
         vs.append(_to_dtype(v, in_dtype))
         las.append(None if la is None else la.astype(np.float32))
         bs.append(_sigmoid(bl).astype(np.float32))
+    bv = None
+    if beta_v:
+        bv = _sigmoid(rng.standard_normal((steps,) + bs[0].shape)).astype(np.float32)
     return DecodeProblem(N, H, Dk, Dv, steps, in_dtype, gate, beta_mode, S,
                          np.stack(qs), np.stack(ks), np.stack(vs),
-                         None if gate == "none" else np.stack(las), np.stack(bs))
+                         None if gate == "none" else np.stack(las), np.stack(bs), bv)

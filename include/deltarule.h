@@ -14,6 +14,12 @@
  *   Gated DeltaNet  scalar alpha_t                   (FG2-GDN page, section 1)
  *   KDA             alpha_t a d_k-vector             (FG2-GDN page, section 1)
  *   FG2-GDN         beta_t a d_k-vector, as sqrt on both k and v (section 2)
+ *   FG2-GDN+        separate d_k-vectors: the erase strength beta^k on k and
+ *                   the write strength beta^v on v (section "Erweiterung:
+ *                   FG2-GDN+"), through the *_kv entry points:
+ *                     kt_t = sqrt(beta^k_t) (.) k_t,  vt_t = sqrt(beta^v_t) (.) v_t
+ *                   and the same S_t and o_t.  The page gives no formula; this
+ *                   is the reading that reduces to FG2-GDN at beta^v == beta^k.
  * No query scaling is applied; callers pre-scale q if they want one.
  *
  * Conventions shared by every entry point
@@ -50,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 2
+#define DR_ABI_VERSION 3
 
 typedef enum {
     DR_OK = 0,
@@ -127,6 +133,23 @@ dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, con
                        float* S_final, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dr_chunk_fwd_kv -- dr_chunk_fwd with separate channel-wise erase and write
+ * strengths (FG2-GDN page, section "Erweiterung: FG2-GDN+"): beta_k takes the
+ * place of beta on kt in both the erase and the write term, beta_v scales v.
+ *
+ *   d->beta    must be DR_BETA_CHANNEL (else DR_ERR_UNSUPPORTED); so Dv == Dk
+ *   beta_k     [B][H][L][Dk] fp32, expected in [0, 1] (not checked)
+ *   beta_v     [B][H][L][Dk] fp32, expected in [0, 1] (not checked)
+ * Every other argument, the workspace (dr_chunk_fwd_workspace_bytes(d)) and
+ * the error behaviour are those of dr_chunk_fwd; beta_v == beta_k gives
+ * dr_chunk_fwd's result.
+ */
+dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta_k, const float* beta_v,
+                          const float* S0, void* o, float* S_final, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * dr_decode_step -- one recurrent step (DeltaNet page, property list: inference
  * uses the recurrent form with a constant-size state) for N x H independent
  * states, one new token each, updating the states in place:
@@ -145,9 +168,25 @@ dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, 
                          void* stream);
 
 /*
+ * dr_decode_step_kv -- dr_decode_step with separate channel-wise erase and
+ * write strengths (FG2-GDN page, section "Erweiterung: FG2-GDN+"):
+ *
+ *   S[n][h] <- (I - kt kt^T) Diag(alpha) S[n][h] + kt vt^T,
+ *   kt = sqrt(beta_k) (.) k,  vt = sqrt(beta_v) (.) v
+ *
+ *   d->beta    must be DR_BETA_CHANNEL (else DR_ERR_UNSUPPORTED)
+ *   beta_k, beta_v  [N][H][Dk] fp32
+ * Every other argument as for dr_decode_step.  Equivalent to dr_chunk_fwd_kv
+ * with L == 1, S0 == S_final == S.
+ */
+dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                            const float* log_alpha, const float* beta_k, const float* beta_v,
+                            float* S, void* o, void* stream);
+
+/*
  * Per-kernel timing, for benchmarks and profiling (not part of the method).
- * Between dr_profile_begin and dr_profile_end every dr_chunk_fwd and
- * dr_decode_step also records HIP events on its stream around each kernel it
+ * Between dr_profile_begin and dr_profile_end every chunked-forward and
+ * decode call also records HIP events on its stream around each kernel it
  * launches; dr_profile_end waits for those events and reports the summed
  * kernel durations (event to event, so a launch gap between two kernels of
  * one call is counted with the earlier kernel).  Calls made while profiling
@@ -156,8 +195,8 @@ dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, 
  * Returns DR_ERR_NULL for a NULL report, DR_ERR_HIP if an event fails.
  */
 typedef struct dr_profile_report {
-    int chunk_calls;    /* dr_chunk_fwd calls that launched kernels */
-    int decode_calls;   /* dr_decode_step calls that launched kernels */
+    int chunk_calls;    /* dr_chunk_fwd(_kv) calls that launched kernels */
+    int decode_calls;   /* dr_decode_step(_kv) calls that launched kernels */
     double prep_ms;     /* chunk preparation kernel (gates, A, T, P) */
     double scan_ms;     /* inter-chunk state scan kernel (o and S_final) */
     double decode_ms;   /* recurrent decode kernel */

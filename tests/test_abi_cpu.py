@@ -141,6 +141,43 @@ def test_decode_validation():
     assert _dcall(D(**{**ok, "N": 0})) == drl.DR_OK
 
 
+def _kvcall(desc, q=FAKE, k=FAKE, v=FAKE, la=FAKE, bk=FAKE, bv=FAKE + 4096, S0=None, o=FAKE, Sf=FAKE,
+            ws=FAKE, wbytes=1 << 40):
+    return drl.lib().dr_chunk_fwd_kv(ctypes.byref(desc) if desc is not None else None, q, k, v, la, bk,
+                                     bv, S0, o, Sf, ws, wbytes, None)
+
+
+def test_chunk_kv_validation():
+    ch = dict(gate="channel", beta_mode="channel")
+    assert _kvcall(None) == drl.DR_ERR_NULL
+    # separate strengths are channel-wise only
+    assert _kvcall(_desc(gate="channel")) == drl.DR_ERR_UNSUPPORTED
+    assert "DR_BETA_CHANNEL" in drl.dr_last_error()
+    assert _kvcall(_desc(**ch), bv=None) == drl.DR_ERR_NULL
+    assert _kvcall(_desc(**ch), bk=None) == drl.DR_ERR_NULL
+    assert _kvcall(_desc(**ch), bv=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
+    assert "beta_v" in drl.dr_last_error()
+    assert _kvcall(_desc(**ch, Dv=64)) == drl.DR_ERR_UNSUPPORTED
+    assert _kvcall(_desc(**ch), ws=None) == drl.DR_ERR_WORKSPACE
+    assert _kvcall(_desc(**ch, B=0), q=None, k=None, v=None, la=None, bk=None, bv=None, o=None,
+                   Sf=None, ws=None, wbytes=0) == drl.DR_OK
+
+
+def test_decode_kv_validation():
+    D = drl.DecodeDesc
+    ok = dict(N=4, H=2, Dk=128, Dv=128, in_dtype=drl.DR_BF16, out_dtype=drl.DR_F32, gate=2, beta=1)
+
+    def call(desc, bk=FAKE, bv=FAKE + 4096, S=FAKE):
+        return drl.lib().dr_decode_step_kv(ctypes.byref(desc) if desc is not None else None, FAKE,
+                                           FAKE, FAKE, FAKE, bk, bv, S, FAKE, None)
+
+    assert call(None) == drl.DR_ERR_NULL
+    assert call(D(**{**ok, "beta": 0})) == drl.DR_ERR_UNSUPPORTED
+    assert call(D(**ok), bv=None) == drl.DR_ERR_NULL
+    assert call(D(**ok), bv=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
+    assert call(D(**{**ok, "N": 0})) == drl.DR_OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(drl, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(drl, "_lib", None)

@@ -101,6 +101,45 @@ def test_very_strong_scalar_gate():
     _check(p)
 
 
+# ------------------------------------- separate erase and write strengths
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("L", [1, 65, 200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_kv_small_sweep(dtype, gate, L, D):
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    p = inputs.make_chunk_problem(1, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode="channel",
+                                  log_alpha_range=rng, s0_var=0.01, seed=L + D + 1, beta_v=True,
+                                  name=f"kv-{dtype}-{gate}-L{L}-D{D}")
+    _check(p, tol=1e-5 if dtype == "f32" else None)
+
+
+def test_kv_channel_prep_loop_uneven_jobs():
+    p = inputs.make_chunk_problem(1, 5, 64 * 60 + 17, 128, 128, gate="channel", beta_mode="channel",
+                                  log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=10, beta_v=True,
+                                  name="kv-cg-loop")
+    _check(p)
+
+
+def test_kv_equal_strengths_match_single_strength_bits():
+    # beta_v == beta_k through the separate-strength entry point gives the
+    # single-strength result bit for bit (same kernels, same operands)
+    import delta_rule_linear_amd as drl
+    from gpu_common import problem_to_dev
+    for gate in ("scalar", "channel"):
+        p = inputs.make_chunk_problem(1, 3, 300, 128, 128, gate=gate, beta_mode="channel",
+                                      log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=11)
+        announce("kv equal strengths", gate)
+        t = problem_to_dev(p)
+        o1, S1 = drl.dr_chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"],
+                                  gate=gate, beta_mode="channel")
+        bv = t["beta"].clone()
+        o2, S2 = drl.dr_chunk_fwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], bv, t["S0"],
+                                     gate=gate)
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
 # ---------------------------------------------------------------- full sizes
 
 FULL = {
@@ -109,6 +148,7 @@ FULL = {
     "gdn_b4h16_4k": [(0, 0), (3, 15), (1, 7)],
     "kda_b2h32_16k": [(0, 0), (1, 31)],
     "fg2_b2h16_16k": [(0, 0), (1, 15)],
+    "fg2plus_b2h16_16k": [(0, 3), (1, 12)],
     "gdn_b2h16_16k": [(0, 0), (1, 15)],
     "gdn_b1h16_64k": [(0, 0), (0, 15)],
 }
@@ -179,6 +219,29 @@ def test_decode_full_batch_sampled():
         oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], dp.log_alpha[t], dp.beta[t],
                                     gate="scalar", beta_mode="scalar")
         assert rel_err(to_np(o), oy) <= 1e-5
+    assert rel_err(to_np(S), Sy) <= 1e-5
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_kv_steps(gate, dtype):
+    import delta_rule_linear_amd as drl
+    import oracle
+    from gpu_common import to_dev
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    dp = inputs.make_decode_problem(5, 3, 128, 128, 4, in_dtype=dtype, gate=gate, beta_mode="channel",
+                                    log_alpha_range=rng, seed=12, beta_v=True)
+    announce("decode kv", gate, dtype)
+    S = to_dev(dp.S, "f32")
+    Sy = dp.S.astype(np.float64)
+    for t in range(dp.steps):
+        la = None if dp.log_alpha is None else dp.log_alpha[t]
+        o = drl.dr_decode_step_kv(S, to_dev(dp.q[t], dtype), to_dev(dp.k[t], dtype),
+                                  to_dev(dp.v[t], dtype), to_dev(la, "f32"), to_dev(dp.beta[t], "f32"),
+                                  to_dev(dp.beta_v[t], "f32"), gate=gate)
+        oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], la, dp.beta[t], gate=gate,
+                                    beta_mode="channel", beta_v=dp.beta_v[t])
+        assert rel_err(to_np(o), oy) <= 1e-5, f"step {t} o"
     assert rel_err(to_np(S), Sy) <= 1e-5
 
 
