@@ -13,6 +13,10 @@ equations; DeltaNet page, step list, step 6 for the output):
 With separate erase and write strengths (FG2-GDN page, section "Erweiterung:
 FG2-GDN+"; the page prints no equation, the reading taken is) kt = sqrt(beta^k)
 * k in both terms and vt = sqrt(beta^v) * v.
+Optional input preparation in front of it (DeltaNet page, step list, step 2
+and its notes on the key/query map and on choosing beta): qk_l2norm replaces q
+and k by unit vectors (a zero vector stays zero); beta_logit takes the
+strength arrays as logits, beta = sigmoid(x).
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ _SRC = os.path.join(_HERE, "dr_oracle.c")
 LIB_PATH = os.path.join(_HERE, "libdr_oracle.so")
 
 GATE_CODES = {"none": 0, "scalar": 1, "channel": 2}
+IN_QK_L2NORM, IN_BETA_LOGIT = 1, 2
 BETA_CODES = {"scalar": 0, "channel": 1}
 
 _lib = None
@@ -53,6 +58,10 @@ def load(path: str = LIB_PATH):
     lib.dro_forward_kv.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp, dp,
                                                          ctypes.c_int, dp, dp, dp, ctypes.c_int]
     lib.dro_forward_kv.restype = ctypes.c_int
+    lib.dro_forward_ex.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp, dp,
+                                                        ctypes.c_int, ctypes.c_int, dp, dp, dp,
+                                                        ctypes.c_int]
+    lib.dro_forward_ex.restype = ctypes.c_int
     lib.dro_max_threads.restype = ctypes.c_int
     return lib
 
@@ -72,12 +81,14 @@ def _f64(a: Optional[np.ndarray]):
 
 
 def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
-            nthreads: int = 0, lib=None, beta_v=None):
+            nthreads: int = 0, lib=None, beta_v=None, qk_l2norm: bool = False,
+            beta_logit: bool = False):
     """Run the recurrence over [B, H, L, D] inputs; returns (o, S_final) in fp64.
 
     log_alpha is [B,H,L] (scalar gate), [B,H,L,Dk] (channel gate) or None
     (gate "none"); beta is [B,H,L] or [B,H,L,Dk]; S0 is [B,H,Dk,Dv] or None.
     beta_v (beta's shape) is a separate write strength; None means beta.
+    qk_l2norm and beta_logit switch on the input preparation.
     """
     lib = lib or _get()
     q = np.asarray(q)
@@ -93,7 +104,14 @@ def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
     Sf = np.empty((B, H, Dk, Dv), np.float64)
     op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     fp = Sf.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
-    if beta_v is None:
+    flags = (IN_QK_L2NORM if qk_l2norm else 0) | (IN_BETA_LOGIT if beta_logit else 0)
+    if flags:
+        bva, bvp = _f64(beta if beta_v is None else beta_v)
+        if np.shape(bva) != np.shape(ba):
+            raise ValueError("beta_v must have beta's shape")
+        rc = lib.dro_forward_ex(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp, bvp,
+                                BETA_CODES[beta_mode], flags, sp, op, fp, int(nthreads))
+    elif beta_v is None:
         rc = lib.dro_forward(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp,
                              BETA_CODES[beta_mode], sp, op, fp, int(nthreads))
     else:
@@ -111,11 +129,13 @@ def forward_problem(p, nthreads: int = 0, lib=None):
     """Oracle over a ChunkProblem-like object (fields as the input generator's)."""
     return forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, gate=p.gate,
                    beta_mode=p.beta_mode, nthreads=nthreads, lib=lib,
-                   beta_v=getattr(p, "beta_v", None))
+                   beta_v=getattr(p, "beta_v", None), qk_l2norm=getattr(p, "qk_l2norm", False),
+                   beta_logit=getattr(p, "beta_logit", False))
 
 
 def decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str,
-                nthreads: int = 0, lib=None, beta_v=None):
+                nthreads: int = 0, lib=None, beta_v=None, qk_l2norm: bool = False,
+                beta_logit: bool = False):
     """One recurrent step for a batch of states: S [N,H,Dk,Dv], q/k/v [N,H,D].
 
     The decode step is the forward with a single token, started from S.
@@ -123,7 +143,8 @@ def decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str,
     """
     ex = lambda a: None if a is None else np.asarray(a)[:, :, None]
     o, Sn = forward(ex(q), ex(k), ex(v), ex(log_alpha), ex(beta), S, gate=gate,
-                    beta_mode=beta_mode, nthreads=nthreads, lib=lib, beta_v=ex(beta_v))
+                    beta_mode=beta_mode, nthreads=nthreads, lib=lib, beta_v=ex(beta_v),
+                    qk_l2norm=qk_l2norm, beta_logit=beta_logit)
     return o[:, :, 0], Sn
 
 

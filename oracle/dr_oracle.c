@@ -24,6 +24,18 @@
  *   write term) and vt = sqrt(beta^v_t) (.) v_t (dro_forward_kv); with
  *   beta^v = beta^k it is the equation above.
  *
+ * Optional input preparation (dro_forward_ex, input_flags), the steps in
+ * front of the recurrence:
+ *   DRO_IN_QK_L2NORM  DeltaNet page, step list, step 2, and its note on the
+ *     key/query map: keys pass through a feature map followed by L2
+ *     normalisation, and queries get the same map.  Here q_t and k_t are
+ *     replaced by q_t / |q_t|_2 and k_t / |k_t|_2 before anything else (a zero
+ *     vector stays zero).  The learned parts of the map (a projection, SiLU, a
+ *     short convolution) belong to the layer in front and are not modelled.
+ *   DRO_IN_BETA_LOGIT  DeltaNet page, list of design choices: beta_t from a
+ *     sigmoid projection.  The strength arrays (beta, and beta^v) hold the
+ *     projection's output x, and beta = 1 / (1 + e^{-x}).
+ *
  * The update is evaluated in the rank-one form that the DeltaNet page's steps
  * 3-5 describe (read the current map, form the error, add the outer product):
  *       S'  = Diag(alpha_t) S_{t-1}
@@ -45,9 +57,24 @@
 
 enum { DRO_GATE_NONE = 0, DRO_GATE_SCALAR = 1, DRO_GATE_CHANNEL = 2 };
 enum { DRO_BETA_SCALAR = 0, DRO_BETA_CHANNEL = 1 };
+enum { DRO_IN_QK_L2NORM = 1, DRO_IN_BETA_LOGIT = 2 };
 
 /* Return codes. */
 enum { DRO_OK = 0, DRO_EINVAL = 1, DRO_ENOMEM = 2 };
+
+/* 1 / |x|_2 over n entries, 0 for the zero vector. */
+static double inv_l2(const double* x, int n)
+{
+    double s = 0.0;
+    for (int c = 0; c < n; ++c) s += x[c] * x[c];
+    return s > 0.0 ? 1.0 / sqrt(s) : 0.0;
+}
+
+/* A strength as given, or the sigmoid of the given logit. */
+static double strength(double x, int logit)
+{
+    return logit ? 1.0 / (1.0 + exp(-x)) : x;
+}
 
 /* One (b, h) sequence.  Pointers are already offset to that sequence:
  *   q, k   [L][Dk]      v, o [L][Dv]
@@ -60,22 +87,29 @@ enum { DRO_OK = 0, DRO_EINVAL = 1, DRO_ENOMEM = 2 };
 static void run_sequence(int L, int Dk, int Dv,
                          const double* q, const double* k, const double* v,
                          const double* la, int gate, const double* beta, const double* betav,
-                         int beta_mode, double* S, double* o, double* kt, double* vt, double* p)
+                         int beta_mode, int flags, double* S, double* o, double* kt, double* vt,
+                         double* p)
 {
+    const int l2 = (flags & DRO_IN_QK_L2NORM) != 0;
+    const int logit = (flags & DRO_IN_BETA_LOGIT) != 0;
     for (int t = 0; t < L; ++t) {
         const double* qt = q + (size_t)t * Dk;
         const double* k_t = k + (size_t)t * Dk;
         const double* v_t = v + (size_t)t * Dv;
 
+        /* input preparation: the factors that make q_t and k_t unit vectors */
+        const double qn = l2 ? inv_l2(qt, Dk) : 1.0;
+        const double kn = l2 ? inv_l2(k_t, Dk) : 1.0;
+
         /* scaled key and value */
         for (int c = 0; c < Dk; ++c) {
             double b = beta_mode == DRO_BETA_SCALAR ? beta[t] : beta[(size_t)t * Dk + c];
-            kt[c] = sqrt(b) * k_t[c];
+            kt[c] = sqrt(strength(b, logit)) * (kn * k_t[c]);
         }
         for (int j = 0; j < Dv; ++j) {
             /* channel beta scales v's channel j by beta's channel j (d_v == d_k) */
             double b = beta_mode == DRO_BETA_SCALAR ? betav[t] : betav[(size_t)t * Dk + j];
-            vt[j] = sqrt(b) * v_t[j];
+            vt[j] = sqrt(strength(b, logit)) * v_t[j];
         }
 
         /* S' = Diag(alpha_t) S : row c of S is scaled by alpha_t[c] */
@@ -105,30 +139,34 @@ static void run_sequence(int L, int Dk, int Dv,
         for (int j = 0; j < Dv; ++j) ot[j] = 0.0;
         for (int c = 0; c < Dk; ++c) {
             const double* row = S + (size_t)c * Dv;
-            for (int j = 0; j < Dv; ++j) ot[j] += row[j] * qt[c];
+            for (int j = 0; j < Dv; ++j) ot[j] += row[j] * (qn * qt[c]);
         }
     }
 }
 
 /*
- * dro_forward_kv -- the whole batch, with separate key and value strengths.
+ * dro_forward_ex -- the whole batch, with separate key and value strengths and
+ * the optional input preparation.
  *   q, k      [B][H][L][Dk] fp64
  *   v         [B][H][L][Dv] fp64
  *   log_alpha [B][H][L] (gate SCALAR) or [B][H][L][Dk] (gate CHANNEL); NULL for NONE
  *   beta      [B][H][L] (SCALAR) or [B][H][L][Dk] (CHANNEL; needs Dv == Dk): beta^k
  *   beta_v    beta^v, the same shape as beta
+ *   input_flags  DRO_IN_QK_L2NORM | DRO_IN_BETA_LOGIT, or 0
  *   S0        [B][H][Dk][Dv] or NULL (zeros)
  *   o         [B][H][L][Dv]     out
  *   S_final   [B][H][Dk][Dv]    out, may be NULL
  *   nthreads  worker threads over (b, h); <= 0 means the OpenMP default
  * Decode is the same call with L == 1 and S0 the current states.
  */
-int dro_forward_kv(int B, int H, int L, int Dk, int Dv,
+int dro_forward_ex(int B, int H, int L, int Dk, int Dv,
                    const double* q, const double* k, const double* v,
                    const double* log_alpha, int gate, const double* beta, const double* beta_v,
-                   int beta_mode, const double* S0, double* o, double* S_final, int nthreads)
+                   int beta_mode, int input_flags, const double* S0, double* o, double* S_final,
+                   int nthreads)
 {
     if (B <= 0 || H <= 0 || L < 0 || Dk <= 0 || Dv <= 0) return DRO_EINVAL;
+    if (input_flags & ~(DRO_IN_QK_L2NORM | DRO_IN_BETA_LOGIT)) return DRO_EINVAL;
     if (!q || !k || !v || !beta || !beta_v || !o) return DRO_EINVAL;
     if (gate < DRO_GATE_NONE || gate > DRO_GATE_CHANNEL) return DRO_EINVAL;
     if (beta_mode != DRO_BETA_SCALAR && beta_mode != DRO_BETA_CHANNEL) return DRO_EINVAL;
@@ -158,13 +196,23 @@ int dro_forward_kv(int B, int H, int L, int Dk, int Dv,
         run_sequence(L, Dk, Dv,
                      q + (size_t)s * L * Dk, k + (size_t)s * L * Dk, v + (size_t)s * L * Dv,
                      log_alpha ? log_alpha + (size_t)s * lw : NULL, gate,
-                     beta + (size_t)s * bw, beta_v + (size_t)s * bw, beta_mode,
+                     beta + (size_t)s * bw, beta_v + (size_t)s * bw, beta_mode, input_flags,
                      S, o + (size_t)s * L * Dv, kt, vt, p);
         if (S_final) memcpy(S_final + (size_t)s * sz, S, sizeof(double) * sz);
         free(S);
     }
     (void)nthreads;
     return err;
+}
+
+/* Separate strengths, inputs as given. */
+int dro_forward_kv(int B, int H, int L, int Dk, int Dv,
+                   const double* q, const double* k, const double* v,
+                   const double* log_alpha, int gate, const double* beta, const double* beta_v,
+                   int beta_mode, const double* S0, double* o, double* S_final, int nthreads)
+{
+    return dro_forward_ex(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta_v, beta_mode, 0, S0,
+                          o, S_final, nthreads);
 }
 
 /* The same with one strength for both the key and the value (beta^v = beta). */

@@ -457,3 +457,83 @@ def pin_kv_superposition(fwd_kv):
 
 
 KV_PINS = [pin_kv_dense_product, pin_kv_write_scaling, pin_kv_superposition]
+
+
+# ---------------------------------------------------------------------------
+# Input preparation in front of the recurrence (DeltaNet page, step list,
+# step 2 and its notes on the key/query map and on choosing beta): qk_l2norm
+# makes q and k unit vectors, beta_logit reads the strengths as logits.
+# Each pin takes fwd_ex(q, k, v, la, beta, beta_v, S0, *, gate, beta_mode,
+# qk_l2norm, beta_logit); beta_v may be None (one strength).
+# ---------------------------------------------------------------------------
+
+def _modes():
+    return [("none", "scalar"), ("scalar", "scalar"), ("channel", "scalar"), ("scalar", "channel"),
+            ("channel", "channel")]
+
+
+def pin_l2norm_ray_invariance(fwd_ex):
+    """With qk_l2norm the result depends on q_t and k_t only through their
+    directions: positive per-token rescaling changes nothing."""
+    for n, (gate, beta_mode) in enumerate(_modes()):
+        q, k, v, la, beta, S0 = random_case(70 + n, L=11, Dk=5, Dv=5, gate=gate, beta_mode=beta_mode,
+                                            unit_keys=False)
+        r = _rng(80 + n)
+        cq = r.uniform(0.2, 5.0, q.shape[:-1] + (1,))
+        ck = r.uniform(0.2, 5.0, k.shape[:-1] + (1,))
+        kw = dict(gate=gate, beta_mode=beta_mode, qk_l2norm=True, beta_logit=False)
+        o1, S1 = fwd_ex(q, k, v, la, beta, None, S0, **kw)
+        o2, S2 = fwd_ex(q * cq, k * ck, v, la, beta, None, S0, **kw)
+        _close(o2, o1, 1e-12, f"o ({gate},{beta_mode})")
+        _close(S2, S1, 1e-12, f"S ({gate},{beta_mode})")
+
+
+def pin_l2norm_fixes_unit_and_zero_vectors(fwd_ex):
+    """Unit vectors, and the zero vector, pass through the normalisation
+    unchanged.  With the ray invariance above this fixes the map x / |x|_2."""
+    for n, (gate, beta_mode) in enumerate(_modes()):
+        q, k, v, la, beta, S0 = random_case(90 + n, L=11, Dk=5, Dv=5, gate=gate, beta_mode=beta_mode)
+        q = _unit(q)
+        q[:, :, 3] = 0.0
+        k[:, :, 5] = 0.0
+        kw = dict(gate=gate, beta_mode=beta_mode, beta_logit=False)
+        o1, S1 = fwd_ex(q, k, v, la, beta, None, S0, qk_l2norm=True, **kw)
+        o2, S2 = fwd_ex(q, k, v, la, beta, None, S0, qk_l2norm=False, **kw)
+        assert np.isfinite(o1).all() and np.isfinite(S1).all()
+        _close(o1, o2, 1e-13, f"o ({gate},{beta_mode})")
+        _close(S1, S2, 1e-13, f"S ({gate},{beta_mode})")
+
+
+def pin_beta_logit_round_trip(fwd_ex):
+    """Strengths given as logits log(b / (1 - b)) reproduce the run with the
+    strengths b themselves, for one strength and for separate erase and
+    write strengths."""
+    for n, (gate, beta_mode) in enumerate(_modes()):
+        q, k, v, la, beta, S0 = random_case(100 + n, L=11, Dk=5, Dv=5, gate=gate, beta_mode=beta_mode)
+        bv = _rng(110 + n).uniform(0.05, 0.95, beta.shape)
+        logit = lambda b: np.log(b) - np.log1p(-b)
+        kw = dict(gate=gate, beta_mode=beta_mode, qk_l2norm=False)
+        for b_v in (None, bv):
+            o1, S1 = fwd_ex(q, k, v, la, beta, b_v, S0, beta_logit=False, **kw)
+            o2, S2 = fwd_ex(q, k, v, la, logit(beta), None if b_v is None else logit(b_v), S0,
+                            beta_logit=True, **kw)
+            _close(o2, o1, 1e-12, f"o ({gate},{beta_mode})")
+            _close(S2, S1, 1e-12, f"S ({gate},{beta_mode})")
+
+
+def pin_beta_logit_saturation(fwd_ex):
+    """Logit +60 is a full write (beta = 1 to 1e-26), logit -60 no write at
+    all: the state only decays (the closed form of beta = 0)."""
+    q, k, v, la, beta, S0 = random_case(120, L=9, Dk=5, Dv=5, gate="channel", beta_mode="channel")
+    kw = dict(gate="channel", beta_mode="channel", qk_l2norm=False)
+    o1, S1 = fwd_ex(q, k, v, la, np.full_like(beta, 60.0), None, S0, beta_logit=True, **kw)
+    o2, S2 = fwd_ex(q, k, v, la, np.ones_like(beta), None, S0, beta_logit=False, **kw)
+    _close(o1, o2, 1e-13, "o at logit +60")
+    _close(S1, S2, 1e-13, "S at logit +60")
+    _, S3 = fwd_ex(q, k, v, la, np.full_like(beta, -60.0), None, S0, beta_logit=True, **kw)
+    decay = np.exp(la.sum(axis=2))                       # [B, H, Dk]
+    _close(S3, decay[..., None] * S0, 1e-12, "S at logit -60")
+
+
+PREP_PINS = [pin_l2norm_ray_invariance, pin_l2norm_fixes_unit_and_zero_vectors,
+             pin_beta_logit_round_trip, pin_beta_logit_saturation]

@@ -3,6 +3,7 @@ the pin suite catches every one of them (CPU only).  The mistakes are planted
 in temporary copies; the committed oracle is never modified."""
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -14,10 +15,11 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "dr_oracle.c")
 MUTANTS = [
     ("drop_decay", "row[j] *= a;", "row[j] *= 1.0;"),
     ("sign_of_error", "row[j] += kt[c] * (vt[j] - p[j]);", "row[j] += kt[c] * (vt[j] + p[j]);"),
-    ("beta_not_sqrt", "kt[c] = sqrt(b) * k_t[c];", "kt[c] = b * k_t[c];"),
-    ("value_unscaled", "vt[j] = sqrt(b) * v_t[j];", "vt[j] = v_t[j];"),
+    ("beta_not_sqrt", "kt[c] = sqrt(strength(b, logit)) * (kn * k_t[c]);",
+     "kt[c] = strength(b, logit) * (kn * k_t[c]);"),
+    ("value_unscaled", "vt[j] = sqrt(strength(b, logit)) * v_t[j];", "vt[j] = v_t[j];"),
     ("read_unscaled_key", "p[j] += row[j] * kt[c];", "p[j] += row[j] * k_t[c];"),
-    ("output_from_query_free_state", "ot[j] += row[j] * qt[c];", "ot[j] += row[j] * k_t[c];"),
+    ("output_from_query_free_state", "ot[j] += row[j] * (qn * qt[c]);", "ot[j] += row[j] * (qn * k_t[c]);"),
     ("gate_index_shift", "exp(la[(size_t)t * Dk + c])", "exp(la[(size_t)t * Dk + (c + 1) % Dk])"),
     ("channel_beta_wrong_channel", "betav[(size_t)t * Dk + j]", "betav[(size_t)t * Dk + (Dk - 1 - j)]"),
     ("error_drops_read", "(vt[j] - p[j])", "(vt[j] - 0.0 * p[j])"),
@@ -52,7 +54,8 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
 KV_MUTANTS = [
     ("value_uses_key_strength", "? betav[t] : betav[(size_t)t * Dk + j]", "? beta[t] : beta[(size_t)t * Dk + j]"),
     ("key_uses_value_strength", "? beta[t] : beta[(size_t)t * Dk + c]", "? betav[t] : betav[(size_t)t * Dk + c]"),
-    ("value_strength_not_sqrt", "vt[j] = sqrt(b) * v_t[j];", "vt[j] = b * v_t[j];"),
+    ("value_strength_not_sqrt", "vt[j] = sqrt(strength(b, logit)) * v_t[j];",
+     "vt[j] = strength(b, logit) * v_t[j];"),
 ]
 
 
@@ -72,6 +75,39 @@ def test_kv_pins_catch_planted_mistake(tmp_path, name, old, new):
     for pin in oracle_pins.KV_PINS:
         try:
             pin(fwd_kv)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
+
+
+# Mistakes in the input preparation, caught by its pins.
+PREP_MUTANTS = [
+    ("query_not_normalised", "const double qn = l2 ? inv_l2(qt, Dk) : 1.0;", "const double qn = 1.0;"),
+    ("key_by_squared_norm", "kt[c] = sqrt(strength(b, logit)) * (kn * k_t[c]);",
+     "kt[c] = sqrt(strength(b, logit)) * (kn * kn * k_t[c]);"),
+    ("zero_vector_not_kept", "return s > 0.0 ? 1.0 / sqrt(s) : 0.0;", "return 1.0 / sqrt(s);"),
+    ("sigmoid_sign", "return logit ? 1.0 / (1.0 + exp(-x)) : x;", "return logit ? 1.0 / (1.0 + exp(x)) : x;"),
+    ("value_strength_not_from_logit", "vt[j] = sqrt(strength(b, logit)) * v_t[j];", "vt[j] = sqrt(b) * v_t[j];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PREP_MUTANTS, ids=[m[0] for m in PREP_MUTANTS])
+def test_prep_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+
+    def fwd_ex(q, k, v, la, beta, beta_v, S0, *, gate, beta_mode, qk_l2norm, beta_logit):
+        return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, lib=lib,
+                              beta_v=beta_v, qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+
+    caught = []
+    for pin in oracle_pins.PREP_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(fwd_ex)
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"

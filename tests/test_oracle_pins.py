@@ -68,3 +68,38 @@ def test_kv_decode_step_is_one_token_forward():
                                 gate="channel", beta_mode="channel", beta_v=bv[:, :, 0])
     o2, S2 = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode="channel", beta_v=bv)
     assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
+
+
+def fwd_ex(q, k, v, la, beta, beta_v, S0, *, gate, beta_mode, qk_l2norm, beta_logit):
+    return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, beta_v=beta_v,
+                          qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.PREP_PINS, ids=lambda f: f.__name__)
+def test_input_preparation_pin(pin):
+    pin(fwd_ex)
+
+
+def test_input_preparation_off_is_the_plain_forward():
+    q, k, v, la, beta, S0 = oracle_pins.random_case(130, L=10, Dk=5, Dv=5, gate="channel",
+                                                    beta_mode="channel")
+    a = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode="channel")
+    lib = oracle._get()
+    import ctypes
+    dp = lambda x: np.ascontiguousarray(x, np.float64).ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    o = np.empty_like(a[0])
+    Sf = np.empty_like(a[1])
+    arrs = [np.ascontiguousarray(x, np.float64) for x in (q, k, v, la, beta, S0)]
+    rc = lib.dro_forward_ex(1, 2, 10, 5, 5, dp(arrs[0]), dp(arrs[1]), dp(arrs[2]), dp(arrs[3]), 2,
+                            dp(arrs[4]), dp(arrs[4]), 1, 0, dp(arrs[5]), dp(o), dp(Sf), 0)
+    assert rc == 0
+    assert np.array_equal(o, a[0]) and np.array_equal(Sf, a[1])
+
+
+def test_input_preparation_decode_is_one_token_forward():
+    q, k, v, la, beta, S0 = oracle_pins.random_case(131, B=3, H=2, L=1, Dk=6, Dv=6, gate="scalar",
+                                                    beta_mode="scalar", unit_keys=False)
+    kw = dict(gate="scalar", beta_mode="scalar", qk_l2norm=True, beta_logit=True)
+    o1, S1 = oracle.decode_step(S0, q[:, :, 0], k[:, :, 0], v[:, :, 0], la[:, :, 0], beta[:, :, 0], **kw)
+    o2, S2 = oracle.forward(q, k, v, la, beta, S0, **kw)
+    assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
