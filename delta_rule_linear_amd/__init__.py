@@ -23,11 +23,12 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 3
+DR_ABI_VERSION = 4
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
 BETAS = {"scalar": 0, "channel": 1}
+DR_IN_QK_L2NORM, DR_IN_BETA_LOGIT = 1, 2
 EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "dr_decode_step",
            "dr_decode_step_kv", "dr_status_str", "dr_last_error", "dr_abi_version",
            "dr_profile_begin", "dr_profile_end")
@@ -44,7 +45,7 @@ class DeltaRuleError(RuntimeError):
 class ChunkDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("L", ctypes.c_int), ("Dk", ctypes.c_int),
                 ("Dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
-                ("gate", ctypes.c_int), ("beta", ctypes.c_int)]
+                ("gate", ctypes.c_int), ("beta", ctypes.c_int), ("input_flags", ctypes.c_uint)]
 
 
 class ProfileReport(ctypes.Structure):
@@ -55,7 +56,7 @@ class ProfileReport(ctypes.Structure):
 class DecodeDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("Dk", ctypes.c_int), ("Dv", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("gate", ctypes.c_int),
-                ("beta", ctypes.c_int)]
+                ("beta", ctypes.c_int), ("input_flags", ctypes.c_uint)]
 
 
 _lib = None
@@ -170,8 +171,13 @@ def _need(t, name, dtype=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def chunk_desc(B, H, L, Dk, Dv, in_dtype, out_dtype, gate: str, beta_mode: str) -> ChunkDesc:
-    return ChunkDesc(B, H, L, Dk, Dv, in_dtype, out_dtype, GATES[gate], BETAS[beta_mode])
+def input_flags(qk_l2norm: bool = False, beta_logit: bool = False) -> int:
+    return (DR_IN_QK_L2NORM if qk_l2norm else 0) | (DR_IN_BETA_LOGIT if beta_logit else 0)
+
+
+def chunk_desc(B, H, L, Dk, Dv, in_dtype, out_dtype, gate: str, beta_mode: str,
+               flags: int = 0) -> ChunkDesc:
+    return ChunkDesc(B, H, L, Dk, Dv, in_dtype, out_dtype, GATES[gate], BETAS[beta_mode], flags)
 
 
 def dr_chunk_fwd_workspace_bytes(desc: ChunkDesc) -> int:
@@ -180,31 +186,34 @@ def dr_chunk_fwd_workspace_bytes(desc: ChunkDesc) -> int:
 
 def dr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
                  out_dtype=None, o=None, S_final=None, want_state: bool = True,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
     """Chunked forward over [B, H, L, D] device tensors; returns (o, S_final).
 
     q, k: [B,H,L,Dk]; v: [B,H,L,Dv] (bf16 or fp32, same dtype); log_alpha:
     [B,H,L] / [B,H,L,Dk] fp32 or None for gate "none"; beta: [B,H,L] /
     [B,H,L,Dk] fp32; S0: [B,H,Dk,Dv] fp32 or None.  S_final may be passed in
     (it may be S0 itself for an in-place carry); with want_state=False no
-    final state is written and None is returned for it.
+    final state is written and None is returned for it.  qk_l2norm and
+    beta_logit switch on the input preparation (DR_IN_QK_L2NORM,
+    DR_IN_BETA_LOGIT).
     """
     return _chunk(q, k, v, log_alpha, beta, None, S0, gate, beta_mode, out_dtype, o, S_final,
-                  want_state, workspace, stream)
+                  want_state, workspace, stream, input_flags(qk_l2norm, beta_logit))
 
 
 def dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0=None, *, gate: str, out_dtype=None,
-                    o=None, S_final=None, want_state: bool = True, workspace=None, stream=None):
+                    o=None, S_final=None, want_state: bool = True, workspace=None, stream=None,
+                    qk_l2norm: bool = False, beta_logit: bool = False):
     """dr_chunk_fwd with separate channel-wise erase (beta_k) and write
     (beta_v) strengths, both [B,H,L,Dk] fp32; Dv == Dk."""
     if beta_v is None:
         raise ValueError("beta_v is required")
     return _chunk(q, k, v, log_alpha, beta_k, beta_v, S0, gate, "channel", out_dtype, o, S_final,
-                  want_state, workspace, stream)
+                  want_state, workspace, stream, input_flags(qk_l2norm, beta_logit))
 
 
 def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, S_final, want_state,
-           workspace, stream):
+           workspace, stream, flags):
     torch = _torch()
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
@@ -232,7 +241,8 @@ def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, 
         S_final = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
     elif S_final is not None:
         _need(S_final, "S_final", torch.float32, (B, H, Dk, Dv))
-    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), gate, beta_mode)
+    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), gate, beta_mode,
+                      flags)
     nbytes = dr_chunk_fwd_workspace_bytes(desc)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -249,25 +259,27 @@ def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, 
 
 
 def dr_decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str, out_dtype=None,
-                   o=None, stream=None):
+                   o=None, stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
     """One decode step for N x H states (updated in place); returns o [N,H,Dv].
 
     S: [N,H,Dk,Dv] fp32; q, k: [N,H,Dk]; v: [N,H,Dv]; log_alpha: [N,H] /
     [N,H,Dk] or None; beta: [N,H] / [N,H,Dk].
     """
-    return _decode(S, q, k, v, log_alpha, beta, None, gate, beta_mode, out_dtype, o, stream)
+    return _decode(S, q, k, v, log_alpha, beta, None, gate, beta_mode, out_dtype, o, stream,
+                   input_flags(qk_l2norm, beta_logit))
 
 
 def dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, *, gate: str, out_dtype=None, o=None,
-                      stream=None):
+                      stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
     """dr_decode_step with separate channel-wise erase (beta_k) and write
     (beta_v) strengths, both [N,H,Dk] fp32; Dv == Dk."""
     if beta_v is None:
         raise ValueError("beta_v is required")
-    return _decode(S, q, k, v, log_alpha, beta_k, beta_v, gate, "channel", out_dtype, o, stream)
+    return _decode(S, q, k, v, log_alpha, beta_k, beta_v, gate, "channel", out_dtype, o, stream,
+                   input_flags(qk_l2norm, beta_logit))
 
 
-def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, stream):
+def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, stream, flags):
     torch = _torch()
     N, H, Dk, Dv = S.shape
     _need(S, "S", torch.float32)
@@ -290,7 +302,7 @@ def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, 
     else:
         _need(o, "o", out_dtype, (N, H, Dv))
     desc = DecodeDesc(N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), GATES[gate],
-                      BETAS[beta_mode])
+                      BETAS[beta_mode], flags)
     if beta_v is None:
         _check(lib().dr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                     _ptr(beta), _ptr(S), _ptr(o), _stream(stream)))

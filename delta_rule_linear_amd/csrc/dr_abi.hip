@@ -36,7 +36,9 @@ bool valid_gate(int x) { return x == DR_GATE_NONE || x == DR_GATE_SCALAR || x ==
 bool valid_beta(int x) { return x == DR_BETA_SCALAR || x == DR_BETA_CHANNEL; }
 
 // Shared shape/mode checks.  `nseq` sequences (or states) of Dk x Dv.
-dr_status check_modes(int Dk, int Dv, int in_dtype, int out_dtype, int gate, int beta) {
+dr_status check_modes(int Dk, int Dv, int in_dtype, int out_dtype, int gate, int beta, unsigned flags) {
+    if (flags & ~(unsigned)(DR_IN_QK_L2NORM | DR_IN_BETA_LOGIT))
+        return fail(DR_ERR_UNSUPPORTED, "unknown input_flags bits 0x%x", flags);
     if (Dk != 64 && Dk != 128) return fail(DR_ERR_UNSUPPORTED, "Dk=%d: supported Dk are 64 and 128", Dk);
     if (Dv < 16 || Dv > 256 || Dv % 16 != 0)
         return fail(DR_ERR_UNSUPPORTED, "Dv=%d: Dv must be a multiple of 16 in [16, 256]", Dv);
@@ -84,7 +86,7 @@ dr_status check_chunk_desc(const dr_chunk_desc* d) {
     if (!d) return fail(DR_ERR_NULL, "descriptor is NULL");
     if (d->B < 0 || d->H < 0 || d->L < 0)
         return fail(DR_ERR_SHAPE, "negative dimension (B=%d H=%d L=%d)", d->B, d->H, d->L);
-    dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta);
+    dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta, d->input_flags);
     if (s != DR_OK) return s;
     if (d->B > 65535 || d->H > 65535)
         return fail(DR_ERR_UNSUPPORTED, "B and H are limited to 65535 (grid dimensions)");
@@ -251,6 +253,8 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.nseq = (int)nseq;
     a.has_gate = d->gate != DR_GATE_NONE;
     a.out_bf16 = d->out_dtype == DR_BF16;
+    a.qk_norm = (d->input_flags & DR_IN_QK_L2NORM) != 0;
+    a.beta_logit = (d->input_flags & DR_IN_BETA_LOGIT) != 0;
     char* ws = (char*)workspace;
     a.wsT = (dr::half_t*)(ws + w.T);
     a.wsP = (dr::half_t*)(ws + w.Pm);
@@ -270,7 +274,7 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
                       void* o, void* stream) {
     if (!d) return fail(DR_ERR_NULL, "descriptor is NULL");
     if (d->N < 0 || d->H < 0) return fail(DR_ERR_SHAPE, "negative dimension (N=%d H=%d)", d->N, d->H);
-    dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta);
+    dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta, d->input_flags);
     if (s != DR_OK) return s;
     const size_t nst = (size_t)d->N * d->H;
     const size_t blocks = nst * ((d->Dv + 63) / 64);
@@ -292,6 +296,8 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
     a.N = d->N; a.H = d->H; a.Dv = d->Dv;
     a.has_gate = d->gate != DR_GATE_NONE;
     a.out_bf16 = d->out_dtype == DR_BF16;
+    a.qk_norm = (d->input_flags & DR_IN_QK_L2NORM) != 0;
+    a.beta_logit = (d->input_flags & DR_IN_BETA_LOGIT) != 0;
     hipError_t e = dr::launch_decode(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL,
                                      d->beta == DR_BETA_CHANNEL, (hipStream_t)stream);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));

@@ -76,7 +76,9 @@ struct PrepSmem {
     static constexpr int kX = kT + 64 * 65;
     static constexpr int kG = CGATE ? kP + 64 * 65 : kX + 3 * 16 * 17;
     static constexpr int kB = kG + 64;
-    static constexpr int kFlag = kB + 64;
+    static constexpr int kNq = kB + 64;   // 1 / |q_r| (input preparation)
+    static constexpr int kNk = kNq + 64;  // 1 / |k_r|
+    static constexpr int kFlag = kNk + 64;
     static constexpr int FLOATS = kFlag + 4;
     static_assert(!CGATE || kX + 3 * 16 * 17 <= kCst, "T and X must fit inside Kg, Ki, Qg");
     static_assert(KP % 4 == 0 && kKi % 4 == 0 && kQg % 4 == 0 && kCst % 4 == 0 && DK % 4 == 0,
@@ -174,7 +176,10 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     float(*sX)[16][17] = reinterpret_cast<float(*)[16][17]>(smem + SM::kX);
     float* sg = smem + SM::kG;
     float* sb = smem + SM::kB;
+    float* snq = smem + SM::kNq;
+    float* snk = smem + SM::kNk;
     int* sflag = reinterpret_cast<int*>(smem + SM::kFlag);
+    const int qkn = a.qk_norm, blg = a.beta_logit;
 
     const size_t cs = (size_t)seq * a.NC + c;
     const int t0 = c * CH;
@@ -191,6 +196,33 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 
     // ---------------------------------------------------------------- gates
     if constexpr (!CGATE) {
+        // input preparation: 1/|q_r| and 1/|k_r|, four lanes per row
+        if (qkn) {
+            const int r = tid >> 2, qd = tid & 3;
+            const int rc = r < Lc ? r : 0;
+            float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+            for (int i = 0; i < DK / 32; ++i) {
+                const int k0 = 8 * (qd + 4 * i);
+                float xk[8], xq[8];
+                cvt_raw8<F32IN>(ld_raw8<F32IN>(a.k, (tok0 + rc) * DK + k0), true, xk);
+                cvt_raw8<F32IN>(ld_raw8<F32IN>(a.q, (tok0 + rc) * DK + k0), true, xq);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    ssk += xk[j] * xk[j];
+                    ssq += xq[j] * xq[j];
+                }
+            }
+            ssk += __shfl_xor(ssk, 1);
+            ssq += __shfl_xor(ssq, 1);
+            ssk += __shfl_xor(ssk, 2);
+            ssq += __shfl_xor(ssq, 2);
+            if (qd == 0) {
+                snk[r] = inv_norm(ssk);
+                snq[r] = inv_norm(ssq);
+            }
+            lds_barrier();
+        }
         if (w == 0) {
             const int lc = l < Lc ? l : 0;   // masked rows load a valid row, then drop it
             float g = a.has_gate ? a.log_alpha[tok0 + lc] : 0.f;
@@ -202,25 +234,40 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             }
             sg[l] = g;
             if constexpr (!CBETA) {
-                const float bl = a.beta[tok0 + lc];
+                const float bl = strength(a.beta[tok0 + lc], blg);
                 sb[l] = l < Lc ? bl : 0.f;
             } else {
                 sb[l] = 0.f;
             }
             const float g63 = __shfl(g, 63);
-            a.wsG[cs * kGW + l] = expf(g);             // gamma_r = e^{G_r}
-            a.wsG[cs * kGW + 64 + l] = expf(g63 - g);  // lambda_r = e^{G_63 - G_r}
+            const float gam = expf(g), lam = expf(g63 - g);
+            a.wsG[cs * kGW + l] = gam;   // gamma_r = e^{G_r}
+            if (!qkn) {
+                a.wsG[cs * kGW + 64 + l] = lam;   // lambda_r = e^{G_63 - G_r}
+            } else {
+                // the raw key rows are scan operands without a channel beta;
+                // with one, the workspace keys are normalised here.  The
+                // fp32 scan reads raw query rows either way.
+                const float nk = CBETA ? 1.f : snk[l];
+                a.wsG[cs * kGW + 64 + l] = lam * nk;
+                a.wsG[cs * kGW + 128 + l] = gam * nk;
+                a.wsG[cs * kGW + 192 + l] = gam * snq[l];
+            }
         }
         // channel beta with a scalar gate: the scan needs kt, vt (and q) in fp16
         if constexpr (CBETA) {
             for (int e = tid; e < CH * DK; e += 256) {
                 const int r = e / DK, col = e % DK;
                 const int rc = r < Lc ? r : 0;
-                const float sbv = sqrtf(a.beta[(tok0 + rc) * DK + col]);
-                const float sbw = sqrtf(a.beta_v[(tok0 + rc) * DK + col]);
+                const float sbv = sqrtf(strength(a.beta[(tok0 + rc) * DK + col], blg));
+                const float sbw = sqrtf(strength(a.beta_v[(tok0 + rc) * DK + col], blg));
                 float kv = sbv * load1<F32IN>(a.k, (tok0 + rc) * DK + col);
                 float vv = sbw * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
                 float qv = load1<F32IN>(a.q, (tok0 + rc) * DK + col);
+                if (qkn) {
+                    kv *= snk[r];
+                    qv *= snq[r];
+                }
                 kv = r < Lc ? kv : 0.f;
                 vv = r < Lc ? vv : 0.f;
                 qv = r < Lc ? qv : 0.f;
@@ -332,13 +379,38 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             float kx[CPT], qx[CPT], vx[CPT];
             cvt_rawn<F32IN, CPT>(in.k[u], kx);
             cvt_rawn<F32IN, CPT>(in.q[u], qx);
+            if (qkn) {
+                // input preparation: the token's squared norms over the
+                // DK / 4 lanes that hold its channels, then unit vectors
+                float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    ssk += kx[cc] * kx[cc];
+                    ssq += qx[cc] * qx[cc];
+                }
+#pragma unroll
+                for (int off = 1; off < DK / 4; off <<= 1) {
+                    ssk += __shfl_xor(ssk, off);
+                    ssq += __shfl_xor(ssq, off);
+                }
+                const float nk = inv_norm(ssk), nq = inv_norm(ssq);
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) {
+                    kx[cc] *= nk;
+                    qx[cc] *= nq;
+                }
+                if (cg == 0) {   // for the exact path of the diagonal blocks
+                    snk[r] = nk;
+                    snq[r] = nq;
+                }
+            }
             if constexpr (SEPV) cvt_rawn<F32IN, CPT>(vin[u], vx);
             else if constexpr (CBETA) cvt_rawn<F32IN, CPT>(in.v[u], vx);
             float okg[CPT], oki[CPT], oqg[CPT], wq[CPT], wks[CPT], wkl[CPT], wv[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                const float sbv = CBETA ? sqrtf(in.be[u][c]) : 1.f;
-                const float sbw = SEPV ? sqrtf(bwv[u][c]) : sbv;
+                const float sbv = CBETA ? sqrtf(strength(in.be[u][c], blg)) : 1.f;
+                const float sbw = SEPV ? sqrtf(strength(bwv[u][c], blg)) : sbv;
                 const float kt = live ? sbv * kx[c] : 0.f;
                 const float qv = live ? qx[c] : 0.f;
                 const float g2 = G[u][c] * kL2E;
@@ -391,7 +463,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             if (badbits) atomicOr(&sflag[0], badbits);
         }
         if constexpr (!CBETA) {
-            if (w == 3) sb[l] = l < Lc ? in.bs : 0.f;
+            if (w == 3) sb[l] = l < Lc ? strength(in.bs, blg) : 0.f;
         }
         if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, 0>(a, in, next_job, tid);
     }
@@ -423,7 +495,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                     float ba[8];
                     load_f32_n<8>(a.beta + (tok0 + rac) * DK + k0, ba);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) xk[j] *= sqrtf(ba[j]);
+                    for (int j = 0; j < 8; ++j) xk[j] *= sqrtf(strength(ba[j], blg));
                 }
             } else {
                 ld8_lds(smem + SM::kKg + ra * SM::KP + k0, xk);
@@ -448,7 +520,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                             float bb[8];
                             load_f32_n<8>(a.beta + (tok0 + cac) * DK + k0, bb);
 #pragma unroll
-                            for (int j = 0; j < 8; ++j) xb[j] *= sqrtf(bb[j]);
+                            for (int j = 0; j < 8; ++j) xb[j] *= sqrtf(strength(bb[j], blg));
                         }
                     } else {
                         const float* cst = smem + SM::kCst;
@@ -501,9 +573,17 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                     const int i = 16 * I + (l & 15);
                     float dec = 1.f;
                     if constexpr (!CGATE) dec = (i <= r) ? expf(sg[r] - sg[i]) : 0.f;
-                    sP[r][i] = (i <= r) ? cP[j] * dec : 0.f;
+                    float vp = cP[j] * dec;
                     float va = cA[j] * dec;
                     if constexpr (!CBETA) va *= sb[r];
+                    if constexpr (!CGATE) {
+                        // raw rows here: the normalisation as row and column factors
+                        if (qkn) {
+                            va *= snk[r] * snk[i];
+                            vp *= snq[r] * snk[i];
+                        }
+                    }
+                    sP[r][i] = (i <= r) ? vp : 0.f;
                     sA[r][i] = (i < r) ? va : 0.f;
                 }
             }
@@ -544,8 +624,8 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                         float kr = load1<F32IN>(a.k, (tok0 + r) * DK + col);
                         float ki = load1<F32IN>(a.k, (tok0 + i) * DK + col);
                         if constexpr (CBETA) {
-                            kr *= sqrtf(a.beta[(tok0 + r) * DK + col]);
-                            ki *= sqrtf(a.beta[(tok0 + i) * DK + col]);
+                            kr *= sqrtf(strength(a.beta[(tok0 + r) * DK + col], blg));
+                            ki *= sqrtf(strength(a.beta[(tok0 + i) * DK + col], blg));
                         }
                         const float qr = load1<F32IN>(a.q, (tok0 + r) * DK + col);
                         accA += kr * ki * dec;
@@ -553,6 +633,10 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                     }
                 }
                 if constexpr (!CBETA) accA *= sb[r];
+                if (qkn) {
+                    accA *= snk[r] * snk[i];
+                    accP *= snq[r] * snk[i];
+                }
                 sA[r][i] = (i < r) ? accA : 0.f;
                 sP[r][i] = (i <= r) ? accP : 0.f;
             }
@@ -710,7 +794,7 @@ struct ScanRegs {
     Frag<P> th[2], pm[2];                     // rows 16w.. of T^ and P
     VT vr[4];                                 // V tile (raw input), accumulator layout
     half_t vh[4][P];                          // V tile from the workspace (channel beta)
-    float gam[4], lam[4];                     // scalar-gate row factors
+    float gam[4], gamq[4], lam[4];            // scalar-gate row factors (key rows, query rows, U)
     float g63[DK / 64 * 4];                   // state decay of this lane's S rows
     Raw8<F32IN> ktr[DK / 32];                 // Kl slice: token tid & 63, DK/4 channels (raw)
     half8 kth[DK / 32][P];                    // the same from the workspace
@@ -756,7 +840,11 @@ __device__ __forceinline__ void scan_fetch(const ChunkArgs& a, ScanRegs<DK, F32I
             g.vr[j] = static_cast<const typename ScanRegs<DK, F32IN>::VT*>(a.v)[(tok0 + rc) * a.Dv + col];
         }
         if constexpr (!CGATE) {
-            g.gam[j] = a.wsG[cs * kGW + r];
+            // with normalised q and k: gamma/|k| for the key rows (gamma
+            // itself when the workspace keys are already normalised), gamma/|q|
+            // for the raw query rows
+            g.gam[j] = a.wsG[cs * kGW + (a.qk_norm ? 128 : 0) + r];
+            g.gamq[j] = a.wsG[cs * kGW + (a.qk_norm ? 192 : 0) + r];
             g.lam[j] = a.wsG[cs * kGW + 64 + r];
         }
     }
@@ -889,7 +977,7 @@ __device__ __forceinline__ void scan_chunk(const ChunkArgs& a, const ScanRegs<DK
     // step 4: O = gamma Y + P U
     f32x4 O;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) O[j] = (CGATE ? 1.f : cur.gam[j]) * Y[j];
+    for (int j = 0; j < 4; ++j) O[j] = (CGATE ? 1.f : cur.gamq[j]) * Y[j];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int k0 = 32 * s + 8 * (l >> 4);

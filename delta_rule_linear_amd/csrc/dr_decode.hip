@@ -1,5 +1,9 @@
 // dr_decode.hip -- one recurrent decode step for a batch of independent states.
 //
+// Optional input preparation (DeltaNet page, step list, step 2 and its notes on
+// the key/query map and on choosing beta): q and k made unit vectors, beta
+// (and beta_v) given as logits.
+//
 // Per state S (d_k x d_v, fp32) and one new token (FG2-GDN page, section 2,
 // the state-update equation; DeltaNet page, step list, steps 3-6; with a
 // separate write strength, vt = sqrt(beta_v) v, section "Erweiterung:
@@ -31,7 +35,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     __shared__ float sa[DK];       // alpha per row
     __shared__ float red[2][16][64];
     __shared__ float su[64];
-    __shared__ float sdot[4];
+    __shared__ float sdot[3][4];
 
     const int nslab = (a.Dv + 63) / 64;
     const int sidx = blockIdx.x / nslab;       // state index n * H + h
@@ -41,37 +45,63 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int col0 = slab * 64 + 4 * cg;
     const bool colok = col0 < a.Dv;            // Dv is a multiple of 16, so 4 columns at once
 
-    // token vectors: kt = sqrt(beta) k, alpha, q;  q . kt
-    float dotp = 0.f;
+    float4 s[RPT];
+    float* S = a.S + (size_t)sidx * DK * a.Dv;
+    if (colok) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            s[i] = *reinterpret_cast<const float4*>(S + (size_t)(rg + 16 * i) * a.Dv + col0);
+    }
+
+    // token vectors: kt = sqrt(beta) k, alpha, q;  q . kt.  With the input
+    // preparation, q and k are first made unit vectors: the three sums q . kt,
+    // |q|^2 and |k|^2 are reduced together, then the vectors are rescaled.
+    float dotp = 0.f, ssq = 0.f, ssk = 0.f, kt = 0.f, qv = 0.f;
     if (tid < DK) {
         const int c = tid;
         const size_t ti = (size_t)sidx * DK + c;
         const float kv = load1<F32IN>(a.k, ti);
-        const float qv = load1<F32IN>(a.q, ti);
-        const float bv = CBETA ? a.beta[ti] : a.beta[sidx];
-        const float kt = sqrtf(bv) * kv;
+        qv = load1<F32IN>(a.q, ti);
+        const float bv = strength(CBETA ? a.beta[ti] : a.beta[sidx], a.beta_logit);
+        kt = sqrtf(bv) * kv;
         float al = 1.f;
         if (a.has_gate) al = expf(CGATE ? a.log_alpha[ti] : a.log_alpha[sidx]);
-        sk[c] = kt;
-        sq[c] = qv;
         sa[c] = al;
         dotp = qv * kt;
+        ssq = qv * qv;
+        ssk = kv * kv;
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dotp += __shfl_xor(dotp, off);
-    if ((tid & 63) == 0) sdot[tid >> 6] = dotp;
+    for (int off = 32; off > 0; off >>= 1) {
+        dotp += __shfl_xor(dotp, off);
+        ssq += __shfl_xor(ssq, off);
+        ssk += __shfl_xor(ssk, off);
+    }
+    if ((tid & 63) == 0) {
+        sdot[0][tid >> 6] = dotp;
+        sdot[1][tid >> 6] = ssq;
+        sdot[2][tid >> 6] = ssk;
+    }
     __syncthreads();
-    const float qk = sdot[0] + sdot[1] + sdot[2] + sdot[3];
+    float rq = 1.f, rk = 1.f;
+    if (a.qk_norm) {
+        rq = inv_norm(sdot[1][0] + sdot[1][1] + sdot[1][2] + sdot[1][3]);
+        rk = inv_norm(sdot[2][0] + sdot[2][1] + sdot[2][2] + sdot[2][3]);
+    }
+    const float qk = (sdot[0][0] + sdot[0][1] + sdot[0][2] + sdot[0][3]) * (rq * rk);
+    if (tid < DK) {
+        sk[tid] = kt * rk;
+        sq[tid] = qv * rq;
+    }
+    __syncthreads();
 
-    // read this thread's slice of S once
-    float4 s[RPT];
-    float* S = a.S + (size_t)sidx * DK * a.Dv;
+    // this thread's slice of S, read once (issued above, before the token
+    // vectors' barriers)
     float pp[4] = {0.f, 0.f, 0.f, 0.f}, pr[4] = {0.f, 0.f, 0.f, 0.f};
     if (colok) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int c = rg + 16 * i;
-            s[i] = *reinterpret_cast<const float4*>(S + (size_t)c * a.Dv + col0);
             const float ka = sa[c] * sk[c], qa = sa[c] * sq[c];
             pp[0] += ka * s[i].x; pp[1] += ka * s[i].y; pp[2] += ka * s[i].z; pp[3] += ka * s[i].w;
             pr[0] += qa * s[i].x; pr[1] += qa * s[i].y; pr[2] += qa * s[i].z; pr[3] += qa * s[i].w;
@@ -96,7 +126,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float u = 0.f;
         if (col < a.Dv) {
             const size_t vi = (size_t)sidx * a.Dv + col;
-            const float bv = CBETA ? a.beta_v[(size_t)sidx * DK + col] : a.beta_v[sidx];
+            const float bv = strength(CBETA ? a.beta_v[(size_t)sidx * DK + col] : a.beta_v[sidx],
+                                      a.beta_logit);
             const float vt = sqrtf(bv) * load1<F32IN>(a.v, vi);
             u = vt - p;
             const float o = r + qk * u;

@@ -258,6 +258,16 @@ __device__ __forceinline__ float load1(const void* base, size_t off) {
     else return bf16_to_f32(static_cast<const uint16_t*>(base)[off]);
 }
 
+// A strength as given, or the sigmoid of the given logit (input preparation).
+__device__ __forceinline__ float strength(float x, int logit) {
+    return logit ? 1.f / (1.f + expf(-x)) : x;
+}
+
+// 1 / |x|_2 from a sum of squares, 0 for the zero vector.
+__device__ __forceinline__ float inv_norm(float ssq) {
+    return ssq > 0.f ? 1.f / sqrtf(ssq) : 0.f;
+}
+
 // Store one fp32 value as P fp16 terms: base[off + idx] (hi) and
 // base[off + plane + idx] (lo).
 template <int P>

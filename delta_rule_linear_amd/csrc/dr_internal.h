@@ -9,9 +9,13 @@
 
 namespace dr {
 
-// floats of per-chunk gate data in the workspace (scalar gate: gamma[64] and
-// lambda[64]; channel gate: the chunk's state decay e^{G_63}[Dk])
-constexpr int kGW = 128;
+// floats of per-chunk gate data in the workspace.  Channel gate: the chunk's
+// state decay e^{G_63}[Dk].  Scalar gate: gamma_r = e^{G_r} at [0, 64) and
+// lambda_r = e^{G_63 - G_r} at [64, 128); when q and k are normalised inside
+// the kernels and the raw inputs are the scan's operands (scalar gate and
+// beta), lambda_r is stored times 1/|k_r|, and [128, 192) holds gamma_r/|k_r|
+// (the key reads) and [192, 256) gamma_r/|q_r| (the query reads).
+constexpr int kGW = 256;
 
 // Packed lower-triangular form of the 64 x 64 per-chunk matrices T^ and P for
 // bf16 inputs: the ten 16 x 16 blocks (R, I), R >= I, in the order
@@ -38,6 +42,9 @@ __host__ __device__ constexpr int tri_off(int r, int c) {
 //   wsV       [NCH][P][64][Dk]   sqrt(beta_v) v (channel beta)
 // beta_v is the write strength that scales v; it is beta itself unless the
 // caller gives a separate one (channel beta only).
+// Input preparation: qk_norm makes every q_t and k_t a unit vector (the zero
+// vector stays zero), beta_logit reads beta (and beta_v) as logits,
+// beta = 1 / (1 + e^{-x}).
 struct ChunkArgs {
     const void* q;
     const void* k;
@@ -51,6 +58,8 @@ struct ChunkArgs {
     int B, H, L, Dv, NC, nseq;
     int has_gate;
     int out_bf16;
+    int qk_norm;
+    int beta_logit;
     half_t* wsT;
     half_t* wsP;
     float* wsG;
@@ -72,6 +81,8 @@ struct DecodeArgs {
     int N, H, Dv;
     int has_gate;
     int out_bf16;
+    int qk_norm;      // input preparation, as in ChunkArgs
+    int beta_logit;
 };
 
 // Optional per-kernel timing: launchers mark the start of each kernel and the

@@ -11,6 +11,14 @@
 // Rows past the sequence end are masked out of A and P, so their T^ rows are
 // zero and the scan's U vanishes there.
 //
+// With the input preparation (q and k made unit vectors, DeltaNet page, step
+// list, step 2), the raw bf16 tiles stay the matrix-core operands and the
+// normalisation becomes row and column factors: A_ri gains 1/(|k_r| |k_i|),
+// P_ri gains 1/(|q_r| |k_i|), and the workspace G record adds gamma_r/|k_r|
+// and gamma_r/|q_r| and stores lambda_r/|k_r|, which the scan applies to the
+// rows of K S, Q S and U.  beta given as logits is passed through a sigmoid
+// where it is loaded.
+//
 // Data path: the chunk's k and q tiles are copied once into LDS (coalesced
 // 16-byte global->LDS loads, XOR-swizzled rows).  k.k and q.k products are
 // exact on bf16 matrix cores (bf16 x bf16 products are exact in fp32).  The
@@ -83,12 +91,12 @@ struct P16 {
     static constexpr int QT = KT + 64 * RB;
     static constexpr int AP = 65;                 // fp32 pitch of A and T
     static constexpr int SA = QT + 64 * RB;
-    static constexpr int SG = SA + 64 * AP * 4;   // G[64], beta[64]
+    static constexpr int SG = SA + 64 * AP * 4;   // G[64], beta[64], 1/|q|[64], 1/|k|[64]
     static constexpr int TX = 64 * AP * 4 + 4 * 16 * 17 * 4;   // T and the scratch
     static constexpr bool ALIAS = TX <= 2 * 64 * RB;            // they fit in the tiles
-    static constexpr int ST = ALIAS ? KT : SG + 128 * 4;
+    static constexpr int ST = ALIAS ? KT : SG + 256 * 4;
     static constexpr int SX = ST + 64 * AP * 4;   // [4][16][17] fp32
-    static constexpr int TOTAL = ALIAS ? SG + 128 * 4 : SX + 4 * 16 * 17 * 4;
+    static constexpr int TOTAL = ALIAS ? SG + 256 * 4 : SX + 4 * 16 * 17 * 4;
 };
 
 template <int DK>
@@ -99,6 +107,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
     float(*sT)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::ST);
     float* sg = reinterpret_cast<float*>(smem + L::SG);
     float* sb = sg + 64;
+    float* snq = sg + 128;   // 1 / |q_r| (input preparation)
+    float* snk = sg + 192;   // 1 / |k_r|
     float(*sX)[16][17] = reinterpret_cast<float(*)[16][17]>(smem + L::SX);
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -121,29 +131,68 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             const float y = __shfl_up(gl, off);
             if (l >= off) gl += y;
         }
-        const float bl = a.beta[tok0 + lc];
+        const float bl = strength(a.beta[tok0 + lc], a.beta_logit);
         sg[l] = gl;
         sb[l] = l < Lc ? bl : 0.f;
         const float g63 = __shfl(gl, 63);
-        a.wsG[cs * kGW + l] = expf(gl);             // gamma_r
-        a.wsG[cs * kGW + 64 + l] = expf(g63 - gl);  // lambda_r
+        a.wsG[cs * kGW + l] = expf(gl);                                // gamma_r
+        if (!a.qk_norm) a.wsG[cs * kGW + 64 + l] = expf(g63 - gl);    // lambda_r
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies landed
     __syncthreads();
 
+    // input preparation: 1/|q_r| and 1/|k_r| from the tiles (four lanes per
+    // row, each summing a quarter of the row), and the scaled gate factors
+    if (a.qk_norm) {
+        const int r = tid >> 2, qd = tid & 3;
+        float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+        for (int pc = qd; pc < L::RB / 16; pc += 4) {
+            const uint4 kv = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::KT, r, pc));
+            const uint4 qv = *reinterpret_cast<const uint4*>(tile_at<L::RB>(smem + L::QT, r, pc));
+            const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, qw[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float k0 = bf16_to_f32((uint16_t)kw[e]), k1 = bf16_to_f32((uint16_t)(kw[e] >> 16));
+                const float q0 = bf16_to_f32((uint16_t)qw[e]), q1 = bf16_to_f32((uint16_t)(qw[e] >> 16));
+                ssk += k0 * k0 + k1 * k1;
+                ssq += q0 * q0 + q1 * q1;
+            }
+        }
+        ssk += __shfl_xor(ssk, 1);
+        ssq += __shfl_xor(ssq, 1);
+        ssk += __shfl_xor(ssk, 2);
+        ssq += __shfl_xor(ssq, 2);
+        if (qd == 0) {
+            snk[r] = inv_norm(ssk);
+            snq[r] = inv_norm(ssq);
+        }
+        __syncthreads();
+        if (w == 0) {
+            const float gam = expf(sg[l]), nk = snk[l];
+            a.wsG[cs * kGW + 64 + l] = expf(sg[63] - sg[l]) * nk;   // lambda_r / |k_r|
+            a.wsG[cs * kGW + 128 + l] = gam * nk;                   // gamma_r / |k_r|
+            a.wsG[cs * kGW + 192 + l] = gam * snq[l];               // gamma_r / |q_r|
+        }
+    }
+
     // gate values this lane needs, in registers (log2 units): rows
     // 16 R + 4 g + j of every block row R, column 16 I + i16 of every block
-    // column I; beta of the rows
+    // column I; beta of the rows (times 1/|k_r| with the input preparation),
+    // 1/|q_r| of the rows and 1/|k_i| of the column (1 without it)
     constexpr float kLog2e = 1.4426950408889634f;
-    float grow[4][4], brow[4][4], gcol[4];
+    float grow[4][4], brow[4][4], gcol[4], qrow[4][4], kcol[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            grow[R][j] = sg[16 * R + 4 * g + j] * kLog2e;
-            brow[R][j] = sb[16 * R + 4 * g + j];
+            const int r = 16 * R + 4 * g + j;
+            grow[R][j] = sg[r] * kLog2e;
+            brow[R][j] = a.qk_norm ? sb[r] * snk[r] : sb[r];
+            qrow[R][j] = a.qk_norm ? snq[r] : 1.f;
         }
         gcol[R] = sg[16 * R + i16] * kLog2e;
+        kcol[R] = a.qk_norm ? snk[16 * R + i16] : 1.f;
     }
 
     // A and P, 16 x 16 block pairs (R, I), R >= I, on the bf16 matrix cores.
@@ -176,16 +225,19 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             if (t < NI) {
                 const int I = I0 + t;
                 const float gi = I == 0 ? gcol[0] : I == 1 ? gcol[1] : I == 2 ? gcol[2] : gcol[3];
+                const float ki = I == 0 ? kcol[0] : I == 1 ? kcol[1] : I == 2 ? kcol[2] : kcol[3];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
                     const float gr = R == 0 ? grow[0][j] : R == 1 ? grow[1][j] : R == 2 ? grow[2][j] : grow[3][j];
                     const float br = R == 0 ? brow[0][j] : R == 1 ? brow[1][j] : R == 2 ? brow[2][j] : brow[3][j];
+                    const float qr = R == 0 ? qrow[0][j] : R == 1 ? qrow[1][j] : R == 2 ? qrow[2][j] : qrow[3][j];
                     const float f = __builtin_amdgcn_exp2f(gr - gi);   // e^{G_r - G_i} <= 1
                     const bool live = r < Lc;
-                    sA[r][i] = (live && i < r) ? accA[t][j] * f * br : 0.f;
+                    sA[r][i] = (live && i < r) ? accA[t][j] * f * br * ki : 0.f;
                     // P to the workspace, packed: 16 lanes write one 32-byte block row
-                    a.wsP[cs * (size_t)(CH * CH) + tri_off(r, i)] = (half_t)((live && i <= r) ? accP[t][j] * f : 0.f);
+                    a.wsP[cs * (size_t)(CH * CH) + tri_off(r, i)] =
+                        (half_t)((live && i <= r) ? accP[t][j] * f * qr * ki : 0.f);
                 }
             }
         }

@@ -244,6 +244,15 @@ struct SD {
     static constexpr int NCOPY = ((CGATE ? 2 : 1) + (QREG ? 0 : 1)) * (RB / 16) / NCW + 4;
 };
 
+// Lanes (16 bytes each) that copy a chunk's gate record into the 1 KiB gate
+// area; the other lanes repeat them.  Channel gate: the state decay [DK].
+// Scalar gate: gamma and lambda, and with normalised q and k on raw operands
+// (QN) also gamma/|k| and gamma/|q|.
+template <int DK, bool CGATE, bool QN>
+__host__ __device__ constexpr int gate_lanes() {
+    return CGATE ? DK / 4 : QN ? 64 : 32;
+}
+
 // Copy wave cw's quarter of a [64][RB]-byte tile of 16-bit values (row r at
 // src + r * pitch elements; rows >= valid read row 0) into swizzled LDS.
 template <int RB>
@@ -263,7 +272,7 @@ __device__ __forceinline__ void copy_tile(const uint16_t* src, size_t pitch, int
 
 // Part `PART` of the copies of chunk c into buffer `buf`, copy wave cw's share:
 //   0: Kl;  1: Q (channel gate);  2: Ks (channel gate), T^, P, the V tile, the gate factors.
-template <int DK, bool RAW, bool CGATE, bool CBETA, int PART>
+template <int DK, bool RAW, bool CGATE, bool CBETA, bool QN, int PART>
 __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq, int c, int n0, int l, int cw) {
     using L = SD<DK, RAW, CGATE>;
     const int t0 = c * CH;
@@ -303,7 +312,7 @@ __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq
                           buf + L::VT + hh * 1024);
                 }
             } else {
-                constexpr int NG = CGATE ? DK / 4 : 32;
+                constexpr int NG = gate_lanes<DK, CGATE, QN>();
                 dma16(a.wsG + cs * kGW + 4 * (l % NG), buf + L::GT);
             }
         }
@@ -325,7 +334,7 @@ __device__ __forceinline__ void s16_copy(const ChunkArgs& a, lchar* buf, int seq
 // it copies, computed once, so that every copy in the chunk loop is a scalar
 // base (per chunk) plus a fixed lane offset.  A partial last chunk, whose raw
 // rows must be clamped, goes through s16_copy instead.
-template <int DK, bool RAW, bool CGATE, bool CBETA>
+template <int DK, bool RAW, bool CGATE, bool CBETA, bool QN>
 struct Copier {
     using L = SD<DK, RAW, CGATE>;
     static constexpr int PPR = L::RB / 16;   // 16-byte pieces per tile row
@@ -357,7 +366,7 @@ struct Copier {
                 const int r = 32 * (k - 10) + (l >> 1), piece = l & 1;
                 o = (unsigned)(r * (CBETA ? DK : a.Dv) + n0 + 8 * piece) * 2u;
             } else {
-                constexpr int NG = CGATE ? DK / 4 : 32;
+                constexpr int NG = gate_lanes<DK, CGATE, QN>();
                 o = 16u * (l % NG);
             }
             soff[jj] = o;
@@ -390,7 +399,7 @@ struct Copier {
         region(a.wsP + cs0 * CH * CH, CH * CH * 2, kTriBytes / 128);
         if constexpr (CBETA) region(reinterpret_cast<const char*>(a.wsV) + cs0 * CH * DK * 2, CH * DK * 2, DK);
         else region(static_cast<const char*>(a.v) + seq0 * a.Dv * 2, CH * a.Dv * 2, a.Dv);
-        region(a.wsG + cs0 * kGW, kGW * 4, kGW * 4 / 128);
+        region(a.wsG + cs0 * kGW, kGW * 4, gate_lanes<DK, CGATE, QN>() * 16 / 128);
         wbase = b ? b : lastb;
         wstride = b ? st : lastst;
     }
@@ -403,7 +412,7 @@ struct Copier {
     __device__ __forceinline__ void copy(const ChunkArgs& a, lchar* buf, int seq, int cn, int n0, int l) const {
         constexpr bool RAWROWS = PART == 2 ? !CBETA : RAW;
         if (RAWROWS && tail(a, cn)) {
-            s16_copy<DK, RAW, CGATE, CBETA, PART>(a, buf, seq, cn, n0, l, cw);
+            s16_copy<DK, RAW, CGATE, CBETA, QN, PART>(a, buf, seq, cn, n0, l, cw);
             return;
         }
         const size_t tok0 = (size_t)seq * a.L + (size_t)cn * CH;
@@ -464,7 +473,10 @@ struct Copier {
     }
 };
 
-template <int DK, bool RAW, bool CGATE, bool CBETA>
+// QN: q and k are made unit vectors in the kernels while the raw inputs are
+// the operands (scalar gate and beta); the rows of K S take gamma/|k|, those
+// of Q S gamma/|q| (lambda/|k| is stored in lambda's place).
+template <int DK, bool RAW, bool CGATE, bool CBETA, bool QN = false>
 __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
     using L = SD<DK, RAW, CGATE>;
     constexpr int NB = L::NB;
@@ -512,7 +524,7 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
     // compute waves' own loads and stores then wait at issue.
     auto sync = [&]() { lds_barrier(); };
 
-    Copier<DK, RAW, CGATE, CBETA> cp;
+    Copier<DK, RAW, CGATE, CBETA, QN> cp;
     if (copier) cp.init(a, seq, n0, l, cw, tile, NT);
     // chunks that are whole (only those are touched ahead)
     const int NCF = a.L / CH;
@@ -565,7 +577,7 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
     auto chunk = [&](const int c, const lchar* buf, lchar* cbuf) {
         const int cn = min(c + NB - 1, a.NC - 1);
         auto gt = [&](int i) { return lds_ld<float>(buf + L::GT + 4 * i); };
-        f32x4 Y, gam, lam;
+        f32x4 Y, gam, lam, gamq;
         // A fragment of a packed triangle: row 16 w + i16, columns 32 s + 8 g
         // .. +7, i.e. block (w, 2 s + g / 2), half g & 1; zero above the
         // diagonal blocks.
@@ -613,8 +625,9 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * w + 4 * g + j;
                 vb[j] = lds_ld<uint16_t>(buf + L::VT + r * 32 + 2 * i16);
-                gam[j] = CGATE ? 1.f : gt(r);
+                gam[j] = CGATE ? 1.f : gt(QN ? 128 + r : r);
                 lam[j] = CGATE ? 1.f : gt(64 + r);
+                if constexpr (QN) gamq[j] = gt(192 + r);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -717,7 +730,7 @@ __global__ __launch_bounds__(512) void scan16_kernel(ChunkArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             f32x4 O;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) O[j] = gam[j] * Y[j];
+            for (int j = 0; j < 4; ++j) O[j] = (QN ? gamq[j] : gam[j]) * Y[j];
 #pragma unroll
             for (int s = 0; s < 2; ++s) O = mfma_raw<false>(pfr[s], uf[s], O);
             // to LDS; the copy waves store it to global memory during the
@@ -774,7 +787,9 @@ static hipError_t launch_s16(const ChunkArgs& a, hipStream_t st) {
     using L = SD<DK, RAW, CGATE>;
     static_assert(L::TOTAL <= 160 * 1024, "LDS plan exceeds 160 KiB");
     static_assert(L::NCOPY + 1 <= 63, "copies per chunk exceed the vector-memory counter");
-    auto kern = scan16_kernel<DK, RAW, CGATE, CBETA>;
+    static_assert(gate_lanes<DK, CGATE, RAW>() * 16 <= 1024, "gate record exceeds its LDS area");
+    auto kern = RAW && a.qk_norm ? scan16_kernel<DK, RAW, CGATE, CBETA, RAW>
+                                 : scan16_kernel<DK, RAW, CGATE, CBETA>;
     const int NT = a.Dv / 16;
     const int groups = (a.nseq + 7) / 8;
     hipLaunchKernelGGL(kern, dim3(groups * 8 * NT), dim3(512), 0, st, a);

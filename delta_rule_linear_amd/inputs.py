@@ -85,6 +85,8 @@ class ChunkProblem:
     S0: Optional[np.ndarray]
     meta: dict = field(default_factory=dict)
     beta_v: Optional[np.ndarray] = None   # separate write strength (FG2-GDN+), beta's shape
+    qk_l2norm: bool = False               # q, k raw: the forward normalises them
+    beta_logit: bool = False              # beta (and beta_v) hold logits
 
     @property
     def token_heads(self) -> int:
@@ -96,16 +98,21 @@ class ChunkProblem:
         return ChunkProblem(
             f"{self.name}[b={b},h={h}]", 1, 1, self.L, self.Dk, self.Dv, self.in_dtype,
             self.gate, self.beta_mode, sl(self.q), sl(self.k), sl(self.v),
-            sl(self.log_alpha), sl(self.beta), sl(self.S0), dict(self.meta), sl(self.beta_v))
+            sl(self.log_alpha), sl(self.beta), sl(self.S0), dict(self.meta), sl(self.beta_v),
+            self.qk_l2norm, self.beta_logit)
 
 
 def make_chunk_problem(B, H, L, Dk, Dv, *, in_dtype="bf16", gate="scalar", beta_mode="scalar",
                        log_alpha_range=(-0.1, -0.001), s0_var: Optional[float] = None,
-                       seed: int = 0, name: str = "custom", beta_v: bool = False) -> ChunkProblem:
+                       seed: int = 0, name: str = "custom", beta_v: bool = False,
+                       raw_inputs: bool = False) -> ChunkProblem:
     """Draw one chunked-forward batch following the module recipe.
 
     beta_v=True adds a separate write strength beta^v (FG2-GDN+), drawn like
     beta and after every other tensor, so the rest of the batch is unchanged.
+    raw_inputs=True keeps the same draws before their last step: q and k
+    are not normalised and the strengths are the logits, for a forward with
+    the input preparation switched on.
     """
     if gate not in GATES or beta_mode not in BETAS or in_dtype not in DTYPES:
         raise ValueError("unknown mode")
@@ -119,18 +126,23 @@ def make_chunk_problem(B, H, L, Dk, Dv, *, in_dtype="bf16", gate="scalar", beta_
     elif gate == "channel":
         la = rng.uniform(log_alpha_range[0], log_alpha_range[1], (B, H, L, Dk))
     bshape = (B, H, L) if beta_mode == "scalar" else (B, H, L, Dk)
-    beta = _sigmoid(rng.standard_normal(bshape))
+    beta_logits = rng.standard_normal(bshape)
+    beta = beta_logits if raw_inputs else _sigmoid(beta_logits)
     S0 = None
     if s0_var is not None:
         S0 = (rng.standard_normal((B, H, Dk, Dv)) * np.sqrt(s0_var)).astype(np.float32)
-    bv = _sigmoid(rng.standard_normal(bshape)).astype(np.float32) if beta_v else None
-    q = _to_dtype(_l2norm(q), in_dtype)
-    k = _to_dtype(_l2norm(k), in_dtype)
+    bv = rng.standard_normal(bshape) if beta_v else None
+    if not raw_inputs:
+        q, k = _l2norm(q), _l2norm(k)
+        bv = None if bv is None else _sigmoid(bv)
+    q = _to_dtype(q, in_dtype)
+    k = _to_dtype(k, in_dtype)
     v = _to_dtype(v, in_dtype)
     return ChunkProblem(name, B, H, L, Dk, Dv, in_dtype, gate, beta_mode, q, k, v,
                         None if la is None else la.astype(np.float32),
                         beta.astype(np.float32), S0,
-                        {"seed": seed, "log_alpha_range": log_alpha_range, "s0_var": s0_var}, bv)
+                        {"seed": seed, "log_alpha_range": log_alpha_range, "s0_var": s0_var},
+                        None if bv is None else bv.astype(np.float32), raw_inputs, raw_inputs)
 
 
 # The named workloads.  Gate ranges are U(lo, hi) on log alpha.
@@ -187,14 +199,18 @@ class DecodeProblem:
     log_alpha: Optional[np.ndarray]   # [steps, N, H] or [steps, N, H, Dk]
     beta: np.ndarray              # [steps, N, H] or [steps, N, H, Dk]
     beta_v: Optional[np.ndarray] = None   # separate write strength (FG2-GDN+), beta's shape
+    qk_l2norm: bool = False               # raw q, k and strength logits (see make_decode_problem)
+    beta_logit: bool = False
 
 
 def make_decode_problem(N=256, H=16, Dk=128, Dv=128, steps=512, *, in_dtype="bf16",
                         gate="scalar", beta_mode="scalar", log_alpha_range=GDN_GATE,
-                        s0_var=0.01, seed=0, beta_v: bool = False) -> DecodeProblem:
+                        s0_var=0.01, seed=0, beta_v: bool = False,
+                        raw_inputs: bool = False) -> DecodeProblem:
     """Decode batch: states first, then each step's tokens, in step order;
     with beta_v=True a separate write strength per step is drawn last, like
-    beta, so the other arrays are those of beta_v=False."""
+    beta, so the other arrays are those of beta_v=False.  raw_inputs=True
+    keeps q and k unnormalised and the strengths as their logits."""
     rng = np.random.default_rng(seed)
     S = (rng.standard_normal((N, H, Dk, Dv)) * np.sqrt(s0_var)).astype(np.float32)
     qs, ks, vs, las, bs = [], [], [], [], []
@@ -208,14 +224,16 @@ def make_decode_problem(N=256, H=16, Dk=128, Dv=128, steps=512, *, in_dtype="bf1
         elif gate == "channel":
             la = rng.uniform(log_alpha_range[0], log_alpha_range[1], (N, H, Dk))
         bl = rng.standard_normal((N, H) if beta_mode == "scalar" else (N, H, Dk))
-        qs.append(_to_dtype(_l2norm(q), in_dtype))
-        ks.append(_to_dtype(_l2norm(k), in_dtype))
+        qs.append(_to_dtype(q if raw_inputs else _l2norm(q), in_dtype))
+        ks.append(_to_dtype(k if raw_inputs else _l2norm(k), in_dtype))
         vs.append(_to_dtype(v, in_dtype))
         las.append(None if la is None else la.astype(np.float32))
-        bs.append(_sigmoid(bl).astype(np.float32))
+        bs.append((bl if raw_inputs else _sigmoid(bl)).astype(np.float32))
     bv = None
     if beta_v:
-        bv = _sigmoid(rng.standard_normal((steps,) + bs[0].shape)).astype(np.float32)
+        bv = rng.standard_normal((steps,) + bs[0].shape)
+        bv = (bv if raw_inputs else _sigmoid(bv)).astype(np.float32)
     return DecodeProblem(N, H, Dk, Dv, steps, in_dtype, gate, beta_mode, S,
                          np.stack(qs), np.stack(ks), np.stack(vs),
-                         None if gate == "none" else np.stack(las), np.stack(bs), bv)
+                         None if gate == "none" else np.stack(las), np.stack(bs), bv,
+                         raw_inputs, raw_inputs)

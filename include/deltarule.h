@@ -22,6 +22,22 @@
  *                   is the reading that reduces to FG2-GDN at beta^v == beta^k.
  * No query scaling is applied; callers pre-scale q if they want one.
  *
+ * Input preparation (optional, descriptor field input_flags), the steps in
+ * front of the recurrence, done inside the kernels so that the prepared
+ * tensors never pass through memory:
+ *   DR_IN_QK_L2NORM   q_t and k_t are replaced by q_t / |q_t|_2 and
+ *                     k_t / |k_t|_2 (per token and head, computed in fp32 from
+ *                     the input values; a zero vector stays zero) -- the
+ *                     L2 normalisation after the key/query feature map of the
+ *                     DeltaNet page, step list, step 2.  The learned parts of
+ *                     that map (a projection, SiLU, a short convolution) are
+ *                     the caller's.
+ *   DR_IN_BETA_LOGIT  the beta arrays (beta_k and beta_v too) hold logits x,
+ *                     and beta = 1 / (1 + e^{-x}) -- beta from a sigmoid
+ *                     projection (DeltaNet page, list of design choices).
+ * log_alpha is always taken as given: the pages fix no parametrisation of the
+ * gate.
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.  Every tensor pointer is a DEVICE pointer owned by the caller; the
@@ -56,7 +72,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 3
+#define DR_ABI_VERSION 4
 
 typedef enum {
     DR_OK = 0,
@@ -76,26 +92,32 @@ typedef enum { DR_GATE_NONE = 0, DR_GATE_SCALAR = 1, DR_GATE_CHANNEL = 2 } dr_ga
 /* beta_t: one scalar per token, or one per key channel (needs d_v == d_k). */
 typedef enum { DR_BETA_SCALAR = 0, DR_BETA_CHANNEL = 1 } dr_beta_mode;
 
+/* Input preparation flags (bitwise or; 0 = inputs used as given). */
+typedef enum { DR_IN_QK_L2NORM = 1, DR_IN_BETA_LOGIT = 2 } dr_input_flags;
+
 /* Shapes and modes of a chunked forward.
  *   B, H >= 0 sequences x heads; L >= 0 tokens; Dk in {64, 128};
  *   Dv a multiple of 16 in [16, 256] (Dv == Dk when beta == DR_BETA_CHANNEL).
- *   in_dtype types q, k, v; out_dtype types o. */
+ *   in_dtype types q, k, v; out_dtype types o.
+ *   input_flags: dr_input_flags bits (other bits: DR_ERR_UNSUPPORTED). */
 typedef struct {
     int B, H, L, Dk, Dv;
     dr_dtype in_dtype;
     dr_dtype out_dtype;
     dr_gate_mode gate;
     dr_beta_mode beta;
+    unsigned input_flags;
 } dr_chunk_desc;
 
 /* Shapes and modes of one recurrent decode step on N x H independent states
- * (same limits as dr_chunk_desc for Dk, Dv and the modes). */
+ * (same limits as dr_chunk_desc for Dk, Dv, the modes and input_flags). */
 typedef struct {
     int N, H, Dk, Dv;
     dr_dtype in_dtype;
     dr_dtype out_dtype;
     dr_gate_mode gate;
     dr_beta_mode beta;
+    unsigned input_flags;
 } dr_decode_desc;
 
 /* Bytes of device workspace dr_chunk_fwd needs for `d` (0 if d is invalid or
@@ -118,7 +140,7 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_chunk_desc* d);
  *   log_alpha  [B][H][L] (GATE_SCALAR) or [B][H][L][Dk] (GATE_CHANNEL) fp32,
  *              natural log of alpha_t; must be NULL iff gate == DR_GATE_NONE
  *   beta       [B][H][L] (BETA_SCALAR) or [B][H][L][Dk] (BETA_CHANNEL) fp32,
- *              expected in [0, 1] (not checked)
+ *              expected in [0, 1] (not checked), or logits (DR_IN_BETA_LOGIT)
  *   S0         [B][H][Dk][Dv] fp32 initial states, or NULL for zeros
  *   o          [B][H][L][Dv]  out_dtype, written
  *   S_final    [B][H][Dk][Dv] fp32, written, or NULL to skip; may alias S0

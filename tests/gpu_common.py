@@ -37,9 +37,13 @@ def to_dev(a, dtype: str, device="cuda"):
 
 
 def problem_to_dev(p):
-    return dict(q=to_dev(p.q, p.in_dtype), k=to_dev(p.k, p.in_dtype), v=to_dev(p.v, p.in_dtype),
-                log_alpha=to_dev(p.log_alpha, "f32"), beta=to_dev(p.beta, "f32"),
-                beta_v=to_dev(getattr(p, "beta_v", None), "f32"), S0=to_dev(p.S0, "f32"))
+    """The problem's tensors on the device, keyed as dr_chunk_fwd's arguments
+    (plus beta_v when the problem has a separate write strength)."""
+    t = dict(q=to_dev(p.q, p.in_dtype), k=to_dev(p.k, p.in_dtype), v=to_dev(p.v, p.in_dtype),
+             log_alpha=to_dev(p.log_alpha, "f32"), beta=to_dev(p.beta, "f32"), S0=to_dev(p.S0, "f32"))
+    if getattr(p, "beta_v", None) is not None:
+        t["beta_v"] = to_dev(p.beta_v, "f32")
+    return t
 
 
 def run_hip(p, out_dtype=None, **kw):
@@ -47,7 +51,9 @@ def run_hip(p, out_dtype=None, **kw):
     has a separate write strength); returns device tensors."""
     import delta_rule_linear_amd as drl
     t = problem_to_dev(p)
-    if t["beta_v"] is not None:
+    kw.setdefault("qk_l2norm", getattr(p, "qk_l2norm", False))
+    kw.setdefault("beta_logit", getattr(p, "beta_logit", False))
+    if "beta_v" in t:
         return drl.dr_chunk_fwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"],
                                    t["S0"], gate=p.gate, out_dtype=out_dtype, **kw)
     return drl.dr_chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"],

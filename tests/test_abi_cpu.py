@@ -41,10 +41,10 @@ def test_version_and_status_text():
 
 def _desc(**kw):
     base = dict(B=2, H=3, L=100, Dk=128, Dv=128, in_dtype=drl.DR_BF16, out_dtype=drl.DR_F32,
-                gate="scalar", beta_mode="scalar")
+                gate="scalar", beta_mode="scalar", flags=0)
     base.update(kw)
     return drl.chunk_desc(base["B"], base["H"], base["L"], base["Dk"], base["Dv"], base["in_dtype"],
-                          base["out_dtype"], base["gate"], base["beta_mode"])
+                          base["out_dtype"], base["gate"], base["beta_mode"], base["flags"])
 
 
 def _call(desc, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, o=FAKE, Sf=FAKE, ws=FAKE,
@@ -109,6 +109,20 @@ def test_chunk_workspace_checks():
     assert drl.dr_chunk_fwd_workspace_bytes(dch) > need
     assert drl.dr_chunk_fwd_workspace_bytes(_desc(L=0)) == 0
     assert drl.dr_chunk_fwd_workspace_bytes(_desc(B=0)) == 0
+
+
+def test_input_flags_validation():
+    d = _desc(flags=drl.DR_IN_QK_L2NORM | drl.DR_IN_BETA_LOGIT)
+    assert _call(d, ws=None) == drl.DR_ERR_WORKSPACE     # known flags pass validation
+    assert drl.dr_chunk_fwd_workspace_bytes(d) == drl.dr_chunk_fwd_workspace_bytes(_desc())
+    d = _desc(flags=4)
+    assert _call(d) == drl.DR_ERR_UNSUPPORTED
+    assert "input_flags" in drl.dr_last_error()
+    assert drl.dr_chunk_fwd_workspace_bytes(d) == 0
+    D = drl.DecodeDesc
+    ok = dict(N=4, H=2, Dk=128, Dv=128, in_dtype=drl.DR_BF16, out_dtype=drl.DR_F32, gate=1, beta=0)
+    assert _dcall(D(**{**ok, "input_flags": 8})) == drl.DR_ERR_UNSUPPORTED
+    assert _dcall(D(**{**ok, "input_flags": 3}), S=None) == drl.DR_ERR_NULL
 
 
 def test_chunk_rejects_partial_state_overlap():

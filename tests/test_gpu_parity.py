@@ -140,6 +140,59 @@ def test_kv_equal_strengths_match_single_strength_bits():
         assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
+# ------------------------------------------- input preparation in the kernels
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,beta_mode", MODES)
+@pytest.mark.parametrize("L", [65, 200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_input_prep_sweep(dtype, gate, beta_mode, L, D):
+    # raw q, k (norms near sqrt(D)) and strength logits; the kernels normalise
+    # and apply the sigmoid
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    p = inputs.make_chunk_problem(1, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
+                                  log_alpha_range=rng, s0_var=0.01, seed=L + D + 2, raw_inputs=True,
+                                  name=f"prep-{dtype}-{gate}-{beta_mode}-L{L}-D{D}")
+    _check(p, tol=1e-5 if dtype == "f32" else None)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_input_prep_separate_strengths(gate):
+    p = inputs.make_chunk_problem(1, 3, 200, 128, 128, gate=gate, beta_mode="channel",
+                                  log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=13, beta_v=True,
+                                  raw_inputs=True, name=f"prep-kv-{gate}")
+    _check(p)
+
+
+@pytest.mark.parametrize("gate,beta_mode", MODES)
+def test_input_prep_zero_vectors(gate, beta_mode):
+    # a zero key writes and erases nothing, a zero query reads nothing
+    p = inputs.make_chunk_problem(1, 2, 130, 128, 128, gate=gate, beta_mode=beta_mode,
+                                  log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=14,
+                                  raw_inputs=True, name=f"prep-zero-{gate}-{beta_mode}")
+    p.k[:, :, [5, 64, 129]] = 0
+    p.q[:, :, [7, 63, 100]] = 0
+    _check(p)
+    o, _ = run_hip(p)
+    assert torch.isfinite(o).all().item()
+    assert to_np(o[:, :, [7, 63, 100]]).max() == 0.0
+
+
+def test_input_prep_full_headline_sampled():
+    # the headline batch drawn raw: the normalisation and the sigmoid in the kernels
+    p = inputs.workload("gdn_b2h16_16k", raw_inputs=True)
+    announce("full raw", p.name)
+    o, S = run_hip(p)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item() and torch.isfinite(S).all().item()
+    for b, h in [(0, 0), (1, 15)]:
+        oy, Sy = run_oracle(p.head(b, h))
+        eo = rel_err(to_np(o[b, h]), oy[0, 0])
+        es = rel_err(to_np(S[b, h]), Sy[0, 0])
+        print(f"raw headline head ({b},{h}): o {eo:.2e}  S {es:.2e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------- full sizes
 
 FULL = {
@@ -241,6 +294,36 @@ def test_decode_kv_steps(gate, dtype):
                                   to_dev(dp.beta_v[t], "f32"), gate=gate)
         oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], la, dp.beta[t], gate=gate,
                                     beta_mode="channel", beta_v=dp.beta_v[t])
+        assert rel_err(to_np(o), oy) <= 1e-5, f"step {t} o"
+    assert rel_err(to_np(S), Sy) <= 1e-5
+
+
+@pytest.mark.parametrize("gate,beta_mode", MODES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_input_prep(gate, beta_mode, dtype):
+    import delta_rule_linear_amd as drl
+    import oracle
+    from gpu_common import to_dev
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    sepv = beta_mode == "channel"
+    dp = inputs.make_decode_problem(5, 3, 128, 128, 4, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
+                                    log_alpha_range=rng, seed=15, beta_v=sepv, raw_inputs=True)
+    announce("decode prep", gate, beta_mode, dtype)
+    S = to_dev(dp.S, "f32")
+    Sy = dp.S.astype(np.float64)
+    for t in range(dp.steps):
+        la = None if dp.log_alpha is None else dp.log_alpha[t]
+        args = (S, to_dev(dp.q[t], dtype), to_dev(dp.k[t], dtype), to_dev(dp.v[t], dtype),
+                to_dev(la, "f32"), to_dev(dp.beta[t], "f32"))
+        if sepv:
+            o = drl.dr_decode_step_kv(*args, to_dev(dp.beta_v[t], "f32"), gate=gate, qk_l2norm=True,
+                                      beta_logit=True)
+        else:
+            o = drl.dr_decode_step(*args, gate=gate, beta_mode=beta_mode, qk_l2norm=True,
+                                   beta_logit=True)
+        oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], la, dp.beta[t], gate=gate,
+                                    beta_mode=beta_mode, beta_v=None if not sepv else dp.beta_v[t],
+                                    qk_l2norm=True, beta_logit=True)
         assert rel_err(to_np(o), oy) <= 1e-5, f"step {t} o"
     assert rel_err(to_np(S), Sy) <= 1e-5
 
