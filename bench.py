@@ -258,27 +258,33 @@ def main():
     # ------------------------------------------------------------ other forward workloads
     configs = {}
     extra = [
-        ("fg2_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, False),
-        ("fg2plus_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, True),
-        ("kda_b2h32_16k", 2, 32, 16384, "channel", "scalar", (-0.2, -0.0005), False, False),
-        ("gdn_b4h16_4k", 4, 16, 4096, "scalar", "scalar", (-0.1, -0.001), True, False),
-        ("gdn_b1h16_64k", 1, 16, 65536, "scalar", "scalar", (-0.1, -0.001), True, False),
+        ("fg2_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, False, False),
+        ("fg2plus_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, True, False),
+        ("kda_b2h32_16k", 2, 32, 16384, "channel", "scalar", (-0.2, -0.0005), False, False, False),
+        ("gdn_b4h16_4k", 4, 16, 4096, "scalar", "scalar", (-0.1, -0.001), True, False, False),
+        ("gdn_b1h16_64k", 1, 16, 65536, "scalar", "scalar", (-0.1, -0.001), True, False, False),
+        # the headline shape with raw q, k and beta logits: the kernels normalise
+        # and apply the sigmoid
+        ("gdn_b2h16_16k_input_prep", 2, 16, 16384, "scalar", "scalar", (-0.1, -0.001), True, False, True),
     ]
-    for name, b_, h_, l_, gate, bmode, rng, s0, sepv in (extra if args.config_steps > 0 else []):
+    for name, b_, h_, l_, gate, bmode, rng, s0, sepv, prep in (extra if args.config_steps > 0 else []):
         gen.manual_seed(0)
-        xq = l2n(torch.randn((b_, h_, l_, D), generator=gen, device=dev)).bfloat16()
-        xk = l2n(torch.randn((b_, h_, l_, D), generator=gen, device=dev)).bfloat16()
+        xq = torch.randn((b_, h_, l_, D), generator=gen, device=dev)
+        xk = torch.randn((b_, h_, l_, D), generator=gen, device=dev)
+        xq, xk = (xq.bfloat16(), xk.bfloat16()) if prep else (l2n(xq).bfloat16(), l2n(xk).bfloat16())
         xv = torch.randn((b_, h_, l_, D), generator=gen, device=dev).bfloat16()
         gshape = (b_, h_, l_) if gate == "scalar" else (b_, h_, l_, D)
         xla = torch.rand(gshape, generator=gen, device=dev) * (rng[1] - rng[0]) + rng[0]
         bshape = (b_, h_, l_) if bmode == "scalar" else (b_, h_, l_, D)
-        xbe = torch.sigmoid(torch.randn(bshape, generator=gen, device=dev))
+        xbe = torch.randn(bshape, generator=gen, device=dev)
+        xbe = xbe if prep else torch.sigmoid(xbe)
         xS0 = torch.randn((b_, h_, D, D), generator=gen, device=dev) * 0.1 if s0 else None
         # separate write strength (FG2-GDN+), drawn like beta
         xbv = torch.sigmoid(torch.randn(bshape, generator=gen, device=dev)) if sepv else None
         xo = torch.empty((b_, h_, l_, D), dtype=torch.float32, device=dev)
         xSf = torch.empty((b_, h_, D, D), dtype=torch.float32, device=dev)
-        xdesc = drl.chunk_desc(b_, h_, l_, D, D, drl.DR_BF16, drl.DR_F32, gate, bmode)
+        xdesc = drl.chunk_desc(b_, h_, l_, D, D, drl.DR_BF16, drl.DR_F32, gate, bmode,
+                               drl.input_flags(prep, prep))
         xws = torch.empty(drl.dr_chunk_fwd_workspace_bytes(xdesc), dtype=torch.uint8, device=dev)
 
         def xstep():
@@ -287,17 +293,29 @@ def main():
                                     workspace=xws)
             else:
                 drl.dr_chunk_fwd(xq, xk, xv, xla, xbe, xS0, gate=gate, beta_mode=bmode, o=xo,
-                                 S_final=xSf, workspace=xws)
+                                 S_final=xSf, workspace=xws, qk_l2norm=prep, beta_logit=prep)
 
         drl.dr_profile_begin()
         xper = time_steps(xstep, args.config_steps, 2)
         xprof = drl.dr_profile_end()
         xms = float(np.median(xper))
         th = b_ * h_ * l_
+        unfused = None
+        if prep:
+            # for comparison: the same preparation as separate torch passes
+            # over HBM, then the forward on the prepared tensors
+            def ustep():
+                uq = l2n(xq.float()).bfloat16()
+                uk = l2n(xk.float()).bfloat16()
+                drl.dr_chunk_fwd(uq, uk, xv, xla, torch.sigmoid(xbe), xS0, gate=gate, beta_mode=bmode,
+                                 o=xo, S_final=xSf, workspace=xws)
+
+            unfused = round(float(np.median(time_steps(ustep, args.config_steps, 2))), 4)
         calls = max(1, xprof["chunk_calls"])
         configs[name] = {
             "shape": f"B={b_} H={h_} L={l_} d={D}, gate {gate}, beta {bmode}"
-                     + (", separate write strength" if sepv else ""),
+                     + (", separate write strength" if sepv else "")
+                     + (", q/k L2 normalisation and beta sigmoid in the kernels" if prep else ""),
             "ms_per_step": round(xms, 4), "tokens_per_s": round(b_ * l_ / (xms * 1e-3), 1),
             "prep_ms": round(xprof["prep_ms"] / calls, 4), "scan_ms": round(xprof["scan_ms"] / calls, 4),
             "mfma_frac": round(flops_per_token_head(D) * th / (xms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
@@ -305,6 +323,8 @@ def main():
                                                        (1 if bmode == "scalar" else D) * (2 if sepv else 1))
                               * th
                               / (xms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if unfused is not None:
+            configs[name]["ms_with_torch_preparation"] = unfused
         del xq, xk, xv, xla, xbe, xbv, xS0, xo, xSf, xws
     torch.cuda.empty_cache()
 

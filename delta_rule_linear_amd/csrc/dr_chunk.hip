@@ -164,7 +164,7 @@ __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBE
 // chunk's raw inputs arrive in `in`; once they are consumed, the inputs of
 // chunk `next_job` (>= 0) are loaded into it, so that those loads are in
 // flight during this chunk's matrix work.
-template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV, bool QKN>
 __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, const int seq, const int c,
                                            CgIn<DK, F32IN, CBETA, SEPV>& in, const int next_job) {
     constexpr int P = F32IN ? 2 : 1;
@@ -179,7 +179,10 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     float* snq = smem + SM::kNq;
     float* snk = smem + SM::kNk;
     int* sflag = reinterpret_cast<int*>(smem + SM::kFlag);
-    const int qkn = a.qk_norm, blg = a.beta_logit;
+    // the channel-gate preparation has no registers to spare: its input
+    // normalisation is a separate variant (QKN), the others test the flag
+    const bool qkn = CGATE ? QKN : a.qk_norm != 0;
+    const int blg = a.beta_logit;
 
     const size_t cs = (size_t)seq * a.NC + c;
     const int t0 = c * CH;
@@ -213,10 +216,8 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                     ssq += xq[j] * xq[j];
                 }
             }
-            ssk += __shfl_xor(ssk, 1);
-            ssq += __shfl_xor(ssq, 1);
-            ssk += __shfl_xor(ssk, 2);
-            ssq += __shfl_xor(ssq, 2);
+            ssk = group_sum<4>(ssk);
+            ssq = group_sum<4>(ssq);
             if (qd == 0) {
                 snk[r] = inv_norm(ssk);
                 snq[r] = inv_norm(ssq);
@@ -380,28 +381,21 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             cvt_rawn<F32IN, CPT>(in.k[u], kx);
             cvt_rawn<F32IN, CPT>(in.q[u], qx);
             if (qkn) {
-                // input preparation: the token's squared norms over the
-                // DK / 4 lanes that hold its channels, then unit vectors
+                // input preparation: the token's squared norms summed over
+                // the DK / 4 lanes that hold its channels (DPP moves), then
+                // unit vectors
                 float ssk = 0.f, ssq = 0.f;
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
                     ssk += kx[cc] * kx[cc];
                     ssq += qx[cc] * qx[cc];
                 }
-#pragma unroll
-                for (int off = 1; off < DK / 4; off <<= 1) {
-                    ssk += __shfl_xor(ssk, off);
-                    ssq += __shfl_xor(ssq, off);
-                }
-                const float nk = inv_norm(ssk), nq = inv_norm(ssq);
+                const float nk = inv_norm(group_sum<DK / 4>(ssk));
+                const float nq = inv_norm(group_sum<DK / 4>(ssq));
 #pragma unroll
                 for (int cc = 0; cc < CPT; ++cc) {
                     kx[cc] *= nk;
                     qx[cc] *= nq;
-                }
-                if (cg == 0) {   // for the exact path of the diagonal blocks
-                    snk[r] = nk;
-                    snq[r] = nq;
                 }
             }
             if constexpr (SEPV) cvt_rawn<F32IN, CPT>(vin[u], vx);
@@ -616,6 +610,9 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 if (tid >= 256) continue;
                 const int r = 16 * R + (tid >> 4), i = 16 * R + (tid & 15);
                 float accA = 0.f, accP = 0.f;
+                // squared norms of the raw rows, for the input preparation
+                // (summed here: this rare path keeps no factors of its own)
+                float ssr = 0.f, ssi = 0.f, ssq = 0.f;
                 if (i <= r && r < Lc) {
                     for (int col = 0; col < DK; ++col) {
                         float e = 0.f;
@@ -623,19 +620,23 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                         const float dec = expf(e);
                         float kr = load1<F32IN>(a.k, (tok0 + r) * DK + col);
                         float ki = load1<F32IN>(a.k, (tok0 + i) * DK + col);
+                        const float qr = load1<F32IN>(a.q, (tok0 + r) * DK + col);
+                        ssr += kr * kr;
+                        ssi += ki * ki;
+                        ssq += qr * qr;
                         if constexpr (CBETA) {
                             kr *= sqrtf(strength(a.beta[(tok0 + r) * DK + col], blg));
                             ki *= sqrtf(strength(a.beta[(tok0 + i) * DK + col], blg));
                         }
-                        const float qr = load1<F32IN>(a.q, (tok0 + r) * DK + col);
                         accA += kr * ki * dec;
                         accP += qr * ki * dec;
                     }
                 }
                 if constexpr (!CBETA) accA *= sb[r];
                 if (qkn) {
-                    accA *= snk[r] * snk[i];
-                    accP *= snq[r] * snk[i];
+                    const float ni = inv_norm(ssi);
+                    accA *= inv_norm(ssr) * ni;
+                    accP *= inv_norm(ssq) * ni;
                 }
                 sA[r][i] = (i < r) ? accA : 0.f;
                 sP[r][i] = (i <= r) ? accP : 0.f;
@@ -743,7 +744,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 // One workgroup per chunk, or, with a channel gate, a persistent loop over
 // chunks (job = chunk + NC * sequence) that loads the next chunk's inputs
 // while it works on the current one.
-template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false, bool QKN = false>
 __global__ __launch_bounds__((prep_threads<DK, CGATE>())) void prep_kernel(ChunkArgs a) {
     using SM = PrepSmem<DK, CGATE>;
     __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
@@ -757,11 +758,12 @@ __global__ __launch_bounds__((prep_threads<DK, CGATE>())) void prep_kernel(Chunk
         for (; job < njobs; job += gridDim.x) {
             if (!PREF) cg_fetch(a, in, job, threadIdx.x);
             const int nj = job + gridDim.x;
-            prep_chunk<DK, F32IN, CGATE, CBETA, SEPV>(a, smem, job / a.NC, job % a.NC, in,
-                                                      PREF && nj < njobs ? nj : -1);
+            prep_chunk<DK, F32IN, CGATE, CBETA, SEPV, QKN>(a, smem, job / a.NC, job % a.NC, in,
+                                                           PREF && nj < njobs ? nj : -1);
         }
     } else {
-        prep_chunk<DK, F32IN, CGATE, CBETA, SEPV>(a, smem, blockIdx.z * a.H + blockIdx.y, blockIdx.x, in, -1);
+        prep_chunk<DK, F32IN, CGATE, CBETA, SEPV, QKN>(a, smem, blockIdx.z * a.H + blockIdx.y, blockIdx.x, in,
+                                                       -1);
     }
 }
 
@@ -1106,7 +1108,7 @@ static long resident_groups(const void* kern, int threads) {
     return n;
 }
 
-template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false, bool QKN = false>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     const int nseq = a.nseq;
     if (a.NC > 0 && nseq > 0) {
@@ -1115,7 +1117,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
         if constexpr (!F32IN && !CGATE && !CBETA) {
             e = launch_prep16(a, DK, st);
         } else if constexpr (CGATE) {
-            auto kern = prep_kernel<DK, F32IN, CGATE, CBETA, SEPV>;
+            auto kern = prep_kernel<DK, F32IN, CGATE, CBETA, SEPV, QKN>;
             const long njobs = (long)nseq * a.NC;
             constexpr int NTH = prep_threads<DK, CGATE>();
             const long slots = resident_groups((const void*)kern, NTH);
@@ -1151,13 +1153,17 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
 // the scalar-gate preparation reads a.beta_v as it is; the channel-gate one
 // holds the next chunk's inputs in registers, so only the variant that needs
 // beta_v carries room for it.
+template <int DK, bool F32IN, bool QKN>
+static hipError_t launch_chunk_cg(const ChunkArgs& a, bool cbeta, bool sepv, hipStream_t st) {
+    if (!cbeta) return launch_chunk_t<DK, F32IN, true, false, false, QKN>(a, st);
+    return sepv ? launch_chunk_t<DK, F32IN, true, true, true, QKN>(a, st)
+                : launch_chunk_t<DK, F32IN, true, true, false, QKN>(a, st);
+}
+
 template <int DK, bool F32IN>
 static hipError_t launch_chunk_d(const ChunkArgs& a, bool cgate, bool cbeta, bool sepv, hipStream_t st) {
-    if (cgate) {
-        if (!cbeta) return launch_chunk_t<DK, F32IN, true, false>(a, st);
-        return sepv ? launch_chunk_t<DK, F32IN, true, true, true>(a, st)
-                    : launch_chunk_t<DK, F32IN, true, true>(a, st);
-    }
+    if (cgate) return a.qk_norm ? launch_chunk_cg<DK, F32IN, true>(a, cbeta, sepv, st)
+                                : launch_chunk_cg<DK, F32IN, false>(a, cbeta, sepv, st);
     return cbeta ? launch_chunk_t<DK, F32IN, false, true>(a, st)
                  : launch_chunk_t<DK, F32IN, false, false>(a, st);
 }

@@ -263,6 +263,32 @@ __device__ __forceinline__ float strength(float x, int logit) {
     return logit ? 1.f / (1.f + expf(-x)) : x;
 }
 
+// Sum of x over aligned groups of N <= 32 consecutive lanes, in every lane of
+// the group.  Within 16 lanes the butterfly runs on DPP moves (VALU speed, no
+// LDS round trip): quad permutations pair lanes at distance 1 and 2, the
+// half-row mirror pairs the two quads of 8 lanes, the row mirror the two
+// halves of 16; the step across 16 lanes is one ds_swizzle in bit-mask mode
+// (source lane (lane & 31) ^ 16).  No lane-address registers are held.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false);
+    return x + __builtin_bit_cast(float, y);
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N >= 1 && N <= 32 && (N & (N - 1)) == 0, "group of 1..32 lanes, a power of two");
+    if constexpr (N >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    if constexpr (N >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    if constexpr (N >= 8) x = dpp_add<0x141>(x);   // row_half_mirror
+    if constexpr (N >= 16) x = dpp_add<0x140>(x);  // row_mirror
+    if constexpr (N >= 32) {
+        const int y = __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F | (16 << 10));
+        x += __builtin_bit_cast(float, y);
+    }
+    return x;
+}
+
 // 1 / |x|_2 from a sum of squares, 0 for the zero vector.
 __device__ __forceinline__ float inv_norm(float ssq) {
     return ssq > 0.f ? 1.f / sqrtf(ssq) : 0.f;

@@ -159,10 +159,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
                 ssq += q0 * q0 + q1 * q1;
             }
         }
-        ssk += __shfl_xor(ssk, 1);
-        ssq += __shfl_xor(ssq, 1);
-        ssk += __shfl_xor(ssk, 2);
-        ssq += __shfl_xor(ssq, 2);
+        ssk = group_sum<4>(ssk);
+        ssq = group_sum<4>(ssq);
         if (qd == 0) {
             snk[r] = inv_norm(ssk);
             snq[r] = inv_norm(ssq);
