@@ -17,6 +17,10 @@ Optional input preparation in front of it (DeltaNet page, step list, step 2
 and its notes on the key/query map and on choosing beta): qk_l2norm replaces q
 and k by unit vectors (a zero vector stays zero); beta_logit takes the
 strength arrays as logits, beta = sigmoid(x).
+Write-side key scaling (OSDN page, "Method"; the preconditioned delta rule
+page, abstract): a diagonal preconditioner s_t on the gradient step, given as
+an input; the write key is w = s * kt:
+    S_t = (I - w kt^T) Diag(alpha_t) S_{t-1} + w vt^T.
 """
 from __future__ import annotations
 
@@ -59,7 +63,7 @@ def load(path: str = LIB_PATH):
                                                          ctypes.c_int, dp, dp, dp, ctypes.c_int]
     lib.dro_forward_kv.restype = ctypes.c_int
     lib.dro_forward_ex.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp, dp,
-                                                        ctypes.c_int, ctypes.c_int, dp, dp, dp,
+                                                        ctypes.c_int, dp, ctypes.c_int, dp, dp, dp,
                                                         ctypes.c_int]
     lib.dro_forward_ex.restype = ctypes.c_int
     lib.dro_max_threads.restype = ctypes.c_int
@@ -82,13 +86,14 @@ def _f64(a: Optional[np.ndarray]):
 
 def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
             nthreads: int = 0, lib=None, beta_v=None, qk_l2norm: bool = False,
-            beta_logit: bool = False):
+            beta_logit: bool = False, key_scale=None):
     """Run the recurrence over [B, H, L, D] inputs; returns (o, S_final) in fp64.
 
     log_alpha is [B,H,L] (scalar gate), [B,H,L,Dk] (channel gate) or None
     (gate "none"); beta is [B,H,L] or [B,H,L,Dk]; S0 is [B,H,Dk,Dv] or None.
     beta_v (beta's shape) is a separate write strength; None means beta.
-    qk_l2norm and beta_logit switch on the input preparation.
+    qk_l2norm and beta_logit switch on the input preparation.  key_scale
+    ([B,H,L,Dk]) scales the write-side key.
     """
     lib = lib or _get()
     q = np.asarray(q)
@@ -105,12 +110,15 @@ def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
     op = o.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     fp = Sf.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     flags = (IN_QK_L2NORM if qk_l2norm else 0) | (IN_BETA_LOGIT if beta_logit else 0)
-    if flags:
+    if flags or key_scale is not None:
+        if key_scale is not None and np.shape(key_scale) != (B, H, L, Dk):
+            raise ValueError("key_scale must be [B, H, L, Dk]")
+        ksa, ksp = _f64(key_scale)
         bva, bvp = _f64(beta if beta_v is None else beta_v)
         if np.shape(bva) != np.shape(ba):
             raise ValueError("beta_v must have beta's shape")
         rc = lib.dro_forward_ex(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp, bvp,
-                                BETA_CODES[beta_mode], flags, sp, op, fp, int(nthreads))
+                                BETA_CODES[beta_mode], ksp, flags, sp, op, fp, int(nthreads))
     elif beta_v is None:
         rc = lib.dro_forward(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp,
                              BETA_CODES[beta_mode], sp, op, fp, int(nthreads))
@@ -130,12 +138,12 @@ def forward_problem(p, nthreads: int = 0, lib=None):
     return forward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, gate=p.gate,
                    beta_mode=p.beta_mode, nthreads=nthreads, lib=lib,
                    beta_v=getattr(p, "beta_v", None), qk_l2norm=getattr(p, "qk_l2norm", False),
-                   beta_logit=getattr(p, "beta_logit", False))
+                   beta_logit=getattr(p, "beta_logit", False), key_scale=getattr(p, "key_scale", None))
 
 
 def decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str,
                 nthreads: int = 0, lib=None, beta_v=None, qk_l2norm: bool = False,
-                beta_logit: bool = False):
+                beta_logit: bool = False, key_scale=None):
     """One recurrent step for a batch of states: S [N,H,Dk,Dv], q/k/v [N,H,D].
 
     The decode step is the forward with a single token, started from S.
@@ -144,7 +152,7 @@ def decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str,
     ex = lambda a: None if a is None else np.asarray(a)[:, :, None]
     o, Sn = forward(ex(q), ex(k), ex(v), ex(log_alpha), ex(beta), S, gate=gate,
                     beta_mode=beta_mode, nthreads=nthreads, lib=lib, beta_v=ex(beta_v),
-                    qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+                    qk_l2norm=qk_l2norm, beta_logit=beta_logit, key_scale=ex(key_scale))
     return o[:, :, 0], Sn
 
 

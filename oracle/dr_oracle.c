@@ -24,6 +24,17 @@
  *   write term) and vt = sqrt(beta^v_t) (.) v_t (dro_forward_kv); with
  *   beta^v = beta^k it is the equation above.
  *
+ * Write-side key scaling (dro_forward_ex, key_scale non-NULL): the OSDN page
+ * (section "Method") and the preconditioned delta rule page (its abstract)
+ * precondition the delta rule's gradient step with a diagonal matrix, which
+ * the OSDN page states is the same as scaling the key on the write side per
+ * feature.  The preconditioner's own online update is not printed; here it is
+ * an input s_t (a d_k-vector per token), and with w_t = s_t (.) kt_t
+ *       S_t = (I - w_t kt_t^T) Diag(alpha_t) S_{t-1} + w_t vt_t^T,
+ * i.e. S' = Diag(alpha_t) S_{t-1}, S_t = S' - Diag(s_t) grad, grad = kt (S'^T kt
+ * - vt)^T the gradient of 1/2 |S^T kt - vt|^2 at S'.  s = 1 is the update
+ * above.
+ *
  * Optional input preparation (dro_forward_ex, input_flags), the steps in
  * front of the recurrence:
  *   DRO_IN_QK_L2NORM  DeltaNet page, step list, step 2, and its note on the
@@ -82,13 +93,14 @@ static double strength(double x, int logit)
  *   beta   [L] or [L][Dk]      scales kt
  *   betav  [L] or [L][Dk]      scales vt (the same array as beta unless the
  *                              write strength is separate)
+ *   ks     [L][Dk] write-side key scales, or NULL (all ones)
  *   S      [Dk][Dv]  in: initial state, out: final state
  *   kt, vt scratch of Dk and Dv doubles, p scratch of Dv doubles. */
 static void run_sequence(int L, int Dk, int Dv,
                          const double* q, const double* k, const double* v,
                          const double* la, int gate, const double* beta, const double* betav,
-                         int beta_mode, int flags, double* S, double* o, double* kt, double* vt,
-                         double* p)
+                         int beta_mode, const double* ks, int flags, double* S, double* o, double* kt,
+                         double* vt, double* p)
 {
     const int l2 = (flags & DRO_IN_QK_L2NORM) != 0;
     const int logit = (flags & DRO_IN_BETA_LOGIT) != 0;
@@ -128,10 +140,11 @@ static void run_sequence(int L, int Dk, int Dv,
             for (int j = 0; j < Dv; ++j) p[j] += row[j] * kt[c];
         }
 
-        /* S_t = S' + kt (vt - p)^T */
+        /* S_t = S' + w (vt - p)^T, the write-side key w = s (.) kt */
         for (int c = 0; c < Dk; ++c) {
+            const double w = ks ? ks[(size_t)t * Dk + c] * kt[c] : kt[c];
             double* row = S + (size_t)c * Dv;
-            for (int j = 0; j < Dv; ++j) row[j] += kt[c] * (vt[j] - p[j]);
+            for (int j = 0; j < Dv; ++j) row[j] += w * (vt[j] - p[j]);
         }
 
         /* o_t = S_t^T q_t */
@@ -152,6 +165,7 @@ static void run_sequence(int L, int Dk, int Dv,
  *   log_alpha [B][H][L] (gate SCALAR) or [B][H][L][Dk] (gate CHANNEL); NULL for NONE
  *   beta      [B][H][L] (SCALAR) or [B][H][L][Dk] (CHANNEL; needs Dv == Dk): beta^k
  *   beta_v    beta^v, the same shape as beta
+ *   key_scale [B][H][L][Dk] write-side key scales s_t, or NULL (no scaling)
  *   input_flags  DRO_IN_QK_L2NORM | DRO_IN_BETA_LOGIT, or 0
  *   S0        [B][H][Dk][Dv] or NULL (zeros)
  *   o         [B][H][L][Dv]     out
@@ -162,8 +176,8 @@ static void run_sequence(int L, int Dk, int Dv,
 int dro_forward_ex(int B, int H, int L, int Dk, int Dv,
                    const double* q, const double* k, const double* v,
                    const double* log_alpha, int gate, const double* beta, const double* beta_v,
-                   int beta_mode, int input_flags, const double* S0, double* o, double* S_final,
-                   int nthreads)
+                   int beta_mode, const double* key_scale, int input_flags, const double* S0,
+                   double* o, double* S_final, int nthreads)
 {
     if (B <= 0 || H <= 0 || L < 0 || Dk <= 0 || Dv <= 0) return DRO_EINVAL;
     if (input_flags & ~(DRO_IN_QK_L2NORM | DRO_IN_BETA_LOGIT)) return DRO_EINVAL;
@@ -196,7 +210,8 @@ int dro_forward_ex(int B, int H, int L, int Dk, int Dv,
         run_sequence(L, Dk, Dv,
                      q + (size_t)s * L * Dk, k + (size_t)s * L * Dk, v + (size_t)s * L * Dv,
                      log_alpha ? log_alpha + (size_t)s * lw : NULL, gate,
-                     beta + (size_t)s * bw, beta_v + (size_t)s * bw, beta_mode, input_flags,
+                     beta + (size_t)s * bw, beta_v + (size_t)s * bw, beta_mode,
+                     key_scale ? key_scale + (size_t)s * L * Dk : NULL, input_flags,
                      S, o + (size_t)s * L * Dv, kt, vt, p);
         if (S_final) memcpy(S_final + (size_t)s * sz, S, sizeof(double) * sz);
         free(S);
@@ -211,8 +226,8 @@ int dro_forward_kv(int B, int H, int L, int Dk, int Dv,
                    const double* log_alpha, int gate, const double* beta, const double* beta_v,
                    int beta_mode, const double* S0, double* o, double* S_final, int nthreads)
 {
-    return dro_forward_ex(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta_v, beta_mode, 0, S0,
-                          o, S_final, nthreads);
+    return dro_forward_ex(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta_v, beta_mode, NULL, 0,
+                          S0, o, S_final, nthreads);
 }
 
 /* The same with one strength for both the key and the value (beta^v = beta). */

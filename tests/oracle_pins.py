@@ -537,3 +537,82 @@ def pin_beta_logit_saturation(fwd_ex):
 
 PREP_PINS = [pin_l2norm_ray_invariance, pin_l2norm_fixes_unit_and_zero_vectors,
              pin_beta_logit_round_trip, pin_beta_logit_saturation]
+
+
+# ---------------------------------------------------------------------------
+# Write-side key scaling: a diagonal preconditioner s_t on the delta rule's
+# gradient step (OSDN page, "Method"; the preconditioned delta rule page,
+# abstract), given as an input.  Each pin takes
+# fwd_ks(q, k, v, la, beta, key_scale, S0, *, gate, beta_mode).
+# ---------------------------------------------------------------------------
+
+def _dense_ks(q, k, v, la, beta, ks, S0, gate, beta_mode):
+    L, Dk = q.shape
+    Dv = v.shape[1]
+    S = S0.copy()
+    o = np.zeros((L, Dv))
+    for t in range(L):
+        sb = np.sqrt(_beta_vec(beta, t, beta_mode, Dk))
+        kt = sb * k[t]
+        vt = (sb[:Dv] if beta_mode == "channel" else sb[0]) * v[t]
+        w = ks[t] * kt
+        S = (np.eye(Dk) - np.outer(w, kt)) @ np.diag(_alpha_vec(la, t, gate, Dk)) @ S + np.outer(w, vt)
+        o[t] = S.T @ q[t]
+    return o, S
+
+
+def pin_ks_dense_product(fwd_ks):
+    """Oracle == literal dense (I - w kt^T) Diag(alpha) S + w vt^T, w = s (.) kt,
+    every gate and beta mode."""
+    salt = 150
+    for gate in ("none", "scalar", "channel"):
+        for beta_mode in ("scalar", "channel"):
+            salt += 1
+            q, k, v, la, beta, S0 = random_case(salt, B=2, H=2, L=9, Dk=6, Dv=6, gate=gate,
+                                                beta_mode=beta_mode)
+            ks = _rng(salt + 50).uniform(0.2, 2.0, q.shape)
+            o, S = fwd_ks(q, k, v, la, beta, ks, S0, gate=gate, beta_mode=beta_mode)
+            for b in range(2):
+                for h in range(2):
+                    oy, Sy = _dense_ks(q[b, h], k[b, h], v[b, h], None if la is None else la[b, h],
+                                       beta[b, h], ks[b, h], S0[b, h], gate, beta_mode)
+                    _close(o[b, h], oy, 1e-12, f"o ({gate},{beta_mode})")
+                    _close(S[b, h], Sy, 1e-12, f"S ({gate},{beta_mode})")
+
+
+def pin_ks_preconditioned_gradient_step(fwd_ks):
+    """One token from S0 is S' - Diag(s) grad, with S' = Diag(alpha) S0 and grad
+    the gradient at S' of the inner regression loss 1/2 |S^T kt - vt|^2, taken
+    here by central differences (exact for a quadratic up to rounding)."""
+    q, k, v, la, beta, S0 = random_case(160, B=1, H=1, L=1, Dk=5, Dv=4, gate="channel",
+                                        beta_mode="scalar")
+    ks = _rng(161).uniform(0.2, 2.0, q.shape)
+    _, S1 = fwd_ks(q, k, v, la, beta, ks, S0, gate="channel", beta_mode="scalar")
+    kt = np.sqrt(beta[0, 0, 0]) * k[0, 0, 0]
+    vt = np.sqrt(beta[0, 0, 0]) * v[0, 0, 0]
+    Sp = np.exp(la[0, 0, 0])[:, None] * S0[0, 0]
+    loss = lambda S: 0.5 * np.sum((S.T @ kt - vt) ** 2)
+    grad = np.zeros_like(Sp)
+    h = 1e-3
+    for i in range(Sp.shape[0]):
+        for j in range(Sp.shape[1]):
+            E = np.zeros_like(Sp)
+            E[i, j] = h
+            grad[i, j] = (loss(Sp + E) - loss(Sp - E)) / (2 * h)
+    _close(S1[0, 0], Sp - ks[0, 0, 0][:, None] * grad, 1e-9, "S after one step")
+
+
+def pin_ks_unit_and_zero_scales(fwd_ks):
+    """s = 1 is the unscaled recurrence; s = 0 neither erases nor writes, so the
+    state only decays: S_L = Diag(e^{sum log alpha}) S0."""
+    q, k, v, la, beta, S0 = random_case(170, L=10, Dk=5, Dv=5, gate="channel", beta_mode="channel")
+    kw = dict(gate="channel", beta_mode="channel")
+    o1, S1 = fwd_ks(q, k, v, la, beta, np.ones_like(q), S0, **kw)
+    o2, S2 = fwd_ks(q, k, v, la, beta, None, S0, **kw)
+    _close(o1, o2, 1e-14, "o at s = 1")
+    _close(S1, S2, 1e-14, "S at s = 1")
+    _, S3 = fwd_ks(q, k, v, la, beta, np.zeros_like(q), S0, **kw)
+    _close(S3, np.exp(la.sum(axis=2))[..., None] * S0, 1e-12, "S at s = 0")
+
+
+KS_PINS = [pin_ks_dense_product, pin_ks_preconditioned_gradient_step, pin_ks_unit_and_zero_scales]

@@ -14,7 +14,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "dr_oracle.c")
 # (name, original text, planted text): each original must occur exactly once.
 MUTANTS = [
     ("drop_decay", "row[j] *= a;", "row[j] *= 1.0;"),
-    ("sign_of_error", "row[j] += kt[c] * (vt[j] - p[j]);", "row[j] += kt[c] * (vt[j] + p[j]);"),
+    ("sign_of_error", "row[j] += w * (vt[j] - p[j]);", "row[j] += w * (vt[j] + p[j]);"),
     ("beta_not_sqrt", "kt[c] = sqrt(strength(b, logit)) * (kn * k_t[c]);",
      "kt[c] = strength(b, logit) * (kn * k_t[c]);"),
     ("value_unscaled", "vt[j] = sqrt(strength(b, logit)) * v_t[j];", "vt[j] = v_t[j];"),
@@ -25,7 +25,7 @@ MUTANTS = [
     ("error_drops_read", "(vt[j] - p[j])", "(vt[j] - 0.0 * p[j])"),
     ("state_not_carried", "if (S0) memcpy(S, S0", "if (0) memcpy(S, S0"),
     ("output_before_update",
-     "/* S_t = S' + kt (vt - p)^T */",
+     "/* S_t = S' + w (vt - p)^T, the write-side key w = s (.) kt */",
      "for (int j = 0; j < Dv; ++j) { double a_ = 0; for (int c = 0; c < Dk; ++c) a_ += S[(size_t)c * Dv + j] * qt[c]; o[(size_t)t * Dv + j] = a_; }\n        if (0)"),
 ]
 
@@ -108,6 +108,38 @@ def test_prep_pins_catch_planted_mistake(tmp_path, name, old, new):
         try:
             with np.errstate(all="ignore"):
                 pin(fwd_ex)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
+
+
+# Mistakes in the write-side key scaling, caught by its pins.
+KS_MUTANTS = [
+    ("write_key_unscaled", "const double w = ks ? ks[(size_t)t * Dk + c] * kt[c] : kt[c];",
+     "const double w = kt[c];"),
+    ("scale_squared", "const double w = ks ? ks[(size_t)t * Dk + c] * kt[c] : kt[c];",
+     "const double w = ks ? ks[(size_t)t * Dk + c] * ks[(size_t)t * Dk + c] * kt[c] : kt[c];"),
+    ("scale_on_the_read_side", "p[j] += row[j] * kt[c];",
+     "p[j] += row[j] * (ks ? ks[(size_t)t * Dk + c] * kt[c] : kt[c]);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", KS_MUTANTS, ids=[m[0] for m in KS_MUTANTS])
+def test_ks_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+
+    def fwd_ks(q, k, v, la, beta, key_scale, S0, *, gate, beta_mode):
+        return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, lib=lib,
+                              key_scale=key_scale)
+
+    caught = []
+    for pin in oracle_pins.KS_PINS:
+        try:
+            pin(fwd_ks)
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"

@@ -91,7 +91,7 @@ def test_input_preparation_off_is_the_plain_forward():
     Sf = np.empty_like(a[1])
     arrs = [np.ascontiguousarray(x, np.float64) for x in (q, k, v, la, beta, S0)]
     rc = lib.dro_forward_ex(1, 2, 10, 5, 5, dp(arrs[0]), dp(arrs[1]), dp(arrs[2]), dp(arrs[3]), 2,
-                            dp(arrs[4]), dp(arrs[4]), 1, 0, dp(arrs[5]), dp(o), dp(Sf), 0)
+                            dp(arrs[4]), dp(arrs[4]), 1, None, 0, dp(arrs[5]), dp(o), dp(Sf), 0)
     assert rc == 0
     assert np.array_equal(o, a[0]) and np.array_equal(Sf, a[1])
 
@@ -102,4 +102,23 @@ def test_input_preparation_decode_is_one_token_forward():
     kw = dict(gate="scalar", beta_mode="scalar", qk_l2norm=True, beta_logit=True)
     o1, S1 = oracle.decode_step(S0, q[:, :, 0], k[:, :, 0], v[:, :, 0], la[:, :, 0], beta[:, :, 0], **kw)
     o2, S2 = oracle.forward(q, k, v, la, beta, S0, **kw)
+    assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
+
+
+def fwd_ks(q, k, v, la, beta, key_scale, S0, *, gate, beta_mode):
+    return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, key_scale=key_scale)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.KS_PINS, ids=lambda f: f.__name__)
+def test_key_scale_pin(pin):
+    pin(fwd_ks)
+
+
+def test_key_scale_decode_is_one_token_forward():
+    q, k, v, la, beta, S0 = oracle_pins.random_case(140, B=3, H=2, L=1, Dk=6, Dv=6, gate="channel",
+                                                    beta_mode="scalar")
+    ks = np.random.default_rng(141).uniform(0.2, 2.0, q.shape)
+    o1, S1 = oracle.decode_step(S0, q[:, :, 0], k[:, :, 0], v[:, :, 0], la[:, :, 0], beta[:, :, 0],
+                                gate="channel", beta_mode="scalar", key_scale=ks[:, :, 0])
+    o2, S2 = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode="scalar", key_scale=ks)
     assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
