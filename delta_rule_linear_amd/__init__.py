@@ -13,6 +13,11 @@ With separate channel-wise erase and write strengths (FG2-GDN+):
 
     o, S = dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0, gate="channel")
     o = dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, gate="channel")
+
+With a diagonal preconditioner on the gradient step (write-side key scales):
+
+    o, S = dr_chunk_fwd_precond(q, k, v, log_alpha, beta, key_scale, S0, gate="scalar",
+                                beta_mode="scalar")
 """
 from __future__ import annotations
 
@@ -23,14 +28,15 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 4
+DR_ABI_VERSION = 5
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
 BETAS = {"scalar": 0, "channel": 1}
 DR_IN_QK_L2NORM, DR_IN_BETA_LOGIT = 1, 2
 EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "dr_decode_step",
-           "dr_decode_step_kv", "dr_status_str", "dr_last_error", "dr_abi_version",
+           "dr_decode_step_kv", "dr_chunk_fwd_precond_workspace_bytes", "dr_chunk_fwd_precond",
+           "dr_decode_step_precond", "dr_status_str", "dr_last_error", "dr_abi_version",
            "dr_profile_begin", "dr_profile_end")
 
 
@@ -83,6 +89,14 @@ def lib() -> ctypes.CDLL:
         L.dr_decode_step.restype = ctypes.c_int
         L.dr_decode_step_kv.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.dr_decode_step_kv.restype = ctypes.c_int
+        L.dr_chunk_fwd_precond_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.dr_chunk_fwd_precond_workspace_bytes.restype = ctypes.c_size_t
+        L.dr_chunk_fwd_precond.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, ctypes.c_size_t, vp]
+        L.dr_chunk_fwd_precond.restype = ctypes.c_int
+        L.dr_decode_step_precond.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                             vp]
+        L.dr_decode_step_precond.restype = ctypes.c_int
         L.dr_status_str.argtypes = [ctypes.c_int]
         L.dr_status_str.restype = ctypes.c_char_p
         L.dr_last_error.argtypes = []
@@ -184,6 +198,10 @@ def dr_chunk_fwd_workspace_bytes(desc: ChunkDesc) -> int:
     return int(lib().dr_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
 
 
+def dr_chunk_fwd_precond_workspace_bytes(desc: ChunkDesc) -> int:
+    return int(lib().dr_chunk_fwd_precond_workspace_bytes(ctypes.byref(desc)))
+
+
 def dr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
                  out_dtype=None, o=None, S_final=None, want_state: bool = True,
                  workspace=None, stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
@@ -201,6 +219,17 @@ def dr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str
                   want_state, workspace, stream, input_flags(qk_l2norm, beta_logit))
 
 
+def dr_chunk_fwd_precond(q, k, v, log_alpha, beta, key_scale, S0=None, *, gate: str, beta_mode: str,
+                         out_dtype=None, o=None, S_final=None, want_state: bool = True, workspace=None,
+                         stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
+    """dr_chunk_fwd with write-side key scales key_scale [B,H,L,Dk] fp32 (the
+    diagonal preconditioner of the gradient step)."""
+    if key_scale is None:
+        raise ValueError("key_scale is required")
+    return _chunk(q, k, v, log_alpha, beta, None, S0, gate, beta_mode, out_dtype, o, S_final,
+                  want_state, workspace, stream, input_flags(qk_l2norm, beta_logit), key_scale)
+
+
 def dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0=None, *, gate: str, out_dtype=None,
                     o=None, S_final=None, want_state: bool = True, workspace=None, stream=None,
                     qk_l2norm: bool = False, beta_logit: bool = False):
@@ -213,7 +242,7 @@ def dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0=None, *, gate: str, o
 
 
 def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, S_final, want_state,
-           workspace, stream, flags):
+           workspace, stream, flags, key_scale=None):
     torch = _torch()
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
@@ -230,6 +259,8 @@ def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, 
     _need(beta, "beta", torch.float32, bshape)
     if beta_v is not None:
         _need(beta_v, "beta_v", torch.float32, bshape)
+    if key_scale is not None:
+        _need(key_scale, "key_scale", torch.float32, (B, H, L, Dk))
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
     out_dtype = torch.float32 if out_dtype is None else out_dtype
@@ -243,11 +274,16 @@ def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, 
         _need(S_final, "S_final", torch.float32, (B, H, Dk, Dv))
     desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), gate, beta_mode,
                       flags)
-    nbytes = dr_chunk_fwd_workspace_bytes(desc)
+    nbytes = (dr_chunk_fwd_workspace_bytes(desc) if key_scale is None
+              else dr_chunk_fwd_precond_workspace_bytes(desc))
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if beta_v is None:
+    if key_scale is not None:
+        _check(lib().dr_chunk_fwd_precond(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                          _ptr(beta), _ptr(key_scale), _ptr(S0), _ptr(o), _ptr(S_final),
+                                          _ptr(workspace), wbytes, _stream(stream)))
+    elif beta_v is None:
         _check(lib().dr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                   _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _ptr(workspace),
                                   wbytes, _stream(stream)))
@@ -269,6 +305,16 @@ def dr_decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str, ou
                    input_flags(qk_l2norm, beta_logit))
 
 
+def dr_decode_step_precond(S, q, k, v, log_alpha, beta, key_scale, *, gate: str, beta_mode: str,
+                           out_dtype=None, o=None, stream=None, qk_l2norm: bool = False,
+                           beta_logit: bool = False):
+    """dr_decode_step with write-side key scales key_scale [N,H,Dk] fp32."""
+    if key_scale is None:
+        raise ValueError("key_scale is required")
+    return _decode(S, q, k, v, log_alpha, beta, None, gate, beta_mode, out_dtype, o, stream,
+                   input_flags(qk_l2norm, beta_logit), key_scale)
+
+
 def dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, *, gate: str, out_dtype=None, o=None,
                       stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
     """dr_decode_step with separate channel-wise erase (beta_k) and write
@@ -279,7 +325,8 @@ def dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, *, gate: str, out_d
                    input_flags(qk_l2norm, beta_logit))
 
 
-def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, stream, flags):
+def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, stream, flags,
+            key_scale=None):
     torch = _torch()
     N, H, Dk, Dv = S.shape
     _need(S, "S", torch.float32)
@@ -296,6 +343,8 @@ def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, 
     _need(beta, "beta", torch.float32, bshape)
     if beta_v is not None:
         _need(beta_v, "beta_v", torch.float32, bshape)
+    if key_scale is not None:
+        _need(key_scale, "key_scale", torch.float32, (N, H, Dk))
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if o is None:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=S.device)
@@ -303,7 +352,10 @@ def _decode(S, q, k, v, log_alpha, beta, beta_v, gate, beta_mode, out_dtype, o, 
         _need(o, "o", out_dtype, (N, H, Dv))
     desc = DecodeDesc(N, H, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), GATES[gate],
                       BETAS[beta_mode], flags)
-    if beta_v is None:
+    if key_scale is not None:
+        _check(lib().dr_decode_step_precond(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                            _ptr(beta), _ptr(key_scale), _ptr(S), _ptr(o), _stream(stream)))
+    elif beta_v is None:
         _check(lib().dr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                     _ptr(beta), _ptr(S), _ptr(o), _stream(stream)))
     else:

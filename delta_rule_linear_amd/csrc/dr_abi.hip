@@ -58,12 +58,13 @@ struct WsLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(const dr_chunk_desc& d) {
+// precond: write-side key scales, which run on the channel-gate path
+WsLayout ws_layout(const dr_chunk_desc& d, bool precond = false) {
     WsLayout w{};
     const size_t P = d.in_dtype == DR_F32 ? 2 : 1;
     const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
     const size_t NCH = (size_t)d.B * d.H * NC;
-    const bool cg = d.gate == DR_GATE_CHANNEL, cb = d.beta == DR_BETA_CHANNEL;
+    const bool cg = d.gate == DR_GATE_CHANNEL || precond, cb = d.beta == DR_BETA_CHANNEL;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -203,8 +204,9 @@ namespace {
 // The chunked forward; beta_v is the write strength on v (beta itself for
 // dr_chunk_fwd, a separate channel-wise array for dr_chunk_fwd_kv).
 dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
-                    const float* log_alpha, const float* beta, const float* beta_v, const float* S0,
-                    void* o, float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
+                    const float* log_alpha, const float* beta, const float* beta_v, const float* key_scale,
+                    bool precond, const float* S0, void* o, float* S_final, void* workspace,
+                    size_t workspace_bytes, void* stream) {
     dr_status s = check_chunk_desc(d);
     if (s != DR_OK) return s;
     const size_t nseq = (size_t)d->B * d->H;
@@ -212,12 +214,14 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     if (tokens) {
         if (!q || !k || !v || !beta || !beta_v || !o)
             return fail(DR_ERR_NULL, "q, k, v, beta (beta_k and beta_v) and o are required");
+        if (precond && !key_scale) return fail(DR_ERR_NULL, "key_scale is required");
         if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
             return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
     }
-    const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, S0, o, S_final, workspace};
-    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "S0", "o", "S_final", "workspace"};
-    for (int i = 0; i < 10; ++i)
+    const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, key_scale, S0, o, S_final, workspace};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "key_scale", "S0", "o", "S_final",
+                           "workspace"};
+    for (int i = 0; i < 11; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     if (S_final && S0 && S_final != S0) {
         const size_t bytes = nseq * d->Dk * d->Dv * sizeof(float);
@@ -226,7 +230,7 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         if (a0 < a1 + bytes && a1 < a0 + bytes)
             return fail(DR_ERR_UNSUPPORTED, "S_final overlaps S0 without being the same array");
     }
-    const WsLayout w = ws_layout(*d);
+    const WsLayout w = ws_layout(*d, precond);
     if (w.total) {
         if (!workspace) return fail(DR_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
         if (workspace_bytes < w.total)
@@ -255,6 +259,8 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.out_bf16 = d->out_dtype == DR_BF16;
     a.qk_norm = (d->input_flags & DR_IN_QK_L2NORM) != 0;
     a.beta_logit = (d->input_flags & DR_IN_BETA_LOGIT) != 0;
+    a.gate_mode = d->gate;
+    a.key_scale = precond ? key_scale : nullptr;
     char* ws = (char*)workspace;
     a.wsT = (dr::half_t*)(ws + w.T);
     a.wsP = (dr::half_t*)(ws + w.Pm);
@@ -263,15 +269,15 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.wsKs = w.Ks ? (dr::half_t*)(ws + w.Ks) : nullptr;
     a.wsKl = w.Kl ? (dr::half_t*)(ws + w.Kl) : nullptr;
     a.wsV = w.V ? (dr::half_t*)(ws + w.V) : nullptr;
-    hipError_t e = dr::launch_chunk(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL,
+    hipError_t e = dr::launch_chunk(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL || precond,
                                     d->beta == DR_BETA_CHANNEL, beta_v != beta, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "chunk kernels launch: %s", hipGetErrorString(e));
     return DR_OK;
 }
 
 dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, const void* v,
-                      const float* log_alpha, const float* beta, const float* beta_v, float* S,
-                      void* o, void* stream) {
+                      const float* log_alpha, const float* beta, const float* beta_v,
+                      const float* key_scale, bool precond, float* S, void* o, void* stream) {
     if (!d) return fail(DR_ERR_NULL, "descriptor is NULL");
     if (d->N < 0 || d->H < 0) return fail(DR_ERR_SHAPE, "negative dimension (N=%d H=%d)", d->N, d->H);
     dr_status s = check_modes(d->Dk, d->Dv, d->in_dtype, d->out_dtype, d->gate, d->beta, d->input_flags);
@@ -283,11 +289,12 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
     if (nst == 0) return DR_OK;
     if (!q || !k || !v || !beta || !beta_v || !S || !o)
         return fail(DR_ERR_NULL, "q, k, v, beta (beta_k and beta_v), S and o are required");
+    if (precond && !key_scale) return fail(DR_ERR_NULL, "key_scale is required");
     if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
         return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
-    const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, S, o};
-    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "S", "o"};
-    for (int i = 0; i < 8; ++i)
+    const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, key_scale, S, o};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "key_scale", "S", "o"};
+    for (int i = 0; i < 9; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     dr::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v;
@@ -298,6 +305,7 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
     a.out_bf16 = d->out_dtype == DR_BF16;
     a.qk_norm = (d->input_flags & DR_IN_QK_L2NORM) != 0;
     a.beta_logit = (d->input_flags & DR_IN_BETA_LOGIT) != 0;
+    a.key_scale = precond ? key_scale : nullptr;
     hipError_t e = dr::launch_decode(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL,
                                      d->beta == DR_BETA_CHANNEL, (hipStream_t)stream);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
@@ -320,8 +328,8 @@ dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, con
                        const float* log_alpha, const float* beta, const float* S0, void* o,
                        float* S_final, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = '\0';
-    return chunk_fwd(d, q, k, v, log_alpha, beta, beta, S0, o, S_final, workspace, workspace_bytes,
-                     stream);
+    return chunk_fwd(d, q, k, v, log_alpha, beta, beta, nullptr, false, S0, o, S_final, workspace,
+                     workspace_bytes, stream);
 }
 
 dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
@@ -330,7 +338,21 @@ dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
                           size_t workspace_bytes, void* stream) {
     g_err[0] = '\0';
     if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
-    return chunk_fwd(d, q, k, v, log_alpha, beta_k, beta_v, S0, o, S_final, workspace,
+    return chunk_fwd(d, q, k, v, log_alpha, beta_k, beta_v, nullptr, false, S0, o, S_final, workspace,
+                     workspace_bytes, stream);
+}
+
+size_t dr_chunk_fwd_precond_workspace_bytes(const dr_chunk_desc* d) {
+    if (check_chunk_desc(d) != DR_OK) return 0;
+    return ws_layout(*d, true).total;
+}
+
+dr_status dr_chunk_fwd_precond(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* key_scale,
+                               const float* S0, void* o, float* S_final, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    return chunk_fwd(d, q, k, v, log_alpha, beta, beta, key_scale, true, S0, o, S_final, workspace,
                      workspace_bytes, stream);
 }
 
@@ -338,7 +360,14 @@ dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, 
                          const float* log_alpha, const float* beta, float* S, void* o,
                          void* stream) {
     g_err[0] = '\0';
-    return decode_step(d, q, k, v, log_alpha, beta, beta, S, o, stream);
+    return decode_step(d, q, k, v, log_alpha, beta, beta, nullptr, false, S, o, stream);
+}
+
+dr_status dr_decode_step_precond(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta, const float* key_scale,
+                                 float* S, void* o, void* stream) {
+    g_err[0] = '\0';
+    return decode_step(d, q, k, v, log_alpha, beta, beta, key_scale, true, S, o, stream);
 }
 
 dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* k, const void* v,
@@ -346,7 +375,7 @@ dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* 
                             float* S, void* o, void* stream) {
     g_err[0] = '\0';
     if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
-    return decode_step(d, q, k, v, log_alpha, beta_k, beta_v, S, o, stream);
+    return decode_step(d, q, k, v, log_alpha, beta_k, beta_v, nullptr, false, S, o, stream);
 }
 
 }  // extern "C"

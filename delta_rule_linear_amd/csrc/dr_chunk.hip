@@ -116,8 +116,10 @@ constexpr int prep_threads() { return CGATE ? 4 * DK : 256; }
 // tg = tid / (DK / 4)).  Rows past the sequence's end load row 0 of the chunk
 // and are masked at use.
 // With a separate write strength (SEPV) v is not held here: v and beta_v are
-// loaded at the start of the chunk's preparation instead.
-template <int DK, bool F32IN, bool CBETA, bool SEPV = false>
+// loaded at the start of the chunk's preparation instead.  KS marks the
+// variant with write-side key scales, whose gate may be scalar or absent (it
+// runs on this path with the gate broadcast to every channel).
+template <int DK, bool F32IN, bool CBETA, bool SEPV = false, bool KS = false>
 struct CgIn {
     static constexpr int CPT = 4;
     float la[4][CPT];               // log alpha
@@ -130,8 +132,8 @@ struct CgIn {
 // Part PART of the loads (0: log alpha and k, 1: q and scalar beta, 2: channel
 // beta and v, -1: all), so that a chunk's loads can be spread over the next
 // chunk's phases instead of queueing behind one another.
-template <int DK, bool F32IN, bool CBETA, bool SEPV, int PART = -1>
-__device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBETA, SEPV>& in, int job,
+template <int DK, bool F32IN, bool CBETA, bool SEPV, bool KS, int PART = -1>
+__device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBETA, SEPV, KS>& in, int job,
                                          int tid) {
     constexpr int CPT = 4;
     constexpr bool P0 = PART < 0 || PART == 0, P1 = PART < 0 || PART == 1, P2 = PART < 0 || PART == 2;
@@ -145,7 +147,17 @@ __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBE
         const int r = 4 * tg + u;
         const size_t row = tok0 + (r < Lc ? r : 0);
         if constexpr (P0) {
-            load_f32_n<CPT>(a.log_alpha + row * DK + ch0, in.la[u]);
+            if constexpr (KS) {
+                if (a.gate_mode == 2) {
+                    load_f32_n<CPT>(a.log_alpha + row * DK + ch0, in.la[u]);
+                } else {
+                    const float x = a.gate_mode == 1 ? a.log_alpha[row] : 0.f;
+#pragma unroll
+                    for (int cc = 0; cc < CPT; ++cc) in.la[u][cc] = x;
+                }
+            } else {
+                load_f32_n<CPT>(a.log_alpha + row * DK + ch0, in.la[u]);
+            }
             in.k[u] = ld_rawn<F32IN, CPT>(a.k, row * DK + ch0);
         }
         if constexpr (P1) in.q[u] = ld_rawn<F32IN, CPT>(a.q, row * DK + ch0);
@@ -164,9 +176,9 @@ __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBE
 // chunk's raw inputs arrive in `in`; once they are consumed, the inputs of
 // chunk `next_job` (>= 0) are loaded into it, so that those loads are in
 // flight during this chunk's matrix work.
-template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV, bool QKN>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV, bool QKN, bool KS>
 __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, const int seq, const int c,
-                                           CgIn<DK, F32IN, CBETA, SEPV>& in, const int next_job) {
+                                           CgIn<DK, F32IN, CBETA, SEPV, KS>& in, const int next_job) {
     constexpr int P = F32IN ? 2 : 1;
     constexpr int NTH = prep_threads<DK, CGATE>();
     using SM = PrepSmem<DK, CGATE>;
@@ -306,6 +318,15 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 vin[u] = ld_rawn<F32IN, CPT>(a.v, row * Dv + ch0);
             }
         }
+        // write-side key scales, likewise loaded here
+        float ksv[KS ? 4 : 1][CPT];
+        if constexpr (KS) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const size_t row = tok0 + (4 * tg + u < Lc ? 4 * tg + u : 0);
+                load_f32_n<CPT>(a.key_scale + row * DK + ch0, ksv[u]);
+            }
+        }
         float G[4][CPT];
         {
             float run[CPT];
@@ -410,13 +431,16 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 const float g2 = G[u][c] * kL2E;
                 const float rowf = __builtin_amdgcn_exp2f(g2 - gs2[c]);
                 const float colf = __builtin_amdgcn_exp2f(ge2[c] - g2);
+                // the write-side key (column side of A and P, the state
+                // update) takes the key scale; the read side keeps kt
+                const float wk = KS ? kt * ksv[u][c] : kt;
                 okg[c] = kt * rowf;
-                oki[c] = kt * colf;
+                oki[c] = wk * colf;
                 oqg[c] = qv * rowf;
                 const float eg = egs[c] * rowf;
                 wq[c] = qv * eg;
                 wks[c] = kt * eg;
-                wkl[c] = kt * (e63[c] * colf);
+                wkl[c] = wk * (e63[c] * colf);
                 wv[c] = CBETA ? (live ? sbw * vx[c] : 0.f) : 0.f;
             }
 #pragma unroll
@@ -459,7 +483,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
         if constexpr (!CBETA) {
             if (w == 3) sb[l] = l < Lc ? strength(in.bs, blg) : 0.f;
         }
-        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, 0>(a, in, next_job, tid);
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, KS, 0>(a, in, next_job, tid);
     }
     lds_barrier();
 
@@ -616,7 +640,14 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 if (i <= r && r < Lc) {
                     for (int col = 0; col < DK; ++col) {
                         float e = 0.f;
-                        for (int t = i + 1; t <= r; ++t) e += a.log_alpha[(tok0 + t) * DK + col];
+                        for (int t = i + 1; t <= r; ++t) {
+                            if constexpr (KS) {
+                                e += a.gate_mode == 2 ? a.log_alpha[(tok0 + t) * DK + col]
+                                   : a.gate_mode == 1 ? a.log_alpha[tok0 + t] : 0.f;
+                            } else {
+                                e += a.log_alpha[(tok0 + t) * DK + col];
+                            }
+                        }
                         const float dec = expf(e);
                         float kr = load1<F32IN>(a.k, (tok0 + r) * DK + col);
                         float ki = load1<F32IN>(a.k, (tok0 + i) * DK + col);
@@ -628,6 +659,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                             kr *= sqrtf(strength(a.beta[(tok0 + r) * DK + col], blg));
                             ki *= sqrtf(strength(a.beta[(tok0 + i) * DK + col], blg));
                         }
+                        if constexpr (KS) ki *= a.key_scale[(tok0 + i) * DK + col];   // write side
                         accA += kr * ki * dec;
                         accP += qr * ki * dec;
                     }
@@ -647,7 +679,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 
     // ------------------------------------------- T = (I + A)^-1, blocked, fp32
     if constexpr (CGATE) {
-        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, 1>(a, in, next_job, tid);
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, KS, 1>(a, in, next_job, tid);
     }
     // diagonal 16x16 blocks: wave w inverts block w, lane j < 16 owns column j
     if (w < 4 && l < 16) {
@@ -665,7 +697,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
     }
     lds_barrier();
     if constexpr (CGATE) {
-        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, 2>(a, in, next_job, tid);
+        if (next_job >= 0) cg_fetch<DK, F32IN, CBETA, SEPV, KS, 2>(a, in, next_job, tid);
     }
     // off-diagonal blocks, one block row R at a time on the fp32 matrix cores;
     // wave I < R computes
@@ -744,11 +776,11 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 // One workgroup per chunk, or, with a channel gate, a persistent loop over
 // chunks (job = chunk + NC * sequence) that loads the next chunk's inputs
 // while it works on the current one.
-template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false, bool QKN = false>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false, bool QKN = false, bool KS = false>
 __global__ __launch_bounds__((prep_threads<DK, CGATE>())) void prep_kernel(ChunkArgs a) {
     using SM = PrepSmem<DK, CGATE>;
     __shared__ __attribute__((aligned(16))) float smem[SM::FLOATS];
-    CgIn<DK, F32IN, CBETA, SEPV> in;
+    CgIn<DK, F32IN, CBETA, SEPV, KS> in;
     if constexpr (CGATE) {
         // fp32 inputs would need twice the registers: they are loaded per chunk
         constexpr bool PREF = !F32IN;
@@ -758,11 +790,11 @@ __global__ __launch_bounds__((prep_threads<DK, CGATE>())) void prep_kernel(Chunk
         for (; job < njobs; job += gridDim.x) {
             if (!PREF) cg_fetch(a, in, job, threadIdx.x);
             const int nj = job + gridDim.x;
-            prep_chunk<DK, F32IN, CGATE, CBETA, SEPV, QKN>(a, smem, job / a.NC, job % a.NC, in,
+            prep_chunk<DK, F32IN, CGATE, CBETA, SEPV, QKN, KS>(a, smem, job / a.NC, job % a.NC, in,
                                                            PREF && nj < njobs ? nj : -1);
         }
     } else {
-        prep_chunk<DK, F32IN, CGATE, CBETA, SEPV, QKN>(a, smem, blockIdx.z * a.H + blockIdx.y, blockIdx.x, in,
+        prep_chunk<DK, F32IN, CGATE, CBETA, SEPV, QKN, KS>(a, smem, blockIdx.z * a.H + blockIdx.y, blockIdx.x, in,
                                                        -1);
     }
 }
@@ -1108,7 +1140,7 @@ static long resident_groups(const void* kern, int threads) {
     return n;
 }
 
-template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false, bool QKN = false>
+template <int DK, bool F32IN, bool CGATE, bool CBETA, bool SEPV = false, bool QKN = false, bool KS = false>
 static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     const int nseq = a.nseq;
     if (a.NC > 0 && nseq > 0) {
@@ -1117,7 +1149,7 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
             prof_mark(st, kProfPrep);
             e = launch_prep16(a, DK, st);
         } else if constexpr (CGATE) {
-            auto kern = prep_kernel<DK, F32IN, CGATE, CBETA, SEPV, QKN>;
+            auto kern = prep_kernel<DK, F32IN, CGATE, CBETA, SEPV, QKN, KS>;
             const long njobs = (long)nseq * a.NC;
             constexpr int NTH = prep_threads<DK, CGATE>();
             // (the occupancy query of a first call stays outside the timing mark)
@@ -1158,6 +1190,10 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
 // beta_v carries room for it.
 template <int DK, bool F32IN, bool QKN>
 static hipError_t launch_chunk_cg(const ChunkArgs& a, bool cbeta, bool sepv, hipStream_t st) {
+    if (a.key_scale) {   // write-side key scales: any gate mode, on this path
+        return cbeta ? launch_chunk_t<DK, F32IN, true, true, false, QKN, true>(a, st)
+                     : launch_chunk_t<DK, F32IN, true, false, false, QKN, true>(a, st);
+    }
     if (!cbeta) return launch_chunk_t<DK, F32IN, true, false, false, QKN>(a, st);
     return sepv ? launch_chunk_t<DK, F32IN, true, true, true, QKN>(a, st)
                 : launch_chunk_t<DK, F32IN, true, true, false, QKN>(a, st);
@@ -1165,6 +1201,7 @@ static hipError_t launch_chunk_cg(const ChunkArgs& a, bool cbeta, bool sepv, hip
 
 template <int DK, bool F32IN>
 static hipError_t launch_chunk_d(const ChunkArgs& a, bool cgate, bool cbeta, bool sepv, hipStream_t st) {
+    cgate = cgate || a.key_scale != nullptr;
     if (cgate) return a.qk_norm ? launch_chunk_cg<DK, F32IN, true>(a, cbeta, sepv, st)
                                 : launch_chunk_cg<DK, F32IN, false>(a, cbeta, sepv, st);
     return cbeta ? launch_chunk_t<DK, F32IN, false, true>(a, st)

@@ -2,7 +2,8 @@
 //
 // Optional input preparation (DeltaNet page, step list, step 2 and its notes on
 // the key/query map and on choosing beta): q and k made unit vectors, beta
-// (and beta_v) given as logits.
+// (and beta_v) given as logits.  Optional write-side key scales s (OSDN page,
+// "Method"): the write key is w = s (.) kt, S = S' + w u^T, o = S'^T q + (q . w) u.
 //
 // Per state S (d_k x d_v, fp32) and one new token (FG2-GDN page, section 2,
 // the state-update equation; DeltaNet page, step list, steps 3-6; with a
@@ -30,7 +31,8 @@ namespace dr {
 template <int DK, bool F32IN, bool CGATE, bool CBETA>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int RPT = DK / 16;   // rows per thread
-    __shared__ float sk[DK];       // kt
+    __shared__ float sk[DK];       // kt (the read side)
+    __shared__ float sw[DK];       // the write-side key: kt, or s (.) kt with key scales
     __shared__ float sq[DK];       // q
     __shared__ float sa[DK];       // alpha per row
     __shared__ float red[2][16][64];
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // token vectors: kt = sqrt(beta) k, alpha, q;  q . kt.  With the input
     // preparation, q and k are first made unit vectors: the three sums q . kt,
     // |q|^2 and |k|^2 are reduced together, then the vectors are rescaled.
-    float dotp = 0.f, ssq = 0.f, ssk = 0.f, kt = 0.f, qv = 0.f;
+    float dotp = 0.f, ssq = 0.f, ssk = 0.f, kt = 0.f, qv = 0.f, ksc = 1.f;
     if (tid < DK) {
         const int c = tid;
         const size_t ti = (size_t)sidx * DK + c;
@@ -64,10 +66,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         qv = load1<F32IN>(a.q, ti);
         const float bv = strength(CBETA ? a.beta[ti] : a.beta[sidx], a.beta_logit);
         kt = sqrtf(bv) * kv;
+        if (a.key_scale) ksc = a.key_scale[ti];
         float al = 1.f;
         if (a.has_gate) al = expf(CGATE ? a.log_alpha[ti] : a.log_alpha[sidx]);
         sa[c] = al;
-        dotp = qv * kt;
+        dotp = qv * (kt * ksc);   // q . w
         ssq = qv * qv;
         ssk = kv * kv;
     }
@@ -91,6 +94,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const float qk = (sdot[0][0] + sdot[0][1] + sdot[0][2] + sdot[0][3]) * (rq * rk);
     if (tid < DK) {
         sk[tid] = kt * rk;
+        sw[tid] = (kt * rk) * ksc;
         sq[tid] = qv * rq;
     }
     __syncthreads();
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // column totals, new value u = vt - p, output o = r + (q . kt) u
+    // column totals, new value u = vt - p, output o = r + (q . w) u
     if (tid < 64) {
         const int col = slab * 64 + tid;
         float p = 0.f, r = 0.f;
@@ -138,18 +142,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    // S = Diag(alpha) S + kt u^T, written once
+    // S = Diag(alpha) S + w u^T, written once
     if (colok) {
         const float u0 = su[4 * cg], u1 = su[4 * cg + 1], u2 = su[4 * cg + 2], u3 = su[4 * cg + 3];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int c = rg + 16 * i;
-            const float al = sa[c], kt = sk[c];
+            const float al = sa[c], w = sw[c];
             float4 n;
-            n.x = al * s[i].x + kt * u0;
-            n.y = al * s[i].y + kt * u1;
-            n.z = al * s[i].z + kt * u2;
-            n.w = al * s[i].w + kt * u3;
+            n.x = al * s[i].x + w * u0;
+            n.y = al * s[i].y + w * u1;
+            n.z = al * s[i].z + w * u2;
+            n.w = al * s[i].w + w * u3;
             *reinterpret_cast<float4*>(S + (size_t)c * a.Dv + col0) = n;
         }
     }

@@ -44,7 +44,10 @@ __host__ __device__ constexpr int tri_off(int r, int c) {
 // caller gives a separate one (channel beta only).
 // Input preparation: qk_norm makes every q_t and k_t a unit vector (the zero
 // vector stays zero), beta_logit reads beta (and beta_v) as logits,
-// beta = 1 / (1 + e^{-x}).
+// beta = 1 / (1 + e^{-x}).  key_scale (write-side key scales s_t) makes the
+// write key w = s (.) kt: S_t = (I - w kt^T) Diag(alpha) S + w vt^T; such calls
+// run on the channel-gate path whatever the gate (scalar and absent gates are
+// broadcast to every channel).
 struct ChunkArgs {
     const void* q;
     const void* k;
@@ -60,6 +63,8 @@ struct ChunkArgs {
     int out_bf16;
     int qk_norm;
     int beta_logit;
+    int gate_mode;              // 0 none, 1 scalar, 2 channel
+    const float* key_scale;     // write-side key scales [B][H][L][Dk], or null
     half_t* wsT;
     half_t* wsP;
     float* wsG;
@@ -83,6 +88,7 @@ struct DecodeArgs {
     int out_bf16;
     int qk_norm;      // input preparation, as in ChunkArgs
     int beta_logit;
+    const float* key_scale;   // write-side key scales [N][H][Dk], or null
 };
 
 // Optional per-kernel timing: launchers mark the start of each kernel and the

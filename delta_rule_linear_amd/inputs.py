@@ -87,6 +87,7 @@ class ChunkProblem:
     beta_v: Optional[np.ndarray] = None   # separate write strength (FG2-GDN+), beta's shape
     qk_l2norm: bool = False               # q, k raw: the forward normalises them
     beta_logit: bool = False              # beta (and beta_v) hold logits
+    key_scale: Optional[np.ndarray] = None   # write-side key scales [B, H, L, Dk]
 
     @property
     def token_heads(self) -> int:
@@ -99,20 +100,22 @@ class ChunkProblem:
             f"{self.name}[b={b},h={h}]", 1, 1, self.L, self.Dk, self.Dv, self.in_dtype,
             self.gate, self.beta_mode, sl(self.q), sl(self.k), sl(self.v),
             sl(self.log_alpha), sl(self.beta), sl(self.S0), dict(self.meta), sl(self.beta_v),
-            self.qk_l2norm, self.beta_logit)
+            self.qk_l2norm, self.beta_logit, sl(self.key_scale))
 
 
 def make_chunk_problem(B, H, L, Dk, Dv, *, in_dtype="bf16", gate="scalar", beta_mode="scalar",
                        log_alpha_range=(-0.1, -0.001), s0_var: Optional[float] = None,
                        seed: int = 0, name: str = "custom", beta_v: bool = False,
-                       raw_inputs: bool = False) -> ChunkProblem:
+                       raw_inputs: bool = False, key_scale: bool = False) -> ChunkProblem:
     """Draw one chunked-forward batch following the module recipe.
 
     beta_v=True adds a separate write strength beta^v (FG2-GDN+), drawn like
     beta and after every other tensor, so the rest of the batch is unchanged.
     raw_inputs=True keeps the same draws before their last step: q and k
     are not normalised and the strengths are the logits, for a forward with
-    the input preparation switched on.
+    the input preparation switched on.  key_scale=True adds write-side key
+    scales (a diagonal preconditioner), U(0.5, 1.5) per token and channel,
+    drawn after everything else.
     """
     if gate not in GATES or beta_mode not in BETAS or in_dtype not in DTYPES:
         raise ValueError("unknown mode")
@@ -142,7 +145,8 @@ def make_chunk_problem(B, H, L, Dk, Dv, *, in_dtype="bf16", gate="scalar", beta_
                         None if la is None else la.astype(np.float32),
                         beta.astype(np.float32), S0,
                         {"seed": seed, "log_alpha_range": log_alpha_range, "s0_var": s0_var},
-                        None if bv is None else bv.astype(np.float32), raw_inputs, raw_inputs)
+                        None if bv is None else bv.astype(np.float32), raw_inputs, raw_inputs,
+                        rng.uniform(0.5, 1.5, (B, H, L, Dk)).astype(np.float32) if key_scale else None)
 
 
 # The named workloads.  Gate ranges are U(lo, hi) on log alpha.
@@ -165,6 +169,9 @@ WORKLOADS = {
     # FG2-GDN+: as FG2-GDN with a separate channel-wise write strength beta^v
     "fg2plus_b2h16_16k": dict(B=2, H=16, L=16384, Dk=128, Dv=128, in_dtype="bf16", gate="channel",
                               beta_mode="channel", log_alpha_range=KDA_GATE, s0_var=None, beta_v=True),
+    # the headline GDN shape with write-side key scales (a diagonal preconditioner)
+    "gdn_precond_b2h16_16k": dict(B=2, H=16, L=16384, Dk=128, Dv=128, in_dtype="bf16", gate="scalar",
+                                  beta_mode="scalar", log_alpha_range=GDN_GATE, s0_var=0.01, key_scale=True),
     # long-context GDN prefill, gating as the B=4 GDN workload
     "gdn_b1h16_64k": dict(B=1, H=16, L=65536, Dk=128, Dv=128, in_dtype="bf16", gate="scalar",
                           beta_mode="scalar", log_alpha_range=GDN_GATE, s0_var=0.01),
@@ -201,12 +208,13 @@ class DecodeProblem:
     beta_v: Optional[np.ndarray] = None   # separate write strength (FG2-GDN+), beta's shape
     qk_l2norm: bool = False               # raw q, k and strength logits (see make_decode_problem)
     beta_logit: bool = False
+    key_scale: Optional[np.ndarray] = None   # write-side key scales [steps, N, H, Dk]
 
 
 def make_decode_problem(N=256, H=16, Dk=128, Dv=128, steps=512, *, in_dtype="bf16",
                         gate="scalar", beta_mode="scalar", log_alpha_range=GDN_GATE,
                         s0_var=0.01, seed=0, beta_v: bool = False,
-                        raw_inputs: bool = False) -> DecodeProblem:
+                        raw_inputs: bool = False, key_scale: bool = False) -> DecodeProblem:
     """Decode batch: states first, then each step's tokens, in step order;
     with beta_v=True a separate write strength per step is drawn last, like
     beta, so the other arrays are those of beta_v=False.  raw_inputs=True
@@ -236,4 +244,5 @@ def make_decode_problem(N=256, H=16, Dk=128, Dv=128, steps=512, *, in_dtype="bf1
     return DecodeProblem(N, H, Dk, Dv, steps, in_dtype, gate, beta_mode, S,
                          np.stack(qs), np.stack(ks), np.stack(vs),
                          None if gate == "none" else np.stack(las), np.stack(bs), bv,
-                         raw_inputs, raw_inputs)
+                         raw_inputs, raw_inputs,
+                         rng.uniform(0.5, 1.5, (steps, N, H, Dk)).astype(np.float32) if key_scale else None)

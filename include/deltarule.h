@@ -20,6 +20,13 @@
  *                     kt_t = sqrt(beta^k_t) (.) k_t,  vt_t = sqrt(beta^v_t) (.) v_t
  *                   and the same S_t and o_t.  The page gives no formula; this
  *                   is the reading that reduces to FG2-GDN at beta^v == beta^k.
+ *   preconditioned  a diagonal preconditioner s_t on the delta rule's gradient
+ *                   step (OSDN page, section "Method"; the preconditioned
+ *                   delta rule page, abstract), which amounts to scaling the
+ *                   write-side key per feature; through the *_precond entry
+ *                   points, with s_t an input (its online update is not
+ *                   printed) and w_t = s_t (.) kt_t:
+ *                     S_t = (I - w_t kt_t^T) Diag(alpha_t) S_{t-1} + w_t vt_t^T
  * No query scaling is applied; callers pre-scale q if they want one.
  *
  * Input preparation (optional, descriptor field input_flags), the steps in
@@ -72,7 +79,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 4
+#define DR_ABI_VERSION 5
 
 typedef enum {
     DR_OK = 0,
@@ -171,6 +178,28 @@ dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
                           const float* S0, void* o, float* S_final, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace dr_chunk_fwd_precond needs for `d` (the channel-gate
+ * operand planes are always used; 0 if d is invalid or there is no work). */
+size_t dr_chunk_fwd_precond_workspace_bytes(const dr_chunk_desc* d);
+
+/*
+ * dr_chunk_fwd_precond -- dr_chunk_fwd with a diagonal preconditioner on the
+ * delta rule's gradient step, i.e. write-side key scales (OSDN page, section
+ * "Method"; the preconditioned delta rule page, abstract): with w = s (.) kt,
+ *   S_t = (I - w_t kt_t^T) Diag(alpha_t) S_{t-1} + w_t vt_t^T,  o_t = S_t^T q_t.
+ * s == 1 gives dr_chunk_fwd's recurrence.
+ *
+ *   key_scale  [B][H][L][Dk] fp32, the preconditioner's diagonal per token
+ *   workspace  at least dr_chunk_fwd_precond_workspace_bytes(d) bytes
+ * Every other argument, every mode (gate, beta, dtypes, input_flags) and the
+ * error behaviour are those of dr_chunk_fwd.  Whatever the gate, the call runs
+ * the channel-gate kernels (a scalar or absent gate broadcast per channel).
+ */
+dr_status dr_chunk_fwd_precond(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* key_scale,
+                               const float* S0, void* o, float* S_final, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /*
  * dr_decode_step -- one recurrent step (DeltaNet page, property list: inference
  * uses the recurrent form with a constant-size state) for N x H independent
@@ -204,6 +233,17 @@ dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, 
 dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* k, const void* v,
                             const float* log_alpha, const float* beta_k, const float* beta_v,
                             float* S, void* o, void* stream);
+
+/*
+ * dr_decode_step_precond -- dr_decode_step with write-side key scales (the
+ * preconditioner's diagonal, as in dr_chunk_fwd_precond):
+ *   S[n][h] <- (I - w kt^T) Diag(alpha) S[n][h] + w vt^T,  w = s (.) kt
+ *   key_scale  [N][H][Dk] fp32
+ * Every other argument as for dr_decode_step.
+ */
+dr_status dr_decode_step_precond(const dr_decode_desc* d, const void* q, const void* k, const void* v,
+                                 const float* log_alpha, const float* beta, const float* key_scale,
+                                 float* S, void* o, void* stream);
 
 /*
  * Per-kernel timing, for benchmarks and profiling (not part of the method).

@@ -38,11 +38,13 @@ def to_dev(a, dtype: str, device="cuda"):
 
 def problem_to_dev(p):
     """The problem's tensors on the device, keyed as dr_chunk_fwd's arguments
-    (plus beta_v when the problem has a separate write strength)."""
+    (plus beta_v and key_scale when the problem has them)."""
     t = dict(q=to_dev(p.q, p.in_dtype), k=to_dev(p.k, p.in_dtype), v=to_dev(p.v, p.in_dtype),
              log_alpha=to_dev(p.log_alpha, "f32"), beta=to_dev(p.beta, "f32"), S0=to_dev(p.S0, "f32"))
     if getattr(p, "beta_v", None) is not None:
         t["beta_v"] = to_dev(p.beta_v, "f32")
+    if getattr(p, "key_scale", None) is not None:
+        t["key_scale"] = to_dev(p.key_scale, "f32")
     return t
 
 
@@ -53,6 +55,10 @@ def run_hip(p, out_dtype=None, **kw):
     t = problem_to_dev(p)
     kw.setdefault("qk_l2norm", getattr(p, "qk_l2norm", False))
     kw.setdefault("beta_logit", getattr(p, "beta_logit", False))
+    if "key_scale" in t:
+        return drl.dr_chunk_fwd_precond(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["key_scale"],
+                                        t["S0"], gate=p.gate, beta_mode=p.beta_mode, out_dtype=out_dtype,
+                                        **kw)
     if "beta_v" in t:
         return drl.dr_chunk_fwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"],
                                    t["S0"], gate=p.gate, out_dtype=out_dtype, **kw)

@@ -197,3 +197,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(drl, "_lib", None)
     with pytest.raises(ImportError):
         drl.lib()
+
+
+def test_precond_validation_and_workspace():
+    lib = drl.lib()
+
+    def call(desc, ks=FAKE + 8192, ws=FAKE, wbytes=1 << 40):
+        return lib.dr_chunk_fwd_precond(ctypes.byref(desc) if desc is not None else None, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, ks, None, FAKE, FAKE, ws, wbytes, None)
+
+    d = _desc()
+    assert call(None) == drl.DR_ERR_NULL
+    assert call(d, ks=None) == drl.DR_ERR_NULL
+    assert "key_scale" in drl.dr_last_error()
+    assert call(d, ks=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
+    # the preconditioned forward runs the channel-gate kernels: more workspace
+    # than the scalar-gate forward, the same as the channel-gate one
+    need = drl.dr_chunk_fwd_precond_workspace_bytes(d)
+    assert need > drl.dr_chunk_fwd_workspace_bytes(d)
+    assert need == drl.dr_chunk_fwd_workspace_bytes(_desc(gate="channel"))
+    assert call(d, wbytes=need - 1) == drl.DR_ERR_WORKSPACE
+    assert drl.dr_chunk_fwd_precond_workspace_bytes(_desc(Dk=96)) == 0
+    D = drl.DecodeDesc
+    ok = dict(N=4, H=2, Dk=128, Dv=128, in_dtype=drl.DR_BF16, out_dtype=drl.DR_F32, gate=1, beta=0)
+    dcall = lambda desc, ks=FAKE + 8192: lib.dr_decode_step_precond(
+        ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, ks, FAKE, FAKE, None)
+    assert dcall(D(**ok), ks=None) == drl.DR_ERR_NULL
+    assert dcall(D(**ok), ks=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
+    assert dcall(D(**{**ok, "N": 0})) == drl.DR_OK

@@ -193,6 +193,59 @@ def test_input_prep_full_headline_sampled():
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+# ------------------------------- write-side key scales (diagonal preconditioner)
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate,beta_mode", MODES)
+@pytest.mark.parametrize("L", [65, 200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_precond_sweep(dtype, gate, beta_mode, L, D):
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    p = inputs.make_chunk_problem(1, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
+                                  log_alpha_range=rng, s0_var=0.01, seed=L + D + 3, key_scale=True,
+                                  name=f"precond-{dtype}-{gate}-{beta_mode}-L{L}-D{D}")
+    _check(p, tol=1e-5 if dtype == "f32" else None)
+
+
+@pytest.mark.parametrize("gate,beta_mode", [("scalar", "scalar"), ("channel", "channel")])
+def test_precond_with_input_prep_and_uneven_jobs(gate, beta_mode):
+    # raw inputs and logits, and the persistent preparation loop with a ragged tail
+    p = inputs.make_chunk_problem(1, 5, 64 * 60 + 17, 128, 128, gate=gate, beta_mode=beta_mode,
+                                  log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=16,
+                                  raw_inputs=True, key_scale=True, name=f"precond-prep-{gate}")
+    _check(p)
+
+
+def test_precond_strong_gate_exact_path():
+    p = inputs.make_chunk_problem(1, 2, 128, 128, 128, gate="channel", beta_mode="scalar",
+                                  log_alpha_range=(-3.0, -0.5), seed=17, key_scale=True,
+                                  name="precond-strong-gate")
+    _check(p)
+
+
+@pytest.mark.parametrize("gate,beta_mode", MODES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_precond(gate, beta_mode, dtype):
+    import delta_rule_linear_amd as drl
+    import oracle
+    from gpu_common import to_dev
+    rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
+    dp = inputs.make_decode_problem(5, 3, 128, 128, 4, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
+                                    log_alpha_range=rng, seed=18, key_scale=True)
+    announce("decode precond", gate, beta_mode, dtype)
+    S = to_dev(dp.S, "f32")
+    Sy = dp.S.astype(np.float64)
+    for t in range(dp.steps):
+        la = None if dp.log_alpha is None else dp.log_alpha[t]
+        o = drl.dr_decode_step_precond(S, to_dev(dp.q[t], dtype), to_dev(dp.k[t], dtype),
+                                       to_dev(dp.v[t], dtype), to_dev(la, "f32"), to_dev(dp.beta[t], "f32"),
+                                       to_dev(dp.key_scale[t], "f32"), gate=gate, beta_mode=beta_mode)
+        oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], la, dp.beta[t], gate=gate,
+                                    beta_mode=beta_mode, key_scale=dp.key_scale[t])
+        assert rel_err(to_np(o), oy) <= 1e-5, f"step {t} o"
+    assert rel_err(to_np(S), Sy) <= 1e-5
+
+
 # ---------------------------------------------------------------- full sizes
 
 FULL = {
@@ -202,6 +255,7 @@ FULL = {
     "kda_b2h32_16k": [(0, 0), (1, 31)],
     "fg2_b2h16_16k": [(0, 0), (1, 15)],
     "fg2plus_b2h16_16k": [(0, 3), (1, 12)],
+    "gdn_precond_b2h16_16k": [(0, 5), (1, 10)],
     "gdn_b2h16_16k": [(0, 0), (1, 15)],
     "gdn_b1h16_64k": [(0, 0), (0, 15)],
 }
