@@ -19,7 +19,8 @@ Also reported in the same line:
   decode        512 consecutive dr_decode_step calls on 256 sequences x 16
                 heads of 128x128 fp32 states (bf16 tokens, GDN gating);
   configs       the other forward workloads (FG2-GDN and FG2-GDN+ at the
-                headline shape, KDA, GDN at L=4K and 64K), a few steps each;
+                headline shape, KDA, GDN at L=4K and 64K, GDN with the input
+                preparation and with write-side key scales), a few steps each;
   cpu_baseline  the fp64 CPU oracle on the whole headline batch, on the
                 host's cores, with the GPU result checked against it.
 The headline inputs follow the seeded NumPy recipe of
@@ -258,16 +259,19 @@ def main():
     # ------------------------------------------------------------ other forward workloads
     configs = {}
     extra = [
-        ("fg2_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, False, False),
-        ("fg2plus_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, True, False),
-        ("kda_b2h32_16k", 2, 32, 16384, "channel", "scalar", (-0.2, -0.0005), False, False, False),
-        ("gdn_b4h16_4k", 4, 16, 4096, "scalar", "scalar", (-0.1, -0.001), True, False, False),
-        ("gdn_b1h16_64k", 1, 16, 65536, "scalar", "scalar", (-0.1, -0.001), True, False, False),
+        ("fg2_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, False, False, False),
+        ("fg2plus_b2h16_16k", 2, 16, 16384, "channel", "channel", (-0.2, -0.0005), False, True, False, False),
+        ("kda_b2h32_16k", 2, 32, 16384, "channel", "scalar", (-0.2, -0.0005), False, False, False, False),
+        ("gdn_b4h16_4k", 4, 16, 4096, "scalar", "scalar", (-0.1, -0.001), True, False, False, False),
+        ("gdn_b1h16_64k", 1, 16, 65536, "scalar", "scalar", (-0.1, -0.001), True, False, False, False),
         # the headline shape with raw q, k and beta logits: the kernels normalise
         # and apply the sigmoid
-        ("gdn_b2h16_16k_input_prep", 2, 16, 16384, "scalar", "scalar", (-0.1, -0.001), True, False, True),
+        ("gdn_b2h16_16k_input_prep", 2, 16, 16384, "scalar", "scalar", (-0.1, -0.001), True, False, True, False),
+        # the headline shape with write-side key scales U(0.5, 1.5) (a diagonal
+        # preconditioner on the gradient step)
+        ("gdn_precond_b2h16_16k", 2, 16, 16384, "scalar", "scalar", (-0.1, -0.001), True, False, False, True),
     ]
-    for name, b_, h_, l_, gate, bmode, rng, s0, sepv, prep in (extra if args.config_steps > 0 else []):
+    for name, b_, h_, l_, gate, bmode, rng, s0, sepv, prep, ks in (extra if args.config_steps > 0 else []):
         gen.manual_seed(0)
         xq = torch.randn((b_, h_, l_, D), generator=gen, device=dev)
         xk = torch.randn((b_, h_, l_, D), generator=gen, device=dev)
@@ -281,14 +285,19 @@ def main():
         xS0 = torch.randn((b_, h_, D, D), generator=gen, device=dev) * 0.1 if s0 else None
         # separate write strength (FG2-GDN+), drawn like beta
         xbv = torch.sigmoid(torch.randn(bshape, generator=gen, device=dev)) if sepv else None
+        xks = torch.rand((b_, h_, l_, D), generator=gen, device=dev) + 0.5 if ks else None
         xo = torch.empty((b_, h_, l_, D), dtype=torch.float32, device=dev)
         xSf = torch.empty((b_, h_, D, D), dtype=torch.float32, device=dev)
         xdesc = drl.chunk_desc(b_, h_, l_, D, D, drl.DR_BF16, drl.DR_F32, gate, bmode,
                                drl.input_flags(prep, prep))
-        xws = torch.empty(drl.dr_chunk_fwd_workspace_bytes(xdesc), dtype=torch.uint8, device=dev)
+        xws = torch.empty(drl.dr_chunk_fwd_precond_workspace_bytes(xdesc) if ks
+                          else drl.dr_chunk_fwd_workspace_bytes(xdesc), dtype=torch.uint8, device=dev)
 
         def xstep():
-            if xbv is not None:
+            if xks is not None:
+                drl.dr_chunk_fwd_precond(xq, xk, xv, xla, xbe, xks, xS0, gate=gate, beta_mode=bmode, o=xo,
+                                         S_final=xSf, workspace=xws)
+            elif xbv is not None:
                 drl.dr_chunk_fwd_kv(xq, xk, xv, xla, xbe, xbv, xS0, gate=gate, o=xo, S_final=xSf,
                                     workspace=xws)
             else:
@@ -318,17 +327,19 @@ def main():
         configs[name] = {
             "shape": f"B={b_} H={h_} L={l_} d={D}, gate {gate}, beta {bmode}"
                      + (", separate write strength" if sepv else "")
-                     + (", q/k L2 normalisation and beta sigmoid in the kernels" if prep else ""),
+                     + (", q/k L2 normalisation and beta sigmoid in the kernels" if prep else "")
+                     + (", write-side key scales (diagonal preconditioner)" if ks else ""),
             "ms_per_step": round(xms, 4), "tokens_per_s": round(b_ * l_ / (xms * 1e-3), 1),
             "prep_ms": round(xprof["prep_ms"] / calls, 4), "scan_ms": round(xprof["scan_ms"] / calls, 4),
             "mfma_frac": round(flops_per_token_head(D) * th / (xms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
             "hbm_frac": round(fwd_bytes_per_token_head(D, l_, 2, 1 if gate == "scalar" else D,
-                                                       (1 if bmode == "scalar" else D) * (2 if sepv else 1))
+                                                       (1 if bmode == "scalar" else D) * (2 if sepv else 1)
+                                                       + (D if ks else 0))
                               * th
                               / (xms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         if unfused is not None:
             configs[name]["ms_with_torch_preparation"] = unfused
-        del xq, xk, xv, xla, xbe, xbv, xS0, xo, xSf, xws
+        del xq, xk, xv, xla, xbe, xbv, xks, xS0, xo, xSf, xws
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline (oracle)
