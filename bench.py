@@ -79,7 +79,8 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (50 bring the clocks to their steady state)")
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--config-steps", type=int, default=5,
                     help="timed steps per extra workload (0 skips them)")
