@@ -9,7 +9,9 @@ L2-normalised, bf16 q/k/v, fp32 S0 ~ N(0, 0.01), fp32 output), B=2, H=16,
 L=16384, d_k=d_v=128.  `value` is tokens/s of that step (B*L per step), from
 HIP events around each step on the launch stream; between steps (outside the
 timed events) a 512 MiB buffer is rewritten so that no input is served from
-the 256 MB last-level cache.
+the 256 MB last-level cache.  Before the W warm-up steps the step runs
+untimed for --warmup-seconds, so that a fresh GPU has reached its steady
+clocks.
 
 Also reported in the same line:
   roofline      the dominant kernel (the state scan) against HBM bandwidth,
@@ -79,8 +81,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps first (50 bring the clocks to their steady state)")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup-seconds", type=float, default=1.5,
+                    help="untimed load before the warm-up steps, so that a fresh GPU reaches steady clocks")
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--config-steps", type=int, default=5,
                     help="timed steps per extra workload (0 skips them)")
@@ -175,6 +178,13 @@ def main():
         drl.dr_chunk_fwd(q, k, v, la, be, S0, gate="scalar", beta_mode="scalar", o=o, S_final=Sf,
                          workspace=ws)
 
+    # untimed: the step repeated for --warmup-seconds (a fresh GPU takes about a
+    # second of load to reach its steady clocks), then --warmup steps
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < args.warmup_seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
