@@ -216,6 +216,26 @@ def test_precond_with_input_prep_and_uneven_jobs(gate, beta_mode):
     _check(p)
 
 
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("Dv", [48, 256])
+def test_precond_and_channel_gate_value_widths(gate, Dv):
+    # d_v != d_k on the channel-gate kernels (key scales, and KDA-style gates)
+    for ks in (True, False):
+        if gate != "channel" and not ks:
+            continue
+        p = inputs.make_chunk_problem(1, 3, 130, 128, Dv, gate=gate, beta_mode="scalar",
+                                      log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=19, key_scale=ks,
+                                      name=f"width-{gate}-dv{Dv}-ks{int(ks)}")
+        _check(p)
+
+
+def test_precond_bf16_output():
+    p = inputs.make_chunk_problem(1, 3, 200, 128, 128, gate="scalar", beta_mode="scalar",
+                                  log_alpha_range=(-0.1, -0.001), s0_var=0.01, seed=20, key_scale=True,
+                                  name="precond-bf16-out")
+    _check(p, out_dtype=torch.bfloat16, tol=TOL["bf16"] + 2 ** -9)
+
+
 def test_precond_strong_gate_exact_path():
     p = inputs.make_chunk_problem(1, 2, 128, 128, 128, gate="channel", beta_mode="scalar",
                                   log_alpha_range=(-3.0, -0.5), seed=17, key_scale=True,
