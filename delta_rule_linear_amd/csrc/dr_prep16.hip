@@ -79,31 +79,38 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, size_t pitch, int 
 
 }  // namespace
 
-// LDS plan (bytes): k tile, q tile, A (fp32), gates.  T (fp32) and the
-// per-wave 16 x 16 scratch of the triangular solve reuse the k / q tiles,
-// which are dead once A and P are formed (d = 128; at d = 64 the tiles are
-// too small and T follows the gates); P goes straight to the workspace.
-// 49.9 KB at d = 128: three workgroups per CU.
+// LDS plan (bytes): k tile, q tile, gates.  A (fp32, its ten lower 16 x 16
+// blocks packed with a row pitch of 17), T (fp32) and the per-wave 16 x 16
+// scratch of the triangular solve reuse the k / q tiles, which are dead once
+// A and P are formed (the waves hold their A blocks in registers until then);
+// at d = 64 the tiles are too small and A, T and the scratch follow them.  P
+// goes straight to the workspace.  33 KB at d = 128: four workgroups per CU.
 template <int DK>
 struct P16 {
     static constexpr int RB = DK * 2;
     static constexpr int KT = 0;
     static constexpr int QT = KT + 64 * RB;
-    static constexpr int AP = 65;                 // fp32 pitch of A and T
-    static constexpr int SA = QT + 64 * RB;
-    static constexpr int SG = SA + 64 * AP * 4;   // G[64], beta[64], 1/|q|[64], 1/|k|[64]
-    static constexpr int TX = 64 * AP * 4 + 4 * 16 * 17 * 4;   // T and the scratch
-    static constexpr bool ALIAS = TX <= 2 * 64 * RB;            // they fit in the tiles
-    static constexpr int ST = ALIAS ? KT : SG + 256 * 4;
+    static constexpr int AP = 65;                 // fp32 pitch of T
+    static constexpr int AB = 16 * 17;            // floats per packed A block
+    static constexpr int ABYTES = 10 * AB * 4;
+    static constexpr int TXA = ABYTES + 64 * AP * 4 + 4 * 16 * 17 * 4;   // A, T and the scratch
+    static constexpr bool ALIAS = TXA <= 2 * 64 * RB;                    // they fit in the tiles
+    static constexpr int SA = ALIAS ? KT : QT + 64 * RB;
+    static constexpr int ST = SA + ABYTES;
     static constexpr int SX = ST + 64 * AP * 4;   // [4][16][17] fp32
-    static constexpr int TOTAL = ALIAS ? SG + 256 * 4 : SX + 4 * 16 * 17 * 4;
+    static constexpr int SG = ALIAS ? QT + 64 * RB : SX + 4 * 16 * 17 * 4;   // G, beta, 1/|q|, 1/|k| [64] each
+    static constexpr int TOTAL = SG + 256 * 4;
 };
 
 template <int DK>
-__global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void prep16_kernel(ChunkArgs a) {
     using L = P16<DK>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    float(*sA)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::SA);
+    float* sAp = reinterpret_cast<float*>(smem + L::SA);
+    // element (r, c), c <= r rounded to blocks, of the packed A
+    auto A_at = [&](int r, int c) -> float& {
+        return sAp[tri_block(r >> 4, c >> 4) * L::AB + (r & 15) * 17 + (c & 15)];
+    };
     float(*sT)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::ST);
     float* sg = reinterpret_cast<float*>(smem + L::SG);
     float* sb = sg + 64;
@@ -198,7 +205,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
     // e^{G_r - G_i}; the pairs of a wave share the block row R, so its k_R and
     // q_R fragments are read once: wave 0 takes (3, 0..2), wave 1 (2, 0..2),
     // wave 2 (1, 0..1), wave 3 (0, 0) and (3, 3).
-    auto pair_group = [&](const int R, const int I0, const int NI) {
+    float areg[3][4];   // this wave's A values (pair slot, row j) until the tiles are dead
+    auto pair_group = [&](const int R, const int I0, const int NI, const int slot0) {
         f32x4 accA[3], accP[3];
 #pragma unroll
         for (int t = 0; t < 3; ++t) accA[t] = accP[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
                     const float qr = R == 0 ? qrow[0][j] : R == 1 ? qrow[1][j] : R == 2 ? qrow[2][j] : qrow[3][j];
                     const float f = __builtin_amdgcn_exp2f(gr - gi);   // e^{G_r - G_i} <= 1
                     const bool live = r < Lc;
-                    sA[r][i] = (live && i < r) ? accA[t][j] * f * br * ki : 0.f;
+                    areg[slot0 + t][j] = (live && i < r) ? accA[t][j] * f * br * ki : 0.f;
                     // P to the workspace, packed: 16 lanes write one 32-byte block row
                     a.wsP[cs * (size_t)(CH * CH) + tri_off(r, i)] =
                         (half_t)((live && i <= r) ? accP[t][j] * f * qr * ki : 0.f);
@@ -240,12 +248,27 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             }
         }
     };
-    if (w == 0) pair_group(3, 0, 3);
-    else if (w == 1) pair_group(2, 0, 3);
-    else if (w == 2) pair_group(1, 0, 2);
+    auto write_a = [&](const int R, const int I0, const int NI, const int slot0) {
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            if (t < NI)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) A_at(16 * R + 4 * g + j, 16 * (I0 + t) + i16) = areg[slot0 + t][j];
+    };
+    if (w == 0) pair_group(3, 0, 3, 0);
+    else if (w == 1) pair_group(2, 0, 3, 0);
+    else if (w == 2) pair_group(1, 0, 2, 0);
     else {
-        pair_group(0, 0, 1);
-        pair_group(3, 3, 1);
+        pair_group(0, 0, 1, 0);
+        pair_group(3, 3, 1, 1);
+    }
+    if constexpr (L::ALIAS) __syncthreads();   // the tiles are dead: A may take their place
+    if (w == 0) write_a(3, 0, 3, 0);
+    else if (w == 1) write_a(2, 0, 3, 0);
+    else if (w == 2) write_a(1, 0, 2, 0);
+    else {
+        write_a(0, 0, 1, 0);
+        write_a(3, 3, 1, 1);
     }
     __syncthreads();
 
@@ -262,7 +285,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             t[i] = (i == j ? 1.f : 0.f) - acc[i];
             if (i < j) t[i] = 0.f;
 #pragma unroll
-            for (int r = i + 1; r < 16; ++r) acc[r] += sA[base + r][base + i] * t[i];
+            for (int r = i + 1; r < 16; ++r) acc[r] += A_at(base + r, base + i) * t[i];
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[base + r][base + j] = t[r];
@@ -296,8 +319,8 @@ __global__ __launch_bounds__(256) void prep16_kernel(ChunkArgs a) {
             f32x4 X0 = {0.f, 0.f, 0.f, 0.f}, X1 = X0;
             for (int s = 0; s < 4 * (R - I); s += 2) {
                 const int m = 16 * I + 4 * s + g;
-                X0 = mfma_f32x4(sA[16 * R + i16][m], sT[m][16 * I + i16], X0);
-                X1 = mfma_f32x4(sA[16 * R + i16][m + 4], sT[m + 4][16 * I + i16], X1);
+                X0 = mfma_f32x4(A_at(16 * R + i16, m), sT[m][16 * I + i16], X0);
+                X1 = mfma_f32x4(A_at(16 * R + i16, m + 4), sT[m + 4][16 * I + i16], X1);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) sX[w][4 * g + j][i16] = X0[j] + X1[j];
