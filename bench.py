@@ -178,11 +178,13 @@ def main():
         drl.dr_chunk_fwd(q, k, v, la, be, S0, gate="scalar", beta_mode="scalar", o=o, S_final=Sf,
                          workspace=ws)
 
-    # untimed: the step repeated for --warmup-seconds (a fresh GPU takes about a
-    # second of load to reach its steady clocks), then --warmup steps
+    # untimed: the step repeated for --warmup-seconds, each after a cache
+    # rewrite like the timed ones (a fresh GPU needs this sustained load, cache
+    # rewrites included, before its step times settle), then --warmup steps
     t_warm = time.perf_counter()
     while time.perf_counter() - t_warm < args.warmup_seconds:
         for _ in range(20):
+            flush()
             step()
         torch.cuda.synchronize()
     for _ in range(args.warmup):
