@@ -19,7 +19,8 @@ Also reported in the same line:
                 library during the timed steps;
   mfma          the whole forward's algorithmic flops against bf16 MFMA peak;
   decode        512 consecutive dr_decode_step calls on 256 sequences x 16
-                heads of 128x128 fp32 states (bf16 tokens, GDN gating);
+                heads of 128x128 fp32 states (bf16 tokens, GDN gating), and
+                per-kernel times of the other gating modes on that batch;
   configs       the other forward workloads (FG2-GDN and FG2-GDN+ at the
                 headline shape, KDA, GDN at L=4K and 64K, GDN with the input
                 preparation and with write-side key scales), a few steps each;
@@ -268,6 +269,45 @@ def main():
                "hbm_frac": round(dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                "alg_bytes_per_step": dbytes}
         del S, dq, dk, dv_, dla, dbe, do
+
+        # the other gating modes, 64 steps each on the same batch shape (per-kernel
+        # events; bytes as above plus the channel-wise gate and beta / key scales)
+        dec["modes"] = {}
+        gen.manual_seed(1)
+        S = torch.randn((N, Hd, D, D), generator=gen, device=dev) * 0.1
+        q1 = l2n(torch.randn((N, Hd, D), generator=gen, device=dev)).bfloat16()
+        k1 = l2n(torch.randn((N, Hd, D), generator=gen, device=dev)).bfloat16()
+        v1 = torch.randn((N, Hd, D), generator=gen, device=dev).bfloat16()
+        lac = torch.rand((N, Hd, D), generator=gen, device=dev) * 0.1995 - 0.2
+        bec = torch.sigmoid(torch.randn((N, Hd, D), generator=gen, device=dev))
+        bvc = torch.sigmoid(torch.randn((N, Hd, D), generator=gen, device=dev))
+        ksc = torch.rand((N, Hd, D), generator=gen, device=dev) + 0.5
+        las, bes = lac[..., 0].contiguous(), bec[..., 0].contiguous()
+        o1 = torch.empty((N, Hd, D), dtype=torch.float32, device=dev)
+        modes = {
+            "kda (channel gate)": (lambda: drl.dr_decode_step(S, q1, k1, v1, lac, bes, gate="channel",
+                                                              beta_mode="scalar", o=o1), 4 * D),
+            "fg2 (channel gate and beta)": (lambda: drl.dr_decode_step(S, q1, k1, v1, lac, bec, gate="channel",
+                                                                       beta_mode="channel", o=o1), 8 * D),
+            "fg2plus (separate write strength)": (lambda: drl.dr_decode_step_kv(S, q1, k1, v1, lac, bec, bvc,
+                                                                                gate="channel", o=o1), 12 * D),
+            "gdn with key scales": (lambda: drl.dr_decode_step_precond(S, q1, k1, v1, las, bes, ksc, gate="scalar",
+                                                                       beta_mode="scalar", o=o1), 4 * D),
+        }
+        for mname, (mstep, extra_b) in modes.items():
+            for _ in range(3):
+                mstep()
+            torch.cuda.synchronize()
+            drl.dr_profile_begin()
+            for _ in range(64):
+                mstep()
+            mprof = drl.dr_profile_end()
+            mk = mprof["decode_ms"] / max(1, mprof["decode_calls"])
+            mbytes = (decode_bytes_per_state(D) + extra_b) * N * Hd
+            dec["modes"][mname] = {"kernel_us_mean": round(mk * 1e3, 2),
+                                   "GB_per_s": round(mbytes / (mk * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(mbytes / (mk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del S, q1, k1, v1, lac, bec, bvc, ksc, las, bes, o1
 
     # ------------------------------------------------------------ other forward workloads
     configs = {}
