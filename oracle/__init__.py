@@ -17,6 +17,8 @@ Optional input preparation in front of it (DeltaNet page, step list, step 2
 and its notes on the key/query map and on choosing beta): qk_l2norm replaces q
 and k by unit vectors (a zero vector stays zero); beta_logit takes the
 strength arrays as logits, beta = sigmoid(x).
+backward() gives the gradients of the one-strength forward (reverse-mode
+differentiation of the token recurrence; the pages print no backward).
 Write-side key scaling (OSDN page, "Method"; the preconditioned delta rule
 page, abstract): a diagonal preconditioner s_t on the gradient step, given as
 an input; the write key is w = s * kt:
@@ -66,6 +68,9 @@ def load(path: str = LIB_PATH):
                                                         ctypes.c_int, dp, ctypes.c_int, dp, dp, dp,
                                                         ctypes.c_int]
     lib.dro_forward_ex.restype = ctypes.c_int
+    lib.dro_backward.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp, ctypes.c_int, dp, dp,
+                                                      dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.dro_backward.restype = ctypes.c_int
     lib.dro_max_threads.restype = ctypes.c_int
     return lib
 
@@ -131,6 +136,36 @@ def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
     if rc != 0:
         raise ValueError(f"dro_forward rejected its arguments (code {rc})")
     return o, Sf
+
+
+def backward(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, beta_mode: str,
+             nthreads: int = 0, lib=None):
+    """Gradients of the forward (one strength, inputs as given) for the loss
+    whose gradients with respect to o and S_final are dO and dS_final.
+    Returns a dict with dq, dk, dv, dlog_alpha (None for gate "none"), dbeta
+    and dS0, in fp64 and in the inputs' shapes."""
+    lib = lib or _get()
+    q = np.asarray(q)
+    B, H, L, Dk = q.shape
+    Dv = np.asarray(v).shape[-1]
+    qa, qp = _f64(q)
+    ka, kp = _f64(k)
+    va, vp = _f64(v)
+    la, lp = _f64(log_alpha)
+    ba, bp = _f64(beta)
+    sa, sp = _f64(S0)
+    da, dp_ = _f64(dO)
+    fa, fp = _f64(dS_final)
+    out = {"dq": np.empty((B, H, L, Dk)), "dk": np.empty((B, H, L, Dk)), "dv": np.empty((B, H, L, Dv)),
+           "dlog_alpha": None if log_alpha is None else np.empty(np.shape(log_alpha)),
+           "dbeta": np.empty(np.shape(beta)), "dS0": np.empty((B, H, Dk, Dv))}
+    ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    rc = lib.dro_backward(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp, BETA_CODES[beta_mode], sp,
+                          dp_, fp, ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]), ptr(out["dlog_alpha"]),
+                          ptr(out["dbeta"]), ptr(out["dS0"]), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"dro_backward rejected its arguments (code {rc})")
+    return out
 
 
 def forward_problem(p, nthreads: int = 0, lib=None):

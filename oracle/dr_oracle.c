@@ -240,6 +240,184 @@ int dro_forward(int B, int H, int L, int Dk, int Dv,
                           S_final, nthreads);
 }
 
+/*
+ * dro_backward -- gradients of the forward above (one strength, no key scales,
+ * inputs as given) by reverse-mode differentiation of the token recurrence.
+ * The pages give no backward (the DeltaNet page, step 7, only says training
+ * uses the chunkwise form); this is the chain rule applied to the update as
+ * written, in the order of the forward's steps:
+ *   S' = Diag(alpha) S_{t-1},  p = S'^T kt,  u = vt - p,
+ *   S_t = S' + kt u^T,  o_t = S_t^T q_t.
+ * With G the gradient of the loss with respect to S_t (dS_final for t = L,
+ * plus q_t do_t^T from the output):
+ *   dq_t = S_t do_t,   dvt = G^T kt,   dkt = G u - S' dvt,
+ *   dS' = G - kt dvt^T,   dalpha_c = sum_j dS'_cj S_{t-1,cj},
+ *   G <- Diag(alpha) dS'   (the gradient with respect to S_{t-1}),
+ * then through kt = sqrt(beta) k, vt = sqrt(beta) v and alpha = e^{log alpha}.
+ *   dO        [B][H][L][Dv]  gradient of the loss with respect to o
+ *   dS_final  [B][H][Dk][Dv] with respect to S_final, or NULL (zero)
+ *   dq, dk    [B][H][L][Dk]  out;  dv [B][H][L][Dv] out
+ *   dlog_alpha  out, log_alpha's shape, or NULL (gate NONE)
+ *   dbeta     out, beta's shape (the derivative of sqrt at 0 is infinite:
+ *             beta > 0 is assumed)
+ *   dS0       [B][H][Dk][Dv] out, or NULL
+ */
+int dro_backward(int B, int H, int L, int Dk, int Dv,
+                 const double* q, const double* k, const double* v,
+                 const double* log_alpha, int gate, const double* beta, int beta_mode,
+                 const double* S0, const double* dO, const double* dS_final,
+                 double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta, double* dS0,
+                 int nthreads)
+{
+    if (B <= 0 || H <= 0 || L < 0 || Dk <= 0 || Dv <= 0) return DRO_EINVAL;
+    if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return DRO_EINVAL;
+    if (gate < DRO_GATE_NONE || gate > DRO_GATE_CHANNEL) return DRO_EINVAL;
+    if (beta_mode != DRO_BETA_SCALAR && beta_mode != DRO_BETA_CHANNEL) return DRO_EINVAL;
+    if ((gate == DRO_GATE_NONE) != (log_alpha == NULL)) return DRO_EINVAL;
+    if (gate != DRO_GATE_NONE && !dlog_alpha) return DRO_EINVAL;
+    if (beta_mode == DRO_BETA_CHANNEL && Dv != Dk) return DRO_EINVAL;
+
+    const long nseq = (long)B * H;
+    const size_t sz = (size_t)Dk * Dv;
+    int err = DRO_OK;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (long s = 0; s < nseq; ++s) {
+        /* the states S_0 .. S_L, then the working arrays */
+        double* St = (double*)malloc(sizeof(double) * ((size_t)(L + 1) * sz + 2 * sz + 4 * (size_t)Dk + 4 * (size_t)Dv));
+        if (!St) {
+            err = DRO_ENOMEM;
+            continue;
+        }
+        double* G = St + (size_t)(L + 1) * sz;
+        double* Sp = G + sz;
+        double* kt = Sp + sz;
+        double* al = kt + Dk;
+        double* sbk = al + Dk;
+        double* dkt = sbk + Dk;
+        double* vt = dkt + Dk;
+        double* u = vt + Dv;
+        double* dvt = u + Dv;
+        double* sbv = dvt + Dv;
+        const size_t lw = (gate == DRO_GATE_CHANNEL) ? (size_t)L * Dk : (size_t)L;
+        const size_t bw = (beta_mode == DRO_BETA_CHANNEL) ? (size_t)L * Dk : (size_t)L;
+        const double* qs = q + (size_t)s * L * Dk;
+        const double* ks_ = k + (size_t)s * L * Dk;
+        const double* vs = v + (size_t)s * L * Dv;
+        const double* las = log_alpha ? log_alpha + (size_t)s * lw : NULL;
+        const double* bs = beta + (size_t)s * bw;
+        double* tmp_o = (double*)malloc(sizeof(double) * ((size_t)L * Dv + 2 * (size_t)Dk + (size_t)Dv + 1));
+        if (!tmp_o) {
+            free(St);
+            err = DRO_ENOMEM;
+            continue;
+        }
+        /* forward, keeping every state */
+        if (S0) memcpy(St, S0 + (size_t)s * sz, sizeof(double) * sz);
+        else memset(St, 0, sizeof(double) * sz);
+        {
+            double* ktmp = tmp_o + (size_t)L * Dv;
+            double* vtmp = ktmp + Dk;
+            double* ptmp = vtmp + Dv;
+            for (int t = 0; t < L; ++t) {
+                memcpy(St + (size_t)(t + 1) * sz, St + (size_t)t * sz, sizeof(double) * sz);
+                run_sequence(1, Dk, Dv, qs + (size_t)t * Dk, ks_ + (size_t)t * Dk, vs + (size_t)t * Dv,
+                             las ? las + (gate == DRO_GATE_CHANNEL ? (size_t)t * Dk : (size_t)t) : NULL, gate,
+                             bs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t),
+                             bs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,
+                             NULL, 0, St + (size_t)(t + 1) * sz, tmp_o + (size_t)t * Dv, ktmp, vtmp, ptmp);
+            }
+        }
+        /* reverse */
+        if (dS_final) memcpy(G, dS_final + (size_t)s * sz, sizeof(double) * sz);
+        else memset(G, 0, sizeof(double) * sz);
+        for (int t = L - 1; t >= 0; --t) {
+            const double* qt = qs + (size_t)t * Dk;
+            const double* k_t = ks_ + (size_t)t * Dk;
+            const double* v_t = vs + (size_t)t * Dv;
+            const double* dot = dO + ((size_t)s * L + t) * Dv;
+            const double* Sprev = St + (size_t)t * sz;
+            const double* Snew = St + (size_t)(t + 1) * sz;
+            for (int c = 0; c < Dk; ++c) {
+                const double b = beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + c];
+                sbk[c] = sqrt(b);
+                kt[c] = sbk[c] * k_t[c];
+                al[c] = gate == DRO_GATE_NONE ? 1.0
+                      : gate == DRO_GATE_SCALAR ? exp(las[t]) : exp(las[(size_t)t * Dk + c]);
+            }
+            for (int j = 0; j < Dv; ++j) {
+                const double b = beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + j];
+                sbv[j] = sqrt(b);
+                vt[j] = sbv[j] * v_t[j];
+            }
+            /* S' and u = vt - S'^T kt */
+            for (int c = 0; c < Dk; ++c)
+                for (int j = 0; j < Dv; ++j) Sp[(size_t)c * Dv + j] = al[c] * Sprev[(size_t)c * Dv + j];
+            for (int j = 0; j < Dv; ++j) {
+                double pj = 0.0;
+                for (int c = 0; c < Dk; ++c) pj += Sp[(size_t)c * Dv + j] * kt[c];
+                u[j] = vt[j] - pj;
+            }
+            /* the output: G += q do^T, dq = S_t do */
+            for (int c = 0; c < Dk; ++c) {
+                double a = 0.0;
+                for (int j = 0; j < Dv; ++j) {
+                    G[(size_t)c * Dv + j] += qt[c] * dot[j];
+                    a += Snew[(size_t)c * Dv + j] * dot[j];
+                }
+                dq[((size_t)s * L + t) * Dk + c] = a;
+            }
+            /* dvt = G^T kt;  dkt = G u - S' dvt */
+            for (int j = 0; j < Dv; ++j) {
+                double a = 0.0;
+                for (int c = 0; c < Dk; ++c) a += G[(size_t)c * Dv + j] * kt[c];
+                dvt[j] = a;
+            }
+            for (int c = 0; c < Dk; ++c) {
+                double a = 0.0;
+                for (int j = 0; j < Dv; ++j) a += G[(size_t)c * Dv + j] * u[j] - Sp[(size_t)c * Dv + j] * dvt[j];
+                dkt[c] = a;
+            }
+            /* dS' = G - kt dvt^T;  dalpha;  G <- Diag(alpha) dS' */
+            double dla_s = 0.0;
+            for (int c = 0; c < Dk; ++c) {
+                double da = 0.0;
+                for (int j = 0; j < Dv; ++j) {
+                    const double g = G[(size_t)c * Dv + j] - kt[c] * dvt[j];
+                    da += g * Sprev[(size_t)c * Dv + j];
+                    G[(size_t)c * Dv + j] = al[c] * g;
+                }
+                /* d/dlog alpha = alpha d/dalpha */
+                if (gate == DRO_GATE_CHANNEL) dlog_alpha[((size_t)s * L + t) * Dk + c] = al[c] * da;
+                dla_s += al[c] * da;
+            }
+            if (gate == DRO_GATE_SCALAR) dlog_alpha[(size_t)s * L + t] = dla_s;
+            /* through kt = sqrt(beta) k and vt = sqrt(beta) v */
+            double db_s = 0.0;
+            for (int c = 0; c < Dk; ++c) {
+                dk[((size_t)s * L + t) * Dk + c] = sbk[c] * dkt[c];
+                const double g = dkt[c] * k_t[c] / (2.0 * sbk[c]);
+                if (beta_mode == DRO_BETA_CHANNEL) dbeta[((size_t)s * L + t) * Dk + c] = g;
+                db_s += g;
+            }
+            for (int j = 0; j < Dv; ++j) {
+                dv[((size_t)s * L + t) * Dv + j] = sbv[j] * dvt[j];
+                const double g = dvt[j] * v_t[j] / (2.0 * sbv[j]);
+                if (beta_mode == DRO_BETA_CHANNEL) dbeta[((size_t)s * L + t) * Dk + j] += g;
+                db_s += g;
+            }
+            if (beta_mode == DRO_BETA_SCALAR) dbeta[(size_t)s * L + t] = db_s;
+        }
+        if (dS0) memcpy(dS0 + (size_t)s * sz, G, sizeof(double) * sz);
+        free(tmp_o);
+        free(St);
+    }
+    (void)nthreads;
+    return err;
+}
+
 /* Threads the OpenMP runtime would use by default (1 without OpenMP). */
 int dro_max_threads(void)
 {

@@ -616,3 +616,66 @@ def pin_ks_unit_and_zero_scales(fwd_ks):
 
 
 KS_PINS = [pin_ks_dense_product, pin_ks_preconditioned_gradient_step, pin_ks_unit_and_zero_scales]
+
+
+# ---------------------------------------------------------------------------
+# The backward (gradients of the one-strength forward).  Each pin takes
+# fwd(q, k, v, la, beta, S0, *, gate, beta_mode) -> (o, S_final) and
+# bwd(q, k, v, la, beta, S0, dO, dS_final, *, gate, beta_mode) -> dict.
+# ---------------------------------------------------------------------------
+
+def _bwd_case(salt, gate, beta_mode, L=7, Dk=5, Dv=5):
+    q, k, v, la, beta, S0 = random_case(salt, L=L, Dk=Dk, Dv=Dv, gate=gate, beta_mode=beta_mode)
+    beta = 0.2 + 0.7 * beta   # away from 0, where sqrt has no derivative
+    r = _rng(salt + 1000)
+    Wo = r.standard_normal((1, 2, L, Dv))
+    WS = r.standard_normal((1, 2, Dk, Dv))
+    return q, k, v, la, beta, S0, Wo, WS
+
+
+def pin_bwd_directional_derivatives(fwd, bwd):
+    """For the loss <Wo, o> + <WS, S_final>, the gradients' inner product with
+    a random direction, for each input alone and for all at once, equals the
+    central difference of the loss along that direction."""
+    salt = 200
+    for gate in ("none", "scalar", "channel"):
+        for beta_mode in ("scalar", "channel"):
+            salt += 1
+            q, k, v, la, beta, S0, Wo, WS = _bwd_case(salt, gate, beta_mode)
+            kw = dict(gate=gate, beta_mode=beta_mode)
+            g = bwd(q, k, v, la, beta, S0, Wo, WS, **kw)
+            x = dict(q=q, k=k, v=v, la=la, beta=beta, S0=S0)
+            grads = dict(q=g["dq"], k=g["dk"], v=g["dv"], la=g["dlog_alpha"], beta=g["dbeta"], S0=g["dS0"])
+            r = _rng(salt + 2000)
+            dirs = {n: (None if a is None else r.standard_normal(a.shape)) for n, a in x.items()}
+
+            def loss(xx):
+                o, S = fwd(xx["q"], xx["k"], xx["v"], xx["la"], xx["beta"], xx["S0"], **kw)
+                return float(np.sum(Wo * o) + np.sum(WS * S))
+
+            for which in [[n] for n in x if x[n] is not None] + [[n for n in x if x[n] is not None]]:
+                h = 1e-5
+                xp = {n: (a if a is None else (a + h * dirs[n] if n in which else a)) for n, a in x.items()}
+                xm = {n: (a if a is None else (a - h * dirs[n] if n in which else a)) for n, a in x.items()}
+                fd = (loss(xp) - loss(xm)) / (2 * h)
+                an = sum(float(np.sum(grads[n] * dirs[n])) for n in which)
+                assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
+                    f"({gate},{beta_mode}) d/d{'+'.join(which)}: analytic {an:.10e} vs difference {fd:.10e}"
+
+
+def pin_bwd_linear_inputs(fwd, bwd):
+    """o and S_final are linear in (v, S0) jointly and o is linear in q, so the
+    loss equals <dv, v> + <dS0, S0> exactly, and its o part <dq, q> (Euler's
+    theorem for degree-1 homogeneous functions)."""
+    for n, (gate, beta_mode) in enumerate([("scalar", "scalar"), ("channel", "channel")]):
+        q, k, v, la, beta, S0, Wo, WS = _bwd_case(300 + n, gate, beta_mode)
+        kw = dict(gate=gate, beta_mode=beta_mode)
+        o, S = fwd(q, k, v, la, beta, S0, **kw)
+        g = bwd(q, k, v, la, beta, S0, Wo, WS, **kw)
+        total = np.sum(Wo * o) + np.sum(WS * S)
+        _close(np.sum(g["dv"] * v) + np.sum(g["dS0"] * S0), total, 1e-12, f"v, S0 ({gate},{beta_mode})")
+        g0 = bwd(q, k, v, la, beta, S0, Wo, np.zeros_like(WS), **kw)
+        _close(np.sum(g0["dq"] * q), np.sum(Wo * o), 1e-12, f"q ({gate},{beta_mode})")
+
+
+BWD_PINS = [pin_bwd_directional_derivatives, pin_bwd_linear_inputs]

@@ -143,3 +143,39 @@ def test_ks_pins_catch_planted_mistake(tmp_path, name, old, new):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
+
+
+# Mistakes in the backward, caught by its pins.
+BWD_MUTANTS = [
+    ("no_decay_on_state_gradient", "G[(size_t)c * Dv + j] = al[c] * g;", "G[(size_t)c * Dv + j] = g;"),
+    ("read_term_sign", "a += G[(size_t)c * Dv + j] * u[j] - Sp[(size_t)c * Dv + j] * dvt[j];",
+     "a += G[(size_t)c * Dv + j] * u[j] + Sp[(size_t)c * Dv + j] * dvt[j];"),
+    ("output_gradient_dropped", "G[(size_t)c * Dv + j] += qt[c] * dot[j];", "G[(size_t)c * Dv + j] += 0.0 * dot[j];"),
+    ("sqrt_factor_half_dropped", "const double g = dkt[c] * k_t[c] / (2.0 * sbk[c]);",
+     "const double g = dkt[c] * k_t[c] / sbk[c];"),
+    ("erase_term_dropped", "const double g = G[(size_t)c * Dv + j] - kt[c] * dvt[j];",
+     "const double g = G[(size_t)c * Dv + j];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_bwd_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+
+    def fwd(q, k, v, la, beta, S0, *, gate, beta_mode):
+        return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode)
+
+    def bwd(q, k, v, la, beta, S0, dO, dS, *, gate, beta_mode):
+        return oracle.backward(q, k, v, la, beta, S0, dO, dS, gate=gate, beta_mode=beta_mode, lib=lib)
+
+    caught = []
+    for pin in oracle_pins.BWD_PINS:
+        try:
+            pin(fwd, bwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"

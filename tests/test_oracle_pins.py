@@ -122,3 +122,24 @@ def test_key_scale_decode_is_one_token_forward():
                                 gate="channel", beta_mode="scalar", key_scale=ks[:, :, 0])
     o2, S2 = oracle.forward(q, k, v, la, beta, S0, gate="channel", beta_mode="scalar", key_scale=ks)
     assert np.array_equal(o1, o2[:, :, 0]) and np.array_equal(S1, S2)
+
+
+def _fwd1(q, k, v, la, beta, S0, *, gate, beta_mode, lib=None):
+    return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, lib=lib)
+
+
+def _bwd1(q, k, v, la, beta, S0, dO, dS, *, gate, beta_mode, lib=None):
+    return oracle.backward(q, k, v, la, beta, S0, dO, dS, gate=gate, beta_mode=beta_mode, lib=lib)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.BWD_PINS, ids=lambda f: f.__name__)
+def test_backward_pin(pin):
+    pin(_fwd1, _bwd1)
+
+
+def test_backward_without_final_state_gradient():
+    q, k, v, la, beta, S0, Wo, WS = oracle_pins._bwd_case(310, "scalar", "scalar")
+    a = oracle.backward(q, k, v, la, beta, S0, Wo, None, gate="scalar", beta_mode="scalar")
+    b = oracle.backward(q, k, v, la, beta, S0, Wo, np.zeros_like(WS), gate="scalar", beta_mode="scalar")
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
