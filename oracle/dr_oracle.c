@@ -308,7 +308,8 @@ int dro_backward(int B, int H, int L, int Dk, int Dv,
         const double* vs = v + (size_t)s * L * Dv;
         const double* las = log_alpha ? log_alpha + (size_t)s * lw : NULL;
         const double* bs = beta + (size_t)s * bw;
-        double* tmp_o = (double*)malloc(sizeof(double) * ((size_t)L * Dv + 2 * (size_t)Dk + (size_t)Dv + 1));
+        /* outputs, then the forward step's scratch: kt (Dk), vt (Dv), p (Dv) */
+        double* tmp_o = (double*)malloc(sizeof(double) * ((size_t)L * Dv + (size_t)Dk + 2 * (size_t)Dv));
         if (!tmp_o) {
             free(St);
             err = DRO_ENOMEM;

@@ -667,8 +667,10 @@ def pin_bwd_linear_inputs(fwd, bwd):
     """o and S_final are linear in (v, S0) jointly and o is linear in q, so the
     loss equals <dv, v> + <dS0, S0> exactly, and its o part <dq, q> (Euler's
     theorem for degree-1 homogeneous functions)."""
-    for n, (gate, beta_mode) in enumerate([("scalar", "scalar"), ("channel", "channel")]):
-        q, k, v, la, beta, S0, Wo, WS = _bwd_case(300 + n, gate, beta_mode)
+    # the last case has d_v well above d_k (value-sized scratch in the forward step)
+    for n, (gate, beta_mode, Dk, Dv) in enumerate([("scalar", "scalar", 5, 5), ("channel", "channel", 5, 5),
+                                                   ("scalar", "scalar", 3, 19)]):
+        q, k, v, la, beta, S0, Wo, WS = _bwd_case(300 + n, gate, beta_mode, Dk=Dk, Dv=Dv)
         kw = dict(gate=gate, beta_mode=beta_mode)
         o, S = fwd(q, k, v, la, beta, S0, **kw)
         g = bwd(q, k, v, la, beta, S0, Wo, WS, **kw)
