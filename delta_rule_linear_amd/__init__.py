@@ -18,6 +18,11 @@ With a diagonal preconditioner on the gradient step (write-side key scales):
 
     o, S = dr_chunk_fwd_precond(q, k, v, log_alpha, beta, key_scale, S0, gate="scalar",
                                 beta_mode="scalar")
+
+Gradients of the chunked forward (scalar gate or none, scalar beta):
+
+    g = dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final, gate="scalar")
+    g["dq"], g["dk"], g["dv"], g["dlog_alpha"], g["dbeta"], g["dS0"]
 """
 from __future__ import annotations
 
@@ -28,7 +33,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 5
+DR_ABI_VERSION = 6
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
@@ -37,7 +42,7 @@ DR_IN_QK_L2NORM, DR_IN_BETA_LOGIT = 1, 2
 EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "dr_decode_step",
            "dr_decode_step_kv", "dr_chunk_fwd_precond_workspace_bytes", "dr_chunk_fwd_precond",
            "dr_decode_step_precond", "dr_status_str", "dr_last_error", "dr_abi_version",
-           "dr_profile_begin", "dr_profile_end")
+           "dr_profile_begin", "dr_profile_end", "dr_chunk_bwd_workspace_bytes", "dr_chunk_bwd")
 
 
 class DeltaRuleError(RuntimeError):
@@ -97,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.dr_decode_step_precond.argtypes = [ctypes.POINTER(DecodeDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                              vp]
         L.dr_decode_step_precond.restype = ctypes.c_int
+        L.dr_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.dr_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.dr_chunk_bwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 15 + [ctypes.c_size_t, vp]
+        L.dr_chunk_bwd.restype = ctypes.c_int
         L.dr_status_str.argtypes = [ctypes.c_int]
         L.dr_status_str.restype = ctypes.c_char_p
         L.dr_last_error.argtypes = []
@@ -292,6 +301,55 @@ def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, 
                                      _ptr(beta), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(S_final),
                                      _ptr(workspace), wbytes, _stream(stream)))
     return o, S_final
+
+
+def dr_chunk_bwd_workspace_bytes(desc: ChunkDesc) -> int:
+    return int(lib().dr_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, want_dS0: bool = True,
+                 workspace=None, stream=None):
+    """Gradients of dr_chunk_fwd (gate "none" or "scalar", scalar beta) for the
+    loss whose gradients with respect to o and S_final are dO [B,H,L,Dv] and
+    dS_final [B,H,Dk,Dv] (fp32; dS_final None means zero).  q, k, v and the
+    other inputs are as for dr_chunk_fwd.  Returns a dict of fp32 device
+    tensors dq, dk, dv, dlog_alpha (None for gate "none"), dbeta and dS0
+    (None with want_dS0=False)."""
+    torch = _torch()
+    B, H, L, Dk = q.shape
+    Dv = v.shape[-1]
+    _need(q, "q")
+    _need(k, "k", q.dtype, (B, H, L, Dk))
+    _need(v, "v", q.dtype, (B, H, L, Dv))
+    if gate == "none":
+        if log_alpha is not None:
+            raise ValueError("gate 'none' takes no log_alpha")
+    elif gate == "scalar":
+        _need(log_alpha, "log_alpha", torch.float32, (B, H, L))
+    else:
+        raise ValueError("the backward covers gate 'none' and 'scalar'")
+    _need(beta, "beta", torch.float32, (B, H, L))
+    if S0 is not None:
+        _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
+    _need(dO, "dO", torch.float32, (B, H, L, Dv))
+    if dS_final is not None:
+        _need(dS_final, "dS_final", torch.float32, (B, H, Dk, Dv))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    out = {"dq": torch.empty((B, H, L, Dk), **f32), "dk": torch.empty((B, H, L, Dk), **f32),
+           "dv": torch.empty((B, H, L, Dv), **f32),
+           "dlog_alpha": torch.empty((B, H, L), **f32) if gate == "scalar" else None,
+           "dbeta": torch.empty((B, H, L), **f32),
+           "dS0": torch.empty((B, H, Dk, Dv), **f32) if want_dS0 else None}
+    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, "scalar")
+    nbytes = dr_chunk_bwd_workspace_bytes(desc)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                              _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                              _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
+                              _ptr(workspace), wbytes, _stream(stream)))
+    return out
 
 
 def dr_decode_step(S, q, k, v, log_alpha, beta, *, gate: str, beta_mode: str, out_dtype=None,

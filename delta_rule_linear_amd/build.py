@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdeltarule.so")
-SOURCES = ["dr_abi.hip", "dr_chunk.hip", "dr_scan16.hip", "dr_prep16.hip", "dr_decode.hip"]
+SOURCES = ["dr_abi.hip", "dr_chunk.hip", "dr_scan16.hip", "dr_prep16.hip", "dr_decode.hip", "dr_bwd.hip"]
 ARCH = os.environ.get("DR_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

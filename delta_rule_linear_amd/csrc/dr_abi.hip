@@ -312,6 +312,113 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
     return DR_OK;
 }
 
+// ----------------------------------------------------------------- backward
+struct BwdLayout {
+    size_t T, Pm, A, G, S, H, U, R, dU, total;
+};
+
+BwdLayout bwd_layout(const dr_chunk_desc& d) {
+    BwdLayout w{};
+    const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
+    const size_t NCH = (size_t)d.B * d.H * NC;
+    const size_t f = sizeof(float);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    w.T = take(NCH * dr::CH * dr::CH * f);
+    w.Pm = take(NCH * dr::CH * dr::CH * f);
+    w.A = take(NCH * dr::CH * dr::CH * f);
+    w.G = take(NCH * dr::CH * f);
+    w.S = take(NCH * d.Dk * d.Dv * f);
+    w.H = take(NCH * d.Dk * d.Dv * f);
+    w.U = take(NCH * dr::CH * d.Dv * f);
+    w.R = take(NCH * dr::CH * d.Dv * f);
+    w.dU = take(NCH * dr::CH * d.Dv * f);
+    w.total = NCH ? off : 0;
+    return w;
+}
+
+dr_status check_bwd_desc(const dr_chunk_desc* d) {
+    dr_status s = check_chunk_desc(d);
+    if (s != DR_OK) return s;
+    if (d->gate == DR_GATE_CHANNEL)
+        return fail(DR_ERR_UNSUPPORTED, "the backward covers the scalar gate and no gate");
+    if (d->beta != DR_BETA_SCALAR) return fail(DR_ERR_UNSUPPORTED, "the backward covers the scalar beta");
+    if (d->input_flags) return fail(DR_ERR_UNSUPPORTED, "the backward takes no input_flags");
+    if (d->out_dtype != DR_F32) return fail(DR_ERR_UNSUPPORTED, "dO and the gradients are fp32: out_dtype must be DR_F32");
+    const size_t NCH = (size_t)d->B * d->H * (((size_t)d->L + dr::CH - 1) / dr::CH);
+    if (NCH > (size_t)std::numeric_limits<int>::max())
+        return fail(DR_ERR_UNSUPPORTED, "B*H*ceil(L/64)=%zu chunks: too many", NCH);
+    return DR_OK;
+}
+
+dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, const float* S0, const float* dO, const float* dS_final, float* dq,
+                    float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    dr_status s = check_bwd_desc(d);
+    if (s != DR_OK) return s;
+    const size_t nseq = (size_t)d->B * d->H;
+    const bool tokens = nseq > 0 && d->L > 0;
+    if (tokens) {
+        if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta)
+            return fail(DR_ERR_NULL, "q, k, v, beta, dO, dq, dk, dv and dbeta are required");
+        if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
+            return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
+        if ((d->gate == DR_GATE_NONE) != (dlog_alpha == nullptr))
+            return fail(DR_ERR_NULL, "dlog_alpha must be NULL exactly when gate is DR_GATE_NONE");
+    }
+    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0,
+                          workspace};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "S0", "dO", "dS_final", "dq", "dk", "dv",
+                           "dlog_alpha", "dbeta", "dS0", "workspace"};
+    for (int i = 0; i < 15; ++i)
+        if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    const BwdLayout w = bwd_layout(*d);
+    if (w.total) {
+        if (!workspace) return fail(DR_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
+        if (workspace_bytes < w.total)
+            return fail(DR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    if (nseq == 0) return DR_OK;
+    if (d->L == 0) {
+        // no tokens: S_final is S0, so dS0 is dS_final
+        if (dS0) {
+            const size_t n = nseq * d->Dk * d->Dv;
+            hipLaunchKernelGGL(copy_state_kernel, dim3(256), dim3(256), 0, st, dS0, dS_final, n);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return fail(DR_ERR_HIP, "state copy launch: %s", hipGetErrorString(e));
+        }
+        return DR_OK;
+    }
+    dr::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.log_alpha = log_alpha; a.beta = beta; a.S0 = S0;
+    a.dO = dO; a.dS_final = dS_final;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;
+    a.B = d->B; a.H = d->H; a.L = d->L; a.Dv = d->Dv;
+    a.NC = (d->L + dr::CH - 1) / dr::CH;
+    a.nseq = (int)nseq;
+    a.has_gate = d->gate != DR_GATE_NONE;
+    char* ws = (char*)workspace;
+    a.wT = (float*)(ws + w.T);
+    a.wP = (float*)(ws + w.Pm);
+    a.wA = (float*)(ws + w.A);
+    a.wG = (float*)(ws + w.G);
+    a.wS = (float*)(ws + w.S);
+    a.wH = (float*)(ws + w.H);
+    a.wU = (float*)(ws + w.U);
+    a.wR = (float*)(ws + w.R);
+    a.wdU = (float*)(ws + w.dU);
+    hipError_t e = dr::launch_bwd(a, d->Dk, d->in_dtype == DR_F32, st);
+    if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
+    return DR_OK;
+}
+
 // The separate-strength entry points take channel-wise strengths only.
 dr_status check_kv_mode(int beta_mode) {
     if (beta_mode != DR_BETA_CHANNEL)
@@ -376,6 +483,20 @@ dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* 
     g_err[0] = '\0';
     if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
     return decode_step(d, q, k, v, log_alpha, beta_k, beta_v, nullptr, false, S, o, stream);
+}
+
+size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d) {
+    if (check_bwd_desc(d) != DR_OK) return 0;
+    return bwd_layout(*d).total;
+}
+
+dr_status dr_chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* S0, const float* dO,
+                       const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
+                       float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    return chunk_bwd(d, q, k, v, log_alpha, beta, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,0 +1,691 @@
+// dr_bwd.hip -- gradients of the chunked forward (scalar gate or none, scalar
+// beta), all in fp32 on the fp32 matrix cores.
+//
+// The pages print no backward; this is the reverse-mode derivative of the
+// chunk algebra of the forward (DeltaNet page, chunkwise form and its
+// hardware notes; FG2-GDN page, section 2 for the gated recurrence).  Per
+// chunk of 64 tokens with start state S, cumulative log-decay g_r, gamma_r =
+// e^{g_r}, lambda_r = e^{g_63 - g_r}, E_ri = e^{g_r - g_i}:
+//   A = strict lower of Diag(beta) K K^T o E,   T = (I + A)^-1,
+//   P = lower (diagonal included) of Q K^T o E,
+//   R = V - Gamma K S,   U = T Diag(beta) R,
+//   O = Gamma Q S + P U,   S' = gamma_63 S + K^T Lambda U.
+// With H the gradient of the loss with respect to S' (the next chunk's start
+// state, dS_final after the last chunk):
+//   dU = P^T dO + Lambda K H,   dR = Diag(beta) T^T dU  (= dV),
+//   dS = gamma_63 H + Q^T Gamma dO - K^T Gamma dR,
+//   dP = dO U^T,   dT^ = dU R^T,   dA = -T^T (dT^ Diag(beta)) T^T,
+// and dq, dk, dbeta, dg follow from the products above; d log alpha is the
+// reverse cumulative sum of dg within the chunk.
+//
+// Four kernels:
+//   prep   one workgroup per chunk: g, A's factor K K^T o E, P, T
+//   fscan  one per (sequence, 16 state columns): the start state of every
+//          chunk, R and U (sequential over chunks)
+//   rscan  one per (sequence, 16 state columns), chunks in reverse: H per
+//          chunk, dU, dV, and dS0
+//   post   one per chunk: dq, dk, dbeta, d log alpha
+// Tokens past the end of a sequence enter the last chunk as zeros (q, k, v,
+// dO, beta and log alpha), which leaves every real token's terms unchanged.
+
+#include "dr_internal.h"
+
+namespace dr {
+namespace {
+
+constexpr int NTH = 256;
+constexpr int PT = CH + 1;   // LDS pitch of 64-wide fp32 rows
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Rows [0, 64) x [0, DK) of q or k for the chunk starting at token t0 into
+// LDS (pitch DK + 1), as fp32, zeros past the end.
+template <int DK, bool F32IN>
+__device__ __forceinline__ void load_rows(float* dst, const void* src, size_t tok0, int valid, int tid) {
+    constexpr int KP = DK + 1;
+    for (int e = tid; e < CH * DK / 8; e += NTH) {
+        const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+        float x[8];
+        load8<F32IN>(src, (tok0 + r) * DK + c8, r < valid, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[r * KP + c8 + j] = x[j];
+    }
+}
+
+// A 64 x 64 fp32 workspace matrix into LDS (pitch 65).
+__device__ __forceinline__ void load_mat(float* dst, const float* src, int tid) {
+    for (int e = tid; e < CH * CH / 4; e += NTH) {
+        const float4 x = reinterpret_cast<const float4*>(src)[e];
+        const int r = e >> 4, c = (e & 15) * 4;
+        dst[r * PT + c] = x.x;
+        dst[r * PT + c + 1] = x.y;
+        dst[r * PT + c + 2] = x.z;
+        dst[r * PT + c + 3] = x.w;
+    }
+}
+
+// Column tiles of one sequence on one XCD (workgroups are dealt round-robin
+// to the 8 XCDs), so they share the chunk's operands in L2.
+__device__ __forceinline__ void scan_tile(const BwdArgs& a, int& seq, int& tile) {
+    const int NT = a.Dv / 16, bid = blockIdx.x;
+    seq = (bid / (8 * NT)) * 8 + (bid & 7);
+    tile = (bid >> 3) % NT;
+}
+
+// --------------------------------------------------------------------- prep
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1;
+    __shared__ float sK[CH * KP];
+    __shared__ float sQ[CH * KP];
+    __shared__ float sA[CH * PT];
+    __shared__ float sT[CH * PT];
+    __shared__ float sX[4][16 * 17];
+    __shared__ float sg[CH], sb[CH];
+    const int cs = blockIdx.x;
+    const int seq = cs / a.NC, c = cs - seq * a.NC;
+    const int t0 = c * CH, valid = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const size_t mo = (size_t)cs * CH * CH;
+
+    load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
+    load_rows<DK, F32IN>(sQ, a.q, tok0, valid, tid);
+    if (tid < CH) {
+        const bool ok = tid < valid;
+        sb[tid] = ok ? a.beta[tok0 + tid] : 0.f;
+        float x = (ok && a.has_gate) ? a.log_alpha[tok0 + tid] : 0.f;
+        // inclusive prefix sum over the 64 lanes of wave 0
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(x, o);
+            if (l >= o) x += y;
+        }
+        sg[tid] = x;
+        a.wG[(size_t)cs * CH + tid] = x;
+    }
+    __syncthreads();
+
+    // lower blocks (R = w, I <= R) of K K^T and Q K^T; E applied per element
+    {
+        const int R = w;
+        for (int I = 0; I < 4; ++I) {
+            f32x4 aK = zero4(), aQ = zero4();
+            if (I <= R) {
+                for (int s = 0; s < DK / 4; ++s) {
+                    const int m = 4 * s + g;
+                    const float kb = sK[(16 * I + i16) * KP + m];
+                    aK = mfma_f32x4(sK[(16 * R + i16) * KP + m], kb, aK);
+                    aQ = mfma_f32x4(sQ[(16 * R + i16) * KP + m], kb, aQ);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
+                const float e = i <= r ? expf(sg[r] - sg[i]) : 0.f;
+                const float araw = i < r ? aK[j] * e : 0.f;
+                sA[r * PT + i] = sb[r] * araw;
+                a.wA[mo + r * CH + i] = araw;
+                a.wP[mo + r * CH + i] = i <= r ? aQ[j] * e : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1.  Diagonal 16 x 16 blocks by forward substitution: wave w
+    // inverts block w, lane j < 16 owns column j.
+    if (l < 16) {
+        const int base = 16 * w, j = l;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) s += sA[(base + r) * PT + base + i] * t[i];
+            t[r] = r == j ? 1.f : (r < j ? 0.f : -s);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(base + r) * PT + base + j] = t[r];
+    }
+    __syncthreads();
+    // Off-diagonal blocks, one block row R at a time:
+    //   T_RI = -T_RR sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .]
+    for (int R = 1; R < 4; ++R) {
+        if (w < R) {
+            const int I = w;
+            f32x4 X = zero4();
+            for (int s = 4 * I; s < 4 * R; ++s) {
+                const int m = 4 * s + g;
+                X = mfma_f32x4(sA[(16 * R + i16) * PT + m], sT[m * PT + 16 * I + i16], X);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sX[w][(4 * g + j) * 17 + i16] = X[j];
+        }
+        __syncthreads();
+        if (w < R) {
+            const int I = w;
+            f32x4 Y = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int m = 4 * s + g;
+                Y = mfma_f32x4(sT[(16 * R + i16) * PT + 16 * R + m], sX[w][m * 17 + i16], Y);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sT[(16 * R + 4 * g + j) * PT + 16 * I + i16] = -Y[j];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < CH * CH; e += NTH) {
+        const int r = e >> 6, i = e & 63;
+        a.wT[mo + e] = i <= r ? sT[r * PT + i] : 0.f;
+    }
+}
+
+// ------------------------------------------------------- forward state scan
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1;
+    __shared__ float sK[CH * KP];
+    __shared__ float sT[CH * PT];
+    __shared__ float sS[DK * 17];
+    __shared__ float sR[CH * 17];
+    __shared__ float sU[CH * 17];
+    __shared__ float sg[CH], sb[CH];
+    int seq, tile;
+    scan_tile(a, seq, tile);
+    if (seq >= a.nseq) return;
+    const int n0 = 16 * tile, Dv = a.Dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+
+    for (int e = tid; e < DK * 16; e += NTH) {
+        const int d = e >> 4, cc = e & 15;
+        sS[d * 17 + cc] = a.S0 ? a.S0[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
+    }
+    for (int c = 0; c < a.NC; ++c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        const size_t tok0 = (size_t)seq * a.L + t0;
+        __syncthreads();
+        for (int e = tid; e < DK * 16; e += NTH) {
+            const int d = e >> 4, cc = e & 15;
+            a.wS[(cs * DK + d) * Dv + n0 + cc] = sS[d * 17 + cc];
+        }
+        load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
+        load_mat(sT, a.wT + cs * CH * CH, tid);
+        if (tid < CH) {
+            sg[tid] = a.wG[cs * CH + tid];
+            sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
+        }
+        float vv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            vv[j] = row < valid ? load1<F32IN>(a.v, (tok0 + row) * Dv + n0 + i16) : 0.f;
+        }
+        __syncthreads();
+        // X = K S, R = V - Gamma X  (rows 16 w ..)
+        f32x4 X = zero4();
+        for (int s = 0; s < DK / 4; ++s) {
+            const int m = 4 * s + g;
+            X = mfma_f32x4(sK[(16 * w + i16) * KP + m], sS[m * 17 + i16], X);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            const float r = vv[j] - expf(sg[row]) * X[j];
+            sR[row * 17 + i16] = r;
+            a.wR[(cs * CH + row) * Dv + n0 + i16] = r;
+        }
+        __syncthreads();
+        // U = T Diag(beta) R
+        f32x4 U = zero4();
+        for (int s = 0; s < 4 * (w + 1); ++s) {
+            const int m = 4 * s + g;
+            U = mfma_f32x4(sT[(16 * w + i16) * PT + m] * sb[m], sR[m * 17 + i16], U);
+        }
+        const float g63 = sg[CH - 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            a.wU[(cs * CH + row) * Dv + n0 + i16] = U[j];
+            sU[row * 17 + i16] = expf(g63 - sg[row]) * U[j];
+        }
+        __syncthreads();
+        // S <- gamma_63 S + K^T Lambda U
+        const float gam63 = expf(g63);
+        for (int b = w; b < DK / 16; b += 4) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int m = 4 * s + g;
+                acc = mfma_f32x4(sK[m * KP + 16 * b + i16], sU[m * 17 + i16], acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 16 * b + 4 * g + j;
+                sS[d * 17 + i16] = gam63 * sS[d * 17 + i16] + acc[j];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------ reverse adjoint scan
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1;
+    __shared__ float sK[CH * KP];
+    __shared__ float sQ[CH * KP];
+    __shared__ float sT[CH * PT];
+    __shared__ float sP[CH * PT];
+    __shared__ float sH[DK * 17];
+    __shared__ float sO[CH * 17];   // Gamma dO
+    __shared__ float sD[CH * 17];   // dU, then Gamma dR
+    __shared__ float sgam[CH], slam[CH], sb[CH];
+    int seq, tile;
+    scan_tile(a, seq, tile);
+    if (seq >= a.nseq) return;
+    const int n0 = 16 * tile, Dv = a.Dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+
+    for (int e = tid; e < DK * 16; e += NTH) {
+        const int d = e >> 4, cc = e & 15;
+        sH[d * 17 + cc] = a.dS_final ? a.dS_final[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
+    }
+    for (int c = a.NC - 1; c >= 0; --c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        const size_t tok0 = (size_t)seq * a.L + t0;
+        __syncthreads();
+        for (int e = tid; e < DK * 16; e += NTH) {
+            const int d = e >> 4, cc = e & 15;
+            a.wH[(cs * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
+        }
+        load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
+        load_rows<DK, F32IN>(sQ, a.q, tok0, valid, tid);
+        load_mat(sT, a.wT + cs * CH * CH, tid);
+        load_mat(sP, a.wP + cs * CH * CH, tid);
+        float gam63;
+        {
+            const float* gp = a.wG + cs * CH;
+            const float g63 = gp[CH - 1];
+            gam63 = expf(g63);
+            if (tid < CH) {
+                sgam[tid] = expf(gp[tid]);
+                slam[tid] = expf(g63 - gp[tid]);
+                sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
+            }
+        }
+        float od[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            od[j] = row < valid ? a.dO[(tok0 + row) * Dv + n0 + i16] : 0.f;
+            sO[row * 17 + i16] = od[j];
+        }
+        __syncthreads();
+        // dU = P^T dO + Lambda K H  (rows 16 w ..)
+        f32x4 Z = zero4(), Y = zero4();
+        for (int s = 0; s < DK / 4; ++s) {
+            const int m = 4 * s + g;
+            Z = mfma_f32x4(sK[(16 * w + i16) * KP + m], sH[m * 17 + i16], Z);
+        }
+        for (int s = 4 * w; s < 16; ++s) {
+            const int m = 4 * s + g;
+            Y = mfma_f32x4(sP[m * PT + 16 * w + i16], sO[m * 17 + i16], Y);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            const float du = slam[row] * Z[j] + Y[j];
+            sD[row * 17 + i16] = du;
+            a.wdU[(cs * CH + row) * Dv + n0 + i16] = du;
+        }
+        __syncthreads();
+        // dR = Diag(beta) T^T dU
+        f32x4 Rr = zero4();
+        for (int s = 4 * w; s < 16; ++s) {
+            const int m = 4 * s + g;
+            Rr = mfma_f32x4(sT[m * PT + 16 * w + i16], sD[m * 17 + i16], Rr);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            const float dr = sb[row] * Rr[j];
+            if (row < valid) a.dv[(tok0 + row) * Dv + n0 + i16] = dr;
+            sD[row * 17 + i16] = sgam[row] * dr;
+            sO[row * 17 + i16] = sgam[row] * od[j];
+        }
+        __syncthreads();
+        // H <- gamma_63 H + Q^T Gamma dO - K^T Gamma dR
+        for (int b = w; b < DK / 16; b += 4) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int m = 4 * s + g;
+                acc = mfma_f32x4(sQ[m * KP + 16 * b + i16], sO[m * 17 + i16], acc);
+                acc = mfma_f32x4(-sK[m * KP + 16 * b + i16], sD[m * 17 + i16], acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 16 * b + 4 * g + j;
+                sH[d * 17 + i16] = gam63 * sH[d * 17 + i16] + acc[j];
+            }
+        }
+    }
+    __syncthreads();
+    if (a.dS0) {
+        for (int e = tid; e < DK * 16; e += NTH) {
+            const int d = e >> 4, cc = e & 15;
+            a.dS0[((size_t)seq * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
+        }
+    }
+}
+
+// -------------------------------------------------- per-chunk gradient terms
+template <int DK>
+struct PostLds {
+    static constexpr int KP = DK + 1;
+    static constexpr int VS = 32;          // state columns per slab
+    static constexpr int SP = VS + 1;
+    static constexpr int SLAB = 2 * DK * SP + 5 * CH * SP;
+    static constexpr int QK = 2 * CH * KP;
+    static constexpr int R1 = SLAB > QK ? SLAB : QK;
+};
+
+// Sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same column of an
+// accumulator block).
+__device__ __forceinline__ float col4_sum(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
+    using Lp = PostLds<DK>;
+    constexpr int KP = Lp::KP, VS = Lp::VS, SP = Lp::SP, ND = DK / 16;
+    __shared__ float s1[Lp::R1];
+    __shared__ float sM0[CH * PT];   // T
+    __shared__ float sM1[CH * PT];   // P, then M = dA Diag-row(beta) o E
+    __shared__ float sM2[CH * PT];   // K K^T o E (strict lower)
+    __shared__ float sM3[CH * PT];   // N = dP o E
+    __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
+    __shared__ float sg[CH], sgam[CH], slam[CH], sb[CH], sdg[CH], sdb[CH];
+    __shared__ float shs;
+    const int cs = blockIdx.x;
+    const int seq = cs / a.NC, c = cs - seq * a.NC;
+    const int t0 = c * CH, valid = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int Dv = a.Dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const size_t mo = (size_t)cs * CH * CH;
+
+    if (tid < CH) {
+        const float* gp = a.wG + (size_t)cs * CH;
+        const float gv = gp[tid], g63 = gp[CH - 1];
+        sg[tid] = gv;
+        sgam[tid] = expf(gv);
+        slam[tid] = expf(g63 - gv);
+        sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
+        sdg[tid] = 0.f;
+        sdb[tid] = 0.f;
+    }
+    if (tid == 0) shs = 0.f;
+
+    // ---- state terms over slabs of VS state columns:
+    //   z1 = dO S^T, z2 = dR S^T, z3 = U H^T  (rows 16 w .., all DK columns)
+    //   dp = dO U^T, dt = dU R^T              (rows 16 w .., all 64 columns)
+    f32x4 z1[ND], z2[ND], z3[ND], dp[4], dt[4];
+#pragma unroll
+    for (int D = 0; D < ND; ++D) z1[D] = z2[D] = z3[D] = zero4();
+#pragma unroll
+    for (int I = 0; I < 4; ++I) dp[I] = dt[I] = zero4();
+    float hs = 0.f;
+    float* sS = s1;
+    float* sH = sS + DK * SP;
+    float* sO = sH + DK * SP;
+    float* sRr = sO + CH * SP;
+    float* sU = sRr + CH * SP;
+    float* sdU = sU + CH * SP;
+    float* sdR = sdU + CH * SP;
+    for (int v0 = 0; v0 < Dv; v0 += VS) {
+        const int vw = min(VS, Dv - v0);   // 16 or 32
+        __syncthreads();
+        for (int e = tid; e < DK * VS / 4; e += NTH) {
+            const int d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
+            float4 sv = {0.f, 0.f, 0.f, 0.f}, hv = sv;
+            if (c4 < vw) {
+                const size_t off = ((size_t)cs * DK + d) * Dv + v0 + c4;
+                sv = *reinterpret_cast<const float4*>(a.wS + off);
+                hv = *reinterpret_cast<const float4*>(a.wH + off);
+            }
+            hs += sv.x * hv.x + sv.y * hv.y + sv.z * hv.z + sv.w * hv.w;
+            float* ps = sS + d * SP + c4;
+            float* ph = sH + d * SP + c4;
+            ps[0] = sv.x; ps[1] = sv.y; ps[2] = sv.z; ps[3] = sv.w;
+            ph[0] = hv.x; ph[1] = hv.y; ph[2] = hv.z; ph[3] = hv.w;
+        }
+        for (int e = tid; e < CH * VS / 4; e += NTH) {
+            const int r = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
+            float4 o4 = {0.f, 0.f, 0.f, 0.f}, d4 = o4, r4 = o4, u4 = o4, du4 = o4;
+            if (c4 < vw) {
+                const size_t wo = ((size_t)cs * CH + r) * Dv + v0 + c4;
+                r4 = *reinterpret_cast<const float4*>(a.wR + wo);
+                u4 = *reinterpret_cast<const float4*>(a.wU + wo);
+                du4 = *reinterpret_cast<const float4*>(a.wdU + wo);
+                if (r < valid) {
+                    const size_t io = (tok0 + r) * Dv + v0 + c4;
+                    o4 = *reinterpret_cast<const float4*>(a.dO + io);
+                    d4 = *reinterpret_cast<const float4*>(a.dv + io);
+                }
+            }
+            const int at = r * SP + c4;
+            sO[at] = o4.x; sO[at + 1] = o4.y; sO[at + 2] = o4.z; sO[at + 3] = o4.w;
+            sdR[at] = d4.x; sdR[at + 1] = d4.y; sdR[at + 2] = d4.z; sdR[at + 3] = d4.w;
+            sRr[at] = r4.x; sRr[at + 1] = r4.y; sRr[at + 2] = r4.z; sRr[at + 3] = r4.w;
+            sU[at] = u4.x; sU[at + 1] = u4.y; sU[at + 2] = u4.z; sU[at + 3] = u4.w;
+            sdU[at] = du4.x; sdU[at + 1] = du4.y; sdU[at + 2] = du4.z; sdU[at + 3] = du4.w;
+        }
+        __syncthreads();
+        for (int s = 0; s < VS / 4; ++s) {
+            const int m = 4 * s + g;
+            const int ra = (16 * w + i16) * SP + m;
+            const float ao = sO[ra], ar = sdR[ra], au = sU[ra], adu = sdU[ra];
+#pragma unroll
+            for (int D = 0; D < ND; ++D) {
+                const float bs = sS[(16 * D + i16) * SP + m];
+                const float bh = sH[(16 * D + i16) * SP + m];
+                z1[D] = mfma_f32x4(ao, bs, z1[D]);
+                z2[D] = mfma_f32x4(ar, bs, z2[D]);
+                z3[D] = mfma_f32x4(au, bh, z3[D]);
+            }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                if (I <= w) {
+                    dp[I] = mfma_f32x4(ao, sU[(16 * I + i16) * SP + m], dp[I]);
+                    dt[I] = mfma_f32x4(adu, sRr[(16 * I + i16) * SP + m], dt[I]);
+                }
+            }
+        }
+    }
+    atomicAdd(&shs, hs);
+    __syncthreads();
+
+    // ---- q, k rows and the 64 x 64 matrices
+    float* sK = s1;
+    float* sQ = s1 + CH * KP;
+    load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
+    load_rows<DK, F32IN>(sQ, a.q, tok0, valid, tid);
+    load_mat(sM0, a.wT + mo, tid);
+    load_mat(sM1, a.wP + mo, tid);
+    load_mat(sM2, a.wA + mo, tid);
+    __syncthreads();
+
+    const int rb = 16 * w + 4 * g;   // this lane's first accumulator row
+    float rowg[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
+    float colg[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};
+    float g63part = 0.f;
+    // state terms: dq = Gamma z1, dk = -Gamma z2 + Lambda z3
+    f32x4 dq[ND], dk[ND];
+#pragma unroll
+    for (int D = 0; D < ND; ++D) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j, col = 16 * D + i16;
+            const float qv = sQ[r * KP + col], kv = sK[r * KP + col];
+            const float x1 = sgam[r] * z1[D][j];
+            const float x2 = -sgam[r] * z2[D][j];
+            const float x3 = slam[r] * z3[D][j];
+            dq[D][j] = x1;
+            dk[D][j] = x2 + x3;
+            rowg[j] += qv * x1 + kv * x2 - kv * x3;
+            g63part += kv * x3;
+        }
+    }
+    // dP -> N = dP o E (lower), sums of dP o P; dT^ -> dT = dT^ Diag(beta),
+    // dbeta from dT^ o T
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j, i = 16 * I + i16;
+            const bool lo = i <= r;
+            const float dpv = lo ? dp[I][j] : 0.f;
+            const float dtv = lo ? dt[I][j] : 0.f;
+            const float pd = dpv * sM1[r * PT + i];
+            rowg[j] += pd;
+            colg[I] -= pd;
+            sM3[r * PT + i] = lo ? dpv * expf(sg[r] - sg[i]) : 0.f;
+            colb[I] += dtv * sM0[r * PT + i];
+            sM4[r * PT + i] = dtv * sb[i];
+        }
+    }
+    __syncthreads();
+    // Y = T^T dT  (rows 16 w .. of Y; T[m][a] vanishes for m < a)
+    f32x4 y[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        y[I] = zero4();
+        for (int s = 4 * w; s < 16; ++s) {
+            const int m = 4 * s + g;
+            y[I] = mfma_f32x4(sM0[m * PT + 16 * w + i16], sM4[m * PT + 16 * I + i16], y[I]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sM4[(rb + j) * PT + 16 * I + i16] = y[I][j];
+    __syncthreads();
+    // dA = -Y T^T on the strict lower part (column blocks I <= w), then
+    // M = Diag(beta) (dA o E) into sM1 (P is no longer read)
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        f32x4 da = zero4();
+        if (I <= w) {
+            for (int s = 0; s < 4 * (I + 1); ++s) {
+                const int m = 4 * s + g;
+                da = mfma_f32x4(sM4[(16 * w + i16) * PT + m], sM0[(16 * I + i16) * PT + m], da);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j, cc = 16 * I + i16;
+            const bool lo = cc < r;
+            const float dav = lo ? -da[j] : 0.f;
+            const float adr = dav * sM2[r * PT + cc];
+            rowb[j] += adr;
+            const float ad = sb[r] * adr;
+            rowg[j] += ad;
+            colg[I] -= ad;
+            sM1[r * PT + cc] = lo ? dav * sb[r] * expf(sg[r] - sg[cc]) : 0.f;
+        }
+    }
+    __syncthreads();
+    // dq += N K;  dk += M K + N^T Q + M^T K
+#pragma unroll
+    for (int D = 0; D < ND; ++D) {
+        for (int s = 0; s < 4 * (w + 1); ++s) {
+            const int m = 4 * s + g;
+            const float kb = sK[m * KP + 16 * D + i16];
+            dq[D] = mfma_f32x4(sM3[(16 * w + i16) * PT + m], kb, dq[D]);
+            dk[D] = mfma_f32x4(sM1[(16 * w + i16) * PT + m], kb, dk[D]);
+        }
+        for (int s = 4 * w; s < 16; ++s) {
+            const int m = 4 * s + g;
+            dk[D] = mfma_f32x4(sM3[m * PT + 16 * w + i16], sQ[m * KP + 16 * D + i16], dk[D]);
+            dk[D] = mfma_f32x4(sM1[m * PT + 16 * w + i16], sK[m * KP + 16 * D + i16], dk[D]);
+        }
+    }
+    // ---- reductions of the gate and strength terms
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float sg_ = group_sum<16>(rowg[j]);
+        const float sb_ = group_sum<16>(rowb[j]);
+        if (i16 == 0) {
+            atomicAdd(&sdg[rb + j], sg_);
+            atomicAdd(&sdb[rb + j], sb_);
+        }
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const float cg = col4_sum(colg[I]);
+        const float cb = col4_sum(colb[I]);
+        if (g == 0) {
+            atomicAdd(&sdg[16 * I + i16], cg);
+            atomicAdd(&sdb[16 * I + i16], cb);
+        }
+    }
+    {
+        float x = group_sum<32>(g63part);
+        x += __shfl_xor(x, 32);
+        if (l == 0) atomicAdd(&sdg[CH - 1], x);
+    }
+    __syncthreads();
+    if (w == 0) {
+        // d log alpha_t = sum over r >= t of dg_r (suffix sum over the lanes)
+        float x = sdg[l];
+        if (l == CH - 1) x += expf(sg[CH - 1]) * shs;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y2 = __shfl_down(x, o);
+            if (l + o < 64) x += y2;
+        }
+        if (l < valid) {
+            if (a.dlog_alpha) a.dlog_alpha[tok0 + l] = x;
+            a.dbeta[tok0 + l] = sdb[l];
+        }
+    }
+#pragma unroll
+    for (int D = 0; D < ND; ++D) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j;
+            if (r < valid) {
+                a.dq[(tok0 + r) * DK + 16 * D + i16] = dq[D][j];
+                a.dk[(tok0 + r) * DK + 16 * D + i16] = dk[D][j];
+            }
+        }
+    }
+}
+
+template <int DK, bool F32IN>
+hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+    const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
+    const unsigned nscan = (unsigned)((a.nseq + 7) / 8) * 8u * (unsigned)(a.Dv / 16);
+    hipLaunchKernelGGL((bwd_prep_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((bwd_fscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((bwd_rscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((bwd_post_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st) {
+    if (Dk == 128) return f32in ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
+    return f32in ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
+}
+
+}  // namespace dr

@@ -91,6 +91,41 @@ struct DecodeArgs {
     const float* key_scale;   // write-side key scales [N][H][Dk], or null
 };
 
+// Everything the backward kernels read and write (scalar gate or none, scalar
+// beta; fp32 gradients).  Workspace planes, fp32, per chunk slot
+// cs = (b * H + h) * NC + c:
+//   wT, wP, wA  [NCH][64][64]   T = (I + A)^-1, P, and K K^T o E (strict lower)
+//   wG          [NCH][64]       cumulative log-decay g_r within the chunk
+//   wS, wH      [NCH][Dk][Dv]   chunk start state, gradient at its end state
+//   wU, wR, wdU [NCH][64][Dv]   U, R = V - Gamma K S, and dU
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const float* S0;
+    const float* dO;
+    const float* dS_final;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dlog_alpha;
+    float* dbeta;
+    float* dS0;
+    int B, H, L, Dv, NC, nseq;
+    int has_gate;
+    float* wT;
+    float* wP;
+    float* wA;
+    float* wG;
+    float* wS;
+    float* wH;
+    float* wU;
+    float* wR;
+    float* wdU;
+};
+
 // Optional per-kernel timing: launchers mark the start of each kernel and the
 // end of their last one (dr_profile_begin / dr_profile_end).
 enum ProfSlot { kProfPrep = 0, kProfScan = 1, kProfDecode = 2, kProfEnd = 3 };
@@ -103,6 +138,8 @@ hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool
 hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);
 // the state scan for bf16 inputs (dr_scan16.hip)
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
+// the backward (dr_bwd.hip)
+hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st);
 

@@ -149,6 +149,16 @@ def make_chunk_problem(B, H, L, Dk, Dv, *, in_dtype="bf16", gate="scalar", beta_
                         rng.uniform(0.5, 1.5, (B, H, L, Dk)).astype(np.float32) if key_scale else None)
 
 
+def backward_cotangents(p: ChunkProblem, seed: int = 0, dS_final: bool = True):
+    """Gradients of a loss with respect to the forward's outputs, for the
+    backward: dO ~ N(0, 1) [B, H, L, Dv] and dS_final ~ N(0, 1)
+    [B, H, Dk, Dv] (None with dS_final=False), fp32."""
+    rng = np.random.default_rng([seed, 7919])
+    dO = rng.standard_normal((p.B, p.H, p.L, p.Dv)).astype(np.float32)
+    dSf = rng.standard_normal((p.B, p.H, p.Dk, p.Dv)).astype(np.float32) if dS_final else None
+    return dO, dSf
+
+
 # The named workloads.  Gate ranges are U(lo, hi) on log alpha.
 GDN_GATE = (-0.1, -0.001)
 KDA_GATE = (-0.2, -0.0005)

@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 5
+#define DR_ABI_VERSION 6
 
 typedef enum {
     DR_OK = 0,
@@ -244,6 +244,49 @@ dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* 
 dr_status dr_decode_step_precond(const dr_decode_desc* d, const void* q, const void* k, const void* v,
                                  const float* log_alpha, const float* beta, const float* key_scale,
                                  float* S, void* o, void* stream);
+
+/* Bytes of device workspace dr_chunk_bwd needs for `d` (0 if d is invalid for
+ * the backward or there is no work): per 64-token chunk of every sequence,
+ * three 64 x 64 matrices, 64 gate values, two Dk x Dv states and three
+ * 64 x Dv blocks, all fp32. */
+size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
+
+/*
+ * dr_chunk_bwd -- gradients of dr_chunk_fwd's o and S_final with respect to
+ * every input, for the loss whose gradients with respect to o and S_final
+ * are dO and dS_final.  The pages print no backward; this is the exact
+ * reverse-mode derivative of the chunkwise form that dr_chunk_fwd computes
+ * (DeltaNet page, step 7 and the hardware notes; FG2-GDN page, section 2),
+ * evaluated chunk by chunk: a sequential pass recomputes each chunk's start
+ * state, a reverse pass carries the state gradient, and a per-chunk pass
+ * forms the gradients of q, k, beta and log alpha.  Everything runs in fp32.
+ *
+ * Covered modes: d->gate DR_GATE_NONE or DR_GATE_SCALAR (plain DeltaNet and
+ * Gated DeltaNet), d->beta DR_BETA_SCALAR, d->input_flags 0 (gradients are
+ * with respect to the strengths and vectors as given), d->out_dtype DR_F32
+ * (the dtype of dO); anything else is DR_ERR_UNSUPPORTED.  in_dtype (fp32 or
+ * bf16) is the dtype of q, k, v; Dk, Dv as for dr_chunk_fwd.
+ *
+ *   q, k, v, log_alpha, beta, S0   as for dr_chunk_fwd (S0 may be NULL: zeros)
+ *   dO         [B][H][L][Dv] fp32, gradient with respect to o
+ *   dS_final   [B][H][Dk][Dv] fp32, gradient with respect to S_final, or NULL
+ *              (zero)
+ *   dq, dk     [B][H][L][Dk] fp32, written
+ *   dv         [B][H][L][Dv] fp32, written
+ *   dlog_alpha [B][H][L] fp32, written; required with the scalar gate, must be
+ *              NULL without a gate
+ *   dbeta      [B][H][L] fp32, written
+ *   dS0        [B][H][Dk][Dv] fp32, gradient with respect to S0, written, or
+ *              NULL to skip
+ *   workspace  device scratch of at least dr_chunk_bwd_workspace_bytes(d)
+ *              bytes; contents on entry ignored, on exit unspecified
+ * Outputs must not overlap each other or any input.  Returns DR_OK or an
+ * error status; nothing is launched on an error.
+ */
+dr_status dr_chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const float* S0, const float* dO,
+                       const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
+                       float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Per-kernel timing, for benchmarks and profiling (not part of the method).

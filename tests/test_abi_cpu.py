@@ -225,3 +225,34 @@ def test_precond_validation_and_workspace():
     assert dcall(D(**ok), ks=None) == drl.DR_ERR_NULL
     assert dcall(D(**ok), ks=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
     assert dcall(D(**{**ok, "N": 0})) == drl.DR_OK
+
+
+def test_backward_validation_and_workspace():
+    lib = drl.lib()
+
+    def call(desc, q=FAKE, la=FAKE, dO=FAKE, dq=FAKE, dla=FAKE, dS0=None, ws=FAKE, wbytes=1 << 40):
+        return lib.dr_chunk_bwd(ctypes.byref(desc) if desc is not None else None, q, FAKE, FAKE, la, FAKE,
+                                None, dO, None, dq, FAKE, FAKE, dla, FAKE, dS0, ws, wbytes, None)
+
+    d = _desc()
+    assert call(None) == drl.DR_ERR_NULL
+    assert call(d, q=None) == drl.DR_ERR_NULL
+    assert call(d, dO=None) == drl.DR_ERR_NULL
+    assert call(d, dq=None) == drl.DR_ERR_NULL
+    assert call(d, dla=None) == drl.DR_ERR_NULL                        # scalar gate: d log alpha needed
+    assert call(_desc(gate="none"), la=None) == drl.DR_ERR_NULL        # no gate: none allowed
+    assert call(d, dS0=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
+    for bad in (dict(gate="channel"), dict(Dv=128, beta_mode="channel"), dict(flags=drl.DR_IN_QK_L2NORM),
+                dict(out_dtype=drl.DR_BF16), dict(Dk=96)):
+        assert call(_desc(**bad)) == drl.DR_ERR_UNSUPPORTED
+        assert drl.dr_chunk_bwd_workspace_bytes(_desc(**bad)) == 0
+    need = drl.dr_chunk_bwd_workspace_bytes(d)
+    NCH = 2 * 3 * ((100 + 63) // 64)
+    # per chunk: T, P, K K^T (64 x 64), 64 gate values, two states and three
+    # 64 x Dv blocks, fp32
+    assert need >= NCH * 4 * (3 * 64 * 64 + 64 + 2 * 128 * 128 + 3 * 64 * 128)
+    assert call(d, ws=None) == drl.DR_ERR_WORKSPACE
+    assert call(d, wbytes=need - 1) == drl.DR_ERR_WORKSPACE
+    assert drl.dr_chunk_bwd_workspace_bytes(_desc(L=0)) == 0
+    # no sequences: validated and done without touching memory
+    assert lib.dr_chunk_bwd(ctypes.byref(_desc(B=0)), *([None] * 15), 0, None) == drl.DR_OK
