@@ -64,6 +64,61 @@ __device__ __forceinline__ void load_mat(float* dst, const float* src, int tid) 
     }
 }
 
+// Register prefetch of a chunk's q or k rows: raw values (bf16 bits or fp32),
+// loaded one chunk ahead and converted when stored to LDS.  Rows past the end
+// load row 0 (in bounds) and are zeroed on the store.
+template <int DK, bool F32IN>
+struct RowsPre {
+    static constexpr int N = CH * DK / 8 / NTH;
+    Raw8<F32IN> x[N];
+};
+
+template <int DK, bool F32IN>
+__device__ __forceinline__ void pre_rows(RowsPre<DK, F32IN>& p, const void* src, size_t tok0, int valid,
+                                         int tid) {
+#pragma unroll
+    for (int n = 0; n < RowsPre<DK, F32IN>::N; ++n) {
+        const int e = tid + n * NTH;
+        const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+        p.x[n] = ld_raw8<F32IN>(src, (tok0 + (r < valid ? r : 0)) * DK + c8);
+    }
+}
+
+template <int DK, bool F32IN>
+__device__ __forceinline__ void put_rows(const RowsPre<DK, F32IN>& p, float* dst, int valid, int tid) {
+    constexpr int KP = DK + 1;
+#pragma unroll
+    for (int n = 0; n < RowsPre<DK, F32IN>::N; ++n) {
+        const int e = tid + n * NTH;
+        const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+        float x[8];
+        cvt_raw8<F32IN>(p.x[n], r < valid, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dst[r * KP + c8 + j] = x[j];
+    }
+}
+
+// Register prefetch of a 64 x 64 fp32 workspace matrix.
+struct MatPre {
+    float4 x[CH * CH / 4 / NTH];
+};
+
+__device__ __forceinline__ void pre_mat(MatPre& p, const float* src, int tid) {
+#pragma unroll
+    for (int n = 0; n < CH * CH / 4 / NTH; ++n) p.x[n] = reinterpret_cast<const float4*>(src)[tid + n * NTH];
+}
+
+__device__ __forceinline__ void put_mat(const MatPre& p, float* dst, int tid) {
+#pragma unroll
+    for (int n = 0; n < CH * CH / 4 / NTH; ++n) {
+        const int e = tid + n * NTH, r = e >> 4, c = (e & 15) * 4;
+        dst[r * PT + c] = p.x[n].x;
+        dst[r * PT + c + 1] = p.x[n].y;
+        dst[r * PT + c + 2] = p.x[n].z;
+        dst[r * PT + c + 3] = p.x[n].w;
+    }
+}
+
 // Column tiles of one sequence on one XCD (workgroups are dealt round-robin
 // to the 8 XCDs), so they share the chunk's operands in L2.
 __device__ __forceinline__ void scan_tile(const BwdArgs& a, int& seq, int& tile) {
@@ -104,7 +159,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         sg[tid] = x;
         a.wG[(size_t)cs * CH + tid] = x;
     }
-    __syncthreads();
+    lds_barrier();
 
     // lower blocks (R = w, I <= R) of K K^T and Q K^T; E applied per element
     {
@@ -130,7 +185,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // T = (I + A)^-1.  Diagonal 16 x 16 blocks by forward substitution: wave w
     // inverts block w, lane j < 16 owns column j.
@@ -147,7 +202,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(base + r) * PT + base + j] = t[r];
     }
-    __syncthreads();
+    lds_barrier();
     // Off-diagonal blocks, one block row R at a time:
     //   T_RI = -T_RR sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .]
     for (int R = 1; R < 4; ++R) {
@@ -161,7 +216,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sX[w][(4 * g + j) * 17 + i16] = X[j];
         }
-        __syncthreads();
+        lds_barrier();
         if (w < R) {
             const int I = w;
             f32x4 Y = zero4();
@@ -173,7 +228,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) sT[(16 * R + 4 * g + j) * PT + 16 * I + i16] = -Y[j];
         }
-        __syncthreads();
+        lds_barrier();
     }
     for (int e = tid; e < CH * CH; e += NTH) {
         const int r = e >> 6, i = e & 63;
@@ -182,6 +237,9 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------- forward state scan
+// The next chunk's operands are loaded into registers while the current one
+// is computed; the barriers are LDS-only, so neither those loads nor the
+// workspace stores are waited for inside the loop.
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
     constexpr int KP = DK + 1;
@@ -197,32 +255,50 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
     const int n0 = 16 * tile, Dv = a.Dv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
 
+    RowsPre<DK, F32IN> pk;
+    MatPre pt;
+    float pg = 0.f, pb = 0.f, pv[4];
+    auto prefetch = [&](int c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        const size_t tok0 = (size_t)seq * a.L + t0;
+        pre_rows<DK, F32IN>(pk, a.k, tok0, valid, tid);
+        pre_mat(pt, a.wT + cs * CH * CH, tid);
+        if (tid < CH) {
+            pg = a.wG[cs * CH + tid];
+            pb = a.beta[tok0 + (tid < valid ? tid : 0)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            pv[j] = load1<F32IN>(a.v, (tok0 + (row < valid ? row : 0)) * Dv + n0 + i16);
+        }
+    };
+
     for (int e = tid; e < DK * 16; e += NTH) {
         const int d = e >> 4, cc = e & 15;
         sS[d * 17 + cc] = a.S0 ? a.S0[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
     }
+    prefetch(0);
     for (int c = 0; c < a.NC; ++c) {
         const size_t cs = (size_t)seq * a.NC + c;
         const int t0 = c * CH, valid = min(CH, a.L - t0);
-        const size_t tok0 = (size_t)seq * a.L + t0;
-        __syncthreads();
+        lds_barrier();
+        put_rows<DK, F32IN>(pk, sK, valid, tid);
+        put_mat(pt, sT, tid);
+        if (tid < CH) {
+            sg[tid] = pg;
+            sb[tid] = tid < valid ? pb : 0.f;
+        }
+        float vv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vv[j] = 16 * w + 4 * g + j < valid ? pv[j] : 0.f;
         for (int e = tid; e < DK * 16; e += NTH) {
             const int d = e >> 4, cc = e & 15;
             a.wS[(cs * DK + d) * Dv + n0 + cc] = sS[d * 17 + cc];
         }
-        load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
-        load_mat(sT, a.wT + cs * CH * CH, tid);
-        if (tid < CH) {
-            sg[tid] = a.wG[cs * CH + tid];
-            sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
-        }
-        float vv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            vv[j] = row < valid ? load1<F32IN>(a.v, (tok0 + row) * Dv + n0 + i16) : 0.f;
-        }
-        __syncthreads();
+        lds_barrier();
+        if (c + 1 < a.NC) prefetch(c + 1);
         // X = K S, R = V - Gamma X  (rows 16 w ..)
         f32x4 X = zero4();
         for (int s = 0; s < DK / 4; ++s) {
@@ -236,7 +312,7 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
             sR[row * 17 + i16] = r;
             a.wR[(cs * CH + row) * Dv + n0 + i16] = r;
         }
-        __syncthreads();
+        lds_barrier();
         // U = T Diag(beta) R
         f32x4 U = zero4();
         for (int s = 0; s < 4 * (w + 1); ++s) {
@@ -250,7 +326,7 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
             a.wU[(cs * CH + row) * Dv + n0 + i16] = U[j];
             sU[row * 17 + i16] = expf(g63 - sg[row]) * U[j];
         }
-        __syncthreads();
+        lds_barrier();
         // S <- gamma_63 S + K^T Lambda U
         const float gam63 = expf(g63);
         for (int b = w; b < DK / 16; b += 4) {
@@ -270,6 +346,7 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------ reverse adjoint scan
+// Prefetched one chunk ahead (backwards) like the forward scan.
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
     constexpr int KP = DK + 1;
@@ -278,7 +355,7 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
     __shared__ float sT[CH * PT];
     __shared__ float sP[CH * PT];
     __shared__ float sH[DK * 17];
-    __shared__ float sO[CH * 17];   // Gamma dO
+    __shared__ float sO[CH * 17];   // dO, then Gamma dO
     __shared__ float sD[CH * 17];   // dU, then Gamma dR
     __shared__ float sgam[CH], slam[CH], sb[CH];
     int seq, tile;
@@ -287,42 +364,61 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
     const int n0 = 16 * tile, Dv = a.Dv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
 
+    RowsPre<DK, F32IN> pk, pq;
+    MatPre pt, pp;
+    float pg = 0.f, pg63 = 0.f, pb = 0.f, po[4];
+    auto prefetch = [&](int c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        const size_t tok0 = (size_t)seq * a.L + t0;
+        pre_rows<DK, F32IN>(pk, a.k, tok0, valid, tid);
+        pre_rows<DK, F32IN>(pq, a.q, tok0, valid, tid);
+        pre_mat(pt, a.wT + cs * CH * CH, tid);
+        pre_mat(pp, a.wP + cs * CH * CH, tid);
+        if (tid < CH) {
+            pg = a.wG[cs * CH + tid];
+            pg63 = a.wG[cs * CH + CH - 1];
+            pb = a.beta[tok0 + (tid < valid ? tid : 0)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 16 * w + 4 * g + j;
+            po[j] = a.dO[(tok0 + (row < valid ? row : 0)) * Dv + n0 + i16];
+        }
+    };
+
     for (int e = tid; e < DK * 16; e += NTH) {
         const int d = e >> 4, cc = e & 15;
         sH[d * 17 + cc] = a.dS_final ? a.dS_final[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
     }
+    prefetch(a.NC - 1);
     for (int c = a.NC - 1; c >= 0; --c) {
         const size_t cs = (size_t)seq * a.NC + c;
         const int t0 = c * CH, valid = min(CH, a.L - t0);
         const size_t tok0 = (size_t)seq * a.L + t0;
-        __syncthreads();
-        for (int e = tid; e < DK * 16; e += NTH) {
-            const int d = e >> 4, cc = e & 15;
-            a.wH[(cs * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
-        }
-        load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
-        load_rows<DK, F32IN>(sQ, a.q, tok0, valid, tid);
-        load_mat(sT, a.wT + cs * CH * CH, tid);
-        load_mat(sP, a.wP + cs * CH * CH, tid);
-        float gam63;
-        {
-            const float* gp = a.wG + cs * CH;
-            const float g63 = gp[CH - 1];
-            gam63 = expf(g63);
-            if (tid < CH) {
-                sgam[tid] = expf(gp[tid]);
-                slam[tid] = expf(g63 - gp[tid]);
-                sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
-            }
+        lds_barrier();
+        put_rows<DK, F32IN>(pk, sK, valid, tid);
+        put_rows<DK, F32IN>(pq, sQ, valid, tid);
+        put_mat(pt, sT, tid);
+        put_mat(pp, sP, tid);
+        if (tid < CH) {
+            sgam[tid] = expf(pg);
+            slam[tid] = expf(pg63 - pg);
+            sb[tid] = tid < valid ? pb : 0.f;
         }
         float od[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * w + 4 * g + j;
-            od[j] = row < valid ? a.dO[(tok0 + row) * Dv + n0 + i16] : 0.f;
+            od[j] = row < valid ? po[j] : 0.f;
             sO[row * 17 + i16] = od[j];
         }
-        __syncthreads();
+        for (int e = tid; e < DK * 16; e += NTH) {
+            const int d = e >> 4, cc = e & 15;
+            a.wH[(cs * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
+        }
+        lds_barrier();
+        if (c > 0) prefetch(c - 1);
         // dU = P^T dO + Lambda K H  (rows 16 w ..)
         f32x4 Z = zero4(), Y = zero4();
         for (int s = 0; s < DK / 4; ++s) {
@@ -340,14 +436,15 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
             sD[row * 17 + i16] = du;
             a.wdU[(cs * CH + row) * Dv + n0 + i16] = du;
         }
-        __syncthreads();
+        lds_barrier();
         // dR = Diag(beta) T^T dU
         f32x4 Rr = zero4();
         for (int s = 4 * w; s < 16; ++s) {
             const int m = 4 * s + g;
             Rr = mfma_f32x4(sT[m * PT + 16 * w + i16], sD[m * 17 + i16], Rr);
         }
-        __syncthreads();
+        const float gam63 = sgam[CH - 1];
+        lds_barrier();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 16 * w + 4 * g + j;
@@ -356,7 +453,7 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
             sD[row * 17 + i16] = sgam[row] * dr;
             sO[row * 17 + i16] = sgam[row] * od[j];
         }
-        __syncthreads();
+        lds_barrier();
         // H <- gamma_63 H + Q^T Gamma dO - K^T Gamma dR
         for (int b = w; b < DK / 16; b += 4) {
             f32x4 acc = zero4();
@@ -373,7 +470,7 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (a.dS0) {
         for (int e = tid; e < DK * 16; e += NTH) {
             const int d = e >> 4, cc = e & 15;
@@ -451,7 +548,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
     float* sdR = sdU + CH * SP;
     for (int v0 = 0; v0 < Dv; v0 += VS) {
         const int vw = min(VS, Dv - v0);   // 16 or 32
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < DK * VS / 4; e += NTH) {
             const int d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
             float4 sv = {0.f, 0.f, 0.f, 0.f}, hv = sv;
@@ -487,7 +584,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
             sU[at] = u4.x; sU[at + 1] = u4.y; sU[at + 2] = u4.z; sU[at + 3] = u4.w;
             sdU[at] = du4.x; sdU[at + 1] = du4.y; sdU[at + 2] = du4.z; sdU[at + 3] = du4.w;
         }
-        __syncthreads();
+        lds_barrier();
         for (int s = 0; s < VS / 4; ++s) {
             const int m = 4 * s + g;
             const int ra = (16 * w + i16) * SP + m;
@@ -510,7 +607,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
         }
     }
     atomicAdd(&shs, hs);
-    __syncthreads();
+    lds_barrier();
 
     // ---- q, k rows and the 64 x 64 matrices
     float* sK = s1;
@@ -520,7 +617,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
     load_mat(sM0, a.wT + mo, tid);
     load_mat(sM1, a.wP + mo, tid);
     load_mat(sM2, a.wA + mo, tid);
-    __syncthreads();
+    lds_barrier();
 
     const int rb = 16 * w + 4 * g;   // this lane's first accumulator row
     float rowg[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -561,7 +658,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
             sM4[r * PT + i] = dtv * sb[i];
         }
     }
-    __syncthreads();
+    lds_barrier();
     // Y = T^T dT  (rows 16 w .. of Y; T[m][a] vanishes for m < a)
     f32x4 y[4];
 #pragma unroll
@@ -572,12 +669,12 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
             y[I] = mfma_f32x4(sM0[m * PT + 16 * w + i16], sM4[m * PT + 16 * I + i16], y[I]);
         }
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
         for (int j = 0; j < 4; ++j) sM4[(rb + j) * PT + 16 * I + i16] = y[I][j];
-    __syncthreads();
+    lds_barrier();
     // dA = -Y T^T on the strict lower part (column blocks I <= w), then
     // M = Diag(beta) (dA o E) into sM1 (P is no longer read)
 #pragma unroll
@@ -602,7 +699,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
             sM1[r * PT + cc] = lo ? dav * sb[r] * expf(sg[r] - sg[cc]) : 0.f;
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dq += N K;  dk += M K + N^T Q + M^T K
 #pragma unroll
     for (int D = 0; D < ND; ++D) {
@@ -642,7 +739,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
         x += __shfl_xor(x, 32);
         if (l == 0) atomicAdd(&sdg[CH - 1], x);
     }
-    __syncthreads();
+    lds_barrier();
     if (w == 0) {
         // d log alpha_t = sum over r >= t of dg_r (suffix sum over the lanes)
         float x = sdg[l];
