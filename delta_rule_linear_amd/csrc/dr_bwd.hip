@@ -67,29 +67,29 @@ __device__ __forceinline__ void load_mat(float* dst, const float* src, int tid) 
 // Register prefetch of a chunk's q or k rows: raw values (bf16 bits or fp32),
 // loaded one chunk ahead and converted when stored to LDS.  Rows past the end
 // load row 0 (in bounds) and are zeroed on the store.
-template <int DK, bool F32IN>
+template <int DK, bool F32IN, int NT = NTH>
 struct RowsPre {
-    static constexpr int N = CH * DK / 8 / NTH;
+    static constexpr int N = CH * DK / 8 / NT;
     Raw8<F32IN> x[N];
 };
 
-template <int DK, bool F32IN>
-__device__ __forceinline__ void pre_rows(RowsPre<DK, F32IN>& p, const void* src, size_t tok0, int valid,
+template <int DK, bool F32IN, int NT>
+__device__ __forceinline__ void pre_rows(RowsPre<DK, F32IN, NT>& p, const void* src, size_t tok0, int valid,
                                          int tid) {
 #pragma unroll
-    for (int n = 0; n < RowsPre<DK, F32IN>::N; ++n) {
-        const int e = tid + n * NTH;
+    for (int n = 0; n < RowsPre<DK, F32IN, NT>::N; ++n) {
+        const int e = tid + n * NT;
         const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
         p.x[n] = ld_raw8<F32IN>(src, (tok0 + (r < valid ? r : 0)) * DK + c8);
     }
 }
 
-template <int DK, bool F32IN>
-__device__ __forceinline__ void put_rows(const RowsPre<DK, F32IN>& p, float* dst, int valid, int tid) {
+template <int DK, bool F32IN, int NT>
+__device__ __forceinline__ void put_rows(const RowsPre<DK, F32IN, NT>& p, float* dst, int valid, int tid) {
     constexpr int KP = DK + 1;
 #pragma unroll
-    for (int n = 0; n < RowsPre<DK, F32IN>::N; ++n) {
-        const int e = tid + n * NTH;
+    for (int n = 0; n < RowsPre<DK, F32IN, NT>::N; ++n) {
+        const int e = tid + n * NT;
         const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
         float x[8];
         cvt_raw8<F32IN>(p.x[n], r < valid, x);
@@ -99,19 +99,22 @@ __device__ __forceinline__ void put_rows(const RowsPre<DK, F32IN>& p, float* dst
 }
 
 // Register prefetch of a 64 x 64 fp32 workspace matrix.
+template <int NT = NTH>
 struct MatPre {
-    float4 x[CH * CH / 4 / NTH];
+    float4 x[CH * CH / 4 / NT];
 };
 
-__device__ __forceinline__ void pre_mat(MatPre& p, const float* src, int tid) {
+template <int NT>
+__device__ __forceinline__ void pre_mat(MatPre<NT>& p, const float* src, int tid) {
 #pragma unroll
-    for (int n = 0; n < CH * CH / 4 / NTH; ++n) p.x[n] = reinterpret_cast<const float4*>(src)[tid + n * NTH];
+    for (int n = 0; n < CH * CH / 4 / NT; ++n) p.x[n] = reinterpret_cast<const float4*>(src)[tid + n * NT];
 }
 
-__device__ __forceinline__ void put_mat(const MatPre& p, float* dst, int tid) {
+template <int NT>
+__device__ __forceinline__ void put_mat(const MatPre<NT>& p, float* dst, int tid) {
 #pragma unroll
-    for (int n = 0; n < CH * CH / 4 / NTH; ++n) {
-        const int e = tid + n * NTH, r = e >> 4, c = (e & 15) * 4;
+    for (int n = 0; n < CH * CH / 4 / NT; ++n) {
+        const int e = tid + n * NT, r = e >> 4, c = (e & 15) * 4;
         dst[r * PT + c] = p.x[n].x;
         dst[r * PT + c + 1] = p.x[n].y;
         dst[r * PT + c + 2] = p.x[n].z;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
 
     RowsPre<DK, F32IN> pk;
-    MatPre pt;
+    MatPre<> pt;
     float pg = 0.f, pb = 0.f, pv[4];
     auto prefetch = [&](int c) {
         const size_t cs = (size_t)seq * a.NC + c;
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
 
     RowsPre<DK, F32IN> pk, pq;
-    MatPre pt, pp;
+    MatPre<> pt, pp;
     float pg = 0.f, pg63 = 0.f, pb = 0.f, po[4];
     auto prefetch = [&](int c) {
         const size_t cs = (size_t)seq * a.NC + c;
@@ -480,6 +483,13 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
 }
 
 // -------------------------------------------------- per-chunk gradient terms
+// Eight waves: wave w takes the 16 rows 16 (w & 3) .. of every product and
+// half (w >> 2) of its columns.  The state-sized operands stream through LDS
+// in slabs of 32 state columns, each prefetched into registers while the
+// previous slab is multiplied; the last slab's turn prefetches q, k, T, P
+// and K K^T o E for the 64 x 64 part.
+constexpr int PNT = 512;
+
 template <int DK>
 struct PostLds {
     static constexpr int KP = DK + 1;
@@ -498,13 +508,19 @@ __device__ __forceinline__ float col4_sum(float x) {
     return x;
 }
 
+__device__ __forceinline__ void st4(float* p, const float4& v) {
+    p[0] = v.x; p[1] = v.y; p[2] = v.z; p[3] = v.w;
+}
+
 template <int DK, bool F32IN>
-__global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
+__global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     using Lp = PostLds<DK>;
-    constexpr int KP = Lp::KP, VS = Lp::VS, SP = Lp::SP, ND = DK / 16;
+    constexpr int KP = Lp::KP, VS = Lp::VS, SP = Lp::SP, ND = DK / 16, NDH = ND / 2;
+    constexpr int NS = DK * VS / 4 / PNT;   // float4 of S (and of H) per thread and slab
+    static_assert(CH * VS / 4 == PNT, "one float4 of each 64-row slab per thread");
     __shared__ float s1[Lp::R1];
     __shared__ float sM0[CH * PT];   // T
-    __shared__ float sM1[CH * PT];   // P, then M = dA Diag-row(beta) o E
+    __shared__ float sM1[CH * PT];   // P, then M = Diag(beta) (dA o E)
     __shared__ float sM2[CH * PT];   // K K^T o E (strict lower)
     __shared__ float sM3[CH * PT];   // N = dP o E
     __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
@@ -516,6 +532,7 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
     const size_t tok0 = (size_t)seq * a.L + t0;
     const int Dv = a.Dv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, hf = w >> 2, D0 = hf * NDH;
     const size_t mo = (size_t)cs * CH * CH;
 
     if (tid < CH) {
@@ -530,14 +547,44 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
     }
     if (tid == 0) shs = 0.f;
 
+    // ---- slab prefetch registers
+    float4 ps[NS], ph[NS], po, pd, pr, pu, pdu;
+    auto pre_slab = [&](int v0) {
+        const int vw = min(VS, Dv - v0);   // 16 or 32
+        const float4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
+            ps[n] = ph[n] = z;
+            if (c4 < vw) {
+                const size_t off = ((size_t)cs * DK + d) * Dv + v0 + c4;
+                ps[n] = *reinterpret_cast<const float4*>(a.wS + off);
+                ph[n] = *reinterpret_cast<const float4*>(a.wH + off);
+            }
+        }
+        const int r = tid / (VS / 4), c4 = (tid % (VS / 4)) * 4;
+        po = pd = pr = pu = pdu = z;
+        if (c4 < vw) {
+            const size_t wo = ((size_t)cs * CH + r) * Dv + v0 + c4;
+            pr = *reinterpret_cast<const float4*>(a.wR + wo);
+            pu = *reinterpret_cast<const float4*>(a.wU + wo);
+            pdu = *reinterpret_cast<const float4*>(a.wdU + wo);
+            const size_t io = (tok0 + (r < valid ? r : 0)) * Dv + v0 + c4;
+            po = *reinterpret_cast<const float4*>(a.dO + io);
+            pd = *reinterpret_cast<const float4*>(a.dv + io);
+        }
+    };
+    RowsPre<DK, F32IN, PNT> pk, pq;
+    MatPre<PNT> pt, pp, pa;
+
     // ---- state terms over slabs of VS state columns:
-    //   z1 = dO S^T, z2 = dR S^T, z3 = U H^T  (rows 16 w .., all DK columns)
-    //   dp = dO U^T, dt = dU R^T              (rows 16 w .., all 64 columns)
-    f32x4 z1[ND], z2[ND], z3[ND], dp[4], dt[4];
+    //   z1 = dO S^T, z2 = dR S^T, z3 = U H^T   (rows 16 R .., column blocks D0 ..)
+    //   acc = dO U^T (hf 0) or dU R^T (hf 1)   (rows 16 R .., column blocks I <= R)
+    f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
 #pragma unroll
-    for (int D = 0; D < ND; ++D) z1[D] = z2[D] = z3[D] = zero4();
+    for (int D = 0; D < NDH; ++D) z1[D] = z2[D] = z3[D] = zero4();
 #pragma unroll
-    for (int I = 0; I < 4; ++I) dp[I] = dt[I] = zero4();
+    for (int I = 0; I < 4; ++I) acc[I] = zero4();
     float hs = 0.f;
     float* sS = s1;
     float* sH = sS + DK * SP;
@@ -546,63 +593,58 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
     float* sU = sRr + CH * SP;
     float* sdU = sU + CH * SP;
     float* sdR = sdU + CH * SP;
+    pre_slab(0);
     for (int v0 = 0; v0 < Dv; v0 += VS) {
-        const int vw = min(VS, Dv - v0);   // 16 or 32
         lds_barrier();
-        for (int e = tid; e < DK * VS / 4; e += NTH) {
-            const int d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
-            float4 sv = {0.f, 0.f, 0.f, 0.f}, hv = sv;
-            if (c4 < vw) {
-                const size_t off = ((size_t)cs * DK + d) * Dv + v0 + c4;
-                sv = *reinterpret_cast<const float4*>(a.wS + off);
-                hv = *reinterpret_cast<const float4*>(a.wH + off);
-            }
-            hs += sv.x * hv.x + sv.y * hv.y + sv.z * hv.z + sv.w * hv.w;
-            float* ps = sS + d * SP + c4;
-            float* ph = sH + d * SP + c4;
-            ps[0] = sv.x; ps[1] = sv.y; ps[2] = sv.z; ps[3] = sv.w;
-            ph[0] = hv.x; ph[1] = hv.y; ph[2] = hv.z; ph[3] = hv.w;
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
+            hs += ps[n].x * ph[n].x + ps[n].y * ph[n].y + ps[n].z * ph[n].z + ps[n].w * ph[n].w;
+            st4(sS + d * SP + c4, ps[n]);
+            st4(sH + d * SP + c4, ph[n]);
         }
-        for (int e = tid; e < CH * VS / 4; e += NTH) {
-            const int r = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
-            float4 o4 = {0.f, 0.f, 0.f, 0.f}, d4 = o4, r4 = o4, u4 = o4, du4 = o4;
-            if (c4 < vw) {
-                const size_t wo = ((size_t)cs * CH + r) * Dv + v0 + c4;
-                r4 = *reinterpret_cast<const float4*>(a.wR + wo);
-                u4 = *reinterpret_cast<const float4*>(a.wU + wo);
-                du4 = *reinterpret_cast<const float4*>(a.wdU + wo);
-                if (r < valid) {
-                    const size_t io = (tok0 + r) * Dv + v0 + c4;
-                    o4 = *reinterpret_cast<const float4*>(a.dO + io);
-                    d4 = *reinterpret_cast<const float4*>(a.dv + io);
-                }
-            }
-            const int at = r * SP + c4;
-            sO[at] = o4.x; sO[at + 1] = o4.y; sO[at + 2] = o4.z; sO[at + 3] = o4.w;
-            sdR[at] = d4.x; sdR[at + 1] = d4.y; sdR[at + 2] = d4.z; sdR[at + 3] = d4.w;
-            sRr[at] = r4.x; sRr[at + 1] = r4.y; sRr[at + 2] = r4.z; sRr[at + 3] = r4.w;
-            sU[at] = u4.x; sU[at + 1] = u4.y; sU[at + 2] = u4.z; sU[at + 3] = u4.w;
-            sdU[at] = du4.x; sdU[at + 1] = du4.y; sdU[at + 2] = du4.z; sdU[at + 3] = du4.w;
+        {
+            const int r = tid / (VS / 4), c4 = (tid % (VS / 4)) * 4, at = r * SP + c4;
+            const float4 z = {0.f, 0.f, 0.f, 0.f};
+            st4(sO + at, r < valid ? po : z);
+            st4(sdR + at, r < valid ? pd : z);
+            st4(sRr + at, pr);
+            st4(sU + at, pu);
+            st4(sdU + at, pdu);
         }
         lds_barrier();
+        if (v0 + VS < Dv) {
+            pre_slab(v0 + VS);
+        } else {
+            if constexpr (!F32IN) {   // fp32 rows would not fit the register budget
+                pre_rows<DK, F32IN, PNT>(pk, a.k, tok0, valid, tid);
+                pre_rows<DK, F32IN, PNT>(pq, a.q, tok0, valid, tid);
+            }
+            pre_mat(pt, a.wT + mo, tid);
+            pre_mat(pp, a.wP + mo, tid);
+            pre_mat(pa, a.wA + mo, tid);
+        }
         for (int s = 0; s < VS / 4; ++s) {
             const int m = 4 * s + g;
-            const int ra = (16 * w + i16) * SP + m;
-            const float ao = sO[ra], ar = sdR[ra], au = sU[ra], adu = sdU[ra];
+            const int ra = (16 * R + i16) * SP + m;
+            const float ao = sO[ra], ar = sdR[ra], au = sU[ra];
 #pragma unroll
-            for (int D = 0; D < ND; ++D) {
-                const float bs = sS[(16 * D + i16) * SP + m];
-                const float bh = sH[(16 * D + i16) * SP + m];
+            for (int D = 0; D < NDH; ++D) {
+                const float bs = sS[(16 * (D0 + D) + i16) * SP + m];
+                const float bh = sH[(16 * (D0 + D) + i16) * SP + m];
                 z1[D] = mfma_f32x4(ao, bs, z1[D]);
                 z2[D] = mfma_f32x4(ar, bs, z2[D]);
                 z3[D] = mfma_f32x4(au, bh, z3[D]);
             }
+            if (hf == 0) {
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                if (I <= w) {
-                    dp[I] = mfma_f32x4(ao, sU[(16 * I + i16) * SP + m], dp[I]);
-                    dt[I] = mfma_f32x4(adu, sRr[(16 * I + i16) * SP + m], dt[I]);
-                }
+                for (int I = 0; I < 4; ++I)
+                    if (I <= R) acc[I] = mfma_f32x4(ao, sU[(16 * I + i16) * SP + m], acc[I]);
+            } else {
+                const float adu = sdU[ra];
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+                    if (I <= R) acc[I] = mfma_f32x4(adu, sRr[(16 * I + i16) * SP + m], acc[I]);
             }
         }
     }
@@ -612,24 +654,37 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
     // ---- q, k rows and the 64 x 64 matrices
     float* sK = s1;
     float* sQ = s1 + CH * KP;
-    load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
-    load_rows<DK, F32IN>(sQ, a.q, tok0, valid, tid);
-    load_mat(sM0, a.wT + mo, tid);
-    load_mat(sM1, a.wP + mo, tid);
-    load_mat(sM2, a.wA + mo, tid);
+    if constexpr (F32IN) {
+        for (int e = tid; e < CH * DK / 8; e += PNT) {
+            const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+            float x[8];
+            load8<F32IN>(a.k, (tok0 + r) * DK + c8, r < valid, x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sK[r * KP + c8 + j] = x[j];
+            load8<F32IN>(a.q, (tok0 + r) * DK + c8, r < valid, x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sQ[r * KP + c8 + j] = x[j];
+        }
+    } else {
+        put_rows<DK, F32IN, PNT>(pk, sK, valid, tid);
+        put_rows<DK, F32IN, PNT>(pq, sQ, valid, tid);
+    }
+    put_mat(pt, sM0, tid);
+    put_mat(pp, sM1, tid);
+    put_mat(pa, sM2, tid);
     lds_barrier();
 
-    const int rb = 16 * w + 4 * g;   // this lane's first accumulator row
+    const int rb = 16 * R + 4 * g;   // this lane's first accumulator row
     float rowg[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f};
     float colg[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};
     float g63part = 0.f;
     // state terms: dq = Gamma z1, dk = -Gamma z2 + Lambda z3
-    f32x4 dq[ND], dk[ND];
+    f32x4 dq[NDH], dk[NDH];
 #pragma unroll
-    for (int D = 0; D < ND; ++D) {
+    for (int D = 0; D < NDH; ++D) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = rb + j, col = 16 * D + i16;
+            const int r = rb + j, col = 16 * (D0 + D) + i16;
             const float qv = sQ[r * KP + col], kv = sK[r * KP + col];
             const float x1 = sgam[r] * z1[D][j];
             const float x2 = -sgam[r] * z2[D][j];
@@ -640,50 +695,54 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
             g63part += kv * x3;
         }
     }
-    // dP -> N = dP o E (lower), sums of dP o P; dT^ -> dT = dT^ Diag(beta),
-    // dbeta from dT^ o T
+    // hf 0: dP -> N = dP o E (lower) and the sums of dP o P;
+    // hf 1: dT^ -> dT = dT^ Diag(beta), and dbeta's column sums of dT^ o T
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = rb + j, i = 16 * I + i16;
             const bool lo = i <= r;
-            const float dpv = lo ? dp[I][j] : 0.f;
-            const float dtv = lo ? dt[I][j] : 0.f;
-            const float pd = dpv * sM1[r * PT + i];
-            rowg[j] += pd;
-            colg[I] -= pd;
-            sM3[r * PT + i] = lo ? dpv * expf(sg[r] - sg[i]) : 0.f;
-            colb[I] += dtv * sM0[r * PT + i];
-            sM4[r * PT + i] = dtv * sb[i];
+            const float x = lo ? acc[I][j] : 0.f;
+            if (hf == 0) {
+                const float pd_ = x * sM1[r * PT + i];
+                rowg[j] += pd_;
+                colg[I] -= pd_;
+                sM3[r * PT + i] = lo ? x * expf(sg[r] - sg[i]) : 0.f;
+            } else {
+                colb[I] += x * sM0[r * PT + i];
+                sM4[r * PT + i] = x * sb[i];
+            }
         }
     }
     lds_barrier();
-    // Y = T^T dT  (rows 16 w .. of Y; T[m][a] vanishes for m < a)
-    f32x4 y[4];
+    // Y = T^T dT  (rows 16 R .., column blocks 2 hf, 2 hf + 1; T[m][a] vanishes for m < a)
+    f32x4 y[2];
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-        y[I] = zero4();
-        for (int s = 4 * w; s < 16; ++s) {
+    for (int h = 0; h < 2; ++h) {
+        const int I = 2 * hf + h;
+        y[h] = zero4();
+        for (int s = 4 * R; s < 16; ++s) {
             const int m = 4 * s + g;
-            y[I] = mfma_f32x4(sM0[m * PT + 16 * w + i16], sM4[m * PT + 16 * I + i16], y[I]);
+            y[h] = mfma_f32x4(sM0[m * PT + 16 * R + i16], sM4[m * PT + 16 * I + i16], y[h]);
         }
     }
     lds_barrier();
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sM4[(rb + j) * PT + 16 * I + i16] = y[I][j];
+        for (int j = 0; j < 4; ++j) sM4[(rb + j) * PT + 16 * (2 * hf + h) + i16] = y[h][j];
     lds_barrier();
-    // dA = -Y T^T on the strict lower part (column blocks I <= w), then
-    // M = Diag(beta) (dA o E) into sM1 (P is no longer read)
+    // dA = -Y T^T on the strict lower part, then M = Diag(beta) (dA o E) into
+    // sM1 (P is no longer read)
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
+    for (int h = 0; h < 2; ++h) {
+        const int I = 2 * hf + h;
         f32x4 da = zero4();
-        if (I <= w) {
+        if (I <= R) {
             for (int s = 0; s < 4 * (I + 1); ++s) {
                 const int m = 4 * s + g;
-                da = mfma_f32x4(sM4[(16 * w + i16) * PT + m], sM0[(16 * I + i16) * PT + m], da);
+                da = mfma_f32x4(sM4[(16 * R + i16) * PT + m], sM0[(16 * I + i16) * PT + m], da);
             }
         }
 #pragma unroll
@@ -702,36 +761,37 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
     lds_barrier();
     // dq += N K;  dk += M K + N^T Q + M^T K
 #pragma unroll
-    for (int D = 0; D < ND; ++D) {
-        for (int s = 0; s < 4 * (w + 1); ++s) {
+    for (int D = 0; D < NDH; ++D) {
+        const int cb = 16 * (D0 + D) + i16;
+        for (int s = 0; s < 4 * (R + 1); ++s) {
             const int m = 4 * s + g;
-            const float kb = sK[m * KP + 16 * D + i16];
-            dq[D] = mfma_f32x4(sM3[(16 * w + i16) * PT + m], kb, dq[D]);
-            dk[D] = mfma_f32x4(sM1[(16 * w + i16) * PT + m], kb, dk[D]);
+            const float kb = sK[m * KP + cb];
+            dq[D] = mfma_f32x4(sM3[(16 * R + i16) * PT + m], kb, dq[D]);
+            dk[D] = mfma_f32x4(sM1[(16 * R + i16) * PT + m], kb, dk[D]);
         }
-        for (int s = 4 * w; s < 16; ++s) {
+        for (int s = 4 * R; s < 16; ++s) {
             const int m = 4 * s + g;
-            dk[D] = mfma_f32x4(sM3[m * PT + 16 * w + i16], sQ[m * KP + 16 * D + i16], dk[D]);
-            dk[D] = mfma_f32x4(sM1[m * PT + 16 * w + i16], sK[m * KP + 16 * D + i16], dk[D]);
+            dk[D] = mfma_f32x4(sM3[m * PT + 16 * R + i16], sQ[m * KP + cb], dk[D]);
+            dk[D] = mfma_f32x4(sM1[m * PT + 16 * R + i16], sK[m * KP + cb], dk[D]);
         }
     }
     // ---- reductions of the gate and strength terms
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const float sg_ = group_sum<16>(rowg[j]);
-        const float sb_ = group_sum<16>(rowb[j]);
+        const float xg = group_sum<16>(rowg[j]);
+        const float xb = group_sum<16>(rowb[j]);
         if (i16 == 0) {
-            atomicAdd(&sdg[rb + j], sg_);
-            atomicAdd(&sdb[rb + j], sb_);
+            atomicAdd(&sdg[rb + j], xg);
+            atomicAdd(&sdb[rb + j], xb);
         }
     }
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-        const float cg = col4_sum(colg[I]);
-        const float cb = col4_sum(colb[I]);
+        const float xg = col4_sum(colg[I]);
+        const float xb = col4_sum(colb[I]);
         if (g == 0) {
-            atomicAdd(&sdg[16 * I + i16], cg);
-            atomicAdd(&sdb[16 * I + i16], cb);
+            atomicAdd(&sdg[16 * I + i16], xg);
+            atomicAdd(&sdb[16 * I + i16], xb);
         }
     }
     {
@@ -755,13 +815,13 @@ __global__ __launch_bounds__(NTH) void bwd_post_kernel(BwdArgs a) {
         }
     }
 #pragma unroll
-    for (int D = 0; D < ND; ++D) {
+    for (int D = 0; D < NDH; ++D) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = rb + j;
             if (r < valid) {
-                a.dq[(tok0 + r) * DK + 16 * D + i16] = dq[D][j];
-                a.dk[(tok0 + r) * DK + 16 * D + i16] = dk[D][j];
+                a.dq[(tok0 + r) * DK + 16 * (D0 + D) + i16] = dq[D][j];
+                a.dk[(tok0 + r) * DK + 16 * (D0 + D) + i16] = dk[D][j];
             }
         }
     }
@@ -774,7 +834,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_prep_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
     hipLaunchKernelGGL((bwd_fscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
     hipLaunchKernelGGL((bwd_rscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
-    hipLaunchKernelGGL((bwd_post_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((bwd_post_kernel<DK, F32IN>), dim3(nch), dim3(PNT), 0, st, a);
     return hipGetLastError();
 }
 
