@@ -24,6 +24,9 @@ Also reported in the same line:
   configs       the other forward workloads (FG2-GDN and FG2-GDN+ at the
                 headline shape, KDA, GDN at L=4K and 64K, GDN with the input
                 preparation and with write-side key scales), a few steps each;
+  backward      dr_chunk_bwd on the headline batch (seeded dO and dS_final),
+                per-kernel times, the dominant kernel against the fp32
+                matrix-core peak, and the CPU oracle's backward on 4 heads;
   cpu_baseline  the fp64 CPU oracle on the whole headline batch, on the
                 host's cores, with the GPU result checked against it.
 The headline inputs follow the seeded NumPy recipe of
@@ -72,6 +75,24 @@ def scan_bytes_per_token_head(d: int, L: int) -> float:
     return 3 * d * 2 + 2 * TRI_BYTES / CH + 2 * 4 + d * 4 + 2 * d * d * 4 / L
 
 
+# the backward (gradients of the chunked forward), algorithmic flops per chunk of
+# C tokens at d_k = dk, d_v = dv: the chunk algebra's products, those with a
+# triangular C x C factor counted at half:
+#   prep   K K^T and Q K^T                                   2 C^2 dk
+#   fscan  K S, T^ R, K^T (Lambda U)                         4 C dk dv + C^2 dv
+#   rscan  K H, P^T dO, T^T dU, Q^T dO, K^T dR               6 C dk dv + 2 C^2 dv
+#   post   dO S^T, dR S^T, U H^T, dO U^T, dU R^T, T^T dT, Y T^T,
+#          N K, N^T Q, M K, M^T K                            6 C dk dv + 2 C^2 dv + 2 C^3 + 4 C^2 dk
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix peak
+
+
+def bwd_flops_per_chunk(dk: int, dv: int) -> dict:
+    C = CH
+    return {"prep": 2 * C * C * dk, "fscan": 4 * C * dk * dv + C * C * dv,
+            "rscan": 6 * C * dk * dv + 2 * C * C * dv,
+            "post": 6 * C * dk * dv + 2 * C * C * dv + 2 * C ** 3 + 4 * C * C * dk}
+
+
 # decode, per state: S read and written once (fp32), q, k, v (bf16), the gate
 # and beta (fp32), o (fp32)
 def decode_bytes_per_state(d: int) -> int:
@@ -88,6 +109,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--config-steps", type=int, default=5,
                     help="timed steps per extra workload (0 skips them)")
+    ap.add_argument("--bwd-steps", type=int, default=5,
+                    help="timed steps of the backward on the headline batch (0 skips it)")
     ap.add_argument("--no-flush", action="store_true", help="do not rewrite the 512 MiB buffer between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -395,6 +418,67 @@ def main():
         del xq, xk, xv, xla, xbe, xbv, xks, xS0, xo, xSf, xws
     torch.cuda.empty_cache()
 
+    # ------------------------------------------------------------ backward
+    bwd = None
+    if args.bwd_steps > 0:
+        dO_np, dSf_np = inputs.backward_cotangents(p, 0)
+        gdO, gdSf = to_dev(dO_np), to_dev(dSf_np)
+        bdesc = drl.chunk_desc(B, H, L, D, D, drl.DR_BF16, drl.DR_F32, "scalar", "scalar")
+        bws = torch.empty(drl.dr_chunk_bwd_workspace_bytes(bdesc), dtype=torch.uint8, device=dev)
+        grads = {}
+
+        def bstep():
+            grads.update(drl.dr_chunk_bwd(q, k, v, la, be, S0, gdO, gdSf, gate="scalar", workspace=bws))
+
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        drl.dr_profile_begin()
+        bper = time_steps(bstep, args.bwd_steps, 0)
+        bprof = drl.dr_profile_end()
+        bms = float(np.median(bper))
+        calls = max(1, bprof["bwd_calls"])
+        kern = {n: bprof[f"bwd_{n}_ms"] / calls for n in ("prep", "fscan", "rscan", "post")}
+        nch = B * H * ((L + CH - 1) // CH)
+        kflops = {n: f * nch for n, f in bwd_flops_per_chunk(D, D).items()}
+        top = max(kern, key=kern.get)
+        ktf = kflops[top] / (kern[top] * 1e-3) / 1e12
+        btf = sum(kflops.values()) / (bms * 1e-3) / 1e12
+        bwd = {"workload": "gradients of the headline forward (B=2 H=16 L=16384 d=128, GDN gating, bf16 q/k/v), "
+                           "dO and dS_final ~ N(0, 1) fp32; all gradients fp32",
+               "ms_per_step": round(bms, 4), "tokens_per_s": round(B * L / (bms * 1e-3), 1),
+               "kernels_ms": {n: round(t, 4) for n, t in kern.items()},
+               "roofline": {"bound": "mfma", "kernel": f"bwd_{top}_kernel", "achieved": round(ktf, 2),
+                            "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(ktf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                            "alg_flops_per_launch": int(kflops[top])},
+               "mfma_whole_backward": {"achieved_tflops": round(btf, 2), "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
+                                       "frac": round(btf / FP32_MFMA_PEAK_TFLOPS, 4),
+                                       "alg_flops_per_step": int(sum(kflops.values()))},
+               "workspace_bytes": int(bws.numel())}
+        if not args.no_cpu_baseline:
+            import oracle
+            nh = 4
+            nthr = min(oracle.max_threads(), len(os.sched_getaffinity(0)), nh)
+            sl = lambda a: None if a is None else a[0:1, 0:nh]
+            tc = time.perf_counter()
+            ref = oracle.backward(sl(p.q), sl(p.k), sl(p.v), sl(p.log_alpha), sl(p.beta), sl(p.S0), sl(dO_np),
+                                  sl(dSf_np), gate="scalar", beta_mode="scalar", nthreads=nthr)
+            tcpu = time.perf_counter() - tc
+            bwd["cpu_baseline"] = {
+                "value": round(nh * L / H / tcpu, 1), "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+                "sample": f"{nh} of the {B * H} heads (b=0, h<{nh}) over all L={L} tokens, fp64 reverse-mode "
+                          f"of the token recurrence, one thread per head, {tcpu:.1f} s wall; tokens/s counts "
+                          f"{H} heads per token"}
+            errs = {}
+            for n in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"):
+                x = grads[n][0:1, 0:nh].double().cpu().numpy()
+                errs[n] = float(np.abs(x - ref[n]).max() / np.abs(ref[n]).max())
+            bwd["parity"] = {"heads": nh, "max_rel_err": errs, "tol": 3e-3}
+            del ref
+        del gdO, gdSf, bws, grads
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------ CPU baseline (oracle)
     cpu = None
     parity = None
@@ -441,6 +525,7 @@ def main():
                  "hbm_frac_whole_forward": round(fwd_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "decode": dec,
         "configs": configs,
+        "backward": bwd,
         "cpu_baseline": cpu,
         "parity": parity,
         "wall_s_timed": round(wall, 3),

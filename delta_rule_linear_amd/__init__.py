@@ -61,7 +61,9 @@ class ChunkDesc(ctypes.Structure):
 
 class ProfileReport(ctypes.Structure):
     _fields_ = [("chunk_calls", ctypes.c_int), ("decode_calls", ctypes.c_int), ("prep_ms", ctypes.c_double),
-                ("scan_ms", ctypes.c_double), ("decode_ms", ctypes.c_double)]
+                ("scan_ms", ctypes.c_double), ("decode_ms", ctypes.c_double), ("bwd_calls", ctypes.c_int),
+                ("bwd_prep_ms", ctypes.c_double), ("bwd_fscan_ms", ctypes.c_double),
+                ("bwd_rscan_ms", ctypes.c_double), ("bwd_post_ms", ctypes.c_double)]
 
 
 class DecodeDesc(ctypes.Structure):

@@ -156,11 +156,12 @@ dr_status dr_profile_end(dr_profile_report* report) {
     }
     *report = dr_profile_report{};
     hipError_t e = g_prof_err;
-    double ms[3] = {0, 0, 0};
+    double ms[dr::kProfSlots] = {};
     for (size_t i = 0; e == hipSuccess && i < g_prof.size(); ++i) {
         const int slot = g_prof[i].slot;
         if (slot == dr::kProfPrep) ++report->chunk_calls;
         if (slot == dr::kProfDecode) ++report->decode_calls;
+        if (slot == dr::kProfBwdPrep) ++report->bwd_calls;
         if (slot == dr::kProfEnd || i + 1 == g_prof.size()) continue;
         e = hipEventSynchronize(g_prof[i + 1].ev);
         float t = 0.f;
@@ -172,6 +173,10 @@ dr_status dr_profile_end(dr_profile_report* report) {
     report->prep_ms = ms[dr::kProfPrep];
     report->scan_ms = ms[dr::kProfScan];
     report->decode_ms = ms[dr::kProfDecode];
+    report->bwd_prep_ms = ms[dr::kProfBwdPrep];
+    report->bwd_fscan_ms = ms[dr::kProfBwdFscan];
+    report->bwd_rscan_ms = ms[dr::kProfBwdRscan];
+    report->bwd_post_ms = ms[dr::kProfBwdPost];
     return DR_OK;
 }
 

@@ -831,10 +831,15 @@ template <int DK, bool F32IN>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
     const unsigned nscan = (unsigned)((a.nseq + 7) / 8) * 8u * (unsigned)(a.Dv / 16);
+    prof_mark(st, kProfBwdPrep);
     hipLaunchKernelGGL((bwd_prep_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
+    prof_mark(st, kProfBwdFscan);
     hipLaunchKernelGGL((bwd_fscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
+    prof_mark(st, kProfBwdRscan);
     hipLaunchKernelGGL((bwd_rscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
+    prof_mark(st, kProfBwdPost);
     hipLaunchKernelGGL((bwd_post_kernel<DK, F32IN>), dim3(nch), dim3(PNT), 0, st, a);
+    prof_mark(st, kProfEnd);
     return hipGetLastError();
 }
 

@@ -128,7 +128,11 @@ struct BwdArgs {
 
 // Optional per-kernel timing: launchers mark the start of each kernel and the
 // end of their last one (dr_profile_begin / dr_profile_end).
-enum ProfSlot { kProfPrep = 0, kProfScan = 1, kProfDecode = 2, kProfEnd = 3 };
+enum ProfSlot {
+    kProfPrep = 0, kProfScan = 1, kProfDecode = 2,
+    kProfBwdPrep = 3, kProfBwdFscan = 4, kProfBwdRscan = 5, kProfBwdPost = 6,
+    kProfSlots = 7, kProfEnd = 7
+};
 void prof_mark(hipStream_t st, int slot);
 
 // sepv: a.beta_v differs from a.beta (channel beta only)

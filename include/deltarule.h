@@ -290,8 +290,8 @@ dr_status dr_chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, con
 
 /*
  * Per-kernel timing, for benchmarks and profiling (not part of the method).
- * Between dr_profile_begin and dr_profile_end every chunked-forward and
- * decode call also records HIP events on its stream around each kernel it
+ * Between dr_profile_begin and dr_profile_end every chunked-forward, backward
+ * and decode call also records HIP events on its stream around each kernel it
  * launches; dr_profile_end waits for those events and reports the summed
  * kernel durations (event to event, so a launch gap between two kernels of
  * one call is counted with the earlier kernel).  Calls made while profiling
@@ -305,6 +305,11 @@ typedef struct dr_profile_report {
     double prep_ms;     /* chunk preparation kernel (gates, A, T, P) */
     double scan_ms;     /* inter-chunk state scan kernel (o and S_final) */
     double decode_ms;   /* recurrent decode kernel */
+    int bwd_calls;      /* dr_chunk_bwd calls that launched kernels */
+    double bwd_prep_ms;   /* backward: per-chunk T, P and K K^T */
+    double bwd_fscan_ms;  /* backward: forward state scan (chunk start states) */
+    double bwd_rscan_ms;  /* backward: reverse scan of the state gradient */
+    double bwd_post_ms;   /* backward: per-chunk gradients of q, k, beta, log alpha */
 } dr_profile_report;
 
 dr_status dr_profile_begin(void);
