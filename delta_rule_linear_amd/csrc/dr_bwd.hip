@@ -134,12 +134,15 @@ __device__ __forceinline__ void scan_tile(const BwdArgs& a, int& seq, int& tile)
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     constexpr int KP = DK + 1;
-    __shared__ float sK[CH * KP];
-    __shared__ float sQ[CH * KP];
-    __shared__ float sA[CH * PT];
-    __shared__ float sT[CH * PT];
+    static_assert(2 * CH * PT <= 2 * CH * KP, "A and T fit where q and k were");
+    // q and k rows, then (once the products are in registers) A and T
+    __shared__ float sKQ[2 * CH * KP];
     __shared__ float sX[4][16 * 17];
     __shared__ float sg[CH], sb[CH];
+    float* sK = sKQ;
+    float* sQ = sKQ + CH * KP;
+    float* sA = sKQ;
+    float* sT = sKQ + CH * PT;
     const int cs = blockIdx.x;
     const int seq = cs / a.NC, c = cs - seq * a.NC;
     const int t0 = c * CH, valid = min(CH, a.L - t0);
@@ -164,27 +167,34 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     }
     lds_barrier();
 
-    // lower blocks (R = w, I <= R) of K K^T and Q K^T; E applied per element
+    // lower blocks (R = w, I <= R) of K K^T and Q K^T, kept in registers until
+    // every wave is done with the q and k rows; E applied per element
     {
         const int R = w;
+        f32x4 aK[4], aQ[4];
+#pragma unroll
         for (int I = 0; I < 4; ++I) {
-            f32x4 aK = zero4(), aQ = zero4();
+            aK[I] = aQ[I] = zero4();
             if (I <= R) {
                 for (int s = 0; s < DK / 4; ++s) {
                     const int m = 4 * s + g;
                     const float kb = sK[(16 * I + i16) * KP + m];
-                    aK = mfma_f32x4(sK[(16 * R + i16) * KP + m], kb, aK);
-                    aQ = mfma_f32x4(sQ[(16 * R + i16) * KP + m], kb, aQ);
+                    aK[I] = mfma_f32x4(sK[(16 * R + i16) * KP + m], kb, aK[I]);
+                    aQ[I] = mfma_f32x4(sQ[(16 * R + i16) * KP + m], kb, aQ[I]);
                 }
             }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
                 const float e = i <= r ? expf(sg[r] - sg[i]) : 0.f;
-                const float araw = i < r ? aK[j] * e : 0.f;
+                const float araw = i < r ? aK[I][j] * e : 0.f;
                 sA[r * PT + i] = sb[r] * araw;
                 a.wA[mo + r * CH + i] = araw;
-                a.wP[mo + r * CH + i] = i <= r ? aQ[j] * e : 0.f;
+                a.wP[mo + r * CH + i] = i <= r ? aQ[I][j] * e : 0.f;
             }
         }
     }
