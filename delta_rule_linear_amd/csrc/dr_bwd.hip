@@ -250,16 +250,21 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------- forward state scan
-// The next chunk's operands are loaded into registers while the current one
-// is computed; the barriers are LDS-only, so neither those loads nor the
-// workspace stores are waited for inside the loop.
+// Eight waves per workgroup: wave w takes the 16 rows 16 (w & 3) .. of X = K S
+// over half (w >> 2) of its contraction (the upper half's partial sums pass
+// through LDS), waves 0-3 form R and U, and wave w updates state rows
+// 16 w .. .  The next chunk's operands are loaded into registers while the
+// current one is computed; the barriers are LDS-only, so neither those loads
+// nor the workspace stores are waited for inside the loop.
+constexpr int SNT = 512;
+
 template <int DK, bool F32IN>
-__global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
-    constexpr int KP = DK + 1;
+__global__ __launch_bounds__(SNT) void bwd_fscan_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1, NKS = DK / 8;
     __shared__ float sK[CH * KP];
     __shared__ float sT[CH * PT];
     __shared__ float sS[DK * 17];
-    __shared__ float sR[CH * 17];
+    __shared__ float sR[CH * 17];   // upper-half partial X, then R
     __shared__ float sU[CH * 17];
     __shared__ float sg[CH], sb[CH];
     int seq, tile;
@@ -267,28 +272,31 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
     if (seq >= a.nseq) return;
     const int n0 = 16 * tile, Dv = a.Dv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, h = w >> 2;
 
-    RowsPre<DK, F32IN> pk;
-    MatPre<> pt;
-    float pg = 0.f, pb = 0.f, pv[4];
+    RowsPre<DK, F32IN, SNT> pk;
+    MatPre<SNT> pt;
+    float pg = 0.f, pb = 0.f, pv[4] = {0.f, 0.f, 0.f, 0.f};
     auto prefetch = [&](int c) {
         const size_t cs = (size_t)seq * a.NC + c;
         const int t0 = c * CH, valid = min(CH, a.L - t0);
         const size_t tok0 = (size_t)seq * a.L + t0;
-        pre_rows<DK, F32IN>(pk, a.k, tok0, valid, tid);
+        pre_rows<DK, F32IN, SNT>(pk, a.k, tok0, valid, tid);
         pre_mat(pt, a.wT + cs * CH * CH, tid);
         if (tid < CH) {
             pg = a.wG[cs * CH + tid];
             pb = a.beta[tok0 + (tid < valid ? tid : 0)];
         }
+        if (h == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            pv[j] = load1<F32IN>(a.v, (tok0 + (row < valid ? row : 0)) * Dv + n0 + i16);
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                pv[j] = load1<F32IN>(a.v, (tok0 + (row < valid ? row : 0)) * Dv + n0 + i16);
+            }
         }
     };
 
-    for (int e = tid; e < DK * 16; e += NTH) {
+    for (int e = tid; e < DK * 16; e += SNT) {
         const int d = e >> 4, cc = e & 15;
         sS[d * 17 + cc] = a.S0 ? a.S0[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
     }
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
         const size_t cs = (size_t)seq * a.NC + c;
         const int t0 = c * CH, valid = min(CH, a.L - t0);
         lds_barrier();
-        put_rows<DK, F32IN>(pk, sK, valid, tid);
+        put_rows<DK, F32IN, SNT>(pk, sK, valid, tid);
         put_mat(pt, sT, tid);
         if (tid < CH) {
             sg[tid] = pg;
@@ -305,53 +313,63 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
         }
         float vv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vv[j] = 16 * w + 4 * g + j < valid ? pv[j] : 0.f;
-        for (int e = tid; e < DK * 16; e += NTH) {
+        for (int j = 0; j < 4; ++j) vv[j] = 16 * R + 4 * g + j < valid ? pv[j] : 0.f;
+        for (int e = tid; e < DK * 16; e += SNT) {
             const int d = e >> 4, cc = e & 15;
             a.wS[(cs * DK + d) * Dv + n0 + cc] = sS[d * 17 + cc];
         }
         lds_barrier();
         if (c + 1 < a.NC) prefetch(c + 1);
-        // X = K S, R = V - Gamma X  (rows 16 w ..)
+        // X = K S over this wave's half of the contraction
         f32x4 X = zero4();
-        for (int s = 0; s < DK / 4; ++s) {
+        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
             const int m = 4 * s + g;
-            X = mfma_f32x4(sK[(16 * w + i16) * KP + m], sS[m * 17 + i16], X);
+            X = mfma_f32x4(sK[(16 * R + i16) * KP + m], sS[m * 17 + i16], X);
         }
+        if (h == 1) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            const float r = vv[j] - expf(sg[row]) * X[j];
-            sR[row * 17 + i16] = r;
-            a.wR[(cs * CH + row) * Dv + n0 + i16] = r;
+            for (int j = 0; j < 4; ++j) sR[(16 * R + 4 * g + j) * 17 + i16] = X[j];
         }
         lds_barrier();
-        // U = T Diag(beta) R
-        f32x4 U = zero4();
-        for (int s = 0; s < 4 * (w + 1); ++s) {
-            const int m = 4 * s + g;
-            U = mfma_f32x4(sT[(16 * w + i16) * PT + m] * sb[m], sR[m * 17 + i16], U);
+        if (h == 0) {
+            // R = V - Gamma X (each lane reads its own partial sums, then overwrites them)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                const float r = vv[j] - expf(sg[row]) * (X[j] + sR[row * 17 + i16]);
+                sR[row * 17 + i16] = r;
+                a.wR[(cs * CH + row) * Dv + n0 + i16] = r;
+            }
         }
+        lds_barrier();
         const float g63 = sg[CH - 1];
+        if (h == 0) {
+            // U = T Diag(beta) R
+            f32x4 U = zero4();
+            for (int s = 0; s < 4 * (R + 1); ++s) {
+                const int m = 4 * s + g;
+                U = mfma_f32x4(sT[(16 * R + i16) * PT + m] * sb[m], sR[m * 17 + i16], U);
+            }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            a.wU[(cs * CH + row) * Dv + n0 + i16] = U[j];
-            sU[row * 17 + i16] = expf(g63 - sg[row]) * U[j];
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                a.wU[(cs * CH + row) * Dv + n0 + i16] = U[j];
+                sU[row * 17 + i16] = expf(g63 - sg[row]) * U[j];
+            }
         }
         lds_barrier();
-        // S <- gamma_63 S + K^T Lambda U
-        const float gam63 = expf(g63);
-        for (int b = w; b < DK / 16; b += 4) {
+        // S <- gamma_63 S + K^T Lambda U  (state rows 16 w ..)
+        if (w < DK / 16) {
+            const float gam63 = expf(g63);
             f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
-                acc = mfma_f32x4(sK[m * KP + 16 * b + i16], sU[m * 17 + i16], acc);
+                acc = mfma_f32x4(sK[m * KP + 16 * w + i16], sU[m * 17 + i16], acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d = 16 * b + 4 * g + j;
+                const int d = 16 * w + 4 * g + j;
                 sS[d * 17 + i16] = gam63 * sS[d * 17 + i16] + acc[j];
             }
         }
@@ -359,33 +377,37 @@ __global__ __launch_bounds__(NTH) void bwd_fscan_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------ reverse adjoint scan
-// Prefetched one chunk ahead (backwards) like the forward scan.
+// Eight waves, prefetched one chunk ahead (backwards) like the forward scan:
+// Z = K H split over the contraction's halves, the upper-half waves also
+// forming P^T dO; waves 0-3 then finish dU and dV; wave w updates H's rows
+// 16 w .. .
 template <int DK, bool F32IN>
-__global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
-    constexpr int KP = DK + 1;
+__global__ __launch_bounds__(SNT) void bwd_rscan_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1, NKS = DK / 8;
     __shared__ float sK[CH * KP];
     __shared__ float sQ[CH * KP];
     __shared__ float sT[CH * PT];
     __shared__ float sP[CH * PT];
     __shared__ float sH[DK * 17];
     __shared__ float sO[CH * 17];   // dO, then Gamma dO
-    __shared__ float sD[CH * 17];   // dU, then Gamma dR
+    __shared__ float sD[CH * 17];   // upper-half partial dU, then dU, then Gamma dR
     __shared__ float sgam[CH], slam[CH], sb[CH];
     int seq, tile;
     scan_tile(a, seq, tile);
     if (seq >= a.nseq) return;
     const int n0 = 16 * tile, Dv = a.Dv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, h = w >> 2;
 
-    RowsPre<DK, F32IN> pk, pq;
-    MatPre<> pt, pp;
-    float pg = 0.f, pg63 = 0.f, pb = 0.f, po[4];
+    RowsPre<DK, F32IN, SNT> pk, pq;
+    MatPre<SNT> pt, pp;
+    float pg = 0.f, pg63 = 0.f, pb = 0.f, po[4] = {0.f, 0.f, 0.f, 0.f};
     auto prefetch = [&](int c) {
         const size_t cs = (size_t)seq * a.NC + c;
         const int t0 = c * CH, valid = min(CH, a.L - t0);
         const size_t tok0 = (size_t)seq * a.L + t0;
-        pre_rows<DK, F32IN>(pk, a.k, tok0, valid, tid);
-        pre_rows<DK, F32IN>(pq, a.q, tok0, valid, tid);
+        pre_rows<DK, F32IN, SNT>(pk, a.k, tok0, valid, tid);
+        pre_rows<DK, F32IN, SNT>(pq, a.q, tok0, valid, tid);
         pre_mat(pt, a.wT + cs * CH * CH, tid);
         pre_mat(pp, a.wP + cs * CH * CH, tid);
         if (tid < CH) {
@@ -393,14 +415,16 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
             pg63 = a.wG[cs * CH + CH - 1];
             pb = a.beta[tok0 + (tid < valid ? tid : 0)];
         }
+        if (h == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            po[j] = a.dO[(tok0 + (row < valid ? row : 0)) * Dv + n0 + i16];
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                po[j] = a.dO[(tok0 + (row < valid ? row : 0)) * Dv + n0 + i16];
+            }
         }
     };
 
-    for (int e = tid; e < DK * 16; e += NTH) {
+    for (int e = tid; e < DK * 16; e += SNT) {
         const int d = e >> 4, cc = e & 15;
         sH[d * 17 + cc] = a.dS_final ? a.dS_final[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
     }
@@ -410,8 +434,8 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
         const int t0 = c * CH, valid = min(CH, a.L - t0);
         const size_t tok0 = (size_t)seq * a.L + t0;
         lds_barrier();
-        put_rows<DK, F32IN>(pk, sK, valid, tid);
-        put_rows<DK, F32IN>(pq, sQ, valid, tid);
+        put_rows<DK, F32IN, SNT>(pk, sK, valid, tid);
+        put_rows<DK, F32IN, SNT>(pq, sQ, valid, tid);
         put_mat(pt, sT, tid);
         put_mat(pp, sP, tid);
         if (tid < CH) {
@@ -419,73 +443,91 @@ __global__ __launch_bounds__(NTH) void bwd_rscan_kernel(BwdArgs a) {
             slam[tid] = expf(pg63 - pg);
             sb[tid] = tid < valid ? pb : 0.f;
         }
-        float od[4];
+        float od[4] = {0.f, 0.f, 0.f, 0.f};
+        if (h == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            od[j] = row < valid ? po[j] : 0.f;
-            sO[row * 17 + i16] = od[j];
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                od[j] = row < valid ? po[j] : 0.f;
+                sO[row * 17 + i16] = od[j];
+            }
         }
-        for (int e = tid; e < DK * 16; e += NTH) {
+        for (int e = tid; e < DK * 16; e += SNT) {
             const int d = e >> 4, cc = e & 15;
             a.wH[(cs * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
         }
         lds_barrier();
         if (c > 0) prefetch(c - 1);
-        // dU = P^T dO + Lambda K H  (rows 16 w ..)
-        f32x4 Z = zero4(), Y = zero4();
-        for (int s = 0; s < DK / 4; ++s) {
+        // dU = P^T dO + Lambda K H  (rows 16 R ..): K H over this wave's half
+        // of the contraction; the upper half also takes P^T dO
+        f32x4 Z = zero4();
+        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
             const int m = 4 * s + g;
-            Z = mfma_f32x4(sK[(16 * w + i16) * KP + m], sH[m * 17 + i16], Z);
+            Z = mfma_f32x4(sK[(16 * R + i16) * KP + m], sH[m * 17 + i16], Z);
         }
-        for (int s = 4 * w; s < 16; ++s) {
-            const int m = 4 * s + g;
-            Y = mfma_f32x4(sP[m * PT + 16 * w + i16], sO[m * 17 + i16], Y);
-        }
+        if (h == 1) {
+            f32x4 Y = zero4();
+            for (int s = 4 * R; s < 16; ++s) {
+                const int m = 4 * s + g;
+                Y = mfma_f32x4(sP[m * PT + 16 * R + i16], sO[m * 17 + i16], Y);
+            }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            const float du = slam[row] * Z[j] + Y[j];
-            sD[row * 17 + i16] = du;
-            a.wdU[(cs * CH + row) * Dv + n0 + i16] = du;
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                sD[row * 17 + i16] = slam[row] * Z[j] + Y[j];
+            }
+        }
+        lds_barrier();
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                const float du = slam[row] * Z[j] + sD[row * 17 + i16];
+                sD[row * 17 + i16] = du;
+                a.wdU[(cs * CH + row) * Dv + n0 + i16] = du;
+            }
         }
         lds_barrier();
         // dR = Diag(beta) T^T dU
         f32x4 Rr = zero4();
-        for (int s = 4 * w; s < 16; ++s) {
-            const int m = 4 * s + g;
-            Rr = mfma_f32x4(sT[m * PT + 16 * w + i16], sD[m * 17 + i16], Rr);
+        if (h == 0) {
+            for (int s = 4 * R; s < 16; ++s) {
+                const int m = 4 * s + g;
+                Rr = mfma_f32x4(sT[m * PT + 16 * R + i16], sD[m * 17 + i16], Rr);
+            }
         }
         const float gam63 = sgam[CH - 1];
         lds_barrier();
+        if (h == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = 16 * w + 4 * g + j;
-            const float dr = sb[row] * Rr[j];
-            if (row < valid) a.dv[(tok0 + row) * Dv + n0 + i16] = dr;
-            sD[row * 17 + i16] = sgam[row] * dr;
-            sO[row * 17 + i16] = sgam[row] * od[j];
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                const float dr = sb[row] * Rr[j];
+                if (row < valid) a.dv[(tok0 + row) * Dv + n0 + i16] = dr;
+                sD[row * 17 + i16] = sgam[row] * dr;
+                sO[row * 17 + i16] = sgam[row] * od[j];
+            }
         }
         lds_barrier();
-        // H <- gamma_63 H + Q^T Gamma dO - K^T Gamma dR
-        for (int b = w; b < DK / 16; b += 4) {
-            f32x4 acc = zero4();
+        // H <- gamma_63 H + Q^T Gamma dO - K^T Gamma dR  (state rows 16 w ..)
+        if (w < DK / 16) {
+            f32x4 hq = zero4(), hk = zero4();
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
-                acc = mfma_f32x4(sQ[m * KP + 16 * b + i16], sO[m * 17 + i16], acc);
-                acc = mfma_f32x4(-sK[m * KP + 16 * b + i16], sD[m * 17 + i16], acc);
+                hq = mfma_f32x4(sQ[m * KP + 16 * w + i16], sO[m * 17 + i16], hq);
+                hk = mfma_f32x4(sK[m * KP + 16 * w + i16], sD[m * 17 + i16], hk);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d = 16 * b + 4 * g + j;
-                sH[d * 17 + i16] = gam63 * sH[d * 17 + i16] + acc[j];
+                const int d = 16 * w + 4 * g + j;
+                sH[d * 17 + i16] = gam63 * sH[d * 17 + i16] + (hq[j] - hk[j]);
             }
         }
     }
     lds_barrier();
     if (a.dS0) {
-        for (int e = tid; e < DK * 16; e += NTH) {
+        for (int e = tid; e < DK * 16; e += SNT) {
             const int d = e >> 4, cc = e & 15;
             a.dS0[((size_t)seq * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
         }
@@ -844,9 +886,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     prof_mark(st, kProfBwdPrep);
     hipLaunchKernelGGL((bwd_prep_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
     prof_mark(st, kProfBwdFscan);
-    hipLaunchKernelGGL((bwd_fscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((bwd_fscan_kernel<DK, F32IN>), dim3(nscan), dim3(SNT), 0, st, a);
     prof_mark(st, kProfBwdRscan);
-    hipLaunchKernelGGL((bwd_rscan_kernel<DK, F32IN>), dim3(nscan), dim3(NTH), 0, st, a);
+    hipLaunchKernelGGL((bwd_rscan_kernel<DK, F32IN>), dim3(nscan), dim3(SNT), 0, st, a);
     prof_mark(st, kProfBwdPost);
     hipLaunchKernelGGL((bwd_post_kernel<DK, F32IN>), dim3(nch), dim3(PNT), 0, st, a);
     prof_mark(st, kProfEnd);
