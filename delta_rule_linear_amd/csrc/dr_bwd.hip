@@ -546,11 +546,42 @@ template <int DK>
 struct PostLds {
     static constexpr int KP = DK + 1;
     static constexpr int VS = 32;          // state columns per slab
-    static constexpr int SP = VS + 1;
-    static constexpr int SLAB = 2 * DK * SP + 5 * CH * SP;
+    // slab planes: (S, H: DK rows; dO, dV, R, U, dU: 64 rows) x 32 columns x
+    // (hi, lo) fp16, in floats
+    static constexpr int SLAB = (2 * DK + 5 * CH) * VS;
     static constexpr int QK = 2 * CH * KP;
     static constexpr int R1 = SLAB > QK ? SLAB : QK;
 };
+
+// A slab operand in LDS: rows of 32 state columns as two fp16 planes, hi and
+// lo (x ~ hi + lo, about 22 significant bits).  Row r keeps its four
+// eight-column groups in the order grp ^ ((r >> 2) & 3), so that the 16 lanes
+// that read one group of 16 consecutive rows fall on distinct banks.
+__device__ __forceinline__ int slab_off(int r, int grp) { return r * 32 + 8 * (grp ^ ((r >> 2) & 3)); }
+
+typedef half_t half4_t __attribute__((ext_vector_type(4)));
+
+// Four consecutive columns c4 .. c4 + 3 (c4 a multiple of 4) of row r.
+__device__ __forceinline__ void put_split4(half_t* hi, half_t* lo, int r, int c4, const float4& v) {
+    const int off = slab_off(r, c4 >> 3) + (c4 & 7);
+    half4_t h, l;
+    half_t a, b;
+    split2(v.x, a, b); h[0] = a; l[0] = b;
+    split2(v.y, a, b); h[1] = a; l[1] = b;
+    split2(v.z, a, b); h[2] = a; l[2] = b;
+    split2(v.w, a, b); h[3] = a; l[3] = b;
+    *reinterpret_cast<half4_t*>(hi + off) = h;
+    *reinterpret_cast<half4_t*>(lo + off) = l;
+}
+
+// The matrix-core fragment of row r, column group grp (eight columns).
+__device__ __forceinline__ Frag<2> slab_frag(const half_t* hi, const half_t* lo, int r, int grp) {
+    const int off = slab_off(r, grp);
+    Frag<2> f;
+    f.t[0] = *reinterpret_cast<const half8*>(hi + off);
+    f.t[1] = *reinterpret_cast<const half8*>(lo + off);
+    return f;
+}
 
 // Sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same column of an
 // accumulator block).
@@ -567,7 +598,7 @@ __device__ __forceinline__ void st4(float* p, const float4& v) {
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     using Lp = PostLds<DK>;
-    constexpr int KP = Lp::KP, VS = Lp::VS, SP = Lp::SP, ND = DK / 16, NDH = ND / 2;
+    constexpr int KP = Lp::KP, VS = Lp::VS, ND = DK / 16, NDH = ND / 2;
     constexpr int NS = DK * VS / 4 / PNT;   // float4 of S (and of H) per thread and slab
     static_assert(CH * VS / 4 == PNT, "one float4 of each 64-row slab per thread");
     __shared__ float s1[Lp::R1];
@@ -629,7 +660,8 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     RowsPre<DK, F32IN, PNT> pk, pq;
     MatPre<PNT> pt, pp, pa;
 
-    // ---- state terms over slabs of VS state columns:
+    // ---- state terms over slabs of VS state columns, on the fp16 matrix cores
+    // with two-term operands (three products per pair, lo * lo dropped):
     //   z1 = dO S^T, z2 = dR S^T, z3 = U H^T   (rows 16 R .., column blocks D0 ..)
     //   acc = dO U^T (hf 0) or dU R^T (hf 1)   (rows 16 R .., column blocks I <= R)
     f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
@@ -638,13 +670,20 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
 #pragma unroll
     for (int I = 0; I < 4; ++I) acc[I] = zero4();
     float hs = 0.f;
-    float* sS = s1;
-    float* sH = sS + DK * SP;
-    float* sO = sH + DK * SP;
-    float* sRr = sO + CH * SP;
-    float* sU = sRr + CH * SP;
-    float* sdU = sU + CH * SP;
-    float* sdR = sdU + CH * SP;
+    half_t* sSh = reinterpret_cast<half_t*>(s1);
+    half_t* sSl = sSh + DK * VS;
+    half_t* sHh = sSl + DK * VS;
+    half_t* sHl = sHh + DK * VS;
+    half_t* sOh = sHl + DK * VS;
+    half_t* sOl = sOh + CH * VS;
+    half_t* sRh = sOl + CH * VS;
+    half_t* sRl = sRh + CH * VS;
+    half_t* sUh = sRl + CH * VS;
+    half_t* sUl = sUh + CH * VS;
+    half_t* sdUh = sUl + CH * VS;
+    half_t* sdUl = sdUh + CH * VS;
+    half_t* sdRh = sdUl + CH * VS;
+    half_t* sdRl = sdRh + CH * VS;
     pre_slab(0);
     for (int v0 = 0; v0 < Dv; v0 += VS) {
         lds_barrier();
@@ -652,17 +691,17 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         for (int n = 0; n < NS; ++n) {
             const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
             hs += ps[n].x * ph[n].x + ps[n].y * ph[n].y + ps[n].z * ph[n].z + ps[n].w * ph[n].w;
-            st4(sS + d * SP + c4, ps[n]);
-            st4(sH + d * SP + c4, ph[n]);
+            put_split4(sSh, sSl, d, c4, ps[n]);
+            put_split4(sHh, sHl, d, c4, ph[n]);
         }
         {
-            const int r = tid / (VS / 4), c4 = (tid % (VS / 4)) * 4, at = r * SP + c4;
+            const int r = tid / (VS / 4), c4 = (tid % (VS / 4)) * 4;
             const float4 z = {0.f, 0.f, 0.f, 0.f};
-            st4(sO + at, r < valid ? po : z);
-            st4(sdR + at, r < valid ? pd : z);
-            st4(sRr + at, pr);
-            st4(sU + at, pu);
-            st4(sdU + at, pdu);
+            put_split4(sOh, sOl, r, c4, r < valid ? po : z);
+            put_split4(sdRh, sdRl, r, c4, r < valid ? pd : z);
+            put_split4(sRh, sRl, r, c4, pr);
+            put_split4(sUh, sUl, r, c4, pu);
+            put_split4(sdUh, sdUl, r, c4, pdu);
         }
         lds_barrier();
         if (v0 + VS < Dv) {
@@ -676,28 +715,27 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
             pre_mat(pp, a.wP + mo, tid);
             pre_mat(pa, a.wA + mo, tid);
         }
-        for (int s = 0; s < VS / 4; ++s) {
-            const int m = 4 * s + g;
-            const int ra = (16 * R + i16) * SP + m;
-            const float ao = sO[ra], ar = sdR[ra], au = sU[ra];
+        const int ra = 16 * R + i16;
+        const Frag<2> fo = slab_frag(sOh, sOl, ra, g);
+        const Frag<2> fr = slab_frag(sdRh, sdRl, ra, g);
+        const Frag<2> fu = slab_frag(sUh, sUl, ra, g);
 #pragma unroll
-            for (int D = 0; D < NDH; ++D) {
-                const float bs = sS[(16 * (D0 + D) + i16) * SP + m];
-                const float bh = sH[(16 * (D0 + D) + i16) * SP + m];
-                z1[D] = mfma_f32x4(ao, bs, z1[D]);
-                z2[D] = mfma_f32x4(ar, bs, z2[D]);
-                z3[D] = mfma_f32x4(au, bh, z3[D]);
-            }
-            if (hf == 0) {
+        for (int D = 0; D < NDH; ++D) {
+            const Frag<2> fs = slab_frag(sSh, sSl, 16 * (D0 + D) + i16, g);
+            const Frag<2> fh = slab_frag(sHh, sHl, 16 * (D0 + D) + i16, g);
+            z1[D] = mma<2, 2>(fo, fs, z1[D]);
+            z2[D] = mma<2, 2>(fr, fs, z2[D]);
+            z3[D] = mma<2, 2>(fu, fh, z3[D]);
+        }
+        if (hf == 0) {
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
-                    if (I <= R) acc[I] = mfma_f32x4(ao, sU[(16 * I + i16) * SP + m], acc[I]);
-            } else {
-                const float adu = sdU[ra];
+            for (int I = 0; I < 4; ++I)
+                if (I <= R) acc[I] = mma<2, 2>(fo, slab_frag(sUh, sUl, 16 * I + i16, g), acc[I]);
+        } else {
+            const Frag<2> fdu = slab_frag(sdUh, sdUl, ra, g);
 #pragma unroll
-                for (int I = 0; I < 4; ++I)
-                    if (I <= R) acc[I] = mfma_f32x4(adu, sRr[(16 * I + i16) * SP + m], acc[I]);
-            }
+            for (int I = 0; I < 4; ++I)
+                if (I <= R) acc[I] = mma<2, 2>(fdu, slab_frag(sRh, sRl, 16 * I + i16, g), acc[I]);
         }
     }
     atomicAdd(&shs, hs);
