@@ -19,7 +19,7 @@ With a diagonal preconditioner on the gradient step (write-side key scales):
     o, S = dr_chunk_fwd_precond(q, k, v, log_alpha, beta, key_scale, S0, gate="scalar",
                                 beta_mode="scalar")
 
-Gradients of the chunked forward (scalar gate or none, scalar beta):
+Gradients of the chunked forward (any gate, scalar beta):
 
     g = dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final, gate="scalar")
     g["dq"], g["dk"], g["dv"], g["dlog_alpha"], g["dbeta"], g["dS0"]
@@ -311,7 +311,7 @@ def dr_chunk_bwd_workspace_bytes(desc: ChunkDesc) -> int:
 
 def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, want_dS0: bool = True,
                  workspace=None, stream=None):
-    """Gradients of dr_chunk_fwd (gate "none" or "scalar", scalar beta) for the
+    """Gradients of dr_chunk_fwd (any gate, scalar beta) for the
     loss whose gradients with respect to o and S_final are dO [B,H,L,Dv] and
     dS_final [B,H,Dk,Dv] (fp32; dS_final None means zero).  q, k, v and the
     other inputs are as for dr_chunk_fwd.  Returns a dict of fp32 device
@@ -323,13 +323,12 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
     _need(q, "q")
     _need(k, "k", q.dtype, (B, H, L, Dk))
     _need(v, "v", q.dtype, (B, H, L, Dv))
-    if gate == "none":
+    gshape = {"none": None, "scalar": (B, H, L), "channel": (B, H, L, Dk)}[gate]
+    if gshape is None:
         if log_alpha is not None:
             raise ValueError("gate 'none' takes no log_alpha")
-    elif gate == "scalar":
-        _need(log_alpha, "log_alpha", torch.float32, (B, H, L))
     else:
-        raise ValueError("the backward covers gate 'none' and 'scalar'")
+        _need(log_alpha, "log_alpha", torch.float32, gshape)
     _need(beta, "beta", torch.float32, (B, H, L))
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
@@ -339,7 +338,7 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
     f32 = dict(dtype=torch.float32, device=q.device)
     out = {"dq": torch.empty((B, H, L, Dk), **f32), "dk": torch.empty((B, H, L, Dk), **f32),
            "dv": torch.empty((B, H, L, Dv), **f32),
-           "dlog_alpha": torch.empty((B, H, L), **f32) if gate == "scalar" else None,
+           "dlog_alpha": torch.empty(gshape, **f32) if gshape is not None else None,
            "dbeta": torch.empty((B, H, L), **f32),
            "dS0": torch.empty((B, H, Dk, Dv), **f32) if want_dS0 else None}
     desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, "scalar")

@@ -319,7 +319,7 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
 
 // ----------------------------------------------------------------- backward
 struct BwdLayout {
-    size_t T, Pm, A, G, S, H, U, R, dU, total;
+    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, total;
 };
 
 BwdLayout bwd_layout(const dr_chunk_desc& d) {
@@ -336,12 +336,19 @@ BwdLayout bwd_layout(const dr_chunk_desc& d) {
     w.T = take(NCH * dr::CH * dr::CH * f);
     w.Pm = take(NCH * dr::CH * dr::CH * f);
     w.A = take(NCH * dr::CH * dr::CH * f);
-    w.G = take(NCH * dr::CH * f);
+    const bool cg = d.gate == DR_GATE_CHANNEL;
+    w.G = take(NCH * dr::CH * (cg ? d.Dk : 1) * f);
     w.S = take(NCH * d.Dk * d.Dv * f);
     w.H = take(NCH * d.Dk * d.Dv * f);
     w.U = take(NCH * dr::CH * d.Dv * f);
     w.R = take(NCH * dr::CH * d.Dv * f);
     w.dU = take(NCH * dr::CH * d.Dv * f);
+    if (cg) {
+        w.Qh = take(NCH * dr::CH * d.Dk * f);
+        w.Kh = take(NCH * dr::CH * d.Dk * f);
+        w.Kc = take(NCH * dr::CH * d.Dk * f);
+        w.Kt = take(NCH * dr::CH * d.Dk * f);
+    }
     w.total = NCH ? off : 0;
     return w;
 }
@@ -349,8 +356,6 @@ BwdLayout bwd_layout(const dr_chunk_desc& d) {
 dr_status check_bwd_desc(const dr_chunk_desc* d) {
     dr_status s = check_chunk_desc(d);
     if (s != DR_OK) return s;
-    if (d->gate == DR_GATE_CHANNEL)
-        return fail(DR_ERR_UNSUPPORTED, "the backward covers the scalar gate and no gate");
     if (d->beta != DR_BETA_SCALAR) return fail(DR_ERR_UNSUPPORTED, "the backward covers the scalar beta");
     if (d->input_flags) return fail(DR_ERR_UNSUPPORTED, "the backward takes no input_flags");
     if (d->out_dtype != DR_F32) return fail(DR_ERR_UNSUPPORTED, "dO and the gradients are fp32: out_dtype must be DR_F32");
@@ -419,6 +424,13 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.wU = (float*)(ws + w.U);
     a.wR = (float*)(ws + w.R);
     a.wdU = (float*)(ws + w.dU);
+    a.cgate = d->gate == DR_GATE_CHANNEL;
+    if (a.cgate) {
+        a.wQh = (float*)(ws + w.Qh);
+        a.wKh = (float*)(ws + w.Kh);
+        a.wKc = (float*)(ws + w.Kc);
+        a.wKt = (float*)(ws + w.Kt);
+    }
     hipError_t e = dr::launch_bwd(a, d->Dk, d->in_dtype == DR_F32, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
     return DR_OK;

@@ -130,6 +130,58 @@ __device__ __forceinline__ void scan_tile(const BwdArgs& a, int& seq, int& tile)
     tile = (bid >> 3) % NT;
 }
 
+// T = (I + A)^-1 for the strictly lower 64 x 64 A in LDS (pitch PT), written to
+// sT and to Tg (64 x 64, zeros above the diagonal).  Four waves.  Diagonal
+// 16 x 16 blocks by forward substitution (wave w inverts block w, lane j < 16
+// owns column j); off-diagonal blocks one block row R at a time:
+//   T_RI = -T_RR sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .]
+__device__ __forceinline__ void tri_inverse(const float* sA, float* sT, float (*sX)[16 * 17], float* Tg, int tid) {
+    const int w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    if (l < 16) {
+        const int base = 16 * w, j = l;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) s += sA[(base + r) * PT + base + i] * t[i];
+            t[r] = r == j ? 1.f : (r < j ? 0.f : -s);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(base + r) * PT + base + j] = t[r];
+    }
+    lds_barrier();
+    for (int R = 1; R < 4; ++R) {
+        if (w < R) {
+            const int I = w;
+            f32x4 X = zero4();
+            for (int s = 4 * I; s < 4 * R; ++s) {
+                const int m = 4 * s + g;
+                X = mfma_f32x4(sA[(16 * R + i16) * PT + m], sT[m * PT + 16 * I + i16], X);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sX[w][(4 * g + j) * 17 + i16] = X[j];
+        }
+        lds_barrier();
+        if (w < R) {
+            const int I = w;
+            f32x4 Y = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int m = 4 * s + g;
+                Y = mfma_f32x4(sT[(16 * R + i16) * PT + 16 * R + m], sX[w][m * 17 + i16], Y);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sT[(16 * R + 4 * g + j) * PT + 16 * I + i16] = -Y[j];
+        }
+        lds_barrier();
+    }
+    for (int e = tid; e < CH * CH; e += NTH) {
+        const int r = e >> 6, i = e & 63;
+        Tg[e] = i <= r ? sT[r * PT + i] : 0.f;
+    }
+}
+
 // --------------------------------------------------------------------- prep
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
@@ -200,53 +252,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     }
     lds_barrier();
 
-    // T = (I + A)^-1.  Diagonal 16 x 16 blocks by forward substitution: wave w
-    // inverts block w, lane j < 16 owns column j.
-    if (l < 16) {
-        const int base = 16 * w, j = l;
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) s += sA[(base + r) * PT + base + i] * t[i];
-            t[r] = r == j ? 1.f : (r < j ? 0.f : -s);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(base + r) * PT + base + j] = t[r];
-    }
-    lds_barrier();
-    // Off-diagonal blocks, one block row R at a time:
-    //   T_RI = -T_RR sum_{m in [16 I, 16 R)} A[16 R + .][m] T[m][16 I + .]
-    for (int R = 1; R < 4; ++R) {
-        if (w < R) {
-            const int I = w;
-            f32x4 X = zero4();
-            for (int s = 4 * I; s < 4 * R; ++s) {
-                const int m = 4 * s + g;
-                X = mfma_f32x4(sA[(16 * R + i16) * PT + m], sT[m * PT + 16 * I + i16], X);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sX[w][(4 * g + j) * 17 + i16] = X[j];
-        }
-        lds_barrier();
-        if (w < R) {
-            const int I = w;
-            f32x4 Y = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int m = 4 * s + g;
-                Y = mfma_f32x4(sT[(16 * R + i16) * PT + 16 * R + m], sX[w][m * 17 + i16], Y);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sT[(16 * R + 4 * g + j) * PT + 16 * I + i16] = -Y[j];
-        }
-        lds_barrier();
-    }
-    for (int e = tid; e < CH * CH; e += NTH) {
-        const int r = e >> 6, i = e & 63;
-        a.wT[mo + e] = i <= r ? sT[r * PT + i] : 0.f;
-    }
+    tri_inverse(sA, sT, sX, a.wT + mo, tid);
 }
 
 // ------------------------------------------------------- forward state scan
@@ -595,41 +601,28 @@ __device__ __forceinline__ void st4(float* p, const float4& v) {
     p[0] = v.x; p[1] = v.y; p[2] = v.z; p[3] = v.w;
 }
 
-template <int DK, bool F32IN>
-__global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
+// The state-sized products of the per-chunk gradient kernel, over slabs of VS
+// state columns on the fp16 matrix cores with two-term operands (three
+// products per pair, lo * lo dropped):
+//   z1 = dO S^T, z2 = dR S^T, z3 = U H^T   (rows 16 R .., column blocks D0 ..)
+//   acc = dO U^T (hf 0) or dU R^T (hf 1)   (rows 16 R .., column blocks I <= R)
+// and <H, S>: summed into shs[0], or per state row into shs[d] (CG).  The
+// last slab's turn prefetches T, P, K K^T (and, for bf16 inputs without a
+// channel gate, the q and k rows) for the 64 x 64 part.
+template <int DK, bool F32IN, bool CG>
+__device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, int valid, size_t tok0, float* s1,
+                                                    f32x4 (&z1)[DK / 32], f32x4 (&z2)[DK / 32], f32x4 (&z3)[DK / 32],
+                                                    f32x4 (&acc)[4], float* shs, RowsPre<DK, F32IN, PNT>& pk,
+                                                    RowsPre<DK, F32IN, PNT>& pq, MatPre<PNT>& pt, MatPre<PNT>& pp,
+                                                    MatPre<PNT>& pa) {
     using Lp = PostLds<DK>;
-    constexpr int KP = Lp::KP, VS = Lp::VS, ND = DK / 16, NDH = ND / 2;
+    constexpr int VS = Lp::VS, NDH = DK / 32;
     constexpr int NS = DK * VS / 4 / PNT;   // float4 of S (and of H) per thread and slab
     static_assert(CH * VS / 4 == PNT, "one float4 of each 64-row slab per thread");
-    __shared__ float s1[Lp::R1];
-    __shared__ float sM0[CH * PT];   // T
-    __shared__ float sM1[CH * PT];   // P, then M = Diag(beta) (dA o E)
-    __shared__ float sM2[CH * PT];   // K K^T o E (strict lower)
-    __shared__ float sM3[CH * PT];   // N = dP o E
-    __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
-    __shared__ float sg[CH], sgam[CH], slam[CH], sb[CH], sdg[CH], sdb[CH];
-    __shared__ float shs;
-    const int cs = blockIdx.x;
-    const int seq = cs / a.NC, c = cs - seq * a.NC;
-    const int t0 = c * CH, valid = min(CH, a.L - t0);
-    const size_t tok0 = (size_t)seq * a.L + t0;
     const int Dv = a.Dv;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
     const int R = w & 3, hf = w >> 2, D0 = hf * NDH;
     const size_t mo = (size_t)cs * CH * CH;
-
-    if (tid < CH) {
-        const float* gp = a.wG + (size_t)cs * CH;
-        const float gv = gp[tid], g63 = gp[CH - 1];
-        sg[tid] = gv;
-        sgam[tid] = expf(gv);
-        slam[tid] = expf(g63 - gv);
-        sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
-        sdg[tid] = 0.f;
-        sdb[tid] = 0.f;
-    }
-    if (tid == 0) shs = 0.f;
-
     // ---- slab prefetch registers
     float4 ps[NS], ph[NS], po, pd, pr, pu, pdu;
     auto pre_slab = [&](int v0) {
@@ -657,14 +650,10 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
             pd = *reinterpret_cast<const float4*>(a.dv + io);
         }
     };
-    RowsPre<DK, F32IN, PNT> pk, pq;
-    MatPre<PNT> pt, pp, pa;
-
     // ---- state terms over slabs of VS state columns, on the fp16 matrix cores
     // with two-term operands (three products per pair, lo * lo dropped):
     //   z1 = dO S^T, z2 = dR S^T, z3 = U H^T   (rows 16 R .., column blocks D0 ..)
     //   acc = dO U^T (hf 0) or dU R^T (hf 1)   (rows 16 R .., column blocks I <= R)
-    f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
 #pragma unroll
     for (int D = 0; D < NDH; ++D) z1[D] = z2[D] = z3[D] = zero4();
 #pragma unroll
@@ -690,7 +679,9 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
 #pragma unroll
         for (int n = 0; n < NS; ++n) {
             const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
-            hs += ps[n].x * ph[n].x + ps[n].y * ph[n].y + ps[n].z * ph[n].z + ps[n].w * ph[n].w;
+            const float hsn = ps[n].x * ph[n].x + ps[n].y * ph[n].y + ps[n].z * ph[n].z + ps[n].w * ph[n].w;
+            if constexpr (CG) atomicAdd(&shs[d], hsn);
+            else hs += hsn;
             put_split4(sSh, sSl, d, c4, ps[n]);
             put_split4(sHh, sHl, d, c4, ph[n]);
         }
@@ -707,7 +698,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         if (v0 + VS < Dv) {
             pre_slab(v0 + VS);
         } else {
-            if constexpr (!F32IN) {   // fp32 rows would not fit the register budget
+            if constexpr (!F32IN && !CG) {   // fp32 rows would not fit the register budget
                 pre_rows<DK, F32IN, PNT>(pk, a.k, tok0, valid, tid);
                 pre_rows<DK, F32IN, PNT>(pq, a.q, tok0, valid, tid);
             }
@@ -738,7 +729,46 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
                 if (I <= R) acc[I] = mma<2, 2>(fdu, slab_frag(sRh, sRl, 16 * I + i16, g), acc[I]);
         }
     }
-    atomicAdd(&shs, hs);
+    if constexpr (!CG) atomicAdd(&shs[0], hs);
+}
+
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
+    using Lp = PostLds<DK>;
+    constexpr int KP = Lp::KP, ND = DK / 16, NDH = ND / 2;
+    __shared__ float s1[Lp::R1];
+    __shared__ float sM0[CH * PT];   // T
+    __shared__ float sM1[CH * PT];   // P, then M = Diag(beta) (dA o E)
+    __shared__ float sM2[CH * PT];   // K K^T o E (strict lower)
+    __shared__ float sM3[CH * PT];   // N = dP o E
+    __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
+    __shared__ float sg[CH], sgam[CH], slam[CH], sb[CH], sdg[CH], sdb[CH];
+    __shared__ float shs;
+    const int cs = blockIdx.x;
+    const int seq = cs / a.NC, c = cs - seq * a.NC;
+    const int t0 = c * CH, valid = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int Dv = a.Dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, hf = w >> 2, D0 = hf * NDH;
+    const size_t mo = (size_t)cs * CH * CH;
+
+    if (tid < CH) {
+        const float* gp = a.wG + (size_t)cs * CH;
+        const float gv = gp[tid], g63 = gp[CH - 1];
+        sg[tid] = gv;
+        sgam[tid] = expf(gv);
+        slam[tid] = expf(g63 - gv);
+        sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
+        sdg[tid] = 0.f;
+        sdb[tid] = 0.f;
+    }
+    if (tid == 0) shs = 0.f;
+
+    RowsPre<DK, F32IN, PNT> pk, pq;
+    MatPre<PNT> pt, pp, pa;
+    f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
+    post_state_products<DK, F32IN, false>(a, cs, valid, tok0, s1, z1, z2, z3, acc, &shs, pk, pq, pt, pp, pa);
     lds_barrier();
 
     // ---- q, k rows and the 64 x 64 matrices
@@ -917,6 +947,599 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     }
 }
 
+// ======================================================= channel gate
+// With a per-channel decay the chunk algebra keeps its form on gated operands
+// (G the per-channel cumulative log decay within the chunk, G_63 its last row):
+//   Q^ = Q o e^G, K^ = K o e^G, Kc = K o e^-G, K~ = K o e^(G_63 - G),
+//   A = strict lower of Diag(beta) K^ Kc^T,  P = lower of Q^ Kc^T,
+//   R = V - K^ S,  U = T Diag(beta) R,  O = Q^ S + P U,
+//   S' = Diag(e^G_63) S + K~^T U.
+// Backward: dU = P^T dO + K~ H, dR = Diag(beta) T^T dU, dS = Diag(e^G_63) H +
+// Q^^T dO - K^^T dR; dQ^ = dO S^T + N Kc, dK^ = -dR S^T + M Kc,
+// dKc = N^T Q^ + M^T K^, dK~ = U H^T (N = lower dP, M = Diag(beta) dA), and
+// per element dq = dQ^ e^G, dk = dK^ e^G + dKc e^-G + dK~ e^(G_63 - G),
+// dG = dQ^ Q^ + dK^ K^ - dKc Kc - dK~ K~, plus at the last row the sums of
+// dK~ K~ over the chunk and e^G_63 <H_c, S_c>; d log alpha is dG's reverse
+// cumulative sum per channel.  e^-G needs the within-chunk cumulative log
+// decay of every channel to stay above about -88 (fp32 range).
+
+// Register prefetch of a chunk's [64][DK] fp32 workspace plane, stored to LDS
+// rows of pitch DK + 1.
+template <int DK, int NT>
+struct PlanePre {
+    float4 x[CH * DK / 4 / NT];
+};
+
+template <int DK, int NT>
+__device__ __forceinline__ void pre_plane(PlanePre<DK, NT>& p, const float* src, int tid) {
+#pragma unroll
+    for (int n = 0; n < CH * DK / 4 / NT; ++n) p.x[n] = reinterpret_cast<const float4*>(src)[tid + n * NT];
+}
+
+template <int DK, int NT>
+__device__ __forceinline__ void put_plane(const PlanePre<DK, NT>& p, float* dst, int tid) {
+    constexpr int KP = DK + 1;
+#pragma unroll
+    for (int n = 0; n < CH * DK / 4 / NT; ++n) {
+        const int e = tid + n * NT, r = e / (DK / 4), c = (e % (DK / 4)) * 4;
+        dst[r * KP + c] = p.x[n].x;
+        dst[r * KP + c + 1] = p.x[n].y;
+        dst[r * KP + c + 2] = p.x[n].z;
+        dst[r * KP + c + 3] = p.x[n].w;
+    }
+}
+
+// A [64][DK] fp32 workspace plane straight into LDS rows of pitch DK + 1.
+template <int DK, int NT>
+__device__ __forceinline__ void load_plane(float* dst, const float* src, int tid) {
+    constexpr int KP = DK + 1;
+    for (int e = tid; e < CH * DK / 4; e += NT) {
+        const float4 x = reinterpret_cast<const float4*>(src)[e];
+        const int r = e / (DK / 4), c = (e % (DK / 4)) * 4;
+        dst[r * KP + c] = x.x;
+        dst[r * KP + c + 1] = x.y;
+        dst[r * KP + c + 2] = x.z;
+        dst[r * KP + c + 3] = x.w;
+    }
+}
+
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1;
+    static_assert(2 * CH * PT <= 3 * CH * KP, "A and T fit where the operands were");
+    __shared__ float sOp[3 * CH * KP];   // K^, Kc, Q^; then A and T
+    __shared__ float sX[4][16 * 17];
+    __shared__ float sb[CH];
+    float* sKh = sOp;
+    float* sKc = sOp + CH * KP;
+    float* sQh = sOp + 2 * CH * KP;
+    float* sA = sOp;
+    float* sT = sOp + CH * PT;
+    const int cs = blockIdx.x;
+    const int seq = cs / a.NC, c = cs - seq * a.NC;
+    const int t0 = c * CH, valid = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const size_t mo = (size_t)cs * CH * CH, po = (size_t)cs * CH * DK;
+
+    if (tid < CH) sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
+    // per channel: the cumulative log decay and the gated operands (rows past
+    // the end: no decay, zero operands)
+    for (int ch = tid; ch < DK; ch += NTH) {
+        float tot = 0.f;
+        for (int r = 0; r < valid; ++r) tot += a.log_alpha[(tok0 + r) * DK + ch];
+        float G = 0.f;
+        for (int r = 0; r < CH; ++r) {
+            float kv = 0.f, qv = 0.f;
+            if (r < valid) {
+                G += a.log_alpha[(tok0 + r) * DK + ch];
+                kv = load1<F32IN>(a.k, (tok0 + r) * DK + ch);
+                qv = load1<F32IN>(a.q, (tok0 + r) * DK + ch);
+            }
+            const float eg = expf(G), emg = expf(-G);
+            const size_t at = po + (size_t)r * DK + ch;
+            sKh[r * KP + ch] = kv * eg;
+            sKc[r * KP + ch] = kv * emg;
+            sQh[r * KP + ch] = qv * eg;
+            a.wG[at] = G;
+            a.wQh[at] = qv * eg;
+            a.wKh[at] = kv * eg;
+            a.wKc[at] = kv * emg;
+            a.wKt[at] = kv * expf(tot - G);
+        }
+    }
+    lds_barrier();
+    // lower blocks (R = w, I <= R) of K^ Kc^T and Q^ Kc^T, in registers until
+    // every wave is done with the operands
+    {
+        const int R = w;
+        f32x4 aK[4], aQ[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            aK[I] = aQ[I] = zero4();
+            if (I <= R) {
+                for (int s = 0; s < DK / 4; ++s) {
+                    const int m = 4 * s + g;
+                    const float kb = sKc[(16 * I + i16) * KP + m];
+                    aK[I] = mfma_f32x4(sKh[(16 * R + i16) * KP + m], kb, aK[I]);
+                    aQ[I] = mfma_f32x4(sQh[(16 * R + i16) * KP + m], kb, aQ[I]);
+                }
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
+                const float araw = i < r ? aK[I][j] : 0.f;
+                sA[r * PT + i] = sb[r] * araw;
+                a.wA[mo + r * CH + i] = araw;
+                a.wP[mo + r * CH + i] = i <= r ? aQ[I][j] : 0.f;
+            }
+        }
+    }
+    lds_barrier();
+    tri_inverse(sA, sT, sX, a.wT + mo, tid);
+}
+
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(SNT) void bwd_fscan_cg_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1, NKS = DK / 8;
+    __shared__ float sKh[CH * KP];
+    __shared__ float sKt[CH * KP];
+    __shared__ float sT[CH * PT];
+    __shared__ float sS[DK * 17];
+    __shared__ float sR[CH * 17];   // upper-half partial X, then R
+    __shared__ float sU[CH * 17];
+    __shared__ float sb[CH], sd63[DK];
+    int seq, tile;
+    scan_tile(a, seq, tile);
+    if (seq >= a.nseq) return;
+    const int n0 = 16 * tile, Dv = a.Dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, h = w >> 2;
+
+    PlanePre<DK, SNT> pkh, pkt;
+    MatPre<SNT> pt;
+    float pb = 0.f, pd = 0.f, pv[4] = {0.f, 0.f, 0.f, 0.f};
+    auto prefetch = [&](int c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        const size_t tok0 = (size_t)seq * a.L + t0;
+        pre_plane(pkh, a.wKh + cs * CH * DK, tid);
+        pre_plane(pkt, a.wKt + cs * CH * DK, tid);
+        pre_mat(pt, a.wT + cs * CH * CH, tid);
+        if (tid < CH) pb = a.beta[tok0 + (tid < valid ? tid : 0)];
+        if (tid < DK) pd = a.wG[cs * CH * DK + (CH - 1) * DK + tid];
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                pv[j] = load1<F32IN>(a.v, (tok0 + (row < valid ? row : 0)) * Dv + n0 + i16);
+            }
+        }
+    };
+
+    for (int e = tid; e < DK * 16; e += SNT) {
+        const int d = e >> 4, cc = e & 15;
+        sS[d * 17 + cc] = a.S0 ? a.S0[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
+    }
+    prefetch(0);
+    for (int c = 0; c < a.NC; ++c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        lds_barrier();
+        put_plane(pkh, sKh, tid);
+        put_plane(pkt, sKt, tid);
+        put_mat(pt, sT, tid);
+        if (tid < CH) sb[tid] = tid < valid ? pb : 0.f;
+        if (tid < DK) sd63[tid] = expf(pd);
+        float vv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vv[j] = 16 * R + 4 * g + j < valid ? pv[j] : 0.f;
+        for (int e = tid; e < DK * 16; e += SNT) {
+            const int d = e >> 4, cc = e & 15;
+            a.wS[(cs * DK + d) * Dv + n0 + cc] = sS[d * 17 + cc];
+        }
+        lds_barrier();
+        if (c + 1 < a.NC) prefetch(c + 1);
+        // X = K^ S over this wave's half of the contraction
+        f32x4 X = zero4();
+        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
+            const int m = 4 * s + g;
+            X = mfma_f32x4(sKh[(16 * R + i16) * KP + m], sS[m * 17 + i16], X);
+        }
+        if (h == 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sR[(16 * R + 4 * g + j) * 17 + i16] = X[j];
+        }
+        lds_barrier();
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                const float r = vv[j] - (X[j] + sR[row * 17 + i16]);
+                sR[row * 17 + i16] = r;
+                a.wR[(cs * CH + row) * Dv + n0 + i16] = r;
+            }
+        }
+        lds_barrier();
+        if (h == 0) {
+            // U = T Diag(beta) R
+            f32x4 U = zero4();
+            for (int s = 0; s < 4 * (R + 1); ++s) {
+                const int m = 4 * s + g;
+                U = mfma_f32x4(sT[(16 * R + i16) * PT + m] * sb[m], sR[m * 17 + i16], U);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                a.wU[(cs * CH + row) * Dv + n0 + i16] = U[j];
+                sU[row * 17 + i16] = U[j];
+            }
+        }
+        lds_barrier();
+        // S <- Diag(e^G_63) S + K~^T U  (state rows 16 w ..)
+        if (w < DK / 16) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int m = 4 * s + g;
+                acc = mfma_f32x4(sKt[m * KP + 16 * w + i16], sU[m * 17 + i16], acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 16 * w + 4 * g + j;
+                sS[d * 17 + i16] = sd63[d] * sS[d * 17 + i16] + acc[j];
+            }
+        }
+    }
+}
+
+template <int DK>
+__global__ __launch_bounds__(SNT) void bwd_rscan_cg_kernel(BwdArgs a) {
+    constexpr int KP = DK + 1, NKS = DK / 8;
+    __shared__ float sKt[CH * KP];
+    __shared__ float sQh[CH * KP];
+    __shared__ float sKh[CH * KP];
+    __shared__ float sT[CH * PT];
+    __shared__ float sP[CH * PT];
+    __shared__ float sH[DK * 17];
+    __shared__ float sO[CH * 17];   // dO
+    __shared__ float sD[CH * 17];   // upper-half partial dU, then dU, then dR
+    __shared__ float sb[CH], sd63[DK];
+    int seq, tile;
+    scan_tile(a, seq, tile);
+    if (seq >= a.nseq) return;
+    const int n0 = 16 * tile, Dv = a.Dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, h = w >> 2;
+
+    PlanePre<DK, SNT> pkt, pqh, pkh;
+    MatPre<SNT> pt, pp;
+    float pb = 0.f, pd = 0.f, po[4] = {0.f, 0.f, 0.f, 0.f};
+    auto prefetch = [&](int c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        const size_t tok0 = (size_t)seq * a.L + t0;
+        pre_plane(pkt, a.wKt + cs * CH * DK, tid);
+        pre_plane(pqh, a.wQh + cs * CH * DK, tid);
+        pre_plane(pkh, a.wKh + cs * CH * DK, tid);
+        pre_mat(pt, a.wT + cs * CH * CH, tid);
+        pre_mat(pp, a.wP + cs * CH * CH, tid);
+        if (tid < CH) pb = a.beta[tok0 + (tid < valid ? tid : 0)];
+        if (tid < DK) pd = a.wG[cs * CH * DK + (CH - 1) * DK + tid];
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                po[j] = a.dO[(tok0 + (row < valid ? row : 0)) * Dv + n0 + i16];
+            }
+        }
+    };
+
+    for (int e = tid; e < DK * 16; e += SNT) {
+        const int d = e >> 4, cc = e & 15;
+        sH[d * 17 + cc] = a.dS_final ? a.dS_final[((size_t)seq * DK + d) * Dv + n0 + cc] : 0.f;
+    }
+    prefetch(a.NC - 1);
+    for (int c = a.NC - 1; c >= 0; --c) {
+        const size_t cs = (size_t)seq * a.NC + c;
+        const int t0 = c * CH, valid = min(CH, a.L - t0);
+        const size_t tok0 = (size_t)seq * a.L + t0;
+        lds_barrier();
+        put_plane(pkt, sKt, tid);
+        put_plane(pqh, sQh, tid);
+        put_plane(pkh, sKh, tid);
+        put_mat(pt, sT, tid);
+        put_mat(pp, sP, tid);
+        if (tid < CH) sb[tid] = tid < valid ? pb : 0.f;
+        if (tid < DK) sd63[tid] = expf(pd);
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                sO[row * 17 + i16] = row < valid ? po[j] : 0.f;
+            }
+        }
+        for (int e = tid; e < DK * 16; e += SNT) {
+            const int d = e >> 4, cc = e & 15;
+            a.wH[(cs * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
+        }
+        lds_barrier();
+        if (c > 0) prefetch(c - 1);
+        // dU = P^T dO + K~ H  (rows 16 R ..): K~ H over this wave's half of
+        // the contraction; the upper half also takes P^T dO
+        f32x4 Z = zero4();
+        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
+            const int m = 4 * s + g;
+            Z = mfma_f32x4(sKt[(16 * R + i16) * KP + m], sH[m * 17 + i16], Z);
+        }
+        if (h == 1) {
+            f32x4 Y = zero4();
+            for (int s = 4 * R; s < 16; ++s) {
+                const int m = 4 * s + g;
+                Y = mfma_f32x4(sP[m * PT + 16 * R + i16], sO[m * 17 + i16], Y);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sD[(16 * R + 4 * g + j) * 17 + i16] = Z[j] + Y[j];
+        }
+        lds_barrier();
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                const float du = Z[j] + sD[row * 17 + i16];
+                sD[row * 17 + i16] = du;
+                a.wdU[(cs * CH + row) * Dv + n0 + i16] = du;
+            }
+        }
+        lds_barrier();
+        // dR = Diag(beta) T^T dU
+        f32x4 Rr = zero4();
+        if (h == 0) {
+            for (int s = 4 * R; s < 16; ++s) {
+                const int m = 4 * s + g;
+                Rr = mfma_f32x4(sT[m * PT + 16 * R + i16], sD[m * 17 + i16], Rr);
+            }
+        }
+        lds_barrier();
+        if (h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * R + 4 * g + j;
+                const float dr = sb[row] * Rr[j];
+                if (row < valid) a.dv[(tok0 + row) * Dv + n0 + i16] = dr;
+                sD[row * 17 + i16] = dr;
+            }
+        }
+        lds_barrier();
+        // H <- Diag(e^G_63) H + Q^^T dO - K^^T dR  (state rows 16 w ..)
+        if (w < DK / 16) {
+            f32x4 hq = zero4(), hk = zero4();
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int m = 4 * s + g;
+                hq = mfma_f32x4(sQh[m * KP + 16 * w + i16], sO[m * 17 + i16], hq);
+                hk = mfma_f32x4(sKh[m * KP + 16 * w + i16], sD[m * 17 + i16], hk);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 16 * w + 4 * g + j;
+                sH[d * 17 + i16] = sd63[d] * sH[d * 17 + i16] + (hq[j] - hk[j]);
+            }
+        }
+    }
+    lds_barrier();
+    if (a.dS0) {
+        for (int e = tid; e < DK * 16; e += SNT) {
+            const int d = e >> 4, cc = e & 15;
+            a.dS0[((size_t)seq * DK + d) * Dv + n0 + cc] = sH[d * 17 + cc];
+        }
+    }
+}
+
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
+    using Lp = PostLds<DK>;
+    constexpr int KP = Lp::KP, ND = DK / 16, NDH = ND / 2;
+    __shared__ float s1[Lp::R1];
+    __shared__ float sM0[CH * PT];   // T
+    __shared__ float sM1[CH * PT];   // P (unused), then M = Diag(beta) dA
+    __shared__ float sM2[CH * PT];   // K^ Kc^T (strict lower)
+    __shared__ float sM3[CH * PT];   // N = lower dP
+    __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
+    __shared__ float sb[CH], sdb[CH], shs[DK];
+    const int cs = blockIdx.x;
+    const int seq = cs / a.NC, c = cs - seq * a.NC;
+    const int t0 = c * CH, valid = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, hf = w >> 2, D0 = hf * NDH;
+    const size_t mo = (size_t)cs * CH * CH, pofs = (size_t)cs * CH * DK;
+
+    if (tid < CH) {
+        sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
+        sdb[tid] = 0.f;
+    }
+    if (tid < DK) shs[tid] = 0.f;
+
+    RowsPre<DK, F32IN, PNT> pk, pq;   // not used with a channel gate
+    MatPre<PNT> pt, pp, pa;
+    f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
+    post_state_products<DK, F32IN, true>(a, cs, valid, tok0, s1, z1, z2, z3, acc, shs, pk, pq, pt, pp, pa);
+    lds_barrier();
+
+    // ---- Kc and Q^ rows, T and K^ Kc^T
+    float* sKx = s1;             // Kc, later K^
+    float* sQh = s1 + CH * KP;
+    load_plane<DK, PNT>(sKx, a.wKc + pofs, tid);
+    load_plane<DK, PNT>(sQh, a.wQh + pofs, tid);
+    put_mat(pt, sM0, tid);
+    put_mat(pa, sM2, tid);
+    lds_barrier();
+
+    const int rb = 16 * R + 4 * g;   // this lane's first accumulator row
+    float rowb[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};
+    // state terms: dQ^ = z1, dK^ = -z2, dK~ = z3; dKc from the 64 x 64 part
+    f32x4 dqh[NDH], dkh[NDH], dkc[NDH], dkt[NDH];
+#pragma unroll
+    for (int D = 0; D < NDH; ++D) {
+        dqh[D] = z1[D];
+        dkh[D] = -z2[D];
+        dkt[D] = z3[D];
+        dkc[D] = zero4();
+    }
+    // hf 0: N = lower dP; hf 1: dT = dT^ Diag(beta) and dbeta's sums of dT^ o T
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j, i = 16 * I + i16;
+            const bool lo = i <= r;
+            const float x = lo ? acc[I][j] : 0.f;
+            if (hf == 0) {
+                sM3[r * PT + i] = x;
+            } else {
+                colb[I] += x * sM0[r * PT + i];
+                sM4[r * PT + i] = x * sb[i];
+            }
+        }
+    }
+    lds_barrier();
+    // Y = T^T dT  (rows 16 R .., column blocks 2 hf, 2 hf + 1)
+    f32x4 y[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int I = 2 * hf + hh;
+        y[hh] = zero4();
+        for (int s = 4 * R; s < 16; ++s) {
+            const int m = 4 * s + g;
+            y[hh] = mfma_f32x4(sM0[m * PT + 16 * R + i16], sM4[m * PT + 16 * I + i16], y[hh]);
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sM4[(rb + j) * PT + 16 * (2 * hf + hh) + i16] = y[hh][j];
+    lds_barrier();
+    // dA = -Y T^T on the strict lower part; M = Diag(beta) dA into sM1
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int I = 2 * hf + hh;
+        f32x4 da = zero4();
+        if (I <= R) {
+            for (int s = 0; s < 4 * (I + 1); ++s) {
+                const int m = 4 * s + g;
+                da = mfma_f32x4(sM4[(16 * R + i16) * PT + m], sM0[(16 * I + i16) * PT + m], da);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j, cc = 16 * I + i16;
+            const bool lo = cc < r;
+            const float dav = lo ? -da[j] : 0.f;
+            rowb[j] += dav * sM2[r * PT + cc];
+            sM1[r * PT + cc] = dav * sb[r];
+        }
+    }
+    lds_barrier();
+    // dQ^ += N Kc;  dK^ += M Kc;  dKc = N^T Q^
+#pragma unroll
+    for (int D = 0; D < NDH; ++D) {
+        const int cb = 16 * (D0 + D) + i16;
+        for (int s = 0; s < 4 * (R + 1); ++s) {
+            const int m = 4 * s + g;
+            const float kb = sKx[m * KP + cb];
+            dqh[D] = mfma_f32x4(sM3[(16 * R + i16) * PT + m], kb, dqh[D]);
+            dkh[D] = mfma_f32x4(sM1[(16 * R + i16) * PT + m], kb, dkh[D]);
+        }
+        for (int s = 4 * R; s < 16; ++s) {
+            const int m = 4 * s + g;
+            dkc[D] = mfma_f32x4(sM3[m * PT + 16 * R + i16], sQh[m * KP + cb], dkc[D]);
+        }
+    }
+    lds_barrier();
+    load_plane<DK, PNT>(sKx, a.wKh + pofs, tid);   // K^ in place of Kc
+    lds_barrier();
+    // dKc += M^T K^
+#pragma unroll
+    for (int D = 0; D < NDH; ++D) {
+        const int cb = 16 * (D0 + D) + i16;
+        for (int s = 4 * R; s < 16; ++s) {
+            const int m = 4 * s + g;
+            dkc[D] = mfma_f32x4(sM1[m * PT + 16 * R + i16], sKx[m * KP + cb], dkc[D]);
+        }
+    }
+    // ---- dbeta's row and column sums
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float xb = group_sum<16>(rowb[j]);
+        if (i16 == 0) atomicAdd(&sdb[rb + j], xb);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const float xb = col4_sum(colb[I]);
+        if (g == 0) atomicAdd(&sdb[16 * I + i16], xb);
+    }
+    lds_barrier();
+    // ---- per element: dq, dk, and the two parts of dG,
+    //   X = dQ^ Q^ + dK^ K^ - dKc Kc,  Y = dK~ K~  (dG = X - Y, plus the last row's sums)
+    float* sXg = s1;
+    float* sYg = s1 + CH * KP;
+#pragma unroll
+    for (int D = 0; D < NDH; ++D) {
+        const int col = 16 * (D0 + D) + i16;
+        const float G63 = a.wG[pofs + (size_t)(CH - 1) * DK + col];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = rb + j;
+            const size_t at = pofs + (size_t)r * DK + col;
+            const float G = a.wG[at];
+            const float eg = expf(G), emg = expf(-G), et = expf(G63 - G);
+            const float xq = dqh[D][j], xh = dkh[D][j], xc = dkc[D][j], xt = dkt[D][j];
+            sXg[r * KP + col] = xq * a.wQh[at] + xh * a.wKh[at] - xc * a.wKc[at];
+            sYg[r * KP + col] = xt * a.wKt[at];
+            if (r < valid) {
+                a.dq[(tok0 + r) * DK + col] = xq * eg;
+                a.dk[(tok0 + r) * DK + col] = xh * eg + xc * emg + xt * et;
+            }
+        }
+    }
+    lds_barrier();
+    // d log alpha_rc = sum_{r' >= r} X + sum_{i < r} Y + e^G_63 <H_c, S_c>
+    for (int ch = tid; ch < DK; ch += PNT) {
+        float totY = 0.f;
+        for (int r = 0; r < CH; ++r) totY += sYg[r * KP + ch];
+        const float hsc = expf(a.wG[pofs + (size_t)(CH - 1) * DK + ch]) * shs[ch];
+        float sufX = 0.f, sufY = 0.f;
+        for (int r = CH - 1; r >= 0; --r) {
+            sufX += sXg[r * KP + ch];
+            sufY += sYg[r * KP + ch];
+            if (r < valid) a.dlog_alpha[(tok0 + r) * DK + ch] = sufX + (totY - sufY) + hsc;
+        }
+    }
+    if (w == 0 && l < valid) a.dbeta[tok0 + l] = sdb[l];
+}
+
+template <int DK, bool F32IN>
+hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
+    const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
+    const unsigned nscan = (unsigned)((a.nseq + 7) / 8) * 8u * (unsigned)(a.Dv / 16);
+    prof_mark(st, kProfBwdPrep);
+    hipLaunchKernelGGL((bwd_prep_cg_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
+    prof_mark(st, kProfBwdFscan);
+    hipLaunchKernelGGL((bwd_fscan_cg_kernel<DK, F32IN>), dim3(nscan), dim3(SNT), 0, st, a);
+    prof_mark(st, kProfBwdRscan);
+    hipLaunchKernelGGL((bwd_rscan_cg_kernel<DK>), dim3(nscan), dim3(SNT), 0, st, a);
+    prof_mark(st, kProfBwdPost);
+    hipLaunchKernelGGL((bwd_post_cg_kernel<DK, F32IN>), dim3(nch), dim3(PNT), 0, st, a);
+    prof_mark(st, kProfEnd);
+    return hipGetLastError();
+}
+
 template <int DK, bool F32IN>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
@@ -936,6 +1559,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st) {
+    if (a.cgate) {
+        if (Dk == 128) return f32in ? launch_bwd_cg_t<128, true>(a, st) : launch_bwd_cg_t<128, false>(a, st);
+        return f32in ? launch_bwd_cg_t<64, true>(a, st) : launch_bwd_cg_t<64, false>(a, st);
+    }
     if (Dk == 128) return f32in ? launch_bwd_t<128, true>(a, st) : launch_bwd_t<128, false>(a, st);
     return f32in ? launch_bwd_t<64, true>(a, st) : launch_bwd_t<64, false>(a, st);
 }

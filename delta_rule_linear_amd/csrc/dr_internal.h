@@ -96,6 +96,9 @@ struct DecodeArgs {
 // cs = (b * H + h) * NC + c:
 //   wT, wP, wA  [NCH][64][64]   T = (I + A)^-1, P, and K K^T o E (strict lower)
 //   wG          [NCH][64]       cumulative log-decay g_r within the chunk
+//                               ([NCH][64][Dk] per channel with a channel gate)
+// With a channel gate (cgate) also the gated operands, [NCH][64][Dk] each:
+//   wQh = q o e^G, wKh = k o e^G, wKc = k o e^-G, wKt = k o e^(G_63 - G)
 //   wS, wH      [NCH][Dk][Dv]   chunk start state, gradient at its end state
 //   wU, wR, wdU [NCH][64][Dv]   U, R = V - Gamma K S, and dU
 struct BwdArgs {
@@ -124,6 +127,11 @@ struct BwdArgs {
     float* wU;
     float* wR;
     float* wdU;
+    int cgate;
+    float* wQh;
+    float* wKh;
+    float* wKc;
+    float* wKt;
 };
 
 // Optional per-kernel timing: launchers mark the start of each kernel and the

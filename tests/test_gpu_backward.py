@@ -59,13 +59,28 @@ def _check(p, seed=0, dS_final=True, tol=None):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("gate", ["none", "scalar"])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 @pytest.mark.parametrize("L", [1, 63, 64, 65, 200])
 @pytest.mark.parametrize("D", [64, 128])
 def test_backward_sweep(dtype, gate, L, D):
+    rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
     p = inputs.make_chunk_problem(2, 2, L, D, D, in_dtype=dtype, gate=gate, s0_var=0.01, seed=L + D,
-                                  name=f"bwd_{gate}_{dtype}")
+                                  log_alpha_range=rng, name=f"bwd_{gate}_{dtype}")
     _check(p, seed=L)
+
+
+@pytest.mark.parametrize("Dv", [16, 48, 256])
+def test_backward_channel_gate_value_width(Dv):
+    p = inputs.make_chunk_problem(1, 2, 130, 128, Dv, in_dtype="f32", gate="channel", s0_var=0.01, seed=Dv,
+                                  log_alpha_range=inputs.KDA_GATE, name="bwd_cg_width")
+    _check(p)
+
+
+def test_backward_channel_gate_strong_decay():
+    # log alpha down to -1 per token: within-chunk cumulative decays reach about -60
+    p = inputs.make_chunk_problem(1, 2, 150, 64, 64, in_dtype="f32", gate="channel", s0_var=0.01,
+                                  log_alpha_range=(-1.0, -0.05), seed=13, name="bwd_cg_strong")
+    _check(p)
 
 
 @pytest.mark.parametrize("Dv", [16, 48, 256])
@@ -103,6 +118,23 @@ def test_backward_no_tokens():
     g = run_bwd(p, dO, dSf)
     assert g["dq"].numel() == 0
     assert np.array_equal(to_np(g["dS0"]), dSf.astype(np.float64))
+
+
+def test_backward_channel_gate_full_size_sampled_sequences():
+    # the KDA shape (B=2, H=32, L=16384, d=128, bf16, channel gate) in one call
+    p = inputs.workload("kda_b2h32_16k")
+    announce("backward full size", p.name)
+    dO, dSf = inputs.backward_cotangents(p, 0)
+    g = run_bwd(p, dO, dSf)
+    for b, h in [(0, 0), (1, 31)]:
+        s = p.head(b, h)
+        ref = oracle_bwd(s, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1])
+        for n in GRADS:
+            x = to_np(g[n][b:b + 1, h:h + 1])
+            e = rel_err(x, ref[n])
+            assert e <= TOL["bf16"], f"sequence ({b},{h}) {n}: {e:.2e}"
+    del g
+    torch.cuda.empty_cache()
 
 
 def test_backward_full_size_sampled_sequences():
