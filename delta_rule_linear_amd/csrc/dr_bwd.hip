@@ -1008,6 +1008,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     constexpr int KP = DK + 1;
     static_assert(2 * CH * PT <= 3 * CH * KP, "A and T fit where the operands were");
     __shared__ float sOp[3 * CH * KP];   // K^, Kc, Q^; then A and T
+    __shared__ float sG[CH * KP];        // log alpha, then its cumulative sums
     __shared__ float sX[4][16 * 17];
     __shared__ float sb[CH];
     float* sKh = sOp;
@@ -1023,29 +1024,53 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     const size_t mo = (size_t)cs * CH * CH, po = (size_t)cs * CH * DK;
 
     if (tid < CH) sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
-    // per channel: the cumulative log decay and the gated operands (rows past
-    // the end: no decay, zero operands)
+    // log alpha rows into LDS (zeros past the end: no decay), then each
+    // channel's cumulative sum in place
+    for (int e = tid; e < CH * DK / 4; e += NTH) {
+        const int r = e / (DK / 4), c4 = (e % (DK / 4)) * 4;
+        float4 x = {0.f, 0.f, 0.f, 0.f};
+        if (r < valid) x = *reinterpret_cast<const float4*>(a.log_alpha + (tok0 + r) * DK + c4);
+        sG[r * KP + c4] = x.x;
+        sG[r * KP + c4 + 1] = x.y;
+        sG[r * KP + c4 + 2] = x.z;
+        sG[r * KP + c4 + 3] = x.w;
+    }
+    lds_barrier();
     for (int ch = tid; ch < DK; ch += NTH) {
-        float tot = 0.f;
-        for (int r = 0; r < valid; ++r) tot += a.log_alpha[(tok0 + r) * DK + ch];
         float G = 0.f;
         for (int r = 0; r < CH; ++r) {
-            float kv = 0.f, qv = 0.f;
-            if (r < valid) {
-                G += a.log_alpha[(tok0 + r) * DK + ch];
-                kv = load1<F32IN>(a.k, (tok0 + r) * DK + ch);
-                qv = load1<F32IN>(a.q, (tok0 + r) * DK + ch);
-            }
+            G += sG[r * KP + ch];
+            sG[r * KP + ch] = G;
+        }
+    }
+    lds_barrier();
+    // the gated operands, eight channels of one row per thread and step (rows
+    // past the end: zero operands)
+    for (int e = tid; e < CH * DK / 8; e += NTH) {
+        const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+        float kx[8], qx[8], gq[8], gh[8], gc[8], gt[8], gg[8];
+        load8<F32IN>(a.k, (tok0 + r) * DK + c8, r < valid, kx);
+        load8<F32IN>(a.q, (tok0 + r) * DK + c8, r < valid, qx);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float G = sG[r * KP + c8 + j], G63 = sG[(CH - 1) * KP + c8 + j];
             const float eg = expf(G), emg = expf(-G);
-            const size_t at = po + (size_t)r * DK + ch;
-            sKh[r * KP + ch] = kv * eg;
-            sKc[r * KP + ch] = kv * emg;
-            sQh[r * KP + ch] = qv * eg;
-            a.wG[at] = G;
-            a.wQh[at] = qv * eg;
-            a.wKh[at] = kv * eg;
-            a.wKc[at] = kv * emg;
-            a.wKt[at] = kv * expf(tot - G);
+            gg[j] = G;
+            gq[j] = qx[j] * eg;
+            gh[j] = kx[j] * eg;
+            gc[j] = kx[j] * emg;
+            gt[j] = kx[j] * expf(G63 - G);
+            sQh[r * KP + c8 + j] = gq[j];
+            sKh[r * KP + c8 + j] = gh[j];
+            sKc[r * KP + c8 + j] = gc[j];
+        }
+        const size_t at = po + (size_t)r * DK + c8;
+        float* const dst[5] = {a.wG + at, a.wQh + at, a.wKh + at, a.wKc + at, a.wKt + at};
+        const float* const src[5] = {gg, gq, gh, gc, gt};
+#pragma unroll
+        for (int t = 0; t < 5; ++t) {
+            reinterpret_cast<float4*>(dst[t])[0] = make_float4(src[t][0], src[t][1], src[t][2], src[t][3]);
+            reinterpret_cast<float4*>(dst[t])[1] = make_float4(src[t][4], src[t][5], src[t][6], src[t][7]);
         }
     }
     lds_barrier();
