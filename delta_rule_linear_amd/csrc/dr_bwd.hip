@@ -601,6 +601,32 @@ __device__ __forceinline__ void st4(float* p, const float4& v) {
     p[0] = v.x; p[1] = v.y; p[2] = v.z; p[3] = v.w;
 }
 
+// Register prefetch of a chunk's [64][DK] fp32 workspace plane, stored to LDS
+// rows of pitch DK + 1.
+template <int DK, int NT>
+struct PlanePre {
+    float4 x[CH * DK / 4 / NT];
+};
+
+template <int DK, int NT>
+__device__ __forceinline__ void pre_plane(PlanePre<DK, NT>& p, const float* src, int tid) {
+#pragma unroll
+    for (int n = 0; n < CH * DK / 4 / NT; ++n) p.x[n] = reinterpret_cast<const float4*>(src)[tid + n * NT];
+}
+
+template <int DK, int NT>
+__device__ __forceinline__ void put_plane(const PlanePre<DK, NT>& p, float* dst, int tid) {
+    constexpr int KP = DK + 1;
+#pragma unroll
+    for (int n = 0; n < CH * DK / 4 / NT; ++n) {
+        const int e = tid + n * NT, r = e / (DK / 4), c = (e % (DK / 4)) * 4;
+        dst[r * KP + c] = p.x[n].x;
+        dst[r * KP + c + 1] = p.x[n].y;
+        dst[r * KP + c + 2] = p.x[n].z;
+        dst[r * KP + c + 3] = p.x[n].w;
+    }
+}
+
 // The state-sized products of the per-chunk gradient kernel, over slabs of VS
 // state columns on the fp16 matrix cores with two-term operands (three
 // products per pair, lo * lo dropped):
@@ -608,13 +634,15 @@ __device__ __forceinline__ void st4(float* p, const float4& v) {
 //   acc = dO U^T (hf 0) or dU R^T (hf 1)   (rows 16 R .., column blocks I <= R)
 // and <H, S>: summed into shs[0], or per state row into shs[d] (CG).  The
 // last slab's turn prefetches T, P, K K^T (and, for bf16 inputs without a
-// channel gate, the q and k rows) for the 64 x 64 part.
+// channel gate, the q and k rows; with one, the gated Kc and Q^ rows) for the
+// 64 x 64 part.
 template <int DK, bool F32IN, bool CG>
 __device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, int valid, size_t tok0, float* s1,
                                                     f32x4 (&z1)[DK / 32], f32x4 (&z2)[DK / 32], f32x4 (&z3)[DK / 32],
                                                     f32x4 (&acc)[4], float* shs, RowsPre<DK, F32IN, PNT>& pk,
                                                     RowsPre<DK, F32IN, PNT>& pq, MatPre<PNT>& pt, MatPre<PNT>& pp,
-                                                    MatPre<PNT>& pa) {
+                                                    MatPre<PNT>& pa, PlanePre<DK, PNT>* pkc = nullptr,
+                                                    PlanePre<DK, PNT>* pqh = nullptr) {
     using Lp = PostLds<DK>;
     constexpr int VS = Lp::VS, NDH = DK / 32;
     constexpr int NS = DK * VS / 4 / PNT;   // float4 of S (and of H) per thread and slab
@@ -705,6 +733,10 @@ __device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, in
             pre_mat(pt, a.wT + mo, tid);
             pre_mat(pp, a.wP + mo, tid);
             pre_mat(pa, a.wA + mo, tid);
+            if constexpr (CG) {   // the gated Kc and Q^ rows
+                pre_plane(*pkc, a.wKc + (size_t)cs * CH * DK, tid);
+                pre_plane(*pqh, a.wQh + (size_t)cs * CH * DK, tid);
+            }
         }
         const int ra = 16 * R + i16;
         const Frag<2> fo = slab_frag(sOh, sOl, ra, g);
@@ -962,32 +994,6 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
 // dK~ K~ over the chunk and e^G_63 <H_c, S_c>; d log alpha is dG's reverse
 // cumulative sum per channel.  e^-G needs the within-chunk cumulative log
 // decay of every channel to stay above about -88 (fp32 range).
-
-// Register prefetch of a chunk's [64][DK] fp32 workspace plane, stored to LDS
-// rows of pitch DK + 1.
-template <int DK, int NT>
-struct PlanePre {
-    float4 x[CH * DK / 4 / NT];
-};
-
-template <int DK, int NT>
-__device__ __forceinline__ void pre_plane(PlanePre<DK, NT>& p, const float* src, int tid) {
-#pragma unroll
-    for (int n = 0; n < CH * DK / 4 / NT; ++n) p.x[n] = reinterpret_cast<const float4*>(src)[tid + n * NT];
-}
-
-template <int DK, int NT>
-__device__ __forceinline__ void put_plane(const PlanePre<DK, NT>& p, float* dst, int tid) {
-    constexpr int KP = DK + 1;
-#pragma unroll
-    for (int n = 0; n < CH * DK / 4 / NT; ++n) {
-        const int e = tid + n * NT, r = e / (DK / 4), c = (e % (DK / 4)) * 4;
-        dst[r * KP + c] = p.x[n].x;
-        dst[r * KP + c + 1] = p.x[n].y;
-        dst[r * KP + c + 2] = p.x[n].z;
-        dst[r * KP + c + 3] = p.x[n].w;
-    }
-}
 
 // A [64][DK] fp32 workspace plane straight into LDS rows of pitch DK + 1.
 template <int DK, int NT>
@@ -1392,15 +1398,17 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
 
     RowsPre<DK, F32IN, PNT> pk, pq;   // not used with a channel gate
     MatPre<PNT> pt, pp, pa;
+    PlanePre<DK, PNT> pkc, pqh;
     f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
-    post_state_products<DK, F32IN, true>(a, cs, valid, tok0, s1, z1, z2, z3, acc, shs, pk, pq, pt, pp, pa);
+    post_state_products<DK, F32IN, true>(a, cs, valid, tok0, s1, z1, z2, z3, acc, shs, pk, pq, pt, pp, pa, &pkc,
+                                         &pqh);
     lds_barrier();
 
     // ---- Kc and Q^ rows, T and K^ Kc^T
     float* sKx = s1;             // Kc, later K^
     float* sQh = s1 + CH * KP;
-    load_plane<DK, PNT>(sKx, a.wKc + pofs, tid);
-    load_plane<DK, PNT>(sQh, a.wQh + pofs, tid);
+    put_plane(pkc, sKx, tid);
+    put_plane(pqh, sQh, tid);
     put_mat(pt, sM0, tid);
     put_mat(pa, sM2, tid);
     lds_barrier();
@@ -1534,17 +1542,32 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
         }
     }
     lds_barrier();
-    // d log alpha_rc = sum_{r' >= r} X + sum_{i < r} Y + e^G_63 <H_c, S_c>
-    for (int ch = tid; ch < DK; ch += PNT) {
-        float totY = 0.f;
-        for (int r = 0; r < CH; ++r) totY += sYg[r * KP + ch];
-        const float hsc = expf(a.wG[pofs + (size_t)(CH - 1) * DK + ch]) * shs[ch];
-        float sufX = 0.f, sufY = 0.f;
-        for (int r = CH - 1; r >= 0; --r) {
-            sufX += sXg[r * KP + ch];
-            sufY += sYg[r * KP + ch];
-            if (r < valid) a.dlog_alpha[(tok0 + r) * DK + ch] = sufX + (totY - sufY) + hsc;
-        }
+    // d log alpha_rc = sum_{r' >= r} X + sum_{i < r} Y + e^G_63 <H_c, S_c>,
+    // each channel's rows split into NP parts of RP rows, one thread per part
+    constexpr int NP = PNT / DK, RP = CH / NP;
+    static_assert(2 * NP * DK <= CH * PT, "part sums fit in sM3");
+    const int ch = tid % DK, part = tid / DK;
+    float px = 0.f, py = 0.f;
+    for (int r = part * RP; r < (part + 1) * RP; ++r) {
+        px += sXg[r * KP + ch];
+        py += sYg[r * KP + ch];
+    }
+    float* sPx = sM3;   // N is no longer read
+    float* sPy = sM3 + NP * DK;
+    sPx[part * DK + ch] = px;
+    sPy[part * DK + ch] = py;
+    lds_barrier();
+    float sufX = 0.f, before = 0.f;   // X below this part, Y above it
+    for (int q = 0; q < NP; ++q) {
+        if (q > part) sufX += sPx[q * DK + ch];
+        if (q < part) before += sPy[q * DK + ch];
+    }
+    const float hsc = expf(a.wG[pofs + (size_t)(CH - 1) * DK + ch]) * shs[ch];
+    float sy = 0.f;   // Y of this part from row r down
+    for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
+        sufX += sXg[r * KP + ch];
+        sy += sYg[r * KP + ch];
+        if (r < valid) a.dlog_alpha[(tok0 + r) * DK + ch] = sufX + before + (py - sy) + hsc;
     }
     if (w == 0 && l < valid) a.dbeta[tok0 + l] = sdb[l];
 }
