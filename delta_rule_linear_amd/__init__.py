@@ -19,7 +19,7 @@ With a diagonal preconditioner on the gradient step (write-side key scales):
     o, S = dr_chunk_fwd_precond(q, k, v, log_alpha, beta, key_scale, S0, gate="scalar",
                                 beta_mode="scalar")
 
-Gradients of the chunked forward (any gate, scalar beta):
+Gradients of the chunked forward (any gate and beta mode):
 
     g = dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final, gate="scalar")
     g["dq"], g["dk"], g["dv"], g["dlog_alpha"], g["dbeta"], g["dS0"]
@@ -309,9 +309,9 @@ def dr_chunk_bwd_workspace_bytes(desc: ChunkDesc) -> int:
     return int(lib().dr_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
 
 
-def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, want_dS0: bool = True,
-                 workspace=None, stream=None):
-    """Gradients of dr_chunk_fwd (any gate, scalar beta) for the
+def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, beta_mode: str = "scalar",
+                 want_dS0: bool = True, workspace=None, stream=None):
+    """Gradients of dr_chunk_fwd (any gate and beta mode) for the
     loss whose gradients with respect to o and S_final are dO [B,H,L,Dv] and
     dS_final [B,H,Dk,Dv] (fp32; dS_final None means zero).  q, k, v and the
     other inputs are as for dr_chunk_fwd.  Returns a dict of fp32 device
@@ -329,7 +329,8 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
             raise ValueError("gate 'none' takes no log_alpha")
     else:
         _need(log_alpha, "log_alpha", torch.float32, gshape)
-    _need(beta, "beta", torch.float32, (B, H, L))
+    bshape = (B, H, L) if beta_mode == "scalar" else (B, H, L, Dk)
+    _need(beta, "beta", torch.float32, bshape)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
     _need(dO, "dO", torch.float32, (B, H, L, Dv))
@@ -339,9 +340,9 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
     out = {"dq": torch.empty((B, H, L, Dk), **f32), "dk": torch.empty((B, H, L, Dk), **f32),
            "dv": torch.empty((B, H, L, Dv), **f32),
            "dlog_alpha": torch.empty(gshape, **f32) if gshape is not None else None,
-           "dbeta": torch.empty((B, H, L), **f32),
+           "dbeta": torch.empty(bshape, **f32),
            "dS0": torch.empty((B, H, Dk, Dv), **f32) if want_dS0 else None}
-    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, "scalar")
+    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, beta_mode)
     nbytes = dr_chunk_bwd_workspace_bytes(desc)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

@@ -319,7 +319,7 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
 
 // ----------------------------------------------------------------- backward
 struct BwdLayout {
-    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, total;
+    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, ones, db1, total;
 };
 
 BwdLayout bwd_layout(const dr_chunk_desc& d) {
@@ -349,6 +349,15 @@ BwdLayout bwd_layout(const dr_chunk_desc& d) {
         w.Kc = take(NCH * dr::CH * d.Dk * f);
         w.Kt = take(NCH * dr::CH * d.Dk * f);
     }
+    if (d.beta == DR_BETA_CHANNEL) {
+        // q, sqrt(beta) k, sqrt(beta) v in fp32, unit strengths and their (unused) gradient
+        const size_t ntok = (size_t)d.B * d.H * d.L;
+        w.q32 = take(ntok * d.Dk * f);
+        w.k32 = take(ntok * d.Dk * f);
+        w.v32 = take(ntok * d.Dv * f);
+        w.ones = take(ntok * f);
+        w.db1 = take(ntok * f);
+    }
     w.total = NCH ? off : 0;
     return w;
 }
@@ -356,7 +365,6 @@ BwdLayout bwd_layout(const dr_chunk_desc& d) {
 dr_status check_bwd_desc(const dr_chunk_desc* d) {
     dr_status s = check_chunk_desc(d);
     if (s != DR_OK) return s;
-    if (d->beta != DR_BETA_SCALAR) return fail(DR_ERR_UNSUPPORTED, "the backward covers the scalar beta");
     if (d->input_flags) return fail(DR_ERR_UNSUPPORTED, "the backward takes no input_flags");
     if (d->out_dtype != DR_F32) return fail(DR_ERR_UNSUPPORTED, "dO and the gradients are fp32: out_dtype must be DR_F32");
     const size_t NCH = (size_t)d->B * d->H * (((size_t)d->L + dr::CH - 1) / dr::CH);
@@ -431,8 +439,29 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         a.wKc = (float*)(ws + w.Kc);
         a.wKt = (float*)(ws + w.Kt);
     }
-    hipError_t e = dr::launch_bwd(a, d->Dk, d->in_dtype == DR_F32, st);
+    bool f32in = d->in_dtype == DR_F32;
+    const bool cbeta = d->beta == DR_BETA_CHANNEL;
+    const size_t ntok = nseq * d->L, nel = ntok * d->Dk;   // Dv == Dk with a channel beta
+    hipError_t e = hipSuccess;
+    if (cbeta) {
+        // the scaled inputs with unit strengths; the beta gradient of that run is discarded
+        float* q32 = (float*)(ws + w.q32);
+        float* k32 = (float*)(ws + w.k32);
+        float* v32 = (float*)(ws + w.v32);
+        float* ones = (float*)(ws + w.ones);
+        e = dr::launch_bwd_cbeta_in(q, k, v, beta, f32in, nel, ntok, q32, k32, v32, ones, st);
+        if (e != hipSuccess) return fail(DR_ERR_HIP, "backward input scaling launch: %s", hipGetErrorString(e));
+        a.q = q32; a.k = k32; a.v = v32;
+        a.beta = ones;
+        a.dbeta = (float*)(ws + w.db1);
+        f32in = true;
+    }
+    e = dr::launch_bwd(a, d->Dk, f32in, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
+    if (cbeta) {
+        e = dr::launch_bwd_cbeta_out(k, v, beta, d->in_dtype == DR_F32, nel, dk, dv, dbeta, st);
+        if (e != hipSuccess) return fail(DR_ERR_HIP, "backward gradient mapping launch: %s", hipGetErrorString(e));
+    }
     return DR_OK;
 }
 

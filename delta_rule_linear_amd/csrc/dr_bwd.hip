@@ -1588,6 +1588,42 @@ hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// ============================================== channel-wise beta (FG2-GDN)
+// With a channel-wise beta, kt = sqrt(beta) (.) k and vt = sqrt(beta) (.) v
+// enter the recurrence as a key and a value of unit strength.  So the
+// backward runs the kernels above on (q, kt, vt) with beta = 1, then maps the
+// gradients of kt and vt back: dk = sqrt(beta) dkt, dv = sqrt(beta) dvt,
+// dbeta = (dkt k + dvt v) / (2 sqrt(beta)) per channel (beta > 0).
+
+// q, kt, vt as fp32, and a unit strength per token
+__global__ void bwd_cbeta_in_kernel(const void* q, const void* k, const void* v, const float* beta, int f32in,
+                                    size_t n, size_t ntok, float* q32, float* k32, float* v32, float* ones) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const float sb = sqrtf(beta[i]);
+        const float qv = f32in ? load1<true>(q, i) : load1<false>(q, i);
+        const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
+        const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
+        q32[i] = qv;
+        k32[i] = sb * kv;
+        v32[i] = sb * vv;
+        if (i < ntok) ones[i] = 1.f;
+    }
+}
+
+// dk, dv hold the gradients of kt and vt on entry, those of k and v on exit
+__global__ void bwd_cbeta_out_kernel(const void* k, const void* v, const float* beta, int f32in, size_t n,
+                                     float* dk, float* dv, float* dbeta) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+        const float sb = sqrtf(beta[i]);
+        const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
+        const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
+        const float dkt = dk[i], dvt = dv[i];
+        dbeta[i] = (dkt * kv + dvt * vv) / (2.f * sb);
+        dk[i] = sb * dkt;
+        dv[i] = sb * dvt;
+    }
+}
+
 template <int DK, bool F32IN>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
@@ -1605,6 +1641,21 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta, bool f32in,
+                               size_t n, size_t ntok, float* q32, float* k32, float* v32, float* ones,
+                               hipStream_t st) {
+    hipLaunchKernelGGL(bwd_cbeta_in_kernel, dim3(2048), dim3(256), 0, st, q, k, v, beta, (int)f32in, n, ntok, q32,
+                       k32, v32, ones);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta, bool f32in, size_t n, float* dk,
+                                float* dv, float* dbeta, hipStream_t st) {
+    hipLaunchKernelGGL(bwd_cbeta_out_kernel, dim3(2048), dim3(256), 0, st, k, v, beta, (int)f32in, n, dk, dv,
+                       dbeta);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st) {
     if (a.cgate) {

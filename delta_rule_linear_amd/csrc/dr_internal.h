@@ -152,6 +152,14 @@ hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
 // the backward (dr_bwd.hip)
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st);
+// channel-wise beta: q, sqrt(beta) k, sqrt(beta) v as fp32 and unit strengths
+// before the backward (n = tokens x Dk, ntok = tokens); the gradients of k,
+// v and beta from those of the scaled key and value after it
+hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta, bool f32in,
+                               size_t n, size_t ntok, float* q32, float* k32, float* v32, float* ones,
+                               hipStream_t st);
+hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta, bool f32in, size_t n, float* dk,
+                                float* dv, float* dbeta, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st);
 

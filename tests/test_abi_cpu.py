@@ -242,7 +242,7 @@ def test_backward_validation_and_workspace():
     assert call(d, dla=None) == drl.DR_ERR_NULL                        # scalar gate: d log alpha needed
     assert call(_desc(gate="none"), la=None) == drl.DR_ERR_NULL        # no gate: none allowed
     assert call(d, dS0=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
-    for bad in (dict(Dv=128, beta_mode="channel"), dict(flags=drl.DR_IN_QK_L2NORM),
+    for bad in (dict(Dv=64, beta_mode="channel"), dict(flags=drl.DR_IN_QK_L2NORM),
                 dict(out_dtype=drl.DR_BF16), dict(Dk=96)):
         assert call(_desc(**bad)) == drl.DR_ERR_UNSUPPORTED
         assert drl.dr_chunk_bwd_workspace_bytes(_desc(**bad)) == 0
@@ -256,5 +256,7 @@ def test_backward_validation_and_workspace():
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(L=0)) == 0
     # a channel gate adds the per-channel decay and four gated operand planes
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(gate="channel")) >= need + NCH * 4 * 5 * 64 * 128 - NCH * 4 * 64
+    # a channel beta runs the unit-strength kernels on fp32 copies of q, sqrt(beta) k, sqrt(beta) v
+    assert drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel")) >= need + 3 * 2 * 3 * 100 * 128 * 4
     # no sequences: validated and done without touching memory
     assert lib.dr_chunk_bwd(ctypes.byref(_desc(B=0)), *([None] * 15), 0, None) == drl.DR_OK

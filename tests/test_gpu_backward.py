@@ -31,7 +31,7 @@ def run_bwd(p, dO, dSf):
     import delta_rule_linear_amd as drl
     t = problem_to_dev(p)
     g = drl.dr_chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"], to_dev(dO, "f32"),
-                         to_dev(dSf, "f32"), gate=p.gate)
+                         to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode)
     torch.cuda.synchronize()
     return g
 
@@ -67,6 +67,18 @@ def test_backward_sweep(dtype, gate, L, D):
     p = inputs.make_chunk_problem(2, 2, L, D, D, in_dtype=dtype, gate=gate, s0_var=0.01, seed=L + D,
                                   log_alpha_range=rng, name=f"bwd_{gate}_{dtype}")
     _check(p, seed=L)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("L", [1, 65, 200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_channel_beta_sweep(dtype, gate, L, D):
+    # FG2-GDN: beta per channel scales k and v by its square root
+    rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
+    p = inputs.make_chunk_problem(2, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode="channel", s0_var=0.01,
+                                  seed=L + D + 7, log_alpha_range=rng, name=f"bwd_cbeta_{gate}_{dtype}")
+    _check(p, seed=L + 1)
 
 
 @pytest.mark.parametrize("Dv", [16, 48, 256])
@@ -127,6 +139,23 @@ def test_backward_channel_gate_full_size_sampled_sequences():
     dO, dSf = inputs.backward_cotangents(p, 0)
     g = run_bwd(p, dO, dSf)
     for b, h in [(0, 0), (1, 31)]:
+        s = p.head(b, h)
+        ref = oracle_bwd(s, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1])
+        for n in GRADS:
+            x = to_np(g[n][b:b + 1, h:h + 1])
+            e = rel_err(x, ref[n])
+            assert e <= TOL["bf16"], f"sequence ({b},{h}) {n}: {e:.2e}"
+    del g
+    torch.cuda.empty_cache()
+
+
+def test_backward_channel_beta_full_size_sampled_sequences():
+    # the FG2-GDN shape (B=2, H=16, L=16384, d=128, bf16, channel gate and beta) in one call
+    p = inputs.workload("fg2_b2h16_16k")
+    announce("backward full size", p.name)
+    dO, dSf = inputs.backward_cotangents(p, 0)
+    g = run_bwd(p, dO, dSf)
+    for b, h in [(0, 3), (1, 12)]:
         s = p.head(b, h)
         ref = oracle_bwd(s, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1])
         for n in GRADS:
