@@ -27,7 +27,8 @@ Also reported in the same line:
   backward      dr_chunk_bwd on the headline batch (seeded dO and dS_final),
                 per-kernel times, the dominant kernel against the fp32
                 matrix-core peak, and the CPU oracle's backward on 4 heads;
-                also the backward at the KDA shape (channel gate);
+                also the backward at the KDA shape (channel gate) and the
+                FG2-GDN shape (channel gate and beta);
   cpu_baseline  the fp64 CPU oracle on the whole headline batch, on the
                 host's cores, with the GPU result checked against it.
 The headline inputs follow the seeded NumPy recipe of
@@ -479,41 +480,44 @@ def main():
             del ref
         del gdO, gdSf, bws, grads
         torch.cuda.empty_cache()
-        # the KDA shape (channel gate), inputs drawn on the device like the
-        # extra forward workloads
-        gen.manual_seed(0)
-        kb, kh, kl = 2, 32, 16384
-        xq = l2n(torch.randn((kb, kh, kl, D), generator=gen, device=dev)).bfloat16()
-        xk = l2n(torch.randn((kb, kh, kl, D), generator=gen, device=dev)).bfloat16()
-        xv = torch.randn((kb, kh, kl, D), generator=gen, device=dev).bfloat16()
-        xla = torch.rand((kb, kh, kl, D), generator=gen, device=dev) * 0.1995 - 0.2
-        xbe = torch.sigmoid(torch.randn((kb, kh, kl), generator=gen, device=dev))
-        xdO = torch.randn((kb, kh, kl, D), generator=gen, device=dev)
-        xdS = torch.randn((kb, kh, D, D), generator=gen, device=dev)
-        xdesc = drl.chunk_desc(kb, kh, kl, D, D, drl.DR_BF16, drl.DR_F32, "channel", "scalar")
-        xws = torch.empty(drl.dr_chunk_bwd_workspace_bytes(xdesc), dtype=torch.uint8, device=dev)
+        # the KDA shape (channel gate) and the FG2-GDN shape (channel gate and
+        # beta), inputs drawn on the device like the extra forward workloads
+        for bname, kb, kh, kl, bmode in (("kda_b2h32_16k", 2, 32, 16384, "scalar"),
+                                         ("fg2_b2h16_16k", 2, 16, 16384, "channel")):
+            gen.manual_seed(0)
+            xq = l2n(torch.randn((kb, kh, kl, D), generator=gen, device=dev)).bfloat16()
+            xk = l2n(torch.randn((kb, kh, kl, D), generator=gen, device=dev)).bfloat16()
+            xv = torch.randn((kb, kh, kl, D), generator=gen, device=dev).bfloat16()
+            xla = torch.rand((kb, kh, kl, D), generator=gen, device=dev) * 0.1995 - 0.2
+            bsh = (kb, kh, kl) if bmode == "scalar" else (kb, kh, kl, D)
+            xbe = torch.sigmoid(torch.randn(bsh, generator=gen, device=dev))
+            xdO = torch.randn((kb, kh, kl, D), generator=gen, device=dev)
+            xdS = torch.randn((kb, kh, D, D), generator=gen, device=dev)
+            xdesc = drl.chunk_desc(kb, kh, kl, D, D, drl.DR_BF16, drl.DR_F32, "channel", bmode)
+            xws = torch.empty(drl.dr_chunk_bwd_workspace_bytes(xdesc), dtype=torch.uint8, device=dev)
 
-        def kstep():
-            drl.dr_chunk_bwd(xq, xk, xv, xla, xbe, None, xdO, xdS, gate="channel", workspace=xws)
+            def kstep():
+                drl.dr_chunk_bwd(xq, xk, xv, xla, xbe, None, xdO, xdS, gate="channel", beta_mode=bmode,
+                                 workspace=xws)
 
-        for _ in range(2):
-            kstep()
-        torch.cuda.synchronize()
-        drl.dr_profile_begin()
-        kper = time_steps(kstep, args.bwd_steps, 0)
-        kprof = drl.dr_profile_end()
-        kms = float(np.median(kper))
-        kcalls = max(1, kprof["bwd_calls"])
-        knch = kb * kh * ((kl + CH - 1) // CH)
-        kfl = sum(bwd_flops_per_chunk(D, D).values()) * knch
-        bwd["kda_b2h32_16k"] = {
-            "shape": f"B={kb} H={kh} L={kl} d={D}, channel gate, scalar beta, bf16 q/k/v, S0 = 0",
-            "ms_per_step": round(kms, 4), "tokens_per_s": round(kb * kl / (kms * 1e-3), 1),
-            "kernels_ms": {n: round(kprof[f"bwd_{n}_ms"] / kcalls, 4) for n in ("prep", "fscan", "rscan", "post")},
-            "mfma_frac_whole_backward": round(kfl / (kms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
-            "workspace_bytes": int(xws.numel())}
-        del xq, xk, xv, xla, xbe, xdO, xdS, xws
-        torch.cuda.empty_cache()
+            for _ in range(2):
+                kstep()
+            torch.cuda.synchronize()
+            drl.dr_profile_begin()
+            kper = time_steps(kstep, args.bwd_steps, 0)
+            kprof = drl.dr_profile_end()
+            kms = float(np.median(kper))
+            kcalls = max(1, kprof["bwd_calls"])
+            knch = kb * kh * ((kl + CH - 1) // CH)
+            kfl = sum(bwd_flops_per_chunk(D, D).values()) * knch
+            bwd[bname] = {
+                "shape": f"B={kb} H={kh} L={kl} d={D}, channel gate, {bmode} beta, bf16 q/k/v, S0 = 0",
+                "ms_per_step": round(kms, 4), "tokens_per_s": round(kb * kl / (kms * 1e-3), 1),
+                "kernels_ms": {n: round(kprof[f"bwd_{n}_ms"] / kcalls, 4) for n in ("prep", "fscan", "rscan", "post")},
+                "mfma_frac_whole_backward": round(kfl / (kms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                "workspace_bytes": int(xws.numel())}
+            del xq, xk, xv, xla, xbe, xdO, xdS, xws
+            torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU baseline (oracle)
     cpu = None

@@ -249,7 +249,8 @@ dr_status dr_decode_step_precond(const dr_decode_desc* d, const void* q, const v
  * the backward or there is no work): per 64-token chunk of every sequence,
  * three 64 x 64 matrices, 64 gate values, two Dk x Dv states and three
  * 64 x Dv blocks, all fp32; with a channel gate 64 x Dk gate values and four
- * more 64 x Dk blocks (the gated keys and queries). */
+ * more 64 x Dk blocks (the gated keys and queries); with a channel beta fp32
+ * copies of q, k and v and two floats per token. */
 size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
 
 /*
@@ -262,10 +263,13 @@ size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
  * state, a reverse pass carries the state gradient, and a per-chunk pass
  * forms the gradients of q, k, beta and log alpha.  Everything runs in fp32.
  *
- * Covered modes: every gate (plain DeltaNet, Gated DeltaNet, KDA), d->beta
- * DR_BETA_SCALAR, d->input_flags 0 (gradients are with respect to the
+ * Covered modes: every gate and beta mode (plain DeltaNet, Gated DeltaNet,
+ * KDA, FG2-GDN), d->input_flags 0 (gradients are with respect to the
  * strengths and vectors as given), d->out_dtype DR_F32 (the dtype of dO);
- * anything else is DR_ERR_UNSUPPORTED.  in_dtype (fp32 or bf16) is the dtype
+ * anything else is DR_ERR_UNSUPPORTED.  With DR_BETA_CHANNEL the kernels run
+ * on fp32 copies of q, sqrt(beta) (.) k and sqrt(beta) (.) v with unit
+ * strength, and map the gradients back elementwise (beta > 0 assumed: the
+ * square root has no derivative at 0).  in_dtype (fp32 or bf16) is the dtype
  * of q, k, v; Dk, Dv as for dr_chunk_fwd.  With DR_GATE_CHANNEL the kernels
  * work on keys and queries scaled by e^{+-G}, G a channel's cumulative log
  * decay within a 64-token chunk, so each G must stay above about -80 (fp32
@@ -279,7 +283,7 @@ size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
  *   dv         [B][H][L][Dv] fp32, written
  *   dlog_alpha log_alpha's shape ([B][H][L] or [B][H][L][Dk]) fp32, written;
  *              required with a gate, must be NULL without one
- *   dbeta      [B][H][L] fp32, written
+ *   dbeta      beta's shape ([B][H][L] or [B][H][L][Dk]) fp32, written
  *   dS0        [B][H][Dk][Dv] fp32, gradient with respect to S0, written, or
  *              NULL to skip
  *   workspace  device scratch of at least dr_chunk_bwd_workspace_bytes(d)
