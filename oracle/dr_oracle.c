@@ -261,13 +261,17 @@ int dro_forward(int B, int H, int L, int Dk, int Dv,
  *   dbeta     out, beta's shape (the derivative of sqrt at 0 is infinite:
  *             beta > 0 is assumed)
  *   dS0       [B][H][Dk][Dv] out, or NULL
+ * dro_backward_kv takes a separate write strength beta_v (beta's shape; the
+ * forward's FG2-GDN+ reading: vt = sqrt(beta_v) v, beta on kt only) and
+ * returns its gradient in dbeta_v; dbeta then holds beta's (erase strength's)
+ * part alone.
  */
-int dro_backward(int B, int H, int L, int Dk, int Dv,
-                 const double* q, const double* k, const double* v,
-                 const double* log_alpha, int gate, const double* beta, int beta_mode,
-                 const double* S0, const double* dO, const double* dS_final,
-                 double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta, double* dS0,
-                 int nthreads)
+static int backward_impl(int B, int H, int L, int Dk, int Dv,
+                         const double* q, const double* k, const double* v,
+                         const double* log_alpha, int gate, const double* beta, const double* beta_v,
+                         int beta_mode, const double* S0, const double* dO, const double* dS_final,
+                         double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta,
+                         double* dbeta_v, double* dS0, int nthreads)
 {
     if (B <= 0 || H <= 0 || L < 0 || Dk <= 0 || Dv <= 0) return DRO_EINVAL;
     if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return DRO_EINVAL;
@@ -308,6 +312,7 @@ int dro_backward(int B, int H, int L, int Dk, int Dv,
         const double* vs = v + (size_t)s * L * Dv;
         const double* las = log_alpha ? log_alpha + (size_t)s * lw : NULL;
         const double* bs = beta + (size_t)s * bw;
+        const double* bvs = beta_v ? beta_v + (size_t)s * bw : bs;   /* the write strength */
         /* outputs, then the forward step's scratch: kt (Dk), vt (Dv), p (Dv) */
         double* tmp_o = (double*)malloc(sizeof(double) * ((size_t)L * Dv + (size_t)Dk + 2 * (size_t)Dv));
         if (!tmp_o) {
@@ -327,7 +332,7 @@ int dro_backward(int B, int H, int L, int Dk, int Dv,
                 run_sequence(1, Dk, Dv, qs + (size_t)t * Dk, ks_ + (size_t)t * Dk, vs + (size_t)t * Dv,
                              las ? las + (gate == DRO_GATE_CHANNEL ? (size_t)t * Dk : (size_t)t) : NULL, gate,
                              bs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t),
-                             bs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,
+                             bvs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,
                              NULL, 0, St + (size_t)(t + 1) * sz, tmp_o + (size_t)t * Dv, ktmp, vtmp, ptmp);
             }
         }
@@ -349,7 +354,7 @@ int dro_backward(int B, int H, int L, int Dk, int Dv,
                       : gate == DRO_GATE_SCALAR ? exp(las[t]) : exp(las[(size_t)t * Dk + c]);
             }
             for (int j = 0; j < Dv; ++j) {
-                const double b = beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + j];
+                const double b = beta_mode == DRO_BETA_SCALAR ? bvs[t] : bvs[(size_t)t * Dk + j];
                 sbv[j] = sqrt(b);
                 vt[j] = sbv[j] * v_t[j];
             }
@@ -403,13 +408,26 @@ int dro_backward(int B, int H, int L, int Dk, int Dv,
                 if (beta_mode == DRO_BETA_CHANNEL) dbeta[((size_t)s * L + t) * Dk + c] = g;
                 db_s += g;
             }
+            /* the value's part goes to the write strength when it is separate */
+            double* dbv = dbeta_v ? dbeta_v : dbeta;
+            double dbv_s = 0.0;
             for (int j = 0; j < Dv; ++j) {
                 dv[((size_t)s * L + t) * Dv + j] = sbv[j] * dvt[j];
                 const double g = dvt[j] * v_t[j] / (2.0 * sbv[j]);
-                if (beta_mode == DRO_BETA_CHANNEL) dbeta[((size_t)s * L + t) * Dk + j] += g;
-                db_s += g;
+                if (beta_mode == DRO_BETA_CHANNEL) {
+                    if (dbeta_v) dbv[((size_t)s * L + t) * Dk + j] = g;
+                    else dbv[((size_t)s * L + t) * Dk + j] += g;
+                }
+                dbv_s += g;
             }
-            if (beta_mode == DRO_BETA_SCALAR) dbeta[(size_t)s * L + t] = db_s;
+            if (beta_mode == DRO_BETA_SCALAR) {
+                if (dbeta_v) {
+                    dbeta[(size_t)s * L + t] = db_s;
+                    dbeta_v[(size_t)s * L + t] = dbv_s;
+                } else {
+                    dbeta[(size_t)s * L + t] = db_s + dbv_s;
+                }
+            }
         }
         if (dS0) memcpy(dS0 + (size_t)s * sz, G, sizeof(double) * sz);
         free(tmp_o);
@@ -417,6 +435,29 @@ int dro_backward(int B, int H, int L, int Dk, int Dv,
     }
     (void)nthreads;
     return err;
+}
+
+int dro_backward(int B, int H, int L, int Dk, int Dv,
+                 const double* q, const double* k, const double* v,
+                 const double* log_alpha, int gate, const double* beta, int beta_mode,
+                 const double* S0, const double* dO, const double* dS_final,
+                 double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta, double* dS0,
+                 int nthreads)
+{
+    return backward_impl(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, NULL, beta_mode, S0, dO, dS_final,
+                         dq, dk, dv, dlog_alpha, dbeta, NULL, dS0, nthreads);
+}
+
+int dro_backward_kv(int B, int H, int L, int Dk, int Dv,
+                    const double* q, const double* k, const double* v,
+                    const double* log_alpha, int gate, const double* beta, const double* beta_v, int beta_mode,
+                    const double* S0, const double* dO, const double* dS_final,
+                    double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta, double* dbeta_v,
+                    double* dS0, int nthreads)
+{
+    if (!beta_v || !dbeta_v) return DRO_EINVAL;
+    return backward_impl(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta_v, beta_mode, S0, dO, dS_final,
+                         dq, dk, dv, dlog_alpha, dbeta, dbeta_v, dS0, nthreads);
 }
 
 /* Threads the OpenMP runtime would use by default (1 without OpenMP). */

@@ -681,3 +681,57 @@ def pin_bwd_linear_inputs(fwd, bwd):
 
 
 BWD_PINS = [pin_bwd_directional_derivatives, pin_bwd_linear_inputs]
+
+
+# Backward with a separate write strength (FG2-GDN+).  Each pin takes
+# fwd(q, k, v, la, beta, S0, *, gate, beta_mode, beta_v) -> (o, S_final) and
+# bwd(q, k, v, la, beta, S0, dO, dS_final, *, gate, beta_mode, beta_v) -> dict
+# (with dbeta_v).
+
+def pin_bwd_kv_directional_derivatives(fwd, bwd):
+    """With beta^v separate from beta^k: for <Wo, o> + <WS, S_final>, the
+    gradients' inner product with random directions (each input alone, beta^v
+    included, then all at once) equals the central difference of the loss,
+    every gate, channel-wise strengths."""
+    salt = 260
+    for gate in ("none", "scalar", "channel"):
+        salt += 1
+        q, k, v, la, beta, S0, Wo, WS = _bwd_case(salt, gate, "channel")
+        bv = 0.2 + 0.7 * _rng(salt + 3000).uniform(0.0, 1.0, beta.shape)
+        kw = dict(gate=gate, beta_mode="channel")
+        g = bwd(q, k, v, la, beta, S0, Wo, WS, beta_v=bv, **kw)
+        x = dict(q=q, k=k, v=v, la=la, beta=beta, bv=bv, S0=S0)
+        grads = dict(q=g["dq"], k=g["dk"], v=g["dv"], la=g["dlog_alpha"], beta=g["dbeta"], bv=g["dbeta_v"],
+                     S0=g["dS0"])
+        r = _rng(salt + 2000)
+        dirs = {n: (None if a is None else r.standard_normal(a.shape)) for n, a in x.items()}
+
+        def loss(xx):
+            o, S = fwd(xx["q"], xx["k"], xx["v"], xx["la"], xx["beta"], xx["S0"], beta_v=xx["bv"], **kw)
+            return float(np.sum(Wo * o) + np.sum(WS * S))
+
+        for which in [[n] for n in x if x[n] is not None] + [[n for n in x if x[n] is not None]]:
+            h = 1e-5
+            xp = {n: (a if a is None else (a + h * dirs[n] if n in which else a)) for n, a in x.items()}
+            xm = {n: (a if a is None else (a - h * dirs[n] if n in which else a)) for n, a in x.items()}
+            fd = (loss(xp) - loss(xm)) / (2 * h)
+            an = sum(float(np.sum(grads[n] * dirs[n])) for n in which)
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
+                f"(kv, {gate}) d/d{'+'.join(which)}: analytic {an:.10e} vs difference {fd:.10e}"
+
+
+def pin_bwd_kv_equal_strengths(fwd, bwd):
+    """beta^v = beta^k is the one-strength rule: the gradients of q, k, v, log
+    alpha and S0 are those of the one-strength backward, and dbeta^k + dbeta^v
+    is its dbeta."""
+    for n, gate in enumerate(("scalar", "channel")):
+        q, k, v, la, beta, S0, Wo, WS = _bwd_case(280 + n, gate, "channel")
+        kw = dict(gate=gate, beta_mode="channel")
+        g2 = bwd(q, k, v, la, beta, S0, Wo, WS, beta_v=beta, **kw)
+        g1 = bwd(q, k, v, la, beta, S0, Wo, WS, beta_v=None, **kw)
+        for name in ("dq", "dk", "dv", "dlog_alpha", "dS0"):
+            _close(g2[name], g1[name], 1e-12, f"kv {gate} {name}")
+        _close(g2["dbeta"] + g2["dbeta_v"], g1["dbeta"], 1e-12, f"kv {gate} dbeta")
+
+
+BWD_KV_PINS = [pin_bwd_kv_directional_derivatives, pin_bwd_kv_equal_strengths]

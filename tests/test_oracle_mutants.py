@@ -179,3 +179,42 @@ def test_bwd_pins_catch_planted_mistake(tmp_path, name, old, new):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"
+
+
+# The backward with a separate write strength: the value scaled by the erase
+# strength, or the forward replayed with the erase strength on the value.
+BWD_KV_MUTANTS = [
+    ("bwd_value_scaled_by_erase_strength",
+     "const double b = beta_mode == DRO_BETA_SCALAR ? bvs[t] : bvs[(size_t)t * Dk + j];",
+     "const double b = beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + j];"),
+    ("bwd_replay_without_write_strength",
+     "bvs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,",
+     "bs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,"),
+    ("bwd_write_strength_gradient_halved",
+     "const double g = dvt[j] * v_t[j] / (2.0 * sbv[j]);",
+     "const double g = dvt[j] * v_t[j] / (4.0 * sbv[j]);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BWD_KV_MUTANTS, ids=[m[0] for m in BWD_KV_MUTANTS])
+def test_bwd_kv_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+
+    def fwd(q, k, v, la, beta, S0, *, gate, beta_mode, beta_v=None):
+        return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, beta_v=beta_v)
+
+    def bwd(q, k, v, la, beta, S0, dO, dS, *, gate, beta_mode, beta_v=None):
+        return oracle.backward(q, k, v, la, beta, S0, dO, dS, gate=gate, beta_mode=beta_mode, beta_v=beta_v,
+                               lib=lib)
+
+    caught = []
+    for pin in oracle_pins.BWD_KV_PINS:
+        try:
+            pin(fwd, bwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"

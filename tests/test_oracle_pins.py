@@ -137,6 +137,19 @@ def test_backward_pin(pin):
     pin(_fwd1, _bwd1)
 
 
+def _fwd_kv(q, k, v, la, beta, S0, *, gate, beta_mode, beta_v=None, lib=None):
+    return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, beta_v=beta_v, lib=lib)
+
+
+def _bwd_kv(q, k, v, la, beta, S0, dO, dS, *, gate, beta_mode, beta_v=None, lib=None):
+    return oracle.backward(q, k, v, la, beta, S0, dO, dS, gate=gate, beta_mode=beta_mode, beta_v=beta_v, lib=lib)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.BWD_KV_PINS, ids=lambda f: f.__name__)
+def test_backward_kv_pin(pin):
+    pin(_fwd_kv, _bwd_kv)
+
+
 def test_backward_without_final_state_gradient():
     q, k, v, la, beta, S0, Wo, WS = oracle_pins._bwd_case(310, "scalar", "scalar")
     a = oracle.backward(q, k, v, la, beta, S0, Wo, None, gate="scalar", beta_mode="scalar")
