@@ -42,7 +42,8 @@ DR_IN_QK_L2NORM, DR_IN_BETA_LOGIT = 1, 2
 EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "dr_decode_step",
            "dr_decode_step_kv", "dr_chunk_fwd_precond_workspace_bytes", "dr_chunk_fwd_precond",
            "dr_decode_step_precond", "dr_status_str", "dr_last_error", "dr_abi_version",
-           "dr_profile_begin", "dr_profile_end", "dr_chunk_bwd_workspace_bytes", "dr_chunk_bwd")
+           "dr_profile_begin", "dr_profile_end", "dr_chunk_bwd_workspace_bytes", "dr_chunk_bwd",
+           "dr_chunk_bwd_kv")
 
 
 class DeltaRuleError(RuntimeError):
@@ -108,6 +109,8 @@ def lib() -> ctypes.CDLL:
         L.dr_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.dr_chunk_bwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 15 + [ctypes.c_size_t, vp]
         L.dr_chunk_bwd.restype = ctypes.c_int
+        L.dr_chunk_bwd_kv.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 17 + [ctypes.c_size_t, vp]
+        L.dr_chunk_bwd_kv.restype = ctypes.c_int
         L.dr_status_str.argtypes = [ctypes.c_int]
         L.dr_status_str.restype = ctypes.c_char_p
         L.dr_last_error.argtypes = []
@@ -309,8 +312,19 @@ def dr_chunk_bwd_workspace_bytes(desc: ChunkDesc) -> int:
     return int(lib().dr_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
 
 
+def dr_chunk_bwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0, dO, dS_final=None, *, gate: str,
+                    want_dS0: bool = True, workspace=None, stream=None):
+    """Gradients of dr_chunk_fwd_kv (separate channel-wise erase and write
+    strengths, both [B,H,L,Dk] fp32): as dr_chunk_bwd, with dbeta the erase
+    strength's gradient and dbeta_v the write strength's."""
+    if beta_v is None:
+        raise ValueError("beta_v is required")
+    return dr_chunk_bwd(q, k, v, log_alpha, beta_k, S0, dO, dS_final, gate=gate, beta_mode="channel",
+                        want_dS0=want_dS0, workspace=workspace, stream=stream, _beta_v=beta_v)
+
+
 def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, beta_mode: str = "scalar",
-                 want_dS0: bool = True, workspace=None, stream=None):
+                 want_dS0: bool = True, workspace=None, stream=None, _beta_v=None):
     """Gradients of dr_chunk_fwd (any gate and beta mode) for the
     loss whose gradients with respect to o and S_final are dO [B,H,L,Dv] and
     dS_final [B,H,Dk,Dv] (fp32; dS_final None means zero).  q, k, v and the
@@ -333,6 +347,8 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
     _need(beta, "beta", torch.float32, bshape)
     if S0 is not None:
         _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
+    if _beta_v is not None:
+        _need(_beta_v, "beta_v", torch.float32, bshape)
     _need(dO, "dO", torch.float32, (B, H, L, Dv))
     if dS_final is not None:
         _need(dS_final, "dS_final", torch.float32, (B, H, Dk, Dv))
@@ -347,10 +363,18 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().dr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                              _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
-                              _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
-                              _ptr(workspace), wbytes, _stream(stream)))
+    if _beta_v is None:
+        _check(lib().dr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
+                                  _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),
+                                  _ptr(workspace), wbytes, _stream(stream)))
+    else:
+        out["dbeta_v"] = torch.empty(bshape, **f32)
+        _check(lib().dr_chunk_bwd_kv(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                     _ptr(_beta_v), _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]),
+                                     _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]),
+                                     _ptr(out["dbeta_v"]), _ptr(out["dS0"]), _ptr(workspace), wbytes,
+                                     _stream(stream)))
     return out
 
 

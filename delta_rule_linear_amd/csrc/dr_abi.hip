@@ -373,10 +373,12 @@ dr_status check_bwd_desc(const dr_chunk_desc* d) {
     return DR_OK;
 }
 
+// beta_v and dbeta_v: the separate write strength and its gradient (channel
+// beta only), or NULL for one strength
 dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v, const float* log_alpha,
-                    const float* beta, const float* S0, const float* dO, const float* dS_final, float* dq,
-                    float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    const float* beta, const float* beta_v, const float* S0, const float* dO,
+                    const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha, float* dbeta,
+                    float* dbeta_v, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
     dr_status s = check_bwd_desc(d);
     if (s != DR_OK) return s;
     const size_t nseq = (size_t)d->B * d->H;
@@ -384,16 +386,18 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     if (tokens) {
         if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta)
             return fail(DR_ERR_NULL, "q, k, v, beta, dO, dq, dk, dv and dbeta are required");
+        if ((beta_v == nullptr) != (dbeta_v == nullptr))
+            return fail(DR_ERR_NULL, "beta_v and dbeta_v are required together");
         if ((d->gate == DR_GATE_NONE) != (log_alpha == nullptr))
             return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
         if ((d->gate == DR_GATE_NONE) != (dlog_alpha == nullptr))
             return fail(DR_ERR_NULL, "dlog_alpha must be NULL exactly when gate is DR_GATE_NONE");
     }
-    const void* ptrs[] = {q, k, v, log_alpha, beta, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0,
-                          workspace};
-    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "S0", "dO", "dS_final", "dq", "dk", "dv",
-                           "dlog_alpha", "dbeta", "dS0", "workspace"};
-    for (int i = 0; i < 15; ++i)
+    const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta,
+                          dbeta_v, dS0, workspace};
+    const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "S0", "dO", "dS_final", "dq", "dk", "dv",
+                           "dlog_alpha", "dbeta", "dbeta_v", "dS0", "workspace"};
+    for (int i = 0; i < 17; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     const BwdLayout w = bwd_layout(*d);
     if (w.total) {
@@ -449,7 +453,8 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         float* k32 = (float*)(ws + w.k32);
         float* v32 = (float*)(ws + w.v32);
         float* ones = (float*)(ws + w.ones);
-        e = dr::launch_bwd_cbeta_in(q, k, v, beta, f32in, nel, ntok, q32, k32, v32, ones, st);
+        e = dr::launch_bwd_cbeta_in(q, k, v, beta, beta_v ? beta_v : beta, f32in, nel, ntok, q32, k32, v32, ones,
+                                    st);
         if (e != hipSuccess) return fail(DR_ERR_HIP, "backward input scaling launch: %s", hipGetErrorString(e));
         a.q = q32; a.k = k32; a.v = v32;
         a.beta = ones;
@@ -459,7 +464,8 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     e = dr::launch_bwd(a, d->Dk, f32in, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
     if (cbeta) {
-        e = dr::launch_bwd_cbeta_out(k, v, beta, d->in_dtype == DR_F32, nel, dk, dv, dbeta, st);
+        e = dr::launch_bwd_cbeta_out(k, v, beta, beta_v ? beta_v : beta, d->in_dtype == DR_F32, nel, dk, dv, dbeta,
+                                     dbeta_v, st);
         if (e != hipSuccess) return fail(DR_ERR_HIP, "backward gradient mapping launch: %s", hipGetErrorString(e));
     }
     return DR_OK;
@@ -541,8 +547,21 @@ dr_status dr_chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, con
                        const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
                        float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = '\0';
-    return chunk_bwd(d, q, k, v, log_alpha, beta, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0,
-                     workspace, workspace_bytes, stream);
+    return chunk_bwd(d, q, k, v, log_alpha, beta, nullptr, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta, nullptr,
+                     dS0, workspace, workspace_bytes, stream);
+}
+
+dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta_k, const float* beta_v, const float* S0,
+                          const float* dO, const float* dS_final, float* dq, float* dk, float* dv,
+                          float* dlog_alpha, float* dbeta_k, float* dbeta_v, float* dS0, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
+    const size_t ntok = d ? (size_t)(d->B > 0 ? d->B : 0) * (d->H > 0 ? d->H : 0) * (d->L > 0 ? d->L : 0) : 0;
+    if (ntok && (!beta_v || !dbeta_v)) return fail(DR_ERR_NULL, "beta_v and dbeta_v are required");
+    return chunk_bwd(d, q, k, v, log_alpha, beta_k, beta_v, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta_k,
+                     dbeta_v, dS0, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

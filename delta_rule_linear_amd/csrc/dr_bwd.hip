@@ -1590,37 +1590,47 @@ hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
 
 // ============================================== channel-wise beta (FG2-GDN)
 // With a channel-wise beta, kt = sqrt(beta) (.) k and vt = sqrt(beta) (.) v
-// enter the recurrence as a key and a value of unit strength.  So the
-// backward runs the kernels above on (q, kt, vt) with beta = 1, then maps the
-// gradients of kt and vt back: dk = sqrt(beta) dkt, dv = sqrt(beta) dvt,
-// dbeta = (dkt k + dvt v) / (2 sqrt(beta)) per channel (beta > 0).
+// enter the recurrence as a key and a value of unit strength (with separate
+// strengths, FG2-GDN+: beta_k on k, beta_v on v).  So the backward runs the
+// kernels above on (q, kt, vt) with beta = 1, then maps the gradients of kt
+// and vt back: dk = sqrt(beta_k) dkt, dv = sqrt(beta_v) dvt,
+// dbeta_k = dkt k / (2 sqrt(beta_k)), dbeta_v = dvt v / (2 sqrt(beta_v)) per
+// channel (strengths > 0), summed for one strength.
 
-// q, kt, vt as fp32, and a unit strength per token
-__global__ void bwd_cbeta_in_kernel(const void* q, const void* k, const void* v, const float* beta, int f32in,
-                                    size_t n, size_t ntok, float* q32, float* k32, float* v32, float* ones) {
+// q, kt = sqrt(beta_k) k, vt = sqrt(beta_v) v as fp32, and a unit strength per
+// token (beta_v is beta_k itself for one strength)
+__global__ void bwd_cbeta_in_kernel(const void* q, const void* k, const void* v, const float* beta_k,
+                                    const float* beta_v, int f32in, size_t n, size_t ntok, float* q32, float* k32,
+                                    float* v32, float* ones) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const float sb = sqrtf(beta[i]);
         const float qv = f32in ? load1<true>(q, i) : load1<false>(q, i);
         const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
         const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
         q32[i] = qv;
-        k32[i] = sb * kv;
-        v32[i] = sb * vv;
+        k32[i] = sqrtf(beta_k[i]) * kv;
+        v32[i] = sqrtf(beta_v[i]) * vv;
         if (i < ntok) ones[i] = 1.f;
     }
 }
 
-// dk, dv hold the gradients of kt and vt on entry, those of k and v on exit
-__global__ void bwd_cbeta_out_kernel(const void* k, const void* v, const float* beta, int f32in, size_t n,
-                                     float* dk, float* dv, float* dbeta) {
+// dk, dv hold the gradients of kt and vt on entry, those of k and v on exit;
+// with dbeta_v NULL (one strength) both strength terms go to dbeta_k
+__global__ void bwd_cbeta_out_kernel(const void* k, const void* v, const float* beta_k, const float* beta_v,
+                                     int f32in, size_t n, float* dk, float* dv, float* dbeta_k, float* dbeta_v) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const float sb = sqrtf(beta[i]);
+        const float sk = sqrtf(beta_k[i]), sv = sqrtf(beta_v[i]);
         const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
         const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
         const float dkt = dk[i], dvt = dv[i];
-        dbeta[i] = (dkt * kv + dvt * vv) / (2.f * sb);
-        dk[i] = sb * dkt;
-        dv[i] = sb * dvt;
+        const float gk = dkt * kv / (2.f * sk), gv = dvt * vv / (2.f * sv);
+        if (dbeta_v) {
+            dbeta_k[i] = gk;
+            dbeta_v[i] = gv;
+        } else {
+            dbeta_k[i] = gk + gv;
+        }
+        dk[i] = sk * dkt;
+        dv[i] = sv * dvt;
     }
 }
 
@@ -1642,18 +1652,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta, bool f32in,
-                               size_t n, size_t ntok, float* q32, float* k32, float* v32, float* ones,
-                               hipStream_t st) {
-    hipLaunchKernelGGL(bwd_cbeta_in_kernel, dim3(2048), dim3(256), 0, st, q, k, v, beta, (int)f32in, n, ntok, q32,
-                       k32, v32, ones);
+hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta_k,
+                               const float* beta_v, bool f32in, size_t n, size_t ntok, float* q32, float* k32,
+                               float* v32, float* ones, hipStream_t st) {
+    hipLaunchKernelGGL(bwd_cbeta_in_kernel, dim3(2048), dim3(256), 0, st, q, k, v, beta_k, beta_v, (int)f32in, n,
+                       ntok, q32, k32, v32, ones);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta, bool f32in, size_t n, float* dk,
-                                float* dv, float* dbeta, hipStream_t st) {
-    hipLaunchKernelGGL(bwd_cbeta_out_kernel, dim3(2048), dim3(256), 0, st, k, v, beta, (int)f32in, n, dk, dv,
-                       dbeta);
+hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta_k, const float* beta_v, bool f32in,
+                                size_t n, float* dk, float* dv, float* dbeta_k, float* dbeta_v, hipStream_t st) {
+    hipLaunchKernelGGL(bwd_cbeta_out_kernel, dim3(2048), dim3(256), 0, st, k, v, beta_k, beta_v, (int)f32in, n, dk,
+                       dv, dbeta_k, dbeta_v);
     return hipGetLastError();
 }
 

@@ -152,14 +152,15 @@ hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
 // the backward (dr_bwd.hip)
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st);
-// channel-wise beta: q, sqrt(beta) k, sqrt(beta) v as fp32 and unit strengths
-// before the backward (n = tokens x Dk, ntok = tokens); the gradients of k,
-// v and beta from those of the scaled key and value after it
-hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta, bool f32in,
-                               size_t n, size_t ntok, float* q32, float* k32, float* v32, float* ones,
-                               hipStream_t st);
-hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta, bool f32in, size_t n, float* dk,
-                                float* dv, float* dbeta, hipStream_t st);
+// channel-wise beta: q, sqrt(beta_k) k, sqrt(beta_v) v as fp32 and unit
+// strengths before the backward (n = tokens x Dk, ntok = tokens); the
+// gradients of k, v and the strengths from those of the scaled key and value
+// after it (dbeta_v NULL: one strength, beta_v == beta_k)
+hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta_k,
+                               const float* beta_v, bool f32in, size_t n, size_t ntok, float* q32, float* k32,
+                               float* v32, float* ones, hipStream_t st);
+hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta_k, const float* beta_v, bool f32in,
+                                size_t n, float* dk, float* dv, float* dbeta_k, float* dbeta_v, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st);
 

@@ -297,6 +297,25 @@ dr_status dr_chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, con
                        float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dr_chunk_bwd_kv -- dr_chunk_bwd for dr_chunk_fwd_kv: gradients with separate
+ * channel-wise erase and write strengths (FG2-GDN page, section "Erweiterung:
+ * FG2-GDN+"; the same reading as the forward, kt = sqrt(beta_k) (.) k,
+ * vt = sqrt(beta_v) (.) v).
+ *
+ *   d->beta    must be DR_BETA_CHANNEL (else DR_ERR_UNSUPPORTED); so Dv == Dk
+ *   beta_k, beta_v    [B][H][L][Dk] fp32, > 0
+ *   dbeta_k, dbeta_v  [B][H][L][Dk] fp32, written
+ * Every other argument, the workspace (dr_chunk_bwd_workspace_bytes(d)) and the
+ * error behaviour are those of dr_chunk_bwd; beta_v == beta_k gives
+ * dr_chunk_bwd's gradients, with dbeta_k + dbeta_v its dbeta.
+ */
+dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                          const float* log_alpha, const float* beta_k, const float* beta_v, const float* S0,
+                          const float* dO, const float* dS_final, float* dq, float* dk, float* dv,
+                          float* dlog_alpha, float* dbeta_k, float* dbeta_v, float* dS0, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Per-kernel timing, for benchmarks and profiling (not part of the method).
  * Between dr_profile_begin and dr_profile_end every chunked-forward, backward
  * and decode call also records HIP events on its stream around each kernel it

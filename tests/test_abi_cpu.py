@@ -260,3 +260,18 @@ def test_backward_validation_and_workspace():
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel")) >= need + 3 * 2 * 3 * 100 * 128 * 4
     # no sequences: validated and done without touching memory
     assert lib.dr_chunk_bwd(ctypes.byref(_desc(B=0)), *([None] * 15), 0, None) == drl.DR_OK
+
+
+def test_backward_kv_validation():
+    lib = drl.lib()
+
+    def call(desc, bv=FAKE + 4096, dbv=FAKE + 8192):
+        return lib.dr_chunk_bwd_kv(ctypes.byref(desc) if desc is not None else None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   bv, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, dbv, None, FAKE, 1 << 40, None)
+
+    assert call(_desc()) == drl.DR_ERR_UNSUPPORTED                  # separate strengths are channel-wise
+    d = _desc(beta_mode="channel")
+    assert call(d, bv=None) == drl.DR_ERR_NULL
+    assert call(d, dbv=None) == drl.DR_ERR_NULL
+    assert call(d, bv=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
+    assert call(_desc(beta_mode="channel", B=0), bv=None, dbv=None) == drl.DR_OK

@@ -149,6 +149,56 @@ def test_backward_channel_gate_full_size_sampled_sequences():
     torch.cuda.empty_cache()
 
 
+def _check_kv(p, seed=0, tol=None):
+    import delta_rule_linear_amd as drl
+    announce("backward kv", p.name, p.B, p.H, p.L, p.Dk, p.Dv, p.in_dtype, p.gate)
+    dO, dSf = inputs.backward_cotangents(p, seed)
+    t = problem_to_dev(p)
+    g = drl.dr_chunk_bwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"], t["S0"],
+                            to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate)
+    torch.cuda.synchronize()
+    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode="channel",
+                          beta_v=p.beta_v)
+    tol = TOL[p.in_dtype] if tol is None else tol
+    errs = {n: rel_err(to_np(g[n]), ref[n]) for n in GRADS + ("dbeta_v",) if ref.get(n) is not None}
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"{p.name}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f" (tol {tol:.0e})"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("L", [1, 65, 200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_kv_sweep(dtype, gate, L, D):
+    # FG2-GDN+: separate channel-wise erase and write strengths
+    rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
+    p = inputs.make_chunk_problem(2, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode="channel", s0_var=0.01,
+                                  seed=L + D + 11, log_alpha_range=rng, beta_v=True, name=f"bwd_kv_{gate}_{dtype}")
+    _check_kv(p, seed=L + 2)
+
+
+def test_backward_kv_full_size_sampled_sequences():
+    import delta_rule_linear_amd as drl
+    p = inputs.workload("fg2plus_b2h16_16k")
+    announce("backward kv full size", p.name)
+    dO, dSf = inputs.backward_cotangents(p, 0)
+    t = problem_to_dev(p)
+    g = drl.dr_chunk_bwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"], t["S0"],
+                            to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate)
+    torch.cuda.synchronize()
+    for b, h in [(0, 5), (1, 9)]:
+        s = p.head(b, h)
+        ref = oracle.backward(s.q, s.k, s.v, s.log_alpha, s.beta, s.S0, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1],
+                              gate=s.gate, beta_mode="channel", beta_v=s.beta_v)
+        for n in GRADS + ("dbeta_v",):
+            if ref.get(n) is None:
+                continue
+            e = rel_err(to_np(g[n][b:b + 1, h:h + 1]), ref[n])
+            assert e <= TOL["bf16"], f"sequence ({b},{h}) {n}: {e:.2e}"
+    del g
+    torch.cuda.empty_cache()
+
+
 def test_backward_channel_beta_full_size_sampled_sequences():
     # the FG2-GDN shape (B=2, H=16, L=16384, d=128, bf16, channel gate and beta) in one call
     p = inputs.workload("fg2_b2h16_16k")
