@@ -1,5 +1,8 @@
-// dr_bwd.hip -- gradients of the chunked forward (scalar gate or none, scalar
-// beta), all in fp32 on the fp32 matrix cores.
+// dr_bwd.hip -- gradients of the chunked forward: the kernels for a scalar gate
+// (or none) first, then their channel-gate variants, then the passes that take
+// a channel-wise beta (or separate strengths) through the same kernels with
+// unit strength.  fp32 arithmetic on the matrix cores (state-sized products of
+// the per-chunk kernel as two fp16 terms).
 //
 // The pages print no backward; this is the reverse-mode derivative of the
 // chunk algebra of the forward (DeltaNet page, chunkwise form and its
@@ -18,7 +21,7 @@
 // and dq, dk, dbeta, dg follow from the products above; d log alpha is the
 // reverse cumulative sum of dg within the chunk.
 //
-// Four kernels:
+// Four kernels (per gate kind):
 //   prep   one workgroup per chunk: g, A's factor K K^T o E, P, T
 //   fscan  one per (sequence, 16 state columns): the start state of every
 //          chunk, R and U (sequential over chunks)

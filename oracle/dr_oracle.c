@@ -242,7 +242,8 @@ int dro_forward(int B, int H, int L, int Dk, int Dv,
 
 /*
  * dro_backward -- gradients of the forward above (one strength, no key scales,
- * inputs as given) by reverse-mode differentiation of the token recurrence.
+ * inputs as given; separate strengths in dro_backward_kv) by reverse-mode
+ * differentiation of the token recurrence.
  * The pages give no backward (the DeltaNet page, step 7, only says training
  * uses the chunkwise form); this is the chain rule applied to the update as
  * written, in the order of the forward's steps:
