@@ -21,6 +21,10 @@
 int dro_forward(int B, int H, int L, int Dk, int Dv, const double* q, const double* k, const double* v,
                 const double* log_alpha, int gate, const double* beta, int beta_mode, const double* S0,
                 double* o, double* S_final, int nthreads);
+int dro_backward(int B, int H, int L, int Dk, int Dv, const double* q, const double* k, const double* v,
+                 const double* log_alpha, int gate, const double* beta, int beta_mode, const double* S0,
+                 const double* dO, const double* dS_final, double* dq, double* dk, double* dv, double* dlog_alpha,
+                 double* dbeta, double* dS0, int nthreads);
 
 static int fails = 0;
 #define CHECK(cond, ...)                                  \
@@ -124,6 +128,49 @@ static int gpu_checks(void) {
     const double eo = max_rel(o, od, nq), es = max_rel(Sf, Sfd, ns);
     printf("chunk forward: o %.2e  S %.2e\n", eo, es);
     CHECK(eo <= 1e-4 && es <= 1e-4, "forward parity o %.2e S %.2e", eo, es);
+
+    /* the backward of the same forward, for seeded gradients of o and S_final */
+    {
+        float *gO = malloc(nq * 4), *gS = malloc(ns * 4);
+        double *gOd = malloc(nq * 8), *gSd = malloc(ns * 8);
+        for (size_t i = 0; i < nq; ++i) { gO[i] = (float)urand(&st); gOd[i] = gO[i]; }
+        for (size_t i = 0; i < ns; ++i) { gS[i] = (float)urand(&st); gSd[i] = gS[i]; }
+        const size_t wbb = dr_chunk_bwd_workspace_bytes(&d);
+        CHECK(wbb > 0, "backward workspace size");
+        void *dgO, *dgS, *dS0b, *gq, *gk, *gv, *gla, *gbe, *gS0, *dwb;
+        HIPOK(hipMalloc(&dgO, nq * 4)); HIPOK(hipMalloc(&dgS, ns * 4)); HIPOK(hipMalloc(&dS0b, ns * 4));
+        HIPOK(hipMalloc(&gq, nq * 4)); HIPOK(hipMalloc(&gk, nq * 4)); HIPOK(hipMalloc(&gv, nq * 4));
+        HIPOK(hipMalloc(&gla, ng * 4)); HIPOK(hipMalloc(&gbe, ng * 4)); HIPOK(hipMalloc(&gS0, ns * 4));
+        HIPOK(hipMalloc(&dwb, wbb));
+        HIPOK(hipMemcpy(dgO, gO, nq * 4, hipMemcpyHostToDevice));
+        HIPOK(hipMemcpy(dgS, gS, ns * 4, hipMemcpyHostToDevice));
+        HIPOK(hipMemcpy(dS0b, S0, ns * 4, hipMemcpyHostToDevice));
+        s = dr_chunk_bwd(&d, dq, dk, dv, dla, dbe, dS0b, dgO, dgS, gq, gk, gv, gla, gbe, gS0, dwb, wbb, NULL);
+        CHECK(s == DR_OK, "dr_chunk_bwd: %s (%s)", dr_status_str(s), dr_last_error());
+        HIPOK(hipDeviceSynchronize());
+        float* hg[6];
+        const size_t cnt[6] = {nq, nq, nq, ng, ng, ns};
+        void* dev[6] = {gq, gk, gv, gla, gbe, gS0};
+        double* ref[6];
+        for (int i = 0; i < 6; ++i) {
+            hg[i] = malloc(cnt[i] * 4);
+            ref[i] = malloc(cnt[i] * 8);
+            HIPOK(hipMemcpy(hg[i], dev[i], cnt[i] * 4, hipMemcpyDeviceToHost));
+        }
+        CHECK(dro_backward(B, H, L, D, D, qd, kd, vd, lad, 1, bed, 0, S0d, gOd, gSd, ref[0], ref[1], ref[2], ref[3],
+                           ref[4], ref[5], 1) == 0, "oracle backward");
+        double eb = 0.0;
+        for (int i = 0; i < 6; ++i) {
+            const double e = max_rel(hg[i], ref[i], cnt[i]);
+            if (e > eb) eb = e;
+        }
+        printf("chunk backward: max over dq, dk, dv, dlog_alpha, dbeta, dS0 %.2e\n", eb);
+        CHECK(eb <= 1e-4, "backward parity %.2e", eb);
+        for (int i = 0; i < 6; ++i) { free(hg[i]); free(ref[i]); }
+        HIPOK(hipFree(dgO)); HIPOK(hipFree(dgS)); HIPOK(hipFree(dS0b)); HIPOK(hipFree(gq)); HIPOK(hipFree(gk));
+        HIPOK(hipFree(gv)); HIPOK(hipFree(gla)); HIPOK(hipFree(gbe)); HIPOK(hipFree(gS0)); HIPOK(hipFree(dwb));
+        free(gO); free(gS); free(gOd); free(gSd);
+    }
 
     /* one decode step on the final states with the first token's inputs */
     dr_decode_desc dd = {B, H, D, D, DR_F32, DR_F32, DR_GATE_SCALAR, DR_BETA_SCALAR, 0};

@@ -24,7 +24,7 @@ def test_c_caller_host_checks():
 
 
 @pytest.mark.gpu
-def test_c_caller_forward_and_decode_on_gpu():
+def test_c_caller_forward_backward_and_decode_on_gpu():
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
