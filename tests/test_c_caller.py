@@ -29,7 +29,7 @@ def test_c_caller_forward_backward_and_decode_on_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     assert os.path.exists(build_c_caller.BIN), "build the C caller first (__graft_entry__.build())"
-    print("[gpu case] C caller forward + decode", file=sys.stderr, flush=True)
+    print("[gpu case] C caller forward + backward + decode", file=sys.stderr, flush=True)
     r = subprocess.run([build_c_caller.BIN, "gpu"], capture_output=True, text=True, timeout=120)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
