@@ -31,6 +31,41 @@ dr_status fail(dr_status s, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// A tensor argument as a byte range (p may be NULL: an absent tensor).
+struct Span {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+bool overlap(const Span& a, const Span& b) {
+    if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+    const char* x = (const char*)a.p;
+    const char* y = (const char*)b.p;
+    return x < y + b.bytes && y < x + a.bytes;
+}
+
+// Every output in `outs` must be disjoint from every input in `ins` and from
+// the other outputs, except that output alias_out may be input alias_in
+// exactly (the same address and size: the in-place state carry); any other
+// overlap is an error.
+dr_status check_disjoint(const Span* outs, int nout, const Span* ins, int nin, const void* alias_out = nullptr,
+                         const void* alias_in = nullptr) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j) {
+            if (!overlap(outs[i], ins[j])) continue;
+            if (alias_out && outs[i].p == alias_out && ins[j].p == alias_in && outs[i].p == ins[j].p &&
+                outs[i].bytes == ins[j].bytes)
+                continue;
+            return fail(DR_ERR_UNSUPPORTED, "%s overlaps %s", outs[i].name, ins[j].name);
+        }
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(DR_ERR_UNSUPPORTED, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+    return DR_OK;
+}
+
 bool valid_dtype(int x) { return x == DR_F32 || x == DR_BF16; }
 bool valid_gate(int x) { return x == DR_GATE_NONE || x == DR_GATE_SCALAR || x == DR_GATE_CHANNEL; }
 bool valid_beta(int x) { return x == DR_BETA_SCALAR || x == DR_BETA_CHANNEL; }
@@ -228,14 +263,27 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
                            "workspace"};
     for (int i = 0; i < 11; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    if (S_final && S0 && S_final != S0) {
-        const size_t bytes = nseq * d->Dk * d->Dv * sizeof(float);
-        const char* a0 = (const char*)S0;
-        const char* a1 = (const char*)S_final;
-        if (a0 < a1 + bytes && a1 < a0 + bytes)
-            return fail(DR_ERR_UNSUPPORTED, "S_final overlaps S0 without being the same array");
-    }
     const WsLayout w = ws_layout(*d, precond);
+    {
+        // o and S_final are disjoint from every input, the workspace and each
+        // other; S_final may be S0 itself (in-place state carry)
+        const size_t ntok = nseq * (size_t)d->L;
+        const size_t inb = d->in_dtype == DR_F32 ? 4 : 2, outb = d->out_dtype == DR_F32 ? 4 : 2;
+        const size_t gw = d->gate == DR_GATE_CHANNEL ? d->Dk : 1, bw = d->beta == DR_BETA_CHANNEL ? d->Dk : 1;
+        const size_t sb = nseq * d->Dk * d->Dv * sizeof(float);
+        const Span ins[] = {{q, ntok * d->Dk * inb, "q"},
+                            {k, ntok * d->Dk * inb, "k"},
+                            {v, ntok * d->Dv * inb, "v"},
+                            {log_alpha, ntok * gw * 4, "log_alpha"},
+                            {beta, ntok * bw * 4, "beta"},
+                            {beta_v, ntok * bw * 4, "beta_v"},
+                            {key_scale, ntok * d->Dk * 4, "key_scale"},
+                            {S0, sb, "S0"},
+                            {workspace, w.total, "workspace"}};
+        const Span outs[] = {{o, ntok * d->Dv * outb, "o"}, {S_final, sb, "S_final"}};
+        s = check_disjoint(outs, 2, ins, 9, S_final, S0);
+        if (s != DR_OK) return s;
+    }
     if (w.total) {
         if (!workspace) return fail(DR_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
         if (workspace_bytes < w.total)
@@ -301,6 +349,18 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
     const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "key_scale", "S", "o"};
     for (int i = 0; i < 9; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+    {
+        // o is disjoint from the states and the inputs; the states from the inputs
+        const size_t inb = d->in_dtype == DR_F32 ? 4 : 2, outb = d->out_dtype == DR_F32 ? 4 : 2;
+        const size_t gw = d->gate == DR_GATE_CHANNEL ? d->Dk : 1, bw = d->beta == DR_BETA_CHANNEL ? d->Dk : 1;
+        const Span ins[] = {{q, nst * d->Dk * inb, "q"},           {k, nst * d->Dk * inb, "k"},
+                            {v, nst * d->Dv * inb, "v"},           {log_alpha, nst * gw * 4, "log_alpha"},
+                            {beta, nst * bw * 4, "beta"},          {beta_v, nst * bw * 4, "beta_v"},
+                            {key_scale, nst * d->Dk * 4, "key_scale"}};
+        const Span outs[] = {{o, nst * d->Dv * outb, "o"}, {S, nst * d->Dk * d->Dv * sizeof(float), "S"}};
+        s = check_disjoint(outs, 2, ins, 7);
+        if (s != DR_OK) return s;
+    }
     dr::DecodeArgs a{};
     a.q = q; a.k = k; a.v = v;
     a.log_alpha = log_alpha; a.beta = beta; a.beta_v = beta_v;
@@ -400,6 +460,27 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     for (int i = 0; i < 17; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
     const BwdLayout w = bwd_layout(*d);
+    {
+        // the gradients are disjoint from every input, the workspace and each other
+        const size_t ntok = nseq * (size_t)d->L;
+        const size_t inb = d->in_dtype == DR_F32 ? 4 : 2;
+        const size_t gw = d->gate == DR_GATE_CHANNEL ? d->Dk : 1, bw = d->beta == DR_BETA_CHANNEL ? d->Dk : 1;
+        const size_t sb = nseq * d->Dk * d->Dv * sizeof(float);
+        const Span ins[] = {{q, ntok * d->Dk * inb, "q"},        {k, ntok * d->Dk * inb, "k"},
+                            {v, ntok * d->Dv * inb, "v"},        {log_alpha, ntok * gw * 4, "log_alpha"},
+                            {beta, ntok * bw * 4, "beta"},       {beta_v, ntok * bw * 4, "beta_v"},
+                            {S0, sb, "S0"},                      {dO, ntok * d->Dv * 4, "dO"},
+                            {dS_final, sb, "dS_final"},          {workspace, w.total, "workspace"}};
+        const Span outs[] = {{dq, ntok * d->Dk * 4, "dq"},
+                             {dk, ntok * d->Dk * 4, "dk"},
+                             {dv, ntok * d->Dv * 4, "dv"},
+                             {dlog_alpha, ntok * gw * 4, "dlog_alpha"},
+                             {dbeta, ntok * bw * 4, "dbeta"},
+                             {dbeta_v, ntok * bw * 4, "dbeta_v"},
+                             {dS0, sb, "dS0"}};
+        s = check_disjoint(outs, 7, ins, 10);
+        if (s != DR_OK) return s;
+    }
     if (w.total) {
         if (!workspace) return fail(DR_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
         if (workspace_bytes < w.total)

@@ -66,9 +66,25 @@
  *   with a channel-wise gate or beta, the gated operands and the state are
  *   single fp16 terms; fp32 inputs use a two-term fp16 split (about 22
  *   significant bits).  The chunk matrices T^ and P are stored in fp16 (two
- *   terms for fp32 inputs).  NaN/Inf inputs propagate and are not checked.  For a channel-wise gate, each chunk's cumulative
- *   log-gate must stay above -80 per channel (i.e. alpha products over 64
- *   tokens above e^-80); stronger decay underflows fp32 in the chunk algebra.
+ *   terms for fp32 inputs).  NaN/Inf inputs propagate and are not checked.
+ *   For a channel-wise gate, each chunk's cumulative log-gate must stay above
+ *   -80 per channel (i.e. alpha products over 64 tokens above e^-80);
+ *   stronger decay underflows fp32 in the chunk algebra.
+ * Magnitudes.  The operands derived from v and the state (R = V - gamma K S
+ *   and U with every mode; with a channel-wise gate or beta also the state and
+ *   the gated operands) are fp16 terms, finite up to 65504 and normal down to
+ *   2^-14.  With unit-norm keys the parity bounds (relative to each output's
+ *   largest entry: 3e-3 for bf16 inputs, 1e-4 for fp32) hold for v and S0
+ *   whose entries are N(0, 1)-like scaled by 2^e, e in [-12, 13] for bf16
+ *   inputs and [-8, 13] for fp32 inputs (largest |v| entries about 3.5e4).
+ *   Larger values overflow, and the outputs then hold Inf or NaN; smaller ones
+ *   lose precision to fp16 subnormals.  Neither is checked: callers scale v
+ *   and S0 by a power of two (the outputs scale with them exactly).
+ * Overlaps.  Outputs (o, S_final, the states of a decode step, gradients)
+ *   must not overlap any input, the workspace or each other; S_final may be
+ *   S0 itself.  Any other overlap is DR_ERR_UNSUPPORTED.
+ * Empty work.  B, H, N or L equal to 0 is valid: nothing is computed, and
+ *   with L == 0 S_final receives S0 (zeros if S0 is NULL).
  */
 #ifndef DELTARULE_H
 #define DELTARULE_H
@@ -84,7 +100,7 @@ extern "C" {
 typedef enum {
     DR_OK = 0,
     DR_ERR_NULL = 1,        /* a required pointer is NULL (or a forbidden one is not) */
-    DR_ERR_SHAPE = 2,       /* a dimension is negative */
+    DR_ERR_SHAPE = 2,       /* a dimension is negative (0 is valid: no work) */
     DR_ERR_UNSUPPORTED = 3, /* d_k / d_v / mode / dtype combination not provided */
     DR_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
     DR_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
@@ -155,7 +171,8 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_chunk_desc* d);
  *   workspace  device scratch of at least dr_chunk_fwd_workspace_bytes(d)
  *              bytes (may be NULL when that is 0); its contents on entry are
  *              ignored and on exit are unspecified
- * o must not overlap any input.  Returns DR_OK or an error status (see above).
+ * o must not overlap any input (DR_ERR_UNSUPPORTED).  Returns DR_OK or an error
+ * status (see above).
  */
 dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
                        const float* log_alpha, const float* beta, const float* S0, void* o,

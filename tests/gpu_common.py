@@ -27,6 +27,20 @@ def rel_err(x, y) -> float:
     return float(np.max(np.abs(x - y)) / scale)
 
 
+def per_head_errors(x, y):
+    """max|x - y| / max|y| of every (b, h) slice of [B, H, ...] arrays."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    B, H = y.shape[:2]
+    xe = x.reshape(B, H, -1)
+    ye = y.reshape(B, H, -1)
+    if ye.shape[2] == 0:
+        return np.zeros((B, H))
+    num = np.abs(xe - ye).max(axis=2)
+    den = np.abs(ye).max(axis=2)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
 def to_dev(a, dtype: str, device="cuda"):
     import torch
     if a is None:

@@ -16,6 +16,12 @@ FAKE = 0x7f0000000000            # 16-byte aligned, never dereferenced
 FAKE_MISALIGNED = FAKE + 8
 
 
+def F(i):
+    """The i-th fake tensor address: 16-byte aligned, 64 GiB apart, so that the
+    host's overlap checks see distinct arrays."""
+    return FAKE + (i << 36)
+
+
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -47,7 +53,7 @@ def _desc(**kw):
                           base["out_dtype"], base["gate"], base["beta_mode"], base["flags"])
 
 
-def _call(desc, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, o=FAKE, Sf=FAKE, ws=FAKE,
+def _call(desc, q=F(0), k=F(1), v=F(2), la=F(3), beta=F(4), S0=None, o=F(5), Sf=F(6), ws=F(7),
           wbytes=1 << 40):
     lib = drl.lib()
     return lib.dr_chunk_fwd(ctypes.byref(desc) if desc is not None else None, q, k, v, la, beta, S0,
@@ -128,7 +134,24 @@ def test_input_flags_validation():
 def test_chunk_rejects_partial_state_overlap():
     d = _desc()
     nbytes = 2 * 3 * 128 * 128 * 4
-    assert _call(d, S0=FAKE, Sf=FAKE + nbytes // 2) == drl.DR_ERR_UNSUPPORTED
+    assert _call(d, S0=F(9), Sf=F(9) + nbytes // 2) == drl.DR_ERR_UNSUPPORTED
+    # the same array exactly is the in-place state carry: validation goes on
+    assert _call(d, S0=F(9), Sf=F(9), ws=None) == drl.DR_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "la", "beta", "S0", "ws"])
+def test_chunk_rejects_output_overlapping_an_input(arg):
+    d = _desc()
+    kw = {arg: F(5) + 4096}          # inside o's 2*3*100*128*4 bytes
+    if arg == "S0":
+        kw["S0"] = F(5)
+    assert _call(d, **kw) == drl.DR_ERR_UNSUPPORTED
+    assert "o overlaps" in drl.dr_last_error()
+    # S_final overlapping an input other than S0
+    assert _call(d, Sf=F(1) + 256) == drl.DR_ERR_UNSUPPORTED
+    assert "S_final overlaps k" in drl.dr_last_error()
+    # o and S_final overlapping each other
+    assert _call(d, Sf=F(5) + 1024) == drl.DR_ERR_UNSUPPORTED
 
 
 def test_empty_work_needs_no_device():
@@ -137,7 +160,7 @@ def test_empty_work_needs_no_device():
                  ws=None, wbytes=0) == drl.DR_OK
 
 
-def _dcall(desc, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S=FAKE, o=FAKE):
+def _dcall(desc, q=F(0), k=F(1), v=F(2), la=F(3), beta=F(4), S=F(5), o=F(6)):
     return drl.lib().dr_decode_step(ctypes.byref(desc) if desc is not None else None, q, k, v, la,
                                     beta, S, o, None)
 
@@ -153,10 +176,15 @@ def test_decode_validation():
     assert _dcall(D(**ok), la=None) == drl.DR_ERR_NULL
     assert _dcall(D(**ok), o=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
     assert _dcall(D(**{**ok, "N": 0})) == drl.DR_OK
+    # o must not overlap the states or an input; the states must not overlap an input
+    assert _dcall(D(**ok), o=F(5) + 1024) == drl.DR_ERR_UNSUPPORTED
+    assert "o overlaps S" in drl.dr_last_error()
+    assert _dcall(D(**ok), o=F(0)) == drl.DR_ERR_UNSUPPORTED
+    assert _dcall(D(**ok), S=F(2) + 16) == drl.DR_ERR_UNSUPPORTED
 
 
-def _kvcall(desc, q=FAKE, k=FAKE, v=FAKE, la=FAKE, bk=FAKE, bv=FAKE + 4096, S0=None, o=FAKE, Sf=FAKE,
-            ws=FAKE, wbytes=1 << 40):
+def _kvcall(desc, q=F(0), k=F(1), v=F(2), la=F(3), bk=F(4), bv=F(8), S0=None, o=F(5), Sf=F(6),
+            ws=F(7), wbytes=1 << 40):
     return drl.lib().dr_chunk_fwd_kv(ctypes.byref(desc) if desc is not None else None, q, k, v, la, bk,
                                      bv, S0, o, Sf, ws, wbytes, None)
 
@@ -181,9 +209,9 @@ def test_decode_kv_validation():
     D = drl.DecodeDesc
     ok = dict(N=4, H=2, Dk=128, Dv=128, in_dtype=drl.DR_BF16, out_dtype=drl.DR_F32, gate=2, beta=1)
 
-    def call(desc, bk=FAKE, bv=FAKE + 4096, S=FAKE):
-        return drl.lib().dr_decode_step_kv(ctypes.byref(desc) if desc is not None else None, FAKE,
-                                           FAKE, FAKE, FAKE, bk, bv, S, FAKE, None)
+    def call(desc, bk=F(4), bv=F(8), S=F(5)):
+        return drl.lib().dr_decode_step_kv(ctypes.byref(desc) if desc is not None else None, F(0),
+                                           F(1), F(2), F(3), bk, bv, S, F(6), None)
 
     assert call(None) == drl.DR_ERR_NULL
     assert call(D(**{**ok, "beta": 0})) == drl.DR_ERR_UNSUPPORTED
@@ -202,9 +230,9 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 def test_precond_validation_and_workspace():
     lib = drl.lib()
 
-    def call(desc, ks=FAKE + 8192, ws=FAKE, wbytes=1 << 40):
-        return lib.dr_chunk_fwd_precond(ctypes.byref(desc) if desc is not None else None, FAKE, FAKE,
-                                        FAKE, FAKE, FAKE, ks, None, FAKE, FAKE, ws, wbytes, None)
+    def call(desc, ks=F(10), ws=F(7), wbytes=1 << 40):
+        return lib.dr_chunk_fwd_precond(ctypes.byref(desc) if desc is not None else None, F(0), F(1),
+                                        F(2), F(3), F(4), ks, None, F(5), F(6), ws, wbytes, None)
 
     d = _desc()
     assert call(None) == drl.DR_ERR_NULL
@@ -220,8 +248,8 @@ def test_precond_validation_and_workspace():
     assert drl.dr_chunk_fwd_precond_workspace_bytes(_desc(Dk=96)) == 0
     D = drl.DecodeDesc
     ok = dict(N=4, H=2, Dk=128, Dv=128, in_dtype=drl.DR_BF16, out_dtype=drl.DR_F32, gate=1, beta=0)
-    dcall = lambda desc, ks=FAKE + 8192: lib.dr_decode_step_precond(
-        ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, ks, FAKE, FAKE, None)
+    dcall = lambda desc, ks=F(10): lib.dr_decode_step_precond(
+        ctypes.byref(desc), F(0), F(1), F(2), F(3), F(4), ks, F(5), F(6), None)
     assert dcall(D(**ok), ks=None) == drl.DR_ERR_NULL
     assert dcall(D(**ok), ks=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
     assert dcall(D(**{**ok, "N": 0})) == drl.DR_OK
@@ -230,9 +258,10 @@ def test_precond_validation_and_workspace():
 def test_backward_validation_and_workspace():
     lib = drl.lib()
 
-    def call(desc, q=FAKE, la=FAKE, dO=FAKE, dq=FAKE, dla=FAKE, dS0=None, ws=FAKE, wbytes=1 << 40):
-        return lib.dr_chunk_bwd(ctypes.byref(desc) if desc is not None else None, q, FAKE, FAKE, la, FAKE,
-                                None, dO, None, dq, FAKE, FAKE, dla, FAKE, dS0, ws, wbytes, None)
+    def call(desc, q=F(0), la=F(3), dO=F(11), dq=F(12), dla=F(13), dS0=None, ws=F(7), wbytes=1 << 40,
+             dk=F(14)):
+        return lib.dr_chunk_bwd(ctypes.byref(desc) if desc is not None else None, q, F(1), F(2), la, F(4),
+                                None, dO, None, dq, dk, F(15), dla, F(16), dS0, ws, wbytes, None)
 
     d = _desc()
     assert call(None) == drl.DR_ERR_NULL
@@ -260,14 +289,20 @@ def test_backward_validation_and_workspace():
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel")) >= need + 3 * 2 * 3 * 100 * 128 * 4
     # no sequences: validated and done without touching memory
     assert lib.dr_chunk_bwd(ctypes.byref(_desc(B=0)), *([None] * 15), 0, None) == drl.DR_OK
+    # gradients must not overlap each other or an input
+    assert call(d, dk=F(12) + 1024) == drl.DR_ERR_UNSUPPORTED
+    assert "dq overlaps dk" in drl.dr_last_error()
+    assert call(d, dq=F(11)) == drl.DR_ERR_UNSUPPORTED
+    assert "dq overlaps dO" in drl.dr_last_error()
 
 
 def test_backward_kv_validation():
     lib = drl.lib()
 
-    def call(desc, bv=FAKE + 4096, dbv=FAKE + 8192):
-        return lib.dr_chunk_bwd_kv(ctypes.byref(desc) if desc is not None else None, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                   bv, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, dbv, None, FAKE, 1 << 40, None)
+    def call(desc, bv=F(8), dbv=F(17)):
+        return lib.dr_chunk_bwd_kv(ctypes.byref(desc) if desc is not None else None, F(0), F(1), F(2), F(3), F(4),
+                                   bv, None, F(11), None, F(12), F(14), F(15), F(13), F(16), dbv, None, F(7), 1 << 40,
+                                   None)
 
     assert call(_desc()) == drl.DR_ERR_UNSUPPORTED                  # separate strengths are channel-wise
     d = _desc(beta_mode="channel")

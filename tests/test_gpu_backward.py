@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from delta_rule_linear_amd import inputs
-from gpu_common import TOL, announce, problem_to_dev, rel_err, to_dev, to_np
+from gpu_common import TOL, announce, per_head_errors, problem_to_dev, rel_err, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,19 @@ def _check(p, seed=0, dS_final=True, tol=None):
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, f"{p.name}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f" (tol {tol:.0e})"
     return errs
+
+
+def _every_sequence(name, g, ref, names):
+    """Each (b, h) sequence of every gradient held to the bf16 bound on its own."""
+    worst = {}
+    for n in names:
+        if ref.get(n) is None:
+            continue
+        e = per_head_errors(to_np(g[n]), ref[n])
+        worst[n] = float(e.max())
+        bh = np.unravel_index(np.argmax(e), e.shape)
+        assert e.max() <= TOL["bf16"], f"{name} {n}: {e.max():.2e} at sequence {tuple(map(int, bh))}"
+    print(f"{name}: every sequence within bounds, worst " + ", ".join(f"{n} {v:.1e}" for n, v in worst.items()))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -132,20 +145,16 @@ def test_backward_no_tokens():
     assert np.array_equal(to_np(g["dS0"]), dSf.astype(np.float64))
 
 
-def test_backward_channel_gate_full_size_sampled_sequences():
+@pytest.mark.timeout(900)
+def test_backward_channel_gate_full_size_every_sequence():
     # the KDA shape (B=2, H=32, L=16384, d=128, bf16, channel gate) in one call
     p = inputs.workload("kda_b2h32_16k")
     announce("backward full size", p.name)
     dO, dSf = inputs.backward_cotangents(p, 0)
     g = run_bwd(p, dO, dSf)
-    for b, h in [(0, 0), (1, 31)]:
-        s = p.head(b, h)
-        ref = oracle_bwd(s, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1])
-        for n in GRADS:
-            x = to_np(g[n][b:b + 1, h:h + 1])
-            e = rel_err(x, ref[n])
-            assert e <= TOL["bf16"], f"sequence ({b},{h}) {n}: {e:.2e}"
-    del g
+    ref = oracle_bwd(p, dO, dSf)
+    _every_sequence(p.name, g, ref, GRADS)
+    del g, ref
     torch.cuda.empty_cache()
 
 
@@ -177,7 +186,8 @@ def test_backward_kv_sweep(dtype, gate, L, D):
     _check_kv(p, seed=L + 2)
 
 
-def test_backward_kv_full_size_sampled_sequences():
+@pytest.mark.timeout(900)
+def test_backward_kv_full_size_every_sequence():
     import delta_rule_linear_amd as drl
     p = inputs.workload("fg2plus_b2h16_16k")
     announce("backward kv full size", p.name)
@@ -186,47 +196,36 @@ def test_backward_kv_full_size_sampled_sequences():
     g = drl.dr_chunk_bwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"], t["S0"],
                             to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate)
     torch.cuda.synchronize()
-    for b, h in [(0, 5), (1, 9)]:
-        s = p.head(b, h)
-        ref = oracle.backward(s.q, s.k, s.v, s.log_alpha, s.beta, s.S0, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1],
-                              gate=s.gate, beta_mode="channel", beta_v=s.beta_v)
-        for n in GRADS + ("dbeta_v",):
-            if ref.get(n) is None:
-                continue
-            e = rel_err(to_np(g[n][b:b + 1, h:h + 1]), ref[n])
-            assert e <= TOL["bf16"], f"sequence ({b},{h}) {n}: {e:.2e}"
-    del g
+    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode="channel",
+                          beta_v=p.beta_v)
+    _every_sequence(p.name, g, ref, GRADS + ("dbeta_v",))
+    del g, ref
     torch.cuda.empty_cache()
 
 
-def test_backward_channel_beta_full_size_sampled_sequences():
+@pytest.mark.timeout(900)
+def test_backward_channel_beta_full_size_every_sequence():
     # the FG2-GDN shape (B=2, H=16, L=16384, d=128, bf16, channel gate and beta) in one call
     p = inputs.workload("fg2_b2h16_16k")
     announce("backward full size", p.name)
     dO, dSf = inputs.backward_cotangents(p, 0)
     g = run_bwd(p, dO, dSf)
-    for b, h in [(0, 3), (1, 12)]:
-        s = p.head(b, h)
-        ref = oracle_bwd(s, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1])
-        for n in GRADS:
-            x = to_np(g[n][b:b + 1, h:h + 1])
-            e = rel_err(x, ref[n])
-            assert e <= TOL["bf16"], f"sequence ({b},{h}) {n}: {e:.2e}"
-    del g
+    ref = oracle_bwd(p, dO, dSf)
+    _every_sequence(p.name, g, ref, GRADS)
+    del g, ref
     torch.cuda.empty_cache()
 
 
-def test_backward_full_size_sampled_sequences():
+@pytest.mark.timeout(900)
+def test_backward_full_size_every_sequence():
     # the benchmark's GDN shape (B=2, H=16, L=16384, d=128, bf16) in one call;
-    # two sequences checked whole against the oracle run on that sequence
+    # every sequence checked whole against the oracle
     p = inputs.workload("gdn_b2h16_16k")
     announce("backward full size", p.name)
     dO, dSf = inputs.backward_cotangents(p, 0)
     g = run_bwd(p, dO, dSf)
-    for b, h in [(0, 0), (1, 15)]:
-        s = p.head(b, h)
-        ref = oracle_bwd(s, dO[b:b + 1, h:h + 1], dSf[b:b + 1, h:h + 1])
-        for n in GRADS:
-            x = to_np(g[n][b:b + 1, h:h + 1])
-            e = rel_err(x, ref[n])
-            assert e <= TOL["bf16"], f"sequence ({b},{h}) {n}: {e:.2e}"
+    ref = oracle_bwd(p, dO, dSf)
+    _every_sequence(p.name, g, ref, GRADS)
+    del g, ref
+    torch.cuda.empty_cache()
+
