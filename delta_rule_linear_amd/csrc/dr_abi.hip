@@ -159,8 +159,11 @@ namespace dr {
 void prof_mark(hipStream_t st, int slot) {
     if (!g_prof_on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
+    // timing-only events: no system-scope fence on record, so the cache
+    // writeback and invalidation of a default event does not slow the kernels
+    // being timed
     hipEvent_t ev;
-    hipError_t e = hipEventCreate(&ev);
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
     if (e == hipSuccess) e = hipEventRecord(ev, st);
     if (e != hipSuccess) {
         if (g_prof_err == hipSuccess) g_prof_err = e;
