@@ -33,7 +33,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 6
+DR_ABI_VERSION = 7
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
@@ -43,7 +43,8 @@ EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "d
            "dr_decode_step_kv", "dr_chunk_fwd_precond_workspace_bytes", "dr_chunk_fwd_precond",
            "dr_decode_step_precond", "dr_status_str", "dr_last_error", "dr_abi_version",
            "dr_profile_begin", "dr_profile_end", "dr_chunk_bwd_workspace_bytes", "dr_chunk_bwd",
-           "dr_chunk_bwd_kv")
+           "dr_chunk_bwd_kv", "dr_chunk_fwd_noalloc")
+DR_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class DeltaRuleError(RuntimeError):
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.dr_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
         L.dr_chunk_fwd.restype = ctypes.c_int
+        L.dr_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.dr_chunk_fwd_noalloc.restype = ctypes.c_int
         L.dr_chunk_fwd_kv.argtypes = [ctypes.POINTER(ChunkDesc), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, ctypes.c_size_t, vp]
         L.dr_chunk_fwd_kv.restype = ctypes.c_int
@@ -255,8 +258,19 @@ def dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0=None, *, gate: str, o
                   want_state, workspace, stream, input_flags(qk_l2norm, beta_logit))
 
 
+def dr_chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str, o, S_final=None,
+                         stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
+    """dr_chunk_fwd without a workspace: the library's per-GPU scratch array
+    (DR_NOALLOC_SCRATCH_BYTES) takes its place, for callers that cannot
+    allocate.  o (and S_final, or None to skip it) are the caller's tensors;
+    nothing is allocated here or in the library.  Calls that overlap in time
+    on one GPU race on the scratch array.  Returns (o, S_final)."""
+    return _chunk(q, k, v, log_alpha, beta, None, S0, gate, beta_mode, o.dtype, o, S_final,
+                  False, None, stream, input_flags(qk_l2norm, beta_logit), noalloc=True)
+
+
 def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, S_final, want_state,
-           workspace, stream, flags, key_scale=None):
+           workspace, stream, flags, key_scale=None, noalloc=False):
     torch = _torch()
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
@@ -288,6 +302,10 @@ def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, 
         _need(S_final, "S_final", torch.float32, (B, H, Dk, Dv))
     desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), _dtype_code(out_dtype), gate, beta_mode,
                       flags)
+    if noalloc:
+        _check(lib().dr_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                          _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _stream(stream)))
+        return o, S_final
     nbytes = (dr_chunk_fwd_workspace_bytes(desc) if key_scale is None
               else dr_chunk_fwd_precond_workspace_bytes(desc))
     if workspace is None and nbytes:

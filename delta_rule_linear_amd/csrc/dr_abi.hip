@@ -16,6 +16,12 @@
 #include "deltarule.h"
 #include "dr_internal.h"
 
+// The allocation-free forward's workspace: one array per GPU, from the
+// library's first use on that GPU until the process ends.  In host code the
+// name stands for a host-side shadow, not the device address: the device
+// address comes from hipGetSymbolAddress, once per device (scratch_for_device).
+static __device__ __align__(256) unsigned char scratch[DR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -129,6 +135,29 @@ dr_status check_chunk_desc(const dr_chunk_desc* d) {
     const size_t nseq = (size_t)d->B * d->H;
     if (nseq > (size_t)std::numeric_limits<int>::max() / 256)
         return fail(DR_ERR_UNSUPPORTED, "B*H=%zu too large", nseq);
+    return DR_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the
+// first call per device, with that device current).
+dr_status scratch_for_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DR_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DR_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(DR_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return DR_OK;
 }
 
@@ -573,6 +602,25 @@ dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, con
     g_err[0] = '\0';
     return chunk_fwd(d, q, k, v, log_alpha, beta, beta, nullptr, false, S0, o, S_final, workspace,
                      workspace_bytes, stream);
+}
+
+dr_status dr_chunk_fwd_noalloc(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* S0, void* o,
+                               float* S_final, void* stream) {
+    g_err[0] = '\0';
+    dr_status s = check_chunk_desc(d);
+    if (s != DR_OK) return s;
+    const size_t need = ws_layout(*d).total;
+    if (need > DR_NOALLOC_SCRATCH_BYTES)
+        return fail(DR_ERR_WORKSPACE, "the call needs %zu bytes of workspace, the scratch array holds %zu", need,
+                    (size_t)DR_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need) {
+        s = scratch_for_device(&ws);
+        if (s != DR_OK) return s;
+    }
+    return chunk_fwd(d, q, k, v, log_alpha, beta, beta, nullptr, false, S0, o, S_final, ws,
+                     need ? (size_t)DR_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,

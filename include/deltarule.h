@@ -95,7 +95,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 6
+#define DR_ABI_VERSION 7
 
 typedef enum {
     DR_OK = 0,
@@ -177,6 +177,31 @@ size_t dr_chunk_fwd_workspace_bytes(const dr_chunk_desc* d);
 dr_status dr_chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
                        const float* log_alpha, const float* beta, const float* S0, void* o,
                        float* S_final, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the per-GPU device scratch array that dr_chunk_fwd_noalloc uses in
+ * place of a workspace (256 MiB: the workspace of B * H * L up to about
+ * 16 * 2^14 tokens with bf16 inputs, a scalar gate and a scalar beta). */
+#define DR_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/*
+ * dr_chunk_fwd_noalloc -- dr_chunk_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same computation, arguments and error behaviour as
+ * dr_chunk_fwd, without the workspace arguments: the library's own device
+ * scratch array of DR_NOALLOC_SCRATCH_BYTES serves as the workspace.  Each GPU
+ * the library runs on holds one such array from the library's first use on it
+ * until the process ends; the call allocates and frees nothing.
+ *   Limit: a call whose dr_chunk_fwd_workspace_bytes(d) exceeds
+ *   DR_NOALLOC_SCRATCH_BYTES returns DR_ERR_WORKSPACE (nothing launched).
+ *   Sharing: every call on one GPU uses that GPU's array, whose contents a
+ *   call neither needs on entry nor leaves defined; two calls on one GPU that
+ *   overlap in time (different streams or host threads without ordering
+ *   between them) race and give undefined results.  Calls ordered on one
+ *   stream are safe.
+ */
+dr_status dr_chunk_fwd_noalloc(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* S0, void* o,
+                               float* S_final, void* stream);
 
 /*
  * dr_chunk_fwd_kv -- dr_chunk_fwd with separate channel-wise erase and write

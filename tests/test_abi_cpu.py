@@ -310,3 +310,23 @@ def test_backward_kv_validation():
     assert call(d, dbv=None) == drl.DR_ERR_NULL
     assert call(d, bv=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
     assert call(_desc(beta_mode="channel", B=0), bv=None, dbv=None) == drl.DR_OK
+
+
+def test_noalloc_validation():
+    # host-side checks of the allocation-free forward: bad descriptors, and a
+    # call whose workspace exceeds the scratch array, return before any device work
+    lib = drl.lib()
+
+    def call(desc, q=F(0), o=F(5)):
+        return lib.dr_chunk_fwd_noalloc(ctypes.byref(desc) if desc is not None else None, q, F(1), F(2), F(3),
+                                        F(4), None, o, F(6), None)
+
+    assert call(None) == drl.DR_ERR_NULL
+    assert call(_desc(Dk=96)) == drl.DR_ERR_UNSUPPORTED
+    big = _desc(B=4, H=16, L=16384)
+    assert drl.dr_chunk_fwd_workspace_bytes(big) > drl.DR_NOALLOC_SCRATCH_BYTES
+    assert call(big) == drl.DR_ERR_WORKSPACE
+    assert "scratch array" in drl.dr_last_error()
+    hdr = open(HEADER).read()
+    assert re.search(r"#define DR_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", hdr)
+    assert drl.DR_NOALLOC_SCRATCH_BYTES == 256 << 20
