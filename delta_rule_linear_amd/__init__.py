@@ -33,7 +33,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 7
+DR_ABI_VERSION = 8
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
@@ -43,7 +43,8 @@ EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "d
            "dr_decode_step_kv", "dr_chunk_fwd_precond_workspace_bytes", "dr_chunk_fwd_precond",
            "dr_decode_step_precond", "dr_status_str", "dr_last_error", "dr_abi_version",
            "dr_profile_begin", "dr_profile_end", "dr_chunk_bwd_workspace_bytes", "dr_chunk_bwd",
-           "dr_chunk_bwd_kv", "dr_chunk_fwd_noalloc")
+           "dr_chunk_bwd_kv", "dr_chunk_fwd_noalloc", "dr_chunk_fwd_kv_workspace_bytes",
+           "dr_chunk_bwd_kv_workspace_bytes")
 DR_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
@@ -110,6 +111,10 @@ def lib() -> ctypes.CDLL:
         L.dr_decode_step_precond.restype = ctypes.c_int
         L.dr_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
         L.dr_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.dr_chunk_fwd_kv_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.dr_chunk_fwd_kv_workspace_bytes.restype = ctypes.c_size_t
+        L.dr_chunk_bwd_kv_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.dr_chunk_bwd_kv_workspace_bytes.restype = ctypes.c_size_t
         L.dr_chunk_bwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 15 + [ctypes.c_size_t, vp]
         L.dr_chunk_bwd.restype = ctypes.c_int
         L.dr_chunk_bwd_kv.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 17 + [ctypes.c_size_t, vp]
@@ -247,15 +252,24 @@ def dr_chunk_fwd_precond(q, k, v, log_alpha, beta, key_scale, S0=None, *, gate: 
                   want_state, workspace, stream, input_flags(qk_l2norm, beta_logit), key_scale)
 
 
-def dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0=None, *, gate: str, out_dtype=None,
-                    o=None, S_final=None, want_state: bool = True, workspace=None, stream=None,
+def dr_chunk_fwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0=None, *, gate: str, beta_mode: str = "channel",
+                    out_dtype=None, o=None, S_final=None, want_state: bool = True, workspace=None, stream=None,
                     qk_l2norm: bool = False, beta_logit: bool = False):
-    """dr_chunk_fwd with separate channel-wise erase (beta_k) and write
-    (beta_v) strengths, both [B,H,L,Dk] fp32; Dv == Dk."""
+    """dr_chunk_fwd with separate erase (beta_k) and write (beta_v)
+    strengths, both [B,H,L,Dk] (beta_mode "channel") or both [B,H,L]
+    (beta_mode "scalar") fp32; Dv == Dk."""
     if beta_v is None:
         raise ValueError("beta_v is required")
-    return _chunk(q, k, v, log_alpha, beta_k, beta_v, S0, gate, "channel", out_dtype, o, S_final,
+    return _chunk(q, k, v, log_alpha, beta_k, beta_v, S0, gate, beta_mode, out_dtype, o, S_final,
                   want_state, workspace, stream, input_flags(qk_l2norm, beta_logit))
+
+
+def dr_chunk_fwd_kv_workspace_bytes(desc: ChunkDesc) -> int:
+    return int(lib().dr_chunk_fwd_kv_workspace_bytes(ctypes.byref(desc)))
+
+
+def dr_chunk_bwd_kv_workspace_bytes(desc: ChunkDesc) -> int:
+    return int(lib().dr_chunk_bwd_kv_workspace_bytes(ctypes.byref(desc)))
 
 
 def dr_chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str, o, S_final=None,
@@ -306,8 +320,9 @@ def _chunk(q, k, v, log_alpha, beta, beta_v, S0, gate, beta_mode, out_dtype, o, 
         _check(lib().dr_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                                           _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_final), _stream(stream)))
         return o, S_final
-    nbytes = (dr_chunk_fwd_workspace_bytes(desc) if key_scale is None
-              else dr_chunk_fwd_precond_workspace_bytes(desc))
+    nbytes = (dr_chunk_fwd_precond_workspace_bytes(desc) if key_scale is not None
+              else dr_chunk_fwd_kv_workspace_bytes(desc) if beta_v is not None
+              else dr_chunk_fwd_workspace_bytes(desc))
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -331,13 +346,13 @@ def dr_chunk_bwd_workspace_bytes(desc: ChunkDesc) -> int:
 
 
 def dr_chunk_bwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0, dO, dS_final=None, *, gate: str,
-                    want_dS0: bool = True, workspace=None, stream=None):
-    """Gradients of dr_chunk_fwd_kv (separate channel-wise erase and write
-    strengths, both [B,H,L,Dk] fp32): as dr_chunk_bwd, with dbeta the erase
+                    beta_mode: str = "channel", want_dS0: bool = True, workspace=None, stream=None):
+    """Gradients of dr_chunk_fwd_kv (separate erase and write strengths, both
+    [B,H,L,Dk] or both [B,H,L] fp32): as dr_chunk_bwd, with dbeta the erase
     strength's gradient and dbeta_v the write strength's."""
     if beta_v is None:
         raise ValueError("beta_v is required")
-    return dr_chunk_bwd(q, k, v, log_alpha, beta_k, S0, dO, dS_final, gate=gate, beta_mode="channel",
+    return dr_chunk_bwd(q, k, v, log_alpha, beta_k, S0, dO, dS_final, gate=gate, beta_mode=beta_mode,
                         want_dS0=want_dS0, workspace=workspace, stream=stream, _beta_v=beta_v)
 
 
@@ -377,7 +392,7 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
            "dbeta": torch.empty(bshape, **f32),
            "dS0": torch.empty((B, H, Dk, Dv), **f32) if want_dS0 else None}
     desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, beta_mode)
-    nbytes = dr_chunk_bwd_workspace_bytes(desc)
+    nbytes = dr_chunk_bwd_workspace_bytes(desc) if _beta_v is None else dr_chunk_bwd_kv_workspace_bytes(desc)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -417,13 +432,14 @@ def dr_decode_step_precond(S, q, k, v, log_alpha, beta, key_scale, *, gate: str,
                    input_flags(qk_l2norm, beta_logit), key_scale)
 
 
-def dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, *, gate: str, out_dtype=None, o=None,
-                      stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
-    """dr_decode_step with separate channel-wise erase (beta_k) and write
-    (beta_v) strengths, both [N,H,Dk] fp32; Dv == Dk."""
+def dr_decode_step_kv(S, q, k, v, log_alpha, beta_k, beta_v, *, gate: str, beta_mode: str = "channel",
+                      out_dtype=None, o=None, stream=None, qk_l2norm: bool = False, beta_logit: bool = False):
+    """dr_decode_step with separate erase (beta_k) and write (beta_v)
+    strengths, both [N,H,Dk] (beta_mode "channel", Dv == Dk) or both [N,H]
+    (beta_mode "scalar") fp32."""
     if beta_v is None:
         raise ValueError("beta_v is required")
-    return _decode(S, q, k, v, log_alpha, beta_k, beta_v, gate, "channel", out_dtype, o, stream,
+    return _decode(S, q, k, v, log_alpha, beta_k, beta_v, gate, beta_mode, out_dtype, o, stream,
                    input_flags(qk_l2norm, beta_logit))
 
 

@@ -99,13 +99,14 @@ struct WsLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// precond: write-side key scales, which run on the channel-gate path
-WsLayout ws_layout(const dr_chunk_desc& d, bool precond = false) {
+// precond: write-side key scales, which run on the channel-gate path;
+// kvtok: separate scalar strengths, which run on the channel-beta path
+WsLayout ws_layout(const dr_chunk_desc& d, bool precond = false, bool kvtok = false) {
     WsLayout w{};
     const size_t P = d.in_dtype == DR_F32 ? 2 : 1;
     const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
     const size_t NCH = (size_t)d.B * d.H * NC;
-    const bool cg = d.gate == DR_GATE_CHANNEL || precond, cb = d.beta == DR_BETA_CHANNEL;
+    const bool cg = d.gate == DR_GATE_CHANNEL || precond, cb = d.beta == DR_BETA_CHANNEL || kvtok;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -275,12 +276,17 @@ namespace {
 
 // The chunked forward; beta_v is the write strength on v (beta itself for
 // dr_chunk_fwd, a separate channel-wise array for dr_chunk_fwd_kv).
+// kvtok: separate strengths of one value per token (beta and beta_v [B][H][L]),
+// run on the channel-beta kernels with every channel sharing its token's value
 dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
                     const float* log_alpha, const float* beta, const float* beta_v, const float* key_scale,
                     bool precond, const float* S0, void* o, float* S_final, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, void* stream, bool kvtok = false) {
     dr_status s = check_chunk_desc(d);
     if (s != DR_OK) return s;
+    if (kvtok && d->Dv != d->Dk)
+        return fail(DR_ERR_UNSUPPORTED, "separate scalar strengths run on the channel-beta kernels: needs Dv == Dk "
+                                        "(%d != %d)", d->Dv, d->Dk);
     const size_t nseq = (size_t)d->B * d->H;
     const bool tokens = nseq > 0 && d->L > 0;
     if (tokens) {
@@ -295,7 +301,7 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
                            "workspace"};
     for (int i = 0; i < 11; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const WsLayout w = ws_layout(*d, precond);
+    const WsLayout w = ws_layout(*d, precond, kvtok);
     {
         // o and S_final are disjoint from every input, the workspace and each
         // other; S_final may be S0 itself (in-place state carry)
@@ -346,6 +352,7 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.beta_logit = (d->input_flags & DR_IN_BETA_LOGIT) != 0;
     a.gate_mode = d->gate;
     a.key_scale = precond ? key_scale : nullptr;
+    a.beta_tok = kvtok;
     char* ws = (char*)workspace;
     a.wsT = (dr::half_t*)(ws + w.T);
     a.wsP = (dr::half_t*)(ws + w.Pm);
@@ -355,7 +362,7 @@ dr_status chunk_fwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.wsKl = w.Kl ? (dr::half_t*)(ws + w.Kl) : nullptr;
     a.wsV = w.V ? (dr::half_t*)(ws + w.V) : nullptr;
     hipError_t e = dr::launch_chunk(a, d->Dk, d->in_dtype == DR_F32, d->gate == DR_GATE_CHANNEL || precond,
-                                    d->beta == DR_BETA_CHANNEL, beta_v != beta, st);
+                                    d->beta == DR_BETA_CHANNEL || kvtok, beta_v != beta, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "chunk kernels launch: %s", hipGetErrorString(e));
     return DR_OK;
 }
@@ -414,7 +421,8 @@ struct BwdLayout {
     size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, ones, db1, total;
 };
 
-BwdLayout bwd_layout(const dr_chunk_desc& d) {
+// kvtok: separate scalar strengths, which take the channel-beta route
+BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
     BwdLayout w{};
     const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
     const size_t NCH = (size_t)d.B * d.H * NC;
@@ -441,7 +449,7 @@ BwdLayout bwd_layout(const dr_chunk_desc& d) {
         w.Kc = take(NCH * dr::CH * d.Dk * f);
         w.Kt = take(NCH * dr::CH * d.Dk * f);
     }
-    if (d.beta == DR_BETA_CHANNEL) {
+    if (d.beta == DR_BETA_CHANNEL || kvtok) {
         // q, sqrt(beta) k, sqrt(beta) v in fp32, unit strengths and their (unused) gradient
         const size_t ntok = (size_t)d.B * d.H * d.L;
         w.q32 = take(ntok * d.Dk * f);
@@ -465,14 +473,18 @@ dr_status check_bwd_desc(const dr_chunk_desc* d) {
     return DR_OK;
 }
 
-// beta_v and dbeta_v: the separate write strength and its gradient (channel
-// beta only), or NULL for one strength
+// beta_v and dbeta_v: the separate write strength and its gradient, or NULL
+// for one strength; kvtok: the two strengths hold one value per token
 dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v, const float* log_alpha,
                     const float* beta, const float* beta_v, const float* S0, const float* dO,
                     const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha, float* dbeta,
-                    float* dbeta_v, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+                    float* dbeta_v, float* dS0, void* workspace, size_t workspace_bytes, void* stream,
+                    bool kvtok = false) {
     dr_status s = check_bwd_desc(d);
     if (s != DR_OK) return s;
+    if (kvtok && d->Dv != d->Dk)
+        return fail(DR_ERR_UNSUPPORTED, "separate scalar strengths take the channel-beta route: needs Dv == Dk "
+                                        "(%d != %d)", d->Dv, d->Dk);
     const size_t nseq = (size_t)d->B * d->H;
     const bool tokens = nseq > 0 && d->L > 0;
     if (tokens) {
@@ -491,7 +503,7 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
                            "dlog_alpha", "dbeta", "dbeta_v", "dS0", "workspace"};
     for (int i = 0; i < 17; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const BwdLayout w = bwd_layout(*d);
+    const BwdLayout w = bwd_layout(*d, kvtok);
     {
         // the gradients are disjoint from every input, the workspace and each other
         const size_t ntok = nseq * (size_t)d->L;
@@ -557,7 +569,7 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         a.wKt = (float*)(ws + w.Kt);
     }
     bool f32in = d->in_dtype == DR_F32;
-    const bool cbeta = d->beta == DR_BETA_CHANNEL;
+    const bool cbeta = d->beta == DR_BETA_CHANNEL || kvtok;
     const size_t ntok = nseq * d->L, nel = ntok * d->Dk;   // Dv == Dk with a channel beta
     hipError_t e = hipSuccess;
     if (cbeta) {
@@ -566,8 +578,8 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         float* k32 = (float*)(ws + w.k32);
         float* v32 = (float*)(ws + w.v32);
         float* ones = (float*)(ws + w.ones);
-        e = dr::launch_bwd_cbeta_in(q, k, v, beta, beta_v ? beta_v : beta, f32in, nel, ntok, q32, k32, v32, ones,
-                                    st);
+        e = dr::launch_bwd_cbeta_in(q, k, v, beta, beta_v ? beta_v : beta, f32in, kvtok, d->Dk, nel, ntok, q32,
+                                    k32, v32, ones, st);
         if (e != hipSuccess) return fail(DR_ERR_HIP, "backward input scaling launch: %s", hipGetErrorString(e));
         a.q = q32; a.k = k32; a.v = v32;
         a.beta = ones;
@@ -577,20 +589,14 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     e = dr::launch_bwd(a, d->Dk, f32in, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
     if (cbeta) {
-        e = dr::launch_bwd_cbeta_out(k, v, beta, beta_v ? beta_v : beta, d->in_dtype == DR_F32, nel, dk, dv, dbeta,
-                                     dbeta_v, st);
+        e = dr::launch_bwd_cbeta_out(k, v, beta, beta_v ? beta_v : beta, d->in_dtype == DR_F32, kvtok, d->Dk, nel,
+                                     dk, dv, dbeta, dbeta_v, st);
         if (e != hipSuccess) return fail(DR_ERR_HIP, "backward gradient mapping launch: %s", hipGetErrorString(e));
     }
     return DR_OK;
 }
 
-// The separate-strength entry points take channel-wise strengths only.
-dr_status check_kv_mode(int beta_mode) {
-    if (beta_mode != DR_BETA_CHANNEL)
-        return fail(DR_ERR_UNSUPPORTED, "separate erase and write strengths are channel-wise: "
-                                        "beta mode must be DR_BETA_CHANNEL");
-    return DR_OK;
-}
+
 
 }  // namespace
 
@@ -628,9 +634,17 @@ dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
                           const float* S0, void* o, float* S_final, void* workspace,
                           size_t workspace_bytes, void* stream) {
     g_err[0] = '\0';
-    if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
+    // scalar strengths: one value per token each, on the channel-beta kernels
+    const bool kvtok = d && d->beta == DR_BETA_SCALAR;
     return chunk_fwd(d, q, k, v, log_alpha, beta_k, beta_v, nullptr, false, S0, o, S_final, workspace,
-                     workspace_bytes, stream);
+                     workspace_bytes, stream, kvtok);
+}
+
+size_t dr_chunk_fwd_kv_workspace_bytes(const dr_chunk_desc* d) {
+    if (check_chunk_desc(d) != DR_OK) return 0;
+    const bool kvtok = d->beta == DR_BETA_SCALAR;
+    if (kvtok && d->Dv != d->Dk) return 0;
+    return ws_layout(*d, false, kvtok).total;
 }
 
 size_t dr_chunk_fwd_precond_workspace_bytes(const dr_chunk_desc* d) {
@@ -665,7 +679,6 @@ dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* 
                             const float* log_alpha, const float* beta_k, const float* beta_v,
                             float* S, void* o, void* stream) {
     g_err[0] = '\0';
-    if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
     return decode_step(d, q, k, v, log_alpha, beta_k, beta_v, nullptr, false, S, o, stream);
 }
 
@@ -689,11 +702,17 @@ dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
                           float* dlog_alpha, float* dbeta_k, float* dbeta_v, float* dS0, void* workspace,
                           size_t workspace_bytes, void* stream) {
     g_err[0] = '\0';
-    if (d && check_kv_mode(d->beta) != DR_OK) return DR_ERR_UNSUPPORTED;
     const size_t ntok = d ? (size_t)(d->B > 0 ? d->B : 0) * (d->H > 0 ? d->H : 0) * (d->L > 0 ? d->L : 0) : 0;
     if (ntok && (!beta_v || !dbeta_v)) return fail(DR_ERR_NULL, "beta_v and dbeta_v are required");
     return chunk_bwd(d, q, k, v, log_alpha, beta_k, beta_v, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta_k,
-                     dbeta_v, dS0, workspace, workspace_bytes, stream);
+                     dbeta_v, dS0, workspace, workspace_bytes, stream, d && d->beta == DR_BETA_SCALAR);
+}
+
+size_t dr_chunk_bwd_kv_workspace_bytes(const dr_chunk_desc* d) {
+    if (check_bwd_desc(d) != DR_OK) return 0;
+    const bool kvtok = d->beta == DR_BETA_SCALAR;
+    if (kvtok && d->Dv != d->Dk) return 0;
+    return bwd_layout(*d, kvtok).total;
 }
 
 }  // extern "C"

@@ -1602,17 +1602,55 @@ hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
 
 // q, kt = sqrt(beta_k) k, vt = sqrt(beta_v) v as fp32, and a unit strength per
 // token (beta_v is beta_k itself for one strength)
+// per_token: the strengths hold one value per token (element i belongs to
+// token i / dk), shared by every channel
 __global__ void bwd_cbeta_in_kernel(const void* q, const void* k, const void* v, const float* beta_k,
-                                    const float* beta_v, int f32in, size_t n, size_t ntok, float* q32, float* k32,
-                                    float* v32, float* ones) {
+                                    const float* beta_v, int f32in, int per_token, int dk, size_t n, size_t ntok,
+                                    float* q32, float* k32, float* v32, float* ones) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
         const float qv = f32in ? load1<true>(q, i) : load1<false>(q, i);
         const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
         const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
+        const size_t bi = per_token ? i / dk : i;
         q32[i] = qv;
-        k32[i] = sqrtf(beta_k[i]) * kv;
-        v32[i] = sqrtf(beta_v[i]) * vv;
+        k32[i] = sqrtf(beta_k[bi]) * kv;
+        v32[i] = sqrtf(beta_v[bi]) * vv;
         if (i < ntok) ones[i] = 1.f;
+    }
+}
+
+// Separate strengths of one value per token: dk, dv as in bwd_cbeta_out_kernel,
+// and each strength's gradient summed over the token's channels,
+//   dbeta^k_t = sum_c dkt_{t,c} k_{t,c} / (2 sqrt(beta^k_t)), dbeta^v_t likewise.
+// One wave per token (dk channels, dk / 64 per lane).
+__global__ void bwd_cbeta_out_tok_kernel(const void* k, const void* v, const float* beta_k, const float* beta_v,
+                                         int f32in, int dk, size_t ntok, float* dkg, float* dvg, float* dbeta_k,
+                                         float* dbeta_v) {
+    const int l = threadIdx.x & 63;
+    const size_t wv = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const size_t nw = ((size_t)gridDim.x * blockDim.x) >> 6;
+    for (size_t t = wv; t < ntok; t += nw) {
+        const float sk = sqrtf(beta_k[t]), sv = sqrtf(beta_v[t]);
+        float gk = 0.f, gv = 0.f;
+        for (int c = l; c < dk; c += 64) {
+            const size_t i = t * dk + c;
+            const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
+            const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
+            const float dkt = dkg[i], dvt = dvg[i];
+            gk += dkt * kv;
+            gv += dvt * vv;
+            dkg[i] = sk * dkt;
+            dvg[i] = sv * dvt;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            gk += __shfl_xor(gk, off);
+            gv += __shfl_xor(gv, off);
+        }
+        if (l == 0) {
+            dbeta_k[t] = gk / (2.f * sk);
+            dbeta_v[t] = gv / (2.f * sv);
+        }
     }
 }
 
@@ -1656,17 +1694,22 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta_k,
-                               const float* beta_v, bool f32in, size_t n, size_t ntok, float* q32, float* k32,
-                               float* v32, float* ones, hipStream_t st) {
-    hipLaunchKernelGGL(bwd_cbeta_in_kernel, dim3(2048), dim3(256), 0, st, q, k, v, beta_k, beta_v, (int)f32in, n,
-                       ntok, q32, k32, v32, ones);
+                               const float* beta_v, bool f32in, bool per_token, int dk, size_t n, size_t ntok,
+                               float* q32, float* k32, float* v32, float* ones, hipStream_t st) {
+    hipLaunchKernelGGL(bwd_cbeta_in_kernel, dim3(2048), dim3(256), 0, st, q, k, v, beta_k, beta_v, (int)f32in,
+                       (int)per_token, dk, n, ntok, q32, k32, v32, ones);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta_k, const float* beta_v, bool f32in,
-                                size_t n, float* dk, float* dv, float* dbeta_k, float* dbeta_v, hipStream_t st) {
-    hipLaunchKernelGGL(bwd_cbeta_out_kernel, dim3(2048), dim3(256), 0, st, k, v, beta_k, beta_v, (int)f32in, n, dk,
-                       dv, dbeta_k, dbeta_v);
+                                bool per_token, int dk, size_t n, float* dk_, float* dv, float* dbeta_k,
+                                float* dbeta_v, hipStream_t st) {
+    if (per_token)
+        hipLaunchKernelGGL(bwd_cbeta_out_tok_kernel, dim3(2048), dim3(256), 0, st, k, v, beta_k, beta_v, (int)f32in,
+                           dk, n / dk, dk_, dv, dbeta_k, dbeta_v);
+    else
+        hipLaunchKernelGGL(bwd_cbeta_out_kernel, dim3(2048), dim3(256), 0, st, k, v, beta_k, beta_v, (int)f32in, n,
+                           dk_, dv, dbeta_k, dbeta_v);
     return hipGetLastError();
 }
 

@@ -162,7 +162,7 @@ __device__ __forceinline__ void cg_fetch(const ChunkArgs& a, CgIn<DK, F32IN, CBE
         }
         if constexpr (P1) in.q[u] = ld_rawn<F32IN, CPT>(a.q, row * DK + ch0);
         if constexpr (CBETA && P2) {
-            load_f32_n<CPT>(a.beta + row * DK + ch0, in.be[u]);
+            load_strength_n<CPT>(a.beta, a.beta_tok, row, DK, ch0, in.be[u]);
             if constexpr (!SEPV) in.v[u] = ld_rawn<F32IN, CPT>(a.v, row * a.Dv + ch0);
         }
     }
@@ -272,8 +272,8 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
             for (int e = tid; e < CH * DK; e += 256) {
                 const int r = e / DK, col = e % DK;
                 const int rc = r < Lc ? r : 0;
-                const float sbv = sqrtf(strength(a.beta[(tok0 + rc) * DK + col], blg));
-                const float sbw = sqrtf(strength(a.beta_v[(tok0 + rc) * DK + col], blg));
+                const float sbv = sqrtf(strength(strength_at(a.beta, a.beta_tok, tok0 + rc, DK, col), blg));
+                const float sbw = sqrtf(strength(strength_at(a.beta_v, a.beta_tok, tok0 + rc, DK, col), blg));
                 float kv = sbv * load1<F32IN>(a.k, (tok0 + rc) * DK + col);
                 float vv = sbw * load1<F32IN>(a.v, (tok0 + rc) * Dv + col);
                 float qv = load1<F32IN>(a.q, (tok0 + rc) * DK + col);
@@ -314,7 +314,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const size_t row = tok0 + (4 * tg + u < Lc ? 4 * tg + u : 0);
-                load_f32_n<CPT>(a.beta_v + row * DK + ch0, bwv[u]);
+                load_strength_n<CPT>(a.beta_v, a.beta_tok, row, DK, ch0, bwv[u]);
                 vin[u] = ld_rawn<F32IN, CPT>(a.v, row * Dv + ch0);
             }
         }
@@ -511,7 +511,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                 cvt_raw8<F32IN>(ld_raw8<F32IN>(a.q, (tok0 + rac) * DK + k0), ra < Lc, xq);
                 if constexpr (CBETA) {
                     float ba[8];
-                    load_f32_n<8>(a.beta + (tok0 + rac) * DK + k0, ba);
+                    load_strength_n<8>(a.beta, a.beta_tok, tok0 + rac, DK, k0, ba);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) xk[j] *= sqrtf(strength(ba[j], blg));
                 }
@@ -536,7 +536,7 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                         cvt_raw8<F32IN>(ld_raw8<F32IN>(a.k, (tok0 + cac) * DK + k0), ca < Lc, xb);
                         if constexpr (CBETA) {
                             float bb[8];
-                            load_f32_n<8>(a.beta + (tok0 + cac) * DK + k0, bb);
+                            load_strength_n<8>(a.beta, a.beta_tok, tok0 + cac, DK, k0, bb);
 #pragma unroll
                             for (int j = 0; j < 8; ++j) xb[j] *= sqrtf(strength(bb[j], blg));
                         }
@@ -656,8 +656,8 @@ __device__ __forceinline__ void prep_chunk(const ChunkArgs& a, float* smem, cons
                         ssi += ki * ki;
                         ssq += qr * qr;
                         if constexpr (CBETA) {
-                            kr *= sqrtf(strength(a.beta[(tok0 + r) * DK + col], blg));
-                            ki *= sqrtf(strength(a.beta[(tok0 + i) * DK + col], blg));
+                            kr *= sqrtf(strength(strength_at(a.beta, a.beta_tok, tok0 + r, DK, col), blg));
+                            ki *= sqrtf(strength(strength_at(a.beta, a.beta_tok, tok0 + i, DK, col), blg));
                         }
                         if constexpr (KS) ki *= a.key_scale[(tok0 + i) * DK + col];   // write side
                         accA += kr * ki * dec;

@@ -363,6 +363,24 @@ __device__ __forceinline__ void load_f32_n(const float* p, float* x) {
     }
 }
 
+// Strengths (beta or beta_v) of row `row`, channels ch0 .. ch0 + N - 1: one
+// value per channel ([rows][dk]), or, with per_token, one value per token
+// ([rows]) that every channel shares.
+template <int N>
+__device__ __forceinline__ void load_strength_n(const float* base, bool per_token, size_t row, int dk, int ch0,
+                                                float* x) {
+    if (per_token) {
+        const float b = base[row];
+#pragma unroll
+        for (int j = 0; j < N; ++j) x[j] = b;
+    } else {
+        load_f32_n<N>(base + row * dk + ch0, x);
+    }
+}
+__device__ __forceinline__ float strength_at(const float* base, bool per_token, size_t row, int dk, int col) {
+    return per_token ? base[row] : base[row * dk + col];
+}
+
 // Store sixteen fp32 values as P fp16 terms at base[idx .. idx + 16) of each
 // plane (16-byte aligned).
 template <int P>

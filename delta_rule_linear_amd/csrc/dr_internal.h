@@ -65,6 +65,9 @@ struct ChunkArgs {
     int beta_logit;
     int gate_mode;              // 0 none, 1 scalar, 2 channel
     const float* key_scale;     // write-side key scales [B][H][L][Dk], or null
+    // beta and beta_v hold one value per token ([B][H][L]) that every channel
+    // shares, on the channel-beta kernels (separate scalar strengths)
+    int beta_tok;
     half_t* wsT;
     half_t* wsP;
     float* wsG;
@@ -155,12 +158,15 @@ hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st);
 // channel-wise beta: q, sqrt(beta_k) k, sqrt(beta_v) v as fp32 and unit
 // strengths before the backward (n = tokens x Dk, ntok = tokens); the
 // gradients of k, v and the strengths from those of the scaled key and value
-// after it (dbeta_v NULL: one strength, beta_v == beta_k)
+// after it (dbeta_v NULL: one strength, beta_v == beta_k).  per_token: the
+// strengths hold one value per token (separate scalar strengths; dbeta_v
+// required), shared by the token's dk channels.
 hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta_k,
-                               const float* beta_v, bool f32in, size_t n, size_t ntok, float* q32, float* k32,
-                               float* v32, float* ones, hipStream_t st);
+                               const float* beta_v, bool f32in, bool per_token, int dk, size_t n, size_t ntok,
+                               float* q32, float* k32, float* v32, float* ones, hipStream_t st);
 hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta_k, const float* beta_v, bool f32in,
-                                size_t n, float* dk, float* dv, float* dbeta_k, float* dbeta_v, hipStream_t st);
+                                bool per_token, int dk, size_t n, float* dk_, float* dv, float* dbeta_k,
+                                float* dbeta_v, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st);
 

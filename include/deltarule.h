@@ -14,9 +14,11 @@
  *   Gated DeltaNet  scalar alpha_t                   (FG2-GDN page, section 1)
  *   KDA             alpha_t a d_k-vector             (FG2-GDN page, section 1)
  *   FG2-GDN         beta_t a d_k-vector, as sqrt on both k and v (section 2)
- *   FG2-GDN+        separate d_k-vectors: the erase strength beta^k on k and
+ *   FG2-GDN+        separate strengths: the erase strength beta^k on k and
  *                   the write strength beta^v on v (section "Erweiterung:
- *                   FG2-GDN+"), through the *_kv entry points:
+ *                   FG2-GDN+"; d_k-vectors, or one scalar each per token,
+ *                   which the page's ablation also decouples), through the
+ *                   *_kv entry points:
  *                     kt_t = sqrt(beta^k_t) (.) k_t,  vt_t = sqrt(beta^v_t) (.) v_t
  *                   and the same S_t and o_t.  The page gives no formula; this
  *                   is the reading that reduces to FG2-GDN at beta^v == beta^k.
@@ -95,7 +97,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 7
+#define DR_ABI_VERSION 8
 
 typedef enum {
     DR_OK = 0,
@@ -203,17 +205,26 @@ dr_status dr_chunk_fwd_noalloc(const dr_chunk_desc* d, const void* q, const void
                                const float* log_alpha, const float* beta, const float* S0, void* o,
                                float* S_final, void* stream);
 
+/* Bytes of device workspace dr_chunk_fwd_kv needs for `d` (0 if d is invalid
+ * for it or there is no work): dr_chunk_fwd_workspace_bytes(d) with a channel
+ * beta; with scalar strengths also the channel-beta operand planes. */
+size_t dr_chunk_fwd_kv_workspace_bytes(const dr_chunk_desc* d);
+
 /*
- * dr_chunk_fwd_kv -- dr_chunk_fwd with separate channel-wise erase and write
- * strengths (FG2-GDN page, section "Erweiterung: FG2-GDN+"): beta_k takes the
- * place of beta on kt in both the erase and the write term, beta_v scales v.
+ * dr_chunk_fwd_kv -- dr_chunk_fwd with separate erase and write strengths
+ * (FG2-GDN page, section "Erweiterung: FG2-GDN+"; its ablation study decouples
+ * them as vectors and as scalars): beta_k takes the place of beta on kt in both
+ * the erase and the write term, beta_v scales v.
  *
- *   d->beta    must be DR_BETA_CHANNEL (else DR_ERR_UNSUPPORTED); so Dv == Dk
- *   beta_k     [B][H][L][Dk] fp32, expected in [0, 1] (not checked)
- *   beta_v     [B][H][L][Dk] fp32, expected in [0, 1] (not checked)
- * Every other argument, the workspace (dr_chunk_fwd_workspace_bytes(d)) and
- * the error behaviour are those of dr_chunk_fwd; beta_v == beta_k gives
- * dr_chunk_fwd's result.
+ *   d->beta    DR_BETA_CHANNEL: d_k-vectors; DR_BETA_SCALAR: one value per
+ *              token each.  Either way Dv == Dk (else DR_ERR_UNSUPPORTED):
+ *              scalar strengths run on the channel-beta kernels, every
+ *              channel taking its token's value.
+ *   beta_k     [B][H][L][Dk] or [B][H][L] fp32, expected in [0, 1] (not checked)
+ *   beta_v     beta_k's shape, fp32, expected in [0, 1] (not checked)
+ *   workspace  at least dr_chunk_fwd_kv_workspace_bytes(d) bytes
+ * Every other argument and the error behaviour are those of dr_chunk_fwd;
+ * beta_v == beta_k gives dr_chunk_fwd's result up to rounding.
  */
 dr_status dr_chunk_fwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta_k, const float* beta_v,
@@ -261,14 +272,14 @@ dr_status dr_decode_step(const dr_decode_desc* d, const void* q, const void* k, 
                          void* stream);
 
 /*
- * dr_decode_step_kv -- dr_decode_step with separate channel-wise erase and
- * write strengths (FG2-GDN page, section "Erweiterung: FG2-GDN+"):
+ * dr_decode_step_kv -- dr_decode_step with separate erase and write strengths
+ * (FG2-GDN page, section "Erweiterung: FG2-GDN+"):
  *
  *   S[n][h] <- (I - kt kt^T) Diag(alpha) S[n][h] + kt vt^T,
  *   kt = sqrt(beta_k) (.) k,  vt = sqrt(beta_v) (.) v
  *
- *   d->beta    must be DR_BETA_CHANNEL (else DR_ERR_UNSUPPORTED)
- *   beta_k, beta_v  [N][H][Dk] fp32
+ *   beta_k, beta_v  [N][H][Dk] (DR_BETA_CHANNEL, needs Dv == Dk) or [N][H]
+ *                   (DR_BETA_SCALAR) fp32
  * Every other argument as for dr_decode_step.  Equivalent to dr_chunk_fwd_kv
  * with L == 1, S0 == S_final == S.
  */
@@ -338,18 +349,25 @@ dr_status dr_chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, con
                        const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
                        float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace dr_chunk_bwd_kv needs for `d` (0 if d is invalid
+ * for it or there is no work). */
+size_t dr_chunk_bwd_kv_workspace_bytes(const dr_chunk_desc* d);
+
 /*
  * dr_chunk_bwd_kv -- dr_chunk_bwd for dr_chunk_fwd_kv: gradients with separate
- * channel-wise erase and write strengths (FG2-GDN page, section "Erweiterung:
- * FG2-GDN+"; the same reading as the forward, kt = sqrt(beta_k) (.) k,
+ * erase and write strengths (FG2-GDN page, section "Erweiterung: FG2-GDN+";
+ * the same reading as the forward, kt = sqrt(beta_k) (.) k,
  * vt = sqrt(beta_v) (.) v).
  *
- *   d->beta    must be DR_BETA_CHANNEL (else DR_ERR_UNSUPPORTED); so Dv == Dk
- *   beta_k, beta_v    [B][H][L][Dk] fp32, > 0
- *   dbeta_k, dbeta_v  [B][H][L][Dk] fp32, written
- * Every other argument, the workspace (dr_chunk_bwd_workspace_bytes(d)) and the
- * error behaviour are those of dr_chunk_bwd; beta_v == beta_k gives
- * dr_chunk_bwd's gradients, with dbeta_k + dbeta_v its dbeta.
+ *   d->beta    DR_BETA_CHANNEL or DR_BETA_SCALAR as for dr_chunk_fwd_kv;
+ *              Dv == Dk either way
+ *   beta_k, beta_v    [B][H][L][Dk] or [B][H][L] fp32, > 0
+ *   dbeta_k, dbeta_v  beta_k's shape, fp32, written (with scalar strengths the
+ *                     sum over the token's channels)
+ *   workspace  at least dr_chunk_bwd_kv_workspace_bytes(d) bytes
+ * Every other argument and the error behaviour are those of dr_chunk_bwd;
+ * beta_v == beta_k gives dr_chunk_bwd's gradients, with dbeta_k + dbeta_v its
+ * dbeta.
  */
 dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
                           const float* log_alpha, const float* beta_k, const float* beta_v, const float* S0,

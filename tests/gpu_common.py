@@ -75,7 +75,7 @@ def run_hip(p, out_dtype=None, **kw):
                                         **kw)
     if "beta_v" in t:
         return drl.dr_chunk_fwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"],
-                                   t["S0"], gate=p.gate, out_dtype=out_dtype, **kw)
+                                   t["S0"], gate=p.gate, beta_mode=p.beta_mode, out_dtype=out_dtype, **kw)
     return drl.dr_chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"],
                             gate=p.gate, beta_mode=p.beta_mode, out_dtype=out_dtype, **kw)
 

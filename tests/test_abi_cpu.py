@@ -192,9 +192,17 @@ def _kvcall(desc, q=F(0), k=F(1), v=F(2), la=F(3), bk=F(4), bv=F(8), S0=None, o=
 def test_chunk_kv_validation():
     ch = dict(gate="channel", beta_mode="channel")
     assert _kvcall(None) == drl.DR_ERR_NULL
-    # separate strengths are channel-wise only
-    assert _kvcall(_desc(gate="channel")) == drl.DR_ERR_UNSUPPORTED
-    assert "DR_BETA_CHANNEL" in drl.dr_last_error()
+    # scalar separate strengths run on the channel-beta kernels: Dv == Dk
+    assert _kvcall(_desc(gate="channel"), ws=None) == drl.DR_ERR_WORKSPACE
+    assert _kvcall(_desc(gate="channel", Dv=64)) == drl.DR_ERR_UNSUPPORTED
+    assert "Dv == Dk" in drl.dr_last_error()
+    sc = _desc(gate="scalar")
+    need_kv = drl.dr_chunk_fwd_kv_workspace_bytes(sc)
+    assert need_kv == drl.dr_chunk_fwd_workspace_bytes(_desc(gate="scalar", beta_mode="channel"))
+    assert need_kv > drl.dr_chunk_fwd_workspace_bytes(sc)
+    assert _kvcall(sc, wbytes=need_kv - 1) == drl.DR_ERR_WORKSPACE
+    assert drl.dr_chunk_fwd_kv_workspace_bytes(_desc(Dv=64)) == 0
+    assert drl.dr_chunk_fwd_kv_workspace_bytes(_desc(**ch)) == drl.dr_chunk_fwd_workspace_bytes(_desc(**ch))
     assert _kvcall(_desc(**ch), bv=None) == drl.DR_ERR_NULL
     assert _kvcall(_desc(**ch), bk=None) == drl.DR_ERR_NULL
     assert _kvcall(_desc(**ch), bv=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
@@ -214,7 +222,7 @@ def test_decode_kv_validation():
                                            F(1), F(2), F(3), bk, bv, S, F(6), None)
 
     assert call(None) == drl.DR_ERR_NULL
-    assert call(D(**{**ok, "beta": 0})) == drl.DR_ERR_UNSUPPORTED
+    assert call(D(**{**ok, "beta": 0, "N": 0})) == drl.DR_OK        # scalar strengths are accepted
     assert call(D(**ok), bv=None) == drl.DR_ERR_NULL
     assert call(D(**ok), bv=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
     assert call(D(**{**ok, "N": 0})) == drl.DR_OK
@@ -304,7 +312,10 @@ def test_backward_kv_validation():
                                    bv, None, F(11), None, F(12), F(14), F(15), F(13), F(16), dbv, None, F(7), 1 << 40,
                                    None)
 
-    assert call(_desc()) == drl.DR_ERR_UNSUPPORTED                  # separate strengths are channel-wise
+    assert call(_desc(Dv=64)) == drl.DR_ERR_UNSUPPORTED            # scalar strengths: Dv == Dk
+    assert drl.dr_chunk_bwd_kv_workspace_bytes(_desc()) == \
+        drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel"))
+    assert drl.dr_chunk_bwd_kv_workspace_bytes(_desc(Dv=64)) == 0
     d = _desc(beta_mode="channel")
     assert call(d, bv=None) == drl.DR_ERR_NULL
     assert call(d, dbv=None) == drl.DR_ERR_NULL

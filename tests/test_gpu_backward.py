@@ -160,13 +160,13 @@ def test_backward_channel_gate_full_size_every_sequence():
 
 def _check_kv(p, seed=0, tol=None):
     import delta_rule_linear_amd as drl
-    announce("backward kv", p.name, p.B, p.H, p.L, p.Dk, p.Dv, p.in_dtype, p.gate)
+    announce("backward kv", p.name, p.B, p.H, p.L, p.Dk, p.Dv, p.in_dtype, p.gate, p.beta_mode)
     dO, dSf = inputs.backward_cotangents(p, seed)
     t = problem_to_dev(p)
     g = drl.dr_chunk_bwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"], t["S0"],
-                            to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate)
+                            to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode)
     torch.cuda.synchronize()
-    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode="channel",
+    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode=p.beta_mode,
                           beta_v=p.beta_v)
     tol = TOL[p.in_dtype] if tol is None else tol
     errs = {n: rel_err(to_np(g[n]), ref[n]) for n in GRADS + ("dbeta_v",) if ref.get(n) is not None}
@@ -174,15 +174,18 @@ def _check_kv(p, seed=0, tol=None):
     assert not bad, f"{p.name}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f" (tol {tol:.0e})"
 
 
+@pytest.mark.parametrize("beta_mode", ["channel", "scalar"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 @pytest.mark.parametrize("L", [1, 65, 200])
 @pytest.mark.parametrize("D", [64, 128])
-def test_backward_kv_sweep(dtype, gate, L, D):
-    # FG2-GDN+: separate channel-wise erase and write strengths
+def test_backward_kv_sweep(dtype, gate, L, D, beta_mode):
+    # FG2-GDN+: separate erase and write strengths, d_k-vectors or one scalar
+    # each per token
     rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
-    p = inputs.make_chunk_problem(2, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode="channel", s0_var=0.01,
-                                  seed=L + D + 11, log_alpha_range=rng, beta_v=True, name=f"bwd_kv_{gate}_{dtype}")
+    p = inputs.make_chunk_problem(2, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode=beta_mode, s0_var=0.01,
+                                  seed=L + D + 11, log_alpha_range=rng, beta_v=True,
+                                  name=f"bwd_kv_{beta_mode}_{gate}_{dtype}")
     _check_kv(p, seed=L + 2)
 
 

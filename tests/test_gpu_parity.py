@@ -138,16 +138,46 @@ def test_value_and_state_magnitude_range(dtype, gate, beta_mode):
 
 # ------------------------------------- separate erase and write strengths
 
+@pytest.mark.parametrize("beta_mode", ["channel", "scalar"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 @pytest.mark.parametrize("L", [1, 65, 200])
 @pytest.mark.parametrize("D", [64, 128])
-def test_kv_small_sweep(dtype, gate, L, D):
+def test_kv_small_sweep(dtype, gate, L, D, beta_mode):
+    # separate erase and write strengths, d_k-vectors or one scalar each per token
     rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
-    p = inputs.make_chunk_problem(1, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode="channel",
+    p = inputs.make_chunk_problem(1, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
                                   log_alpha_range=rng, s0_var=0.01, seed=L + D + 1, beta_v=True,
-                                  name=f"kv-{dtype}-{gate}-L{L}-D{D}")
+                                  name=f"kv-{beta_mode}-{dtype}-{gate}-L{L}-D{D}")
     _check(p, tol=1e-5 if dtype == "f32" else None)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_kv_scalar_strengths_uneven_jobs_and_input_prep(gate):
+    # scalar separate strengths on the persistent channel-gate loop with a
+    # ragged tail, and with raw q, k and strength logits
+    for raw in (False, True):
+        p = inputs.make_chunk_problem(1, 5, 64 * 60 + 17, 128, 128, gate=gate, beta_mode="scalar",
+                                      log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=23, beta_v=True,
+                                      raw_inputs=raw, name=f"kv-scalar-loop-{gate}-raw{int(raw)}")
+        _check(p)
+
+
+def test_kv_scalar_equal_strengths_match_single_strength():
+    # beta_v == beta_k (scalar) through the separate-strength entry point (the
+    # channel-beta kernels) agrees with dr_chunk_fwd (the scalar-beta kernels)
+    import delta_rule_linear_amd as drl
+    from gpu_common import problem_to_dev
+    for gate in ("scalar", "channel"):
+        p = inputs.make_chunk_problem(1, 3, 300, 128, 128, gate=gate, beta_mode="scalar",
+                                      log_alpha_range=(-0.2, -0.0005), s0_var=0.01, seed=24)
+        announce("kv scalar equal strengths", gate)
+        t = problem_to_dev(p)
+        o1, S1 = drl.dr_chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"], gate=gate,
+                                  beta_mode="scalar")
+        o2, S2 = drl.dr_chunk_fwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta"].clone(),
+                                     t["S0"], gate=gate, beta_mode="scalar")
+        assert rel_err(to_np(o2), to_np(o1)) <= 2e-3 and rel_err(to_np(S2), to_np(S1)) <= 2e-3
 
 
 def test_kv_channel_prep_loop_uneven_jobs():
@@ -397,25 +427,27 @@ def test_decode_full_batch_512_steps():
     assert step_err.max() <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("beta_mode", ["channel", "scalar"])
 @pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_decode_kv_steps(gate, dtype):
+def test_decode_kv_steps(gate, dtype, beta_mode):
     import delta_rule_linear_amd as drl
     import oracle
     from gpu_common import to_dev
     rng = (-0.2, -0.0005) if gate == "channel" else (-0.1, -0.001)
-    dp = inputs.make_decode_problem(5, 3, 128, 128, 4, in_dtype=dtype, gate=gate, beta_mode="channel",
+    dv = 128 if beta_mode == "channel" else 48   # scalar strengths allow Dv != Dk
+    dp = inputs.make_decode_problem(5, 3, 128, dv, 4, in_dtype=dtype, gate=gate, beta_mode=beta_mode,
                                     log_alpha_range=rng, seed=12, beta_v=True)
-    announce("decode kv", gate, dtype)
+    announce("decode kv", gate, dtype, beta_mode)
     S = to_dev(dp.S, "f32")
     Sy = dp.S.astype(np.float64)
     for t in range(dp.steps):
         la = None if dp.log_alpha is None else dp.log_alpha[t]
         o = drl.dr_decode_step_kv(S, to_dev(dp.q[t], dtype), to_dev(dp.k[t], dtype),
                                   to_dev(dp.v[t], dtype), to_dev(la, "f32"), to_dev(dp.beta[t], "f32"),
-                                  to_dev(dp.beta_v[t], "f32"), gate=gate)
+                                  to_dev(dp.beta_v[t], "f32"), gate=gate, beta_mode=beta_mode)
         oy, Sy = oracle.decode_step(Sy, dp.q[t], dp.k[t], dp.v[t], la, dp.beta[t], gate=gate,
-                                    beta_mode="channel", beta_v=dp.beta_v[t])
+                                    beta_mode=beta_mode, beta_v=dp.beta_v[t])
         assert rel_err(to_np(o), oy) <= 1e-5, f"step {t} o"
     assert rel_err(to_np(S), Sy) <= 1e-5
 
