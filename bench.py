@@ -226,18 +226,12 @@ def main():
     tflops = alg_flops / (ms * 1e-3) / 1e12
     fwd_bytes = fwd_bytes_per_token_head(D, L) * token_heads
     # per-kernel durations: a separate pass of the same steps with the
-    # library's per-kernel events on, one profiling window per step (after the
-    # cache rewrite); the median over the steps
-    scan_l, prep_l = [], []
-    for _ in range(max(args.steps, 20)):
-        flush()
-        drl.dr_profile_begin()
-        step()
-        pr = drl.dr_profile_end()
-        scan_l.append(pr["scan_ms"])
-        prep_l.append(pr["prep_ms"])
-    scan_ms = float(np.median(scan_l))
-    prep_ms = float(np.median(prep_l))
+    # library's per-kernel timing on (each kernel's dispatch timestamps)
+    drl.dr_profile_begin()
+    time_steps(step, args.steps, 0)
+    prof = drl.dr_profile_end()
+    scan_ms = prof["scan_ms"] / max(1, prof["chunk_calls"])
+    prep_ms = prof["prep_ms"] / max(1, prof["chunk_calls"])
     # the dominant kernel against HBM: the forward's algorithmic bytes (inputs
     # read once, outputs written once) over the scan kernel's duration
     scan_gbs = fwd_bytes / (scan_ms * 1e-3) / 1e9

@@ -170,7 +170,7 @@ __global__ void copy_state_kernel(float* dst, const float* src, size_t n) {
 
 // ---------------------------------------------------------------- profiling
 struct ProfRec {
-    hipEvent_t ev;
+    hipEvent_t start, stop;
     int slot;
 };
 std::mutex g_prof_mu;
@@ -179,27 +179,35 @@ std::vector<ProfRec> g_prof;
 hipError_t g_prof_err = hipSuccess;
 
 void prof_clear() {
-    for (auto& r : g_prof) hipEventDestroy(r.ev);
+    for (auto& r : g_prof) {
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
     g_prof.clear();
 }
 
 }  // namespace
 
 namespace dr {
-void prof_mark(hipStream_t st, int slot) {
-    if (!g_prof_on.load(std::memory_order_relaxed)) return;
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    // timing-only events: no system-scope fence on record, so the cache
-    // writeback and invalidation of a default event does not slow the kernels
-    // being timed
-    hipEvent_t ev;
-    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
-    if (e == hipSuccess) e = hipEventRecord(ev, st);
-    if (e != hipSuccess) {
-        if (g_prof_err == hipSuccess) g_prof_err = e;
-        return;
+bool prof_events(hipEvent_t* start, hipEvent_t* stop) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return false;
+    hipError_t e = hipEventCreate(start);
+    if (e == hipSuccess) {
+        e = hipEventCreate(stop);
+        if (e != hipSuccess) hipEventDestroy(*start);
     }
-    g_prof.push_back({ev, slot});
+    if (e != hipSuccess) {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (g_prof_err == hipSuccess) g_prof_err = e;
+        *start = *stop = nullptr;
+        return false;
+    }
+    return true;
+}
+
+void prof_record(hipEvent_t start, hipEvent_t stop, int slot) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({start, stop, slot});
 }
 }  // namespace dr
 
@@ -230,10 +238,9 @@ dr_status dr_profile_end(dr_profile_report* report) {
         if (slot == dr::kProfPrep) ++report->chunk_calls;
         if (slot == dr::kProfDecode) ++report->decode_calls;
         if (slot == dr::kProfBwdPrep) ++report->bwd_calls;
-        if (slot == dr::kProfEnd || i + 1 == g_prof.size()) continue;
-        e = hipEventSynchronize(g_prof[i + 1].ev);
+        e = hipEventSynchronize(g_prof[i].stop);
         float t = 0.f;
-        if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof[i].ev, g_prof[i + 1].ev);
+        if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof[i].start, g_prof[i].stop);
         if (e == hipSuccess) ms[slot] += t;
     }
     prof_clear();

@@ -1579,16 +1579,12 @@ template <int DK, bool F32IN>
 hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
     const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
     const unsigned nscan = (unsigned)((a.nseq + 7) / 8) * 8u * (unsigned)(a.Dv / 16);
-    prof_mark(st, kProfBwdPrep);
-    hipLaunchKernelGGL((bwd_prep_cg_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
-    prof_mark(st, kProfBwdFscan);
-    hipLaunchKernelGGL((bwd_fscan_cg_kernel<DK, F32IN>), dim3(nscan), dim3(SNT), 0, st, a);
-    prof_mark(st, kProfBwdRscan);
-    hipLaunchKernelGGL((bwd_rscan_cg_kernel<DK>), dim3(nscan), dim3(SNT), 0, st, a);
-    prof_mark(st, kProfBwdPost);
-    hipLaunchKernelGGL((bwd_post_cg_kernel<DK, F32IN>), dim3(nch), dim3(PNT), 0, st, a);
-    prof_mark(st, kProfEnd);
-    return hipGetLastError();
+    hipError_t e = launch_k(kProfBwdPrep, bwd_prep_cg_kernel<DK, F32IN>, dim3(nch), dim3(NTH), 0, st, a);
+    if (e == hipSuccess)
+        e = launch_k(kProfBwdFscan, bwd_fscan_cg_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
+    if (e == hipSuccess) e = launch_k(kProfBwdRscan, bwd_rscan_cg_kernel<DK>, dim3(nscan), dim3(SNT), 0, st, a);
+    if (e == hipSuccess) e = launch_k(kProfBwdPost, bwd_post_cg_kernel<DK, F32IN>, dim3(nch), dim3(PNT), 0, st, a);
+    return e;
 }
 
 // ============================================== channel-wise beta (FG2-GDN)
@@ -1679,16 +1675,11 @@ template <int DK, bool F32IN>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
     const unsigned nscan = (unsigned)((a.nseq + 7) / 8) * 8u * (unsigned)(a.Dv / 16);
-    prof_mark(st, kProfBwdPrep);
-    hipLaunchKernelGGL((bwd_prep_kernel<DK, F32IN>), dim3(nch), dim3(NTH), 0, st, a);
-    prof_mark(st, kProfBwdFscan);
-    hipLaunchKernelGGL((bwd_fscan_kernel<DK, F32IN>), dim3(nscan), dim3(SNT), 0, st, a);
-    prof_mark(st, kProfBwdRscan);
-    hipLaunchKernelGGL((bwd_rscan_kernel<DK, F32IN>), dim3(nscan), dim3(SNT), 0, st, a);
-    prof_mark(st, kProfBwdPost);
-    hipLaunchKernelGGL((bwd_post_kernel<DK, F32IN>), dim3(nch), dim3(PNT), 0, st, a);
-    prof_mark(st, kProfEnd);
-    return hipGetLastError();
+    hipError_t e = launch_k(kProfBwdPrep, bwd_prep_kernel<DK, F32IN>, dim3(nch), dim3(NTH), 0, st, a);
+    if (e == hipSuccess) e = launch_k(kProfBwdFscan, bwd_fscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
+    if (e == hipSuccess) e = launch_k(kProfBwdRscan, bwd_rscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
+    if (e == hipSuccess) e = launch_k(kProfBwdPost, bwd_post_kernel<DK, F32IN>, dim3(nch), dim3(PNT), 0, st, a);
+    return e;
 }
 
 }  // namespace

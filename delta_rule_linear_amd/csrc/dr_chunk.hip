@@ -1146,40 +1146,29 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
     if (a.NC > 0 && nseq > 0) {
         hipError_t e;
         if constexpr (!F32IN && !CGATE && !CBETA) {
-            prof_mark(st, kProfPrep);
             e = launch_prep16(a, DK, st);
         } else if constexpr (CGATE) {
             auto kern = prep_kernel<DK, F32IN, CGATE, CBETA, SEPV, QKN, KS>;
             const long njobs = (long)nseq * a.NC;
             constexpr int NTH = prep_threads<DK, CGATE>();
-            // (the occupancy query of a first call stays outside the timing mark)
             const long slots = resident_groups((const void*)kern, NTH);
             const int grid = (int)(njobs < slots ? njobs : slots);
-            prof_mark(st, kProfPrep);
-            hipLaunchKernelGGL(kern, dim3(grid), dim3(NTH), 0, st, a);
-            e = hipGetLastError();
+            e = launch_k(kProfPrep, kern, dim3(grid), dim3(NTH), 0, st, a);
         } else {
             dim3 g1(a.NC, a.H, a.B);
-            prof_mark(st, kProfPrep);
-            hipLaunchKernelGGL((prep_kernel<DK, F32IN, CGATE, CBETA>), g1, dim3(256), 0, st, a);
-            e = hipGetLastError();
+            e = launch_k(kProfPrep, prep_kernel<DK, F32IN, CGATE, CBETA>, g1, dim3(256), 0, st, a);
         }
         if (e != hipSuccess) return e;
     }
     if (nseq > 0) {
-        prof_mark(st, kProfScan);
-        hipError_t e;
         if constexpr (!F32IN) {
-            e = launch_scan16(a, DK, CGATE, CBETA, st);
+            return launch_scan16(a, DK, CGATE, CBETA, st);
         } else {
             const int NT = a.Dv / 16;
             const int groups = (nseq + 7) / 8;
-            hipLaunchKernelGGL((scan_kernel<DK, F32IN, CGATE, CBETA>), dim3(groups * 8 * NT), dim3(256),
-                               0, st, a);
-            e = hipGetLastError();
+            return launch_k(kProfScan, scan_kernel<DK, F32IN, CGATE, CBETA>, dim3(groups * 8 * NT), dim3(256), 0,
+                            st, a);
         }
-        prof_mark(st, kProfEnd);
-        return e;
     }
     return hipSuccess;
 }

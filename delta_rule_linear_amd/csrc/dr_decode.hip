@@ -178,25 +178,21 @@ static hipError_t launch_decode_d(const DecodeArgs& a, bool cgate, bool cbeta, h
     const int nslab = (a.Dv + 63) / 64;
     dim3 grid((unsigned)((size_t)a.N * a.H * nslab));
     if (cgate) {
-        if (cbeta) hipLaunchKernelGGL((decode_kernel<DK, F32IN, true, true>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((decode_kernel<DK, F32IN, true, false>), grid, dim3(256), 0, st, a);
-    } else {
-        if (cbeta) hipLaunchKernelGGL((decode_kernel<DK, F32IN, false, true>), grid, dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((decode_kernel<DK, F32IN, false, false>), grid, dim3(256), 0, st, a);
+        if (cbeta) return launch_k(kProfDecode, decode_kernel<DK, F32IN, true, true>, grid, dim3(256), 0, st, a);
+        return launch_k(kProfDecode, decode_kernel<DK, F32IN, true, false>, grid, dim3(256), 0, st, a);
     }
-    return hipGetLastError();
+    if (cbeta) return launch_k(kProfDecode, decode_kernel<DK, F32IN, false, true>, grid, dim3(256), 0, st, a);
+    return launch_k(kProfDecode, decode_kernel<DK, F32IN, false, false>, grid, dim3(256), 0, st, a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st) {
     if ((size_t)a.N * a.H == 0) return hipSuccess;
-    prof_mark(st, kProfDecode);
     hipError_t e;
     if (Dk == 64) e = f32in ? launch_decode_d<64, true>(a, cgate, cbeta, st)
                             : launch_decode_d<64, false>(a, cgate, cbeta, st);
     else e = f32in ? launch_decode_d<128, true>(a, cgate, cbeta, st)
                    : launch_decode_d<128, false>(a, cgate, cbeta, st);
-    prof_mark(st, kProfEnd);
     return e;
 }
 

@@ -2,6 +2,7 @@
 // the kernel translation units (not part of the public interface).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
@@ -137,14 +138,28 @@ struct BwdArgs {
     float* wKt;
 };
 
-// Optional per-kernel timing: launchers mark the start of each kernel and the
-// end of their last one (dr_profile_begin / dr_profile_end).
+// Optional per-kernel timing (dr_profile_begin / dr_profile_end).  While it is
+// on, launch_k gives each kernel launch a start and a stop event of its own,
+// set from the dispatch's own timestamps, so that no marker packets sit
+// between the kernels being timed; the pair is kept under the kernel's slot.
 enum ProfSlot {
     kProfPrep = 0, kProfScan = 1, kProfDecode = 2,
     kProfBwdPrep = 3, kProfBwdFscan = 4, kProfBwdRscan = 5, kProfBwdPost = 6,
-    kProfSlots = 7, kProfEnd = 7
+    kProfSlots = 7, kProfNone = -1
 };
-void prof_mark(hipStream_t st, int slot);
+// two new timing events while timing is on (false otherwise)
+bool prof_events(hipEvent_t* start, hipEvent_t* stop);
+void prof_record(hipEvent_t start, hipEvent_t stop, int slot);
+
+template <typename F, typename... Args>
+hipError_t launch_k(int slot, F kernel, dim3 grid, dim3 block, unsigned shmem, hipStream_t st, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    const bool timed = slot != kProfNone && prof_events(&e0, &e1);
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, st, e0, e1, 0u, args...);
+    const hipError_t e = hipGetLastError();
+    if (timed) prof_record(e0, e1, slot);
+    return e;
+}
 
 // sepv: a.beta_v differs from a.beta (channel beta only)
 hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool cbeta, bool sepv,

@@ -349,8 +349,7 @@ static hipError_t launch_p16(const ChunkArgs& a, hipStream_t st) {
     auto kern = prep16_kernel<DK>;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.NC, a.H, a.B), dim3(256), L::TOTAL, st, a);
-    return hipGetLastError();
+    return launch_k(kProfPrep, kern, dim3(a.NC, a.H, a.B), dim3(256), L::TOTAL, st, a);
 }
 
 hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st) {

@@ -792,8 +792,7 @@ static hipError_t launch_s16(const ChunkArgs& a, hipStream_t st) {
                                  : scan16_kernel<DK, RAW, CGATE, CBETA>;
     const int NT = a.Dv / 16;
     const int groups = (a.nseq + 7) / 8;
-    hipLaunchKernelGGL(kern, dim3(groups * 8 * NT), dim3(512), 0, st, a);
-    return hipGetLastError();
+    return launch_k(kProfScan, kern, dim3(groups * 8 * NT), dim3(512), 0, st, a);
 }
 
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st) {

@@ -378,12 +378,12 @@ dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
 /*
  * Per-kernel timing, for benchmarks and profiling (not part of the method).
  * Between dr_profile_begin and dr_profile_end every chunked-forward, backward
- * and decode call also records HIP events on its stream around each kernel it
- * launches; dr_profile_end waits for those events and reports the summed
- * kernel durations (event to event, so a launch gap between two kernels of
- * one call is counted with the earlier kernel).  Calls made while profiling
- * must come from one host thread.  dr_profile_begin discards any earlier
- * unreported records.  The events are created and destroyed by the library.
+ * and decode call launches each of its kernels with a start and a stop event
+ * of its own, set from the kernel dispatch's timestamps (no marker packets
+ * between the kernels); dr_profile_end waits for those events and reports the
+ * summed kernel durations.  Calls made while profiling must come from one
+ * host thread.  dr_profile_begin discards any earlier unreported records.  The
+ * events are created and destroyed by the library.
  * Returns DR_ERR_NULL for a NULL report, DR_ERR_HIP if an event fails.
  */
 typedef struct dr_profile_report {
