@@ -18,8 +18,9 @@ and its notes on the key/query map and on choosing beta): qk_l2norm replaces q
 and k by unit vectors (a zero vector stays zero); beta_logit takes the
 strength arrays as logits, beta = sigmoid(x).
 backward() gives the gradients of the forward, with one strength or separate
-erase and write strengths (reverse-mode differentiation of the token
-recurrence; the pages print no backward).
+erase and write strengths, write-side key scales and the input preparation
+(reverse-mode differentiation of the token recurrence; the pages print no
+backward).
 Write-side key scaling (OSDN page, "Method"; the preconditioned delta rule
 page, abstract): a diagonal preconditioner s_t on the gradient step, given as
 an input; the write key is w = s * kt:
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH):
     lib.dro_backward_kv.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp, dp, ctypes.c_int, dp, dp,
                                                          dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.dro_backward_kv.restype = ctypes.c_int
+    lib.dro_backward_ex.argtypes = [ctypes.c_int] * 5 + [dp, dp, dp, dp, ctypes.c_int, dp, dp, ctypes.c_int, dp,
+                                                         ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                                         ctypes.c_int]
+    lib.dro_backward_ex.restype = ctypes.c_int
     lib.dro_max_threads.restype = ctypes.c_int
     return lib
 
@@ -143,12 +148,15 @@ def forward(q, k, v, log_alpha, beta, S0=None, *, gate: str, beta_mode: str,
 
 
 def backward(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, beta_mode: str,
-             nthreads: int = 0, lib=None, beta_v=None):
-    """Gradients of the forward (inputs as given) for the loss whose gradients
-    with respect to o and S_final are dO and dS_final.  Returns a dict with dq,
-    dk, dv, dlog_alpha (None for gate "none"), dbeta and dS0, in fp64 and in
-    the inputs' shapes.  With a separate write strength beta_v (beta's shape)
-    dbeta is the erase strength's gradient and dbeta_v the write strength's."""
+             nthreads: int = 0, lib=None, beta_v=None, key_scale=None, qk_l2norm: bool = False,
+             beta_logit: bool = False):
+    """Gradients of the forward for the loss whose gradients with respect to o
+    and S_final are dO and dS_final, with respect to the inputs as passed (raw
+    q, k and strength logits when the input preparation is on).  Returns a
+    dict with dq, dk, dv, dlog_alpha (None for gate "none"), dbeta and dS0, in
+    fp64 and in the inputs' shapes.  With a separate write strength beta_v
+    (beta's shape) dbeta is the erase strength's gradient and dbeta_v the write
+    strength's; with key_scale ([B,H,L,Dk]) dkey_scale is its gradient."""
     lib = lib or _get()
     q = np.asarray(q)
     B, H, L, Dk = q.shape
@@ -165,6 +173,25 @@ def backward(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, beta
            "dlog_alpha": None if log_alpha is None else np.empty(np.shape(log_alpha)),
            "dbeta": np.empty(np.shape(beta)), "dS0": np.empty((B, H, Dk, Dv))}
     ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    flags = (IN_QK_L2NORM if qk_l2norm else 0) | (IN_BETA_LOGIT if beta_logit else 0)
+    if flags or key_scale is not None:
+        if key_scale is not None and np.shape(key_scale) != (B, H, L, Dk):
+            raise ValueError("key_scale must be [B, H, L, Dk]")
+        ksa, ksp = _f64(key_scale)
+        bva, bvp = _f64(beta_v)
+        if beta_v is not None:
+            if np.shape(beta_v) != np.shape(beta):
+                raise ValueError("beta_v must have beta's shape")
+            out["dbeta_v"] = np.empty(np.shape(beta))
+        if key_scale is not None:
+            out["dkey_scale"] = np.empty((B, H, L, Dk))
+        rc = lib.dro_backward_ex(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp, bvp, BETA_CODES[beta_mode],
+                                 ksp, flags, sp, dp_, fp, ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]),
+                                 ptr(out["dlog_alpha"]), ptr(out["dbeta"]), ptr(out.get("dbeta_v")),
+                                 ptr(out.get("dkey_scale")), ptr(out["dS0"]), int(nthreads))
+        if rc != 0:
+            raise ValueError(f"dro_backward_ex rejected its arguments (code {rc})")
+        return out
     if beta_v is None:
         rc = lib.dro_backward(B, H, L, Dk, Dv, qp, kp, vp, lp, GATE_CODES[gate], bp, BETA_CODES[beta_mode], sp,
                               dp_, fp, ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]), ptr(out["dlog_alpha"]),

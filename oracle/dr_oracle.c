@@ -241,38 +241,48 @@ int dro_forward(int B, int H, int L, int Dk, int Dv,
 }
 
 /*
- * dro_backward -- gradients of the forward above (one strength, no key scales,
- * inputs as given; separate strengths in dro_backward_kv) by reverse-mode
- * differentiation of the token recurrence.
+ * dro_backward -- gradients of the forward above by reverse-mode
+ * differentiation of the token recurrence (dro_backward: one strength, inputs
+ * as given; dro_backward_kv: separate strengths; dro_backward_ex: any of
+ * these with write-side key scales and the input preparation).
  * The pages give no backward (the DeltaNet page, step 7, only says training
  * uses the chunkwise form); this is the chain rule applied to the update as
- * written, in the order of the forward's steps:
+ * written, in the order of the forward's steps, with qh, kh the prepared query
+ * and key (the inputs themselves, or their unit vectors) and w = s (.) kt the
+ * write-side key (kt itself without key scales):
  *   S' = Diag(alpha) S_{t-1},  p = S'^T kt,  u = vt - p,
- *   S_t = S' + kt u^T,  o_t = S_t^T q_t.
+ *   S_t = S' + w u^T,  o_t = S_t^T qh_t.
  * With G the gradient of the loss with respect to S_t (dS_final for t = L,
- * plus q_t do_t^T from the output):
- *   dq_t = S_t do_t,   dvt = G^T kt,   dkt = G u - S' dvt,
- *   dS' = G - kt dvt^T,   dalpha_c = sum_j dS'_cj S_{t-1,cj},
+ * plus qh_t do_t^T from the output):
+ *   dqh_t = S_t do_t,   du = G^T w,   dw = G u,   dvt = du,
+ *   dkt = s (.) dw - S' du,   ds = kt (.) dw,
+ *   dS' = G - kt du^T,   dalpha_c = sum_j dS'_cj S_{t-1,cj},
  *   G <- Diag(alpha) dS'   (the gradient with respect to S_{t-1}),
- * then through kt = sqrt(beta) k, vt = sqrt(beta) v and alpha = e^{log alpha}.
+ * then through kt = sqrt(beta) kh, vt = sqrt(beta) v, alpha = e^{log alpha},
+ * beta = sigmoid(x) (logits: dx = dbeta beta (1 - beta)) and the
+ * normalisation qh = q / |q| (dq = (dqh - qh (qh . dqh)) / |q|; the
+ * normalisation is not differentiable at the zero vector, which it leaves
+ * at zero: its gradient there is taken as zero), likewise for k.
  *   dO        [B][H][L][Dv]  gradient of the loss with respect to o
  *   dS_final  [B][H][Dk][Dv] with respect to S_final, or NULL (zero)
  *   dq, dk    [B][H][L][Dk]  out;  dv [B][H][L][Dv] out
  *   dlog_alpha  out, log_alpha's shape, or NULL (gate NONE)
  *   dbeta     out, beta's shape (the derivative of sqrt at 0 is infinite:
- *             beta > 0 is assumed)
+ *             beta > 0 is assumed; with logits it always is)
  *   dS0       [B][H][Dk][Dv] out, or NULL
  * dro_backward_kv takes a separate write strength beta_v (beta's shape; the
  * forward's FG2-GDN+ reading: vt = sqrt(beta_v) v, beta on kt only) and
  * returns its gradient in dbeta_v; dbeta then holds beta's (erase strength's)
- * part alone.
+ * part alone.  dro_backward_ex: beta_v and dbeta_v as for dro_backward_kv or
+ * both NULL (one strength); key_scale [B][H][L][Dk] and its gradient
+ * dkey_scale, both NULL without key scales; input_flags as for the forward.
  */
 static int backward_impl(int B, int H, int L, int Dk, int Dv,
                          const double* q, const double* k, const double* v,
                          const double* log_alpha, int gate, const double* beta, const double* beta_v,
-                         int beta_mode, const double* S0, const double* dO, const double* dS_final,
-                         double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta,
-                         double* dbeta_v, double* dS0, int nthreads)
+                         int beta_mode, const double* key_scale, int flags, const double* S0, const double* dO,
+                         const double* dS_final, double* dq, double* dk, double* dv, double* dlog_alpha,
+                         double* dbeta, double* dbeta_v, double* dkey_scale, double* dS0, int nthreads)
 {
     if (B <= 0 || H <= 0 || L < 0 || Dk <= 0 || Dv <= 0) return DRO_EINVAL;
     if (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta) return DRO_EINVAL;
@@ -281,6 +291,10 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
     if ((gate == DRO_GATE_NONE) != (log_alpha == NULL)) return DRO_EINVAL;
     if (gate != DRO_GATE_NONE && !dlog_alpha) return DRO_EINVAL;
     if (beta_mode == DRO_BETA_CHANNEL && Dv != Dk) return DRO_EINVAL;
+    if ((key_scale == NULL) != (dkey_scale == NULL)) return DRO_EINVAL;
+    if (flags & ~(DRO_IN_QK_L2NORM | DRO_IN_BETA_LOGIT)) return DRO_EINVAL;
+    const int l2 = (flags & DRO_IN_QK_L2NORM) != 0;
+    const int logit = (flags & DRO_IN_BETA_LOGIT) != 0;
 
     const long nseq = (long)B * H;
     const size_t sz = (size_t)Dk * Dv;
@@ -291,21 +305,32 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
 #endif
     for (long s = 0; s < nseq; ++s) {
         /* the states S_0 .. S_L, then the working arrays */
-        double* St = (double*)malloc(sizeof(double) * ((size_t)(L + 1) * sz + 2 * sz + 4 * (size_t)Dk + 4 * (size_t)Dv));
+        double* St = (double*)malloc(sizeof(double) * ((size_t)(L + 1) * sz + 2 * sz + 11 * (size_t)Dk +
+                                                       6 * (size_t)Dv));
         if (!St) {
             err = DRO_ENOMEM;
             continue;
         }
         double* G = St + (size_t)(L + 1) * sz;
         double* Sp = G + sz;
-        double* kt = Sp + sz;
+        double* kt = Sp + sz;       /* Dk each: */
         double* al = kt + Dk;
         double* sbk = al + Dk;
         double* dkt = sbk + Dk;
-        double* vt = dkt + Dk;
+        double* qh = dkt + Dk;
+        double* kh = qh + Dk;
+        double* w = kh + Dk;
+        double* dw = w + Dk;
+        double* dqh = dw + Dk;
+        double* dkh = dqh + Dk;
+        double* bkv = dkh + Dk;
+        double* vt = bkv + Dk;      /* Dv each: */
         double* u = vt + Dv;
         double* dvt = u + Dv;
         double* sbv = dvt + Dv;
+        double* bvv = sbv + Dv;
+        double* pp = bvv + Dv;
+        (void)pp;
         const size_t lw = (gate == DRO_GATE_CHANNEL) ? (size_t)L * Dk : (size_t)L;
         const size_t bw = (beta_mode == DRO_BETA_CHANNEL) ? (size_t)L * Dk : (size_t)L;
         const double* qs = q + (size_t)s * L * Dk;
@@ -314,6 +339,7 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
         const double* las = log_alpha ? log_alpha + (size_t)s * lw : NULL;
         const double* bs = beta + (size_t)s * bw;
         const double* bvs = beta_v ? beta_v + (size_t)s * bw : bs;   /* the write strength */
+        const double* kss = key_scale ? key_scale + (size_t)s * L * Dk : NULL;
         /* outputs, then the forward step's scratch: kt (Dk), vt (Dv), p (Dv) */
         double* tmp_o = (double*)malloc(sizeof(double) * ((size_t)L * Dv + (size_t)Dk + 2 * (size_t)Dv));
         if (!tmp_o) {
@@ -334,7 +360,8 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
                              las ? las + (gate == DRO_GATE_CHANNEL ? (size_t)t * Dk : (size_t)t) : NULL, gate,
                              bs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t),
                              bvs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,
-                             NULL, 0, St + (size_t)(t + 1) * sz, tmp_o + (size_t)t * Dv, ktmp, vtmp, ptmp);
+                             kss ? kss + (size_t)t * Dk : NULL, flags, St + (size_t)(t + 1) * sz,
+                             tmp_o + (size_t)t * Dv, ktmp, vtmp, ptmp);
             }
         }
         /* reverse */
@@ -347,16 +374,23 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
             const double* dot = dO + ((size_t)s * L + t) * Dv;
             const double* Sprev = St + (size_t)t * sz;
             const double* Snew = St + (size_t)(t + 1) * sz;
+            const double* st_ = kss ? kss + (size_t)t * Dk : NULL;
+            /* the prepared query and key, the strengths, kt, w and alpha */
+            const double rq = l2 ? inv_l2(qt, Dk) : 1.0;   /* 1 / |q_t| */
+            const double rk = l2 ? inv_l2(k_t, Dk) : 1.0;   /* 1 / |k_t| */
             for (int c = 0; c < Dk; ++c) {
-                const double b = beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + c];
-                sbk[c] = sqrt(b);
-                kt[c] = sbk[c] * k_t[c];
+                qh[c] = rq * qt[c];
+                kh[c] = rk * k_t[c];
+                bkv[c] = strength(beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + c], logit);
+                sbk[c] = sqrt(bkv[c]);
+                kt[c] = sbk[c] * kh[c];
+                w[c] = st_ ? st_[c] * kt[c] : kt[c];
                 al[c] = gate == DRO_GATE_NONE ? 1.0
                       : gate == DRO_GATE_SCALAR ? exp(las[t]) : exp(las[(size_t)t * Dk + c]);
             }
             for (int j = 0; j < Dv; ++j) {
-                const double b = beta_mode == DRO_BETA_SCALAR ? bvs[t] : bvs[(size_t)t * Dk + j];
-                sbv[j] = sqrt(b);
+                bvv[j] = strength(beta_mode == DRO_BETA_SCALAR ? bvs[t] : bvs[(size_t)t * Dk + j], logit);
+                sbv[j] = sqrt(bvv[j]);
                 vt[j] = sbv[j] * v_t[j];
             }
             /* S' and u = vt - S'^T kt */
@@ -367,27 +401,32 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
                 for (int c = 0; c < Dk; ++c) pj += Sp[(size_t)c * Dv + j] * kt[c];
                 u[j] = vt[j] - pj;
             }
-            /* the output: G += q do^T, dq = S_t do */
+            /* the output: G += qh do^T, dqh = S_t do */
             for (int c = 0; c < Dk; ++c) {
                 double a = 0.0;
                 for (int j = 0; j < Dv; ++j) {
-                    G[(size_t)c * Dv + j] += qt[c] * dot[j];
+                    G[(size_t)c * Dv + j] += qh[c] * dot[j];
                     a += Snew[(size_t)c * Dv + j] * dot[j];
                 }
-                dq[((size_t)s * L + t) * Dk + c] = a;
+                dqh[c] = a;
             }
-            /* dvt = G^T kt;  dkt = G u - S' dvt */
+            /* du = G^T w (= dvt);  dw = G u;  dkt = s (.) dw - S' du;  ds = kt (.) dw */
             for (int j = 0; j < Dv; ++j) {
                 double a = 0.0;
-                for (int c = 0; c < Dk; ++c) a += G[(size_t)c * Dv + j] * kt[c];
+                for (int c = 0; c < Dk; ++c) a += G[(size_t)c * Dv + j] * w[c];
                 dvt[j] = a;
             }
             for (int c = 0; c < Dk; ++c) {
-                double a = 0.0;
-                for (int j = 0; j < Dv; ++j) a += G[(size_t)c * Dv + j] * u[j] - Sp[(size_t)c * Dv + j] * dvt[j];
-                dkt[c] = a;
+                double a = 0.0, b = 0.0;
+                for (int j = 0; j < Dv; ++j) {
+                    a += G[(size_t)c * Dv + j] * u[j];
+                    b += Sp[(size_t)c * Dv + j] * dvt[j];
+                }
+                dw[c] = a;
+                dkt[c] = (st_ ? st_[c] : 1.0) * a - b;
+                if (st_) dkey_scale[((size_t)s * L + t) * Dk + c] = kt[c] * a;
             }
-            /* dS' = G - kt dvt^T;  dalpha;  G <- Diag(alpha) dS' */
+            /* dS' = G - kt du^T;  dalpha;  G <- Diag(alpha) dS' */
             double dla_s = 0.0;
             for (int c = 0; c < Dk; ++c) {
                 double da = 0.0;
@@ -401,11 +440,13 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
                 dla_s += al[c] * da;
             }
             if (gate == DRO_GATE_SCALAR) dlog_alpha[(size_t)s * L + t] = dla_s;
-            /* through kt = sqrt(beta) k and vt = sqrt(beta) v */
+            /* through kt = sqrt(beta) kh and vt = sqrt(beta) v; a logit adds
+               beta (1 - beta) */
             double db_s = 0.0;
             for (int c = 0; c < Dk; ++c) {
-                dk[((size_t)s * L + t) * Dk + c] = sbk[c] * dkt[c];
-                const double g = dkt[c] * k_t[c] / (2.0 * sbk[c]);
+                dkh[c] = sbk[c] * dkt[c];
+                double g = dkt[c] * kh[c] / (2.0 * sbk[c]);
+                if (logit) g *= bkv[c] * (1.0 - bkv[c]);
                 if (beta_mode == DRO_BETA_CHANNEL) dbeta[((size_t)s * L + t) * Dk + c] = g;
                 db_s += g;
             }
@@ -414,7 +455,8 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
             double dbv_s = 0.0;
             for (int j = 0; j < Dv; ++j) {
                 dv[((size_t)s * L + t) * Dv + j] = sbv[j] * dvt[j];
-                const double g = dvt[j] * v_t[j] / (2.0 * sbv[j]);
+                double g = dvt[j] * v_t[j] / (2.0 * sbv[j]);
+                if (logit) g *= bvv[j] * (1.0 - bvv[j]);
                 if (beta_mode == DRO_BETA_CHANNEL) {
                     if (dbeta_v) dbv[((size_t)s * L + t) * Dk + j] = g;
                     else dbv[((size_t)s * L + t) * Dk + j] += g;
@@ -428,6 +470,16 @@ static int backward_impl(int B, int H, int L, int Dk, int Dv,
                 } else {
                     dbeta[(size_t)s * L + t] = db_s + dbv_s;
                 }
+            }
+            /* through the normalisation: dx = (dxh - xh (xh . dxh)) / |x| */
+            double pq = 0.0, pk = 0.0;
+            for (int c = 0; c < Dk; ++c) {
+                pq += qh[c] * dqh[c];
+                pk += kh[c] * dkh[c];
+            }
+            for (int c = 0; c < Dk; ++c) {
+                dq[((size_t)s * L + t) * Dk + c] = l2 ? rq * (dqh[c] - qh[c] * pq) : dqh[c];
+                dk[((size_t)s * L + t) * Dk + c] = l2 ? rk * (dkh[c] - kh[c] * pk) : dkh[c];
             }
         }
         if (dS0) memcpy(dS0 + (size_t)s * sz, G, sizeof(double) * sz);
@@ -445,8 +497,8 @@ int dro_backward(int B, int H, int L, int Dk, int Dv,
                  double* dq, double* dk, double* dv, double* dlog_alpha, double* dbeta, double* dS0,
                  int nthreads)
 {
-    return backward_impl(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, NULL, beta_mode, S0, dO, dS_final,
-                         dq, dk, dv, dlog_alpha, dbeta, NULL, dS0, nthreads);
+    return backward_impl(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, NULL, beta_mode, NULL, 0, S0, dO,
+                         dS_final, dq, dk, dv, dlog_alpha, dbeta, NULL, NULL, dS0, nthreads);
 }
 
 int dro_backward_kv(int B, int H, int L, int Dk, int Dv,
@@ -457,8 +509,21 @@ int dro_backward_kv(int B, int H, int L, int Dk, int Dv,
                     double* dS0, int nthreads)
 {
     if (!beta_v || !dbeta_v) return DRO_EINVAL;
-    return backward_impl(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta_v, beta_mode, S0, dO, dS_final,
-                         dq, dk, dv, dlog_alpha, dbeta, dbeta_v, dS0, nthreads);
+    return backward_impl(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta_v, beta_mode, NULL, 0, S0, dO,
+                         dS_final, dq, dk, dv, dlog_alpha, dbeta, dbeta_v, NULL, dS0, nthreads);
+}
+
+int dro_backward_ex(int B, int H, int L, int Dk, int Dv,
+                    const double* q, const double* k, const double* v,
+                    const double* log_alpha, int gate, const double* beta, const double* beta_v, int beta_mode,
+                    const double* key_scale, int input_flags, const double* S0, const double* dO,
+                    const double* dS_final, double* dq, double* dk, double* dv, double* dlog_alpha,
+                    double* dbeta, double* dbeta_v, double* dkey_scale, double* dS0, int nthreads)
+{
+    if ((beta_v == NULL) != (dbeta_v == NULL)) return DRO_EINVAL;
+    return backward_impl(B, H, L, Dk, Dv, q, k, v, log_alpha, gate, beta, beta_v, beta_mode, key_scale,
+                         input_flags, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta, dbeta_v, dkey_scale, dS0,
+                         nthreads);
 }
 
 /* Threads the OpenMP runtime would use by default (1 without OpenMP). */

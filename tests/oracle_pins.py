@@ -735,3 +735,111 @@ def pin_bwd_kv_equal_strengths(fwd, bwd):
 
 
 BWD_KV_PINS = [pin_bwd_kv_directional_derivatives, pin_bwd_kv_equal_strengths]
+
+
+# Backward with write-side key scales and the input preparation.  Each pin
+# takes fwd_ex(q, k, v, la, beta, beta_v, ks, S0, *, gate, beta_mode,
+# qk_l2norm, beta_logit) -> (o, S_final) and bwd_ex(q, k, v, la, beta, beta_v,
+# ks, S0, dO, dS_final, *, gate, beta_mode, qk_l2norm, beta_logit) -> dict
+# (with dbeta_v when beta_v is given, dkey_scale when ks is).
+
+def _bwd_ex_case(salt, gate, beta_mode, *, logits, ks, sepv, L=7, Dk=5, Dv=5):
+    q, k, v, la, beta, S0, Wo, WS = _bwd_case(salt, gate, beta_mode, L=L, Dk=Dk, Dv=Dv)
+    r = _rng(salt + 4000)
+    q = q * r.uniform(0.5, 3.0, q.shape[:-1] + (1,))      # raw rows, not unit vectors
+    k = k * r.uniform(0.5, 3.0, k.shape[:-1] + (1,))
+    if logits:
+        beta = r.standard_normal(beta.shape)
+    bv = None
+    if sepv:
+        bv = r.standard_normal(beta.shape) if logits else 0.2 + 0.7 * r.uniform(0.0, 1.0, beta.shape)
+    s = r.uniform(0.5, 1.5, q.shape) if ks else None
+    return q, k, v, la, beta, bv, s, S0, Wo, WS
+
+
+def pin_bwd_ex_directional_derivatives(fwd_ex, bwd_ex):
+    """With key scales and/or the input preparation (raw q, k; strength
+    logits): for <Wo, o> + <WS, S_final>, the gradients' inner product with
+    random directions (each input alone, the key scales and the write strength
+    included, then all at once) equals the central difference of the loss."""
+    salt = 320
+    cases = [("scalar", "scalar", True, False, False), ("channel", "channel", True, False, False),
+             ("none", "scalar", False, True, False), ("channel", "scalar", False, True, False),
+             ("scalar", "channel", True, True, True), ("channel", "channel", True, True, True),
+             ("scalar", "scalar", True, True, True)]
+    for gate, beta_mode, prep, ks, sepv in cases:
+        salt += 1
+        q, k, v, la, beta, bv, s, S0, Wo, WS = _bwd_ex_case(salt, gate, beta_mode, logits=prep, ks=ks, sepv=sepv)
+        kw = dict(gate=gate, beta_mode=beta_mode, qk_l2norm=prep, beta_logit=prep)
+        g = bwd_ex(q, k, v, la, beta, bv, s, S0, Wo, WS, **kw)
+        x = dict(q=q, k=k, v=v, la=la, beta=beta, bv=bv, s=s, S0=S0)
+        grads = dict(q=g["dq"], k=g["dk"], v=g["dv"], la=g["dlog_alpha"], beta=g["dbeta"], bv=g.get("dbeta_v"),
+                     s=g.get("dkey_scale"), S0=g["dS0"])
+        r = _rng(salt + 2000)
+        dirs = {n: (None if a is None else r.standard_normal(a.shape)) for n, a in x.items()}
+
+        def loss(xx):
+            o, S = fwd_ex(xx["q"], xx["k"], xx["v"], xx["la"], xx["beta"], xx["bv"], xx["s"], xx["S0"], **kw)
+            return float(np.sum(Wo * o) + np.sum(WS * S))
+
+        live = [n for n in x if x[n] is not None]
+        for which in [[n] for n in live] + [live]:
+            h = 1e-5
+            xp = {n: (a if a is None else (a + h * dirs[n] if n in which else a)) for n, a in x.items()}
+            xm = {n: (a if a is None else (a - h * dirs[n] if n in which else a)) for n, a in x.items()}
+            fd = (loss(xp) - loss(xm)) / (2 * h)
+            an = sum(float(np.sum(grads[n] * dirs[n])) for n in which)
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), \
+                f"(ex {gate},{beta_mode},prep={prep},ks={ks}) d/d{'+'.join(which)}: analytic {an:.10e} " \
+                f"vs difference {fd:.10e}"
+
+
+def pin_bwd_ex_normalisation_is_scale_free(fwd_ex, bwd_ex):
+    """With q and k normalised, the loss does not change when q_t or k_t is
+    scaled by a positive factor, so the gradient of each row is orthogonal to
+    the row itself: sum_c dq_tc q_tc = 0 and sum_c dk_tc k_tc = 0 for every t."""
+    for n, (gate, beta_mode) in enumerate((("scalar", "scalar"), ("channel", "channel"))):
+        q, k, v, la, beta, bv, s, S0, Wo, WS = _bwd_ex_case(340 + n, gate, beta_mode, logits=True, ks=True,
+                                                             sepv=False)
+        g = bwd_ex(q, k, v, la, beta, bv, s, S0, Wo, WS, gate=gate, beta_mode=beta_mode, qk_l2norm=True,
+                   beta_logit=True)
+        scale = np.abs(g["dq"]).max() * np.abs(q).max()
+        assert np.abs(np.sum(g["dq"] * q, axis=-1)).max() <= 1e-12 * scale, "dq not orthogonal to q"
+        assert np.abs(np.sum(g["dk"] * k, axis=-1)).max() <= 1e-12 * np.abs(g["dk"]).max() * np.abs(k).max(), \
+            "dk not orthogonal to k"
+
+
+def pin_bwd_ex_off_is_the_plain_backward(fwd_ex, bwd_ex):
+    """Unit key scales and no input preparation: the gradients of q, k, v,
+    log alpha, beta and S0 are those of the plain backward (whose own pins fix
+    it), and with the input preparation on already-normalised rows and
+    strengths given as logits x, dbeta_x = dbeta sigmoid(x) (1 - sigmoid(x))
+    while the row gradients lose their radial part only."""
+    import oracle
+    for n, (gate, beta_mode) in enumerate((("scalar", "scalar"), ("channel", "channel"), ("none", "scalar"))):
+        q, k, v, la, beta, S0, Wo, WS = _bwd_case(350 + n, gate, beta_mode)
+        kw = dict(gate=gate, beta_mode=beta_mode)
+        ref = oracle.backward(q, k, v, la, beta, S0, Wo, WS, **kw)
+        g = bwd_ex(q, k, v, la, beta, None, np.ones_like(q), S0, Wo, WS, qk_l2norm=False, beta_logit=False, **kw)
+        for name in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"):
+            if ref[name] is None:
+                assert g[name] is None, name
+                continue
+            _close(g[name], ref[name], 1e-12, f"unit scales {gate} {name}")
+        # rows already unit vectors, strengths as logits
+        qu = q / np.linalg.norm(q, axis=-1, keepdims=True)
+        ku = k / np.linalg.norm(k, axis=-1, keepdims=True)
+        x = np.log(beta / (1.0 - beta))
+        ref = oracle.backward(qu, ku, v, la, beta, S0, Wo, WS, **kw)
+        g = bwd_ex(qu, ku, v, la, x, None, None, S0, Wo, WS, qk_l2norm=True, beta_logit=True, **kw)
+        _close(g["dbeta"], ref["dbeta"] * beta * (1.0 - beta), 1e-10, f"logit {gate} dbeta")
+        for name, rows in (("dq", qu), ("dk", ku)):
+            radial = np.sum(ref[name] * rows, axis=-1, keepdims=True) * rows
+            _close(g[name], ref[name] - radial, 1e-10, f"normalised {gate} {name}")
+        for name in ("dv", "dlog_alpha", "dS0"):
+            if ref[name] is not None:
+                _close(g[name], ref[name], 1e-10, f"normalised {gate} {name}")
+
+
+BWD_EX_PINS = [pin_bwd_ex_directional_derivatives, pin_bwd_ex_normalisation_is_scale_free,
+               pin_bwd_ex_off_is_the_plain_backward]

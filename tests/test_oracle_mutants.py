@@ -148,11 +148,9 @@ def test_ks_pins_catch_planted_mistake(tmp_path, name, old, new):
 # Mistakes in the backward, caught by its pins.
 BWD_MUTANTS = [
     ("no_decay_on_state_gradient", "G[(size_t)c * Dv + j] = al[c] * g;", "G[(size_t)c * Dv + j] = g;"),
-    ("read_term_sign", "a += G[(size_t)c * Dv + j] * u[j] - Sp[(size_t)c * Dv + j] * dvt[j];",
-     "a += G[(size_t)c * Dv + j] * u[j] + Sp[(size_t)c * Dv + j] * dvt[j];"),
-    ("output_gradient_dropped", "G[(size_t)c * Dv + j] += qt[c] * dot[j];", "G[(size_t)c * Dv + j] += 0.0 * dot[j];"),
-    ("sqrt_factor_half_dropped", "const double g = dkt[c] * k_t[c] / (2.0 * sbk[c]);",
-     "const double g = dkt[c] * k_t[c] / sbk[c];"),
+    ("read_term_sign", "dkt[c] = (st_ ? st_[c] : 1.0) * a - b;", "dkt[c] = (st_ ? st_[c] : 1.0) * a + b;"),
+    ("output_gradient_dropped", "G[(size_t)c * Dv + j] += qh[c] * dot[j];", "G[(size_t)c * Dv + j] += 0.0 * dot[j];"),
+    ("sqrt_factor_half_dropped", "double g = dkt[c] * kh[c] / (2.0 * sbk[c]);", "double g = dkt[c] * kh[c] / sbk[c];"),
     ("erase_term_dropped", "const double g = G[(size_t)c * Dv + j] - kt[c] * dvt[j];",
      "const double g = G[(size_t)c * Dv + j];"),
 ]
@@ -185,14 +183,14 @@ def test_bwd_pins_catch_planted_mistake(tmp_path, name, old, new):
 # strength, or the forward replayed with the erase strength on the value.
 BWD_KV_MUTANTS = [
     ("bwd_value_scaled_by_erase_strength",
-     "const double b = beta_mode == DRO_BETA_SCALAR ? bvs[t] : bvs[(size_t)t * Dk + j];",
-     "const double b = beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + j];"),
+     "bvv[j] = strength(beta_mode == DRO_BETA_SCALAR ? bvs[t] : bvs[(size_t)t * Dk + j], logit);",
+     "bvv[j] = strength(beta_mode == DRO_BETA_SCALAR ? bs[t] : bs[(size_t)t * Dk + j], logit);"),
     ("bwd_replay_without_write_strength",
      "bvs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,",
      "bs + (beta_mode == DRO_BETA_CHANNEL ? (size_t)t * Dk : (size_t)t), beta_mode,"),
     ("bwd_write_strength_gradient_halved",
-     "const double g = dvt[j] * v_t[j] / (2.0 * sbv[j]);",
-     "const double g = dvt[j] * v_t[j] / (4.0 * sbv[j]);"),
+     "double g = dvt[j] * v_t[j] / (2.0 * sbv[j]);",
+     "double g = dvt[j] * v_t[j] / (4.0 * sbv[j]);"),
 ]
 
 
@@ -215,6 +213,46 @@ def test_bwd_kv_pins_catch_planted_mistake(tmp_path, name, old, new):
     for pin in oracle_pins.BWD_KV_PINS:
         try:
             pin(fwd, bwd)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
+
+
+# Mistakes in the backward of the key scales and of the input preparation.
+BWD_EX_MUTANTS = [
+    ("bwd_query_projection_dropped", "l2 ? rq * (dqh[c] - qh[c] * pq) : dqh[c]", "l2 ? rq * dqh[c] : dqh[c]"),
+    ("bwd_key_projection_dropped", "l2 ? rk * (dkh[c] - kh[c] * pk) : dkh[c]", "l2 ? rk * dkh[c] : dkh[c]"),
+    ("bwd_logit_factor_dropped", "if (logit) g *= bkv[c] * (1.0 - bkv[c]);", "if (0) g *= bkv[c] * (1.0 - bkv[c]);"),
+    ("bwd_write_logit_factor_dropped", "if (logit) g *= bvv[j] * (1.0 - bvv[j]);",
+     "if (0) g *= bvv[j] * (1.0 - bvv[j]);"),
+    ("bwd_write_scale_dropped", "dkt[c] = (st_ ? st_[c] : 1.0) * a - b;", "dkt[c] = a - b;"),
+    ("bwd_scale_gradient_from_write_key", "dkey_scale[((size_t)s * L + t) * Dk + c] = kt[c] * a;",
+     "dkey_scale[((size_t)s * L + t) * Dk + c] = w[c] * a;"),
+    ("bwd_value_gradient_through_read_key", "for (int c = 0; c < Dk; ++c) a += G[(size_t)c * Dv + j] * w[c];",
+     "for (int c = 0; c < Dk; ++c) a += G[(size_t)c * Dv + j] * kt[c];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BWD_EX_MUTANTS, ids=[m[0] for m in BWD_EX_MUTANTS])
+def test_bwd_ex_pins_catch_planted_mistake(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert text.count(old) == 1, f"mutation anchor for {name} not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(text.replace(old, new))
+    lib = oracle.load(oracle.build(str(src), str(tmp_path / "libmutant.so")))
+
+    def fwd_ex(q, k, v, la, beta, beta_v, ks, S0, *, gate, beta_mode, qk_l2norm, beta_logit):
+        return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, beta_v=beta_v, key_scale=ks,
+                              qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+
+    def bwd_ex(q, k, v, la, beta, beta_v, ks, S0, dO, dS, *, gate, beta_mode, qk_l2norm, beta_logit):
+        return oracle.backward(q, k, v, la, beta, S0, dO, dS, gate=gate, beta_mode=beta_mode, beta_v=beta_v,
+                               key_scale=ks, qk_l2norm=qk_l2norm, beta_logit=beta_logit, lib=lib)
+
+    caught = []
+    for pin in oracle_pins.BWD_EX_PINS:
+        try:
+            pin(fwd_ex, bwd_ex)
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {name}"

@@ -156,3 +156,18 @@ def test_backward_without_final_state_gradient():
     b = oracle.backward(q, k, v, la, beta, S0, Wo, np.zeros_like(WS), gate="scalar", beta_mode="scalar")
     for n in a:
         assert np.array_equal(a[n], b[n]), n
+
+
+def _fwd_ex(q, k, v, la, beta, beta_v, ks, S0, *, gate, beta_mode, qk_l2norm, beta_logit, lib=None):
+    return oracle.forward(q, k, v, la, beta, S0, gate=gate, beta_mode=beta_mode, beta_v=beta_v, key_scale=ks,
+                          qk_l2norm=qk_l2norm, beta_logit=beta_logit, lib=lib)
+
+
+def _bwd_ex(q, k, v, la, beta, beta_v, ks, S0, dO, dS, *, gate, beta_mode, qk_l2norm, beta_logit, lib=None):
+    return oracle.backward(q, k, v, la, beta, S0, dO, dS, gate=gate, beta_mode=beta_mode, beta_v=beta_v,
+                           key_scale=ks, qk_l2norm=qk_l2norm, beta_logit=beta_logit, lib=lib)
+
+
+@pytest.mark.parametrize("pin", oracle_pins.BWD_EX_PINS, ids=lambda f: f.__name__)
+def test_backward_ex_pin(pin):
+    pin(_fwd_ex, _bwd_ex)
