@@ -346,24 +346,28 @@ def dr_chunk_bwd_workspace_bytes(desc: ChunkDesc) -> int:
 
 
 def dr_chunk_bwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0, dO, dS_final=None, *, gate: str,
-                    beta_mode: str = "channel", want_dS0: bool = True, workspace=None, stream=None):
+                    beta_mode: str = "channel", want_dS0: bool = True, workspace=None, stream=None,
+                    qk_l2norm: bool = False, beta_logit: bool = False):
     """Gradients of dr_chunk_fwd_kv (separate erase and write strengths, both
     [B,H,L,Dk] or both [B,H,L] fp32): as dr_chunk_bwd, with dbeta the erase
     strength's gradient and dbeta_v the write strength's."""
     if beta_v is None:
         raise ValueError("beta_v is required")
     return dr_chunk_bwd(q, k, v, log_alpha, beta_k, S0, dO, dS_final, gate=gate, beta_mode=beta_mode,
-                        want_dS0=want_dS0, workspace=workspace, stream=stream, _beta_v=beta_v)
+                        want_dS0=want_dS0, workspace=workspace, stream=stream, qk_l2norm=qk_l2norm,
+                        beta_logit=beta_logit, _beta_v=beta_v)
 
 
 def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, beta_mode: str = "scalar",
-                 want_dS0: bool = True, workspace=None, stream=None, _beta_v=None):
+                 want_dS0: bool = True, workspace=None, stream=None, qk_l2norm: bool = False,
+                 beta_logit: bool = False, _beta_v=None):
     """Gradients of dr_chunk_fwd (any gate and beta mode) for the
     loss whose gradients with respect to o and S_final are dO [B,H,L,Dv] and
     dS_final [B,H,Dk,Dv] (fp32; dS_final None means zero).  q, k, v and the
-    other inputs are as for dr_chunk_fwd.  Returns a dict of fp32 device
-    tensors dq, dk, dv, dlog_alpha (None for gate "none"), dbeta and dS0
-    (None with want_dS0=False)."""
+    other inputs are as for dr_chunk_fwd, with the same input preparation
+    (qk_l2norm, beta_logit): the gradients are those of the raw inputs.
+    Returns a dict of fp32 device tensors dq, dk, dv, dlog_alpha (None for
+    gate "none"), dbeta and dS0 (None with want_dS0=False)."""
     torch = _torch()
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]
@@ -391,7 +395,8 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
            "dlog_alpha": torch.empty(gshape, **f32) if gshape is not None else None,
            "dbeta": torch.empty(bshape, **f32),
            "dS0": torch.empty((B, H, Dk, Dv), **f32) if want_dS0 else None}
-    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, beta_mode)
+    desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, beta_mode,
+                      input_flags(qk_l2norm, beta_logit))
     nbytes = dr_chunk_bwd_workspace_bytes(desc) if _beta_v is None else dr_chunk_bwd_kv_workspace_bytes(desc)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

@@ -425,10 +425,16 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
 
 // ----------------------------------------------------------------- backward
 struct BwdLayout {
-    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, ones, db1, total;
+    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, b32, db1, rq, rk, total;
 };
 
-// kvtok: separate scalar strengths, which take the channel-beta route
+// Whether a backward call runs on prepared fp32 copies of its inputs: a
+// channel-wise strength, separate strengths (kvtok: of one value per token),
+// or the input preparation.
+bool bwd_mapped(const dr_chunk_desc& d, bool kvtok) {
+    return d.beta == DR_BETA_CHANNEL || kvtok || d.input_flags != 0;
+}
+
 BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
     BwdLayout w{};
     const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
@@ -456,14 +462,19 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
         w.Kc = take(NCH * dr::CH * d.Dk * f);
         w.Kt = take(NCH * dr::CH * d.Dk * f);
     }
-    if (d.beta == DR_BETA_CHANNEL || kvtok) {
-        // q, sqrt(beta) k, sqrt(beta) v in fp32, unit strengths and their (unused) gradient
+    if (bwd_mapped(d, kvtok)) {
+        // the fp32 copies and their strengths (with the unused gradient of
+        // the unit strengths on the channel-beta route), 1/|q|, 1/|k|
         const size_t ntok = (size_t)d.B * d.H * d.L;
         w.q32 = take(ntok * d.Dk * f);
         w.k32 = take(ntok * d.Dk * f);
         w.v32 = take(ntok * d.Dv * f);
-        w.ones = take(ntok * f);
-        w.db1 = take(ntok * f);
+        w.b32 = take(ntok * f);
+        if (d.beta == DR_BETA_CHANNEL || kvtok) w.db1 = take(ntok * f);
+        if (d.input_flags & DR_IN_QK_L2NORM) {
+            w.rq = take(ntok * f);
+            w.rk = take(ntok * f);
+        }
     }
     w.total = NCH ? off : 0;
     return w;
@@ -472,7 +483,6 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
 dr_status check_bwd_desc(const dr_chunk_desc* d) {
     dr_status s = check_chunk_desc(d);
     if (s != DR_OK) return s;
-    if (d->input_flags) return fail(DR_ERR_UNSUPPORTED, "the backward takes no input_flags");
     if (d->out_dtype != DR_F32) return fail(DR_ERR_UNSUPPORTED, "dO and the gradients are fp32: out_dtype must be DR_F32");
     const size_t NCH = (size_t)d->B * d->H * (((size_t)d->L + dr::CH - 1) / dr::CH);
     if (NCH > (size_t)std::numeric_limits<int>::max())
@@ -575,29 +585,41 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         a.wKc = (float*)(ws + w.Kc);
         a.wKt = (float*)(ws + w.Kt);
     }
-    bool f32in = d->in_dtype == DR_F32;
     const bool cbeta = d->beta == DR_BETA_CHANNEL || kvtok;
-    const size_t ntok = nseq * d->L, nel = ntok * d->Dk;   // Dv == Dk with a channel beta
+    const bool mapped = bwd_mapped(*d, kvtok);
     hipError_t e = hipSuccess;
-    if (cbeta) {
-        // the scaled inputs with unit strengths; the beta gradient of that run is discarded
-        float* q32 = (float*)(ws + w.q32);
-        float* k32 = (float*)(ws + w.k32);
-        float* v32 = (float*)(ws + w.v32);
-        float* ones = (float*)(ws + w.ones);
-        e = dr::launch_bwd_cbeta_in(q, k, v, beta, beta_v ? beta_v : beta, f32in, kvtok, d->Dk, nel, ntok, q32,
-                                    k32, v32, ones, st);
-        if (e != hipSuccess) return fail(DR_ERR_HIP, "backward input scaling launch: %s", hipGetErrorString(e));
-        a.q = q32; a.k = k32; a.v = v32;
-        a.beta = ones;
-        a.dbeta = (float*)(ws + w.db1);
-        f32in = true;
+    dr::BwdMap m{};
+    if (mapped) {
+        // the recurrence's inputs as fp32 copies; on the channel-beta route
+        // the unit strengths' gradient goes to db1 and is discarded
+        m.q = q; m.k = k; m.v = v;
+        m.beta = beta; m.beta_v = beta_v ? beta_v : beta;
+        m.f32in = d->in_dtype == DR_F32;
+        m.cbeta = cbeta;
+        m.per_token = kvtok;
+        m.sepv = beta_v != nullptr;
+        m.l2 = (d->input_flags & DR_IN_QK_L2NORM) != 0;
+        m.logit = (d->input_flags & DR_IN_BETA_LOGIT) != 0;
+        m.Dk = d->Dk; m.Dv = d->Dv;
+        m.ntok = nseq * d->L;
+        m.q32 = (float*)(ws + w.q32);
+        m.k32 = (float*)(ws + w.k32);
+        m.v32 = (float*)(ws + w.v32);
+        m.b32 = (float*)(ws + w.b32);
+        if (m.l2) {
+            m.rq = (float*)(ws + w.rq);
+            m.rk = (float*)(ws + w.rk);
+        }
+        e = dr::launch_bwd_map_in(m, st);
+        if (e != hipSuccess) return fail(DR_ERR_HIP, "backward input mapping launch: %s", hipGetErrorString(e));
+        a.q = m.q32; a.k = m.k32; a.v = m.v32;
+        a.beta = m.b32;
+        if (cbeta) a.dbeta = (float*)(ws + w.db1);
     }
-    e = dr::launch_bwd(a, d->Dk, f32in, st);
+    e = dr::launch_bwd(a, d->Dk, mapped || d->in_dtype == DR_F32, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
-    if (cbeta) {
-        e = dr::launch_bwd_cbeta_out(k, v, beta, beta_v ? beta_v : beta, d->in_dtype == DR_F32, kvtok, d->Dk, nel,
-                                     dk, dv, dbeta, dbeta_v, st);
+    if (mapped) {
+        e = dr::launch_bwd_map_out(m, dq, dk, dv, dbeta, dbeta_v, st);
         if (e != hipSuccess) return fail(DR_ERR_HIP, "backward gradient mapping launch: %s", hipGetErrorString(e));
     }
     return DR_OK;

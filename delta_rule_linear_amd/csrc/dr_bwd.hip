@@ -1598,76 +1598,141 @@ hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
 
 // q, kt = sqrt(beta_k) k, vt = sqrt(beta_v) v as fp32, and a unit strength per
 // token (beta_v is beta_k itself for one strength)
-// per_token: the strengths hold one value per token (element i belongs to
-// token i / dk), shared by every channel
-__global__ void bwd_cbeta_in_kernel(const void* q, const void* k, const void* v, const float* beta_k,
-                                    const float* beta_v, int f32in, int per_token, int dk, size_t n, size_t ntok,
-                                    float* q32, float* k32, float* v32, float* ones) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const float qv = f32in ? load1<true>(q, i) : load1<false>(q, i);
-        const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
-        const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
-        const size_t bi = per_token ? i / dk : i;
-        q32[i] = qv;
-        k32[i] = sqrtf(beta_k[bi]) * kv;
-        v32[i] = sqrtf(beta_v[bi]) * vv;
-        if (i < ntok) ones[i] = 1.f;
-    }
+// One wave per token (grid-stride over tokens): the lane owns channels
+// l, l + 64, ... of the token's rows.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
 }
 
-// Separate strengths of one value per token: dk, dv as in bwd_cbeta_out_kernel,
-// and each strength's gradient summed over the token's channels,
-//   dbeta^k_t = sum_c dkt_{t,c} k_{t,c} / (2 sqrt(beta^k_t)), dbeta^v_t likewise.
-// One wave per token (dk channels, dk / 64 per lane).
-__global__ void bwd_cbeta_out_tok_kernel(const void* k, const void* v, const float* beta_k, const float* beta_v,
-                                         int f32in, int dk, size_t ntok, float* dkg, float* dvg, float* dbeta_k,
-                                         float* dbeta_v) {
+__device__ __forceinline__ float ld_in(const void* p, size_t i, int f32in) {
+    return f32in ? load1<true>(p, i) : load1<false>(p, i);
+}
+
+// What the recurrence sees, as fp32 copies (the mapping is described at
+// launch_bwd_map_in in dr_internal.h).
+__global__ void bwd_map_in_kernel(BwdMap m) {
     const int l = threadIdx.x & 63;
     const size_t wv = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const size_t nw = ((size_t)gridDim.x * blockDim.x) >> 6;
-    for (size_t t = wv; t < ntok; t += nw) {
-        const float sk = sqrtf(beta_k[t]), sv = sqrtf(beta_v[t]);
-        float gk = 0.f, gv = 0.f;
-        for (int c = l; c < dk; c += 64) {
-            const size_t i = t * dk + c;
-            const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
-            const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
-            const float dkt = dkg[i], dvt = dvg[i];
-            gk += dkt * kv;
-            gv += dvt * vv;
-            dkg[i] = sk * dkt;
-            dvg[i] = sv * dvt;
+    for (size_t t = wv; t < m.ntok; t += nw) {
+        float qv[2] = {0.f, 0.f}, kv[2] = {0.f, 0.f}, ssq = 0.f, ssk = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = l + 64 * i;
+            if (c < m.Dk) {
+                qv[i] = ld_in(m.q, t * m.Dk + c, m.f32in);
+                kv[i] = ld_in(m.k, t * m.Dk + c, m.f32in);
+                ssq += qv[i] * qv[i];
+                ssk += kv[i] * kv[i];
+            }
+        }
+        float rq = 1.f, rk = 1.f;
+        if (m.l2) {
+            rq = inv_norm(wave_sum(ssq));
+            rk = inv_norm(wave_sum(ssk));
+            if (l == 0) {
+                m.rq[t] = rq;
+                m.rk[t] = rk;
+            }
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            gk += __shfl_xor(gk, off);
-            gv += __shfl_xor(gv, off);
+        for (int i = 0; i < 2; ++i) {
+            const int c = l + 64 * i;
+            if (c < m.Dk) {
+                const float kh = rk * kv[i];
+                m.q32[t * m.Dk + c] = rq * qv[i];
+                m.k32[t * m.Dk + c] =
+                    m.cbeta ? sqrtf(strength(strength_at(m.beta, m.per_token, t, m.Dk, c), m.logit)) * kh : kh;
+            }
         }
-        if (l == 0) {
-            dbeta_k[t] = gk / (2.f * sk);
-            dbeta_v[t] = gv / (2.f * sv);
+        for (int j = l; j < m.Dv; j += 64) {
+            const float vv = ld_in(m.v, t * m.Dv + j, m.f32in);
+            m.v32[t * m.Dv + j] =
+                m.cbeta ? sqrtf(strength(strength_at(m.beta_v, m.per_token, t, m.Dk, j), m.logit)) * vv : vv;
         }
+        if (l == 0) m.b32[t] = m.cbeta ? 1.f : strength(m.beta[t], m.logit);
     }
 }
 
-// dk, dv hold the gradients of kt and vt on entry, those of k and v on exit;
-// with dbeta_v NULL (one strength) both strength terms go to dbeta_k
-__global__ void bwd_cbeta_out_kernel(const void* k, const void* v, const float* beta_k, const float* beta_v,
-                                     int f32in, size_t n, float* dk, float* dv, float* dbeta_k, float* dbeta_v) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const float sk = sqrtf(beta_k[i]), sv = sqrtf(beta_v[i]);
-        const float kv = f32in ? load1<true>(k, i) : load1<false>(k, i);
-        const float vv = f32in ? load1<true>(v, i) : load1<false>(v, i);
-        const float dkt = dk[i], dvt = dv[i];
-        const float gk = dkt * kv / (2.f * sk), gv = dvt * vv / (2.f * sv);
-        if (dbeta_v) {
-            dbeta_k[i] = gk;
-            dbeta_v[i] = gv;
-        } else {
-            dbeta_k[i] = gk + gv;
+// The gradients of the copies, on entry in dq, dk, dv (and dbeta for a scalar
+// beta, with respect to the strength's value), mapped to those of the inputs
+// in place.
+__global__ void bwd_map_out_kernel(BwdMap m, float* dq, float* dk, float* dv, float* dbeta, float* dbeta_v) {
+    const int l = threadIdx.x & 63;
+    const size_t wv = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const size_t nw = ((size_t)gridDim.x * blockDim.x) >> 6;
+    for (size_t t = wv; t < m.ntok; t += nw) {
+        const float rq = m.l2 ? m.rq[t] : 1.f, rk = m.l2 ? m.rk[t] : 1.f;
+        float qh[2] = {0.f, 0.f}, dqh[2] = {0.f, 0.f}, kh[2] = {0.f, 0.f}, dkh[2] = {0.f, 0.f};
+        float pq = 0.f, pk = 0.f, gks = 0.f, gvs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = l + 64 * i;
+            if (c < m.Dk) {
+                const size_t e = t * m.Dk + c;
+                qh[i] = rq * ld_in(m.q, e, m.f32in);
+                kh[i] = rk * ld_in(m.k, e, m.f32in);
+                dqh[i] = dq[e];
+                const float dkt = dk[e];
+                if (m.cbeta) {
+                    const float bk = strength(strength_at(m.beta, m.per_token, t, m.Dk, c), m.logit);
+                    const float sbk = sqrtf(bk);
+                    dkh[i] = sbk * dkt;
+                    float g = dkt * kh[i] / (2.f * sbk);
+                    if (m.logit) g *= bk * (1.f - bk);
+                    if (m.per_token) gks += g;
+                    else dbeta[e] = g;
+                } else {
+                    dkh[i] = dkt;
+                }
+                pq += qh[i] * dqh[i];
+                pk += kh[i] * dkh[i];
+            }
         }
-        dk[i] = sk * dkt;
-        dv[i] = sv * dvt;
+        if (m.l2) {
+            pq = wave_sum(pq);
+            pk = wave_sum(pk);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = l + 64 * i;
+            if (c < m.Dk) {
+                const size_t e = t * m.Dk + c;
+                dq[e] = m.l2 ? rq * (dqh[i] - qh[i] * pq) : dqh[i];
+                dk[e] = m.l2 ? rk * (dkh[i] - kh[i] * pk) : dkh[i];
+            }
+        }
+        if (m.cbeta) {
+            for (int j = l; j < m.Dv; j += 64) {
+                const size_t e = t * m.Dv + j;
+                const float dvt = dv[e];
+                const float bv = strength(strength_at(m.beta_v, m.per_token, t, m.Dk, j), m.logit);
+                const float sbv = sqrtf(bv);
+                dv[e] = sbv * dvt;
+                float g = dvt * ld_in(m.v, e, m.f32in) / (2.f * sbv);
+                if (m.logit) g *= bv * (1.f - bv);
+                if (m.per_token) gvs += g;
+                else if (m.sepv) dbeta_v[t * m.Dk + j] = g;
+                else dbeta[t * m.Dk + j] += g;   // one strength: this lane wrote the channel's key part above
+            }
+            if (m.per_token) {
+                gks = wave_sum(gks);
+                gvs = wave_sum(gvs);
+                if (l == 0) {
+                    if (m.sepv) {
+                        dbeta[t] = gks;
+                        dbeta_v[t] = gvs;
+                    } else {
+                        dbeta[t] = gks + gvs;
+                    }
+                }
+            }
+        } else if (m.logit && l == 0) {
+            const float b = strength(m.beta[t], 1);
+            dbeta[t] *= b * (1.f - b);
+        }
     }
 }
 
@@ -1684,24 +1749,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta_k,
-                               const float* beta_v, bool f32in, bool per_token, int dk, size_t n, size_t ntok,
-                               float* q32, float* k32, float* v32, float* ones, hipStream_t st) {
-    hipLaunchKernelGGL(bwd_cbeta_in_kernel, dim3(2048), dim3(256), 0, st, q, k, v, beta_k, beta_v, (int)f32in,
-                       (int)per_token, dk, n, ntok, q32, k32, v32, ones);
-    return hipGetLastError();
+hipError_t launch_bwd_map_in(const BwdMap& m, hipStream_t st) {
+    return launch_k(kProfNone, bwd_map_in_kernel, dim3(2048), dim3(256), 0, st, m);
 }
 
-hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta_k, const float* beta_v, bool f32in,
-                                bool per_token, int dk, size_t n, float* dk_, float* dv, float* dbeta_k,
-                                float* dbeta_v, hipStream_t st) {
-    if (per_token)
-        hipLaunchKernelGGL(bwd_cbeta_out_tok_kernel, dim3(2048), dim3(256), 0, st, k, v, beta_k, beta_v, (int)f32in,
-                           dk, n / dk, dk_, dv, dbeta_k, dbeta_v);
-    else
-        hipLaunchKernelGGL(bwd_cbeta_out_kernel, dim3(2048), dim3(256), 0, st, k, v, beta_k, beta_v, (int)f32in, n,
-                           dk_, dv, dbeta_k, dbeta_v);
-    return hipGetLastError();
+hipError_t launch_bwd_map_out(const BwdMap& m, float* dq, float* dk, float* dv, float* dbeta, float* dbeta_v,
+                              hipStream_t st) {
+    return launch_k(kProfNone, bwd_map_out_kernel, dim3(2048), dim3(256), 0, st, m, dq, dk, dv, dbeta, dbeta_v);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st) {

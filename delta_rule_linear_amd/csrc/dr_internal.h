@@ -170,18 +170,39 @@ hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
 // the backward (dr_bwd.hip)
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st);
-// channel-wise beta: q, sqrt(beta_k) k, sqrt(beta_v) v as fp32 and unit
-// strengths before the backward (n = tokens x Dk, ntok = tokens); the
-// gradients of k, v and the strengths from those of the scaled key and value
-// after it (dbeta_v NULL: one strength, beta_v == beta_k).  per_token: the
-// strengths hold one value per token (separate scalar strengths; dbeta_v
-// required), shared by the token's dk channels.
-hipError_t launch_bwd_cbeta_in(const void* q, const void* k, const void* v, const float* beta_k,
-                               const float* beta_v, bool f32in, bool per_token, int dk, size_t n, size_t ntok,
-                               float* q32, float* k32, float* v32, float* ones, hipStream_t st);
-hipError_t launch_bwd_cbeta_out(const void* k, const void* v, const float* beta_k, const float* beta_v, bool f32in,
-                                bool per_token, int dk, size_t n, float* dk_, float* dv, float* dbeta_k,
-                                float* dbeta_v, hipStream_t st);
+// The backward kernels differentiate the recurrence with respect to q, k, v
+// and a scalar beta as they receive them.  When a call's inputs are not those
+// (a channel-wise or separate beta, or the input preparation), a per-token
+// pass writes fp32 copies of what the recurrence sees, the kernels run on the
+// copies, and a second per-token pass maps the gradients back:
+//   qh = q / |q|, kh = k / |k| with the normalisation (1/|x| kept per token),
+//   beta = sigmoid(x) for logits,
+//   on the channel-beta route (channel-wise or separate strengths) the copies
+//   are kt = sqrt(beta^k) (.) kh and vt = sqrt(beta^v) (.) v with unit
+//   strength; otherwise kh, v and the scalar beta itself;
+// back: dk = sqrt(beta^k) (.) dkt, dv = sqrt(beta^v) (.) dvt,
+//   dbeta^k = dkt (.) kh / (2 sqrt(beta^k)) (summed over the token's channels
+//   for per-token strengths; one strength adds dbeta^v to it), times
+//   beta (1 - beta) for logits; dq = (dqh - qh (qh . dqh)) / |q|, likewise dk.
+struct BwdMap {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* beta;
+    const float* beta_v;   // == beta with one strength
+    int f32in, cbeta, per_token, sepv, l2, logit, Dk, Dv;
+    size_t ntok;
+    float* q32;
+    float* k32;
+    float* v32;
+    float* b32;            // unit strengths (channel-beta route) or the scalar beta's values
+    float* rq;             // 1/|q_t|, 1/|k_t| (normalisation only)
+    float* rk;
+};
+hipError_t launch_bwd_map_in(const BwdMap& m, hipStream_t st);
+// dq, dk, dv (and dbeta for a scalar beta) hold the copies' gradients on entry
+hipError_t launch_bwd_map_out(const BwdMap& m, float* dq, float* dk, float* dv, float* dbeta, float* dbeta_v,
+                              hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int Dk, bool f32in, bool cgate, bool cbeta,
                          hipStream_t st);
 

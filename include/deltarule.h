@@ -302,8 +302,9 @@ dr_status dr_decode_step_precond(const dr_decode_desc* d, const void* q, const v
  * the backward or there is no work): per 64-token chunk of every sequence,
  * three 64 x 64 matrices, 64 gate values, two Dk x Dv states and three
  * 64 x Dv blocks, all fp32; with a channel gate 64 x Dk gate values and four
- * more 64 x Dk blocks (the gated keys and queries); with a channel beta fp32
- * copies of q, k and v and two floats per token. */
+ * more 64 x Dk blocks (the gated keys and queries); with a channel beta or
+ * the input preparation fp32 copies of q, k and v and one or two floats per
+ * token (two more with DR_IN_QK_L2NORM). */
 size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
 
 /*
@@ -317,12 +318,17 @@ size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
  * forms the gradients of q, k, beta and log alpha.  Everything runs in fp32.
  *
  * Covered modes: every gate and beta mode (plain DeltaNet, Gated DeltaNet,
- * KDA, FG2-GDN), d->input_flags 0 (gradients are with respect to the
- * strengths and vectors as given), d->out_dtype DR_F32 (the dtype of dO);
- * anything else is DR_ERR_UNSUPPORTED.  With DR_BETA_CHANNEL the kernels run
- * on fp32 copies of q, sqrt(beta) (.) k and sqrt(beta) (.) v with unit
- * strength, and map the gradients back elementwise (beta > 0 assumed: the
- * square root has no derivative at 0).  in_dtype (fp32 or bf16) is the dtype
+ * KDA, FG2-GDN), every input_flags combination, d->out_dtype DR_F32 (the
+ * dtype of dO); anything else is DR_ERR_UNSUPPORTED.  The gradients are with
+ * respect to the arrays as passed: with DR_IN_QK_L2NORM those of the raw q
+ * and k (through the normalisation; a zero row has a zero gradient), with
+ * DR_IN_BETA_LOGIT those of the logits (through the sigmoid).  With
+ * DR_BETA_CHANNEL or the input preparation a per-token pass first writes fp32
+ * copies of what the recurrence sees (normalised q and k, the strengths'
+ * values; with DR_BETA_CHANNEL sqrt(beta) (.) k and sqrt(beta) (.) v with
+ * unit strength), the kernels run on those, and a second per-token pass maps
+ * the gradients back (DR_BETA_CHANNEL: beta > 0 assumed, the square root has
+ * no derivative at 0; logits always satisfy it).  in_dtype (fp32 or bf16) is the dtype
  * of q, k, v; Dk, Dv as for dr_chunk_fwd.  With DR_GATE_CHANNEL the kernels
  * work on keys and queries scaled by e^{+-G}, G a channel's cumulative log
  * decay within a 64-token chunk, so each G must stay above about -80 (fp32

@@ -279,7 +279,7 @@ def test_backward_validation_and_workspace():
     assert call(d, dla=None) == drl.DR_ERR_NULL                        # scalar gate: d log alpha needed
     assert call(_desc(gate="none"), la=None) == drl.DR_ERR_NULL        # no gate: none allowed
     assert call(d, dS0=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
-    for bad in (dict(Dv=64, beta_mode="channel"), dict(flags=drl.DR_IN_QK_L2NORM),
+    for bad in (dict(Dv=64, beta_mode="channel"), dict(flags=4),
                 dict(out_dtype=drl.DR_BF16), dict(Dk=96)):
         assert call(_desc(**bad)) == drl.DR_ERR_UNSUPPORTED
         assert drl.dr_chunk_bwd_workspace_bytes(_desc(**bad)) == 0
@@ -295,6 +295,15 @@ def test_backward_validation_and_workspace():
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(gate="channel")) >= need + NCH * 4 * 5 * 64 * 128 - NCH * 4 * 64
     # a channel beta runs the unit-strength kernels on fp32 copies of q, sqrt(beta) k, sqrt(beta) v
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel")) >= need + 3 * 2 * 3 * 100 * 128 * 4
+    # the input preparation runs the kernels on fp32 copies of q, k, v (and
+    # keeps 1/|q|, 1/|k| per token with the normalisation)
+    ntok = 2 * 3 * 100
+    lgt = drl.dr_chunk_bwd_workspace_bytes(_desc(flags=drl.DR_IN_BETA_LOGIT))
+    l2 = drl.dr_chunk_bwd_workspace_bytes(_desc(flags=drl.DR_IN_QK_L2NORM))
+    assert lgt >= need + 3 * ntok * 128 * 4 + ntok * 4
+    assert l2 >= lgt + 2 * ntok * 4
+    assert drl.dr_chunk_bwd_workspace_bytes(_desc(flags=3)) == l2
+    assert call(_desc(flags=3), wbytes=l2 - 1) == drl.DR_ERR_WORKSPACE
     # no sequences: validated and done without touching memory
     assert lib.dr_chunk_bwd(ctypes.byref(_desc(B=0)), *([None] * 15), 0, None) == drl.DR_OK
     # gradients must not overlap each other or an input

@@ -232,3 +232,109 @@ def test_backward_full_size_every_sequence():
     del g, ref
     torch.cuda.empty_cache()
 
+
+
+def _check_prepared(p, seed=0, tol=None):
+    """The backward with the input preparation on, against the oracle's
+    gradients with respect to the raw inputs (unnormalised q and k, strength
+    logits)."""
+    import delta_rule_linear_amd as drl
+    announce("backward prepared", p.name, p.B, p.H, p.L, p.Dk, p.Dv, p.in_dtype, p.gate, p.beta_mode,
+             p.qk_l2norm, p.beta_logit)
+    dO, dSf = inputs.backward_cotangents(p, seed)
+    t = problem_to_dev(p)
+    flags = dict(qk_l2norm=p.qk_l2norm, beta_logit=p.beta_logit)
+    if p.beta_v is None:
+        g = drl.dr_chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"], to_dev(dO, "f32"),
+                             to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode, **flags)
+    else:
+        g = drl.dr_chunk_bwd_kv(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["beta_v"], t["S0"],
+                                to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode,
+                                **flags)
+    torch.cuda.synchronize()
+    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode=p.beta_mode,
+                          beta_v=p.beta_v, **flags)
+    tol = TOL[p.in_dtype] if tol is None else tol
+    errs = {n: rel_err(to_np(g[n]), ref[n]) for n in GRADS + ("dbeta_v",) if ref.get(n) is not None}
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"{p.name}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f" (tol {tol:.0e})"
+
+
+def _raw(p, qk_l2norm, beta_logit):
+    """p drawn with raw_inputs=True, with one or both preparation steps on:
+    a step that stays off gets its prepared values (normalised q, k; the
+    strengths' sigmoid), so the forward sees the same recurrence."""
+    import dataclasses
+
+    def sig(x):
+        return None if x is None else (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+    def unit(x):
+        x64 = x.astype(np.float32).astype(np.float64)
+        n = np.linalg.norm(x64, axis=-1, keepdims=True)
+        return inputs._to_dtype(np.where(n > 0, x64 / np.where(n > 0, n, 1), 0.0), p.in_dtype)
+
+    upd = dict(qk_l2norm=qk_l2norm, beta_logit=beta_logit)
+    if not qk_l2norm:
+        upd.update(q=unit(p.q), k=unit(p.k))
+    if not beta_logit:
+        upd.update(beta=sig(p.beta), beta_v=sig(p.beta_v))
+    return dataclasses.replace(p, **upd)
+
+
+@pytest.mark.parametrize("prep", ["l2", "logit", "both"])
+@pytest.mark.parametrize("beta_mode", ["scalar", "channel", "kv_scalar", "kv_channel"])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_input_preparation(prep, beta_mode, gate, dtype):
+    # DeltaNet page, step list, step 2 and its notes: the gradients are those
+    # of the raw q and k (through the normalisation) and of the strength
+    # logits (through the sigmoid)
+    kv = beta_mode.startswith("kv_")
+    bm = beta_mode[3:] if kv else beta_mode
+    rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
+    D = 128 if dtype == "bf16" else 64
+    p = inputs.make_chunk_problem(2, 2, 150, D, D, in_dtype=dtype, gate=gate, beta_mode=bm, s0_var=0.01,
+                                  seed=17 + D, log_alpha_range=rng, beta_v=kv, raw_inputs=True,
+                                  name=f"bwd_prep_{prep}_{beta_mode}_{gate}_{dtype}")
+    p = _raw(p, prep in ("l2", "both"), prep in ("logit", "both"))
+    _check_prepared(p, seed=3)
+
+
+@pytest.mark.parametrize("Dv", [16, 48, 256])
+def test_backward_input_preparation_value_width(Dv):
+    p = inputs.make_chunk_problem(1, 2, 130, 128, Dv, in_dtype="f32", gate="scalar", s0_var=0.01, seed=Dv + 1,
+                                  log_alpha_range=inputs.GDN_GATE, raw_inputs=True, name=f"bwd_prep_dv{Dv}")
+    _check_prepared(p, seed=4)
+
+
+def test_backward_input_preparation_zero_rows():
+    # a zero q or k row normalises to zero (both sides take that reading),
+    # and its gradient is zero
+    p = inputs.make_chunk_problem(1, 2, 100, 64, 64, in_dtype="f32", gate="scalar", s0_var=0.01, seed=23,
+                                  log_alpha_range=inputs.GDN_GATE, raw_inputs=True, name="bwd_prep_zero_rows")
+    p.q[0, 0, 5] = 0
+    p.k[0, 1, 70] = 0
+    p.q[0, 1, 99] = 0
+    p.k[0, 1, 99] = 0
+    _check_prepared(p, seed=5)
+
+
+@pytest.mark.timeout(900)
+def test_backward_input_preparation_full_size_every_sequence():
+    # the benchmark's GDN shape with raw q, k and strength logits
+    import delta_rule_linear_amd as drl
+    p = inputs.make_chunk_problem(2, 16, 16384, 128, 128, in_dtype="bf16", gate="scalar",
+                                  log_alpha_range=inputs.GDN_GATE, s0_var=0.01, seed=0, raw_inputs=True,
+                                  name="bwd_prep_gdn_b2h16_16k")
+    announce("backward prepared full size", p.name)
+    dO, dSf = inputs.backward_cotangents(p, 0)
+    t = problem_to_dev(p)
+    g = drl.dr_chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"], to_dev(dO, "f32"),
+                         to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode, qk_l2norm=True, beta_logit=True)
+    torch.cuda.synchronize()
+    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode=p.beta_mode,
+                          qk_l2norm=True, beta_logit=True)
+    _every_sequence(p.name, g, ref, GRADS)
+    del g, ref
+    torch.cuda.empty_cache()
