@@ -124,8 +124,9 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-SCAN_SOURCES = ["delta_rule_linear_amd/csrc/dr_scan16.hip", "delta_rule_linear_amd/csrc/dr_device.h",
-                "delta_rule_linear_amd/csrc/dr_internal.h"]
+# the scan kernel's source and its device helpers: a change to either may
+# change the kernel, and then the recorded traffic no longer applies
+SCAN_SOURCES = ["delta_rule_linear_amd/csrc/dr_scan16.hip", "delta_rule_linear_amd/csrc/dr_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan16_gdn_b2h16_16k_traffic.md")
 
 

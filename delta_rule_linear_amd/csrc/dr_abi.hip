@@ -435,6 +435,10 @@ bool bwd_mapped(const dr_chunk_desc& d, bool kvtok) {
     return d.beta == DR_BETA_CHANNEL || kvtok || d.input_flags != 0;
 }
 
+bool bwd_copies(const dr_chunk_desc& d, bool kvtok) {
+    return d.beta == DR_BETA_CHANNEL || kvtok || (d.input_flags & DR_IN_QK_L2NORM);
+}
+
 BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
     BwdLayout w{};
     const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
@@ -463,12 +467,15 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
         w.Kt = take(NCH * dr::CH * d.Dk * f);
     }
     if (bwd_mapped(d, kvtok)) {
-        // the fp32 copies and their strengths (with the unused gradient of
-        // the unit strengths on the channel-beta route), 1/|q|, 1/|k|
+        // the fp32 copies (not with logits alone) and their strengths (with
+        // the unused gradient of the unit strengths on the channel-beta
+        // route), 1/|q|, 1/|k|
         const size_t ntok = (size_t)d.B * d.H * d.L;
-        w.q32 = take(ntok * d.Dk * f);
-        w.k32 = take(ntok * d.Dk * f);
-        w.v32 = take(ntok * d.Dv * f);
+        if (bwd_copies(d, kvtok)) {
+            w.q32 = take(ntok * d.Dk * f);
+            w.k32 = take(ntok * d.Dk * f);
+            w.v32 = take(ntok * d.Dv * f);
+        }
         w.b32 = take(ntok * f);
         if (d.beta == DR_BETA_CHANNEL || kvtok) w.db1 = take(ntok * f);
         if (d.input_flags & DR_IN_QK_L2NORM) {
@@ -602,9 +609,12 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         m.logit = (d->input_flags & DR_IN_BETA_LOGIT) != 0;
         m.Dk = d->Dk; m.Dv = d->Dv;
         m.ntok = nseq * d->L;
-        m.q32 = (float*)(ws + w.q32);
-        m.k32 = (float*)(ws + w.k32);
-        m.v32 = (float*)(ws + w.v32);
+        m.copy = bwd_copies(*d, kvtok);
+        if (m.copy) {
+            m.q32 = (float*)(ws + w.q32);
+            m.k32 = (float*)(ws + w.k32);
+            m.v32 = (float*)(ws + w.v32);
+        }
         m.b32 = (float*)(ws + w.b32);
         if (m.l2) {
             m.rq = (float*)(ws + w.rq);
@@ -612,11 +622,13 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         }
         e = dr::launch_bwd_map_in(m, st);
         if (e != hipSuccess) return fail(DR_ERR_HIP, "backward input mapping launch: %s", hipGetErrorString(e));
-        a.q = m.q32; a.k = m.k32; a.v = m.v32;
+        if (m.copy) {
+            a.q = m.q32; a.k = m.k32; a.v = m.v32;
+        }
         a.beta = m.b32;
         if (cbeta) a.dbeta = (float*)(ws + w.db1);
     }
-    e = dr::launch_bwd(a, d->Dk, mapped || d->in_dtype == DR_F32, st);
+    e = dr::launch_bwd(a, d->Dk, m.copy || d->in_dtype == DR_F32, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
     if (mapped) {
         e = dr::launch_bwd_map_out(m, dq, dk, dv, dbeta, dbeta_v, st);

@@ -31,6 +31,8 @@
 // Tokens past the end of a sequence enter the last chunk as zeros (q, k, v,
 // dO, beta and log alpha), which leaves every real token's terms unchanged.
 
+#include <algorithm>
+
 #include "dr_internal.h"
 
 namespace dr {
@@ -1598,140 +1600,149 @@ hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
 
 // q, kt = sqrt(beta_k) k, vt = sqrt(beta_v) v as fp32, and a unit strength per
 // token (beta_v is beta_k itself for one strength)
-// One wave per token (grid-stride over tokens): the lane owns channels
-// l, l + 64, ... of the token's rows.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+// The per-token mapping passes: DK / 4 consecutive lanes take one token, four
+// channels each (16-byte accesses for fp32 arrays, 8-byte for bf16), so a wave
+// covers 64 / (DK / 4) tokens per step of its grid-stride loop.
+template <bool F32IN>
+__device__ __forceinline__ f32x4 ld4(const void* p, size_t i) {
+    if constexpr (F32IN) {
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        return f32x4{bf16_to_f32((uint16_t)u.x), bf16_to_f32((uint16_t)(u.x >> 16)), bf16_to_f32((uint16_t)u.y),
+                     bf16_to_f32((uint16_t)(u.y >> 16))};
+    }
 }
-
-__device__ __forceinline__ float ld_in(const void* p, size_t i, int f32in) {
-    return f32in ? load1<true>(p, i) : load1<false>(p, i);
+__device__ __forceinline__ f32x4 ldf4(const float* p, size_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+__device__ __forceinline__ void stf4(float* p, size_t i, const f32x4& x) { *reinterpret_cast<f32x4*>(p + i) = x; }
+__device__ __forceinline__ float sum4(const f32x4& x) { return (x[0] + x[1]) + (x[2] + x[3]); }
+__device__ __forceinline__ f32x4 strength4(const f32x4& x, int logit) {
+    return f32x4{strength(x[0], logit), strength(x[1], logit), strength(x[2], logit), strength(x[3], logit)};
+}
+__device__ __forceinline__ f32x4 sqrt4(const f32x4& x) {
+    return f32x4{sqrtf(x[0]), sqrtf(x[1]), sqrtf(x[2]), sqrtf(x[3])};
+}
+// the four strengths of channels c4 .. c4 + 3 of token t (one value per token
+// with per_token)
+__device__ __forceinline__ f32x4 strengths_at(const float* base, int per_token, size_t t, int dk, int c4,
+                                              int logit) {
+    const f32x4 x = per_token ? f32x4{base[t], base[t], base[t], base[t]} : ldf4(base, t * dk + c4);
+    return strength4(x, logit);
 }
 
 // What the recurrence sees, as fp32 copies (the mapping is described at
 // launch_bwd_map_in in dr_internal.h).
-__global__ void bwd_map_in_kernel(BwdMap m) {
-    const int l = threadIdx.x & 63;
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(256) void bwd_map_in_kernel(BwdMap m) {
+    constexpr int LPT = DK / 4, TPW = 64 / LPT;
+    const int l = threadIdx.x & 63, c4 = 4 * (l % LPT);
     const size_t wv = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const size_t nw = ((size_t)gridDim.x * blockDim.x) >> 6;
-    for (size_t t = wv; t < m.ntok; t += nw) {
-        float qv[2] = {0.f, 0.f}, kv[2] = {0.f, 0.f}, ssq = 0.f, ssk = 0.f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = l + 64 * i;
-            if (c < m.Dk) {
-                qv[i] = ld_in(m.q, t * m.Dk + c, m.f32in);
-                kv[i] = ld_in(m.k, t * m.Dk + c, m.f32in);
-                ssq += qv[i] * qv[i];
-                ssk += kv[i] * kv[i];
-            }
+    for (size_t t0 = wv * TPW; t0 < m.ntok; t0 += nw * TPW) {
+        const size_t tl = t0 + l / LPT;
+        const bool ok = tl < m.ntok;
+        const size_t t = ok ? tl : t0;   // lanes past the end repeat token t0 and store nothing
+        if (!m.copy) {
+            if (ok && c4 == 0) m.b32[t] = strength(m.beta[t], m.logit);
+            continue;
         }
+        const f32x4 q = ld4<F32IN>(m.q, t * DK + c4), k = ld4<F32IN>(m.k, t * DK + c4);
         float rq = 1.f, rk = 1.f;
         if (m.l2) {
-            rq = inv_norm(wave_sum(ssq));
-            rk = inv_norm(wave_sum(ssk));
-            if (l == 0) {
-                m.rq[t] = rq;
-                m.rk[t] = rk;
-            }
+            rq = inv_norm(group_sum<LPT>(sum4(q * q)));
+            rk = inv_norm(group_sum<LPT>(sum4(k * k)));
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = l + 64 * i;
-            if (c < m.Dk) {
-                const float kh = rk * kv[i];
-                m.q32[t * m.Dk + c] = rq * qv[i];
-                m.k32[t * m.Dk + c] =
-                    m.cbeta ? sqrtf(strength(strength_at(m.beta, m.per_token, t, m.Dk, c), m.logit)) * kh : kh;
-            }
+        if (!ok) continue;
+        if (m.l2 && c4 == 0) {
+            m.rq[t] = rq;
+            m.rk[t] = rk;
         }
-        for (int j = l; j < m.Dv; j += 64) {
-            const float vv = ld_in(m.v, t * m.Dv + j, m.f32in);
-            m.v32[t * m.Dv + j] =
-                m.cbeta ? sqrtf(strength(strength_at(m.beta_v, m.per_token, t, m.Dk, j), m.logit)) * vv : vv;
+        stf4(m.q32, t * DK + c4, q * rq);
+        if (m.cbeta) {
+            // Dv == DK on this route
+            const f32x4 v = ld4<F32IN>(m.v, t * DK + c4);
+            stf4(m.k32, t * DK + c4, sqrt4(strengths_at(m.beta, m.per_token, t, DK, c4, m.logit)) * (k * rk));
+            stf4(m.v32, t * DK + c4, sqrt4(strengths_at(m.beta_v, m.per_token, t, DK, c4, m.logit)) * v);
+            if (c4 == 0) m.b32[t] = 1.f;
+        } else {
+            stf4(m.k32, t * DK + c4, k * rk);
+            for (int j4 = c4; j4 < m.Dv; j4 += 4 * LPT)
+                stf4(m.v32, t * m.Dv + j4, ld4<F32IN>(m.v, t * m.Dv + j4));
+            if (c4 == 0) m.b32[t] = strength(m.beta[t], m.logit);
         }
-        if (l == 0) m.b32[t] = m.cbeta ? 1.f : strength(m.beta[t], m.logit);
     }
 }
 
 // The gradients of the copies, on entry in dq, dk, dv (and dbeta for a scalar
 // beta, with respect to the strength's value), mapped to those of the inputs
 // in place.
-__global__ void bwd_map_out_kernel(BwdMap m, float* dq, float* dk, float* dv, float* dbeta, float* dbeta_v) {
-    const int l = threadIdx.x & 63;
+template <int DK, bool F32IN>
+__global__ __launch_bounds__(256) void bwd_map_out_kernel(BwdMap m, float* dq, float* dk, float* dv, float* dbeta,
+                                                          float* dbeta_v) {
+    constexpr int LPT = DK / 4, TPW = 64 / LPT;
+    const int l = threadIdx.x & 63, c4 = 4 * (l % LPT);
     const size_t wv = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const size_t nw = ((size_t)gridDim.x * blockDim.x) >> 6;
-    for (size_t t = wv; t < m.ntok; t += nw) {
-        const float rq = m.l2 ? m.rq[t] : 1.f, rk = m.l2 ? m.rk[t] : 1.f;
-        float qh[2] = {0.f, 0.f}, dqh[2] = {0.f, 0.f}, kh[2] = {0.f, 0.f}, dkh[2] = {0.f, 0.f};
-        float pq = 0.f, pk = 0.f, gks = 0.f, gvs = 0.f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = l + 64 * i;
-            if (c < m.Dk) {
-                const size_t e = t * m.Dk + c;
-                qh[i] = rq * ld_in(m.q, e, m.f32in);
-                kh[i] = rk * ld_in(m.k, e, m.f32in);
-                dqh[i] = dq[e];
-                const float dkt = dk[e];
-                if (m.cbeta) {
-                    const float bk = strength(strength_at(m.beta, m.per_token, t, m.Dk, c), m.logit);
-                    const float sbk = sqrtf(bk);
-                    dkh[i] = sbk * dkt;
-                    float g = dkt * kh[i] / (2.f * sbk);
-                    if (m.logit) g *= bk * (1.f - bk);
-                    if (m.per_token) gks += g;
-                    else dbeta[e] = g;
-                } else {
-                    dkh[i] = dkt;
-                }
-                pq += qh[i] * dqh[i];
-                pk += kh[i] * dkh[i];
+    for (size_t t0 = wv * TPW; t0 < m.ntok; t0 += nw * TPW) {
+        const size_t tl = t0 + l / LPT;
+        const bool ok = tl < m.ntok;
+        const size_t t = ok ? tl : t0;
+        const size_t e = t * DK + c4;
+        if (!m.cbeta) {
+            // a scalar strength: its gradient (written by the kernels with
+            // respect to the strength's value) through the sigmoid
+            if (m.logit && ok && c4 == 0) {
+                const float b = strength(m.beta[t], 1);
+                dbeta[t] *= b * (1.f - b);
             }
+            if (!m.l2) continue;
+        }
+        const float rq = m.l2 ? m.rq[t] : 1.f, rk = m.l2 ? m.rk[t] : 1.f;
+        const f32x4 kh = ld4<F32IN>(m.k, e) * rk;
+        const f32x4 dkt = ldf4(dk, e);
+        f32x4 dkh = dkt, gk = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (m.cbeta) {
+            const f32x4 bk = strengths_at(m.beta, m.per_token, t, DK, c4, m.logit), sbk = sqrt4(bk);
+            dkh = sbk * dkt;
+            gk = dkt * kh / (2.f * sbk);
+            if (m.logit) gk = gk * bk * (1.f - bk);
         }
         if (m.l2) {
-            pq = wave_sum(pq);
-            pk = wave_sum(pk);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = l + 64 * i;
-            if (c < m.Dk) {
-                const size_t e = t * m.Dk + c;
-                dq[e] = m.l2 ? rq * (dqh[i] - qh[i] * pq) : dqh[i];
-                dk[e] = m.l2 ? rk * (dkh[i] - kh[i] * pk) : dkh[i];
+            const f32x4 qh = ld4<F32IN>(m.q, e) * rq;
+            const f32x4 dqh = ldf4(dq, e);
+            const float pq = group_sum<LPT>(sum4(qh * dqh));
+            const float pk = group_sum<LPT>(sum4(kh * dkh));
+            if (ok) {
+                stf4(dq, e, rq * (dqh - qh * pq));
+                stf4(dk, e, rk * (dkh - kh * pk));
             }
+        } else if (ok) {
+            stf4(dk, e, dkh);
         }
-        if (m.cbeta) {
-            for (int j = l; j < m.Dv; j += 64) {
-                const size_t e = t * m.Dv + j;
-                const float dvt = dv[e];
-                const float bv = strength(strength_at(m.beta_v, m.per_token, t, m.Dk, j), m.logit);
-                const float sbv = sqrtf(bv);
-                dv[e] = sbv * dvt;
-                float g = dvt * ld_in(m.v, e, m.f32in) / (2.f * sbv);
-                if (m.logit) g *= bv * (1.f - bv);
-                if (m.per_token) gvs += g;
-                else if (m.sepv) dbeta_v[t * m.Dk + j] = g;
-                else dbeta[t * m.Dk + j] += g;   // one strength: this lane wrote the channel's key part above
-            }
-            if (m.per_token) {
-                gks = wave_sum(gks);
-                gvs = wave_sum(gvs);
-                if (l == 0) {
-                    if (m.sepv) {
-                        dbeta[t] = gks;
-                        dbeta_v[t] = gvs;
-                    } else {
-                        dbeta[t] = gks + gvs;
-                    }
+        if (!m.cbeta) continue;
+        // the value side (Dv == DK on this route)
+        const f32x4 dvt = ldf4(dv, e);
+        const f32x4 bv = strengths_at(m.beta_v, m.per_token, t, DK, c4, m.logit), sbv = sqrt4(bv);
+        f32x4 gv = dvt * ld4<F32IN>(m.v, e) / (2.f * sbv);
+        if (m.logit) gv = gv * bv * (1.f - bv);
+        if (ok) stf4(dv, e, sbv * dvt);
+        if (m.per_token) {
+            const float gks = group_sum<LPT>(sum4(gk)), gvs = group_sum<LPT>(sum4(gv));
+            if (ok && c4 == 0) {
+                if (m.sepv) {
+                    dbeta[t] = gks;
+                    dbeta_v[t] = gvs;
+                } else {
+                    dbeta[t] = gks + gvs;
                 }
             }
-        } else if (m.logit && l == 0) {
-            const float b = strength(m.beta[t], 1);
-            dbeta[t] *= b * (1.f - b);
+        } else if (ok) {
+            if (m.sepv) {
+                stf4(dbeta, e, gk);
+                stf4(dbeta_v, e, gv);
+            } else {
+                stf4(dbeta, e, gk + gv);
+            }
         }
     }
 }
@@ -1749,13 +1760,31 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+static unsigned map_blocks(const BwdMap& m) {
+    const size_t per_block = 4 * (size_t)(256 / m.Dk);   // tokens per step of a 256-thread block
+    return (unsigned)std::min<size_t>((m.ntok + per_block - 1) / per_block, 4096);
+}
+
 hipError_t launch_bwd_map_in(const BwdMap& m, hipStream_t st) {
-    return launch_k(kProfNone, bwd_map_in_kernel, dim3(2048), dim3(256), 0, st, m);
+    if (m.ntok == 0) return hipSuccess;
+    const dim3 g(map_blocks(m)), b(256);
+    if (m.Dk == 64)
+        return m.f32in ? launch_k(kProfNone, bwd_map_in_kernel<64, true>, g, b, 0, st, m)
+                       : launch_k(kProfNone, bwd_map_in_kernel<64, false>, g, b, 0, st, m);
+    return m.f32in ? launch_k(kProfNone, bwd_map_in_kernel<128, true>, g, b, 0, st, m)
+                   : launch_k(kProfNone, bwd_map_in_kernel<128, false>, g, b, 0, st, m);
 }
 
 hipError_t launch_bwd_map_out(const BwdMap& m, float* dq, float* dk, float* dv, float* dbeta, float* dbeta_v,
                               hipStream_t st) {
-    return launch_k(kProfNone, bwd_map_out_kernel, dim3(2048), dim3(256), 0, st, m, dq, dk, dv, dbeta, dbeta_v);
+    if (m.ntok == 0) return hipSuccess;
+    const dim3 g(map_blocks(m)), b(256);
+    if (m.Dk == 64)
+        return m.f32in ? launch_k(kProfNone, bwd_map_out_kernel<64, true>, g, b, 0, st, m, dq, dk, dv, dbeta, dbeta_v)
+                       : launch_k(kProfNone, bwd_map_out_kernel<64, false>, g, b, 0, st, m, dq, dk, dv, dbeta,
+                                  dbeta_v);
+    return m.f32in ? launch_k(kProfNone, bwd_map_out_kernel<128, true>, g, b, 0, st, m, dq, dk, dv, dbeta, dbeta_v)
+                   : launch_k(kProfNone, bwd_map_out_kernel<128, false>, g, b, 0, st, m, dq, dk, dv, dbeta, dbeta_v);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st) {

@@ -179,7 +179,8 @@ hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st);
 //   beta = sigmoid(x) for logits,
 //   on the channel-beta route (channel-wise or separate strengths) the copies
 //   are kt = sqrt(beta^k) (.) kh and vt = sqrt(beta^v) (.) v with unit
-//   strength; otherwise kh, v and the scalar beta itself;
+//   strength; otherwise kh, v and the scalar beta itself (with logits alone
+//   only the strengths are written: q, k and v are used as they are);
 // back: dk = sqrt(beta^k) (.) dkt, dv = sqrt(beta^v) (.) dvt,
 //   dbeta^k = dkt (.) kh / (2 sqrt(beta^k)) (summed over the token's channels
 //   for per-token strengths; one strength adds dbeta^v to it), times
@@ -191,6 +192,7 @@ struct BwdMap {
     const float* beta;
     const float* beta_v;   // == beta with one strength
     int f32in, cbeta, per_token, sepv, l2, logit, Dk, Dv;
+    int copy;              // q, k, v copied (channel-beta route or normalisation); else only b32
     size_t ntok;
     float* q32;
     float* k32;

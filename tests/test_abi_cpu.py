@@ -295,13 +295,13 @@ def test_backward_validation_and_workspace():
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(gate="channel")) >= need + NCH * 4 * 5 * 64 * 128 - NCH * 4 * 64
     # a channel beta runs the unit-strength kernels on fp32 copies of q, sqrt(beta) k, sqrt(beta) v
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel")) >= need + 3 * 2 * 3 * 100 * 128 * 4
-    # the input preparation runs the kernels on fp32 copies of q, k, v (and
-    # keeps 1/|q|, 1/|k| per token with the normalisation)
+    # the normalisation runs the kernels on fp32 copies of q, k, v and keeps
+    # 1/|q|, 1/|k| per token; logits alone need only the strengths' values
     ntok = 2 * 3 * 100
     lgt = drl.dr_chunk_bwd_workspace_bytes(_desc(flags=drl.DR_IN_BETA_LOGIT))
     l2 = drl.dr_chunk_bwd_workspace_bytes(_desc(flags=drl.DR_IN_QK_L2NORM))
-    assert lgt >= need + 3 * ntok * 128 * 4 + ntok * 4
-    assert l2 >= lgt + 2 * ntok * 4
+    assert need + ntok * 4 <= lgt < need + ntok * 128
+    assert l2 >= need + 3 * ntok * 128 * 4 + 3 * ntok * 4
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(flags=3)) == l2
     assert call(_desc(flags=3), wbytes=l2 - 1) == drl.DR_ERR_WORKSPACE
     # no sequences: validated and done without touching memory
