@@ -177,13 +177,29 @@ std::mutex g_prof_mu;
 std::atomic<bool> g_prof_on{false};
 std::vector<ProfRec> g_prof;
 hipError_t g_prof_err = hipSuccess;
+// Events are kept for reuse: none is created or destroyed while a profiling
+// window is open once the pool holds enough (creating events allocates in
+// the runtime, which would run beside the kernels being timed).
+std::vector<hipEvent_t> g_pool;
+constexpr size_t kPoolFill = 1024;
 
 void prof_clear() {
     for (auto& r : g_prof) {
-        hipEventDestroy(r.start);
-        hipEventDestroy(r.stop);
+        g_pool.push_back(r.start);
+        g_pool.push_back(r.stop);
     }
     g_prof.clear();
+}
+
+// tops the pool up to kPoolFill events (called with g_prof_mu held)
+hipError_t pool_fill() {
+    while (g_pool.size() < kPoolFill) {
+        hipEvent_t e;
+        const hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) return r;
+        g_pool.push_back(e);
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -191,17 +207,18 @@ void prof_clear() {
 namespace dr {
 bool prof_events(hipEvent_t* start, hipEvent_t* stop) {
     if (!g_prof_on.load(std::memory_order_relaxed)) return false;
-    hipError_t e = hipEventCreate(start);
-    if (e == hipSuccess) {
-        e = hipEventCreate(stop);
-        if (e != hipSuccess) hipEventDestroy(*start);
-    }
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipError_t e = hipSuccess;
+    if (g_pool.size() < 2) e = pool_fill();
     if (e != hipSuccess) {
-        std::lock_guard<std::mutex> lk(g_prof_mu);
         if (g_prof_err == hipSuccess) g_prof_err = e;
         *start = *stop = nullptr;
         return false;
     }
+    *stop = g_pool.back();
+    g_pool.pop_back();
+    *start = g_pool.back();
+    g_pool.pop_back();
     return true;
 }
 
@@ -217,7 +234,8 @@ dr_status dr_profile_begin(void) {
     g_err[0] = '\0';
     std::lock_guard<std::mutex> lk(g_prof_mu);
     prof_clear();
-    g_prof_err = hipSuccess;
+    g_prof_err = pool_fill();
+    if (g_prof_err != hipSuccess) return fail(DR_ERR_HIP, "profiling events: %s", hipGetErrorString(g_prof_err));
     g_prof_on.store(true);
     return DR_OK;
 }

@@ -389,7 +389,9 @@ dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
  * between the kernels); dr_profile_end waits for those events and reports the
  * summed kernel durations.  Calls made while profiling must come from one
  * host thread.  dr_profile_begin discards any earlier unreported records.  The
- * events are created and destroyed by the library.
+ * events belong to the library: dr_profile_begin creates a pool of 1024 (more
+ * only if a window needs them), and the library keeps them for reuse until
+ * the process ends, so that no event is created while kernels are timed.
  * Returns DR_ERR_NULL for a NULL report, DR_ERR_HIP if an event fails.
  */
 typedef struct dr_profile_report {
