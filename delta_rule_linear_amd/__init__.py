@@ -33,7 +33,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 8
+DR_ABI_VERSION = 9
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
@@ -44,7 +44,7 @@ EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "d
            "dr_decode_step_precond", "dr_status_str", "dr_last_error", "dr_abi_version",
            "dr_profile_begin", "dr_profile_end", "dr_chunk_bwd_workspace_bytes", "dr_chunk_bwd",
            "dr_chunk_bwd_kv", "dr_chunk_fwd_noalloc", "dr_chunk_fwd_kv_workspace_bytes",
-           "dr_chunk_bwd_kv_workspace_bytes")
+           "dr_chunk_bwd_kv_workspace_bytes", "dr_chunk_bwd_precond_workspace_bytes", "dr_chunk_bwd_precond")
 DR_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
@@ -119,6 +119,10 @@ def lib() -> ctypes.CDLL:
         L.dr_chunk_bwd.restype = ctypes.c_int
         L.dr_chunk_bwd_kv.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 17 + [ctypes.c_size_t, vp]
         L.dr_chunk_bwd_kv.restype = ctypes.c_int
+        L.dr_chunk_bwd_precond_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.dr_chunk_bwd_precond_workspace_bytes.restype = ctypes.c_size_t
+        L.dr_chunk_bwd_precond.argtypes = [ctypes.POINTER(ChunkDesc)] + [vp] * 17 + [ctypes.c_size_t, vp]
+        L.dr_chunk_bwd_precond.restype = ctypes.c_int
         L.dr_status_str.argtypes = [ctypes.c_int]
         L.dr_status_str.restype = ctypes.c_char_p
         L.dr_last_error.argtypes = []
@@ -358,9 +362,25 @@ def dr_chunk_bwd_kv(q, k, v, log_alpha, beta_k, beta_v, S0, dO, dS_final=None, *
                         beta_logit=beta_logit, _beta_v=beta_v)
 
 
+def dr_chunk_bwd_precond_workspace_bytes(desc: ChunkDesc) -> int:
+    return int(lib().dr_chunk_bwd_precond_workspace_bytes(ctypes.byref(desc)))
+
+
+def dr_chunk_bwd_precond(q, k, v, log_alpha, beta, key_scale, S0, dO, dS_final=None, *, gate: str,
+                         beta_mode: str = "scalar", want_dS0: bool = True, workspace=None, stream=None,
+                         qk_l2norm: bool = False, beta_logit: bool = False):
+    """Gradients of dr_chunk_fwd_precond (write-side key scales key_scale,
+    [B,H,L,Dk] fp32): as dr_chunk_bwd, with dkey_scale the scales' gradient."""
+    if key_scale is None:
+        raise ValueError("key_scale is required")
+    return dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final, gate=gate, beta_mode=beta_mode,
+                        want_dS0=want_dS0, workspace=workspace, stream=stream, qk_l2norm=qk_l2norm,
+                        beta_logit=beta_logit, _key_scale=key_scale)
+
+
 def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, beta_mode: str = "scalar",
                  want_dS0: bool = True, workspace=None, stream=None, qk_l2norm: bool = False,
-                 beta_logit: bool = False, _beta_v=None):
+                 beta_logit: bool = False, _beta_v=None, _key_scale=None):
     """Gradients of dr_chunk_fwd (any gate and beta mode) for the
     loss whose gradients with respect to o and S_final are dO [B,H,L,Dv] and
     dS_final [B,H,Dk,Dv] (fp32; dS_final None means zero).  q, k, v and the
@@ -386,6 +406,8 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
         _need(S0, "S0", torch.float32, (B, H, Dk, Dv))
     if _beta_v is not None:
         _need(_beta_v, "beta_v", torch.float32, bshape)
+    if _key_scale is not None:
+        _need(_key_scale, "key_scale", torch.float32, (B, H, L, Dk))
     _need(dO, "dO", torch.float32, (B, H, L, Dv))
     if dS_final is not None:
         _need(dS_final, "dS_final", torch.float32, (B, H, Dk, Dv))
@@ -397,11 +419,23 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
            "dS0": torch.empty((B, H, Dk, Dv), **f32) if want_dS0 else None}
     desc = chunk_desc(B, H, L, Dk, Dv, _dtype_code(q.dtype), DR_F32, gate, beta_mode,
                       input_flags(qk_l2norm, beta_logit))
-    nbytes = dr_chunk_bwd_workspace_bytes(desc) if _beta_v is None else dr_chunk_bwd_kv_workspace_bytes(desc)
+    if _key_scale is not None:
+        nbytes = dr_chunk_bwd_precond_workspace_bytes(desc)
+    elif _beta_v is not None:
+        nbytes = dr_chunk_bwd_kv_workspace_bytes(desc)
+    else:
+        nbytes = dr_chunk_bwd_workspace_bytes(desc)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if _beta_v is None:
+    if _key_scale is not None:
+        out["dkey_scale"] = torch.empty((B, H, L, Dk), **f32)
+        _check(lib().dr_chunk_bwd_precond(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                          _ptr(beta), _ptr(_key_scale), _ptr(S0), _ptr(dO), _ptr(dS_final),
+                                          _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                          _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dkey_scale"]),
+                                          _ptr(out["dS0"]), _ptr(workspace), wbytes, _stream(stream)))
+    elif _beta_v is None:
         _check(lib().dr_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                   _ptr(S0), _ptr(dO), _ptr(dS_final), _ptr(out["dq"]), _ptr(out["dk"]),
                                   _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]),

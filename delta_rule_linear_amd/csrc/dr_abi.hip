@@ -443,7 +443,7 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
 
 // ----------------------------------------------------------------- backward
 struct BwdLayout {
-    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, b32, db1, rq, rk, total;
+    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, b32, db1, rq, rk, dla, total;
 };
 
 // Whether a backward call runs on prepared fp32 copies of its inputs: a
@@ -457,7 +457,9 @@ bool bwd_copies(const dr_chunk_desc& d, bool kvtok) {
     return d.beta == DR_BETA_CHANNEL || kvtok || (d.input_flags & DR_IN_QK_L2NORM);
 }
 
-BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
+// precond: write-side key scales, which take the channel-gate kernels for
+// every gate mode
+BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = false) {
     BwdLayout w{};
     const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
     const size_t NCH = (size_t)d.B * d.H * NC;
@@ -471,7 +473,7 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
     w.T = take(NCH * dr::CH * dr::CH * f);
     w.Pm = take(NCH * dr::CH * dr::CH * f);
     w.A = take(NCH * dr::CH * dr::CH * f);
-    const bool cg = d.gate == DR_GATE_CHANNEL;
+    const bool cg = d.gate == DR_GATE_CHANNEL || precond;
     w.G = take(NCH * dr::CH * (cg ? d.Dk : 1) * f);
     w.S = take(NCH * d.Dk * d.Dv * f);
     w.H = take(NCH * d.Dk * d.Dv * f);
@@ -501,6 +503,8 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false) {
             w.rk = take(ntok * f);
         }
     }
+    if (precond && d.gate == DR_GATE_SCALAR)   // d log alpha per channel, summed per token at the end
+        w.dla = take((size_t)d.B * d.H * d.L * d.Dk * f);
     w.total = NCH ? off : 0;
     return w;
 }
@@ -517,11 +521,13 @@ dr_status check_bwd_desc(const dr_chunk_desc* d) {
 
 // beta_v and dbeta_v: the separate write strength and its gradient, or NULL
 // for one strength; kvtok: the two strengths hold one value per token
+// key_scale and dkey_scale (precond): the write-side key scales and their gradient
 dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v, const float* log_alpha,
                     const float* beta, const float* beta_v, const float* S0, const float* dO,
                     const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha, float* dbeta,
                     float* dbeta_v, float* dS0, void* workspace, size_t workspace_bytes, void* stream,
-                    bool kvtok = false) {
+                    bool kvtok = false, const float* key_scale = nullptr, float* dkey_scale = nullptr,
+                    bool precond = false) {
     dr_status s = check_bwd_desc(d);
     if (s != DR_OK) return s;
     if (kvtok && d->Dv != d->Dk)
@@ -538,14 +544,16 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
             return fail(DR_ERR_NULL, "log_alpha must be NULL exactly when gate is DR_GATE_NONE");
         if ((d->gate == DR_GATE_NONE) != (dlog_alpha == nullptr))
             return fail(DR_ERR_NULL, "dlog_alpha must be NULL exactly when gate is DR_GATE_NONE");
+        if (precond && (!key_scale || !dkey_scale))
+            return fail(DR_ERR_NULL, "key_scale and dkey_scale are required");
     }
     const void* ptrs[] = {q, k, v, log_alpha, beta, beta_v, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta,
-                          dbeta_v, dS0, workspace};
+                          dbeta_v, dS0, workspace, key_scale, dkey_scale};
     const char* names[] = {"q", "k", "v", "log_alpha", "beta", "beta_v", "S0", "dO", "dS_final", "dq", "dk", "dv",
-                           "dlog_alpha", "dbeta", "dbeta_v", "dS0", "workspace"};
-    for (int i = 0; i < 17; ++i)
+                           "dlog_alpha", "dbeta", "dbeta_v", "dS0", "workspace", "key_scale", "dkey_scale"};
+    for (int i = 0; i < 19; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const BwdLayout w = bwd_layout(*d, kvtok);
+    const BwdLayout w = bwd_layout(*d, kvtok, precond);
     {
         // the gradients are disjoint from every input, the workspace and each other
         const size_t ntok = nseq * (size_t)d->L;
@@ -556,15 +564,17 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
                             {v, ntok * d->Dv * inb, "v"},        {log_alpha, ntok * gw * 4, "log_alpha"},
                             {beta, ntok * bw * 4, "beta"},       {beta_v, ntok * bw * 4, "beta_v"},
                             {S0, sb, "S0"},                      {dO, ntok * d->Dv * 4, "dO"},
-                            {dS_final, sb, "dS_final"},          {workspace, w.total, "workspace"}};
+                            {dS_final, sb, "dS_final"},          {workspace, w.total, "workspace"},
+                            {key_scale, ntok * d->Dk * 4, "key_scale"}};
         const Span outs[] = {{dq, ntok * d->Dk * 4, "dq"},
                              {dk, ntok * d->Dk * 4, "dk"},
                              {dv, ntok * d->Dv * 4, "dv"},
                              {dlog_alpha, ntok * gw * 4, "dlog_alpha"},
                              {dbeta, ntok * bw * 4, "dbeta"},
                              {dbeta_v, ntok * bw * 4, "dbeta_v"},
-                             {dS0, sb, "dS0"}};
-        s = check_disjoint(outs, 7, ins, 10);
+                             {dS0, sb, "dS0"},
+                             {dkey_scale, ntok * d->Dk * 4, "dkey_scale"}};
+        s = check_disjoint(outs, 8, ins, 11);
         if (s != DR_OK) return s;
     }
     if (w.total) {
@@ -603,12 +613,18 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.wU = (float*)(ws + w.U);
     a.wR = (float*)(ws + w.R);
     a.wdU = (float*)(ws + w.dU);
-    a.cgate = d->gate == DR_GATE_CHANNEL;
+    a.cgate = d->gate == DR_GATE_CHANNEL || precond;
     if (a.cgate) {
         a.wQh = (float*)(ws + w.Qh);
         a.wKh = (float*)(ws + w.Kh);
         a.wKc = (float*)(ws + w.Kc);
         a.wKt = (float*)(ws + w.Kt);
+        a.gmode = d->gate == DR_GATE_CHANNEL ? 2 : d->gate == DR_GATE_SCALAR ? 1 : 0;
+        a.dla_cg = d->gate == DR_GATE_CHANNEL ? dlog_alpha : d->gate == DR_GATE_SCALAR ? (float*)(ws + w.dla) : nullptr;
+    }
+    if (precond) {
+        a.ks = key_scale;
+        a.dks = dkey_scale;
     }
     const bool cbeta = d->beta == DR_BETA_CHANNEL || kvtok;
     const bool mapped = bwd_mapped(*d, kvtok);
@@ -648,6 +664,10 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     }
     e = dr::launch_bwd(a, d->Dk, m.copy || d->in_dtype == DR_F32, st);
     if (e != hipSuccess) return fail(DR_ERR_HIP, "backward kernels launch: %s", hipGetErrorString(e));
+    if (precond && d->gate == DR_GATE_SCALAR) {
+        e = dr::launch_bwd_gate_sum(a.dla_cg, dlog_alpha, nseq * d->L, d->Dk, st);
+        if (e != hipSuccess) return fail(DR_ERR_HIP, "backward gate sum launch: %s", hipGetErrorString(e));
+    }
     if (mapped) {
         e = dr::launch_bwd_map_out(m, dq, dk, dv, dbeta, dbeta_v, st);
         if (e != hipSuccess) return fail(DR_ERR_HIP, "backward gradient mapping launch: %s", hipGetErrorString(e));
@@ -765,6 +785,21 @@ dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
     if (ntok && (!beta_v || !dbeta_v)) return fail(DR_ERR_NULL, "beta_v and dbeta_v are required");
     return chunk_bwd(d, q, k, v, log_alpha, beta_k, beta_v, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta_k,
                      dbeta_v, dS0, workspace, workspace_bytes, stream, d && d->beta == DR_BETA_SCALAR);
+}
+
+size_t dr_chunk_bwd_precond_workspace_bytes(const dr_chunk_desc* d) {
+    if (check_bwd_desc(d) != DR_OK) return 0;
+    return bwd_layout(*d, false, true).total;
+}
+
+dr_status dr_chunk_bwd_precond(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* key_scale, const float* S0,
+                               const float* dO, const float* dS_final, float* dq, float* dk, float* dv,
+                               float* dlog_alpha, float* dbeta, float* dkey_scale, float* dS0, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    g_err[0] = '\0';
+    return chunk_bwd(d, q, k, v, log_alpha, beta, nullptr, S0, dO, dS_final, dq, dk, dv, dlog_alpha, dbeta, nullptr,
+                     dS0, workspace, workspace_bytes, stream, false, key_scale, dkey_scale, true);
 }
 
 size_t dr_chunk_bwd_kv_workspace_bytes(const dr_chunk_desc* d) {

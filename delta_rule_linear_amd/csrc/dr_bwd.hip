@@ -1040,7 +1040,8 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     for (int e = tid; e < CH * DK / 4; e += NTH) {
         const int r = e / (DK / 4), c4 = (e % (DK / 4)) * 4;
         float4 x = {0.f, 0.f, 0.f, 0.f};
-        if (r < valid) x = *reinterpret_cast<const float4*>(a.log_alpha + (tok0 + r) * DK + c4);
+        if (r < valid && a.gmode == 2) x = *reinterpret_cast<const float4*>(a.log_alpha + (tok0 + r) * DK + c4);
+        if (r < valid && a.gmode == 1) x.x = x.y = x.z = x.w = a.log_alpha[tok0 + r];
         sG[r * KP + c4] = x.x;
         sG[r * KP + c4 + 1] = x.y;
         sG[r * KP + c4 + 2] = x.z;
@@ -1059,18 +1060,20 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     // past the end: zero operands)
     for (int e = tid; e < CH * DK / 8; e += NTH) {
         const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
-        float kx[8], qx[8], gq[8], gh[8], gc[8], gt[8], gg[8];
+        float kx[8], qx[8], gq[8], gh[8], gc[8], gt[8], gg[8], wx[8];
         load8<F32IN>(a.k, (tok0 + r) * DK + c8, r < valid, kx);
         load8<F32IN>(a.q, (tok0 + r) * DK + c8, r < valid, qx);
+        if (a.ks) load8<true>(a.ks, (tok0 + r) * DK + c8, r < valid, wx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float G = sG[r * KP + c8 + j], G63 = sG[(CH - 1) * KP + c8 + j];
             const float eg = expf(G), emg = expf(-G);
+            const float wk = a.ks ? wx[j] * kx[j] : kx[j];   // the write key
             gg[j] = G;
             gq[j] = qx[j] * eg;
             gh[j] = kx[j] * eg;
-            gc[j] = kx[j] * emg;
-            gt[j] = kx[j] * expf(G63 - G);
+            gc[j] = wk * emg;
+            gt[j] = wk * expf(G63 - G);
             sQh[r * KP + c8 + j] = gq[j];
             sKh[r * KP + c8 + j] = gh[j];
             sKc[r * KP + c8 + j] = gc[j];
@@ -1541,8 +1544,15 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
             sXg[r * KP + col] = xq * a.wQh[at] + xh * a.wKh[at] - xc * a.wKc[at];
             sYg[r * KP + col] = xt * a.wKt[at];
             if (r < valid) {
-                a.dq[(tok0 + r) * DK + col] = xq * eg;
-                a.dk[(tok0 + r) * DK + col] = xh * eg + xc * emg + xt * et;
+                const size_t e = (tok0 + r) * DK + col;
+                const float dw = xc * emg + xt * et;   // gradient of the write key
+                a.dq[e] = xq * eg;
+                if (a.ks) {
+                    a.dk[e] = xh * eg + a.ks[e] * dw;
+                    a.dks[e] = load1<F32IN>(a.k, e) * dw;
+                } else {
+                    a.dk[e] = xh * eg + dw;
+                }
             }
         }
     }
@@ -1572,7 +1582,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     for (int r = (part + 1) * RP - 1; r >= part * RP; --r) {
         sufX += sXg[r * KP + ch];
         sy += sYg[r * KP + ch];
-        if (r < valid) a.dlog_alpha[(tok0 + r) * DK + ch] = sufX + before + (py - sy) + hsc;
+        if (r < valid && a.dla_cg) a.dla_cg[(tok0 + r) * DK + ch] = sufX + before + (py - sy) + hsc;
     }
     if (w == 0 && l < valid) a.dbeta[tok0 + l] = sdb[l];
 }
@@ -1759,6 +1769,26 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// One wave per token: the sum of its DK per-channel values.
+__global__ __launch_bounds__(256) void bwd_gate_sum_kernel(const float* dla_ch, float* dla, size_t ntok, int dk) {
+    const int l = threadIdx.x & 63;
+    const size_t wv = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const size_t nw = ((size_t)gridDim.x * blockDim.x) >> 6;
+    for (size_t t = wv; t < ntok; t += nw) {
+        float x = 0.f;
+        for (int c = l; c < dk; c += 64) x += dla_ch[t * dk + c];
+        x = group_sum<32>(x);
+        x += __shfl_xor(x, 32);
+        if (l == 0) dla[t] = x;
+    }
+}
+
+hipError_t launch_bwd_gate_sum(const float* dla_ch, float* dla, size_t ntok, int dk, hipStream_t st) {
+    if (ntok == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<size_t>((ntok + 3) / 4, 4096);
+    return launch_k(kProfNone, bwd_gate_sum_kernel, dim3(blocks), dim3(256), 0, st, dla_ch, dla, ntok, dk);
+}
 
 static unsigned map_blocks(const BwdMap& m) {
     const size_t per_block = 4 * (size_t)(256 / m.Dk);   // tokens per step of a 256-thread block

@@ -136,6 +136,15 @@ struct BwdArgs {
     float* wKh;
     float* wKc;
     float* wKt;
+    // channel-gate kernels only: gmode 2 reads log alpha per channel, 1 one
+    // value per token (broadcast to every channel), 0 none; the per-channel
+    // d log alpha goes to dla_cg (NULL: not written)
+    int gmode;
+    float* dla_cg;
+    // write-side key scales (NULL: none): the write key is ks (.) k, on the
+    // column side of A and P and in the state update; dks its gradient
+    const float* ks;
+    float* dks;
 };
 
 // Optional per-kernel timing (dr_profile_begin / dr_profile_end).  While it is
@@ -202,6 +211,9 @@ struct BwdMap {
     float* rk;
 };
 hipError_t launch_bwd_map_in(const BwdMap& m, hipStream_t st);
+// dla[t] = sum over the DK channels of dla_ch[t][.] (a scalar gate through the
+// channel-gate kernels)
+hipError_t launch_bwd_gate_sum(const float* dla_ch, float* dla, size_t ntok, int dk, hipStream_t st);
 // dq, dk, dv (and dbeta for a scalar beta) hold the copies' gradients on entry
 hipError_t launch_bwd_map_out(const BwdMap& m, float* dq, float* dk, float* dv, float* dbeta, float* dbeta_v,
                               hipStream_t st);

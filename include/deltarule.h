@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 8
+#define DR_ABI_VERSION 9
 
 typedef enum {
     DR_OK = 0,
@@ -380,6 +380,36 @@ dr_status dr_chunk_bwd_kv(const dr_chunk_desc* d, const void* q, const void* k, 
                           const float* dO, const float* dS_final, float* dq, float* dk, float* dv,
                           float* dlog_alpha, float* dbeta_k, float* dbeta_v, float* dS0, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace dr_chunk_bwd_precond needs for `d` (0 if d is
+ * invalid for it or there is no work): that of the channel-gate backward for
+ * every gate mode, plus Dk floats per token with a scalar gate. */
+size_t dr_chunk_bwd_precond_workspace_bytes(const dr_chunk_desc* d);
+
+/*
+ * dr_chunk_bwd_precond -- dr_chunk_bwd for dr_chunk_fwd_precond: gradients of
+ * the preconditioned rule, write key w_t = s_t (.) kt (OSDN page, "Method";
+ * the reading of dr_chunk_fwd_precond).  In the chunk algebra w takes kt's
+ * place on the column side of A and P and in the state update, and the read
+ * side keeps kt, so the gradient of kt gathers both roles:
+ * dk = dk_read + s (.) dw and ds = kt (.) dw (through the input preparation
+ * and sqrt(beta) as in dr_chunk_bwd).  Every gate mode runs the channel-gate
+ * kernels, a scalar or absent gate broadcast to every channel (the same limit
+ * on each channel's cumulative log decay within a chunk applies); with a
+ * scalar gate, d log alpha is summed over the channels at the end.
+ *
+ *   key_scale   [B][H][L][Dk] fp32, the diagonal s_t
+ *   dkey_scale  [B][H][L][Dk] fp32, written
+ *   workspace   at least dr_chunk_bwd_precond_workspace_bytes(d) bytes
+ * Every other argument, the modes (every gate and beta mode, input_flags) and
+ * the error behaviour are those of dr_chunk_bwd; key_scale and dkey_scale are
+ * required when there are tokens.
+ */
+dr_status dr_chunk_bwd_precond(const dr_chunk_desc* d, const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const float* key_scale, const float* S0,
+                               const float* dO, const float* dS_final, float* dq, float* dk, float* dv,
+                               float* dlog_alpha, float* dbeta, float* dkey_scale, float* dS0, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * Per-kernel timing, for benchmarks and profiling (not part of the method).

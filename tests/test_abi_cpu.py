@@ -332,6 +332,35 @@ def test_backward_kv_validation():
     assert call(_desc(beta_mode="channel", B=0), bv=None, dbv=None) == drl.DR_OK
 
 
+def test_backward_precond_validation():
+    lib = drl.lib()
+
+    def call(desc, ks=F(8), dks=F(17), wbytes=1 << 40):
+        return lib.dr_chunk_bwd_precond(ctypes.byref(desc) if desc is not None else None, F(0), F(1), F(2), F(3),
+                                        F(4), ks, None, F(11), None, F(12), F(14), F(15), F(13), F(16), dks, None,
+                                        F(7), wbytes, None)
+
+    d = _desc()
+    assert call(None) == drl.DR_ERR_NULL
+    assert call(d, ks=None) == drl.DR_ERR_NULL
+    assert call(d, dks=None) == drl.DR_ERR_NULL
+    assert call(d, ks=FAKE_MISALIGNED) == drl.DR_ERR_ALIGN
+    assert call(d, dks=F(8)) == drl.DR_ERR_UNSUPPORTED               # the scales' gradient over the scales
+    assert "dkey_scale overlaps key_scale" in drl.dr_last_error()
+    assert call(_desc(flags=4)) == drl.DR_ERR_UNSUPPORTED
+    # every gate mode runs the channel-gate kernels: their gated planes, and with
+    # a scalar gate one more fp32 plane of per-channel d log alpha
+    ntok = 2 * 3 * 100
+    cg = drl.dr_chunk_bwd_workspace_bytes(_desc(gate="channel"))
+    sc = drl.dr_chunk_bwd_precond_workspace_bytes(_desc())
+    assert drl.dr_chunk_bwd_precond_workspace_bytes(_desc(gate="channel")) == cg
+    assert drl.dr_chunk_bwd_precond_workspace_bytes(_desc(gate="none")) == cg
+    assert sc >= cg + ntok * 128 * 4
+    assert call(d, wbytes=sc - 1) == drl.DR_ERR_WORKSPACE
+    assert drl.dr_chunk_bwd_precond_workspace_bytes(_desc(L=0)) == 0
+    assert lib.dr_chunk_bwd_precond(ctypes.byref(_desc(B=0)), *([None] * 17), 0, None) == drl.DR_OK
+
+
 def test_noalloc_validation():
     # host-side checks of the allocation-free forward: bad descriptors, and a
     # call whose workspace exceeds the scratch array, return before any device work

@@ -338,3 +338,88 @@ def test_backward_input_preparation_full_size_every_sequence():
     _every_sequence(p.name, g, ref, GRADS)
     del g, ref
     torch.cuda.empty_cache()
+
+
+def _check_precond(p, seed=0, tol=None):
+    """dr_chunk_bwd_precond against the oracle's gradients of the
+    preconditioned rule, dkey_scale included."""
+    import delta_rule_linear_amd as drl
+    announce("backward precond", p.name, p.B, p.H, p.L, p.Dk, p.Dv, p.in_dtype, p.gate, p.beta_mode,
+             p.qk_l2norm, p.beta_logit)
+    dO, dSf = inputs.backward_cotangents(p, seed)
+    t = problem_to_dev(p)
+    flags = dict(qk_l2norm=p.qk_l2norm, beta_logit=p.beta_logit)
+    g = drl.dr_chunk_bwd_precond(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["key_scale"], t["S0"],
+                                 to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode, **flags)
+    torch.cuda.synchronize()
+    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode=p.beta_mode,
+                          key_scale=p.key_scale, **flags)
+    tol = TOL[p.in_dtype] if tol is None else tol
+    errs = {n: rel_err(to_np(g[n]), ref[n]) for n in GRADS + ("dkey_scale",) if ref.get(n) is not None}
+    assert set(errs) >= {"dq", "dk", "dv", "dbeta", "dS0", "dkey_scale"}
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"{p.name}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()) + f" (tol {tol:.0e})"
+    return g, ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta_mode", ["scalar", "channel"])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+@pytest.mark.parametrize("L", [1, 65, 200])
+def test_backward_precond_sweep(L, gate, beta_mode, dtype):
+    # OSDN page, "Method": the write-side key w = s (.) kt; every gate mode
+    # runs the channel-gate kernels (a scalar or absent gate broadcast)
+    rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
+    D = 128 if dtype == "bf16" else 64
+    p = inputs.make_chunk_problem(2, 2, L, D, D, in_dtype=dtype, gate=gate, beta_mode=beta_mode, s0_var=0.01,
+                                  seed=L + D + 31, log_alpha_range=rng, key_scale=True,
+                                  name=f"bwd_precond_{gate}_{beta_mode}_{dtype}")
+    _check_precond(p, seed=L + 5)
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
+def test_backward_precond_input_preparation(gate):
+    # raw q, k and strength logits with key scales: the normalisation and the
+    # sigmoid in front of the preconditioned rule
+    rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
+    p = inputs.make_chunk_problem(1, 3, 150, 128, 128, in_dtype="bf16", gate=gate, s0_var=0.01, seed=41,
+                                  log_alpha_range=rng, raw_inputs=True, key_scale=True,
+                                  name=f"bwd_precond_prep_{gate}")
+    _check_precond(p, seed=6)
+
+
+def test_backward_precond_unit_scales_match_plain():
+    # s = 1 is the unscaled rule: the same gradients as dr_chunk_bwd, and
+    # dkey_scale = k (.) (the write key's gradient)
+    import delta_rule_linear_amd as drl
+    p = inputs.make_chunk_problem(1, 2, 130, 128, 128, in_dtype="bf16", gate="channel", s0_var=0.01, seed=43,
+                                  log_alpha_range=inputs.KDA_GATE, key_scale=True, name="bwd_precond_unit")
+    p.key_scale[:] = 1.0
+    g, ref = _check_precond(p, seed=7)
+    plain = run_bwd(p, *inputs.backward_cotangents(p, 7))
+    for n in GRADS:
+        assert rel_err(to_np(g[n]), to_np(plain[n])) <= 1e-5, n
+
+
+def test_backward_precond_value_width():
+    p = inputs.make_chunk_problem(1, 2, 130, 128, 48, in_dtype="f32", gate="scalar", s0_var=0.01, seed=47,
+                                  log_alpha_range=inputs.GDN_GATE, key_scale=True, name="bwd_precond_dv48")
+    _check_precond(p, seed=8)
+
+
+@pytest.mark.timeout(900)
+def test_backward_precond_full_size_every_sequence():
+    # the headline GDN shape with write-side key scales U(0.5, 1.5), every sequence
+    import delta_rule_linear_amd as drl
+    p = inputs.workload("gdn_precond_b2h16_16k")
+    announce("backward precond full size", p.name)
+    dO, dSf = inputs.backward_cotangents(p, 0)
+    t = problem_to_dev(p)
+    g = drl.dr_chunk_bwd_precond(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["key_scale"], t["S0"],
+                                 to_dev(dO, "f32"), to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode)
+    torch.cuda.synchronize()
+    ref = oracle.backward(p.q, p.k, p.v, p.log_alpha, p.beta, p.S0, dO, dSf, gate=p.gate, beta_mode=p.beta_mode,
+                          key_scale=p.key_scale)
+    _every_sequence(p.name, g, ref, GRADS + ("dkey_scale",))
+    del g, ref
+    torch.cuda.empty_cache()
