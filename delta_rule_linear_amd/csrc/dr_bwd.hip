@@ -997,8 +997,17 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
 // per element dq = dQ^ e^G, dk = dK^ e^G + dKc e^-G + dK~ e^(G_63 - G),
 // dG = dQ^ Q^ + dK^ K^ - dKc Kc - dK~ K~, plus at the last row the sums of
 // dK~ K~ over the chunk and e^G_63 <H_c, S_c>; d log alpha is dG's reverse
-// cumulative sum per channel.  e^-G needs the within-chunk cumulative log
-// decay of every channel to stay above about -88 (fp32 range).
+// cumulative sum per channel.
+//
+// Strong decays.  e^-G overflows fp32 once a channel's decay over the chunk,
+// G_63, falls below about -88.  A chunk in which some channel's G_63 is below
+// kShiftBelow takes shifted operands for its 64 x 64 products instead: with
+// the per-channel reference G_m = G_63 / 2, the products run on
+// Q o e^(G - G_m), K o e^(G - G_m) and Kc o e^(G_m) = K o e^(G_m - G), every
+// factor within e^(|G_63| / 2), and the per-element step applies e^(G - G_m)
+// or e^(G_m - G) to their terms (the state-sized terms keep e^G).  That holds
+// a chunk's decay down to about -170 in every channel (an average log alpha of
+// about -2.7 per token).  The other chunks keep the unshifted arithmetic.
 
 // A [64][DK] fp32 workspace plane straight into LDS rows of pitch DK + 1.
 template <int DK, int NT>
@@ -1014,6 +1023,8 @@ __device__ __forceinline__ void load_plane(float* dst, const float* src, int tid
     }
 }
 
+constexpr float kShiftBelow = -60.f;
+
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     constexpr int KP = DK + 1;
@@ -1022,6 +1033,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     __shared__ float sG[CH * KP];        // log alpha, then its cumulative sums
     __shared__ float sX[4][16 * 17];
     __shared__ float sb[CH];
+    __shared__ int s_shift;
     float* sKh = sOp;
     float* sKc = sOp + CH * KP;
     float* sQh = sOp + 2 * CH * KP;
@@ -1035,6 +1047,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     const size_t mo = (size_t)cs * CH * CH, po = (size_t)cs * CH * DK;
 
     if (tid < CH) sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
+    if (tid == 0) s_shift = 0;
     // log alpha rows into LDS (zeros past the end: no decay), then each
     // channel's cumulative sum in place
     for (int e = tid; e < CH * DK / 4; e += NTH) {
@@ -1054,10 +1067,13 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
             G += sG[r * KP + ch];
             sG[r * KP + ch] = G;
         }
+        if (G < kShiftBelow) s_shift = 1;
     }
     lds_barrier();
+    const bool shift = s_shift != 0;   // workgroup-uniform
     // the gated operands, eight channels of one row per thread and step (rows
-    // past the end: zero operands)
+    // past the end: zero operands); with shift the 64 x 64 products take them
+    // relative to G_m = G_63 / 2 (Kc's workspace plane too)
     for (int e = tid; e < CH * DK / 8; e += NTH) {
         const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
         float kx[8], qx[8], gq[8], gh[8], gc[8], gt[8], gg[8], wx[8];
@@ -1067,15 +1083,17 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const float G = sG[r * KP + c8 + j], G63 = sG[(CH - 1) * KP + c8 + j];
-            const float eg = expf(G), emg = expf(-G);
+            const float Gm = shift ? 0.5f * G63 : 0.f;
+            const float eg = expf(G), emg = expf(Gm - G);
             const float wk = a.ks ? wx[j] * kx[j] : kx[j];   // the write key
             gg[j] = G;
             gq[j] = qx[j] * eg;
             gh[j] = kx[j] * eg;
             gc[j] = wk * emg;
             gt[j] = wk * expf(G63 - G);
-            sQh[r * KP + c8 + j] = gq[j];
-            sKh[r * KP + c8 + j] = gh[j];
+            const float es = shift ? expf(G - Gm) : eg;
+            sQh[r * KP + c8 + j] = qx[j] * es;
+            sKh[r * KP + c8 + j] = kx[j] * es;
             sKc[r * KP + c8 + j] = gc[j];
         }
         const size_t at = po + (size_t)r * DK + c8;
@@ -1390,6 +1408,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     __shared__ float sM3[CH * PT];   // N = lower dP
     __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
     __shared__ float sb[CH], sdb[CH], shs[DK];
+    __shared__ int s_shift;
     const int cs = blockIdx.x;
     const int seq = cs / a.NC, c = cs - seq * a.NC;
     const int t0 = c * CH, valid = min(CH, a.L - t0);
@@ -1403,6 +1422,17 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
         sdb[tid] = 0.f;
     }
     if (tid < DK) shs[tid] = 0.f;
+    if (tid == 0) s_shift = 0;
+    // shifted operands, as the preparation kernel chose them for this chunk
+    // (rows of a chunk operand relative to G_m = G_63 / 2)
+    auto shifted_rows = [&](float* dst, const void* src) {
+        for (int e = tid; e < CH * DK; e += PNT) {
+            const int r = e / DK, cc = e % DK;
+            const float G = a.wG[pofs + (size_t)r * DK + cc], G63 = a.wG[pofs + (size_t)(CH - 1) * DK + cc];
+            const float x = r < valid ? load1<F32IN>(src, (tok0 + r) * DK + cc) : 0.f;
+            dst[r * KP + cc] = x * expf(G - 0.5f * G63);
+        }
+    };
 
     RowsPre<DK, F32IN, PNT> pk, pq;   // not used with a channel gate
     MatPre<PNT> pt, pp, pa;
@@ -1415,22 +1445,43 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     // ---- Kc and Q^ rows, T and K^ Kc^T
     float* sKx = s1;             // Kc, later K^
     float* sQh = s1 + CH * KP;
+    if (tid < DK && a.wG[pofs + (size_t)(CH - 1) * DK + tid] < kShiftBelow) s_shift = 1;
     put_plane(pkc, sKx, tid);
     put_plane(pqh, sQh, tid);
     put_mat(pt, sM0, tid);
     put_mat(pa, sM2, tid);
     lds_barrier();
+    const bool shift = s_shift != 0;   // workgroup-uniform
+    if (shift) {
+        shifted_rows(sQh, a.q);
+        lds_barrier();
+    }
 
     const int rb = 16 * R + 4 * g;   // this lane's first accumulator row
     float rowb[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};
-    // state terms: dQ^ = z1, dK^ = -z2, dK~ = z3; dKc from the 64 x 64 part
+    // state terms: dQ^ = z1, dK^ = -z2, dK~ = z3; dKc from the 64 x 64 part.
+    // With shift the 64 x 64 terms accumulate on their own; the state terms'
+    // share of dq and dk (z1 e^G, -z2 e^G) is stored now and completed below
+    // by the same lanes.
     f32x4 dqh[NDH], dkh[NDH], dkc[NDH], dkt[NDH];
 #pragma unroll
     for (int D = 0; D < NDH; ++D) {
-        dqh[D] = z1[D];
-        dkh[D] = -z2[D];
+        dqh[D] = shift ? zero4() : z1[D];
+        dkh[D] = shift ? zero4() : -z2[D];
         dkt[D] = z3[D];
         dkc[D] = zero4();
+        if (shift) {
+            const int col = 16 * (D0 + D) + i16;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = rb + j;
+                if (r < valid) {
+                    const float eg = expf(a.wG[pofs + (size_t)r * DK + col]);
+                    a.dq[(tok0 + r) * DK + col] = z1[D][j] * eg;
+                    a.dk[(tok0 + r) * DK + col] = -z2[D][j] * eg;
+                }
+            }
+        }
     }
     // hf 0: N = lower dP; hf 1: dT = dT^ Diag(beta) and dbeta's sums of dT^ o T
 #pragma unroll
@@ -1503,7 +1554,8 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
         }
     }
     lds_barrier();
-    load_plane<DK, PNT>(sKx, a.wKh + pofs, tid);   // K^ in place of Kc
+    if (shift) shifted_rows(sKx, a.k);   // K^, shifted, in place of Kc
+    else load_plane<DK, PNT>(sKx, a.wKh + pofs, tid);   // K^ in place of Kc
     lds_barrier();
     // dKc += M^T K^
 #pragma unroll
@@ -1530,6 +1582,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     //   X = dQ^ Q^ + dK^ K^ - dKc Kc,  Y = dK~ K~  (dG = X - Y, plus the last row's sums)
     float* sXg = s1;
     float* sYg = s1 + CH * KP;
+    if (shift) __threadfence_block();   // the partial dq, dk stores above, read back by the same lanes
 #pragma unroll
     for (int D = 0; D < NDH; ++D) {
         const int col = 16 * (D0 + D) + i16;
@@ -1539,8 +1592,30 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
             const int r = rb + j;
             const size_t at = pofs + (size_t)r * DK + col;
             const float G = a.wG[at];
-            const float eg = expf(G), emg = expf(-G), et = expf(G63 - G);
             const float xq = dqh[D][j], xh = dkh[D][j], xc = dkc[D][j], xt = dkt[D][j];
+            const float et = expf(G63 - G);
+            if (shift) {
+                // every term relative to G_m: dq = z1 e^G + xq e^(G - G_m),
+                // dk_read likewise, Kc's term e^(G_m - G); X and Y from the
+                // inputs and the complete gradients
+                const float Gm = 0.5f * G63, es = expf(G - Gm), ems = expf(Gm - G);
+                const size_t e = (tok0 + r) * DK + col;
+                const bool ok = r < valid;
+                const float qv = ok ? load1<F32IN>(a.q, e) : 0.f, kv = ok ? load1<F32IN>(a.k, e) : 0.f;
+                const float sv = (a.ks && ok) ? a.ks[e] : 1.f;
+                const float dqt = (ok ? a.dq[e] : 0.f) + xq * es;
+                const float dkr = (ok ? a.dk[e] : 0.f) + xh * es;
+                const float dwc = xc * ems, dwt = xt * et, wv = sv * kv;
+                sXg[r * KP + col] = dqt * qv + dkr * kv - dwc * wv;
+                sYg[r * KP + col] = dwt * wv;
+                if (ok) {
+                    a.dq[e] = dqt;
+                    a.dk[e] = dkr + sv * (dwc + dwt);
+                    if (a.ks) a.dks[e] = kv * (dwc + dwt);
+                }
+                continue;
+            }
+            const float eg = expf(G), emg = expf(-G);
             sXg[r * KP + col] = xq * a.wQh[at] + xh * a.wKh[at] - xc * a.wKc[at];
             sYg[r * KP + col] = xt * a.wKt[at];
             if (r < valid) {

@@ -331,8 +331,10 @@ size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
  * no derivative at 0; logits always satisfy it).  in_dtype (fp32 or bf16) is the dtype
  * of q, k, v; Dk, Dv as for dr_chunk_fwd.  With DR_GATE_CHANNEL the kernels
  * work on keys and queries scaled by e^{+-G}, G a channel's cumulative log
- * decay within a 64-token chunk, so each G must stay above about -80 (fp32
- * range; not checked): log alpha of -1 per token is well inside.
+ * decay within a 64-token chunk; a chunk in which some channel's decay falls
+ * below -60 takes those products relative to the channel's mid-chunk decay,
+ * so every channel's decay over a chunk must stay above about -170 (an
+ * average log alpha of about -2.7 per token; not checked).
  *
  *   q, k, v, log_alpha, beta, S0   as for dr_chunk_fwd (S0 may be NULL: zeros)
  *   dO         [B][H][L][Dv] fp32, gradient with respect to o

@@ -108,6 +108,29 @@ def test_backward_channel_gate_strong_decay():
     _check(p)
 
 
+@pytest.mark.parametrize("mode", ["kda", "fg2", "kv", "precond_channel", "precond_scalar"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("la", [(-3.0, -0.5), (-1.6, -0.3)])
+def test_backward_strong_channel_decay(la, dtype, mode):
+    # log alpha in (-3, -0.5): a chunk's decay reaches about -110 in every
+    # channel, past e^-G's fp32 range, so every chunk takes the shifted
+    # operands; (-1.6, -0.3) puts chunks on both sides of the switch
+    import delta_rule_linear_amd as drl
+    bm = "channel" if mode in ("fg2", "kv") else "scalar"
+    gate = "scalar" if mode == "precond_scalar" else "channel"
+    p = inputs.make_chunk_problem(2, 2, 200, 128, 128, in_dtype=dtype, gate=gate, beta_mode=bm, s0_var=0.01,
+                                  log_alpha_range=la, seed=53, beta_v=mode == "kv",
+                                  key_scale=mode.startswith("precond"), name=f"bwd_strong_{mode}_{dtype}")
+    # the first chunk's decay, below the switch at -60 in some channel
+    assert p.log_alpha[:, :, :64].astype(np.float64).sum(axis=2).min() < -60
+    if mode.startswith("precond"):
+        _check_precond(p, seed=9)
+    elif mode == "kv":
+        _check_kv(p, seed=9)
+    else:
+        _check(p, seed=9)
+
+
 @pytest.mark.parametrize("Dv", [16, 48, 256])
 def test_backward_value_width(Dv):
     p = inputs.make_chunk_problem(1, 2, 130, 128, Dv, in_dtype="f32", gate="scalar", s0_var=0.01, seed=Dv,
