@@ -8,10 +8,13 @@ A step is one dr_chunk_fwd over the headline batch: Gated DeltaNet gating
 L2-normalised, bf16 q/k/v, fp32 S0 ~ N(0, 0.01), fp32 output), B=2, H=16,
 L=16384, d_k=d_v=128.  `value` is tokens/s of that step (B*L per step), from
 HIP events around each step on the launch stream; between steps (outside the
-timed events) a 512 MiB buffer is rewritten so that no input is served from
-the 256 MB last-level cache.  Before the W warm-up steps the step runs
-untimed for --warmup-seconds, so that a fresh GPU has reached its steady
-clocks.
+timed events) a 512 MiB buffer is read through, so that no input is served
+from the 256 MB last-level cache and no dirty line of anything but the step
+itself is left to write back inside the timed events (rewriting the buffer
+instead leaves it dirty in the cache, and the step's first kernel then pays
+for its write-back: that figure is reported as ms_per_step_after_write_flush).
+Before the W warm-up steps the step runs untimed for --warmup-seconds, so that
+a fresh GPU has reached its steady clocks.
 
 Also reported in the same line:
   roofline      the dominant kernel (the state scan) against HBM bandwidth:
@@ -111,7 +114,7 @@ def parse():
                     help="timed steps per extra workload (0 skips them)")
     ap.add_argument("--bwd-steps", type=int, default=5,
                     help="timed steps of the backward on the headline batch (0 skips it)")
-    ap.add_argument("--no-flush", action="store_true", help="do not rewrite the 512 MiB buffer between steps")
+    ap.add_argument("--no-flush", action="store_true", help="do not read through the 512 MiB buffer between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -162,20 +165,29 @@ def main():
     torch.cuda.set_device(dev)
     drl.lib()
     stream = torch.cuda.current_stream()
-    flush_buf = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush_buf = None if args.no_flush else torch.ones(64 << 20, dtype=torch.int64, device=dev)   # 512 MiB
+    flush_sum = torch.empty((), dtype=torch.int64, device=dev)
 
     def flush():
+        """Read the 512 MiB buffer through (a sum into one value): the inputs
+        leave the caches, which then hold clean lines only."""
+        if flush_buf is not None:
+            torch.sum(flush_buf, dim=0, out=flush_sum)
+
+    def write_flush():
         if flush_buf is not None:
             flush_buf.fill_(1)
 
-    def time_steps(fn, steps, warmup):
-        """Per-step event times (ms), the cache rewritten between steps."""
+    def time_steps(fn, steps, warmup, pre=None):
+        """Per-step event times (ms), the cache flushed between steps (pre:
+        another flush)."""
+        pre = pre or flush
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for e0, e1 in ev:
-            flush()
+            pre()
             e0.record(stream)
             fn()
             e1.record(stream)
@@ -223,8 +235,8 @@ def main():
                          workspace=ws)
 
     # untimed: the step repeated for --warmup-seconds, each after a cache
-    # rewrite like the timed ones (a fresh GPU needs this sustained load, cache
-    # rewrites included, before its step times settle), then --warmup steps
+    # flush like the timed ones (a fresh GPU needs this sustained load before
+    # its step times settle), then --warmup steps
     t_warm = time.perf_counter()
     while time.perf_counter() - t_warm < args.warmup_seconds:
         for _ in range(20):
@@ -240,6 +252,14 @@ def main():
     per = time_steps(step, args.steps, 0)
     wall = time.perf_counter() - t_wall
     ms = float(np.median(per))
+    # the same steps after a rewrite of the buffer instead (its dirty lines
+    # are written back during the step), for comparison
+    ms_wflush = None
+    if flush_buf is not None:
+        for _ in range(30):   # untimed: the step times settle after a change of flush pattern
+            write_flush()
+            step()
+        ms_wflush = float(np.median(time_steps(step, args.steps, 0, pre=write_flush)))
     tok_s = B * L / (ms * 1e-3)
     token_heads = B * H * L
     alg_flops = flops_per_token_head(D) * token_heads
@@ -628,6 +648,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_after_write_flush": None if ms_wflush is None else round(ms_wflush, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
