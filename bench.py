@@ -37,8 +37,9 @@ Also reported in the same line:
   backward      dr_chunk_bwd on the headline batch (seeded dO and dS_final),
                 per-kernel times, the dominant kernel against the fp32
                 matrix-core peak, and the CPU oracle's backward on 4 heads;
-                also the backward at the KDA shape (channel gate) and the
-                FG2-GDN shape (channel gate and beta);
+                also the backward at the KDA shape (channel gate), the
+                FG2-GDN shape (channel gate and beta) and the headline
+                batch with write-side key scales;
   cpu_baseline  the fp64 CPU oracle on the whole headline batch, on the
                 host's cores, with the GPU result checked against it, and on
                 one core for one head; the CPU model.
@@ -563,6 +564,31 @@ def main():
                 errs[n] = float(np.abs(x - ref[n]).max() / np.abs(ref[n]).max())
             bwd["parity"] = {"heads": nh, "max_rel_err": errs, "tol": 3e-3}
             del ref
+        # the headline batch with write-side key scales U(0.5, 1.5): the
+        # preconditioned rule's backward (channel-gate kernels, the scalar gate
+        # broadcast)
+        gen.manual_seed(1)
+        ksc = torch.rand((B, H, L, D), generator=gen, device=dev) + 0.5
+        pdesc = drl.chunk_desc(B, H, L, D, D, drl.DR_BF16, drl.DR_F32, "scalar", "scalar")
+        pws = torch.empty(drl.dr_chunk_bwd_precond_workspace_bytes(pdesc), dtype=torch.uint8, device=dev)
+
+        def pstep():
+            drl.dr_chunk_bwd_precond(q, k, v, la, be, ksc, S0, gdO, gdSf, gate="scalar", workspace=pws)
+
+        for _ in range(2):
+            pstep()
+        torch.cuda.synchronize()
+        pper = time_steps(pstep, args.bwd_steps, 0)
+        pms = float(np.median(pper))
+        pprof = kernel_pass(pstep, args.bwd_steps, pms)
+        pcalls = max(1, pprof["bwd_calls"])
+        bwd["gdn_precond_b2h16_16k"] = {
+            "shape": f"B={B} H={H} L={L} d={D}, scalar gate and beta, write-side key scales, bf16 q/k/v",
+            "ms_per_step": round(pms, 4), "tokens_per_s": round(B * L / (pms * 1e-3), 1),
+            "kernels_ms": {n: round(pprof[f"bwd_{n}_ms"] / pcalls, 4) for n in ("prep", "fscan", "rscan", "post")},
+            "workspace_bytes": int(pws.numel())}
+        del ksc, pws
+        torch.cuda.empty_cache()
         del gdO, gdSf, bws, grads
         torch.cuda.empty_cache()
         # the KDA shape (channel gate) and the FG2-GDN shape (channel gate and
