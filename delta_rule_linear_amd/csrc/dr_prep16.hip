@@ -79,12 +79,16 @@ __device__ __forceinline__ void dma_tile(const uint16_t* src, size_t pitch, int 
 
 }  // namespace
 
-// LDS plan (bytes): k tile, q tile, gates.  A (fp32, its ten lower 16 x 16
-// blocks packed with a row pitch of 17), T (fp32) and the per-wave 16 x 16
-// scratch of the triangular solve reuse the k / q tiles, which are dead once
-// A and P are formed (the waves hold their A blocks in registers until then);
-// at d = 64 the tiles are too small and A, T and the scratch follow them.  P
-// goes straight to the workspace.  33 KB at d = 128: four workgroups per CU.
+// LDS plan (bytes): k tile, q tile.  A (fp32, its ten lower 16 x 16 blocks
+// packed with a row pitch of 17), T (fp32), the per-wave 16 x 16 scratch of
+// the triangular solve and the chunk's strengths reuse the k / q tiles, which
+// are dead once A and P are formed (the waves hold their A blocks in
+// registers until then); at d = 64 the tiles are too small and A, T and the
+// scratch follow them.  P goes straight to the workspace.  The gates live in
+// registers (every wave forms the chunk's prefix sums itself); only with the
+// input preparation are 1/|q_r| and 1/|k_r| exchanged through LDS, after the
+// tiles.  32 KB at d = 128 (five workgroups per CU), 32.5 KB with the input
+// preparation (four).
 template <int DK>
 struct P16 {
     static constexpr int RB = DK * 2;
@@ -98,11 +102,14 @@ struct P16 {
     static constexpr int SA = ALIAS ? KT : QT + 64 * RB;
     static constexpr int ST = SA + ABYTES;
     static constexpr int SX = ST + 64 * AP * 4;   // [4][16][17] fp32
-    static constexpr int SG = ALIAS ? QT + 64 * RB : SX + 4 * 16 * 17 * 4;   // G, beta, 1/|q|, 1/|k| [64] each
-    static constexpr int TOTAL = SG + 256 * 4;
+    static constexpr int SB = ALIAS ? TXA : SX + 4 * 16 * 17 * 4;       // beta [64], once the tiles are dead
+    static constexpr int SN = ALIAS ? QT + 64 * RB : SB + 64 * 4;         // 1/|q|, 1/|k| [64] each
+    static constexpr int TOTAL = ALIAS ? 2 * 64 * RB : SN;
+    static constexpr int TOTAL_QN = SN + 128 * 4;
+    static_assert(!ALIAS || TXA + 64 * 4 <= 2 * 64 * RB, "beta fits beside A, T and the scratch");
 };
 
-template <int DK>
+template <int DK, bool QN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void prep16_kernel(ChunkArgs a) {
     using L = P16<DK>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -112,10 +119,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         return sAp[tri_block(r >> 4, c >> 4) * L::AB + (r & 15) * 17 + (c & 15)];
     };
     float(*sT)[L::AP] = reinterpret_cast<float(*)[L::AP]>(smem + L::ST);
-    float* sg = reinterpret_cast<float*>(smem + L::SG);
-    float* sb = sg + 64;
-    float* snq = sg + 128;   // 1 / |q_r| (input preparation)
-    float* snk = sg + 192;   // 1 / |k_r|
+    float* sb = reinterpret_cast<float*>(smem + L::SB);    // beta, written once the tiles are dead
+    float* snq = reinterpret_cast<float*>(smem + L::SN);   // 1 / |q_r| (input preparation)
+    float* snk = snq + 64;                                 // 1 / |k_r|
     float(*sX)[16][17] = reinterpret_cast<float(*)[16][17]>(smem + L::SX);
 
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -129,28 +135,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 
     dma_tile<L::RB>(static_cast<const uint16_t*>(a.k) + tok0 * DK, DK, Lc, smem + L::KT, w, l);
     dma_tile<L::RB>(static_cast<const uint16_t*>(a.q) + tok0 * DK, DK, Lc, smem + L::QT, w, l);
-    if (w == 0) {
+    // every wave: lane l holds row l's cumulative log gate gl and strength bl
+    // (zero past the end)
+    float gl, bl;
+    {
         const int lc = l < Lc ? l : 0;
-        float gl = a.has_gate ? a.log_alpha[tok0 + lc] : 0.f;
+        gl = a.has_gate ? a.log_alpha[tok0 + lc] : 0.f;
         gl = l < Lc ? gl : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(gl, off);
             if (l >= off) gl += y;
         }
-        const float bl = strength(a.beta[tok0 + lc], a.beta_logit);
-        sg[l] = gl;
-        sb[l] = l < Lc ? bl : 0.f;
-        const float g63 = __shfl(gl, 63);
-        a.wsG[cs * kGW + l] = expf(gl);                                // gamma_r
-        if (!a.qk_norm) a.wsG[cs * kGW + 64 + l] = expf(g63 - gl);    // lambda_r
+        bl = l < Lc ? strength(a.beta[tok0 + lc], a.beta_logit) : 0.f;
+    }
+    const float g63 = __shfl(gl, 63);
+    if (w == 0) {
+        a.wsG[cs * kGW + l] = expf(gl);                         // gamma_r
+        if (!QN) a.wsG[cs * kGW + 64 + l] = expf(g63 - gl);    // lambda_r
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies landed
     __syncthreads();
 
     // input preparation: 1/|q_r| and 1/|k_r| from the tiles (four lanes per
     // row, each summing a quarter of the row), and the scaled gate factors
-    if (a.qk_norm) {
+    if constexpr (QN) {
         const int r = tid >> 2, qd = tid & 3;
         float ssq = 0.f, ssk = 0.f;
 #pragma unroll
@@ -174,10 +183,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         }
         __syncthreads();
         if (w == 0) {
-            const float gam = expf(sg[l]), nk = snk[l];
-            a.wsG[cs * kGW + 64 + l] = expf(sg[63] - sg[l]) * nk;   // lambda_r / |k_r|
-            a.wsG[cs * kGW + 128 + l] = gam * nk;                   // gamma_r / |k_r|
-            a.wsG[cs * kGW + 192 + l] = gam * snq[l];               // gamma_r / |q_r|
+            const float gam = expf(gl), nk = snk[l];
+            a.wsG[cs * kGW + 64 + l] = expf(g63 - gl) * nk;   // lambda_r / |k_r|
+            a.wsG[cs * kGW + 128 + l] = gam * nk;             // gamma_r / |k_r|
+            a.wsG[cs * kGW + 192 + l] = gam * snq[l];         // gamma_r / |q_r|
         }
     }
 
@@ -192,12 +201,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 16 * R + 4 * g + j;
-            grow[R][j] = sg[r] * kLog2e;
-            brow[R][j] = a.qk_norm ? sb[r] * snk[r] : sb[r];
-            qrow[R][j] = a.qk_norm ? snq[r] : 1.f;
+            grow[R][j] = __shfl(gl, r) * kLog2e;
+            const float br = __shfl(bl, r);
+            brow[R][j] = QN ? br * snk[r] : br;
+            qrow[R][j] = QN ? snq[r] : 1.f;
         }
-        gcol[R] = sg[16 * R + i16] * kLog2e;
-        kcol[R] = a.qk_norm ? snk[16 * R + i16] : 1.f;
+        gcol[R] = __shfl(gl, 16 * R + i16) * kLog2e;
+        kcol[R] = QN ? snk[16 * R + i16] : 1.f;
     }
 
     // A and P, 16 x 16 block pairs (R, I), R >= I, on the bf16 matrix cores.
@@ -263,6 +273,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         pair_group(3, 3, 1, 1);
     }
     if constexpr (L::ALIAS) __syncthreads();   // the tiles are dead: A may take their place
+    if (w == 0) sb[l] = bl;                     // the strengths, for T^ = T Diag(beta)
     if (w == 0) write_a(3, 0, 3, 0);
     else if (w == 1) write_a(2, 0, 3, 0);
     else if (w == 2) write_a(1, 0, 2, 0);
@@ -343,17 +354,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     out_row(3, tid, 256);
 }
 
-template <int DK>
+template <int DK, bool QN>
 static hipError_t launch_p16(const ChunkArgs& a, hipStream_t st) {
     using L = P16<DK>;
-    auto kern = prep16_kernel<DK>;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+    constexpr int lds = QN ? L::TOTAL_QN : L::TOTAL;
+    auto kern = prep16_kernel<DK, QN>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    return launch_k(kProfPrep, kern, dim3(a.NC, a.H, a.B), dim3(256), L::TOTAL, st, a);
+    return launch_k(kProfPrep, kern, dim3(a.NC, a.H, a.B), dim3(256), lds, st, a);
 }
 
 hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st) {
-    return Dk == 64 ? launch_p16<64>(a, st) : launch_p16<128>(a, st);
+    if (a.qk_norm) return Dk == 64 ? launch_p16<64, true>(a, st) : launch_p16<128, true>(a, st);
+    return Dk == 64 ? launch_p16<64, false>(a, st) : launch_p16<128, false>(a, st);
 }
 
 }  // namespace dr
