@@ -3,9 +3,11 @@
  *
  * TEST PROGRAM.  "cpu" mode needs no GPU: it checks the version, the status
  * text and host-side validation.  "gpu" mode runs a small chunked forward
- * (fp32 inputs, scalar gate and beta, a ragged last chunk) and one decode step
- * through the C ABI with device buffers from the HIP runtime, and compares
- * them with the fp64 oracle (oracle/libdr_oracle.so, test infrastructure).
+ * (fp32 inputs, scalar gate and beta, a ragged last chunk), its backward, the
+ * backward of the preconditioned rule with the input preparation, and one
+ * decode step through the C ABI with device buffers from the HIP runtime, and
+ * compares them with the fp64 oracle (oracle/libdr_oracle.so, test
+ * infrastructure).
  * Exit status 0 on success.
  */
 #include <math.h>
@@ -25,6 +27,12 @@ int dro_backward(int B, int H, int L, int Dk, int Dv, const double* q, const dou
                  const double* log_alpha, int gate, const double* beta, int beta_mode, const double* S0,
                  const double* dO, const double* dS_final, double* dq, double* dk, double* dv, double* dlog_alpha,
                  double* dbeta, double* dS0, int nthreads);
+
+int dro_backward_ex(int B, int H, int L, int Dk, int Dv, const double* q, const double* k, const double* v,
+                    const double* log_alpha, int gate, const double* beta, const double* beta_v, int beta_mode,
+                    const double* key_scale, int input_flags, const double* S0, const double* dO,
+                    const double* dS_final, double* dq, double* dk, double* dv, double* dlog_alpha,
+                    double* dbeta, double* dbeta_v, double* dkey_scale, double* dS0, int nthreads);
 
 static int fails = 0;
 #define CHECK(cond, ...)                                  \
@@ -167,6 +175,50 @@ static int gpu_checks(void) {
         printf("chunk backward: max over dq, dk, dv, dlog_alpha, dbeta, dS0 %.2e\n", eb);
         CHECK(eb <= 1e-4, "backward parity %.2e", eb);
         for (int i = 0; i < 6; ++i) { free(hg[i]); free(ref[i]); }
+
+        /* the preconditioned rule with the input preparation: key scales in
+           [0.5, 1.5), q and k normalised in the library, strengths as logits */
+        {
+            dr_chunk_desc dp = d;
+            dp.input_flags = DR_IN_QK_L2NORM | DR_IN_BETA_LOGIT;
+            float *ks = malloc(nq * 4), *lg = malloc(ng * 4);
+            double *ksd = malloc(nq * 8), *lgd = malloc(ng * 8);
+            for (size_t i = 0; i < nq; ++i) { ks[i] = (float)(1.0 + 0.5 * urand(&st)); ksd[i] = ks[i]; }
+            for (size_t i = 0; i < ng; ++i) { lg[i] = (float)log(be[i] / (1.0 - be[i])); lgd[i] = lg[i]; }
+            const size_t wpb = dr_chunk_bwd_precond_workspace_bytes(&dp);
+            CHECK(wpb > 0, "precond backward workspace size");
+            void *dks, *dlg, *gks, *dwp;
+            HIPOK(hipMalloc(&dks, nq * 4)); HIPOK(hipMalloc(&dlg, ng * 4)); HIPOK(hipMalloc(&gks, nq * 4));
+            HIPOK(hipMalloc(&dwp, wpb));
+            HIPOK(hipMemcpy(dks, ks, nq * 4, hipMemcpyHostToDevice));
+            HIPOK(hipMemcpy(dlg, lg, ng * 4, hipMemcpyHostToDevice));
+            s = dr_chunk_bwd_precond(&dp, dq, dk, dv, dla, dlg, dks, dS0b, dgO, dgS, gq, gk, gv, gla, gbe, gks, gS0,
+                                     dwp, wpb, NULL);
+            CHECK(s == DR_OK, "dr_chunk_bwd_precond: %s (%s)", dr_status_str(s), dr_last_error());
+            HIPOK(hipDeviceSynchronize());
+            const size_t pc[7] = {nq, nq, nq, ng, ng, ns, nq};
+            void* pdev[7] = {gq, gk, gv, gla, gbe, gS0, gks};
+            float* ph[7];
+            double* pref[7];
+            for (int i = 0; i < 7; ++i) {
+                ph[i] = malloc(pc[i] * 4);
+                pref[i] = malloc(pc[i] * 8);
+                HIPOK(hipMemcpy(ph[i], pdev[i], pc[i] * 4, hipMemcpyDeviceToHost));
+            }
+            CHECK(dro_backward_ex(B, H, L, D, D, qd, kd, vd, lad, 1, lgd, NULL, 0, ksd, 3, S0d, gOd, gSd, pref[0],
+                                  pref[1], pref[2], pref[3], pref[4], NULL, pref[6], pref[5], 1) == 0,
+                  "oracle backward_ex");
+            double ep = 0.0;
+            for (int i = 0; i < 7; ++i) {
+                const double e = max_rel(ph[i], pref[i], pc[i]);
+                if (e > ep) ep = e;
+            }
+            printf("preconditioned backward with input preparation: max over the gradients %.2e\n", ep);
+            CHECK(ep <= 1e-4, "precond backward parity %.2e", ep);
+            for (int i = 0; i < 7; ++i) { free(ph[i]); free(pref[i]); }
+            HIPOK(hipFree(dks)); HIPOK(hipFree(dlg)); HIPOK(hipFree(gks)); HIPOK(hipFree(dwp));
+            free(ks); free(lg); free(ksd); free(lgd);
+        }
         HIPOK(hipFree(dgO)); HIPOK(hipFree(dgS)); HIPOK(hipFree(dS0b)); HIPOK(hipFree(gq)); HIPOK(hipFree(gk));
         HIPOK(hipFree(gv)); HIPOK(hipFree(gla)); HIPOK(hipFree(gbe)); HIPOK(hipFree(gS0)); HIPOK(hipFree(dwb));
         free(gO); free(gS); free(gOd); free(gSd);
