@@ -130,7 +130,8 @@ def source_hash(files) -> str:
 
 # the scan kernel's source and its device helpers: a change to either may
 # change the kernel, and then the recorded traffic no longer applies
-SCAN_SOURCES = ["delta_rule_linear_amd/csrc/dr_scan16.hip", "delta_rule_linear_amd/csrc/dr_device.h"]
+SCAN_SOURCES = ["delta_rule_linear_amd/csrc/dr_scan16.hip", "delta_rule_linear_amd/csrc/dr_lds.h",
+                "delta_rule_linear_amd/csrc/dr_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan16_gdn_b2h16_16k_traffic.md")
 
 

@@ -443,7 +443,7 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
 
 // ----------------------------------------------------------------- backward
 struct BwdLayout {
-    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, b32, db1, rq, rk, dla, total;
+    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, b32, db1, rq, rk, dla, F, total;
 };
 
 // Whether a backward call runs on prepared fp32 copies of its inputs: a
@@ -455,6 +455,12 @@ bool bwd_mapped(const dr_chunk_desc& d, bool kvtok) {
 
 bool bwd_copies(const dr_chunk_desc& d, bool kvtok) {
     return d.beta == DR_BETA_CHANNEL || kvtok || (d.input_flags & DR_IN_QK_L2NORM);
+}
+
+// Whether the backward's state scans run on the matrix cores: bf16 inputs
+// seen by the kernels as they are, no channel gate.
+bool bwd_mc(const dr_chunk_desc& d, bool kvtok, bool precond) {
+    return d.in_dtype == DR_BF16 && d.gate != DR_GATE_CHANNEL && !precond && !bwd_copies(d, kvtok);
 }
 
 // precond: write-side key scales, which take the channel-gate kernels for
@@ -505,6 +511,7 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = 
     }
     if (precond && d.gate == DR_GATE_SCALAR)   // d log alpha per channel, summed per token at the end
         w.dla = take((size_t)d.B * d.H * d.L * d.Dk * f);
+    if (bwd_mc(d, kvtok, precond)) w.F = take(NCH * dr::kBF);
     w.total = NCH ? off : 0;
     return w;
 }
@@ -626,6 +633,7 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         a.ks = key_scale;
         a.dks = dkey_scale;
     }
+    if (bwd_mc(*d, kvtok, precond)) a.wF = ws + w.F;
     const bool cbeta = d->beta == DR_BETA_CHANNEL || kvtok;
     const bool mapped = bwd_mapped(*d, kvtok);
     hipError_t e = hipSuccess;

@@ -187,19 +187,76 @@ __device__ __forceinline__ void tri_inverse(const float* sA, float* sT, float (*
     }
 }
 
+// x as a bf16 pair, x = hi + lo to 16 significant bits (bit patterns)
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+    asm volatile("" : "+v"(x));   // one rounding for both uses of h
+    const __bf16 h = (__bf16)x;
+    hi = __builtin_bit_cast(uint16_t, h);
+    lo = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)h));
+}
+
+// The matrix-core scans' operands of chunk slot cs (layout at kBF in
+// dr_internal.h): T^ = T Diag(beta) in packed lower blocks, T^T and P^T in
+// packed upper blocks, each as hi and lo planes, then gamma and lambda.  T and
+// P are fp32 in LDS (pitch PT, lower blocks valid, zero above the diagonal).
+__device__ void pack_scan_operands(const BwdArgs& a, const float* sT, const float* sPm, const float* sg,
+                                   const float* sb, size_t cs, int tid) {
+    char* base = a.wF + cs * (size_t)kBF;
+    // three matrices of 10 blocks x 16 rows x 2 halves of 8 values
+    for (int e = tid; e < 3 * 320; e += NTH) {
+        const int mat = e / 320, pc = e - 320 * mat;
+        const int b = pc >> 5, rr = (pc >> 1) & 15, hh = pc & 1;
+        const int R = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;   // lower block (R, I) at index b
+        const int I = b - R * (R + 1) / 2;
+        const int ch = hh ^ ((rr >> 3) & 1);                        // column half held by this piece
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            float x;
+            if (mat == 0) {
+                const int r = 16 * R + rr, c = 16 * I + 8 * ch + q;
+                x = c <= r ? sT[r * PT + c] * sb[c] : 0.f;
+            } else {
+                // element (r, c) of the transpose, upper block (3 - R, 3 - I)
+                const int r = 16 * (3 - R) + rr, c = 16 * (3 - I) + 8 * ch + q;
+                x = r > c ? 0.f : mat == 1 ? sT[c * PT + r] * sb[r] : sPm[c * PT + r];
+            }
+            split_bf16(x, hi[q], lo[q]);
+        }
+        const size_t at = (size_t)mat * 2 * kTriBytes + (size_t)b * 512 + rr * 32 + 16 * hh;
+        uint4 vh, vl;
+        vh.x = hi[0] | ((unsigned)hi[1] << 16); vh.y = hi[2] | ((unsigned)hi[3] << 16);
+        vh.z = hi[4] | ((unsigned)hi[5] << 16); vh.w = hi[6] | ((unsigned)hi[7] << 16);
+        vl.x = lo[0] | ((unsigned)lo[1] << 16); vl.y = lo[2] | ((unsigned)lo[3] << 16);
+        vl.z = lo[4] | ((unsigned)lo[5] << 16); vl.w = lo[6] | ((unsigned)lo[7] << 16);
+        *reinterpret_cast<uint4*>(base + at) = vh;
+        *reinterpret_cast<uint4*>(base + at + kTriBytes) = vl;
+    }
+    if (tid < CH) {
+        float* gr = reinterpret_cast<float*>(base + kBfGate);
+        gr[tid] = expf(sg[tid]);                    // gamma_r
+        gr[CH + tid] = expf(sg[CH - 1] - sg[tid]);  // lambda_r
+    }
+}
+
 // --------------------------------------------------------------------- prep
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     constexpr int KP = DK + 1;
     static_assert(2 * CH * PT <= 2 * CH * KP, "A and T fit where q and k were");
-    // q and k rows, then (once the products are in registers) A and T
+    // q and k rows, then (once the products are in registers) A and T, and
+    // (bf16 inputs) P beside them when it fits
+    constexpr bool PFIT = 3 * CH * PT <= 2 * CH * KP;
     __shared__ float sKQ[2 * CH * KP];
+    __shared__ float sPx[!F32IN && !PFIT ? CH * PT : 1];
     __shared__ float sX[4][16 * 17];
     __shared__ float sg[CH], sb[CH];
     float* sK = sKQ;
     float* sQ = sKQ + CH * KP;
     float* sA = sKQ;
     float* sT = sKQ + CH * PT;
+    float* sPm = PFIT ? sKQ + 2 * CH * PT : sPx;
+    const bool fast = !F32IN && a.wF != nullptr;
     const int cs = blockIdx.x;
     const int seq = cs / a.NC, c = cs - seq * a.NC;
     const int t0 = c * CH, valid = min(CH, a.L - t0);
@@ -251,13 +308,16 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
                 const float araw = i < r ? aK[I][j] * e : 0.f;
                 sA[r * PT + i] = sb[r] * araw;
                 a.wA[mo + r * CH + i] = araw;
-                a.wP[mo + r * CH + i] = i <= r ? aQ[I][j] * e : 0.f;
+                const float pv = i <= r ? aQ[I][j] * e : 0.f;
+                a.wP[mo + r * CH + i] = pv;
+                if (fast && I <= R) sPm[r * PT + i] = pv;
             }
         }
     }
     lds_barrier();
 
     tri_inverse(sA, sT, sX, a.wT + mo, tid);
+    if (fast) pack_scan_operands(a, sT, sPm, sg, sb, (size_t)cs, tid);
 }
 
 // ------------------------------------------------------- forward state scan
@@ -1836,9 +1896,16 @@ template <int DK, bool F32IN>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
     const unsigned nscan = (unsigned)((a.nseq + 7) / 8) * 8u * (unsigned)(a.Dv / 16);
+    // bf16 inputs: the scans on the matrix cores (dr_bwd16.hip) when the prep
+    // kernel writes their operands
+    const bool mc = !F32IN && a.wF != nullptr;
     hipError_t e = launch_k(kProfBwdPrep, bwd_prep_kernel<DK, F32IN>, dim3(nch), dim3(NTH), 0, st, a);
-    if (e == hipSuccess) e = launch_k(kProfBwdFscan, bwd_fscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
-    if (e == hipSuccess) e = launch_k(kProfBwdRscan, bwd_rscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
+    if (e == hipSuccess)
+        e = mc ? launch_bwd_fscan16(a, DK, st)
+               : launch_k(kProfBwdFscan, bwd_fscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
+    if (e == hipSuccess)
+        e = mc ? launch_bwd_rscan16(a, DK, st)
+               : launch_k(kProfBwdRscan, bwd_rscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
     if (e == hipSuccess) e = launch_k(kProfBwdPost, bwd_post_kernel<DK, F32IN>, dim3(nch), dim3(PNT), 0, st, a);
     return e;
 }

@@ -105,6 +105,19 @@ struct DecodeArgs {
 //   wQh = q o e^G, wKh = k o e^G, wKc = k o e^-G, wKt = k o e^(G_63 - G)
 //   wS, wH      [NCH][Dk][Dv]   chunk start state, gradient at its end state
 //   wU, wR, wdU [NCH][64][Dv]   U, R = V - Gamma K S, and dU
+// For bf16 inputs without a channel gate (wF not NULL) the prep kernel also
+// writes, per chunk, the operands of the matrix-core state scans (kBF bytes):
+//   [T^ hi][T^ lo]      T^ = T Diag(beta), packed lower blocks (tri_off)
+//   [T^T hi][T^T lo]    its transpose, packed upper blocks (kBfTt)
+//   [P^T hi][P^T lo]    P transposed, packed upper blocks (kBfPt)
+//   [gamma 64][lambda 64] fp32 at kBfGate
+// as bf16 hi + lo pairs (x = hi + lo to 16 significant bits).  A packed upper
+// block (R, I), I >= R, of a 64 x 64 matrix sits where tri_block(3 - R, 3 - I)
+// puts a lower one, with the same layout inside the block.
+constexpr int kBfTt = 2 * kTriBytes;
+constexpr int kBfPt = 4 * kTriBytes;
+constexpr int kBfGate = 6 * kTriBytes;
+constexpr int kBF = kBfGate + 1024;
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -145,6 +158,8 @@ struct BwdArgs {
     // column side of A and P and in the state update; dks its gradient
     const float* ks;
     float* dks;
+    // the matrix-core scans' operands (bf16 inputs, no channel gate), or NULL
+    char* wF;
 };
 
 // Optional per-kernel timing (dr_profile_begin / dr_profile_end).  While it is
@@ -179,6 +194,11 @@ hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
 // the backward (dr_bwd.hip)
 hipError_t launch_bwd(const BwdArgs& a, int Dk, bool f32in, hipStream_t st);
+// the backward's two state scans on the matrix cores for bf16 inputs with a
+// scalar gate (or none) and a scalar beta, from the operands in a.wF
+// (dr_bwd16.hip)
+hipError_t launch_bwd_fscan16(const BwdArgs& a, int Dk, hipStream_t st);
+hipError_t launch_bwd_rscan16(const BwdArgs& a, int Dk, hipStream_t st);
 // The backward kernels differentiate the recurrence with respect to q, k, v
 // and a scalar beta as they receive them.  When a call's inputs are not those
 // (a channel-wise or separate beta, or the input preparation), a per-token

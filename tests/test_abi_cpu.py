@@ -291,17 +291,22 @@ def test_backward_validation_and_workspace():
     assert call(d, ws=None) == drl.DR_ERR_WORKSPACE
     assert call(d, wbytes=need - 1) == drl.DR_ERR_WORKSPACE
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(L=0)) == 0
+    # bf16 inputs that the kernels see as they are, without a channel gate:
+    # the matrix-core scans' operands, 31744 bytes per chunk (T^, T^T and P^T
+    # as bf16 hi and lo packed triangles, gamma and lambda)
+    base = drl.dr_chunk_bwd_workspace_bytes(_desc(in_dtype=drl.DR_F32))
+    assert need == base + NCH * 31744
     # a channel gate adds the per-channel decay and four gated operand planes
-    assert drl.dr_chunk_bwd_workspace_bytes(_desc(gate="channel")) >= need + NCH * 4 * 5 * 64 * 128 - NCH * 4 * 64
+    assert drl.dr_chunk_bwd_workspace_bytes(_desc(gate="channel")) >= base + NCH * 4 * 5 * 64 * 128 - NCH * 4 * 64
     # a channel beta runs the unit-strength kernels on fp32 copies of q, sqrt(beta) k, sqrt(beta) v
-    assert drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel")) >= need + 3 * 2 * 3 * 100 * 128 * 4
+    assert drl.dr_chunk_bwd_workspace_bytes(_desc(beta_mode="channel")) >= base + 3 * 2 * 3 * 100 * 128 * 4
     # the normalisation runs the kernels on fp32 copies of q, k, v and keeps
     # 1/|q|, 1/|k| per token; logits alone need only the strengths' values
     ntok = 2 * 3 * 100
     lgt = drl.dr_chunk_bwd_workspace_bytes(_desc(flags=drl.DR_IN_BETA_LOGIT))
     l2 = drl.dr_chunk_bwd_workspace_bytes(_desc(flags=drl.DR_IN_QK_L2NORM))
     assert need + ntok * 4 <= lgt < need + ntok * 128
-    assert l2 >= need + 3 * ntok * 128 * 4 + 3 * ntok * 4
+    assert l2 >= base + 3 * ntok * 128 * 4 + 3 * ntok * 4
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(flags=3)) == l2
     assert call(_desc(flags=3), wbytes=l2 - 1) == drl.DR_ERR_WORKSPACE
     # no sequences: validated and done without touching memory
