@@ -34,6 +34,7 @@
 #include <algorithm>
 
 #include "dr_internal.h"
+#include "dr_lds.h"
 
 namespace dr {
 namespace {
@@ -829,11 +830,51 @@ __device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, in
     if constexpr (!CG) atomicAdd(&shs[0], hs);
 }
 
+// Where piece `piece` of row r of a swizzled tile is written (as tile_at).
+template <int RB>
+__device__ __forceinline__ lchar* tile_st(lchar* tile, int r, int piece) {
+    return tile + r * RB + 16 * (piece ^ swz<RB>(r));
+}
+
+// bf16 rows prefetched by pre_rows into a swizzled [64][2 DK]-byte tile (rows
+// at or past `valid` zeroed), the layout of the matrix-core scans' tiles.
+template <int DK, int NT>
+__device__ __forceinline__ void put_rows_tile(const RowsPre<DK, false, NT>& p, lchar* tile, int valid, int tid) {
+#pragma unroll
+    for (int n = 0; n < RowsPre<DK, false, NT>::N; ++n) {
+        const int e = tid + n * NT;
+        const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
+        const uint4 z = {0u, 0u, 0u, 0u};
+        lds_st(tile_st<2 * DK>(tile, r, c8 >> 3), r < valid ? p.x[n].x : z);
+    }
+}
+
+// Element (r, col) of such a tile.
+template <int DK>
+__device__ __forceinline__ float tile_val(const lchar* tile, int r, int col) {
+    return bf16_to_f32(lds_ld<uint16_t>(tile_at<2 * DK>(tile, r, col >> 3) + 2 * (col & 7)));
+}
+
+// The K^T-style fragment of a row-major 16-bit tile (RB bytes per row):
+// lane (i16, g) receives column c0 + i16 at rows 32 s + 8 g .. +7, i.e. the A
+// operand of (tile^T) rows c0 .. or the B operand of tile columns c0 ..
+template <int RB>
+__device__ __forceinline__ uint4 tr_frag(const lchar* tile, int c0, int s, int i16, int g) {
+    const int tok = 32 * s + 8 * g + (i16 >> 2);
+    const int d = c0 + 4 * (i16 & 3);
+    const uint2 lo4 = lds_tr4(tile_at<RB>(tile, tok, d >> 3) + 2 * (d & 7));
+    const uint2 hi4 = lds_tr4(tile_at<RB>(tile, tok + 4, d >> 3) + 2 * (d & 7));
+    return {lo4.x, lo4.y, hi4.x, hi4.y};
+}
+
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     using Lp = PostLds<DK>;
     constexpr int KP = Lp::KP, ND = DK / 16, NDH = ND / 2;
-    __shared__ float s1[Lp::R1];
+    // bf16 inputs: the q and k rows as bf16 tiles, then N and M as bf16 hi + lo tiles
+    constexpr int RB = 2 * DK, TB = CH * RB, MB = CH * 128;
+    static_assert(F32IN || 2 * TB + 4 * MB <= (int)sizeof(float) * Lp::R1, "tiles fit the slab area");
+    __shared__ __attribute__((aligned(16))) float s1[Lp::R1];
     __shared__ float sM0[CH * PT];   // T
     __shared__ float sM1[CH * PT];   // P, then M = Diag(beta) (dA o E)
     __shared__ float sM2[CH * PT];   // K K^T o E (strict lower)
@@ -871,6 +912,8 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     // ---- q, k rows and the 64 x 64 matrices
     float* sK = s1;
     float* sQ = s1 + CH * KP;
+    lchar* tK = (lchar*)s1;
+    lchar* tQ = tK + TB;
     if constexpr (F32IN) {
         for (int e = tid; e < CH * DK / 8; e += PNT) {
             const int r = e / (DK / 8), c8 = (e % (DK / 8)) * 8;
@@ -883,8 +926,8 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
             for (int j = 0; j < 8; ++j) sQ[r * KP + c8 + j] = x[j];
         }
     } else {
-        put_rows<DK, F32IN, PNT>(pk, sK, valid, tid);
-        put_rows<DK, F32IN, PNT>(pq, sQ, valid, tid);
+        put_rows_tile<DK, PNT>(pk, tK, valid, tid);
+        put_rows_tile<DK, PNT>(pq, tQ, valid, tid);
     }
     put_mat(pt, sM0, tid);
     put_mat(pp, sM1, tid);
@@ -902,7 +945,8 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = rb + j, col = 16 * (D0 + D) + i16;
-            const float qv = sQ[r * KP + col], kv = sK[r * KP + col];
+            const float qv = F32IN ? sQ[r * KP + col] : tile_val<DK>(tQ, r, col);
+            const float kv = F32IN ? sK[r * KP + col] : tile_val<DK>(tK, r, col);
             const float x1 = sgam[r] * z1[D][j];
             const float x2 = -sgam[r] * z2[D][j];
             const float x3 = slam[r] * z3[D][j];
@@ -977,19 +1021,68 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     }
     lds_barrier();
     // dq += N K;  dk += M K + N^T Q + M^T K
+    if constexpr (!F32IN) {
+        // on the bf16 matrix cores: N and M as hi + lo tiles (N at tN, M at
+        // tN + 2 MB), q and k exact; the products over all 64 tokens (N and M
+        // vanish outside their triangles)
+        lchar* tN = tQ + TB;
+        for (int e = tid; e < 2 * CH * 8; e += PNT) {
+            const int mat = e >> 9, r = (e >> 3) & 63, pc = e & 7;
+            const float* src = (mat ? sM1 : sM3) + r * PT + 8 * pc;
+            uint16_t hi[8], lo[8];
 #pragma unroll
-    for (int D = 0; D < NDH; ++D) {
-        const int cb = 16 * (D0 + D) + i16;
-        for (int s = 0; s < 4 * (R + 1); ++s) {
-            const int m = 4 * s + g;
-            const float kb = sK[m * KP + cb];
-            dq[D] = mfma_f32x4(sM3[(16 * R + i16) * PT + m], kb, dq[D]);
-            dk[D] = mfma_f32x4(sM1[(16 * R + i16) * PT + m], kb, dk[D]);
+            for (int q = 0; q < 8; ++q) split_bf16(src[q], hi[q], lo[q]);
+            uint4 vh, vl;
+            vh.x = hi[0] | ((unsigned)hi[1] << 16); vh.y = hi[2] | ((unsigned)hi[3] << 16);
+            vh.z = hi[4] | ((unsigned)hi[5] << 16); vh.w = hi[6] | ((unsigned)hi[7] << 16);
+            vl.x = lo[0] | ((unsigned)lo[1] << 16); vl.y = lo[2] | ((unsigned)lo[3] << 16);
+            vl.z = lo[4] | ((unsigned)lo[5] << 16); vl.w = lo[6] | ((unsigned)lo[7] << 16);
+            lchar* t = tN + mat * 2 * MB;
+            lds_st(tile_st<128>(t, r, pc), vh);
+            lds_st(tile_st<128>(t + MB, r, pc), vl);
         }
-        for (int s = 4 * R; s < 16; ++s) {
-            const int m = 4 * s + g;
-            dk[D] = mfma_f32x4(sM3[m * PT + 16 * R + i16], sQ[m * KP + cb], dk[D]);
-            dk[D] = mfma_f32x4(sM1[m * PT + 16 * R + i16], sK[m * KP + cb], dk[D]);
+        lds_barrier();
+        uint4 nf[2][2], mf[2][2], ntf[2][2], mtf[2][2];   // [s][hi, lo]
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                nf[s][p] = lds16(tile_at<128>(tN + p * MB, 16 * R + i16, 4 * s + g));
+                mf[s][p] = lds16(tile_at<128>(tN + 2 * MB + p * MB, 16 * R + i16, 4 * s + g));
+                ntf[s][p] = tr_frag<128>(tN + p * MB, 16 * R, s, i16, g);
+                mtf[s][p] = tr_frag<128>(tN + 2 * MB + p * MB, 16 * R, s, i16, g);
+            }
+#pragma unroll
+        for (int D = 0; D < NDH; ++D) {
+            const int c0 = 16 * (D0 + D);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const uint4 kb = tr_frag<RB>(tK, c0, s, i16, g);
+                const uint4 qb = tr_frag<RB>(tQ, c0, s, i16, g);
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    dq[D] = mfma_raw<true>(nf[s][p], kb, dq[D]);
+                    dk[D] = mfma_raw<true>(mf[s][p], kb, dk[D]);
+                    dk[D] = mfma_raw<true>(ntf[s][p], qb, dk[D]);
+                    dk[D] = mfma_raw<true>(mtf[s][p], kb, dk[D]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int D = 0; D < NDH; ++D) {
+            const int cb = 16 * (D0 + D) + i16;
+            for (int s = 0; s < 4 * (R + 1); ++s) {
+                const int m = 4 * s + g;
+                const float kb = sK[m * KP + cb];
+                dq[D] = mfma_f32x4(sM3[(16 * R + i16) * PT + m], kb, dq[D]);
+                dk[D] = mfma_f32x4(sM1[(16 * R + i16) * PT + m], kb, dk[D]);
+            }
+            for (int s = 4 * R; s < 16; ++s) {
+                const int m = 4 * s + g;
+                dk[D] = mfma_f32x4(sM3[m * PT + 16 * R + i16], sQ[m * KP + cb], dk[D]);
+                dk[D] = mfma_f32x4(sM1[m * PT + 16 * R + i16], sK[m * KP + cb], dk[D]);
+            }
         }
     }
     // ---- reductions of the gate and strength terms
