@@ -540,7 +540,10 @@ def main():
                "roofline": {"bound": "mfma", "kernel": f"bwd_{top}_kernel", "achieved": round(ktf, 2),
                             "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(ktf / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                            "alg_flops_per_launch": int(kflops[top])},
+                            "alg_flops_per_launch": int(kflops[top]),
+                            "arith": "fp32-accurate products: fp32 matrix ops, or bf16/fp16 ones on hi + lo "
+                                     "operands; peak is the fp32 matrix peak",
+                            "frac_of_bf16_peak": round(ktf / 2500.0, 4)},
                "mfma_whole_backward": {"achieved_tflops": round(btf, 2), "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
                                        "frac": round(btf / FP32_MFMA_PEAK_TFLOPS, 4),
                                        "alg_flops_per_step": int(sum(kflops.values()))},
