@@ -483,8 +483,12 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = 
     w.G = take(NCH * dr::CH * (cg ? d.Dk : 1) * f);
     w.S = take(NCH * d.Dk * d.Dv * f);
     w.H = take(NCH * d.Dk * d.Dv * f);
-    w.U = take(NCH * dr::CH * d.Dv * f);
-    w.R = take(NCH * dr::CH * d.Dv * f);
+    // U and R: the matrix-core path forms them again in the per-chunk kernel
+    const bool mc = bwd_mc(d, kvtok, precond);
+    if (!mc) {
+        w.U = take(NCH * dr::CH * d.Dv * f);
+        w.R = take(NCH * dr::CH * d.Dv * f);
+    }
     w.dU = take(NCH * dr::CH * d.Dv * f);
     if (cg) {
         w.Qh = take(NCH * dr::CH * d.Dk * f);
@@ -511,7 +515,7 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = 
     }
     if (precond && d.gate == DR_GATE_SCALAR)   // d log alpha per channel, summed per token at the end
         w.dla = take((size_t)d.B * d.H * d.L * d.Dk * f);
-    if (bwd_mc(d, kvtok, precond)) w.F = take(NCH * dr::kBF);
+    if (mc) w.F = take(NCH * dr::kBF);
     w.total = NCH ? off : 0;
     return w;
 }
@@ -617,8 +621,9 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.wG = (float*)(ws + w.G);
     a.wS = (float*)(ws + w.S);
     a.wH = (float*)(ws + w.H);
-    a.wU = (float*)(ws + w.U);
-    a.wR = (float*)(ws + w.R);
+    const bool mc = bwd_mc(*d, kvtok, precond);
+    a.wU = mc ? nullptr : (float*)(ws + w.U);
+    a.wR = mc ? nullptr : (float*)(ws + w.R);
     a.wdU = (float*)(ws + w.dU);
     a.cgate = d->gate == DR_GATE_CHANNEL || precond;
     if (a.cgate) {
@@ -633,7 +638,7 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
         a.ks = key_scale;
         a.dks = dkey_scale;
     }
-    if (bwd_mc(*d, kvtok, precond)) a.wF = ws + w.F;
+    if (mc) a.wF = ws + w.F;
     const bool cbeta = d->beta == DR_BETA_CHANNEL || kvtok;
     const bool mapped = bwd_mapped(*d, kvtok);
     hipError_t e = hipSuccess;

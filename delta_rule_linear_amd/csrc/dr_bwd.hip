@@ -836,6 +836,255 @@ __device__ __forceinline__ lchar* tile_st(lchar* tile, int r, int piece) {
     return tile + r * RB + 16 * (piece ^ swz<RB>(r));
 }
 
+// bf16 hi + lo pair of a 16-byte fragment (eight values)
+struct BF2 {
+    uint4 h, l;
+};
+
+// c += a b for split a and b: hi hi + hi lo + lo hi
+__device__ __forceinline__ f32x4 mma3(const BF2& a, const BF2& b, f32x4 c) {
+    c = mfma_raw<true>(a.h, b.h, c);
+    c = mfma_raw<true>(a.h, b.l, c);
+    return mfma_raw<true>(a.l, b.h, c);
+}
+
+// Four consecutive fp32 values (columns c4 .. c4 + 3 of row r) into a bf16 hi
+// and lo slab plane pair (the slab_off layout, byte planes).
+__device__ __forceinline__ void put_split4_bf(lchar* hi, lchar* lo, int r, int c4, const float4& v) {
+    const int off = 2 * (slab_off(r, c4 >> 3) + (c4 & 7));
+    uint16_t h[4], o[4];
+    split_bf16(v.x, h[0], o[0]);
+    split_bf16(v.y, h[1], o[1]);
+    split_bf16(v.z, h[2], o[2]);
+    split_bf16(v.w, h[3], o[3]);
+    uint2 vh, vl;
+    vh.x = h[0] | ((unsigned)h[1] << 16); vh.y = h[2] | ((unsigned)h[3] << 16);
+    vl.x = o[0] | ((unsigned)o[1] << 16); vl.y = o[2] | ((unsigned)o[3] << 16);
+    lds_st(hi + off, vh);
+    lds_st(lo + off, vl);
+}
+
+// One value into a bf16 hi and lo slab plane pair.
+__device__ __forceinline__ void put_split1_bf(lchar* hi, lchar* lo, int r, int c, float x) {
+    const int off = 2 * (slab_off(r, c >> 3) + (c & 7));
+    uint16_t h, o;
+    split_bf16(x, h, o);
+    lds_st(hi + off, h);
+    lds_st(lo + off, o);
+}
+
+// Row fragment of a slab plane pair: row r, columns 8 grp .. +7.
+__device__ __forceinline__ BF2 slab_row(const lchar* hi, const lchar* lo, int r, int grp) {
+    const int off = 2 * slab_off(r, grp);
+    return {lds16(hi + off), lds16(lo + off)};
+}
+
+// Column fragment of one slab plane (the B operand of a contraction over its
+// rows): lane (i16, g) receives column c0 + i16 at rows 32 s + 8 g .. +7,
+// through the transposing LDS read.
+__device__ __forceinline__ uint4 slab_col(const lchar* pl, int c0, int s, int i16, int g) {
+    const int r = 32 * s + 8 * g + (i16 >> 2);
+    const int c = c0 + 4 * (i16 & 3);
+    const uint2 lo4 = lds_tr4(pl + 2 * (slab_off(r, c >> 3) + (c & 7)));
+    const uint2 hi4 = lds_tr4(pl + 2 * (slab_off(r + 4, c >> 3) + (c & 7)));
+    return {lo4.x, lo4.y, hi4.x, hi4.y};
+}
+
+// The per-chunk kernel's state products for bf16 inputs without a channel
+// gate.  R and U are not read back: per slab of VS state columns they are
+// formed here, R = V - Gamma K S (rows past the end zero) and U = T^ R, with k
+// exact and S, R, T^ as bf16 hi + lo; then
+//   z1 = dO S^T, z2 = dR S^T, z3 = U H^T   (rows 16 R .., column blocks D0 ..)
+//   acc = dO U^T (hf 0) or dU R^T (hf 1)   (rows 16 R .., column blocks I <= R)
+// and <H, S> into shs[0], every slab operand a bf16 hi + lo pair.  The chunk's
+// k tile and T^ (packed lower, hi and lo) arrive with the first slab, into
+// tKs and tTs; the slab planes are in `slab`.  The last slab's turn prefetches
+// T, P, K K^T and the q rows for the 64 x 64 part (the k rows stay in tKs).
+template <int DK>
+__device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, int valid, size_t tok0, lchar* slab,
+                                              lchar* tKs, lchar* tTs, const float* sgam,
+                                              f32x4 (&z1)[DK / 32], f32x4 (&z2)[DK / 32], f32x4 (&z3)[DK / 32],
+                                              f32x4 (&acc)[4], float* shs, RowsPre<DK, false, PNT>& pq,
+                                              MatPre<PNT>& pt, MatPre<PNT>& pp, MatPre<PNT>& pa) {
+    constexpr int VS = PostLds<DK>::VS, NDH = DK / 32, RB = 2 * DK;
+    constexpr int NS = DK * VS / 4 / PNT;   // float4 of S (and of H) per thread and slab
+    static_assert(CH * VS / 4 == PNT, "one float4 of each 64-row slab per thread");
+    constexpr int PS = DK * VS * 2, PT6 = CH * VS * 2;   // bytes of an S / H plane and of a 64-row plane
+    const int Dv = a.Dv;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
+    const int R = w & 3, hf = w >> 2, D0 = hf * NDH;
+    const size_t mo = (size_t)cs * CH * CH;
+    lchar* sSh = slab;
+    lchar* sSl = sSh + PS;
+    lchar* sHh = sSl + PS;
+    lchar* sHl = sHh + PS;
+    lchar* sOh = sHl + PS;
+    lchar* sOl = sOh + PT6;
+    lchar* sRh = sOl + PT6;
+    lchar* sRl = sRh + PT6;
+    lchar* sUh = sRl + PT6;
+    lchar* sUl = sUh + PT6;
+    lchar* sdUh = sUl + PT6;
+    lchar* sdUl = sdUh + PT6;
+    lchar* sdRh = sdUl + PT6;
+    lchar* sdRl = sdRh + PT6;
+    // this wave's block of R and U: rows 16 R .., slab columns 16 hf ..
+    const int rrow = 16 * R + 4 * g;
+    // ---- prefetch registers: S, H, dO, dR, dU of a slab, V at this lane's R
+    // entries, and with the first slab the k tile and T^
+    float4 ps[NS], ph[NS], po, pd, pdu;
+    uint16_t pv[4];
+    uint4 kt[2], tt[2];
+    auto pre_slab = [&](int v0) {
+        const int vw = min(VS, Dv - v0);   // 16 or 32
+        const float4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
+            ps[n] = ph[n] = z;
+            if (c4 < vw) {
+                const size_t off = ((size_t)cs * DK + d) * Dv + v0 + c4;
+                ps[n] = *reinterpret_cast<const float4*>(a.wS + off);
+                ph[n] = *reinterpret_cast<const float4*>(a.wH + off);
+            }
+        }
+        const int r = tid / (VS / 4), c4 = (tid % (VS / 4)) * 4;
+        po = pd = pdu = z;
+        if (c4 < vw) {
+            pdu = *reinterpret_cast<const float4*>(a.wdU + ((size_t)cs * CH + r) * Dv + v0 + c4);
+            const size_t io = (tok0 + (r < valid ? r : 0)) * Dv + v0 + c4;
+            po = *reinterpret_cast<const float4*>(a.dO + io);
+            pd = *reinterpret_cast<const float4*>(a.dv + io);
+        }
+        const int vc = 16 * hf + i16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = rrow + j;
+            pv[j] = vc < vw ? static_cast<const uint16_t*>(a.v)[(tok0 + (rr < valid ? rr : 0)) * Dv + v0 + vc] : 0;
+        }
+    };
+#pragma unroll
+    for (int D = 0; D < NDH; ++D) z1[D] = z2[D] = z3[D] = zero4();
+#pragma unroll
+    for (int I = 0; I < 4; ++I) acc[I] = zero4();
+    float hs = 0.f;
+    {
+        // the k tile (64 x DK bf16) and T^ (two 5 KiB planes), 16 bytes per piece
+        const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + tok0 * DK);
+        const uint4* ts = reinterpret_cast<const uint4*>(a.wF + (size_t)cs * kBF);
+        const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int e = tid + n * PNT;                    // piece: row e / (DK / 8), 16 bytes
+            const int r = e / (DK / 8);
+            kt[n] = e < CH * DK / 8 ? ks[(size_t)(r < valid ? r : 0) * (DK / 8) + e % (DK / 8)] : z;
+            tt[n] = e < 2 * kTriBytes / 16 ? ts[e] : z;
+        }
+    }
+    pre_slab(0);
+    for (int v0 = 0; v0 < Dv; v0 += VS) {
+        const int vw = min(VS, Dv - v0);
+        lds_barrier();
+        if (v0 == 0) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int e = tid + n * PNT;
+                if (e < CH * DK / 8) {
+                    const int r = e / (DK / 8), pc = e % (DK / 8);
+                    const uint4 z = {0u, 0u, 0u, 0u};
+                    lds_st(tile_st<RB>(tKs, r, pc), r < valid ? kt[n] : z);
+                }
+                if (e < 2 * kTriBytes / 16) lds_st(tTs + 16 * e, tt[n]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
+            hs += ps[n].x * ph[n].x + ps[n].y * ph[n].y + ps[n].z * ph[n].z + ps[n].w * ph[n].w;
+            put_split4_bf(sSh, sSl, d, c4, ps[n]);
+            put_split4_bf(sHh, sHl, d, c4, ph[n]);
+        }
+        float vv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vv[j] = bf16_to_f32(pv[j]);
+        {
+            const int r = tid / (VS / 4), c4 = (tid % (VS / 4)) * 4;
+            const float4 z = {0.f, 0.f, 0.f, 0.f};
+            put_split4_bf(sOh, sOl, r, c4, r < valid ? po : z);
+            put_split4_bf(sdRh, sdRl, r, c4, r < valid ? pd : z);
+            put_split4_bf(sdUh, sdUl, r, c4, pdu);
+        }
+        lds_barrier();
+        if (v0 + VS < Dv) {
+            pre_slab(v0 + VS);
+        } else {
+            pre_rows<DK, false, PNT>(pq, a.q, tok0, valid, tid);
+            pre_mat(pt, a.wT + mo, tid);
+            pre_mat(pp, a.wP + mo, tid);
+            pre_mat(pa, a.wA + mo, tid);
+        }
+        // R = V - Gamma K S: this wave's block (rows 16 R .., columns 16 hf ..)
+        {
+            f32x4 X = zero4();
+#pragma unroll
+            for (int s = 0; s < DK / 32; ++s) {
+                const uint4 kf = lds16(tile_at<RB>(tKs, 16 * R + i16, 4 * s + g));
+                X = mfma_raw<true>(kf, slab_col(sSh, 16 * hf, s, i16, g), X);
+                X = mfma_raw<true>(kf, slab_col(sSl, 16 * hf, s, i16, g), X);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = rrow + j, c = 16 * hf + i16;
+                const float rv = r < valid && c < vw ? vv[j] - sgam[r] * X[j] : 0.f;
+                put_split1_bf(sRh, sRl, r, c, rv);
+            }
+        }
+        lds_barrier();
+        // U = T^ R
+        {
+            f32x4 U = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int I = 2 * s + (g >> 1);
+                const int Ic = I <= R ? I : R;
+                const int off = tri_block(R, Ic) * 512 + i16 * 32 + 16 * ((g & 1) ^ ((i16 >> 3) & 1));
+                const uint32_t m = I <= R ? ~0u : 0u;
+                uint4 th = lds16(tTs + off), tl = lds16(tTs + kTriBytes + off);
+                th.x &= m; th.y &= m; th.z &= m; th.w &= m;
+                tl.x &= m; tl.y &= m; tl.z &= m; tl.w &= m;
+                const BF2 rb = {slab_col(sRh, 16 * hf, s, i16, g), slab_col(sRl, 16 * hf, s, i16, g)};
+                U = mma3({th, tl}, rb, U);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) put_split1_bf(sUh, sUl, rrow + j, 16 * hf + i16, U[j]);
+        }
+        lds_barrier();
+        const int ra = 16 * R + i16;
+        const BF2 fo = slab_row(sOh, sOl, ra, g);
+        const BF2 fr = slab_row(sdRh, sdRl, ra, g);
+        const BF2 fu = slab_row(sUh, sUl, ra, g);
+#pragma unroll
+        for (int D = 0; D < NDH; ++D) {
+            const BF2 fs = slab_row(sSh, sSl, 16 * (D0 + D) + i16, g);
+            const BF2 fh = slab_row(sHh, sHl, 16 * (D0 + D) + i16, g);
+            z1[D] = mma3(fo, fs, z1[D]);
+            z2[D] = mma3(fr, fs, z2[D]);
+            z3[D] = mma3(fu, fh, z3[D]);
+        }
+        if (hf == 0) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+                if (I <= R) acc[I] = mma3(fo, slab_row(sUh, sUl, 16 * I + i16, g), acc[I]);
+        } else {
+            const BF2 fdu = slab_row(sdUh, sdUl, ra, g);
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+                if (I <= R) acc[I] = mma3(fdu, slab_row(sRh, sRl, 16 * I + i16, g), acc[I]);
+        }
+    }
+    atomicAdd(&shs[0], hs);
+}
+
 // bf16 rows prefetched by pre_rows into a swizzled [64][2 DK]-byte tile (rows
 // at or past `valid` zeroed), the layout of the matrix-core scans' tiles.
 template <int DK, int NT>
@@ -875,8 +1124,9 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     constexpr int RB = 2 * DK, TB = CH * RB, MB = CH * 128;
     static_assert(F32IN || 2 * TB + 4 * MB <= (int)sizeof(float) * Lp::R1, "tiles fit the slab area");
     __shared__ __attribute__((aligned(16))) float s1[Lp::R1];
-    __shared__ float sM0[CH * PT];   // T
-    __shared__ float sM1[CH * PT];   // P, then M = Diag(beta) (dA o E)
+    // bf16 inputs: sM0 and sM1 hold the k tile and T^ during the slabs
+    __shared__ __attribute__((aligned(16))) float sM0[CH * PT];   // T
+    __shared__ __attribute__((aligned(16))) float sM1[CH * PT];   // P, then M = Diag(beta) (dA o E)
     __shared__ float sM2[CH * PT];   // K K^T o E (strict lower)
     __shared__ float sM3[CH * PT];   // N = dP o E
     __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
@@ -906,7 +1156,14 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     RowsPre<DK, F32IN, PNT> pk, pq;
     MatPre<PNT> pt, pp, pa;
     f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
-    post_state_products<DK, F32IN, false>(a, cs, valid, tok0, s1, z1, z2, z3, acc, &shs, pk, pq, pt, pp, pa);
+    if constexpr (F32IN) {
+        post_state_products<DK, F32IN, false>(a, cs, valid, tok0, s1, z1, z2, z3, acc, &shs, pk, pq, pt, pp, pa);
+    } else {
+        static_assert(F32IN || CH * 2 * DK <= (int)sizeof(float) * CH * PT, "the k tile fits sM0");
+        static_assert(F32IN || 2 * kTriBytes <= (int)sizeof(float) * CH * PT, "T^ fits sM1");
+        post_slabs_rc<DK>(a, cs, valid, tok0, (lchar*)s1, (lchar*)sM0, (lchar*)sM1, sgam, z1, z2, z3, acc, &shs, pq,
+                          pt, pp, pa);
+    }
     lds_barrier();
 
     // ---- q, k rows and the 64 x 64 matrices
@@ -926,8 +1183,11 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
             for (int j = 0; j < 8; ++j) sQ[r * KP + c8 + j] = x[j];
         }
     } else {
-        put_rows_tile<DK, PNT>(pk, tK, valid, tid);
+        // the k tile from where the slabs used it (sM0, in the same layout),
+        // before T takes that space
+        for (int e = tid; e < TB / 16; e += PNT) lds_st(tK + 16 * e, lds16((const lchar*)sM0 + 16 * e));
         put_rows_tile<DK, PNT>(pq, tQ, valid, tid);
+        lds_barrier();
     }
     put_mat(pt, sM0, tid);
     put_mat(pp, sM1, tid);

@@ -7,7 +7,8 @@
 // chunk of 64 tokens, with T^ = T Diag(beta), gamma_r = e^{g_r} and
 // lambda_r = e^{g_63 - g_r}:
 //   forward   R = V - Gamma K S,  U = T^ R,  S <- gamma_63 S + K^T Lambda U
-//             (the start state S of every chunk, R and U are stored);
+//             (the start state S of every chunk is stored; the per-chunk
+//             kernel forms R and U again from it);
 //   reverse   dU = P^T dO + Lambda K H,  dR = T^T dU  (= dV),
 //             H <- gamma_63 H + Q^T Gamma dO - K^T Gamma dR
 //             (H at every chunk's end state and dU are stored, dR is dv,
@@ -19,7 +20,8 @@
 //    16-byte global->LDS loads ahead of use (three buffers in the forward
 //    scan, two in the reverse one, whose tiles are larger), touch the lines
 //    of a chunk four ahead to start their HBM reads, and store the fp32
-//    results that the compute waves stage in LDS, with 16-byte stores;
+//    results that the compute waves stage in LDS (S; H, dU and dV), with
+//    16-byte stores;
 //  * fp32 values enter the bf16 matrix-core ops as hi + lo pairs (16
 //    significant bits, the fp32 range): the states S and H and the per-chunk
 //    R, U, dO, dU, Gamma dO, Gamma dR on the chunk's side, and T^, T^T, P^T
@@ -141,8 +143,7 @@ __device__ __forceinline__ void copy_rows(const char* src, int valid, lchar* til
 
 // ------------------------------------------------------------ forward scan
 // LDS: three operand buffers [K 64 x RB][T^ hi][T^ lo][V 64 x 32][gate 1024]
-// and the working area [S^T hi/lo][R^T hi/lo][(lambda U)^T hi/lo][S fp32]
-// [R fp32][U fp32].
+// and the working area [S^T hi/lo][R^T hi/lo][(lambda U)^T hi/lo][S fp32].
 template <int DK>
 struct FL {
     static constexpr int RB = DK * 2;
@@ -156,14 +157,12 @@ struct FL {
     static constexpr int WR = WS + 2 * 16 * SP;
     static constexpr int WUL = WR + 2 * 16 * RP;
     static constexpr int WSF = WUL + 2 * 16 * RP;
-    static constexpr int WRF = WSF + DK * FP;
-    static constexpr int WUF = WRF + 64 * FP;
-    static constexpr int WORK = WUF + 64 * FP;
+    static constexpr int WORK = WSF + DK * FP;
     static constexpr int TOTAL = 3 * BUF + WORK + 1024;
     static constexpr int NTI = RB / 16 / 4;   // K-tile copies per copy wave
     // a copy wave's vector-memory operations per chunk: the K tile, 4 part-2
-    // slots, the stores of S (DK / 64), R and U, the line touch
-    static constexpr int NOPS = NTI + 4 + DK / 64 + 2 + 1;
+    // slots, the stores of S (DK / 64), the line touch
+    static constexpr int NOPS = NTI + 4 + DK / 64 + 1;
 };
 
 template <int DK>
@@ -196,8 +195,6 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
     lchar* sR = work + L::WR;
     lchar* sUl = work + L::WUL;
     lchar* sSf = work + L::WSF;
-    lchar* sRf = work + L::WRF;
-    lchar* sUf = work + L::WUF;
     auto sync = [&]() { lds_barrier(); };
 
     const char* kbase = static_cast<const char*>(a.k) + (size_t)seq * a.L * DK * 2;
@@ -265,7 +262,7 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
         uint4 tfr[2][2], kfr[NTS][2];
         float lam[4];
 
-        // ---------------- phase 1: X = K S, R = V - Gamma X; stage S and R
+        // ---------------- phase 1: X = K S, R = V - Gamma X; stage S
         if (copier) {
             copy0(cbuf, cn);
         } else {
@@ -304,7 +301,6 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * w + 4 * g + j;
                 Rv[j] = r < Lc ? bf16_to_f32(vb[j]) - gam[j] * X[j] : 0.f;
-                lds_st(sRf + r * FP + 4 * i16, Rv[j]);
             }
             st4_terms<true, 2>(sR + i16 * RP + 2 * (16 * w + 4 * g), 16 * RP, Rv);
 #pragma unroll
@@ -315,10 +311,9 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
         }
         sync();
 
-        // ---------------- phase 2: U = T^ R; stage U, lambda U
+        // ---------------- phase 2: U = T^ R, lambda U
         if (copier) {
             store_staged<DK>(sSf, a.wS + cs * DK * Dv + n0, Dv, DK, l, cw);
-            store_staged<64>(sRf, a.wR + cs * CH * Dv + n0, Dv, CH, l, cw);
         } else {
             uint4 rf[2][2];
 #pragma unroll
@@ -344,17 +339,13 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
             for (int s = 0; s < 2; ++s) U = mfma3(tfr[s][0], tfr[s][1], rf[s][0], rf[s][1], U);
             f32x4 Ul;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                lds_st(sUf + (16 * w + 4 * g + j) * FP + 4 * i16, U[j]);
-                Ul[j] = lam[j] * U[j];
-            }
+            for (int j = 0; j < 4; ++j) Ul[j] = lam[j] * U[j];
             st4_terms<true, 2>(sUl + i16 * RP + 2 * (16 * w + 4 * g), 16 * RP, Ul);
         }
         sync();
 
         // ---------------- phase 3: S = gamma_63 S + K^T (lambda U)
         if (copier) {
-            store_staged<64>(sUf, a.wU + cs * CH * Dv + n0, Dv, CH, l, cw);
             copy2(cbuf, cn);
             if (NCF > 0) dma4(wm.base + (size_t)min(c + DR_BWD_PFD, NCF - 1) * wm.stride, sink + 256 * cw);
             else dma4(fbase, sink + 256 * cw);

@@ -301,8 +301,10 @@ dr_status dr_decode_step_precond(const dr_decode_desc* d, const void* q, const v
 /* Bytes of device workspace dr_chunk_bwd needs for `d` (0 if d is invalid for
  * the backward or there is no work): per 64-token chunk of every sequence,
  * three 64 x 64 matrices, 64 gate values, two Dk x Dv states and three
- * 64 x Dv blocks, all fp32; with a channel gate 64 x Dk gate values and four
- * more 64 x Dk blocks (the gated keys and queries); with a channel beta or
+ * 64 x Dv blocks, all fp32 (for bf16 inputs without a channel gate, channel
+ * beta or DR_IN_QK_L2NORM: one 64 x Dv block and 31744 bytes of packed
+ * operands in place of the other two); with a channel gate 64 x Dk gate
+ * values and four more 64 x Dk blocks (the gated keys and queries); with a channel beta or
  * DR_IN_QK_L2NORM fp32 copies of q, k and v and up to four floats per token;
  * with DR_IN_BETA_LOGIT alone one float per token. */
 size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
