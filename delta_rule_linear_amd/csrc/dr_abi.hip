@@ -476,15 +476,18 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = 
         off = align256(off + bytes);
         return at;
     };
+    // the matrix-core path keeps P, U and R in other forms (packed operands,
+    // formed again) and K K^T o E not at all
+    const bool mc = bwd_mc(d, kvtok, precond);
     w.T = take(NCH * dr::CH * dr::CH * f);
-    w.Pm = take(NCH * dr::CH * dr::CH * f);
-    w.A = take(NCH * dr::CH * dr::CH * f);
+    if (!mc) {
+        w.Pm = take(NCH * dr::CH * dr::CH * f);
+        w.A = take(NCH * dr::CH * dr::CH * f);
+    }
     const bool cg = d.gate == DR_GATE_CHANNEL || precond;
     w.G = take(NCH * dr::CH * (cg ? d.Dk : 1) * f);
     w.S = take(NCH * d.Dk * d.Dv * f);
     w.H = take(NCH * d.Dk * d.Dv * f);
-    // U and R: the matrix-core path forms them again in the per-chunk kernel
-    const bool mc = bwd_mc(d, kvtok, precond);
     if (!mc) {
         w.U = take(NCH * dr::CH * d.Dv * f);
         w.R = take(NCH * dr::CH * d.Dv * f);
@@ -615,13 +618,13 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.nseq = (int)nseq;
     a.has_gate = d->gate != DR_GATE_NONE;
     char* ws = (char*)workspace;
+    const bool mc = bwd_mc(*d, kvtok, precond);
     a.wT = (float*)(ws + w.T);
-    a.wP = (float*)(ws + w.Pm);
-    a.wA = (float*)(ws + w.A);
+    a.wP = mc ? nullptr : (float*)(ws + w.Pm);
+    a.wA = mc ? nullptr : (float*)(ws + w.A);
     a.wG = (float*)(ws + w.G);
     a.wS = (float*)(ws + w.S);
     a.wH = (float*)(ws + w.H);
-    const bool mc = bwd_mc(*d, kvtok, precond);
     a.wU = mc ? nullptr : (float*)(ws + w.U);
     a.wR = mc ? nullptr : (float*)(ws + w.R);
     a.wdU = (float*)(ws + w.dU);

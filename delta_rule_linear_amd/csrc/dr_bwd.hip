@@ -197,14 +197,14 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 }
 
 // The matrix-core scans' operands of chunk slot cs (layout at kBF in
-// dr_internal.h): T^ = T Diag(beta) in packed lower blocks, T^T and P^T in
-// packed upper blocks, each as hi and lo planes, then gamma and lambda.  T and
-// P are fp32 in LDS (pitch PT, lower blocks valid, zero above the diagonal).
+// dr_internal.h): T^ = T Diag(beta) in packed lower blocks and P^T in packed
+// upper blocks, each as hi and lo planes, then gamma and lambda.  T and P are
+// fp32 in LDS (pitch PT, lower blocks valid, zero above the diagonal).
 __device__ void pack_scan_operands(const BwdArgs& a, const float* sT, const float* sPm, const float* sg,
                                    const float* sb, size_t cs, int tid) {
     char* base = a.wF + cs * (size_t)kBF;
-    // three matrices of 10 blocks x 16 rows x 2 halves of 8 values
-    for (int e = tid; e < 3 * 320; e += NTH) {
+    // two matrices of 10 blocks x 16 rows x 2 halves of 8 values
+    for (int e = tid; e < 2 * 320; e += NTH) {
         const int mat = e / 320, pc = e - 320 * mat;
         const int b = pc >> 5, rr = (pc >> 1) & 15, hh = pc & 1;
         const int R = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0;   // lower block (R, I) at index b
@@ -220,7 +220,7 @@ __device__ void pack_scan_operands(const BwdArgs& a, const float* sT, const floa
             } else {
                 // element (r, c) of the transpose, upper block (3 - R, 3 - I)
                 const int r = 16 * (3 - R) + rr, c = 16 * (3 - I) + 8 * ch + q;
-                x = r > c ? 0.f : mat == 1 ? sT[c * PT + r] * sb[r] : sPm[c * PT + r];
+                x = r > c ? 0.f : sPm[c * PT + r];
             }
             split_bf16(x, hi[q], lo[q]);
         }
@@ -308,10 +308,13 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
                 const float e = i <= r ? expf(sg[r] - sg[i]) : 0.f;
                 const float araw = i < r ? aK[I][j] * e : 0.f;
                 sA[r * PT + i] = sb[r] * araw;
-                a.wA[mo + r * CH + i] = araw;
                 const float pv = i <= r ? aQ[I][j] * e : 0.f;
-                a.wP[mo + r * CH + i] = pv;
-                if (fast && I <= R) sPm[r * PT + i] = pv;
+                if (fast) {
+                    if (I <= R) sPm[r * PT + i] = pv;
+                } else {
+                    a.wA[mo + r * CH + i] = araw;
+                    a.wP[mo + r * CH + i] = pv;
+                }
             }
         }
     }
@@ -899,13 +902,14 @@ __device__ __forceinline__ uint4 slab_col(const lchar* pl, int c0, int s, int i1
 // and <H, S> into shs[0], every slab operand a bf16 hi + lo pair.  The chunk's
 // k tile and T^ (packed lower, hi and lo) arrive with the first slab, into
 // tKs and tTs; the slab planes are in `slab`.  The last slab's turn prefetches
-// T, P, K K^T and the q rows for the 64 x 64 part (the k rows stay in tKs).
+// T, the packed P^T (hi and lo: pieces tid < 320 into ppk) and the q rows for
+// the 64 x 64 part (the k rows stay in tKs).
 template <int DK>
 __device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, int valid, size_t tok0, lchar* slab,
                                               lchar* tKs, lchar* tTs, const float* sgam,
                                               f32x4 (&z1)[DK / 32], f32x4 (&z2)[DK / 32], f32x4 (&z3)[DK / 32],
                                               f32x4 (&acc)[4], float* shs, RowsPre<DK, false, PNT>& pq,
-                                              MatPre<PNT>& pt, MatPre<PNT>& pp, MatPre<PNT>& pa) {
+                                              MatPre<PNT>& pt, uint4 (&ppk)[2]) {
     constexpr int VS = PostLds<DK>::VS, NDH = DK / 32, RB = 2 * DK;
     constexpr int NS = DK * VS / 4 / PNT;   // float4 of S (and of H) per thread and slab
     static_assert(CH * VS / 4 == PNT, "one float4 of each 64-row slab per thread");
@@ -1020,8 +1024,11 @@ __device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, int vali
         } else {
             pre_rows<DK, false, PNT>(pq, a.q, tok0, valid, tid);
             pre_mat(pt, a.wT + mo, tid);
-            pre_mat(pp, a.wP + mo, tid);
-            pre_mat(pa, a.wA + mo, tid);
+            if (tid < kTriBytes / 16) {
+                const uint4* pk2 = reinterpret_cast<const uint4*>(a.wF + (size_t)cs * kBF + kBfPt);
+                ppk[0] = pk2[tid];
+                ppk[1] = pk2[kTriBytes / 16 + tid];
+            }
         }
         // R = V - Gamma K S: this wave's block (rows 16 R .., columns 16 hf ..)
         {
@@ -1155,6 +1162,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
 
     RowsPre<DK, F32IN, PNT> pk, pq;
     MatPre<PNT> pt, pp, pa;
+    uint4 ppk[2] = {};   // bf16 inputs: the packed P^T (hi, lo), pieces tid < 320
     f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
     if constexpr (F32IN) {
         post_state_products<DK, F32IN, false>(a, cs, valid, tok0, s1, z1, z2, z3, acc, &shs, pk, pq, pt, pp, pa);
@@ -1162,7 +1170,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         static_assert(F32IN || CH * 2 * DK <= (int)sizeof(float) * CH * PT, "the k tile fits sM0");
         static_assert(F32IN || 2 * kTriBytes <= (int)sizeof(float) * CH * PT, "T^ fits sM1");
         post_slabs_rc<DK>(a, cs, valid, tok0, (lchar*)s1, (lchar*)sM0, (lchar*)sM1, sgam, z1, z2, z3, acc, &shs, pq,
-                          pt, pp, pa);
+                          pt, ppk);
     }
     lds_barrier();
 
@@ -1190,8 +1198,53 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         lds_barrier();
     }
     put_mat(pt, sM0, tid);
-    put_mat(pp, sM1, tid);
-    put_mat(pa, sM2, tid);
+    if constexpr (F32IN) {
+        put_mat(pp, sM1, tid);
+        put_mat(pa, sM2, tid);
+    } else {
+        // P from the packed P^T (hi + lo): piece tid of each plane holds row
+        // rr of upper block (3 - Rb, 3 - Ib), columns 8 ch .. +7, i.e. P at
+        // those columns' rows and that row's column; zero above P's diagonal
+        // blocks
+        if (tid < kTriBytes / 16) {
+            const int b = tid >> 5, rr = (tid >> 1) & 15, hh = tid & 1;
+            const int Rb = b >= 6 ? 3 : b >= 3 ? 2 : b >= 1 ? 1 : 0, Ib = b - Rb * (Rb + 1) / 2;
+            const int ch = hh ^ ((rr >> 3) & 1);
+            const int pr = 16 * (3 - Rb) + rr, pc0 = 16 * (3 - Ib) + 8 * ch;   // P^T row, first column
+            const uint32_t hw[4] = {ppk[0].x, ppk[0].y, ppk[0].z, ppk[0].w};
+            const uint32_t lw[4] = {ppk[1].x, ppk[1].y, ppk[1].z, ppk[1].w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float x = bf16_to_f32((uint16_t)(hw[q >> 1] >> (16 * (q & 1)))) +
+                                bf16_to_f32((uint16_t)(lw[q >> 1] >> (16 * (q & 1))));
+                sM1[(pc0 + q) * PT + pr] = x;
+            }
+        }
+        for (int e = tid; e < 6 * 256; e += PNT) {   // the six blocks above the diagonal
+            const int ub = e >> 8, rb = ub >= 5 ? 2 : ub >= 3 ? 1 : 0;   // (0,1..3) (1,2..3) (2,3)
+            const int ib = rb == 0 ? ub + 1 : rb == 1 ? ub - 1 : 3;
+            sM1[(16 * rb + ((e >> 4) & 15)) * PT + 16 * ib + (e & 15)] = 0.f;
+        }
+        // K K^T o E, strictly lower, from the k tile: row block R, column
+        // blocks 2 hf, 2 hf + 1 (zero above the diagonal blocks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int I = 2 * hf + h;
+            f32x4 ak = zero4();
+            if (I <= R) {
+#pragma unroll
+                for (int s = 0; s < DK / 32; ++s)
+                    ak = mfma_raw<true>(lds16(tile_at<RB>(tK, 16 * R + i16, 4 * s + g)),
+                                        lds16(tile_at<RB>(tK, 16 * I + i16, 4 * s + g)), ak);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
+                const float ee = __builtin_amdgcn_exp2f((sg[r] - sg[i]) * 1.4426950408889634f);
+                sM2[r * PT + i] = I <= R && i < r ? ak[j] * ee : 0.f;
+            }
+        }
+    }
     lds_barrier();
 
     const int rb = 16 * R + 4 * g;   // this lane's first accumulator row

@@ -65,6 +65,22 @@ __device__ __forceinline__ uint4 tri_frag(const lchar* tri, int w, int s, int i1
     const int b = UPPER ? tri_block(3 - w, 3 - Ic) : tri_block(w, Ic);
     return lds16(tri + b * 512 + i16 * 32 + 16 * ((g & 1) ^ ((i16 >> 3) & 1)));
 }
+// The same fragment of T^T from the packed lower T^: T^ at rows 32 s + 8 g ..
+// +7 of column 16 w + i16, through the transposing LDS read (lane q of a
+// 16-lane group addresses row 8 (g & 1) + q / 4 (+ 4) of the block and its
+// columns 4 (q & 3) .. +3).  Blocks above T^'s diagonal (2 s + g / 2 < w) read
+// a valid block; tri_mask<true> zeroes them.
+__device__ __forceinline__ uint4 tri_frag_t(const lchar* tri, int w, int s, int i16, int g) {
+    const int mb = 2 * s + (g >> 1);
+    const int b = tri_block(mb >= w ? mb : w, w);
+    const int rho = 8 * (g & 1) + (i16 >> 2);
+    const int cq = 4 * (i16 & 3);
+    auto at = [&](int r) { return tri + b * 512 + r * 32 + 16 * (((cq >> 3) & 1) ^ ((r >> 3) & 1)) + 2 * (cq & 7); };
+    const uint2 lo4 = lds_tr4(at(rho));
+    const uint2 hi4 = lds_tr4(at(rho + 4));
+    return {lo4.x, lo4.y, hi4.x, hi4.y};
+}
+
 template <bool UPPER>
 __device__ __forceinline__ void tri_mask(uint4& f, int w, int s, int g) {
     const int I = 2 * s + (g >> 1);
@@ -385,9 +401,9 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------ reverse scan
-// LDS: two operand buffers [K 64 x RB][Q 64 x RB][T^T hi][T^T lo][P^T hi]
-// [P^T lo][gate 1024] (the last five are one contiguous run of the chunk's
-// kBF slot) and the working area [H^T hi/lo][dO^T hi/lo][(Gamma dO)^T hi/lo]
+// LDS: two operand buffers [K 64 x RB][Q 64 x RB][T^ hi][T^ lo][P^T hi]
+// [P^T lo][gate 1024] (the last five are the chunk's kBF slot, one contiguous
+// run) and the working area [H^T hi/lo][dO^T hi/lo][(Gamma dO)^T hi/lo]
 // [dU^T hi/lo][(Gamma dR)^T hi/lo][H fp32][dU fp32][dR fp32].  The compute
 // waves load their own dO values one chunk ahead into registers.
 template <int DK>
@@ -395,7 +411,7 @@ struct RL {
     static constexpr int RB = DK * 2;
     static constexpr int KT = 0;
     static constexpr int QT = KT + 64 * RB;
-    static constexpr int MT = QT + 64 * RB;           // T^T hi, lo, P^T hi, lo, gate
+    static constexpr int MT = QT + 64 * RB;           // T^ hi, lo, P^T hi, lo, gate
     static constexpr int GT = MT + 4 * kTriBytes;
     static constexpr int BUF = GT + 1024;
     static constexpr int SP = (DK + 8) * 2;
@@ -462,7 +478,7 @@ __global__ __launch_bounds__(512) void bwd_rscan16_kernel(BwdArgs a) {
         copy_rows<L::RB>(uniform_ptr(qbase + (size_t)c * CH * L::RB), Lc, buf + L::QT, l, cw);
     };
     auto copy2 = [&](lchar* buf, int c) {
-        const char* fb = uniform_ptr(fbase + (size_t)c * kBF + kBfTt);
+        const char* fb = uniform_ptr(fbase + (size_t)c * kBF);
 #pragma unroll
         for (int jj = 0; jj < L::NS2; ++jj) {
             const int k = min(cw + 4 * jj, L::NSLOT - 1);   // wave-uniform; the last slot (gate) repeated
@@ -473,7 +489,7 @@ __global__ __launch_bounds__(512) void bwd_rscan16_kernel(BwdArgs a) {
     if (copier) {
         wm.region(kbase, CH * L::RB, L::RB / 2);
         wm.region(qbase, CH * L::RB, L::RB / 2);
-        wm.region(fbase + kBfTt, kBF, (4 * kTriBytes + 512) / 128);
+        wm.region(fbase, kBF, (4 * kTriBytes + 512) / 128);
         wm.region(obase - n0, CH * Dv * 4, 2 * Dv);
         wm.done();
     }
@@ -545,8 +561,8 @@ __global__ __launch_bounds__(512) void bwd_rscan16_kernel(BwdArgs a) {
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int p = 0; p < 2; ++p) {
-                    pfr[s][p] = tri_frag<true>(buf + L::MT + (2 + p) * kTriBytes, w, s, i16, g);
-                    tfr[s][p] = tri_frag<true>(buf + L::MT + p * kTriBytes, w, s, i16, g);
+                    pfr[s][p] = tri_frag<true>(buf + L::MT + kBfPt + p * kTriBytes, w, s, i16, g);
+                    tfr[s][p] = tri_frag_t(buf + L::MT + p * kTriBytes, w, s, i16, g);
                     ofr[s][p] = plane16(sO + p * 16 * RP, i16, s, g);
                 }
             float lam[4];

@@ -105,18 +105,18 @@ struct DecodeArgs {
 //   wQh = q o e^G, wKh = k o e^G, wKc = k o e^-G, wKt = k o e^(G_63 - G)
 //   wS, wH      [NCH][Dk][Dv]   chunk start state, gradient at its end state
 //   wU, wR, wdU [NCH][64][Dv]   U, R = V - Gamma K S, and dU
-// For bf16 inputs without a channel gate (wF not NULL) the prep kernel also
-// writes, per chunk, the operands of the matrix-core state scans (kBF bytes):
+// For bf16 inputs without a channel gate (wF not NULL) the prep kernel writes,
+// per chunk, the operands of the matrix-core scans and of the per-chunk
+// kernel (kBF bytes) in place of wP and wA (wU and wR are not used either):
 //   [T^ hi][T^ lo]      T^ = T Diag(beta), packed lower blocks (tri_off)
-//   [T^T hi][T^T lo]    its transpose, packed upper blocks (kBfTt)
 //   [P^T hi][P^T lo]    P transposed, packed upper blocks (kBfPt)
 //   [gamma 64][lambda 64] fp32 at kBfGate
 // as bf16 hi + lo pairs (x = hi + lo to 16 significant bits).  A packed upper
 // block (R, I), I >= R, of a 64 x 64 matrix sits where tri_block(3 - R, 3 - I)
-// puts a lower one, with the same layout inside the block.
-constexpr int kBfTt = 2 * kTriBytes;
-constexpr int kBfPt = 4 * kTriBytes;
-constexpr int kBfGate = 6 * kTriBytes;
+// puts a lower one, with the same layout inside the block.  T^T is read from
+// T^ through the transposing LDS read.
+constexpr int kBfPt = 2 * kTriBytes;
+constexpr int kBfGate = 4 * kTriBytes;
 constexpr int kBF = kBfGate + 1024;
 struct BwdArgs {
     const void* q;

@@ -285,18 +285,18 @@ def test_backward_validation_and_workspace():
         assert drl.dr_chunk_bwd_workspace_bytes(_desc(**bad)) == 0
     need = drl.dr_chunk_bwd_workspace_bytes(d)
     NCH = 2 * 3 * ((100 + 63) // 64)
-    # per chunk: T, P, K K^T (64 x 64), 64 gate values, two states and the
-    # 64 x Dv block dU, fp32 (with fp32 inputs also U and R)
-    assert need >= NCH * 4 * (3 * 64 * 64 + 64 + 2 * 128 * 128 + 64 * 128)
+    # per chunk: T (64 x 64), 64 gate values, two states and the 64 x Dv block
+    # dU, fp32 (with fp32 inputs also P, K K^T o E, U and R)
+    assert need >= NCH * 4 * (64 * 64 + 64 + 2 * 128 * 128 + 64 * 128)
     assert call(d, ws=None) == drl.DR_ERR_WORKSPACE
     assert call(d, wbytes=need - 1) == drl.DR_ERR_WORKSPACE
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(L=0)) == 0
     # bf16 inputs that the kernels see as they are, without a channel gate:
-    # the matrix-core scans' operands, 31744 bytes per chunk (T^, T^T and P^T
-    # as bf16 hi and lo packed triangles, gamma and lambda), and no U or R
-    # (the per-chunk kernel forms them again)
+    # the matrix-core operands, 21504 bytes per chunk (T^ and P^T as bf16 hi
+    # and lo packed triangles, gamma and lambda), in place of the fp32 P and
+    # K K^T o E planes, and no U or R (the per-chunk kernel forms them again)
     base = drl.dr_chunk_bwd_workspace_bytes(_desc(in_dtype=drl.DR_F32))
-    assert need == base + NCH * 31744 - 2 * NCH * 64 * 128 * 4
+    assert need == base + NCH * 21504 - 2 * NCH * 64 * 64 * 4 - 2 * NCH * 64 * 128 * 4
     # a channel gate adds the per-channel decay and four gated operand planes
     assert drl.dr_chunk_bwd_workspace_bytes(_desc(gate="channel")) >= base + NCH * 4 * 5 * 64 * 128 - NCH * 4 * 64
     # a channel beta runs the unit-strength kernels on fp32 copies of q, sqrt(beta) k, sqrt(beta) v
