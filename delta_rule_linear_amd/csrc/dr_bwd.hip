@@ -1282,7 +1282,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
                 const float pd_ = x * sM1[r * PT + i];
                 rowg[j] += pd_;
                 colg[I] -= pd_;
-                sM3[r * PT + i] = lo ? x * expf(sg[r] - sg[i]) : 0.f;
+                sM3[r * PT + i] = lo ? x * __builtin_amdgcn_exp2f((sg[r] - sg[i]) * 1.4426950408889634f) : 0.f;
             } else {
                 colb[I] += x * sM0[r * PT + i];
                 sM4[r * PT + i] = x * sb[i];
@@ -1290,16 +1290,17 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         }
     }
     lds_barrier();
-    // Y = T^T dT  (rows 16 R .., column blocks 2 hf, 2 hf + 1; T[m][a] vanishes for m < a)
-    f32x4 y[2];
+    // Y = T^T dT  (rows 16 R .., column blocks 2 hf, 2 hf + 1).  T holds exact
+    // zeros above its diagonal (T[m][a] = 0 for m < a), so the contraction runs
+    // over all 64 rows m with a fixed trip count: every operand read is issued
+    // ahead of the products instead of one LDS round trip per k-step.
+    f32x4 y[2] = {zero4(), zero4()};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int I = 2 * hf + h;
-        y[h] = zero4();
-        for (int s = 4 * R; s < 16; ++s) {
-            const int m = 4 * s + g;
-            y[h] = mfma_f32x4(sM0[m * PT + 16 * R + i16], sM4[m * PT + 16 * I + i16], y[h]);
-        }
+    for (int s = 0; s < 16; ++s) {
+        const int m = 4 * s + g;
+        const float tv = sM0[m * PT + 16 * R + i16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) y[h] = mfma_f32x4(tv, sM4[m * PT + 16 * (2 * hf + h) + i16], y[h]);
     }
     lds_barrier();
 #pragma unroll
@@ -1308,13 +1309,15 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         for (int j = 0; j < 4; ++j) sM4[(rb + j) * PT + 16 * (2 * hf + h) + i16] = y[h][j];
     lds_barrier();
     // dA = -Y T^T on the strict lower part, then M = Diag(beta) (dA o E) into
-    // sM1 (P is no longer read)
+    // sM1 (P is no longer read).  T[c][m] = 0 for m > c: the contraction runs
+    // over all 64 m with a fixed trip count, as for Y.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int I = 2 * hf + h;
         f32x4 da = zero4();
         if (I <= R) {
-            for (int s = 0; s < 4 * (I + 1); ++s) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 da = mfma_f32x4(sM4[(16 * R + i16) * PT + m], sM0[(16 * I + i16) * PT + m], da);
             }
@@ -1329,7 +1332,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
             const float ad = sb[r] * adr;
             rowg[j] += ad;
             colg[I] -= ad;
-            sM1[r * PT + cc] = lo ? dav * sb[r] * expf(sg[r] - sg[cc]) : 0.f;
+            sM1[r * PT + cc] = lo ? dav * sb[r] * __builtin_amdgcn_exp2f((sg[r] - sg[cc]) * 1.4426950408889634f) : 0.f;
         }
     }
     lds_barrier();
