@@ -265,8 +265,27 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, i16 = l & 15, g = l >> 4;
     const size_t mo = (size_t)cs * CH * CH;
 
-    load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
-    load_rows<DK, F32IN>(sQ, a.q, tok0, valid, tid);
+    // bf16 inputs: the raw k and q rows as bf16 tiles (16-byte pieces
+    // XOR-swizzled by row), the matrix-core operands of the products below;
+    // fp32 inputs: fp32 rows
+    constexpr int RB = 2 * DK;
+    lchar* tK = (lchar*)sKQ;
+    lchar* tQ = tK + CH * RB;
+    if constexpr (F32IN) {
+        load_rows<DK, F32IN>(sK, a.k, tok0, valid, tid);
+        load_rows<DK, F32IN>(sQ, a.q, tok0, valid, tid);
+    } else {
+        static_assert(2 * CH * RB <= (int)sizeof(float) * 2 * CH * KP, "the bf16 tiles fit");
+        const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + tok0 * DK);
+        const uint4* qs = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + tok0 * DK);
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int e = tid; e < CH * (DK / 8); e += NTH) {
+            const int r = e / (DK / 8), pc = e % (DK / 8);
+            const int at = r * RB + 16 * (pc ^ swz<RB>(r));
+            lds_st(tK + at, r < valid ? ks[e] : z);
+            lds_st(tQ + at, r < valid ? qs[e] : z);
+        }
+    }
     if (tid < CH) {
         const bool ok = tid < valid;
         sb[tid] = ok ? a.beta[tok0 + tid] : 0.f;
@@ -291,11 +310,23 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
         for (int I = 0; I < 4; ++I) {
             aK[I] = aQ[I] = zero4();
             if (I <= R) {
-                for (int s = 0; s < DK / 4; ++s) {
-                    const int m = 4 * s + g;
-                    const float kb = sK[(16 * I + i16) * KP + m];
-                    aK[I] = mfma_f32x4(sK[(16 * R + i16) * KP + m], kb, aK[I]);
-                    aQ[I] = mfma_f32x4(sQ[(16 * R + i16) * KP + m], kb, aQ[I]);
+                if constexpr (F32IN) {
+                    for (int s = 0; s < DK / 4; ++s) {
+                        const int m = 4 * s + g;
+                        const float kb = sK[(16 * I + i16) * KP + m];
+                        aK[I] = mfma_f32x4(sK[(16 * R + i16) * KP + m], kb, aK[I]);
+                        aQ[I] = mfma_f32x4(sQ[(16 * R + i16) * KP + m], kb, aQ[I]);
+                    }
+                } else {
+                    // bf16 x bf16 products are exact in fp32: the 16 x 16 x 32
+                    // ops on the raw tiles (rows 16 R + i16 and 16 I + i16,
+                    // columns 32 s + 8 g .. + 7), same output fragments
+#pragma unroll
+                    for (int s = 0; s < DK / 32; ++s) {
+                        const uint4 kb = lds16(tile_at<RB>(tK, 16 * I + i16, 4 * s + g));
+                        aK[I] = mfma_raw<true>(lds16(tile_at<RB>(tK, 16 * R + i16, 4 * s + g)), kb, aK[I]);
+                        aQ[I] = mfma_raw<true>(lds16(tile_at<RB>(tQ, 16 * R + i16, 4 * s + g)), kb, aQ[I]);
+                    }
                 }
             }
         }
@@ -305,7 +336,7 @@ __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * R + 4 * g + j, i = 16 * I + i16;
-                const float e = i <= r ? expf(sg[r] - sg[i]) : 0.f;
+                const float e = i <= r ? __builtin_amdgcn_exp2f((sg[r] - sg[i]) * 1.4426950408889634f) : 0.f;
                 const float araw = i < r ? aK[I][j] * e : 0.f;
                 sA[r * PT + i] = sb[r] * araw;
                 const float pv = i <= r ? aQ[I][j] * e : 0.f;
