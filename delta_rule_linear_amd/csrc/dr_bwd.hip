@@ -1561,10 +1561,16 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
         sG[r * KP + c4 + 3] = x.w;
     }
     lds_barrier();
+    // each channel's 64 values into registers first (independent reads), the
+    // running sum there, then back
     for (int ch = tid; ch < DK; ch += NTH) {
+        float v[CH];
+#pragma unroll
+        for (int r = 0; r < CH; ++r) v[r] = sG[r * KP + ch];
         float G = 0.f;
+#pragma unroll
         for (int r = 0; r < CH; ++r) {
-            G += sG[r * KP + ch];
+            G += v[r];
             sG[r * KP + ch] = G;
         }
         if (G < kShiftBelow) s_shift = 1;
@@ -1584,14 +1590,16 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
         for (int j = 0; j < 8; ++j) {
             const float G = sG[r * KP + c8 + j], G63 = sG[(CH - 1) * KP + c8 + j];
             const float Gm = shift ? 0.5f * G63 : 0.f;
-            const float eg = expf(G), emg = expf(Gm - G);
+            // e^x as the hardware 2^(x log2 e)
+            auto ex = [](float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); };
+            const float eg = ex(G), emg = ex(Gm - G);
             const float wk = a.ks ? wx[j] * kx[j] : kx[j];   // the write key
             gg[j] = G;
             gq[j] = qx[j] * eg;
             gh[j] = kx[j] * eg;
             gc[j] = wk * emg;
-            gt[j] = wk * expf(G63 - G);
-            const float es = shift ? expf(G - Gm) : eg;
+            gt[j] = wk * ex(G63 - G);
+            const float es = shift ? ex(G - Gm) : eg;
             sQh[r * KP + c8 + j] = qx[j] * es;
             sKh[r * KP + c8 + j] = kx[j] * es;
             sKc[r * KP + c8 + j] = gc[j];
