@@ -428,7 +428,9 @@ __global__ __launch_bounds__(SNT) void bwd_fscan_kernel(BwdArgs a) {
         if (c + 1 < a.NC) prefetch(c + 1);
         // X = K S over this wave's half of the contraction
         f32x4 X = zero4();
-        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) {
+            const int s = h * NKS + s2;
             const int m = 4 * s + g;
             X = mfma_f32x4(sK[(16 * R + i16) * KP + m], sS[m * 17 + i16], X);
         }
@@ -452,7 +454,9 @@ __global__ __launch_bounds__(SNT) void bwd_fscan_kernel(BwdArgs a) {
         if (h == 0) {
             // U = T Diag(beta) R
             f32x4 U = zero4();
-            for (int s = 0; s < 4 * (R + 1); ++s) {
+            // the factor's row 16 R + i16 is zero past the diagonal: all 16 k-steps
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 U = mfma_f32x4(sT[(16 * R + i16) * PT + m] * sb[m], sR[m * 17 + i16], U);
             }
@@ -567,13 +571,17 @@ __global__ __launch_bounds__(SNT) void bwd_rscan_kernel(BwdArgs a) {
         // dU = P^T dO + Lambda K H  (rows 16 R ..): K H over this wave's half
         // of the contraction; the upper half also takes P^T dO
         f32x4 Z = zero4();
-        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) {
+            const int s = h * NKS + s2;
             const int m = 4 * s + g;
             Z = mfma_f32x4(sK[(16 * R + i16) * KP + m], sH[m * 17 + i16], Z);
         }
         if (h == 1) {
             f32x4 Y = zero4();
-            for (int s = 4 * R; s < 16; ++s) {
+            // the factor's column 16 R + i16 is zero above the diagonal: all 16 k-steps
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 Y = mfma_f32x4(sP[m * PT + 16 * R + i16], sO[m * 17 + i16], Y);
             }
@@ -597,7 +605,9 @@ __global__ __launch_bounds__(SNT) void bwd_rscan_kernel(BwdArgs a) {
         // dR = Diag(beta) T^T dU
         f32x4 Rr = zero4();
         if (h == 0) {
-            for (int s = 4 * R; s < 16; ++s) {
+            // the factor's column 16 R + i16 is zero above the diagonal: all 16 k-steps
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 Rr = mfma_f32x4(sT[m * PT + 16 * R + i16], sD[m * 17 + i16], Rr);
             }
@@ -1711,7 +1721,9 @@ __global__ __launch_bounds__(SNT) void bwd_fscan_cg_kernel(BwdArgs a) {
         if (c + 1 < a.NC) prefetch(c + 1);
         // X = K^ S over this wave's half of the contraction
         f32x4 X = zero4();
-        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) {
+            const int s = h * NKS + s2;
             const int m = 4 * s + g;
             X = mfma_f32x4(sKh[(16 * R + i16) * KP + m], sS[m * 17 + i16], X);
         }
@@ -1733,7 +1745,9 @@ __global__ __launch_bounds__(SNT) void bwd_fscan_cg_kernel(BwdArgs a) {
         if (h == 0) {
             // U = T Diag(beta) R
             f32x4 U = zero4();
-            for (int s = 0; s < 4 * (R + 1); ++s) {
+            // the factor's row 16 R + i16 is zero past the diagonal: all 16 k-steps
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 U = mfma_f32x4(sT[(16 * R + i16) * PT + m] * sb[m], sR[m * 17 + i16], U);
             }
@@ -1837,13 +1851,17 @@ __global__ __launch_bounds__(SNT) void bwd_rscan_cg_kernel(BwdArgs a) {
         // dU = P^T dO + K~ H  (rows 16 R ..): K~ H over this wave's half of
         // the contraction; the upper half also takes P^T dO
         f32x4 Z = zero4();
-        for (int s = h * NKS; s < (h + 1) * NKS; ++s) {
+#pragma unroll
+        for (int s2 = 0; s2 < NKS; ++s2) {
+            const int s = h * NKS + s2;
             const int m = 4 * s + g;
             Z = mfma_f32x4(sKt[(16 * R + i16) * KP + m], sH[m * 17 + i16], Z);
         }
         if (h == 1) {
             f32x4 Y = zero4();
-            for (int s = 4 * R; s < 16; ++s) {
+            // the factor's column 16 R + i16 is zero above the diagonal: all 16 k-steps
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 Y = mfma_f32x4(sP[m * PT + 16 * R + i16], sO[m * 17 + i16], Y);
             }
@@ -1864,7 +1882,9 @@ __global__ __launch_bounds__(SNT) void bwd_rscan_cg_kernel(BwdArgs a) {
         // dR = Diag(beta) T^T dU
         f32x4 Rr = zero4();
         if (h == 0) {
-            for (int s = 4 * R; s < 16; ++s) {
+            // the factor's column 16 R + i16 is zero above the diagonal: all 16 k-steps
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 Rr = mfma_f32x4(sT[m * PT + 16 * R + i16], sD[m * 17 + i16], Rr);
             }
@@ -2014,7 +2034,9 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     for (int hh = 0; hh < 2; ++hh) {
         const int I = 2 * hf + hh;
         y[hh] = zero4();
-        for (int s = 4 * R; s < 16; ++s) {
+        // the factor's column 16 R + i16 is zero above the diagonal: all 16 k-steps
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
             const int m = 4 * s + g;
             y[hh] = mfma_f32x4(sM0[m * PT + 16 * R + i16], sM4[m * PT + 16 * I + i16], y[hh]);
         }
@@ -2050,13 +2072,17 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
 #pragma unroll
     for (int D = 0; D < NDH; ++D) {
         const int cb = 16 * (D0 + D) + i16;
-        for (int s = 0; s < 4 * (R + 1); ++s) {
+        // the factor's row 16 R + i16 is zero past the diagonal: all 16 k-steps
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
             const int m = 4 * s + g;
             const float kb = sKx[m * KP + cb];
             dqh[D] = mfma_f32x4(sM3[(16 * R + i16) * PT + m], kb, dqh[D]);
             dkh[D] = mfma_f32x4(sM1[(16 * R + i16) * PT + m], kb, dkh[D]);
         }
-        for (int s = 4 * R; s < 16; ++s) {
+        // the factor's column 16 R + i16 is zero above the diagonal: all 16 k-steps
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
             const int m = 4 * s + g;
             dkc[D] = mfma_f32x4(sM3[m * PT + 16 * R + i16], sQh[m * KP + cb], dkc[D]);
         }
@@ -2069,7 +2095,9 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
 #pragma unroll
     for (int D = 0; D < NDH; ++D) {
         const int cb = 16 * (D0 + D) + i16;
-        for (int s = 4 * R; s < 16; ++s) {
+        // the factor's column 16 R + i16 is zero above the diagonal: all 16 k-steps
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
             const int m = 4 * s + g;
             dkc[D] = mfma_f32x4(sM1[m * PT + 16 * R + i16], sKx[m * KP + cb], dkc[D]);
         }
