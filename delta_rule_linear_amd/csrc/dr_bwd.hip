@@ -2053,7 +2053,9 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
         const int I = 2 * hf + hh;
         f32x4 da = zero4();
         if (I <= R) {
-            for (int s = 0; s < 4 * (I + 1); ++s) {
+            // T's row 16 I + i16 is zero past the diagonal: all 16 k-steps
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
                 const int m = 4 * s + g;
                 da = mfma_f32x4(sM4[(16 * R + i16) * PT + m], sM0[(16 * I + i16) * PT + m], da);
             }
@@ -2119,6 +2121,8 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     float* sXg = s1;
     float* sYg = s1 + CH * KP;
     if (shift) __threadfence_block();   // the partial dq, dk stores above, read back by the same lanes
+    // e^x as the hardware 2^(x log2 e)
+    auto ex = [](float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); };
 #pragma unroll
     for (int D = 0; D < NDH; ++D) {
         const int col = 16 * (D0 + D) + i16;
@@ -2129,12 +2133,12 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
             const size_t at = pofs + (size_t)r * DK + col;
             const float G = a.wG[at];
             const float xq = dqh[D][j], xh = dkh[D][j], xc = dkc[D][j], xt = dkt[D][j];
-            const float et = expf(G63 - G);
+            const float et = ex(G63 - G);
             if (shift) {
                 // every term relative to G_m: dq = z1 e^G + xq e^(G - G_m),
                 // dk_read likewise, Kc's term e^(G_m - G); X and Y from the
                 // inputs and the complete gradients
-                const float Gm = 0.5f * G63, es = expf(G - Gm), ems = expf(Gm - G);
+                const float Gm = 0.5f * G63, es = ex(G - Gm), ems = ex(Gm - G);
                 const size_t e = (tok0 + r) * DK + col;
                 const bool ok = r < valid;
                 const float qv = ok ? load1<F32IN>(a.q, e) : 0.f, kv = ok ? load1<F32IN>(a.k, e) : 0.f;
@@ -2151,7 +2155,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
                 }
                 continue;
             }
-            const float eg = expf(G), emg = expf(-G);
+            const float eg = ex(G), emg = ex(-G);
             sXg[r * KP + col] = xq * a.wQh[at] + xh * a.wKh[at] - xc * a.wKc[at];
             sYg[r * KP + col] = xt * a.wKt[at];
             if (r < valid) {
