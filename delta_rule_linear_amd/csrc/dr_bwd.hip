@@ -245,8 +245,9 @@ template <int DK, bool F32IN>
 __global__ __launch_bounds__(NTH) void bwd_prep_kernel(BwdArgs a) {
     constexpr int KP = DK + 1;
     static_assert(2 * CH * PT <= 2 * CH * KP, "A and T fit where q and k were");
-    // q and k rows, then (once the products are in registers) A and T, and
-    // (bf16 inputs) P beside them when it fits
+    // the k and q rows (fp32 for fp32 inputs; the raw bf16 tiles for bf16
+    // inputs), then (once the products are in registers) A and T, and (bf16
+    // inputs) P beside them when it fits
     constexpr bool PFIT = 3 * CH * PT <= 2 * CH * KP;
     __shared__ float sKQ[2 * CH * KP];
     __shared__ float sPx[!F32IN && !PFIT ? CH * PT : 1];
