@@ -1147,6 +1147,8 @@ static hipError_t launch_chunk_t(const ChunkArgs& a, hipStream_t st) {
         hipError_t e;
         if constexpr (!F32IN && !CGATE && !CBETA) {
             e = launch_prep16(a, DK, st);
+        } else if constexpr (CGATE && !F32IN) {
+            e = launch_prepcg16(a, DK, CBETA, SEPV, st);
         } else if constexpr (CGATE) {
             auto kern = prep_kernel<DK, F32IN, CGATE, CBETA, SEPV, QKN, KS>;
             const long njobs = (long)nseq * a.NC;

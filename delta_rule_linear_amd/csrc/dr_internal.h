@@ -190,6 +190,9 @@ hipError_t launch_chunk(const ChunkArgs& a, int Dk, bool f32in, bool cgate, bool
                         hipStream_t st);
 // chunk preparation for bf16 inputs, scalar gate and scalar beta (dr_prep16.hip)
 hipError_t launch_prep16(const ChunkArgs& a, int Dk, hipStream_t st);
+// the same with a channel-wise gate, or with write-side key scales and any
+// gate (dr_prepcg16.hip)
+hipError_t launch_prepcg16(const ChunkArgs& a, int Dk, bool cbeta, bool sepv, hipStream_t st);
 // the state scan for bf16 inputs (dr_scan16.hip)
 hipError_t launch_scan16(const ChunkArgs& a, int Dk, bool cgate, bool cbeta, hipStream_t st);
 // the backward (dr_bwd.hip)
