@@ -26,8 +26,10 @@
 //         cores, T = (I + A)^-1 by blocked forward substitution in fp32,
 //         writes T^ and P, the gate factors, and for channel-wise gates /
 //         betas the gated fp16 operands the scan needs.  Used for fp32 inputs
-//         and for channel-wise gates or betas; bf16 inputs with a scalar gate
-//         and beta use prep16_kernel (dr_prep16.hip).
+//         and for bf16 inputs with a scalar gate and a channel-wise beta;
+//         other bf16 inputs use prep16_kernel (dr_prep16.hip, scalar gate and
+//         beta) or prepcg16_kernel (dr_prepcg16.hip, channel-wise gate or
+//         write-side key scales).
 //   scan  (fp32 inputs) one workgroup per (sequence, 16-column tile of S):
 //         walks the chunks in order holding its fp32 S tile in registers; per
 //         chunk X = Ks S, R = V - g X, U = T^ R, O = g Q S + P U,
