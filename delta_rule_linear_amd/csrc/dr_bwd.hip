@@ -1659,6 +1659,281 @@ __global__ __launch_bounds__(NTH) void bwd_prep_cg_kernel(BwdArgs a) {
     tri_inverse(sA, sT, sX, a.wT + mo, tid);
 }
 
+// bf16 inputs: the same outputs from one workgroup per chunk with the rows in
+// the 16x16x32 operand layout (as in the forward's channel-gate preparation):
+// wave w owns rows 16 w .. 16 w + 15, lane (i16, g) row 16 w + i16 at
+// channels 32 s + 8 g .. + 7, so a row's inputs stay in its lane.  The gate's
+// prefix over a block's 16 rows runs across a DPP row; one thread per channel
+// combines the four blocks into per-block constants (E_b: G at the end of
+// block b, E_{-1} = 0, T_b = E_b - E_{b-1}).  Per element two exponentials
+// inside the row's own block, y = e^{G_r - E_{w-1}} and z = e^{E_w - G_r}:
+//   e^G = e^{E_{w-1}} y,  e^{G_63 - G} = e^{G_63 - E_w} z,
+//   e^{G_m - G} = e^{G_m - E_w} z,  e^{G - G_m} = e^{E_{w-1} - G_m} y
+// (G_m = 0, or G_63 / 2 for a shifted chunk).  The 64 x 64 products run on
+// bf16 ops with hi + lo operands (16 significant bits each, three ops per
+// product); the column side of blocks 0..2 goes through LDS, the diagonal
+// pair takes both sides from registers.
+template <int DK>
+struct BPC16 {
+    static constexpr int RB = DK * 2;             // bytes per bf16 row
+    static constexpr int KC = 0;                  // column side, blocks 0..2: hi [48][RB], then lo
+    static constexpr int GS = 0;                  // in-block gate sums [4][DK], read before the tiles are written
+    static constexpr int CT = 2 * 48 * RB;        // constants [CB_ROWS][DK]
+    static constexpr int CTE = CT + 24 * DK * 4;
+    static constexpr int SA = 0;                  // A, T and the solve's scratch once the products are formed
+    static constexpr int ST = SA + CH * PT * 4;
+    static constexpr int SX = ST + CH * PT * 4;
+    static constexpr int SXE = SX + 4 * 16 * 17 * 4;
+    static constexpr int SB = SXE > CTE ? SXE : CTE;
+    static constexpr int FL = SB + CH * 4;
+    static constexpr int TOTAL = FL + 16;
+    static_assert(4 * DK * 4 <= CT, "the gate sums fit under the tiles");
+};
+// constant rows (+ block b): T_b, E_{b-1}, e^{E_{b-1}}, e^{G_63 - E_b},
+// e^{G_m - E_b}, e^{E_{b-1} - G_m}
+enum { CB_T = 0, CB_EP = 4, CB_C1 = 8, CB_C2 = 12, CB_C3 = 16, CB_C4 = 20 };
+
+// Lane i of each 16-lane row receives lane i - N of that row, 0 for i < N.
+template <int N>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, false));
+}
+
+// Eight floats from 16-byte aligned shared memory.
+__device__ __forceinline__ void ld8f(const float* p, float* x) {
+    const float4 u = reinterpret_cast<const float4*>(p)[0];
+    const float4 v = reinterpret_cast<const float4*>(p)[1];
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+}
+
+template <int DK>
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3, 8))) void bwd_prep_cg16_kernel(BwdArgs a) {
+    using L = BPC16<DK>;
+    constexpr int NS = DK / 32;
+    constexpr float kL2E = 1.4426950408889634f;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    lchar* sKc = (lchar*)(smem + L::KC);
+    float* sGS = reinterpret_cast<float*>(smem + L::GS);
+    float* sCT = reinterpret_cast<float*>(smem + L::CT);
+    float* sA = reinterpret_cast<float*>(smem + L::SA);
+    float* sT = reinterpret_cast<float*>(smem + L::ST);
+    float(*sX)[16 * 17] = reinterpret_cast<float(*)[16 * 17]>(smem + L::SX);
+    float* sb = reinterpret_cast<float*>(smem + L::SB);
+    int* sflag = reinterpret_cast<int*>(smem + L::FL);
+
+    const int cs = blockIdx.x;
+    const int seq = cs / a.NC, c = cs - seq * a.NC;
+    const int t0 = c * CH, valid = min(CH, a.L - t0);
+    const size_t tok0 = (size_t)seq * a.L + t0;
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: its branches are scalar
+    const int i16 = l & 15, g = l >> 4;
+    const int r = 16 * w + i16;
+    const bool live = r < valid;
+    const size_t row = tok0 + (live ? r : 0);   // rows past the end load row 0 and are masked
+    const size_t mo = (size_t)cs * CH * CH, po = (size_t)cs * CH * DK + (size_t)r * DK;
+    auto ex = [](float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); };
+
+    // ------------------------------------------------------------ loads
+    uint4 kr[NS], qr[NS];
+    float G[NS][8];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int c0 = 32 * s + 8 * g;
+        kr[s] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * DK + c0);
+        qr[s] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + row * DK + c0);
+        if (a.gmode == 2) {
+            load_f32_n<8>(a.log_alpha + row * DK + c0, G[s]);
+        } else {
+            const float x = a.gmode == 1 ? a.log_alpha[row] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) G[s][j] = x;
+        }
+    }
+    if (!live) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) kr[s] = qr[s] = uint4{0u, 0u, 0u, 0u};
+    }
+    if (g == 0) sb[r] = live ? a.beta[row] : 0.f;
+    if (tid == 0) sflag[0] = 0;
+
+    // ------------------------------------ the gate's prefix inside the block
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float x = live ? G[s][j] : 0.f;
+            x += dpp_row_shr<1>(x);
+            x += dpp_row_shr<2>(x);
+            x += dpp_row_shr<4>(x);
+            x += dpp_row_shr<8>(x);
+            G[s][j] = x;   // sum over rows 16 w .. r
+        }
+    if (i16 == 15) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float* d = sGS + w * DK + 32 * s + 8 * g;
+            reinterpret_cast<float4*>(d)[0] = make_float4(G[s][0], G[s][1], G[s][2], G[s][3]);
+            reinterpret_cast<float4*>(d)[1] = make_float4(G[s][4], G[s][5], G[s][6], G[s][7]);
+        }
+    }
+    lds_barrier();
+    // one thread per channel: the block constants, and whether the chunk is
+    // shifted (some channel's G_63 below kShiftBelow); then the constants
+    // that depend on the shift
+    float E[4] = {0.f, 0.f, 0.f, 0.f};
+    if (tid < DK) {
+        float run = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float t = sGS[b * DK + tid];
+            run += t;
+            E[b] = run;
+            const float ep = b > 0 ? E[b - 1] : 0.f;
+            sCT[(CB_T + b) * DK + tid] = t;
+            sCT[(CB_EP + b) * DK + tid] = ep;
+        }
+        if (E[3] < kShiftBelow) atomicOr(sflag, 1);
+    }
+    lds_barrier();
+    const bool shift = sflag[0] != 0;   // workgroup-uniform
+    if (tid < DK) {
+        const float gm = shift ? 0.5f * E[3] : 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float ep = b > 0 ? E[b - 1] : 0.f;
+            sCT[(CB_C1 + b) * DK + tid] = ex(ep);
+            sCT[(CB_C2 + b) * DK + tid] = ex(E[3] - E[b]);
+            sCT[(CB_C3 + b) * DK + tid] = ex(gm - E[b]);
+            sCT[(CB_C4 + b) * DK + tid] = ex(ep - gm);
+        }
+    }
+    lds_barrier();
+
+    // ----- planes, the column-side tiles and the diagonal pair (own rows);
+    // the row side of the off-diagonal pairs (k e^{G - G_m}, q e^{G - G_m})
+    // stays as bf16 hi + lo fragments
+    uint4 fk[NS][2], fq[NS][2];
+    f32x4 dA = zero4(), dP = zero4();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int c0 = 32 * s + 8 * g;
+        // (a) the two exponentials and the five workspace planes
+        float kx[8], qx[8], y[8], pc[8];
+        {
+            float tw[8], ep[8], c1[8], c2[8], c3[8], wk[8];
+            ld8f(sCT + (CB_T + w) * DK + c0, tw);
+            ld8f(sCT + (CB_EP + w) * DK + c0, ep);
+            ld8f(sCT + (CB_C1 + w) * DK + c0, c1);
+            ld8f(sCT + (CB_C2 + w) * DK + c0, c2);
+            ld8f(sCT + (CB_C3 + w) * DK + c0, c3);
+            unpack_bf16x8(kr[s], kx);
+            unpack_bf16x8(qr[s], qx);
+            if (a.ks) load_f32_n<8>(a.ks + row * DK + c0, wk);
+            float pg[8], pq[8], ph[8], pt[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float gl = G[s][j];
+                y[j] = ex(gl);
+                const float z = ex(tw[j] - gl);
+                const float eg = c1[j] * y[j];
+                const float wz = (a.ks ? wk[j] * kx[j] : kx[j]) * z;   // the write key times z
+                pg[j] = gl + ep[j];
+                pq[j] = qx[j] * eg;
+                ph[j] = kx[j] * eg;
+                pc[j] = wz * c3[j];
+                pt[j] = wz * c2[j];
+            }
+            float* const dst[5] = {a.wG + po + c0, a.wQh + po + c0, a.wKh + po + c0, a.wKc + po + c0,
+                                   a.wKt + po + c0};
+            const float* const src[5] = {pg, pq, ph, pc, pt};
+#pragma unroll
+            for (int t = 0; t < 5; ++t) {
+                reinterpret_cast<float4*>(dst[t])[0] = make_float4(src[t][0], src[t][1], src[t][2], src[t][3]);
+                reinterpret_cast<float4*>(dst[t])[1] = make_float4(src[t][4], src[t][5], src[t][6], src[t][7]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // (b) the row and column sides of the products as bf16 hi + lo
+        uint16_t akh[8], akl[8], aqh[8], aql[8], bh[8], bl[8];
+        {
+            float c4[8];
+            ld8f(sCT + (CB_C4 + w) * DK + c0, c4);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float es = y[j] * c4[j];   // e^{G - G_m}
+                split_bf16(kx[j] * es, akh[j], akl[j]);
+                split_bf16(qx[j] * es, aqh[j], aql[j]);
+                split_bf16(pc[j], bh[j], bl[j]);
+            }
+        }
+        auto pack = [](const uint16_t* x) {
+            return uint4{x[0] | ((uint32_t)x[1] << 16), x[2] | ((uint32_t)x[3] << 16), x[4] | ((uint32_t)x[5] << 16),
+                         x[6] | ((uint32_t)x[7] << 16)};
+        };
+        fk[s][0] = pack(akh);
+        fk[s][1] = pack(akl);
+        fq[s][0] = pack(aqh);
+        fq[s][1] = pack(aql);
+        const uint4 b0 = pack(bh), b1 = pack(bl);
+        if (w < 3) {
+            const int at = r * L::RB + 16 * ((4 * s + g) ^ swz<L::RB>(r));   // as tile_at
+            lds_st(sKc + at, b0);
+            lds_st(sKc + 48 * L::RB + at, b1);
+        }
+        dA = mfma_raw<true>(fk[s][0], b0, dA);
+        dA = mfma_raw<true>(fk[s][0], b1, dA);
+        dA = mfma_raw<true>(fk[s][1], b0, dA);
+        dP = mfma_raw<true>(fq[s][0], b0, dP);
+        dP = mfma_raw<true>(fq[s][0], b1, dP);
+        dP = mfma_raw<true>(fq[s][1], b0, dP);
+        __builtin_amdgcn_sched_barrier(0);   // one slice of channels at a time: fewer live registers
+    }
+    lds_barrier();   // the column-side tiles are complete
+
+    // ------------------------- off-diagonal pairs (w, I), I < w, on bf16 ops
+    f32x4 oA[3], oP[3];
+#pragma unroll
+    for (int I = 0; I < 3; ++I) oA[I] = oP[I] = zero4();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+#pragma unroll
+        for (int I = 0; I < 3; ++I) {
+            if (I < w) {   // wave-uniform
+                const uint4 b0 = lds16(tile_at<L::RB>(sKc, 16 * I + i16, 4 * s + g));
+                const uint4 b1 = lds16(tile_at<L::RB>(sKc + 48 * L::RB, 16 * I + i16, 4 * s + g));
+                oA[I] = mfma_raw<true>(fk[s][0], b0, oA[I]);
+                oA[I] = mfma_raw<true>(fk[s][0], b1, oA[I]);
+                oA[I] = mfma_raw<true>(fk[s][1], b0, oA[I]);
+                oP[I] = mfma_raw<true>(fq[s][0], b0, oP[I]);
+                oP[I] = mfma_raw<true>(fq[s][0], b1, oP[I]);
+                oP[I] = mfma_raw<true>(fq[s][1], b0, oP[I]);
+            }
+        }
+    }
+    lds_barrier();   // every product is formed: A, T and the scratch take the tiles' place
+
+    // K^ Kc^T (strict lower, without beta) and Q^ Kc^T (lower) of block row w
+    // to the workspace, zeros above the diagonal blocks; beta-scaled A to LDS
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+        const f32x4 cA = I == w ? dA : I == 0 ? oA[0] : I == 1 ? oA[1] : oA[2];
+        const f32x4 cP = I == w ? dP : I == 0 ? oP[0] : I == 1 ? oP[1] : oP[2];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 16 * w + 4 * g + j, ii = 16 * I + i16;
+            const float araw = I <= w && ii < rr ? cA[j] : 0.f;
+            sA[rr * PT + ii] = sb[rr] * araw;
+            a.wA[mo + rr * CH + ii] = araw;
+            a.wP[mo + rr * CH + ii] = I <= w && ii <= rr ? cP[j] : 0.f;
+        }
+    }
+    lds_barrier();
+    tri_inverse(sA, sT, sX, a.wT + mo, tid);
+}
+
 template <int DK, bool F32IN>
 __global__ __launch_bounds__(SNT) void bwd_fscan_cg_kernel(BwdArgs a) {
     constexpr int KP = DK + 1, NKS = DK / 8;
@@ -2207,7 +2482,14 @@ template <int DK, bool F32IN>
 hipError_t launch_bwd_cg_t(const BwdArgs& a, hipStream_t st) {
     const unsigned nch = (unsigned)a.nseq * (unsigned)a.NC;
     const unsigned nscan = (unsigned)((a.nseq + 7) / 8) * 8u * (unsigned)(a.Dv / 16);
-    hipError_t e = launch_k(kProfBwdPrep, bwd_prep_cg_kernel<DK, F32IN>, dim3(nch), dim3(NTH), 0, st, a);
+    hipError_t e;
+    if constexpr (F32IN) {
+        e = launch_k(kProfBwdPrep, bwd_prep_cg_kernel<DK, F32IN>, dim3(nch), dim3(NTH), 0, st, a);
+    } else {
+        constexpr int lds = BPC16<DK>::TOTAL;
+        static_assert(lds <= 64 * 1024, "LDS plan of the channel-gate backward preparation");
+        e = launch_k(kProfBwdPrep, bwd_prep_cg16_kernel<DK>, dim3(nch), dim3(NTH), lds, st, a);
+    }
     if (e == hipSuccess)
         e = launch_k(kProfBwdFscan, bwd_fscan_cg_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
     if (e == hipSuccess) e = launch_k(kProfBwdRscan, bwd_rscan_cg_kernel<DK>, dim3(nscan), dim3(SNT), 0, st, a);
