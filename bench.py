@@ -568,6 +568,32 @@ def main():
                 errs[n] = float(np.abs(x - ref[n]).max() / np.abs(ref[n]).max())
             bwd["parity"] = {"heads": nh, "max_rel_err": errs, "tol": 3e-3}
             del ref
+        # the same gradients with the least workspace the library accepts:
+        # segments of chunks, each segment's states recomputed from a
+        # checkpoint (one more forward state pass, three launches a segment)
+        lws = torch.empty(drl.dr_chunk_bwd_workspace_bytes_min(bdesc), dtype=torch.uint8, device=dev)
+        lgrads = {}
+
+        def lstep():
+            lgrads.update(drl.dr_chunk_bwd(q, k, v, la, be, S0, gdO, gdSf, gate="scalar", workspace=lws))
+
+        for _ in range(2):
+            lstep()
+        torch.cuda.synchronize()
+        lper = time_steps(lstep, args.bwd_steps, 0)
+        lms = float(np.median(lper))
+        lprof = kernel_pass(lstep, args.bwd_steps, lms)
+        lcalls = max(1, lprof["bwd_calls"])
+        bwd["least_workspace"] = {
+            "workspace_bytes": int(lws.numel()), "segment_chunks": 32,
+            "ms_per_step": round(lms, 4), "tokens_per_s": round(B * L / (lms * 1e-3), 1),
+            "kernels_ms": {n: round(lprof[f"bwd_{n}_ms"] / lcalls, 4) for n in ("prep", "fscan", "rscan", "post")},
+            "bit_identical_to_full_workspace": {n: bool(torch.equal(lgrads[n], grads[n]))
+                                                for n in ("dq", "dk", "dv", "dS0")},
+            "max_rel_diff_atomic_sums": {n: float((lgrads[n] - grads[n]).abs().max() / grads[n].abs().max())
+                                         for n in ("dlog_alpha", "dbeta")}}
+        del lws, lgrads
+        torch.cuda.empty_cache()
         # the headline batch with write-side key scales U(0.5, 1.5): the
         # preconditioned rule's backward (channel-gate kernels, the scalar gate
         # broadcast)

@@ -33,7 +33,7 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdeltarule.so")
 
-DR_ABI_VERSION = 9
+DR_ABI_VERSION = 10
 DR_OK, DR_ERR_NULL, DR_ERR_SHAPE, DR_ERR_UNSUPPORTED, DR_ERR_ALIGN, DR_ERR_WORKSPACE, DR_ERR_HIP = range(7)
 DR_F32, DR_BF16 = 0, 1
 GATES = {"none": 0, "scalar": 1, "channel": 2}
@@ -44,7 +44,8 @@ EXPORTS = ("dr_chunk_fwd_workspace_bytes", "dr_chunk_fwd", "dr_chunk_fwd_kv", "d
            "dr_decode_step_precond", "dr_status_str", "dr_last_error", "dr_abi_version",
            "dr_profile_begin", "dr_profile_end", "dr_chunk_bwd_workspace_bytes", "dr_chunk_bwd",
            "dr_chunk_bwd_kv", "dr_chunk_fwd_noalloc", "dr_chunk_fwd_kv_workspace_bytes",
-           "dr_chunk_bwd_kv_workspace_bytes", "dr_chunk_bwd_precond_workspace_bytes", "dr_chunk_bwd_precond")
+           "dr_chunk_bwd_kv_workspace_bytes", "dr_chunk_bwd_precond_workspace_bytes", "dr_chunk_bwd_precond",
+           "dr_chunk_bwd_workspace_bytes_min")
 DR_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
@@ -111,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.dr_decode_step_precond.restype = ctypes.c_int
         L.dr_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
         L.dr_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.dr_chunk_bwd_workspace_bytes_min.argtypes = [ctypes.POINTER(ChunkDesc)]
+        L.dr_chunk_bwd_workspace_bytes_min.restype = ctypes.c_size_t
         L.dr_chunk_fwd_kv_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
         L.dr_chunk_fwd_kv_workspace_bytes.restype = ctypes.c_size_t
         L.dr_chunk_bwd_kv_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
@@ -272,6 +275,12 @@ def dr_chunk_fwd_kv_workspace_bytes(desc: ChunkDesc) -> int:
     return int(lib().dr_chunk_fwd_kv_workspace_bytes(ctypes.byref(desc)))
 
 
+def dr_chunk_bwd_workspace_bytes_min(desc: ChunkDesc) -> int:
+    """The least workspace dr_chunk_bwd accepts (segments of chunks below
+    dr_chunk_bwd_workspace_bytes; equal to it where segments do not apply)."""
+    return int(lib().dr_chunk_bwd_workspace_bytes_min(ctypes.byref(desc)))
+
+
 def dr_chunk_bwd_kv_workspace_bytes(desc: ChunkDesc) -> int:
     return int(lib().dr_chunk_bwd_kv_workspace_bytes(ctypes.byref(desc)))
 
@@ -387,7 +396,10 @@ def dr_chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_final=None, *, gate: str, 
     other inputs are as for dr_chunk_fwd, with the same input preparation
     (qk_l2norm, beta_logit): the gradients are those of the raw inputs.
     Returns a dict of fp32 device tensors dq, dk, dv, dlog_alpha (None for
-    gate "none"), dbeta and dS0 (None with want_dS0=False)."""
+    gate "none"), dbeta and dS0 (None with want_dS0=False).  workspace: a
+    device uint8 tensor (None: one of dr_chunk_bwd_workspace_bytes bytes is
+    allocated); one smaller than that, down to dr_chunk_bwd_workspace_bytes_min,
+    makes the library run the backward in segments of chunks."""
     torch = _torch()
     B, H, L, Dk = q.shape
     Dv = v.shape[-1]

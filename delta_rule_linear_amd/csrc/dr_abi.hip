@@ -443,8 +443,13 @@ dr_status decode_step(const dr_decode_desc* d, const void* q, const void* k, con
 
 // ----------------------------------------------------------------- backward
 struct BwdLayout {
-    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, b32, db1, rq, rk, dla, F, total;
+    size_t T, Pm, A, G, S, H, U, R, dU, Qh, Kh, Kc, Kt, q32, k32, v32, b32, db1, rq, rk, dla, F, Ck, Hc, total;
+    size_t sC;   // chunks per segment (the chunk count of a sequence: no segments)
 };
+
+// The shortest segment a bounded-workspace backward takes, in 64-token chunks
+// (each segment costs three launches).
+constexpr size_t kMinSegChunks = 32;
 
 // Whether a backward call runs on prepared fp32 copies of its inputs: a
 // channel-wise strength, separate strengths (kvtok: of one value per token),
@@ -464,11 +469,17 @@ bool bwd_mc(const dr_chunk_desc& d, bool kvtok, bool precond) {
 }
 
 // precond: write-side key scales, which take the channel-gate kernels for
-// every gate mode
-BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = false) {
+// every gate mode.  seg: chunks per segment of a bounded-workspace backward
+// (matrix-core path only; 0 or >= the chunk count: none), which keeps S_c,
+// H_c and dU for one segment of every sequence, plus a checkpoint of S per
+// later segment and the carried state gradient.
+BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = false, size_t seg = 0) {
     BwdLayout w{};
     const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
     const size_t NCH = (size_t)d.B * d.H * NC;
+    const size_t nseq = (size_t)d.B * d.H;
+    w.sC = seg == 0 || seg >= NC ? NC : seg;
+    const size_t NSL = nseq * w.sC;   // state slots
     const size_t f = sizeof(float);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -486,13 +497,17 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = 
     }
     const bool cg = d.gate == DR_GATE_CHANNEL || precond;
     w.G = take(NCH * dr::CH * (cg ? d.Dk : 1) * f);
-    w.S = take(NCH * d.Dk * d.Dv * f);
-    w.H = take(NCH * d.Dk * d.Dv * f);
+    w.S = take(NSL * d.Dk * d.Dv * f);
+    w.H = take(NSL * d.Dk * d.Dv * f);
     if (!mc) {
         w.U = take(NCH * dr::CH * d.Dv * f);
         w.R = take(NCH * dr::CH * d.Dv * f);
     }
-    w.dU = take(NCH * dr::CH * d.Dv * f);
+    w.dU = take(NSL * dr::CH * d.Dv * f);
+    if (w.sC < NC) {
+        w.Ck = take(((NC + w.sC - 1) / w.sC - 1) * nseq * d.Dk * d.Dv * f);
+        w.Hc = take(nseq * d.Dk * d.Dv * f);
+    }
     if (cg) {
         w.Qh = take(NCH * dr::CH * d.Dk * f);
         w.Kh = take(NCH * dr::CH * d.Dk * f);
@@ -521,6 +536,30 @@ BwdLayout bwd_layout(const dr_chunk_desc& d, bool kvtok = false, bool precond = 
     if (mc) w.F = take(NCH * dr::kBF);
     w.total = NCH ? off : 0;
     return w;
+}
+
+// The workspace layout for `bytes` of workspace: every chunk's states when
+// they fit (or segments are not available), else the longest segments that
+// fit (total > bytes: none does).
+BwdLayout bwd_layout_for(const dr_chunk_desc& d, bool kvtok, bool precond, size_t bytes) {
+    const BwdLayout full = bwd_layout(d, kvtok, precond);
+    const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
+    if (full.total <= bytes || !bwd_mc(d, kvtok, precond)) return full;
+    for (size_t seg = NC - 1; seg >= kMinSegChunks; --seg) {
+        const BwdLayout w = bwd_layout(d, kvtok, precond, seg);
+        if (w.total <= bytes) return w;
+    }
+    return full;
+}
+
+// The least workspace over the segment lengths (the full layout when
+// segments are not available)
+size_t bwd_min_bytes(const dr_chunk_desc& d) {
+    size_t best = bwd_layout(d).total;
+    if (!bwd_mc(d, false, false)) return best;
+    const size_t NC = ((size_t)d.L + dr::CH - 1) / dr::CH;
+    for (size_t seg = kMinSegChunks; seg < NC; ++seg) best = std::min(best, bwd_layout(d, false, false, seg).total);
+    return best;
 }
 
 dr_status check_bwd_desc(const dr_chunk_desc* d) {
@@ -567,7 +606,7 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
                            "dlog_alpha", "dbeta", "dbeta_v", "dS0", "workspace", "key_scale", "dkey_scale"};
     for (int i = 0; i < 19; ++i)
         if (ptrs[i] && !aligned16(ptrs[i])) return fail(DR_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-    const BwdLayout w = bwd_layout(*d, kvtok, precond);
+    const BwdLayout w = bwd_layout_for(*d, kvtok, precond, workspace ? workspace_bytes : 0);
     {
         // the gradients are disjoint from every input, the workspace and each other
         const size_t ntok = nseq * (size_t)d->L;
@@ -594,7 +633,8 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     if (w.total) {
         if (!workspace) return fail(DR_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", w.total);
         if (workspace_bytes < w.total)
-            return fail(DR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, w.total);
+            return fail(DR_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed (%zu at least, in segments)",
+                        workspace_bytes, w.total, kvtok || precond ? w.total : bwd_min_bytes(*d));
     }
     hipStream_t st = (hipStream_t)stream;
     if (nseq == 0) return DR_OK;
@@ -616,6 +656,9 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.B = d->B; a.H = d->H; a.L = d->L; a.Dv = d->Dv;
     a.NC = (d->L + dr::CH - 1) / dr::CH;
     a.nseq = (int)nseq;
+    a.c0 = 0;
+    a.cN = a.NC;
+    a.sC = (int)w.sC;
     a.has_gate = d->gate != DR_GATE_NONE;
     char* ws = (char*)workspace;
     const bool mc = bwd_mc(*d, kvtok, precond);
@@ -628,6 +671,10 @@ dr_status chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const 
     a.wU = mc ? nullptr : (float*)(ws + w.U);
     a.wR = mc ? nullptr : (float*)(ws + w.R);
     a.wdU = (float*)(ws + w.dU);
+    if (w.sC < (size_t)a.NC) {
+        a.wCk = (float*)(ws + w.Ck);
+        a.wHc = (float*)(ws + w.Hc);
+    }
     a.cgate = d->gate == DR_GATE_CHANNEL || precond;
     if (a.cgate) {
         a.wQh = (float*)(ws + w.Qh);
@@ -780,6 +827,11 @@ dr_status dr_decode_step_kv(const dr_decode_desc* d, const void* q, const void* 
 size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d) {
     if (check_bwd_desc(d) != DR_OK) return 0;
     return bwd_layout(*d).total;
+}
+
+size_t dr_chunk_bwd_workspace_bytes_min(const dr_chunk_desc* d) {
+    if (check_bwd_desc(d) != DR_OK) return 0;
+    return bwd_min_bytes(*d);
 }
 
 dr_status dr_chunk_bwd(const dr_chunk_desc* d, const void* q, const void* k, const void* v,

@@ -947,7 +947,7 @@ __device__ __forceinline__ uint4 slab_col(const lchar* pl, int c0, int s, int i1
 // T, the packed P^T (hi and lo: pieces tid < 320 into ppk) and the q rows for
 // the 64 x 64 part (the k rows stay in tKs).
 template <int DK>
-__device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, int valid, size_t tok0, lchar* slab,
+__device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, size_t ss, int valid, size_t tok0, lchar* slab,
                                               lchar* tKs, lchar* tTs, const float* sgam,
                                               f32x4 (&z1)[DK / 32], f32x4 (&z2)[DK / 32], f32x4 (&z3)[DK / 32],
                                               f32x4 (&acc)[4], float* shs, RowsPre<DK, false, PNT>& pq,
@@ -989,7 +989,7 @@ __device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, int vali
             const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
             ps[n] = ph[n] = z;
             if (c4 < vw) {
-                const size_t off = ((size_t)cs * DK + d) * Dv + v0 + c4;
+                const size_t off = (ss * DK + d) * Dv + v0 + c4;
                 ps[n] = *reinterpret_cast<const float4*>(a.wS + off);
                 ph[n] = *reinterpret_cast<const float4*>(a.wH + off);
             }
@@ -997,7 +997,7 @@ __device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, int vali
         const int r = tid / (VS / 4), c4 = (tid % (VS / 4)) * 4;
         po = pd = pdu = z;
         if (c4 < vw) {
-            pdu = *reinterpret_cast<const float4*>(a.wdU + ((size_t)cs * CH + r) * Dv + v0 + c4);
+            pdu = *reinterpret_cast<const float4*>(a.wdU + (ss * CH + r) * Dv + v0 + c4);
             const size_t io = (tok0 + (r < valid ? r : 0)) * Dv + v0 + c4;
             po = *reinterpret_cast<const float4*>(a.dO + io);
             pd = *reinterpret_cast<const float4*>(a.dv + io);
@@ -1181,8 +1181,10 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
     __shared__ float sg[CH], sgam[CH], slam[CH], sb[CH], sdg[CH], sdb[CH];
     __shared__ float shs;
-    const int cs = blockIdx.x;
-    const int seq = cs / a.NC, c = cs - seq * a.NC;
+    // chunk c0 + (bid mod cN) of sequence bid / cN; S_c, H_c and dU in slot ss
+    const int seq = blockIdx.x / a.cN, c = a.c0 + (blockIdx.x - seq * a.cN);
+    const int cs = seq * a.NC + c;
+    const size_t ss = (size_t)seq * a.sC + c % a.sC;
     const int t0 = c * CH, valid = min(CH, a.L - t0);
     const size_t tok0 = (size_t)seq * a.L + t0;
     const int Dv = a.Dv;
@@ -1207,11 +1209,12 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     uint4 ppk[2] = {};   // bf16 inputs: the packed P^T (hi, lo), pieces tid < 320
     f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
     if constexpr (F32IN) {
+        // one slot per chunk on this path (sC == NC, so ss == cs)
         post_state_products<DK, F32IN, false>(a, cs, valid, tok0, s1, z1, z2, z3, acc, &shs, pk, pq, pt, pp, pa);
     } else {
         static_assert(F32IN || CH * 2 * DK <= (int)sizeof(float) * CH * PT, "the k tile fits sM0");
         static_assert(F32IN || 2 * kTriBytes <= (int)sizeof(float) * CH * PT, "T^ fits sM1");
-        post_slabs_rc<DK>(a, cs, valid, tok0, (lchar*)s1, (lchar*)sM0, (lchar*)sM1, sgam, z1, z2, z3, acc, &shs, pq,
+        post_slabs_rc<DK>(a, cs, ss, valid, tok0, (lchar*)s1, (lchar*)sM0, (lchar*)sM1, sgam, z1, z2, z3, acc, &shs, pq,
                           pt, ppk);
     }
     lds_barrier();
@@ -2663,13 +2666,45 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     // kernel writes their operands
     const bool mc = !F32IN && a.wF != nullptr;
     hipError_t e = launch_k(kProfBwdPrep, bwd_prep_kernel<DK, F32IN>, dim3(nch), dim3(NTH), 0, st, a);
-    if (e == hipSuccess)
+    if (e != hipSuccess) return e;
+    if (!mc || a.sC >= a.NC) {
         e = mc ? launch_bwd_fscan16(a, DK, st)
                : launch_k(kProfBwdFscan, bwd_fscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
-    if (e == hipSuccess)
-        e = mc ? launch_bwd_rscan16(a, DK, st)
-               : launch_k(kProfBwdRscan, bwd_rscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
-    if (e == hipSuccess) e = launch_k(kProfBwdPost, bwd_post_kernel<DK, F32IN>, dim3(nch), dim3(PNT), 0, st, a);
+        if (e == hipSuccess)
+            e = mc ? launch_bwd_rscan16(a, DK, st)
+                   : launch_k(kProfBwdRscan, bwd_rscan_kernel<DK, F32IN>, dim3(nscan), dim3(SNT), 0, st, a);
+        if (e == hipSuccess) e = launch_k(kProfBwdPost, bwd_post_kernel<DK, F32IN>, dim3(nch), dim3(PNT), 0, st, a);
+        return e;
+    }
+    // Bounded workspace: segments of sC chunks.  A first forward pass over
+    // every chunk leaves checkpoints of S at the segments' starts and the
+    // last segment's S_c in the slots; then, last segment first, the forward
+    // scan recomputes a segment's S_c from its checkpoint (not for the last
+    // one), the reverse scan walks it from the gradient carried in from the
+    // next segment (dS_final for the last one) and leaves the gradient at
+    // its start in the carry (dS0 for the first one), and the per-chunk
+    // kernel takes its chunks.
+    const int nseg = (a.NC + a.sC - 1) / a.sC, last = (nseg - 1) * a.sC;
+    const size_t sts = (size_t)a.nseq * DK * a.Dv;   // floats of one state per sequence
+    BwdArgs f = a;
+    f.ckEnd = last;
+    e = launch_bwd_fscan16(f, DK, st);
+    for (int sg = nseg - 1; sg >= 0 && e == hipSuccess; --sg) {
+        BwdArgs s = a;
+        s.wCk = nullptr;
+        s.c0 = sg * a.sC;
+        s.cN = std::min(a.sC, a.NC - s.c0);
+        if (sg < nseg - 1) {
+            s.S0 = sg == 0 ? a.S0 : a.wCk + (size_t)(sg - 1) * sts;
+            e = launch_bwd_fscan16(s, DK, st);
+        }
+        s.dS_final = sg == nseg - 1 ? a.dS_final : a.wHc;
+        s.dS0 = sg == 0 ? a.dS0 : a.wHc;
+        if (e == hipSuccess) e = launch_bwd_rscan16(s, DK, st);
+        if (e == hipSuccess)
+            e = launch_k(kProfBwdPost, bwd_post_kernel<DK, F32IN>, dim3((unsigned)a.nseq * (unsigned)s.cN),
+                         dim3(PNT), 0, st, s);
+    }
     return e;
 }
 

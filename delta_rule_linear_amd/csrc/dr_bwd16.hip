@@ -13,6 +13,9 @@
 //             H <- gamma_63 H + Q^T Gamma dO - K^T Gamma dR
 //             (H at every chunk's end state and dU are stored, dR is dv,
 //             and H after the first chunk is dS0).
+// Each launch walks chunks [c0, c0 + cN) of its sequences: all of them, or
+// one segment of a bounded-workspace backward, started from a checkpoint of
+// S (forward) or from the gradient carried from the next segment (reverse).
 // Built like the forward's scan16_kernel (dr_scan16.hip):
 //  * one workgroup per (sequence, 16-column tile of the state), the tiles of
 //    one sequence on one XCD; four compute waves and four copy waves.  The
@@ -248,6 +251,7 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
         wm.done();
     }
     const int NCF = a.L / CH;   // whole chunks (only those are touched ahead)
+    const int cE = a.c0 + a.cN;  // chunks [c0, cE), from the state S0 points to
 
     f32x4 S[NTS];
     if (!copier) {
@@ -261,9 +265,9 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
             st4_terms<true, 2>(sS + i16 * L::SP + 2 * (16 * (w * NTS + t) + 4 * g), 16 * L::SP, S[t]);
         }
     } else {
-        copy0(b0, 0);
-        copy2(b0, 0);
-        const int c1 = min(1, a.NC - 1);
+        copy0(b0, a.c0);
+        copy2(b0, a.c0);
+        const int c1 = min(a.c0 + 1, cE - 1);
         copy0(b1, c1);
         copy2(b1, c1);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(L::NTI + 4));   // chunk 0 has landed
@@ -271,9 +275,8 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
     sync();
 
     auto chunk = [&](const int c, const lchar* buf, lchar* cbuf) {
-        const int cn = min(c + 2, a.NC - 1);
+        const int cn = min(c + 2, cE - 1);
         const int Lc = valid_of(c);
-        const size_t cs = (size_t)seq * a.NC + c;
         auto gt = [&](int i) { return lds_ld<float>(buf + L::GT + 4 * i); };
         uint4 tfr[2][2], kfr[NTS][2];
         float lam[4];
@@ -329,7 +332,11 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
 
         // ---------------- phase 2: U = T^ R, lambda U
         if (copier) {
-            store_staged<DK>(sSf, a.wS + cs * DK * Dv + n0, Dv, DK, l, cw);
+            // one store of S_c per chunk: its slot, or a checkpoint
+            const bool ck = a.wCk && c > 0 && c < a.ckEnd && c % a.sC == 0;
+            float* dst = ck ? a.wCk + ((size_t)(c / a.sC - 1) * a.nseq + seq) * DK * Dv
+                            : a.wS + ((size_t)seq * a.sC + c % a.sC) * DK * Dv;
+            store_staged<DK>(sSf, dst + n0, Dv, DK, l, cw);
         } else {
             uint4 rf[2][2];
 #pragma unroll
@@ -392,10 +399,10 @@ __global__ __launch_bounds__(512) void bwd_fscan16_kernel(BwdArgs a) {
         sync();
     };
 
-    for (int c = 0; c < a.NC; c += 3) {
+    for (int c = a.c0; c < cE; c += 3) {
         chunk(c, b0, b2);
-        if (c + 1 < a.NC) chunk(c + 1, b1, b0);
-        if (c + 2 < a.NC) chunk(c + 2, b2, b1);
+        if (c + 1 < cE) chunk(c + 1, b1, b0);
+        if (c + 2 < cE) chunk(c + 2, b2, b1);
     }
     if (copier) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no copy may land after the workgroup ends
 }
@@ -494,6 +501,7 @@ __global__ __launch_bounds__(512) void bwd_rscan16_kernel(BwdArgs a) {
         wm.done();
     }
     const int NCF = a.L / CH;
+    const int cE = a.c0 + a.cN;   // chunks [c0, cE) in reverse, from the gradient dS_final points to
 
     // dO of chunk c, rows 16 w + 4 g + j, column n0 + i16 (zero past the end)
     auto load_do = [&](int c, float* od) {
@@ -523,29 +531,29 @@ __global__ __launch_bounds__(512) void bwd_rscan16_kernel(BwdArgs a) {
             }
             st4_terms<true, 2>(sH + i16 * L::SP + 2 * (16 * (w * NTS + t) + 4 * g), 16 * L::SP, H[t]);
         }
-        load_do(a.NC - 1, oc);
-        mask_do(a.NC - 1, oc);
+        load_do(cE - 1, oc);
+        mask_do(cE - 1, oc);
         st4_terms<true, 2>(sO + i16 * RP + 2 * (16 * w + 4 * g), 16 * RP, f32x4{oc[0], oc[1], oc[2], oc[3]});
-        if (a.NC > 1) load_do(a.NC - 2, on);
+        if (cE - 1 > a.c0) load_do(cE - 2, on);
     } else {
-        copy0(b0, a.NC - 1);
-        copy2(b0, a.NC - 1);
+        copy0(b0, cE - 1);
+        copy2(b0, cE - 1);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
     sync();
 
     // chunk c (operands in buf); the copy waves fill cbuf with chunk c - 1
     auto chunk = [&](const int c, const lchar* buf, lchar* cbuf) {
-        const int cn = max(c - 1, 0);
+        const int cn = max(c - 1, a.c0);
         const int Lc = valid_of(c);
-        const size_t cs = (size_t)seq * a.NC + c;
+        const size_t cs = (size_t)seq * a.sC + c % a.sC;   // slot of H_c and dU
         auto gt = [&](int i) { return lds_ld<float>(buf + L::GT + 4 * i); };
         uint4 tfr[2][2], kfr[NTS][2], qfr[NTS][2];
         float gam[4];
 
         // ---------------- phase A: dU = P^T dO + Lambda K H; stage H and dU
         if (copier) {
-            if (c + 1 < a.NC)   // dV of chunk c + 1
+            if (c + 1 < cE)   // dV of chunk c + 1
                 store_staged<64>(sDRf, a.dv + ((size_t)seq * a.L + (size_t)(c + 1) * CH) * Dv + n0, Dv,
                                  valid_of(c + 1), l, cw);
             copy0(cbuf, cn);
@@ -679,24 +687,25 @@ __global__ __launch_bounds__(512) void bwd_rscan16_kernel(BwdArgs a) {
                 for (int j = 0; j < 4; ++j) H[t][j] = d63 * H[t][j] + (hq[j] - hk[j]);
                 st4_terms<true, 2>(sH + i16 * L::SP + 2 * (rt + 4 * g), 16 * L::SP, H[t]);
             }
-            if (c > 0) {
+            if (c > a.c0) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) oc[j] = on[j];
                 mask_do(c - 1, oc);
                 st4_terms<true, 2>(sO + i16 * RP + 2 * (16 * w + 4 * g), 16 * RP, f32x4{oc[0], oc[1], oc[2], oc[3]});
-                if (c > 1) load_do(c - 2, on);
+                if (c > a.c0 + 1) load_do(c - 2, on);
             }
         }
         sync();
     };
 
-    for (int i = 0; i < a.NC; i += 2) {
-        const int c = a.NC - 1 - i;
+    for (int i = 0; i < a.cN; i += 2) {
+        const int c = cE - 1 - i;
         chunk(c, b0, b1);
-        if (c - 1 >= 0) chunk(c - 1, b1, b0);
+        if (c - 1 >= a.c0) chunk(c - 1, b1, b0);
     }
     if (copier) {
-        store_staged<64>(sDRf, a.dv + (size_t)seq * a.L * Dv + n0, Dv, valid_of(0), l, cw);   // dV of chunk 0
+        // dV of chunk c0
+        store_staged<64>(sDRf, a.dv + ((size_t)seq * a.L + (size_t)a.c0 * CH) * Dv + n0, Dv, valid_of(a.c0), l, cw);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     } else if (a.dS0) {
 #pragma unroll

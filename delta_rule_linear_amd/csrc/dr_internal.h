@@ -160,6 +160,19 @@ struct BwdArgs {
     float* dks;
     // the matrix-core scans' operands (bf16 inputs, no channel gate), or NULL
     char* wF;
+    // Chunk range and state slots.  A launch of the scans or of the per-chunk
+    // kernel covers chunks [c0, c0 + cN) of every sequence.  The per-chunk
+    // S_c, H_c and dU sit in slot seq * sC + c % sC of wS, wH and wdU (sC ==
+    // NC: one slot per chunk).  With sC < NC (bounded workspace, matrix-core
+    // path only) the host walks segments of sC chunks, last to first; the
+    // forward scan's first pass over all chunks then stores S_c of every
+    // chunk c = j sC with 0 < c < ckEnd into the checkpoint slot
+    // wCk[(j - 1) nseq + seq] in place of its slot in wS.
+    // wHc carries the reverse scan's gradient from one segment to the next.
+    int c0, cN, sC;
+    float* wCk;
+    int ckEnd;
+    float* wHc;
 };
 
 // Optional per-kernel timing (dr_profile_begin / dr_profile_end).  While it is

@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define DR_ABI_VERSION 9
+#define DR_ABI_VERSION 10
 
 typedef enum {
     DR_OK = 0,
@@ -309,6 +309,20 @@ dr_status dr_decode_step_precond(const dr_decode_desc* d, const void* q, const v
  * with DR_IN_BETA_LOGIT alone one float per token. */
 size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
 
+/* The least workspace dr_chunk_bwd accepts for `d` (0 if d is invalid or
+ * there is no work).  For bf16 inputs with a scalar gate or none, a scalar
+ * beta and no input preparation, a workspace below
+ * dr_chunk_bwd_workspace_bytes(d) makes the call run in segments of at least
+ * 32 chunks (2048 tokens), the longest that fit: it keeps S_c, H_c and dU of
+ * one segment of every sequence instead of every chunk's, plus a checkpoint
+ * of S at each later segment's start and the state gradient carried between
+ * segments.  That costs one more forward state pass (every segment's start
+ * states are recomputed from their checkpoints) and three launches per
+ * segment; the gradients are the same up to rounding order (none: the
+ * arithmetic per chunk is unchanged).  For every other mode this equals
+ * dr_chunk_bwd_workspace_bytes(d). */
+size_t dr_chunk_bwd_workspace_bytes_min(const dr_chunk_desc* d);
+
 /*
  * dr_chunk_bwd -- gradients of dr_chunk_fwd's o and S_final with respect to
  * every input, for the loss whose gradients with respect to o and S_final
@@ -349,8 +363,11 @@ size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
  *   dbeta      beta's shape ([B][H][L] or [B][H][L][Dk]) fp32, written
  *   dS0        [B][H][Dk][Dv] fp32, gradient with respect to S0, written, or
  *              NULL to skip
- *   workspace  device scratch of at least dr_chunk_bwd_workspace_bytes(d)
- *              bytes; contents on entry ignored, on exit unspecified
+ *   workspace  device scratch of workspace_bytes bytes, at least
+ *              dr_chunk_bwd_workspace_bytes_min(d); with less than
+ *              dr_chunk_bwd_workspace_bytes(d) the call runs in segments
+ *              (see dr_chunk_bwd_workspace_bytes_min); contents on entry
+ *              ignored, on exit unspecified; fewer bytes: DR_ERR_WORKSPACE
  * Outputs must not overlap each other or any input.  Returns DR_OK or an
  * error status; nothing is launched on an error.
  */

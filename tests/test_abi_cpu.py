@@ -385,3 +385,28 @@ def test_noalloc_validation():
     hdr = open(HEADER).read()
     assert re.search(r"#define DR_NOALLOC_SCRATCH_BYTES \(\(size_t\)256 << 20\)", hdr)
     assert drl.DR_NOALLOC_SCRATCH_BYTES == 256 << 20
+
+
+def test_backward_least_workspace():
+    # bf16, scalar gate, 16384 tokens: segments of 32 chunks keep the
+    # workspace far below the one that stores every chunk's states
+    d = _desc(B=2, H=16, L=16384)
+    full, least = drl.dr_chunk_bwd_workspace_bytes(d), drl.dr_chunk_bwd_workspace_bytes_min(d)
+    assert least < 0.6e9 < full
+    nseq, NC, st = 32, 256, 128 * 128 * 4
+    # the states S_c and H_c of every chunk (the larger part of the full one)
+    assert full - least > 2 * nseq * (NC - 32) * st
+    # no segments: 32 chunks or fewer, fp32 inputs, a channel gate or beta, the input preparation
+    for kw in (dict(L=32 * 64), dict(in_dtype=drl.DR_F32), dict(gate="channel"), dict(beta_mode="channel"),
+               dict(flags=drl.DR_IN_QK_L2NORM)):
+        dd = _desc(**{**dict(B=2, H=16, L=16384), **kw})
+        assert drl.dr_chunk_bwd_workspace_bytes_min(dd) == drl.dr_chunk_bwd_workspace_bytes(dd), kw
+    assert drl.dr_chunk_bwd_workspace_bytes_min(_desc(L=0)) == 0
+    assert drl.dr_chunk_bwd_workspace_bytes_min(_desc(Dk=96)) == 0
+    # below the least workspace the call is rejected before any launch
+    lib = drl.lib()
+    args = [F(i) for i in range(14)]
+    for wbytes, code in ((least - 1, drl.DR_ERR_WORKSPACE), (0, drl.DR_ERR_WORKSPACE)):
+        st_ = lib.dr_chunk_bwd(ctypes.byref(d), *args[:6], *args[6:8], *args[8:13], None, F(13), wbytes, None)
+        assert st_ == code
+        assert "at least" in drl.dr_last_error()

@@ -446,3 +446,105 @@ def test_backward_precond_full_size_every_sequence():
     _every_sequence(p.name, g, ref, GRADS + ("dkey_scale",))
     del g, ref
     torch.cuda.empty_cache()
+
+
+# ------------------------------------- bounded workspace: segments of chunks
+
+def _bwd_with_workspace(p, dO, dSf, nbytes, want_dS0=True):
+    import delta_rule_linear_amd as drl
+    t = problem_to_dev(p)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+    g = drl.dr_chunk_bwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S0"], to_dev(dO, "f32"),
+                         None if dSf is None else to_dev(dSf, "f32"), gate=p.gate, beta_mode=p.beta_mode,
+                         want_dS0=want_dS0, workspace=ws)
+    torch.cuda.synchronize()
+    return g
+
+
+ATOMIC_SUMS = ("dlog_alpha", "dbeta")
+
+
+def _same_gradients(name, g, f, what):
+    for n in GRADS:
+        if f[n] is None:
+            assert g[n] is None, n
+        elif n in ATOMIC_SUMS:
+            d = (g[n] - f[n]).abs().max().item() / max(f[n].abs().max().item(), 1e-30)
+            assert d <= 1e-6, f"{name}: {n} differs by {d:.1e} ({what})"
+        else:
+            assert torch.equal(g[n], f[n]), f"{name}: {n} differs ({what})"
+
+
+def _desc(p):
+    import delta_rule_linear_amd as drl
+    return drl.chunk_desc(p.B, p.H, p.L, p.Dk, p.Dv, drl.DR_BF16 if p.in_dtype == "bf16" else drl.DR_F32,
+                          drl.DR_F32, p.gate, p.beta_mode, 0)
+
+
+@pytest.mark.parametrize("gate", ["none", "scalar"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_segments_match_full_workspace(gate, D):
+    # 76 chunks (a ragged last one): with the least workspace the call runs
+    # segments of 32, 32 and 12 chunks; one byte short of the full workspace
+    # gives segments of 75 and 1; in between 38 and 38.  Each segment starts
+    # from a checkpoint of S and the carried state gradient, with the same
+    # per-chunk arithmetic, so the gradients are bit-identical to those of
+    # the call that keeps every chunk's states, and within bounds of the
+    # oracle
+    # (dbeta and dlog_alpha are sums that the per-chunk kernel accumulates
+    # with LDS atomics, in an order that varies from run to run, so those two
+    # are compared to 1e-6 of their largest entry, as two full-workspace runs
+    # differ too)
+    import delta_rule_linear_amd as drl
+    p = inputs.make_chunk_problem(1, 3, 64 * 75 + 17, D, D, gate=gate, s0_var=0.01, seed=D + 5,
+                                  name=f"segments-{gate}-D{D}")
+    d = _desc(p)
+    full, least = drl.dr_chunk_bwd_workspace_bytes(d), drl.dr_chunk_bwd_workspace_bytes_min(d)
+    assert least < full
+    dO, dSf = inputs.backward_cotangents(p, 1)
+    announce("backward segments", p.name, full, least)
+    ref_g = _bwd_with_workspace(p, dO, dSf, full)
+    for nbytes in (least, full - 1, (least + full) // 2):
+        g = _bwd_with_workspace(p, dO, dSf, nbytes)
+        _same_gradients(p.name, g, ref_g, f"{nbytes} of {full} bytes")
+    ref = oracle_bwd(p, dO, dSf)
+    for n in GRADS:
+        if ref[n] is not None:
+            assert rel_err(to_np(g[n]), ref[n]) <= TOL["bf16"], n
+    # without S0, dS_final and dS0
+    p.S0 = None
+    g0 = _bwd_with_workspace(p, dO, None, least, want_dS0=False)
+    f0 = _bwd_with_workspace(p, dO, None, full, want_dS0=False)
+    assert g0["dS0"] is None
+    _same_gradients(p.name, g0, f0, "no S0, dS_final or dS0")
+
+
+def test_backward_segments_full_size_every_sequence():
+    # the benchmark's GDN shape with the least workspace (segments of 32
+    # chunks): the same gradients as the full-workspace call (bit for bit
+    # but for the atomic sums), every sequence within bounds of the oracle
+    import delta_rule_linear_amd as drl
+    p = inputs.workload("gdn_b2h16_16k")
+    d = _desc(p)
+    full, least = drl.dr_chunk_bwd_workspace_bytes(d), drl.dr_chunk_bwd_workspace_bytes_min(d)
+    announce("backward segments full size", p.name, full, least)
+    assert least < 0.6e9 < full
+    dO, dSf = inputs.backward_cotangents(p, 0)
+    g = _bwd_with_workspace(p, dO, dSf, least)
+    f = _bwd_with_workspace(p, dO, dSf, full)
+    _same_gradients(p.name, g, f, "least workspace")
+    del f
+    torch.cuda.empty_cache()
+    ref = oracle_bwd(p, dO, dSf)
+    _every_sequence(p.name, g, ref, GRADS)
+    del g, ref
+    torch.cuda.empty_cache()
+
+
+def test_backward_workspace_below_least_is_rejected():
+    import delta_rule_linear_amd as drl
+    p = inputs.make_chunk_problem(1, 1, 64 * 40, 64, 64, gate="scalar", seed=2, name="segments-too-small")
+    least = drl.dr_chunk_bwd_workspace_bytes_min(_desc(p))
+    dO, dSf = inputs.backward_cotangents(p, 1)
+    with pytest.raises(RuntimeError, match="at least"):
+        _bwd_with_workspace(p, dO, dSf, least - 256)
