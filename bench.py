@@ -588,10 +588,8 @@ def main():
             "workspace_bytes": int(lws.numel()), "segment_chunks": 32,
             "ms_per_step": round(lms, 4), "tokens_per_s": round(B * L / (lms * 1e-3), 1),
             "kernels_ms": {n: round(lprof[f"bwd_{n}_ms"] / lcalls, 4) for n in ("prep", "fscan", "rscan", "post")},
-            "bit_identical_to_full_workspace": {n: bool(torch.equal(lgrads[n], grads[n]))
-                                                for n in ("dq", "dk", "dv", "dS0")},
-            "max_rel_diff_atomic_sums": {n: float((lgrads[n] - grads[n]).abs().max() / grads[n].abs().max())
-                                         for n in ("dlog_alpha", "dbeta")}}
+            "bit_identical_to_full_workspace": all(bool(torch.equal(lgrads[n], grads[n])) for n in grads
+                                                   if grads[n] is not None)}
         del lws, lgrads
         torch.cuda.empty_cache()
         # the headline batch with write-side key scales U(0.5, 1.5): the

@@ -702,6 +702,14 @@ __device__ __forceinline__ Frag<2> slab_frag(const half_t* hi, const half_t* lo,
 
 // Sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the same column of an
 // accumulator block).
+// x summed over the wave's 64 lanes by shuffles (a fixed order), written to
+// part[wave] by lane 0
+__device__ __forceinline__ void wave_partial(float x, float* part) {
+    x = group_sum<32>(x);
+    x += __shfl_xor(x, 32);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+}
+
 __device__ __forceinline__ float col4_sum(float x) {
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
@@ -872,7 +880,7 @@ __device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, in
                 if (I <= R) acc[I] = mma<2, 2>(fdu, slab_frag(sRh, sRl, 16 * I + i16, g), acc[I]);
         }
     }
-    if constexpr (!CG) atomicAdd(&shs[0], hs);
+    if constexpr (!CG) wave_partial(hs, shs);
 }
 
 // Where piece `piece` of row r of a swizzled tile is written (as tile_at).
@@ -1131,7 +1139,7 @@ __device__ __forceinline__ void post_slabs_rc(const BwdArgs& a, int cs, size_t s
                 if (I <= R) acc[I] = mma3(fdu, slab_row(sRh, sRl, 16 * I + i16, g), acc[I]);
         }
     }
-    atomicAdd(&shs[0], hs);
+    wave_partial(hs, shs);
 }
 
 // bf16 rows prefetched by pre_rows into a swizzled [64][2 DK]-byte tile (rows
@@ -1179,8 +1187,8 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     __shared__ float sM2[CH * PT];   // K K^T o E (strict lower)
     __shared__ float sM3[CH * PT];   // N = dP o E
     __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
-    __shared__ float sg[CH], sgam[CH], slam[CH], sb[CH], sdg[CH], sdb[CH];
-    __shared__ float shs;
+    __shared__ float sg[CH], sgam[CH], slam[CH], sb[CH];
+    __shared__ float shs[PNT / 64];   // <H, S>: one partial per wave
     // chunk c0 + (bid mod cN) of sequence bid / cN; S_c, H_c and dU in slot ss
     const int seq = blockIdx.x / a.cN, c = a.c0 + (blockIdx.x - seq * a.cN);
     const int cs = seq * a.NC + c;
@@ -1199,10 +1207,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         sgam[tid] = expf(gv);
         slam[tid] = expf(g63 - gv);
         sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
-        sdg[tid] = 0.f;
-        sdb[tid] = 0.f;
     }
-    if (tid == 0) shs = 0.f;
 
     RowsPre<DK, F32IN, PNT> pk, pq;
     MatPre<PNT> pt, pp, pa;
@@ -1210,11 +1215,11 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
     f32x4 z1[NDH], z2[NDH], z3[NDH], acc[4];
     if constexpr (F32IN) {
         // one slot per chunk on this path (sC == NC, so ss == cs)
-        post_state_products<DK, F32IN, false>(a, cs, valid, tok0, s1, z1, z2, z3, acc, &shs, pk, pq, pt, pp, pa);
+        post_state_products<DK, F32IN, false>(a, cs, valid, tok0, s1, z1, z2, z3, acc, shs, pk, pq, pt, pp, pa);
     } else {
         static_assert(F32IN || CH * 2 * DK <= (int)sizeof(float) * CH * PT, "the k tile fits sM0");
         static_assert(F32IN || 2 * kTriBytes <= (int)sizeof(float) * CH * PT, "T^ fits sM1");
-        post_slabs_rc<DK>(a, cs, ss, valid, tok0, (lchar*)s1, (lchar*)sM0, (lchar*)sM1, sgam, z1, z2, z3, acc, &shs, pq,
+        post_slabs_rc<DK>(a, cs, ss, valid, tok0, (lchar*)s1, (lchar*)sM0, (lchar*)sM1, sgam, z1, z2, z3, acc, shs, pq,
                           pt, ppk);
     }
     lds_barrier();
@@ -1446,14 +1451,25 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
             }
         }
     }
-    // ---- reductions of the gate and strength terms
+    // ---- reductions of the gate and strength terms, in a fixed order (so
+    // that the gradients do not depend on the order the waves finish in):
+    // each wave's row and column partials go to their own slots of sM2
+    // (K K^T o E, no longer read), then lane l of wave 0 adds those of
+    // token l.  Rows: [2 halves][64] for dg, then for dbeta; columns: [8
+    // waves][64] for each; then the 8 waves' parts of the last row's sum.
+    float* prg = sM2;
+    float* prb = prg + 2 * CH;
+    float* pcg = prb + 2 * CH;
+    float* pcb = pcg + 8 * CH;
+    float* p63 = pcb + 8 * CH;
+    static_assert(PNT == 512 && 20 * CH + 8 <= CH * PT, "the partials fit sM2");
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float xg = group_sum<16>(rowg[j]);
         const float xb = group_sum<16>(rowb[j]);
         if (i16 == 0) {
-            atomicAdd(&sdg[rb + j], xg);
-            atomicAdd(&sdb[rb + j], xb);
+            prg[hf * CH + rb + j] = xg;
+            prb[hf * CH + rb + j] = xb;
         }
     }
 #pragma unroll
@@ -1461,20 +1477,33 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         const float xg = col4_sum(colg[I]);
         const float xb = col4_sum(colb[I]);
         if (g == 0) {
-            atomicAdd(&sdg[16 * I + i16], xg);
-            atomicAdd(&sdb[16 * I + i16], xb);
+            pcg[w * CH + 16 * I + i16] = xg;
+            pcb[w * CH + 16 * I + i16] = xb;
         }
     }
     {
         float x = group_sum<32>(g63part);
         x += __shfl_xor(x, 32);
-        if (l == 0) atomicAdd(&sdg[CH - 1], x);
+        if (l == 0) p63[w] = x;
     }
     lds_barrier();
     if (w == 0) {
+        float x = prg[l] + prg[CH + l], xb = prb[l] + prb[CH + l];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            x += pcg[v * CH + l];
+            xb += pcb[v * CH + l];
+        }
+        if (l == CH - 1) {
+            float h = 0.f;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                x += p63[v];
+                h += shs[v];
+            }
+            x += expf(sg[CH - 1]) * h;
+        }
         // d log alpha_t = sum over r >= t of dg_r (suffix sum over the lanes)
-        float x = sdg[l];
-        if (l == CH - 1) x += expf(sg[CH - 1]) * shs;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const float y2 = __shfl_down(x, o);
@@ -1482,7 +1511,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_kernel(BwdArgs a) {
         }
         if (l < valid) {
             if (a.dlog_alpha) a.dlog_alpha[tok0 + l] = x;
-            a.dbeta[tok0 + l] = sdb[l];
+            a.dbeta[tok0 + l] = xb;
         }
     }
 #pragma unroll
