@@ -806,6 +806,7 @@ __device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, in
 #pragma unroll
     for (int I = 0; I < 4; ++I) acc[I] = zero4();
     float hs = 0.f;
+    float hsr[NS] = {};   // CG: <H, S> of this thread's state row in each of its NS pieces, over the slabs
     half_t* sSh = reinterpret_cast<half_t*>(s1);
     half_t* sSl = sSh + DK * VS;
     half_t* sHh = sSl + DK * VS;
@@ -827,7 +828,7 @@ __device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, in
         for (int n = 0; n < NS; ++n) {
             const int e = tid + n * PNT, d = e / (VS / 4), c4 = (e % (VS / 4)) * 4;
             const float hsn = ps[n].x * ph[n].x + ps[n].y * ph[n].y + ps[n].z * ph[n].z + ps[n].w * ph[n].w;
-            if constexpr (CG) atomicAdd(&shs[d], hsn);
+            if constexpr (CG) hsr[n] += hsn;
             else hs += hsn;
             put_split4(sSh, sSl, d, c4, ps[n]);
             put_split4(sHh, sHl, d, c4, ph[n]);
@@ -880,7 +881,17 @@ __device__ __forceinline__ void post_state_products(const BwdArgs& a, int cs, in
                 if (I <= R) acc[I] = mma<2, 2>(fdu, slab_frag(sRh, sRl, 16 * I + i16, g), acc[I]);
         }
     }
-    if constexpr (!CG) wave_partial(hs, shs);
+    if constexpr (CG) {
+        // the VS / 4 consecutive lanes of a state row summed by shuffles (a
+        // fixed order), written once per row
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            const float x = group_sum<VS / 4>(hsr[n]);
+            if (tid % (VS / 4) == 0) shs[(tid + n * PNT) / (VS / 4)] = x;
+        }
+    } else {
+        wave_partial(hs, shs);
+    }
 }
 
 // Where piece `piece` of row r of a swizzled tile is written (as tile_at).
@@ -2243,7 +2254,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     __shared__ float sM2[CH * PT];   // K^ Kc^T (strict lower)
     __shared__ float sM3[CH * PT];   // N = lower dP
     __shared__ float sM4[CH * PT];   // dT^ Diag(beta), then T^T of it
-    __shared__ float sb[CH], sdb[CH], shs[DK];
+    __shared__ float sb[CH], shs[DK];
     __shared__ int s_shift;
     const int cs = blockIdx.x;
     const int seq = cs / a.NC, c = cs - seq * a.NC;
@@ -2253,11 +2264,7 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
     const int R = w & 3, hf = w >> 2, D0 = hf * NDH;
     const size_t mo = (size_t)cs * CH * CH, pofs = (size_t)cs * CH * DK;
 
-    if (tid < CH) {
-        sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
-        sdb[tid] = 0.f;
-    }
-    if (tid < DK) shs[tid] = 0.f;
+    if (tid < CH) sb[tid] = tid < valid ? a.beta[tok0 + tid] : 0.f;
     if (tid == 0) s_shift = 0;
     // shifted operands, as the preparation kernel chose them for this chunk
     // (rows of a chunk operand relative to G_m = G_63 / 2)
@@ -2412,16 +2419,21 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
             dkc[D] = mfma_f32x4(sM1[m * PT + 16 * R + i16], sKx[m * KP + cb], dkc[D]);
         }
     }
-    // ---- dbeta's row and column sums
+    // ---- dbeta's row and column sums, in a fixed order: each wave's partials
+    // to their own slots of sM2 (K^ Kc^T, no longer read), rows [2 halves][64]
+    // then columns [8 waves][64], added up per token at the end
+    float* prb = sM2;
+    float* pcb = prb + 2 * CH;
+    static_assert(PNT == 512 && 10 * CH <= CH * PT, "the partials fit sM2");
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float xb = group_sum<16>(rowb[j]);
-        if (i16 == 0) atomicAdd(&sdb[rb + j], xb);
+        if (i16 == 0) prb[hf * CH + rb + j] = xb;
     }
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
         const float xb = col4_sum(colb[I]);
-        if (g == 0) atomicAdd(&sdb[16 * I + i16], xb);
+        if (g == 0) pcb[w * CH + 16 * I + i16] = xb;
     }
     lds_barrier();
     // ---- per element: dq, dk, and the two parts of dG,
@@ -2507,7 +2519,12 @@ __global__ __launch_bounds__(PNT) void bwd_post_cg_kernel(BwdArgs a) {
         sy += sYg[r * KP + ch];
         if (r < valid && a.dla_cg) a.dla_cg[(tok0 + r) * DK + ch] = sufX + before + (py - sy) + hsc;
     }
-    if (w == 0 && l < valid) a.dbeta[tok0 + l] = sdb[l];
+    if (w == 0 && l < valid) {
+        float xb = prb[l] + prb[CH + l];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) xb += pcb[v * CH + l];
+        a.dbeta[tok0 + l] = xb;
+    }
 }
 
 template <int DK, bool F32IN>

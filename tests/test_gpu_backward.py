@@ -470,12 +470,13 @@ def _same_gradients(name, g, f, what):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("gate", ["none", "scalar"])
+@pytest.mark.parametrize("gate", ["none", "scalar", "channel"])
 def test_backward_is_deterministic(dtype, gate):
-    # without a channel gate every sum of the backward runs in a fixed order
-    # (no float atomics), so repeated calls give the same bits
+    # every sum of the backward runs in a fixed order (no float atomics), so
+    # repeated calls give the same bits
+    rng = inputs.KDA_GATE if gate == "channel" else inputs.GDN_GATE
     p = inputs.make_chunk_problem(2, 3, 64 * 9 + 5, 128, 128, in_dtype=dtype, gate=gate, s0_var=0.01, seed=11,
-                                  name=f"determinism-{dtype}-{gate}")
+                                  log_alpha_range=rng, name=f"determinism-{dtype}-{gate}")
     announce("backward determinism", p.name)
     dO, dSf = inputs.backward_cotangents(p, 2)
     first = run_bwd(p, dO, dSf)
