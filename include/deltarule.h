@@ -318,9 +318,9 @@ size_t dr_chunk_bwd_workspace_bytes(const dr_chunk_desc* d);
  * of S at each later segment's start and the state gradient carried between
  * segments.  That costs one more forward state pass (every segment's start
  * states are recomputed from their checkpoints) and three launches per
- * segment; the gradients are the same up to rounding order (none: the
- * arithmetic per chunk is unchanged).  For every other mode this equals
- * dr_chunk_bwd_workspace_bytes(d). */
+ * segment; the gradients are bit-identical to those of a call with the full
+ * workspace (the arithmetic per chunk is unchanged).  For every other mode
+ * this equals dr_chunk_bwd_workspace_bytes(d). */
 size_t dr_chunk_bwd_workspace_bytes_min(const dr_chunk_desc* d);
 
 /*
@@ -331,7 +331,8 @@ size_t dr_chunk_bwd_workspace_bytes_min(const dr_chunk_desc* d);
  * (DeltaNet page, step 7 and the hardware notes; FG2-GDN page, section 2),
  * evaluated chunk by chunk: a sequential pass recomputes each chunk's start
  * state, a reverse pass carries the state gradient, and a per-chunk pass
- * forms the gradients of q, k, beta and log alpha.  Everything runs in fp32.
+ * forms the gradients of q, k, beta and log alpha.  Everything runs in fp32,
+ * and every sum in a fixed order: repeated calls give the same bits.
  *
  * Covered modes: every gate and beta mode (plain DeltaNet, Gated DeltaNet,
  * KDA, FG2-GDN), every input_flags combination, d->out_dtype DR_F32 (the
